@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs for the four fused operators.
+
+This module is shared by the tests, ``bench.py`` and ``smoke()``: it is the
+only code that both the CPU oracle and the HIP path consume.  It therefore
+holds no arithmetic of the fused operators themselves -- only random draws,
+the fp32 -> bf16 encoding of the drawn values (round to nearest even), and
+index sampling.
+
+Recipe (the same for every size):
+
+* ``numpy.random.default_rng(seed)`` (PCG64); tensors are drawn in the order
+  they are listed for the operator.
+* ``N(0, s)``: ``standard_normal(float32) * s`` (``s`` is a standard
+  deviation); ``U[-1, 1)``: ``uniform(-1, 1)`` cast to float32.
+* bf16 tensors are the round-to-nearest-even encoding of the fp32 draws and
+  are carried as ``uint16`` bit patterns.
+* Embedding indices: bounded Zipf over ranks ``k = 1..R`` with
+  ``p(k) ~ k**-alpha`` and row ``k - 1`` (hot rows are the low row numbers),
+  drawn per table by inverse-CDF sampling from
+  ``SeedSequence(seed).spawn(T)[t]``.
+* Embedding tables too large for host memory are drawn on the device with
+  ``torch.randn`` from a ``torch.Generator`` seeded ``seed * 1000 + t`` per
+  table (``embbag_tables_torch``); the oracle then receives the rows it needs
+  copied back from those same device bytes.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+F32 = 0
+BF16 = 1
+
+
+def bf16_encode(x: np.ndarray) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns (uint16), round to nearest even.
+
+    Inputs are finite (the generators never draw NaN or Inf)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_decode(h: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> fp32 values (exact)."""
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    return rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+
+
+def _draw(rng, shape, dist, dtype):
+    """Draw one tensor.  dist: ('normal', std) | ('uniform',) | ('int', lo, hi)."""
+    kind = dist[0]
+    if kind == "normal":
+        v = _normal(rng, shape, dist[1])
+    elif kind == "uniform":
+        v = rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
+    elif kind == "int":
+        v = rng.integers(dist[1], dist[2] + 1, size=shape).astype(np.float32)
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    return bf16_encode(v) if dtype == BF16 else v
+
+
+def gemm_rs_inputs(P, M, N, K, dtype, seed=0, dist_a=("normal", 1.0), dist_w=("normal", 0.02)):
+    """A [P][M][K] then W [P][K][N]."""
+    rng = np.random.default_rng(seed)
+    A = _draw(rng, (P, M, K), dist_a, dtype)
+    W = _draw(rng, (P, K, N), dist_w, dtype)
+    return A, W
+
+
+def gemv_ar_inputs(P, Mb, N, K, dtype=BF16, seed=0, dist_x=("normal", 1.0), dist_w=("normal", 0.02)):
+    """x [P][Mb][K] then W [P][K][N]."""
+    rng = np.random.default_rng(seed)
+    x = _draw(rng, (P, Mb, K), dist_x, dtype)
+    W = _draw(rng, (P, K, N), dist_w, dtype)
+    return x, W
+
+
+def ag_gemm_inputs(P, Mc, N, K, dtype=BF16, seed=0, dist_a=("normal", 1.0), dist_w=("normal", 0.02)):
+    """chunks [P][Mc][K], then W [K][N], then the chunk release order."""
+    rng = np.random.default_rng(seed)
+    chunks = _draw(rng, (P, Mc, K), dist_a, dtype)
+    W = _draw(rng, (K, N), dist_w, dtype)
+    order = rng.permutation(P).astype(np.int64)
+    return chunks, W, order
+
+
+def zipf_cdf(R: int, alpha: float) -> np.ndarray:
+    """CDF of the bounded Zipf law over ranks 1..R (fp64)."""
+    w = np.arange(1, R + 1, dtype=np.float64) ** (-alpha)
+    c = np.cumsum(w)
+    return c / c[-1]
+
+
+def zipf_indices(T, B, L, R, alpha=1.05, seed=0, cdf=None) -> np.ndarray:
+    """int32 indices [T][B][L]; table t drawn from SeedSequence(seed).spawn(T)[t]."""
+    if cdf is None:
+        cdf = zipf_cdf(R, alpha)
+    out = np.empty((T, B, L), dtype=np.int32)
+    for t, ss in enumerate(np.random.SeedSequence(seed).spawn(T)):
+        u = np.random.default_rng(ss).random(B * L)
+        k = np.searchsorted(cdf, u, side="right")
+        np.minimum(k, R - 1, out=k)
+        out[t] = k.reshape(B, L).astype(np.int32)
+    return out
+
+
+def uniform_indices(T, B, L, R, seed=0) -> np.ndarray:
+    out = np.empty((T, B, L), dtype=np.int32)
+    for t, ss in enumerate(np.random.SeedSequence(seed).spawn(T)):
+        out[t] = np.random.default_rng(ss).integers(0, R, size=(B, L), dtype=np.int32)
+    return out
+
+
+def embbag_tables(T, R, D, std=0.01, seed=0) -> np.ndarray:
+    """fp32 tables [T][R][D] drawn on the host (sizes that fit in host memory)."""
+    rng = np.random.default_rng(seed)
+    return _normal(rng, (T, R, D), std)
+
+
+def embbag_tables_torch(T, R, D, std=0.01, seed=0, device="cuda"):
+    """fp32 tables [T][R][D] drawn on ``device``, one seeded generator per table."""
+    import torch
+
+    tab = torch.empty((T, R, D), dtype=torch.float32, device=device)
+    for t in range(T):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed * 1000 + t)
+        tab[t].normal_(0.0, 1.0, generator=g)
+        tab[t].mul_(std)
+    return tab
+
+
+def tagged_tables(T, R, D) -> np.ndarray:
+    """Table t, row i = (i & 0xFFF, i >> 12, t, 1, 0, ...): pooled sums of these
+    rows are exact small integers, so a misrouted bag, a wrong index or a wrong
+    table shows up bit-exactly (dimension 3 counts the bag's length)."""
+    assert D >= 4
+    tab = np.zeros((T, R, D), dtype=np.float32)
+    i = np.arange(R)
+    tab[:, :, 0] = (i & 0xFFF)[None, :]
+    tab[:, :, 1] = (i >> 12)[None, :]
+    tab[:, :, 2] = np.arange(T, dtype=np.float32)[:, None]
+    tab[:, :, 3] = 1.0
+    return tab
+
+
+def csr_bag_offsets(T, B, max_len, seed=0, empty_frac=0.1) -> np.ndarray:
+    """int64 offsets [T*B + 1] for ragged bags: lengths uniform in 1..max_len,
+    with a fraction ``empty_frac`` of bags forced empty."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, max_len + 1, size=T * B)
+    lens[rng.random(T * B) < empty_frac] = 0
+    off = np.zeros(T * B + 1, dtype=np.int64)
+    np.cumsum(lens, out=off[1:])
+    return off

@@ -1,0 +1,156 @@
+"""CPU oracle for the fused computation + collective-epilogue operators.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``, never by the product path.  It
+shares no code with the HIP library; it is a thin ctypes wrapper over
+``oracle.c`` (plain C, fp64 accumulation, fixed rank-order fp32 folds).
+
+Data types: 0 = fp32 (numpy float32), 1 = bf16 carried as numpy uint16 bit
+patterns.  Every array argument must be C-contiguous.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+F32 = 0
+BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        lib.oracle_gemm_rs.argtypes = [i32] * 7 + [vp] * 4
+        lib.oracle_gemm_rs_points.argtypes = [i32] * 7 + [vp, vp, i64, vp, vp, vp, vp]
+        lib.oracle_gemv_ar.argtypes = [i32] * 7 + [vp] * 4
+        lib.oracle_ag_gemm.argtypes = [i32] * 6 + [vp] * 4
+        lib.oracle_ag_gemm_points.argtypes = [i32] * 6 + [vp, vp, i64, vp, vp, vp]
+        lib.oracle_embbag_a2a.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp]
+        for f in (lib.oracle_gemm_rs, lib.oracle_gemm_rs_points, lib.oracle_gemv_ar,
+                  lib.oracle_ag_gemm, lib.oracle_ag_gemm_points, lib.oracle_embbag_a2a):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _np_dt(dt):
+    return np.uint16 if dt == BF16 else np.float32
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _check(dt, *arrays):
+    for a in arrays:
+        assert a.dtype == _np_dt(dt), f"expected {_np_dt(dt)}, got {a.dtype}"
+
+
+def set_threads(n: int) -> None:
+    """Number of OpenMP threads the oracle uses (call before the first use)."""
+    os.environ["OMP_NUM_THREADS"] = str(int(n))
+
+
+def gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, A, W, want_slots=True):
+    """GEMM + ReduceScatter.  Returns (slots [P][P][Mc][N] or None, out [M][N])."""
+    _check(in_dt, A, W)
+    assert A.shape == (P, M, K) and W.shape == (P, K, N)
+    Mc = M // P
+    slots = np.empty((P, P, Mc, N), dtype=_np_dt(slot_dt)) if want_slots else None
+    out = np.empty((M, N), dtype=_np_dt(out_dt))
+    rc = _load().oracle_gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, _ptr(A), _ptr(W),
+                                _ptr(slots), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_rs rejected its arguments (rc={rc})")
+    return slots, out
+
+
+def gemm_rs_points(P, M, N, K, in_dt, slot_dt, out_dt, A, W, ms, ns):
+    """Sampled GEMM + ReduceScatter at (ms[i], ns[i]).  Returns (slot_vals [n][P], out_vals [n])."""
+    _check(in_dt, A, W)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    sv = np.empty((len(ms), P), dtype=_np_dt(slot_dt))
+    ov = np.empty(len(ms), dtype=_np_dt(out_dt))
+    rc = _load().oracle_gemm_rs_points(P, M, N, K, in_dt, slot_dt, out_dt, _ptr(A), _ptr(W),
+                                       len(ms), _ptr(ms), _ptr(ns), _ptr(sv), _ptr(ov))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_rs_points rejected its arguments (rc={rc})")
+    return sv, ov
+
+
+def gemv_ar(P, Mb, N, K, in_dt, slot_dt, out_dt, x, W):
+    """GEMV + AllReduce.  Returns (part [P][Mb][N], win [P][Mb][N])."""
+    _check(in_dt, x, W)
+    assert x.shape == (P, Mb, K) and W.shape == (P, K, N)
+    part = np.empty((P, Mb, N), dtype=_np_dt(slot_dt))
+    win = np.empty((P, Mb, N), dtype=_np_dt(out_dt))
+    rc = _load().oracle_gemv_ar(P, Mb, N, K, in_dt, slot_dt, out_dt, _ptr(x), _ptr(W),
+                                _ptr(part), _ptr(win))
+    if rc != 0:
+        raise ValueError(f"oracle_gemv_ar rejected its arguments (rc={rc})")
+    return part, win
+
+
+def _chunk_ptrs(chunks):
+    return (ctypes.c_void_p * len(chunks))(*[_ptr(c) for c in chunks])
+
+
+def ag_gemm(P, Mc, N, K, in_dt, out_dt, chunks, W):
+    """AllGather + GEMM.  chunks: list of P arrays [Mc][K] (rank c's chunk).
+    Returns (gathered [P*Mc][K], out [P*Mc][N])."""
+    assert len(chunks) == P
+    _check(in_dt, W, *chunks)
+    g = np.empty((P * Mc, K), dtype=_np_dt(in_dt))
+    out = np.empty((P * Mc, N), dtype=_np_dt(out_dt))
+    cp = _chunk_ptrs(chunks)
+    rc = _load().oracle_ag_gemm(P, Mc, N, K, in_dt, out_dt, cp, _ptr(W), _ptr(g), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_ag_gemm rejected its arguments (rc={rc})")
+    return g, out
+
+
+def ag_gemm_points(P, Mc, N, K, in_dt, out_dt, chunks, W, ms, ns):
+    assert len(chunks) == P
+    _check(in_dt, W, *chunks)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    ov = np.empty(len(ms), dtype=_np_dt(out_dt))
+    cp = _chunk_ptrs(chunks)
+    rc = _load().oracle_ag_gemm_points(P, Mc, N, K, in_dt, out_dt, cp, _ptr(W), len(ms),
+                                       _ptr(ms), _ptr(ns), _ptr(ov))
+    if rc != 0:
+        raise ValueError(f"oracle_ag_gemm_points rejected its arguments (rc={rc})")
+    return ov
+
+
+def embbag_a2a(T, R, D, B, L, P, tables, indices, offsets=None):
+    """Embedding bag + All-to-All.  Returns win [P][B/P][T][D] fp32.
+    Raises IndexError if an index lies outside [0, R)."""
+    assert tables.dtype == np.float32 and tables.shape == (T, R, D)
+    assert indices.dtype == np.int32
+    if offsets is not None:
+        assert offsets.dtype == np.int64 and offsets.shape == (T * B + 1,)
+    win = np.empty((P, B // P, T, D), dtype=np.float32)
+    rc = _load().oracle_embbag_a2a(T, R, D, B, L, P, _ptr(tables), _ptr(indices),
+                                   _ptr(offsets), _ptr(win))
+    if rc == -2:
+        raise IndexError("embedding index outside the table")
+    if rc != 0:
+        raise ValueError(f"oracle_embbag_a2a rejected its arguments (rc={rc})")
+    return win

@@ -1,0 +1,283 @@
+/*
+ * CPU oracle for the fused computation + collective-epilogue operators.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the tests, the smoke check and the bench's CPU
+ * baseline leg use it.  It shares no code with the HIP library (no headers,
+ * no helpers, no tables) and generates none of its own inputs: it consumes
+ * the exact bytes the GPU receives.
+ *
+ * What it computes.  "Optimizing Distributed ML Communication with Fused
+ * Computation-Collective Operations" (SC24, abstract) fuses a computation
+ * with the collective that follows it: workgroups send their results on as
+ * soon as they finish, while others still compute.  Fusion changes when the
+ * data moves, not what is computed, so the oracle is the unfused definition
+ * written out: the per-shard computation, then the textbook collective
+ * (ReduceScatter, AllReduce, AllGather, All-to-All).  The operator pairs are
+ * the ones those pages name: GEMM + ReduceScatter and AllGather + GEMM (the
+ * mKernel news item "GPU-vezérelt kommunikációval gyorsítják az
+ * AI-betanítást a kutatók", section on the five fused kernels), GEMV +
+ * AllReduce and embedding + All-to-All (SC24 abstract).
+ *
+ * Readings taken where the pages are silent:
+ *  - per-shard products are accumulated in fp64 with k ascending, then
+ *    rounded to fp32 (RNE), and from fp32 to bf16 (RNE) when the partial is
+ *    carried in bf16 -- the two-step rounding of an fp32 accumulator;
+ *  - partials are reduced by a left fold in fp32 in rank order
+ *    p = 0, 1, ..., P-1, starting from partial 0, then rounded once to the
+ *    output type;
+ *  - chunk r of a ReduceScatter is the contiguous row block
+ *    [r*Mc, (r+1)*Mc) of the full result; it goes to destination r; the slot
+ *    inside destination r is the source rank p;
+ *  - embedding bags are summed in fp32 in index order starting from +0.0;
+ *    an empty bag pools to zeros; bag b goes to destination b / (B/P), slot
+ *    b mod (B/P);
+ *  - an AllGather concatenates the chunks in rank order, whatever the order
+ *    in which they arrived.
+ *
+ * Data types: code 0 = fp32, code 1 = bf16 carried as uint16 bit patterns.
+ * Every function returns 0 on success, -1 on an invalid argument.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define DT_F32 0
+#define DT_BF16 1
+
+/* ---- element conversions (this file's own; IEEE-754 binary32 -> bfloat16) ---- */
+
+static float from_bf16(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round an fp32 value to bfloat16, nearest-even.  bfloat16 keeps the top 16
+ * bits of the binary32 pattern; the dropped 16 bits decide the rounding. */
+static uint16_t to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) /* NaN: keep it quiet */
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lower = u & 0xFFFFu;
+    uint32_t upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1u; /* carries into the exponent correctly, up to infinity */
+    return (uint16_t)upper;
+}
+
+static double load_in(const void* base, int dt, int64_t i) {
+    if (dt == DT_BF16) return (double)from_bf16(((const uint16_t*)base)[i]);
+    return (double)((const float*)base)[i];
+}
+
+/* Store a value that is already an fp32 number into a buffer of type dt. */
+static void store_f32_as(void* base, int dt, int64_t i, float v) {
+    if (dt == DT_BF16) ((uint16_t*)base)[i] = to_bf16(v);
+    else ((float*)base)[i] = v;
+}
+
+/* The partial C_p[m][n] as it is carried: fp64 sum -> fp32 -> (bf16). */
+static float carried(double s, int slot_dt) {
+    float f = (float)s; /* RNE */
+    if (slot_dt == DT_BF16) f = from_bf16(to_bf16(f));
+    return f;
+}
+
+static int dt_ok(int dt) { return dt == DT_F32 || dt == DT_BF16; }
+
+/* ---- GEMM + ReduceScatter ------------------------------------------------
+ * A [P][M][K], W [P][K][N] (row-major).  Shard p computes C_p = A_p . W_p
+ * (M x N).  The ReduceScatter hands chunk r (rows r*Mc .. r*Mc+Mc-1) of every
+ * C_p to destination r, which folds the P partials in rank order.
+ *   slots: [P dst r][P src p][Mc][N] of slot_dt (may be NULL): C_p chunk r
+ *   out:   [M][N] of out_dt == [P][Mc][N]: the reduced chunks in dest order
+ */
+int oracle_gemm_rs(int P, int M, int N, int K, int in_dt, int slot_dt, int out_dt,
+                   const void* A, const void* W, void* slots, void* out) {
+    if (P <= 0 || M < 0 || N < 0 || K < 0 || M % P != 0) return -1;
+    if (!dt_ok(in_dt) || !dt_ok(slot_dt) || !dt_ok(out_dt)) return -1;
+    const int64_t Mc = M / P;
+    /* carried partials C_p, fp32 values after the slot rounding: [P][M][N] */
+    float* C = (float*)malloc(sizeof(float) * (size_t)P * (size_t)M * (size_t)(N > 0 ? N : 1));
+    if (!C) return -1;
+
+    /* 1. per-shard GEMM, fp64, k ascending */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t pm = 0; pm < (int64_t)P * M; ++pm) {
+        const int64_t p = pm / M, m = pm % M;
+        double* acc = (double*)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = load_in(A, in_dt, (p * M + m) * K + k);
+            const int64_t wrow = (p * K + k) * N;
+            for (int64_t n = 0; n < N; ++n) acc[n] += a * load_in(W, in_dt, wrow + n);
+        }
+        for (int64_t n = 0; n < N; ++n) C[(p * M + m) * N + n] = carried(acc[n], slot_dt);
+        free(acc);
+    }
+
+    /* 2. scatter: chunk r of C_p -> destination r, slot p */
+    if (slots) {
+        for (int64_t r = 0; r < P; ++r)
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t i = 0; i < Mc; ++i)
+                    for (int64_t n = 0; n < N; ++n)
+                        store_f32_as(slots, slot_dt, ((r * P + p) * Mc + i) * N + n,
+                                     C[(p * M + r * Mc + i) * N + n]);
+    }
+
+    /* 3. each destination folds its P slots in rank order, in fp32 */
+    for (int64_t r = 0; r < P; ++r)
+        for (int64_t i = 0; i < Mc; ++i)
+            for (int64_t n = 0; n < N; ++n) {
+                const int64_t m = r * Mc + i;
+                float acc = C[(0 * M + m) * N + n];
+                for (int64_t p = 1; p < P; ++p) acc = acc + C[(p * M + m) * N + n];
+                store_f32_as(out, out_dt, m * N + n, acc);
+            }
+    free(C);
+    return 0;
+}
+
+/* Sampled GEMM + ReduceScatter: the same definition evaluated at npts output
+ * coordinates (m[i], n[i]) only.  slot_vals: [npts][P] of slot_dt (may be
+ * NULL) = C_p[m][n] as carried; out_vals: [npts] of out_dt. */
+int oracle_gemm_rs_points(int P, int M, int N, int K, int in_dt, int slot_dt, int out_dt,
+                          const void* A, const void* W, int64_t npts, const int64_t* ms,
+                          const int64_t* ns, void* slot_vals, void* out_vals) {
+    if (P <= 0 || M % P != 0 || !dt_ok(in_dt) || !dt_ok(slot_dt) || !dt_ok(out_dt)) return -1;
+    for (int64_t i = 0; i < npts; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < npts; ++i) {
+        const int64_t m = ms[i], n = ns[i];
+        float acc = 0.0f;
+        for (int64_t p = 0; p < P; ++p) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += load_in(A, in_dt, (p * M + m) * K + k) * load_in(W, in_dt, (p * K + k) * N + n);
+            const float c = carried(s, slot_dt);
+            if (slot_vals) store_f32_as(slot_vals, slot_dt, i * P + p, c);
+            acc = (p == 0) ? c : acc + c;
+        }
+        store_f32_as(out_vals, out_dt, i, acc);
+    }
+    return 0;
+}
+
+/* ---- GEMV + AllReduce -----------------------------------------------------
+ * x [P][Mb][K], W [P][K][N].  Shard p computes y_p = x_p . W_p (Mb x N),
+ * carried in slot_dt; the AllReduce folds y_0..y_{P-1} in rank order in fp32,
+ * rounds once to out_dt and leaves the same result in every one of the P
+ * receive windows.
+ *   part: [P][Mb][N] of slot_dt (may be NULL); win: [P][Mb][N] of out_dt */
+int oracle_gemv_ar(int P, int Mb, int N, int K, int in_dt, int slot_dt, int out_dt,
+                   const void* x, const void* W, void* part, void* win) {
+    if (P <= 0 || Mb < 0 || N < 0 || K < 0) return -1;
+    if (!dt_ok(in_dt) || !dt_ok(slot_dt) || !dt_ok(out_dt)) return -1;
+    float* Y = (float*)malloc(sizeof(float) * (size_t)P * (size_t)(Mb > 0 ? Mb : 1) * (size_t)(N > 0 ? N : 1));
+    if (!Y) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t pb = 0; pb < (int64_t)P * Mb; ++pb) {
+        const int64_t p = pb / Mb, b = pb % Mb;
+        double* acc = (double*)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = load_in(x, in_dt, (p * Mb + b) * K + k);
+            const int64_t wrow = (p * K + k) * N;
+            for (int64_t n = 0; n < N; ++n) acc[n] += a * load_in(W, in_dt, wrow + n);
+        }
+        for (int64_t n = 0; n < N; ++n) Y[(p * Mb + b) * N + n] = carried(acc[n], slot_dt);
+        free(acc);
+    }
+    if (part)
+        for (int64_t i = 0; i < (int64_t)P * Mb * N; ++i) store_f32_as(part, slot_dt, i, Y[i]);
+    for (int64_t b = 0; b < Mb; ++b)
+        for (int64_t n = 0; n < N; ++n) {
+            float acc = Y[(0 * Mb + b) * N + n];
+            for (int64_t p = 1; p < P; ++p) acc = acc + Y[(p * Mb + b) * N + n];
+            for (int64_t q = 0; q < P; ++q) store_f32_as(win, out_dt, (q * Mb + b) * N + n, acc);
+        }
+    free(Y);
+    return 0;
+}
+
+/* ---- AllGather + GEMM -----------------------------------------------------
+ * chunks: P pointers, chunk c = [Mc][K] held by rank c; W [K][N].
+ * The AllGather builds A_g = [chunk 0; chunk 1; ...; chunk P-1] (rank order);
+ * then out = A_g . W, fp64 accumulation, rounded to fp32 then to out_dt.
+ *   gathered: [P*Mc][K] of in_dt (may be NULL); out: [P*Mc][N] of out_dt */
+int oracle_ag_gemm(int P, int Mc, int N, int K, int in_dt, int out_dt,
+                   const void* const* chunks, const void* W, void* gathered, void* out) {
+    if (P <= 0 || Mc < 0 || N < 0 || K < 0 || !dt_ok(in_dt) || !dt_ok(out_dt)) return -1;
+    const size_t esz = in_dt == DT_BF16 ? 2 : 4;
+    const int64_t M = (int64_t)P * Mc;
+    char* Ag = (char*)malloc(esz * (size_t)(M > 0 ? M : 1) * (size_t)(K > 0 ? K : 1));
+    if (!Ag) return -1;
+    for (int64_t c = 0; c < P; ++c) /* rank order */
+        memcpy(Ag + (size_t)c * Mc * K * esz, chunks[c], (size_t)Mc * K * esz);
+    if (gathered) memcpy(gathered, Ag, (size_t)M * K * esz);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        double* acc = (double*)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = load_in(Ag, in_dt, m * K + k);
+            for (int64_t n = 0; n < N; ++n) acc[n] += a * load_in(W, in_dt, k * N + n);
+        }
+        for (int64_t n = 0; n < N; ++n) store_f32_as(out, out_dt, m * N + n, (float)acc[n]);
+        free(acc);
+    }
+    free(Ag);
+    return 0;
+}
+
+/* Sampled AllGather + GEMM at output coordinates (ms[i], ns[i]). */
+int oracle_ag_gemm_points(int P, int Mc, int N, int K, int in_dt, int out_dt,
+                          const void* const* chunks, const void* W, int64_t npts,
+                          const int64_t* ms, const int64_t* ns, void* out_vals) {
+    if (P <= 0 || Mc <= 0 || !dt_ok(in_dt) || !dt_ok(out_dt)) return -1;
+    for (int64_t i = 0; i < npts; ++i)
+        if (ms[i] < 0 || ms[i] >= (int64_t)P * Mc || ns[i] < 0 || ns[i] >= N) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < npts; ++i) {
+        const int64_t c = ms[i] / Mc, row = ms[i] % Mc, n = ns[i];
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += load_in(chunks[c], in_dt, row * K + k) * load_in(W, in_dt, k * N + n);
+        store_f32_as(out_vals, out_dt, i, (float)s);
+    }
+    return 0;
+}
+
+/* ---- embedding bag + All-to-All ------------------------------------------
+ * tables [T][R][D] fp32; indices: fixed-length bags [T][B][L] (offsets NULL)
+ * or CSR bags (offsets [T*B+1], bag (t,b) = indices[offsets[t*B+b] ..
+ * offsets[t*B+b+1]) ).  pooled(t,b) = sum of the bag's rows, fp32, in index
+ * order from +0.0.  The All-to-All sends bag b to destination d = b / Bd
+ * (Bd = B/P), slot b mod Bd:
+ *   win: [P][Bd][T][D] fp32, win[d][b mod Bd][t][:] = pooled(t, b).
+ * An index outside [0, R) makes the call fail (-2) and leaves win unspecified. */
+int oracle_embbag_a2a(int T, int64_t R, int D, int B, int L, int P, const float* tables,
+                      const int32_t* indices, const int64_t* offsets, float* win) {
+    if (T < 0 || R < 0 || D < 0 || B < 0 || P <= 0 || B % P != 0) return -1;
+    if (!offsets && L < 0) return -1;
+    const int64_t Bd = B / P;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+    for (int64_t tb = 0; tb < (int64_t)T * B; ++tb) {
+        const int64_t t = tb / B, b = tb % B;
+        const int64_t lo = offsets ? offsets[tb] : tb * (int64_t)L;
+        const int64_t hi = offsets ? offsets[tb + 1] : lo + L;
+        float* dst = win + (((b / Bd) * Bd + (b % Bd)) * T + t) * (int64_t)D;
+        for (int64_t d = 0; d < D; ++d) dst[d] = 0.0f;
+        for (int64_t j = lo; j < hi; ++j) {
+            const int64_t row = indices[j];
+            if (row < 0 || row >= R) { bad = 1; continue; }
+            const float* src = tables + (t * R + row) * (int64_t)D;
+            for (int64_t d = 0; d < D; ++d) dst[d] = dst[d] + src[d];
+        }
+    }
+    return bad ? -2 : 0;
+}

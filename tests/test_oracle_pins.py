@@ -1,0 +1,406 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test ties the oracle to something it does not share code with: values
+worked by hand from the operators' definitions (tests/golden/, each file
+citing its passage), an exact rational brute force with its own IEEE-754
+rounding (tests/exact_ref.py), numpy/torch library routines on special cases
+that reduce to them, integer-valued inputs where every result is exact, and
+the structural invariants of the collectives (every chunk lands in exactly
+one slot, all AllReduce windows identical, the AllGather is the rank-order
+concatenation, every bag lands in exactly one bucket).  The cases are chosen
+so that a dropped term, a sign or index slip, a transposed operand, a wrong
+chunk or bucket mapping, or a different reduction order fails one of them.
+"""
+
+import glob
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_ref as ex
+from computation_collective_amd import inputs as gen
+
+F32, BF16 = 0, 1
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _arr(v, dt):
+    a = np.asarray(v, dtype=np.float32)
+    return gen.bf16_encode(a) if dt == BF16 else np.ascontiguousarray(a)
+
+
+def _val(a, dt):
+    """Oracle output -> float64 values."""
+    return (gen.bf16_decode(a) if dt == BF16 else a).astype(np.float64)
+
+
+def _fr_list(a):
+    return np.asarray([float(x) for x in np.asarray(a, dtype=object).ravel()], dtype=np.float64)
+
+
+def _golden(op):
+    out = []
+    for f in sorted(glob.glob(os.path.join(GOLD, f"{op}_*.json"))):
+        with open(f) as fh:
+            out.append(pytest.param(json.load(fh), id=os.path.basename(f)))
+    return out
+
+
+# ------------------------------------------------------------------ golden fixtures
+
+@pytest.mark.parametrize("g", _golden("gemm_rs"))
+def test_gemm_rs_golden(g):
+    A, W = _arr(g["A"], g["in_dt"]), _arr(g["W"], g["in_dt"])
+    slots, out = oracle.gemm_rs(g["P"], g["M"], g["N"], g["K"], g["in_dt"], g["slot_dt"],
+                                g["out_dt"], A, W)
+    np.testing.assert_array_equal(_val(out, g["out_dt"]), np.asarray(g["out"], dtype=np.float64))
+    if "slots" in g:
+        np.testing.assert_array_equal(_val(slots, g["slot_dt"]),
+                                      np.asarray(g["slots"], dtype=np.float64))
+
+
+@pytest.mark.parametrize("g", _golden("gemv_ar"))
+def test_gemv_ar_golden(g):
+    x, W = _arr(g["x"], g["in_dt"]), _arr(g["W"], g["in_dt"])
+    part, win = oracle.gemv_ar(g["P"], g["Mb"], g["N"], g["K"], g["in_dt"], g["slot_dt"],
+                               g["out_dt"], x, W)
+    np.testing.assert_array_equal(_val(part, g["slot_dt"]), np.asarray(g["part"], dtype=np.float64))
+    np.testing.assert_array_equal(_val(win, g["out_dt"]), np.asarray(g["win"], dtype=np.float64))
+
+
+@pytest.mark.parametrize("g", _golden("ag_gemm"))
+def test_ag_gemm_golden(g):
+    chunks = [_arr(c, g["in_dt"]) for c in g["chunks"]]
+    W = _arr(g["W"], g["in_dt"])
+    gathered, out = oracle.ag_gemm(g["P"], g["Mc"], g["N"], g["K"], g["in_dt"], g["out_dt"],
+                                   chunks, W)
+    np.testing.assert_array_equal(_val(gathered, g["in_dt"]), np.asarray(g["gathered"], np.float64))
+    np.testing.assert_array_equal(_val(out, g["out_dt"]), np.asarray(g["out"], np.float64))
+
+
+@pytest.mark.parametrize("g", _golden("embbag_a2a"))
+def test_embbag_golden(g):
+    tables = np.asarray(g["tables"], dtype=np.float32)
+    idx = np.asarray(g["indices"], dtype=np.int32)
+    off = np.asarray(g["offsets"], dtype=np.int64) if "offsets" in g else None
+    win = oracle.embbag_a2a(g["T"], g["R"], g["D"], g["B"], g["L"], g["P"], tables,
+                            np.ascontiguousarray(idx.ravel()), off)
+    np.testing.assert_array_equal(win, np.asarray(g["win"], dtype=np.float32))
+
+
+# ------------------------------------------------------------------ exact brute force
+
+def _exact_check(got, want_fr, dt, ulps=0):
+    got = _val(got, dt).ravel()
+    want = _fr_list(want_fr)
+    if ulps == 0:
+        np.testing.assert_array_equal(got, want)
+    else:
+        sp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - want) <= ulps * sp + 0.0), (got, want)
+
+
+CASES = [(P, M1, N, K) for P in (1, 2, 3) for (M1, N, K) in ((1, 1, 1), (2, 3, 4), (3, 2, 3), (1, 4, 2))]
+
+
+@pytest.mark.parametrize("P,Mc,N,K", CASES)
+@pytest.mark.parametrize("in_dt,slot_dt,out_dt", [(F32, F32, F32), (BF16, F32, BF16),
+                                                  (BF16, BF16, BF16), (BF16, BF16, F32)])
+def test_gemm_rs_bruteforce(P, Mc, N, K, in_dt, slot_dt, out_dt):
+    M = P * Mc
+    seed = 1000 * P + 100 * Mc + 10 * N + K + 7 * in_dt
+    A, W = gen.gemm_rs_inputs(P, M, N, K, in_dt, seed=seed)
+    slots, out = oracle.gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, A, W)
+    Av, Wv = _val(A, in_dt), _val(W, in_dt)
+    es, eo = ex.gemm_rs(P, M, N, K, Av.tolist(), Wv.tolist(),
+                        ex.BF16 if slot_dt == BF16 else ex.FP32,
+                        ex.BF16 if out_dt == BF16 else ex.FP32)
+    # bf16 inputs: every dot product is exact in fp64, so the oracle is bit-exact;
+    # fp32 inputs: the fp64 sum may round once before the fp32 rounding (<= 1 ulp)
+    ulps = 0 if in_dt == BF16 else 1
+    _exact_check(slots, es, slot_dt, ulps)
+    if ulps == 0:
+        _exact_check(out, eo, out_dt)
+    else:
+        # the fold itself is exact given the oracle's own partials
+        sv = _val(slots, slot_dt)               # [r][p][i][n]
+        want = []
+        for r in range(P):
+            for i in range(Mc):
+                for n in range(N):
+                    acc = ex.fr(sv[r, 0, i, n])
+                    for p in range(1, P):
+                        acc = ex.round_to(acc + ex.fr(sv[r, p, i, n]), ex.FP32)
+                    want.append(ex.round_to(acc, ex.BF16) if out_dt == BF16 else acc)
+        _exact_check(out, want, out_dt)
+
+
+def test_gemm_rs_dyadic_exact():
+    """fp32 inputs on a 2^-6 grid: every product and sum is exact, so bit-exact."""
+    P, Mc, N, K = 3, 2, 3, 4
+    rng = np.random.default_rng(5)
+    A = (rng.integers(-64, 65, size=(P, P * Mc, K)) / 64.0).astype(np.float32)
+    W = (rng.integers(-64, 65, size=(P, K, N)) / 64.0).astype(np.float32)
+    slots, out = oracle.gemm_rs(P, P * Mc, N, K, F32, F32, F32, A, W)
+    es, eo = ex.gemm_rs(P, P * Mc, N, K, A.tolist(), W.tolist(), ex.FP32, ex.FP32)
+    _exact_check(slots, es, F32)
+    _exact_check(out, eo, F32)
+
+
+@pytest.mark.parametrize("P,Mb,N,K", [(1, 1, 2, 3), (2, 2, 3, 4), (3, 1, 4, 2)])
+@pytest.mark.parametrize("slot_dt,out_dt", [(F32, BF16), (BF16, BF16), (F32, F32)])
+def test_gemv_ar_bruteforce(P, Mb, N, K, slot_dt, out_dt):
+    x, W = gen.gemv_ar_inputs(P, Mb, N, K, BF16, seed=17 * P + N)
+    part, win = oracle.gemv_ar(P, Mb, N, K, BF16, slot_dt, out_dt, x, W)
+    ep, ew = ex.gemv_ar(P, Mb, N, K, _val(x, BF16).tolist(), _val(W, BF16).tolist(),
+                        ex.BF16 if slot_dt == BF16 else ex.FP32, ex.BF16 if out_dt == BF16 else ex.FP32)
+    _exact_check(part, ep, slot_dt)
+    _exact_check(win, ew, out_dt)
+
+
+@pytest.mark.parametrize("P,Mc,N,K", [(1, 2, 2, 3), (2, 1, 3, 4), (3, 2, 2, 2)])
+@pytest.mark.parametrize("out_dt", [BF16, F32])
+def test_ag_gemm_bruteforce(P, Mc, N, K, out_dt):
+    chunks, W, order = gen.ag_gemm_inputs(P, Mc, N, K, BF16, seed=31 * P + K)
+    g, out = oracle.ag_gemm(P, Mc, N, K, BF16, out_dt, list(chunks), W)
+    eg, eo = ex.ag_gemm(P, Mc, N, K, _val(chunks, BF16).tolist(), _val(W, BF16).tolist(),
+                        ex.BF16 if out_dt == BF16 else ex.FP32)
+    np.testing.assert_array_equal(_val(g, BF16), np.asarray(eg, dtype=np.float64))
+    _exact_check(out, eo, out_dt)
+
+
+@pytest.mark.parametrize("T,R,D,B,L,P", [(1, 3, 2, 2, 1, 1), (2, 5, 3, 4, 3, 2), (3, 4, 4, 6, 2, 3)])
+def test_embbag_bruteforce(T, R, D, B, L, P):
+    tables = gen.embbag_tables(T, R, D, std=1.0, seed=T + R)
+    idx = gen.uniform_indices(T, B, L, R, seed=B)
+    win = oracle.embbag_a2a(T, R, D, B, L, P, tables, idx)
+    bags = [[list(idx[t, b]) for b in range(B)] for t in range(T)]
+    ew = ex.embbag_a2a(T, R, D, B, P, tables.tolist(), bags)
+    np.testing.assert_array_equal(win.astype(np.float64), np.asarray(
+        [[[[float(v) for v in ew[d][s][t]] for t in range(T)] for s in range(B // P)] for d in range(P)]))
+
+
+def test_embbag_bruteforce_csr():
+    T, R, D, B, P = 2, 6, 3, 6, 3
+    tables = gen.embbag_tables(T, R, D, std=1.0, seed=3)
+    off = gen.csr_bag_offsets(T, B, 4, seed=4, empty_frac=0.3)
+    rng = np.random.default_rng(9)
+    idx = rng.integers(0, R, size=int(off[-1]), dtype=np.int32)
+    win = oracle.embbag_a2a(T, R, D, B, 0, P, tables, idx, off)
+    bags = [[list(idx[off[t * B + b]:off[t * B + b + 1]]) for b in range(B)] for t in range(T)]
+    assert any(len(bags[t][b]) == 0 for t in range(T) for b in range(B))
+    ew = ex.embbag_a2a(T, R, D, B, P, tables.tolist(), bags)
+    np.testing.assert_array_equal(win.astype(np.float64), np.asarray(
+        [[[[float(v) for v in ew[d][s][t]] for t in range(T)] for s in range(B // P)] for d in range(P)]))
+
+
+# ------------------------------------------------------------------ closed forms (library routines)
+
+def _normwise(got, want):
+    return np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-300)
+
+
+@pytest.mark.parametrize("in_dt,slot_dt,out_dt,tol", [(F32, F32, F32, 2e-6), (BF16, F32, BF16, 8e-3),
+                                                      (BF16, BF16, BF16, 1.6e-2)])
+def test_gemm_rs_closed_form(in_dt, slot_dt, out_dt, tol):
+    """vcat_r(out_r) = round(hcat_p(A_p) . vcat_p(W_p)) (numpy fp64 matmul); also the
+    sum-of-chunks invariant: the concatenated destination chunks equal the full product."""
+    P, M, N, K = 4, 64, 48, 40
+    A, W = gen.gemm_rs_inputs(P, M, N, K, in_dt, seed=3)
+    _, out = oracle.gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, A, W)
+    Av, Wv = _val(A, in_dt), _val(W, in_dt)
+    full = np.concatenate(list(Av), axis=1) @ np.concatenate(list(Wv), axis=0)
+    assert _normwise(_val(out, out_dt), full) < tol
+
+
+def test_gemm_rs_slots_are_shard_products():
+    """Every row of every C_p lands in exactly one slot: slot[r][p][i] = C_p[r*Mc+i]."""
+    P, M, N, K = 3, 12, 5, 6
+    A, W = gen.gemm_rs_inputs(P, M, N, K, BF16, seed=8)
+    slots, _ = oracle.gemm_rs(P, M, N, K, BF16, F32, BF16, A, W)
+    Av, Wv = _val(A, BF16), _val(W, BF16)
+    Mc = M // P
+    for p in range(P):
+        Cp = (Av[p] @ Wv[p]).astype(np.float32)   # exact in fp64 for bf16 inputs at this K
+        for r in range(P):
+            np.testing.assert_array_equal(slots[r, p], Cp[r * Mc:(r + 1) * Mc])
+
+
+@pytest.mark.parametrize("slot_dt,out_dt", [(F32, F32), (F32, BF16), (BF16, BF16)])
+def test_gemm_rs_integer_inputs_exact(slot_dt, out_dt):
+    """Entries in {-2..2}: every partial and every fold is an exact integer, so the
+    result is the int64 matmul, rounded once (bf16 rounding by torch's RNE)."""
+    P, M, N, K = 4, 32, 24, 80
+    A, W = gen.gemm_rs_inputs(P, M, N, K, BF16, seed=2, dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    _, out = oracle.gemm_rs(P, M, N, K, BF16, slot_dt, out_dt, A, W)
+    Ai, Wi = _val(A, BF16).astype(np.int64), _val(W, BF16).astype(np.int64)
+    exact = sum(Ai[p] @ Wi[p] for p in range(P))
+    want = torch.from_numpy(exact.astype(np.float32))
+    if out_dt == BF16:
+        want = want.to(torch.bfloat16).float()
+    np.testing.assert_array_equal(_val(out, out_dt), want.double().numpy())
+
+
+def test_gemm_rs_p1_is_plain_gemm():
+    M, N, K = 16, 12, 20
+    A, W = gen.gemm_rs_inputs(1, M, N, K, F32, seed=4, dist_a=("int", -3, 3), dist_w=("int", -3, 3))
+    _, out = oracle.gemm_rs(1, M, N, K, F32, F32, F32, A, W)
+    np.testing.assert_array_equal(out, (A[0].astype(np.float64) @ W[0]).astype(np.float32))
+
+
+def test_gemm_rs_all_ones():
+    P, M, N, K = 4, 8, 8, 33
+    A = np.ones((P, M, K), np.float32)
+    W = np.ones((P, K, N), np.float32)
+    _, out = oracle.gemm_rs(P, M, N, K, F32, F32, F32, A, W)
+    assert np.all(out == P * K)
+
+
+def test_bf16_rounding_matches_torch():
+    """The oracle's fp32->bf16 rounding (a bf16 slot carried through a 1-term fold)
+    equals torch's round-to-nearest-even conversion, ties of both parities included."""
+    rng = np.random.default_rng(11)
+    base = rng.standard_normal(4000).astype(np.float32)
+    u = base.view(np.uint32)
+    ties = ((u & 0xFFFF0000) | 0x8000).view(np.float32)          # exact midpoints
+    near = ((u & 0xFFFF0000) | 0x7FFF).view(np.float32)
+    vals = np.concatenate([base, ties, near, np.float32([3.3895314e38, -1.1754944e-38, 1e-40])])
+    M = len(vals)
+    A = np.ascontiguousarray(vals.reshape(1, M, 1))
+    W = np.ones((1, 1, 1), np.float32)
+    slots, out = oracle.gemm_rs(1, M, 1, 1, F32, BF16, F32, A, W)
+    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(slots.reshape(-1), want)
+
+
+@pytest.mark.parametrize("slot_dt,out_dt", [(F32, BF16), (BF16, BF16)])
+def test_gemv_ar_closed_form_and_replicas(slot_dt, out_dt):
+    P, Mb, N, K = 8, 4, 96, 128
+    x, W = gen.gemv_ar_inputs(P, Mb, N, K, seed=6)
+    part, win = oracle.gemv_ar(P, Mb, N, K, BF16, slot_dt, out_dt, x, W)
+    for q in range(1, P):                       # every window holds the same bits
+        np.testing.assert_array_equal(win[q], win[0])
+    xv, Wv = _val(x, BF16), _val(W, BF16)
+    full = np.concatenate(list(xv), axis=1) @ np.concatenate(list(Wv), axis=0)
+    assert _normwise(_val(win[0], out_dt), full) < 1.6e-2
+    for p in range(P):                          # partials are the shard products
+        assert _normwise(_val(part[p], slot_dt), xv[p] @ Wv[p]) < 8e-3
+
+
+def test_gemv_ar_integer_exact():
+    P, Mb, N, K = 8, 4, 40, 64
+    x, W = gen.gemv_ar_inputs(P, Mb, N, K, seed=1, dist_x=("int", -2, 2), dist_w=("int", -2, 2))
+    _, win = oracle.gemv_ar(P, Mb, N, K, BF16, F32, F32, x, W)
+    xi, Wi = _val(x, BF16).astype(np.int64), _val(W, BF16).astype(np.int64)
+    exact = sum(xi[p] @ Wi[p] for p in range(P))
+    for q in range(P):
+        np.testing.assert_array_equal(win[q], exact.astype(np.float32))
+
+
+def test_ag_gemm_gather_is_rank_order_and_closed_form():
+    P, Mc, N, K = 4, 8, 24, 32
+    chunks, W, order = gen.ag_gemm_inputs(P, Mc, N, K, seed=12)
+    g, out = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
+    np.testing.assert_array_equal(g, np.concatenate(list(chunks), axis=0))
+    full = _val(g, BF16) @ _val(W, BF16)
+    # out = bf16(fp32(exact)): within half a bf16 ulp elementwise
+    assert np.all(np.abs(_val(out, BF16) - full) <= np.abs(full) * 2.0 ** -8 + 1e-30)
+
+
+def test_points_match_full():
+    P, M, N, K = 4, 32, 20, 24
+    A, W = gen.gemm_rs_inputs(P, M, N, K, BF16, seed=21)
+    slots, out = oracle.gemm_rs(P, M, N, K, BF16, F32, BF16, A, W)
+    ms = np.array([0, 5, 31, 17, 8]); ns = np.array([0, 19, 3, 10, 11])
+    sv, ov = oracle.gemm_rs_points(P, M, N, K, BF16, F32, BF16, A, W, ms, ns)
+    np.testing.assert_array_equal(ov, out[ms, ns])
+    Mc = M // P
+    for j in range(len(ms)):
+        r, i = ms[j] // Mc, ms[j] % Mc
+        np.testing.assert_array_equal(sv[j], slots[r, :, i, ns[j]])
+    chunks, Wg, _ = gen.ag_gemm_inputs(P, 8, N, K, seed=22)
+    _, aout = oracle.ag_gemm(P, 8, N, K, BF16, BF16, list(chunks), Wg)
+    av = oracle.ag_gemm_points(P, 8, N, K, BF16, BF16, list(chunks), Wg, ms, ns)
+    np.testing.assert_array_equal(av, aout[ms, ns])
+
+
+# ------------------------------------------------------------------ embedding structure
+
+def test_embbag_tagged_routing():
+    """Tagged rows pool to exact integers: (sum of low bits, sum of high bits,
+    table id * L, L).  Any wrong bucket, slot, table or index shows up exactly;
+    every (bag, table) pair is written exactly once (NaN-free window)."""
+    T, R, D, B, L, P = 5, 20000, 8, 64, 7, 4
+    tables = gen.tagged_tables(T, R, D)
+    idx = gen.zipf_indices(T, B, L, R, seed=3)
+    win = oracle.embbag_a2a(T, R, D, B, L, P, tables, idx)
+    assert not np.isnan(win).any()
+    Bd = B // P
+    for t in range(T):
+        for b in range(B):
+            v = win[b // Bd, b % Bd, t]
+            rows = idx[t, b].astype(np.int64)
+            assert v[0] == np.sum(rows & 0xFFF) and v[1] == np.sum(rows >> 12)
+            assert v[2] == t * L and v[3] == L and np.all(v[4:] == 0)
+
+
+def test_embbag_l1_is_gather_and_constant_index():
+    T, R, D, B, P = 3, 50, 6, 8, 2
+    tables = gen.embbag_tables(T, R, D, std=1.0, seed=1)
+    idx = gen.uniform_indices(T, B, 1, R, seed=2)
+    win = oracle.embbag_a2a(T, R, D, B, 1, P, tables, idx)
+    Bd = B // P
+    for t in range(T):
+        for b in range(B):
+            np.testing.assert_array_equal(win[b // Bd, b % Bd, t], tables[t, idx[t, b, 0]])
+    # constant index, dyadic rows: L additions of the same row are exact = L * row
+    L = 9
+    dy = (np.random.default_rng(3).integers(-512, 512, size=(T, R, D)) / 256.0).astype(np.float32)
+    cidx = np.full((T, B, L), 7, dtype=np.int32)
+    win = oracle.embbag_a2a(T, R, D, B, L, P, dy, cidx)
+    for t in range(T):
+        np.testing.assert_array_equal(win[:, :, t].reshape(B, D), np.tile(L * dy[t, 7], (B, 1)))
+
+
+def test_embbag_empty_and_bad_index():
+    T, R, D, B, P = 1, 4, 4, 2, 1
+    tables = gen.embbag_tables(T, R, D, std=1.0, seed=1)
+    win = oracle.embbag_a2a(T, R, D, B, 0, P, tables, np.zeros(0, np.int32))
+    assert np.all(win == 0) and not np.signbit(win).any()
+    with pytest.raises(IndexError):
+        oracle.embbag_a2a(T, R, D, B, 1, P, tables, np.array([0, 4], np.int32))
+
+
+# ------------------------------------------------------------------ input generators
+
+def test_generator_bf16_encode_matches_torch():
+    v = np.random.default_rng(0).standard_normal(100000).astype(np.float32)
+    got = gen.bf16_encode(v)
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(gen.bf16_decode(got), torch.from_numpy(v).to(torch.bfloat16).float().numpy())
+
+
+def test_generator_zipf_law():
+    R, alpha = 1_000_000, 1.05
+    idx = gen.zipf_indices(4, 4096, 20, R, alpha=alpha, seed=0)
+    assert idx.min() >= 0 and idx.max() < R
+    H = np.sum(np.arange(1, R + 1, dtype=np.float64) ** -alpha)
+    n = idx[0].size
+    for k in (1, 2, 10):
+        p = k ** -alpha / H
+        f = np.mean(idx[0] == k - 1)
+        assert abs(f - p) < 5 * np.sqrt(p * (1 - p) / n), (k, f, p)
+    # tables draw independent streams
+    assert not np.array_equal(idx[0], idx[1])
+
+
+def test_generator_seeded():
+    a1, w1 = gen.gemm_rs_inputs(2, 4, 4, 4, BF16, seed=0)
+    a2, w2 = gen.gemm_rs_inputs(2, 4, 4, 4, BF16, seed=0)
+    np.testing.assert_array_equal(a1, a2)
+    np.testing.assert_array_equal(w1, w2)
