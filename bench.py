@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Bench of the fused computation + collective-epilogue hot path on one MI355X.
+
+One step = one pass of the whole hot path: one call of each fused operator
+at its workload size, on one HIP stream, inputs already resident in HBM:
+
+  gemm_rs     GEMM+ReduceScatter, P=8, A_p 8192x1792, W_p 1792x4096 bf16, tile 256x256
+  gemv_ar     GEMV+AllReduce, P=8, x_p 4x1024, W_p 1024x8192 bf16 (4 weight replicas rotate)
+  ag_gemm     AllGather+GEMM, 8 chunks 1024x4096, W 4096x1792 bf16, chunks released in a
+              seeded random order by the command processor of a second stream
+  embbag_a2a  64 tables 1e6x128 fp32, batch 16384, 20 rows per bag, Zipf(1.05), P=8
+
+`value` is the GEMM+ReduceScatter throughput (TFLOP/s, the headline kernel);
+each operator's own throughput and roofline fraction are in `ops`.  Each
+kernel's time comes from HIP events recorded on the stream it runs on.
+
+  python bench.py [--steps K] [--warmup W] [--slot-dtype f32|bf16] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused GEMM+ReduceScatter TFLOP/s & GEMV/embbag GB/s, % roofline, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
+    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    return ap.parse_args()
+
+
+def median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def cpu_baseline(target_s):
+    """The oracle (unchanged) on the host cores, on a bounded sample of the
+    GEMM+ReduceScatter workload: the first rows of every destination chunk
+    (an exact sub-problem: same P, N, K and chunk structure)."""
+    import numpy as np
+
+    cores = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16") or 16), 16)
+    os.environ["OMP_NUM_THREADS"] = str(cores)
+    import oracle
+    from computation_collective_amd import configs as cfgs
+    from computation_collective_amd import inputs as gen
+
+    c = cfgs.GEMM_RS_MLP
+    Mc = c.M // c.P
+
+    A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, c.in_dt, seed=0)
+
+    def run(rows_per_chunk):
+        sel = np.concatenate([np.arange(r * Mc, r * Mc + rows_per_chunk) for r in range(c.P)])
+        As = np.ascontiguousarray(A[:, sel, :])
+        Ms = c.P * rows_per_chunk
+        t0 = time.perf_counter()
+        oracle.gemm_rs(c.P, Ms, c.N, c.K, c.in_dt, c.slot_dt, c.out_dt, As, W, want_slots=False)
+        dt = time.perf_counter() - t0
+        return dt, 2.0 * c.P * Ms * c.N * c.K
+
+    dt, fl = run(1)
+    rows = max(1, min(Mc, int(target_s / max(dt, 1e-3))))
+    dt, fl = run(rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{rows} rows of each of the {c.P} destination chunks ({c.P * rows} of {c.M} "
+                      f"output rows) of gemm_rs P={c.P} {c.M}x{c.N}x{c.K} bf16, fp32 partials"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from computation_collective_amd import buffers as bf
+    from computation_collective_amd import configs as cfgs
+    from computation_collective_amd import hocf
+    from computation_collective_amd import inputs as gen
+
+    if not os.path.exists(hocf.LIB_PATH):
+        from computation_collective_amd import build as hip_build
+        hip_build.build()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    rel_stream = torch.cuda.Stream()
+    ops = [o for o in args.ops.split(",") if o]
+    sdt = bf.F32 if args.slot_dtype == "f32" else bf.BF16
+    runs = {}
+
+    if "gemm_rs" in ops:
+        c = cfgs.GEMM_RS_MLP
+        log(f"inputs {c.name}")
+        A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, c.in_dt, seed=0)
+        r = bf.GemmRS(c.P, c.M, c.N, c.K, c.in_dt, sdt, c.out_dt, c.tile_m, c.tile_n, A, W)
+        del A, W
+        flops = c.flops
+        algo_bytes = (2 * (c.P * c.M * c.K + c.P * c.K * c.N)            # A, W read
+                      + 2 * (4 if sdt == bf.F32 else 2) * c.P * c.M * c.N  # slots written + read
+                      + 2 * c.M * c.N)                                     # out written
+        runs["gemm_rs"] = dict(call=lambda r=r: r.run(stream), obj=r, work=flops, unit="TFLOP/s",
+                               bound="mfma", peak=PEAK_BF16_TFLOPS, bytes=algo_bytes,
+                               config=dict(workload=c.name, P=c.P, M=c.M, N=c.N, K=c.K,
+                                           tile=[c.tile_m, c.tile_n], slot_dtype=args.slot_dtype))
+    if "gemv_ar" in ops:
+        c = cfgs.GEMV_AR_DECODE
+        log(f"inputs {c.name}")
+        x, W = gen.gemv_ar_inputs(c.P, c.Mb, c.N, c.K, seed=0)
+        g = bf.GemvAR(c.P, c.Mb, c.N, c.K, c.in_dt, c.slot_dt, c.out_dt, c.tile_n, x, W)
+        # 4 replicas of the weights (537 MB > the 256 MB Infinity Cache) rotate per call
+        reps = [(g.x, g.W)] + [(g.x.clone(), g.W.clone()) for _ in range(3)]
+        state = {"i": 0}
+
+        def gemv_call(g=g, reps=reps, state=state):
+            xr, Wr = reps[state["i"] % len(reps)]
+            state["i"] += 1
+            g.set_weights(xr, Wr)
+            g.run(stream)
+
+        algo_bytes = (2 * c.P * c.K * c.N + 2 * c.P * c.Mb * c.K          # W, x read
+                      + 2 * 4 * c.P * c.Mb * c.N                          # partials written + read
+                      + 2 * c.P * c.Mb * c.N)                             # P windows written
+        runs["gemv_ar"] = dict(call=gemv_call, obj=g, work=algo_bytes, unit="GB/s", bound="hbm",
+                               peak=PEAK_HBM_GBS, bytes=algo_bytes, flops=c.flops,
+                               config=dict(workload=c.name, P=c.P, Mb=c.Mb, N=c.N, K=c.K, tile_n=c.tile_n,
+                                           weight_replicas=4))
+    if "ag_gemm" in ops:
+        c = cfgs.AG_GEMM_COL
+        log(f"inputs {c.name}")
+        chunks, W, order = gen.ag_gemm_inputs(c.P, c.Mc, c.N, c.K, seed=0)
+        a = bf.AgGemm(c.P, c.Mc, c.N, c.K, bf.BF16, c.tile_m, c.tile_n, chunks, W)
+
+        def ag_call(a=a, order=order):
+            a.run_released(order, stream=stream, release_stream=rel_stream)
+
+        algo_bytes = 2 * (c.P * c.Mc * c.K + c.K * c.N + c.P * c.Mc * c.N)
+        runs["ag_gemm"] = dict(call=ag_call, obj=a, work=c.flops, unit="TFLOP/s", bound="mfma",
+                               peak=PEAK_BF16_TFLOPS, bytes=algo_bytes,
+                               config=dict(workload=c.name, P=c.P, Mc=c.Mc, N=c.N, K=c.K,
+                                           tile=[c.tile_m, c.tile_n], release_order=[int(v) for v in order]))
+    if "embbag_a2a" in ops:
+        c = cfgs.EMBBAG_DLRM
+        log(f"inputs {c.name} (tables on the device)")
+        tables = gen.embbag_tables_torch(c.T, c.R, c.D, seed=0, device=dev)
+        idx = gen.zipf_indices(c.T, c.B, c.L, c.R, alpha=c.alpha, seed=0)
+        e = bf.EmbbagA2A(c.T, c.R, c.D, c.B, c.L, c.P, c.tile_bags, tables, idx)
+        algo_bytes = (4 * c.T * c.B * c.L * c.D      # every looked-up row (logical, no dedup)
+                      + 4 * c.T * c.B * c.L          # indices
+                      + 4 * c.T * c.B * c.D)         # pooled rows written to the buckets
+        runs["embbag_a2a"] = dict(call=lambda e=e: e.run(stream), obj=e, work=algo_bytes, unit="GB/s",
+                                  bound="hbm", peak=PEAK_HBM_GBS, bytes=algo_bytes,
+                                  config=dict(workload=c.name, T=c.T, R=c.R, D=c.D, B=c.B, L=c.L, P=c.P,
+                                              tile_bags=c.tile_bags, zipf_alpha=c.alpha))
+    torch.cuda.synchronize()
+
+    names = list(runs)
+    ev = {n: [] for n in names}
+
+    def step(record):
+        for n in names:
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                runs[n]["call"]()
+                e1.record(stream)
+                ev[n].append((e0, e1))
+            else:
+                runs[n]["call"]()
+
+    log(f"warmup {args.warmup}")
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step(False)
+    torch.cuda.synchronize()
+    log(f"timed {args.steps} steps")
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    for n in names:
+        st = runs[n]["obj"].status_value()
+        if st != 0:
+            raise SystemExit(f"{n}: device status {st} ({hocf.status_string(st)})")
+
+    out_ops = {}
+    for n in names:
+        ms = [a.elapsed_time(b) for a, b in ev[n]]
+        med = median(ms)
+        R = runs[n]
+        if R["unit"] == "TFLOP/s":
+            v = R["work"] / (med * 1e-3) / 1e12
+        else:
+            v = R["work"] / (med * 1e-3) / 1e9
+        out_ops[n] = {
+            "value": round(v, 2), "unit": R["unit"], "ms_median": round(med, 4),
+            "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4),
+            "roofline": {"bound": R["bound"], "achieved": round(v, 2), "peak": R["peak"],
+                         "unit": R["unit"] if R["bound"] == "mfma" else "GB/s",
+                         "frac": round(v / R["peak"], 4), "traffic": None},
+            "algo_bytes": R["bytes"],
+            "config": R["config"],
+        }
+        log(f"{n}: {v:.1f} {R['unit']} ({med:.4f} ms median, {100 * v / R['peak']:.1f}% of peak)")
+
+    head = "gemm_rs" if "gemm_rs" in out_ops else names[0]
+    res = {
+        "metric": METRIC,
+        "value": out_ops[head]["value"],
+        "unit": out_ops[head]["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": out_ops[head]["config"]["workload"],
+                   "step": "one call each of " + ", ".join(names),
+                   "slot_dtype": args.slot_dtype},
+        "roofline": out_ops[head]["roofline"],
+        "ops": out_ops,
+    }
+    if not args.no_cpu_baseline and "gemm_rs" in out_ops:
+        log("cpu baseline (oracle on a bounded sample)")
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+"""Device buffers for one call of each fused operator, and the call itself.
+
+Owns the plumbing around an entry point -- uploading the seeded inputs,
+allocating the receive windows, flag arrays, workspace and status word with
+PyTorch, advancing the epoch -- so that tests, the bench and the smoke check
+drive the C ABI the same way.  No arithmetic of the operators lives here.
+bf16 tensors are carried as ``torch.int16`` (their bit patterns).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import hocf
+
+F32, BF16 = hocf.HOCF_F32, hocf.HOCF_BF16
+
+
+def tdtype(dt):
+    return torch.int16 if dt == BF16 else torch.float32
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_host(t: torch.Tensor, dt) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    return a.view(np.uint16) if dt == BF16 else a
+
+
+def nan_fill(t: torch.Tensor) -> None:
+    """Poison a buffer so that any element the kernel does not write shows up."""
+    if t.dtype == torch.int16:
+        t.fill_(0x7FC0)          # bf16 quiet NaN
+    elif t.dtype == torch.float32:
+        t.fill_(float("nan"))
+    else:
+        t.fill_(-1)
+
+
+def cdiv(a, b):
+    return (a + b - 1) // b
+
+
+class _Common:
+    def _alloc_sync(self, ws_bytes, device):
+        self.ws_bytes = max(int(ws_bytes), 16)
+        self.ws = torch.zeros(cdiv(self.ws_bytes, 4) + 4, dtype=torch.int32, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.epoch = 0
+
+    def next_sync(self, spin_timeout_ns=0, abort_flag=None):
+        self.epoch = (self.epoch % 0xFFFFFFF0) + 1
+        return hocf.sync(self.epoch, self.ws, self.ws_bytes, status=self.status,
+                         abort_flag=abort_flag, spin_timeout_ns=spin_timeout_ns)
+
+    def status_value(self) -> int:
+        return int(self.status.item())
+
+
+class GemmRS(_Common):
+    """hocf_gemm_rs: A [P][M][K], W [P][K][N] -> windows [P dst][P src][Mc][N], out [M][N]."""
+
+    def __init__(self, P, M, N, K, in_dt, slot_dt, out_dt, tile_m, tile_n, A, W, device="cuda"):
+        self.P, self.M, self.N, self.K = P, M, N, K
+        self.in_dt, self.slot_dt, self.out_dt = in_dt, slot_dt, out_dt
+        self.tile_m, self.tile_n = tile_m, tile_n
+        self.Mc = M // P
+        self.A = A if isinstance(A, torch.Tensor) else to_device(A, device)
+        self.W = W if isinstance(W, torch.Tensor) else to_device(W, device)
+        self.tpc = cdiv(self.Mc, tile_m) * cdiv(N, tile_n)
+        self.win_data = torch.empty((P, P, self.Mc, N), dtype=tdtype(slot_dt), device=device)
+        self.win_flags = torch.zeros((P, P, self.tpc), dtype=torch.int32, device=device)
+        self.out = torch.empty((M, N), dtype=tdtype(out_dt), device=device)
+        self.win = hocf.windows([(self.win_data[r], self.win_flags[r]) for r in range(P)])
+        self._alloc_sync(hocf.hocf_gemm_rs_workspace_bytes(P, M, N, tile_m, tile_n), device)
+
+    def poison(self):
+        nan_fill(self.win_data)
+        nan_fill(self.out)
+
+    def call(self, stream=None, **kw) -> int:
+        s = self.next_sync(**kw)
+        return hocf.hocf_gemm_rs(self.P, self.M, self.N, self.K, self.in_dt, self.slot_dt,
+                                 self.out_dt, self.A, self.W, self.win, self.out, self.tile_m,
+                                 self.tile_n, s, stream)
+
+    def run(self, stream=None, **kw):
+        hocf.check(self.call(stream, **kw))
+
+
+class GemvAR(_Common):
+    """hocf_gemv_ar: x [P][Mb][K], W [P][K][N] -> part [P][Mb][N], windows [P][Mb][N]."""
+
+    def __init__(self, P, Mb, N, K, in_dt, slot_dt, out_dt, tile_n, x, W, device="cuda"):
+        self.P, self.Mb, self.N, self.K = P, Mb, N, K
+        self.in_dt, self.slot_dt, self.out_dt, self.tile_n = in_dt, slot_dt, out_dt, tile_n
+        self.x = x if isinstance(x, torch.Tensor) else to_device(x, device)
+        self.W = W if isinstance(W, torch.Tensor) else to_device(W, device)
+        self.nt = cdiv(N, tile_n)
+        self.part = torch.empty((P, Mb, N), dtype=tdtype(slot_dt), device=device)
+        self.part_flags = torch.zeros((P, self.nt), dtype=torch.int32, device=device)
+        self.win_data = torch.empty((P, Mb, N), dtype=tdtype(out_dt), device=device)
+        self.win_flags = torch.zeros((P, self.nt), dtype=torch.int32, device=device)
+        self.win = hocf.windows([(self.win_data[q], self.win_flags[q]) for q in range(P)])
+        self._alloc_sync(hocf.hocf_gemv_ar_workspace_bytes(P, N, tile_n), device)
+
+    def set_weights(self, x, W):
+        self.x, self.W = x, W
+
+    def poison(self):
+        nan_fill(self.part)
+        nan_fill(self.win_data)
+
+    def call(self, stream=None, **kw) -> int:
+        s = self.next_sync(**kw)
+        return hocf.hocf_gemv_ar(self.P, self.Mb, self.N, self.K, self.in_dt, self.slot_dt,
+                                 self.out_dt, self.x, self.W, self.part, self.part_flags, self.win,
+                                 self.tile_n, s, stream)
+
+    def run(self, stream=None, **kw):
+        hocf.check(self.call(stream, **kw))
+
+
+class AgGemm(_Common):
+    """hocf_ag_gemm: gathered chunks [P][Mc][K] gated by chunk_flags [P]; W [K][N] -> out."""
+
+    def __init__(self, P, Mc, N, K, out_dt, tile_m, tile_n, chunks, W, device="cuda"):
+        self.P, self.Mc, self.N, self.K = P, Mc, N, K
+        self.out_dt, self.tile_m, self.tile_n = out_dt, tile_m, tile_n
+        self.A = chunks if isinstance(chunks, torch.Tensor) else to_device(chunks, device)
+        self.W = W if isinstance(W, torch.Tensor) else to_device(W, device)
+        self.chunk_flags = torch.zeros(P, dtype=torch.int32, device=device)
+        self.out = torch.empty((P * Mc, N), dtype=tdtype(out_dt), device=device)
+        self._alloc_sync(hocf.hocf_ag_gemm_workspace_bytes(P), device)
+
+    def poison(self):
+        nan_fill(self.out)
+
+    def call(self, sync_, stream=None) -> int:
+        return hocf.hocf_ag_gemm(self.P, self.Mc, self.N, self.K, BF16, self.out_dt, self.A,
+                                 self.chunk_flags, self.W, self.out, self.tile_m, self.tile_n,
+                                 sync_, stream)
+
+    def run_released(self, order, stream=None, release_stream=None, release_first=False, **kw):
+        """One call whose chunks are released in `order` by the command processor of
+        `release_stream` (after the kernel is enqueued unless release_first)."""
+        s = self.next_sync(**kw)
+        stream = stream or torch.cuda.current_stream()
+        release_stream = release_stream or torch.cuda.Stream()
+        # the releases of this call must not overtake the previous call's kernel
+        # (it waits for the previous epoch); they may overtake this call's kernel
+        prev = torch.cuda.Event()
+        prev.record(stream)
+        release_stream.wait_event(prev)
+        if release_first:
+            hocf.release_chunks(release_stream, self.chunk_flags, order, s.epoch)
+            hocf.check(self.call(s, stream))
+        else:
+            hocf.check(self.call(s, stream))
+            hocf.release_chunks(release_stream, self.chunk_flags, order, s.epoch)
+        return release_stream
+
+
+class EmbbagA2A(_Common):
+    """hocf_embbag_a2a: tables [T][R][D], indices -> windows [P][Bd][T][D]."""
+
+    def __init__(self, T, R, D, B, L, P, tile_bags, tables, indices, offsets=None, device="cuda"):
+        self.T, self.R, self.D, self.B, self.L, self.P = T, R, D, B, L, P
+        self.tile_bags = tile_bags
+        self.Bd = B // P
+        self.nj = cdiv(self.Bd, tile_bags)
+        self.tables = tables if isinstance(tables, torch.Tensor) else to_device(tables, device)
+        self.indices = indices if isinstance(indices, torch.Tensor) else to_device(indices, device)
+        self.offsets = None
+        if offsets is not None:
+            self.offsets = offsets if isinstance(offsets, torch.Tensor) else to_device(offsets, device)
+        self.win_data = torch.empty((P, self.Bd, T, D), dtype=torch.float32, device=device)
+        self.win_flags = torch.zeros((P, T, self.nj), dtype=torch.int32, device=device)
+        self.win = hocf.windows([(self.win_data[d], self.win_flags[d]) for d in range(P)])
+        self._alloc_sync(hocf.hocf_embbag_a2a_workspace_bytes(), device)
+
+    def poison(self):
+        nan_fill(self.win_data)
+
+    def call(self, stream=None, **kw) -> int:
+        s = self.next_sync(**kw)
+        return hocf.hocf_embbag_a2a(self.T, self.R, self.D, self.B, 0 if self.offsets is not None else self.L,
+                                    self.P, self.tables, self.indices, self.offsets, self.win,
+                                    self.tile_bags, s, stream)
+
+    def run(self, stream=None, **kw):
+        hocf.check(self.call(stream, **kw))

@@ -1,0 +1,338 @@
+// C ABI of libhocf.so: argument validation, launch-argument packing, error
+// reporting.  Every check runs before anything is enqueued, so an invalid
+// call leaves the stream untouched.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
+#include "../../include/hocf.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hocf_status fail(hocf_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+hocf_status ok() {
+  g_err[0] = 0;
+  return HOCF_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Checks on the sync block (no HIP call).  `need` = workspace bytes the call needs.
+hocf_status check_sync(const hocf_sync* s, size_t need) {
+  if (!s) return fail(HOCF_ERR_INVALID_ARG, "sync is NULL");
+  if (s->epoch == 0) return fail(HOCF_ERR_INVALID_ARG, "epoch must be nonzero");
+  if (need > 0) {
+    if (!s->workspace) return fail(HOCF_ERR_INVALID_ARG, "workspace is NULL");
+    if (!aligned16(s->workspace)) return fail(HOCF_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    if (s->workspace_bytes < need)
+      return fail(HOCF_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", s->workspace_bytes, need);
+  }
+  if (s->status && (reinterpret_cast<uintptr_t>(s->status) & 3u))
+    return fail(HOCF_ERR_INVALID_ARG, "status word not 4-byte aligned");
+  if (s->abort_flag && (reinterpret_cast<uintptr_t>(s->abort_flag) & 3u))
+    return fail(HOCF_ERR_INVALID_ARG, "abort word not 4-byte aligned");
+  return HOCF_OK;
+}
+
+// Converts a checked sync block for the kernels (queries the device clock).
+hocf_status to_sync_args(const hocf_sync* s, hocf::SyncArgs* out) {
+  hocf::DeviceInfo di;
+  if (hocf::device_info(&di) != hipSuccess) return fail(HOCF_ERR_HIP, "device query failed");
+  const uint64_t ns = s->spin_timeout_ns ? s->spin_timeout_ns : 1000000000ull;
+  out->epoch = s->epoch;
+  out->status = s->status;
+  out->abort_flag = s->abort_flag;
+  // wall_clock64() ticks at wall_clock_khz kHz
+  const long double ticks = (long double)ns * (long double)di.wall_clock_khz / 1.0e6L;
+  out->timeout_ticks = ticks > 1.8e19L ? ~0ull : (uint64_t)ticks;
+  return HOCF_OK;
+}
+
+hocf_status check_windows(const hocf_window* win, int P, const char* what) {
+  if (!win) return fail(HOCF_ERR_INVALID_ARG, "%s: window array is NULL", what);
+  for (int r = 0; r < P; ++r) {
+    if (!win[r].data || !win[r].flags)
+      return fail(HOCF_ERR_INVALID_ARG, "%s: window %d has a NULL data or flags pointer", what, r);
+    if (!aligned16(win[r].data) || (reinterpret_cast<uintptr_t>(win[r].flags) & 3u))
+      return fail(HOCF_ERR_INVALID_ARG, "%s: window %d misaligned", what, r);
+  }
+  return HOCF_OK;
+}
+
+bool dt_ok(hocf_dtype d) { return d == HOCF_F32 || d == HOCF_BF16; }
+
+hocf_status launched(hipError_t e, const char* what) {
+  if (e == hipErrorInvalidValue) return fail(HOCF_ERR_UNSUPPORTED, "%s: no kernel for this shape", what);
+  if (e != hipSuccess) return fail(HOCF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+namespace hocf {
+
+hipError_t device_info(DeviceInfo* out) {
+  static std::mutex mu;
+  static std::unordered_map<int, DeviceInfo> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    DeviceInfo di;
+    int v = 0;
+    if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    di.cus = v;
+    if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;
+    di.wall_clock_khz = v > 0 ? v : 100000;
+    it = cache.emplace(dev, di).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+
+hipError_t persistent_grid(const void* kernel, int threads, int64_t work, int* grid) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, std::unordered_map<int, int>> occ;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  int dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  int per_cu = 0;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto& m = occ[kernel];
+    auto it = m.find(dev);
+    if (it == m.end()) {
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+      if (e != hipSuccess) return e;
+      if (per_cu < 1) per_cu = 1;
+      m[dev] = per_cu;
+    } else {
+      per_cu = it->second;
+    }
+  }
+  int64_t g = (int64_t)per_cu * di.cus;
+  if (work < g) g = work;
+  if (g < 1) g = 1;
+  *grid = (int)g;
+  return hipSuccess;
+}
+
+}  // namespace hocf
+
+extern "C" {
+
+int hocf_abi_version(void) { return HOCF_ABI_VERSION; }
+
+const char* hocf_status_string(hocf_status s) {
+  switch (s) {
+    case HOCF_OK: return "ok";
+    case HOCF_ERR_INVALID_ARG: return "invalid argument";
+    case HOCF_ERR_UNSUPPORTED: return "unsupported combination";
+    case HOCF_ERR_HIP: return "HIP runtime error";
+    case HOCF_ERR_TIMEOUT: return "flag wait timed out";
+    case HOCF_ERR_ABORTED: return "aborted";
+    case HOCF_ERR_BAD_INDEX: return "embedding index out of range";
+    case HOCF_ERR_PROTOCOL: return "partial consumed before its flag was set";
+  }
+  return "unknown status";
+}
+
+const char* hocf_last_error(void) { return g_err; }
+
+/* ------------------------------------------------------------ GEMM + RS */
+
+size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n) {
+  if (P <= 0 || M < 0 || N < 0 || tile_m <= 0 || tile_n <= 0 || M % P) return 0;
+  const int64_t tpc = cdiv(M / P, tile_m) * cdiv(N, tile_n);
+  return (size_t)(hocf::kWsBaseWords + (int64_t)P * tpc) * 4;
+}
+
+hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                         hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
+                         void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
+  if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: P=%d outside [1, %d]", P, HOCF_MAX_P);
+  if (M < 0 || N < 0 || K < 0) return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: negative dimension");
+  if (M % P) return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: M=%d not divisible by P=%d", M, P);
+  if (!dt_ok(in_dt) || !dt_ok(slot_dt) || !dt_ok(out_dt))
+    return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: unknown dtype");
+  const int vec = in_dt == HOCF_BF16 ? 8 : 4;
+  if (N % vec || K % vec)
+    return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: N=%d and K=%d must be multiples of %d", N, K, vec);
+  bool tile_ok;
+  if (in_dt == HOCF_BF16) tile_ok = (tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128);
+  else tile_ok = (tile_m == 64 && tile_n == 64) && slot_dt == HOCF_F32 && out_dt == HOCF_F32;
+  if (!tile_ok)
+    return fail(HOCF_ERR_UNSUPPORTED, "gemm_rs: no kernel for in=%d slot=%d out=%d tile %dx%d",
+                in_dt, slot_dt, out_dt, tile_m, tile_n);
+  const size_t need = hocf_gemm_rs_workspace_bytes(P, M, N, tile_m, tile_n);
+  hocf_status st = check_sync(sync, need);
+  if (st != HOCF_OK) return st;
+  if (M == 0 || N == 0) return ok();
+  if (!A || !W || !out) return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: NULL tensor");
+  if ((K && (!aligned16(A) || !aligned16(W))) || !aligned16(out))
+    return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: tensors must be 16-byte aligned");
+  if ((st = check_windows(win, P, "gemm_rs")) != HOCF_OK) return st;
+
+  hocf::SyncArgs sa;
+  if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
+  hocf::GemmRsArgs a{};
+  a.A = A; a.W = W; a.out = out;
+  for (int r = 0; r < P; ++r) { a.win_data[r] = win[r].data; a.win_flags[r] = win[r].flags; }
+  a.ws = static_cast<uint32_t*>(sync->workspace);
+  a.P = P; a.M = M; a.N = N; a.K = K; a.Mc = M / P;
+  a.slot_dt = slot_dt; a.out_dt = out_dt;
+  a.mtiles = (int)cdiv(a.Mc, tile_m);
+  a.ntiles = (int)cdiv(N, tile_n);
+  a.total = (int64_t)P * P * a.mtiles * a.ntiles;
+  a.sync = sa;
+  return launched(hocf::launch_gemm_rs(a, tile_m, tile_n, in_dt, static_cast<hipStream_t>(stream)),
+                  "gemm_rs");
+}
+
+/* ------------------------------------------------------------ GEMV + AR */
+
+size_t hocf_gemv_ar_workspace_bytes(int P, int N, int tile_n) {
+  if (P <= 0 || N < 0 || tile_n <= 0) return 0;
+  return (size_t)(hocf::kWsBaseWords + cdiv(N, tile_n)) * 4;
+}
+
+hocf_status hocf_gemv_ar(int P, int Mb, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                         hocf_dtype out_dt, const void* x, const void* W, void* part,
+                         uint32_t* part_flags, const hocf_window* win, int tile_n,
+                         const hocf_sync* sync, void* stream) {
+  if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: P=%d outside [1, %d]", P, HOCF_MAX_P);
+  if (Mb < 0 || N < 0 || K < 0) return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: negative dimension");
+  if (!dt_ok(in_dt) || !dt_ok(slot_dt) || !dt_ok(out_dt))
+    return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: unknown dtype");
+  if (in_dt != HOCF_BF16) return fail(HOCF_ERR_UNSUPPORTED, "gemv_ar: inputs must be bf16");
+  if (Mb > 8) return fail(HOCF_ERR_UNSUPPORTED, "gemv_ar: Mb=%d > 8", Mb);
+  if (tile_n != 128 && tile_n != 256 && tile_n != 512)
+    return fail(HOCF_ERR_UNSUPPORTED, "gemv_ar: tile_n=%d not in {128, 256, 512}", tile_n);
+  if (N % 8 || K % 8) return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: N and K must be multiples of 8");
+  hocf_status st = check_sync(sync, hocf_gemv_ar_workspace_bytes(P, N, tile_n));
+  if (st != HOCF_OK) return st;
+  if (Mb == 0 || N == 0) return ok();
+  if (!x || !W || !part || !part_flags) return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: NULL tensor");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(part))
+    return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: tensors must be 16-byte aligned");
+  if ((st = check_windows(win, P, "gemv_ar")) != HOCF_OK) return st;
+
+  hocf::SyncArgs sa;
+  if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
+  hocf::GemvArArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.W = static_cast<const uint16_t*>(W);
+  a.part = part; a.part_flags = part_flags;
+  for (int q = 0; q < P; ++q) { a.win_data[q] = win[q].data; a.win_flags[q] = win[q].flags; }
+  a.ws = static_cast<uint32_t*>(sync->workspace);
+  a.P = P; a.Mb = Mb; a.N = N; a.K = K; a.tile_n = tile_n;
+  a.ntiles = (int)cdiv(N, tile_n);
+  a.slot_dt = slot_dt; a.out_dt = out_dt;
+  a.total = (int64_t)P * a.ntiles;
+  a.sync = sa;
+  return launched(hocf::launch_gemv_ar(a, static_cast<hipStream_t>(stream)), "gemv_ar");
+}
+
+/* ------------------------------------------------------------ AG + GEMM */
+
+size_t hocf_ag_gemm_workspace_bytes(int P) {
+  if (P <= 0) return 0;
+  return (size_t)(hocf::kWsBaseWords + 2 * (int64_t)P + 3) * 4;
+}
+
+hocf_status hocf_ag_gemm(int P, int Mc, int N, int K, hocf_dtype in_dt, hocf_dtype out_dt,
+                         const void* A_gathered, const uint32_t* chunk_flags, const void* W,
+                         void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
+  if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "ag_gemm: P=%d outside [1, %d]", P, HOCF_MAX_P);
+  if (Mc < 0 || N < 0 || K < 0) return fail(HOCF_ERR_INVALID_ARG, "ag_gemm: negative dimension");
+  if (!dt_ok(in_dt) || !dt_ok(out_dt)) return fail(HOCF_ERR_INVALID_ARG, "ag_gemm: unknown dtype");
+  if (in_dt != HOCF_BF16) return fail(HOCF_ERR_UNSUPPORTED, "ag_gemm: inputs must be bf16");
+  if (!((tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128)))
+    return fail(HOCF_ERR_UNSUPPORTED, "ag_gemm: no kernel for tile %dx%d", tile_m, tile_n);
+  if (N % 8 || K % 8) return fail(HOCF_ERR_INVALID_ARG, "ag_gemm: N and K must be multiples of 8");
+  hocf_status st = check_sync(sync, hocf_ag_gemm_workspace_bytes(P));
+  if (st != HOCF_OK) return st;
+  if (Mc == 0 || N == 0) return ok();
+  if (!A_gathered || !chunk_flags || !W || !out) return fail(HOCF_ERR_INVALID_ARG, "ag_gemm: NULL tensor");
+  if ((K && (!aligned16(A_gathered) || !aligned16(W))) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(chunk_flags) & 3u))
+    return fail(HOCF_ERR_INVALID_ARG, "ag_gemm: misaligned tensor");
+
+  hocf::SyncArgs sa;
+  if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
+  hocf::AgGemmArgs a{};
+  a.A = static_cast<const uint16_t*>(A_gathered);
+  a.chunk_flags = chunk_flags;
+  a.W = static_cast<const uint16_t*>(W);
+  a.out = out;
+  a.ws = static_cast<uint32_t*>(sync->workspace);
+  a.P = P; a.Mc = Mc; a.N = N; a.K = K; a.out_dt = out_dt;
+  a.mtiles = (int)cdiv(Mc, tile_m);
+  a.ntiles = (int)cdiv(N, tile_n);
+  a.sync = sa;
+  return launched(hocf::launch_ag_gemm(a, tile_m, tile_n, static_cast<hipStream_t>(stream)), "ag_gemm");
+}
+
+/* ------------------------------------------------------------ emb-bag + A2A */
+
+size_t hocf_embbag_a2a_workspace_bytes(void) { return (size_t)hocf::kWsBaseWords * 4; }
+
+hocf_status hocf_embbag_a2a(int T, int64_t R, int D, int B, int L, int P, const float* tables,
+                            const int32_t* indices, const int64_t* offsets,
+                            const hocf_window* win, int tile_bags, const hocf_sync* sync,
+                            void* stream) {
+  if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "embbag_a2a: P=%d outside [1, %d]", P, HOCF_MAX_P);
+  if (T < 0 || R < 0 || D < 0 || B < 0 || (!offsets && L < 0))
+    return fail(HOCF_ERR_INVALID_ARG, "embbag_a2a: negative dimension");
+  if (B % P) return fail(HOCF_ERR_INVALID_ARG, "embbag_a2a: B=%d not divisible by P=%d", B, P);
+  if (D % 4) return fail(HOCF_ERR_INVALID_ARG, "embbag_a2a: D=%d not a multiple of 4", D);
+  if (D > 512) return fail(HOCF_ERR_UNSUPPORTED, "embbag_a2a: D=%d > 512", D);
+  if (tile_bags < 1 || tile_bags > 4096)
+    return fail(HOCF_ERR_INVALID_ARG, "embbag_a2a: tile_bags=%d outside [1, 4096]", tile_bags);
+  hocf_status st = check_sync(sync, hocf_embbag_a2a_workspace_bytes());
+  if (st != HOCF_OK) return st;
+  if (T == 0 || B == 0 || D == 0) return ok();
+  if (!tables && R > 0) return fail(HOCF_ERR_INVALID_ARG, "embbag_a2a: NULL tables");
+  if (!indices && (offsets || L > 0)) return fail(HOCF_ERR_INVALID_ARG, "embbag_a2a: NULL indices");
+  if ((tables && !aligned16(tables)) || (offsets && (reinterpret_cast<uintptr_t>(offsets) & 7u)))
+    return fail(HOCF_ERR_INVALID_ARG, "embbag_a2a: misaligned tensor");
+  if ((st = check_windows(win, P, "embbag_a2a")) != HOCF_OK) return st;
+
+  hocf::SyncArgs sa;
+  if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
+  hocf::EmbbagArgs a{};
+  a.tables = tables; a.indices = indices; a.offsets = offsets;
+  for (int d = 0; d < P; ++d) {
+    a.win_data[d] = static_cast<float*>(win[d].data);
+    a.win_flags[d] = win[d].flags;
+  }
+  a.ws = static_cast<uint32_t*>(sync->workspace);
+  a.R = R; a.T = T; a.D = D; a.B = B; a.L = offsets ? 0 : L; a.P = P;
+  a.Bd = B / P; a.tile_bags = tile_bags;
+  a.nj = (int)cdiv(a.Bd, tile_bags);
+  a.total = (int64_t)T * P * a.nj;
+  a.sync = sa;
+  return launched(hocf::launch_embbag_a2a(a, static_cast<hipStream_t>(stream)), "embbag_a2a");
+}
+
+}  // extern "C"

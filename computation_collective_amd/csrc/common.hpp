@@ -1,0 +1,85 @@
+// Device-side basics shared by the hocf kernels: vector types, bfloat16
+// encoding, and the launch-argument structs the host fills in.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hocf {
+
+constexpr int kMaxP = 16;      // largest shard count (matches HOCF_MAX_P)
+constexpr int kNumQueues = 8;  // one ticket queue per XCD (MI355X has 8)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+enum Dt : int { kF32 = 0, kBF16 = 1 };
+
+// bfloat16 is the top half of a binary32 pattern.
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// binary32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Compile-time-typed vector access: 4 consecutive elements as fp32.
+template <int DT>
+__device__ __forceinline__ floatx4 ld4(const void* base, int64_t i) {
+  floatx4 r;
+  if constexpr (DT == kBF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + i);
+    r[0] = bf16_to_f32(u.x & 0xffffu);
+    r[1] = bf16_to_f32(u.x >> 16);
+    r[2] = bf16_to_f32(u.y & 0xffffu);
+    r[3] = bf16_to_f32(u.y >> 16);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + i);
+    r[0] = f.x; r[1] = f.y; r[2] = f.z; r[3] = f.w;
+  }
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void st4(void* base, int64_t i, floatx4 v) {
+  if constexpr (DT == kBF16) {
+    uint2 u;
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + i) = u;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + i) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float ld1(const void* base, int64_t i) {
+  if constexpr (DT == kBF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
+  else return reinterpret_cast<const float*>(base)[i];
+}
+
+template <int DT>
+__device__ __forceinline__ void st1(void* base, int64_t i, float v) {
+  if constexpr (DT == kBF16) reinterpret_cast<uint16_t*>(base)[i] = (uint16_t)f32_to_bf16(v);
+  else reinterpret_cast<float*>(base)[i] = v;
+}
+
+// Status codes the kernels record (values of hocf_status).
+constexpr uint32_t kErrTimeout = 4, kErrAborted = 5, kErrBadIndex = 6, kErrProtocol = 7;
+
+// Synchronisation arguments common to every kernel.
+struct SyncArgs {
+  uint32_t epoch;
+  uint32_t* status;            // nullable device word
+  const uint32_t* abort_flag;  // nullable
+  uint64_t timeout_ticks;      // in wall_clock64() ticks
+};
+
+}  // namespace hocf

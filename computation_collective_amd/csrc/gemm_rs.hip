@@ -1,0 +1,157 @@
+// GEMM + ReduceScatter, fused in one persistent kernel.
+//
+// mKernel news item ("GPU-vezérelt kommunikációval gyorsítják az
+// AI-betanítást a kutatók"): GEMM + ReduceScatter is one of its five fused
+// kernels, with communication in the same persistent kernel as the compute
+// and tile-level overlap.  SC24 ("Optimizing Distributed ML Communication
+// with Fused Computation-Collective Operations", abstract): each workgroup
+// sends its result on as soon as its computation is done while the other
+// workgroups of the kernel keep computing.
+//
+// Work item = one TM x TN tile of one shard's partial C_p = A_p . W_p.
+// Items are dealt from eight ticket queues, one per XCD: queue q holds a
+// contiguous range of the item list ordered (p, chunk r, column tile, row
+// tile), so with P = 8 an XCD computes one shard and its 32 concurrent
+// tiles share A row panels and W column panels in that XCD's L2.
+//
+// When a tile is done the workgroup
+//   1. stores it into destination r's window, slot p (publish),
+//   2. releases the tile's ready flag (epoch) in window r,
+//   3. counts itself in the output tile's arrival counter; the workgroup
+//      that completes the count (the last of the P producers) acquires, checks
+//      the P flags, and folds the P slots in rank order p = 0..P-1 in fp32
+//      into the destination's output chunk -- while other workgroups are
+//      still computing.
+// No workgroup ever waits on another, so the persistent grid cannot stall.
+#include <type_traits>
+
+#include "internal.hpp"
+#include "mfma_tile.hpp"
+#include "sync.hpp"
+
+namespace hocf {
+
+template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
+__global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
+  using Elem = typename std::conditional<BF16IN, uint16_t, float>::type;
+  __shared__ __attribute__((aligned(16))) Elem lds[Tile::LDS_BYTES / sizeof(Elem)];
+  __shared__ int s_qcur;
+  __shared__ int64_t s_item;
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = a.P, N = a.N, K = a.K, Mc = a.Mc;
+  const int tpc = a.mtiles * a.ntiles;
+  uint32_t* grp = a.ws + kWsExtra;
+  if (tid == 0) s_qcur = 0;
+  __syncthreads();
+
+  for (;;) {
+    const int64_t item = claim_item(a.ws, a.total, &s_qcur, &s_item);
+    if (item < 0) break;
+    const int tq = (int)(item % tpc);
+    const int r = (int)((item / tpc) % P);
+    const int p = (int)(item / ((int64_t)tpc * P));
+    const int nt = tq / a.mtiles, mt = tq % a.mtiles;
+    const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
+    const int cols_valid = min(Tile::TN, N - nt * Tile::TN);
+
+    const Elem* At = reinterpret_cast<const Elem*>(a.A) +
+                     ((int64_t)p * a.M + (int64_t)r * Mc + (int64_t)mt * Tile::TM) * K;
+    const Elem* Wt = reinterpret_cast<const Elem*>(a.W) + (int64_t)p * K * N + (int64_t)nt * Tile::TN;
+    floatx16 acc[Tile::FM][Tile::FN];
+    Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, lds, acc);
+
+    // 1. publish the tile into window r, slot p
+    void* wdata = a.win_data[r];
+    const int64_t slot_off = ((int64_t)p * Mc + (int64_t)mt * Tile::TM) * N + (int64_t)nt * Tile::TN;
+#pragma unroll
+    for (int i = 0; i < Tile::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Tile::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          int row, col;
+          Tile::quad(i, j, g, lane, wave, row, col);
+          if (!RAGGED || (row < rows_valid && col < cols_valid)) {
+            const floatx4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                               acc[i][j][4 * g + 3]};
+            st4<SDT>(wdata, slot_off + (int64_t)row * N + col, v);
+          }
+        }
+    __syncthreads();
+
+    // 2. ready flag; 3. arrival count -> the last producer reduces
+    const int tflag = mt * a.ntiles + nt;
+    if (tid == 0) {
+      release_flag(&a.win_flags[r][(int64_t)p * tpc + tflag], a.sync.epoch);
+      uint32_t* cnt = &grp[(int64_t)r * tpc + tflag];
+      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = (prev == (uint32_t)(P - 1));
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (s_last) {
+      acquire_agent();
+      if (tid < P && load_flag_agent(&a.win_flags[r][(int64_t)tid * tpc + tflag]) != a.sync.epoch)
+        report_status(a.sync, kErrProtocol);
+      const int64_t slot_stride = (int64_t)Mc * N;
+      const int64_t base = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
+      const int64_t obase = (int64_t)r * Mc * N + base;
+      for (int e = tid * 4; e < Tile::TM * Tile::TN; e += Tile::NT * 4) {
+        const int row = e / Tile::TN, col = e % Tile::TN;
+        if (RAGGED && (row >= rows_valid || col >= cols_valid)) continue;
+        const int64_t off = base + (int64_t)row * N + col;
+        floatx4 v[kMaxP];
+#pragma unroll
+        for (int q = 0; q < kMaxP; ++q)
+          if (q < P) v[q] = ld4<SDT>(wdata, q * slot_stride + off);
+        floatx4 s = v[0];
+#pragma unroll
+        for (int q = 1; q < kMaxP; ++q)
+          if (q < P) s = s + v[q];
+        st4<ODT>(a.out, obase + (int64_t)row * N + col, s);
+      }
+    }
+  }
+  finish_workgroup(a.ws);
+}
+
+template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
+static hipError_t launch_one(const GemmRsArgs& a, hipStream_t s) {
+  auto kern = &gemm_rs_kernel<Tile, RAGGED, BF16IN, SDT, ODT>;
+  int grid = 0;
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), Tile::NT, a.total, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(Tile::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class Tile, bool BF16IN, int SDT, int ODT>
+static hipError_t launch_tile(const GemmRsArgs& a, hipStream_t s) {
+  const bool ragged = (a.Mc % Tile::TM) || (a.N % Tile::TN) || (a.K % Tile::BK);
+  return ragged ? launch_one<Tile, true, BF16IN, SDT, ODT>(a, s)
+                : launch_one<Tile, false, BF16IN, SDT, ODT>(a, s);
+}
+
+template <class Tile>
+static hipError_t launch_bf16(const GemmRsArgs& a, hipStream_t s) {
+  if (a.slot_dt == kF32 && a.out_dt == kBF16) return launch_tile<Tile, true, kF32, kBF16>(a, s);
+  if (a.slot_dt == kBF16 && a.out_dt == kBF16) return launch_tile<Tile, true, kBF16, kBF16>(a, s);
+  if (a.slot_dt == kF32 && a.out_dt == kF32) return launch_tile<Tile, true, kF32, kF32>(a, s);
+  if (a.slot_dt == kBF16 && a.out_dt == kF32) return launch_tile<Tile, true, kBF16, kF32>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_rs(const GemmRsArgs& a, int tm, int tn, int in_dt, hipStream_t s) {
+  if (in_dt == kBF16) {
+    if (tm == 256 && tn == 256) return launch_bf16<TileBf16<256, 256, 2, 2>>(a, s);
+    if (tm == 128 && tn == 128) return launch_bf16<TileBf16<128, 128, 2, 2>>(a, s);
+  } else if (a.slot_dt == kF32 && a.out_dt == kF32) {
+    if (tm == 64 && tn == 64) return launch_tile<TileF32<64, 64, 2, 2>, false, kF32, kF32>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hocf

@@ -1,0 +1,84 @@
+// Launch-side declarations shared by the C ABI (abi.cpp) and the kernel
+// translation units.  Arguments reaching these functions are validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace hocf {
+
+struct GemmRsArgs {
+  const void* A;
+  const void* W;
+  void* out;
+  void* win_data[kMaxP];
+  uint32_t* win_flags[kMaxP];
+  uint32_t* ws;
+  int P, M, N, K, Mc;
+  int slot_dt, out_dt;
+  int mtiles, ntiles;  // tile grid of one chunk
+  int64_t total;       // P (sources) * P (chunks) * mtiles * ntiles
+  SyncArgs sync;
+};
+
+struct GemvArArgs {
+  const uint16_t* x;
+  const uint16_t* W;
+  void* part;
+  uint32_t* part_flags;
+  void* win_data[kMaxP];
+  uint32_t* win_flags[kMaxP];
+  uint32_t* ws;
+  int P, Mb, N, K, tile_n, ntiles;
+  int slot_dt, out_dt;
+  int64_t total;  // P * ntiles
+  SyncArgs sync;
+};
+
+struct AgGemmArgs {
+  const uint16_t* A;
+  const uint32_t* chunk_flags;
+  const uint16_t* W;
+  void* out;
+  uint32_t* ws;
+  int P, Mc, N, K, out_dt;
+  int mtiles, ntiles;
+  SyncArgs sync;
+};
+
+struct EmbbagArgs {
+  const float* tables;
+  const int32_t* indices;
+  const int64_t* offsets;
+  float* win_data[kMaxP];
+  uint32_t* win_flags[kMaxP];
+  uint32_t* ws;
+  int64_t R;
+  int T, D, B, L, P, Bd, tile_bags, nj;
+  int64_t total;  // T * P * nj
+  SyncArgs sync;
+};
+
+// Device properties the launches need, cached per device.
+struct DeviceInfo {
+  int cus = 0;
+  int64_t wall_clock_khz = 0;
+};
+hipError_t device_info(DeviceInfo* out);
+
+// Persistent-grid size for a kernel: resident workgroups the device can hold
+// (occupancy x CUs), capped by the work available.
+hipError_t persistent_grid(const void* kernel, int threads, int64_t work, int* grid);
+
+// Each returns hipErrorInvalidValue for a tile shape it has no kernel for.
+hipError_t launch_gemm_rs(const GemmRsArgs& a, int tile_m, int tile_n, int in_dt, hipStream_t s);
+hipError_t launch_gemv_ar(const GemvArArgs& a, hipStream_t s);
+hipError_t launch_ag_gemm(const AgGemmArgs& a, int tile_m, int tile_n, hipStream_t s);
+hipError_t launch_embbag_a2a(const EmbbagArgs& a, hipStream_t s);
+
+// Workspace words each operator needs.
+constexpr int64_t kWsBaseWords = kNumQueues + 1;
+
+}  // namespace hocf

@@ -1,0 +1,299 @@
+// One workgroup computes one TM x TN output tile  C = A[rows, :] . W[:, cols]
+// on the matrix cores (fp32 accumulation), staging A and W tiles through
+// LDS with a two-stage pipeline: while the MFMAs consume stage s, the next
+// K-slice is already in flight from global memory into registers, and is
+// written to stage s^1 before the single barrier of the step.
+//
+// bf16 path (gfx950 v_mfma_f32_32x32x16_bf16): each lane feeds 8 consecutive
+// k of one row of A and 8 consecutive k of one column of W.  A is row-major
+// [M][K], so its rows are copied to LDS as they are.  W is row-major [K][N],
+// so its K-slice is transposed on the way into LDS: each thread loads a
+// 4(k) x 8(n) block (four 16-byte row pieces, 128-byte coalesced per 8
+// lanes), regroups it in registers into eight 4(k) pieces and writes those
+// into the transposed tile Wt[n][k].  LDS rows are padded to 144 bytes and
+// Wt's 8-byte k-slots are XOR-swizzled by bit 4 of n, so both the
+// transposing writes and the MFMA operand reads spread over all banks.
+//
+// fp32 path (v_mfma_f32_32x32x2f32, one element per lane and operand): no
+// transpose is needed; W's K-slice is kept [k][n].
+//
+// The MFMA is fed with W as its first operand and A as its second, so each
+// 32x32 accumulator block holds C^T: lane l, block (i, j), element v = 4g+e
+// holds tile row  wm*WTM + 32i + l%32  and column  wn*WTN + 32j + 8g +
+// 4(l/32) + e.  Each lane therefore owns runs of 4 consecutive columns of
+// one row, which the epilogues store as 16-byte (fp32) or 8-byte (bf16)
+// vectors.
+#pragma once
+
+#include "common.hpp"
+
+namespace hocf {
+
+__device__ __forceinline__ uint32_t u4_word(const uint4& v, int d) {
+  return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+}
+
+template <int TM_, int TN_, int WM_, int WN_>
+struct TileBf16 {
+  static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int BK = 64;
+  static constexpr int LDK = BK + 8;  // padded row: 72 bf16 = 144 bytes
+  static constexpr int WTM = TM / WM, WTN = TN / WN;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int A_ELEMS = TM * LDK, B_ELEMS = TN * LDK, STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int A_LD = (TM * BK / 8) / NT;  // 16-byte A pieces per thread per step
+  static constexpr int NBH = TN / 64;              // W wave-blocks along n (8 lanes x 8 n)
+  static constexpr int B_BLK = 2 * NBH / NW;       // 4(k) x 8(n) W blocks per thread per step
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert((TM * BK / 8) % NT == 0 && A_LD >= 1, "A slice must split evenly");
+  static_assert(B_BLK >= 1 && B_BLK * NW == 2 * NBH, "W slice must split evenly over the waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+  // Tile coordinates of accumulator elements acc[i][j][4g .. 4g+3]: one row, 4 columns.
+  __device__ static __forceinline__ void quad(int i, int j, int g, int lane, int wave, int& row,
+                                              int& col0) {
+    const int wm = wave / WN, wn = wave % WN;
+    row = wm * WTM + 32 * i + (lane & 31);
+    col0 = wn * WTN + 32 * j + 8 * g + 4 * (lane >> 5);
+  }
+
+  // Physical 8-byte k-slot of logical slot s in Wt row n (bit 3 flipped by bit 4 of n).
+  __device__ static __forceinline__ int wslot(int n, int s) { return s ^ (((n >> 4) & 1) << 3); }
+
+  template <bool RAGGED>
+  __device__ static __forceinline__ void run(const uint16_t* __restrict__ A, int64_t lda,
+                                             const uint16_t* __restrict__ W, int64_t ldw,
+                                             int rows_valid, int cols_valid, int K,
+                                             uint16_t* lds, floatx16 (&acc)[FM][FN]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // this thread's W blocks: 4 k-rows x 8 n-columns each; wave-block id
+    // wave + NW*i covers n-block group (id mod NBH) and k-half (id / NBH)
+    int nbv[B_BLK], kbv[B_BLK];
+#pragma unroll
+    for (int i = 0; i < B_BLK; ++i) {
+      const int id = wave + NW * i;
+      nbv[i] = (id % NBH) * 8 + (lane & 7);
+      kbv[i] = (id / NBH) * 8 + (lane >> 3);
+    }
+
+    uint4 ra[A_LD];
+    uint4 rb[B_BLK][4];
+    const int nk = (K + BK - 1) / BK;
+
+    auto load_global = [&](int ks) {
+      const int k0 = ks * BK;
+#pragma unroll
+      for (int t = 0; t < A_LD; ++t) {
+        const int c = tid + t * NT;
+        const int row = c / (BK / 8), kc = c % (BK / 8);
+        const int k = k0 + kc * 8;
+        if (!RAGGED || (row < rows_valid && k < K))
+          ra[t] = *reinterpret_cast<const uint4*>(A + (int64_t)row * lda + k);
+        else
+          ra[t] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < B_BLK; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int k = k0 + kbv[i] * 4 + j, n = nbv[i] * 8;
+          if (!RAGGED || (k < K && n < cols_valid))
+            rb[i][j] = *reinterpret_cast<const uint4*>(W + (int64_t)k * ldw + n);
+          else
+            rb[i][j] = make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    auto store_lds = [&](int stage) {
+      uint16_t* As = lds + stage * STAGE;
+      uint16_t* Bs = As + A_ELEMS;
+#pragma unroll
+      for (int t = 0; t < A_LD; ++t) {
+        const int c = tid + t * NT;
+        const int row = c / (BK / 8), kc = c % (BK / 8);
+        *reinterpret_cast<uint4*>(As + row * LDK + kc * 8) = ra[t];
+      }
+      // transpose each 4x8 block: for column e, pack k = 0..3 into 8 bytes
+#pragma unroll
+      for (int i = 0; i < B_BLK; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = e >> 1;
+          const uint32_t w0 = u4_word(rb[i][0], d), w1 = u4_word(rb[i][1], d);
+          const uint32_t w2 = u4_word(rb[i][2], d), w3 = u4_word(rb[i][3], d);
+          uint32_t lo, hi;
+          if (e & 1) {
+            lo = (w0 >> 16) | (w1 & 0xffff0000u);
+            hi = (w2 >> 16) | (w3 & 0xffff0000u);
+          } else {
+            lo = (w0 & 0xffffu) | (w1 << 16);
+            hi = (w2 & 0xffffu) | (w3 << 16);
+          }
+          const int n = nbv[i] * 8 + e;
+          *reinterpret_cast<uint2*>(Bs + n * LDK + wslot(n, kbv[i]) * 4) = make_uint2(lo, hi);
+        }
+    };
+
+    auto compute = [&](int stage) {
+      const uint16_t* As = lds + stage * STAGE;
+      const uint16_t* Bs = As + A_ELEMS;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 a[FM], b[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int m = wm * WTM + 32 * i + (lane & 31);
+          a[i] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const uint4*>(As + m * LDK + kk * 16 + (lane >> 5) * 8));
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int n = wn * WTN + 32 * j + (lane & 31);
+          const int s = kk * 4 + (lane >> 5) * 2;
+          b[j] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const uint4*>(Bs + n * LDK + wslot(n, s) * 4));
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      }
+    };
+
+    if (nk == 0) return;
+    load_global(0);
+    store_lds(0);
+    __syncthreads();
+    for (int ks = 0; ks < nk; ++ks) {
+      if (ks + 1 < nk) load_global(ks + 1);
+      compute(ks & 1);
+      if (ks + 1 < nk) store_lds((ks + 1) & 1);
+      __syncthreads();
+    }
+  }
+};
+
+template <int TM_, int TN_, int WM_, int WN_>
+struct TileF32 {
+  static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int BK = 32;
+  static constexpr int LDA = BK + 1, LDB = TN + 4;
+  static constexpr int WTM = TM / WM, WTN = TN / WN;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int A_ELEMS = TM * LDA, B_ELEMS = BK * LDB, STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int LDS_BYTES = 2 * STAGE * 4;
+  static constexpr int A_LD = (TM * BK / 4) / NT, B_LD = (BK * TN / 4) / NT;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(A_LD >= 1 && B_LD >= 1 && (TM * BK / 4) % NT == 0 && (BK * TN / 4) % NT == 0,
+                "slices must split evenly");
+
+  // Tile coordinates of accumulator elements acc[i][j][4g .. 4g+3]: one row, 4 columns.
+  __device__ static __forceinline__ void quad(int i, int j, int g, int lane, int wave, int& row,
+                                              int& col0) {
+    const int wm = wave / WN, wn = wave % WN;
+    row = wm * WTM + 32 * i + (lane & 31);
+    col0 = wn * WTN + 32 * j + 8 * g + 4 * (lane >> 5);
+  }
+
+  template <bool RAGGED>
+  __device__ static __forceinline__ void run(const float* __restrict__ A, int64_t lda,
+                                             const float* __restrict__ W, int64_t ldw,
+                                             int rows_valid, int cols_valid, int K, float* lds,
+                                             floatx16 (&acc)[FM][FN]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    float4 ra[A_LD], rb[B_LD];
+    const int nk = (K + BK - 1) / BK;
+
+    auto load_global = [&](int ks) {
+      const int k0 = ks * BK;
+#pragma unroll
+      for (int t = 0; t < A_LD; ++t) {
+        const int c = tid + t * NT;
+        const int row = c / (BK / 4), k = k0 + (c % (BK / 4)) * 4;
+        if (!RAGGED || (row < rows_valid && k < K))
+          ra[t] = *reinterpret_cast<const float4*>(A + (int64_t)row * lda + k);
+        else
+          ra[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int t = 0; t < B_LD; ++t) {
+        const int c = tid + t * NT;
+        const int k = k0 + c / (TN / 4), n = (c % (TN / 4)) * 4;
+        if (!RAGGED || (k < K && n < cols_valid))
+          rb[t] = *reinterpret_cast<const float4*>(W + (int64_t)k * ldw + n);
+        else
+          rb[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    auto store_lds = [&](int stage) {
+      float* As = lds + stage * STAGE;
+      float* Bs = As + A_ELEMS;
+#pragma unroll
+      for (int t = 0; t < A_LD; ++t) {
+        const int c = tid + t * NT;
+        const int row = c / (BK / 4), kq = (c % (BK / 4)) * 4;
+        As[row * LDA + kq + 0] = ra[t].x;
+        As[row * LDA + kq + 1] = ra[t].y;
+        As[row * LDA + kq + 2] = ra[t].z;
+        As[row * LDA + kq + 3] = ra[t].w;
+      }
+#pragma unroll
+      for (int t = 0; t < B_LD; ++t) {
+        const int c = tid + t * NT;
+        const int k = c / (TN / 4), n = (c % (TN / 4)) * 4;
+        *reinterpret_cast<float4*>(Bs + k * LDB + n) = rb[t];
+      }
+    };
+    auto compute = [&](int stage) {
+      const float* As = lds + stage * STAGE;
+      const float* Bs = As + A_ELEMS;
+#pragma unroll
+      for (int kk = 0; kk < BK / 2; ++kk) {
+        const int k = kk * 2 + (lane >> 5);
+        float a[FM], b[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[i] = As[(wm * WTM + 32 * i + (lane & 31)) * LDA + k];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b[j] = Bs[k * LDB + wn * WTN + 32 * j + (lane & 31)];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[j], a[i], acc[i][j], 0, 0, 0);
+      }
+    };
+
+    if (nk == 0) return;
+    load_global(0);
+    store_lds(0);
+    __syncthreads();
+    for (int ks = 0; ks < nk; ++ks) {
+      if (ks + 1 < nk) load_global(ks + 1);
+      compute(ks & 1);
+      if (ks + 1 < nk) store_lds((ks + 1) & 1);
+      __syncthreads();
+    }
+  }
+};
+
+}  // namespace hocf

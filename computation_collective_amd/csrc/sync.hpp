@@ -1,0 +1,105 @@
+// Flag protocol and persistent-workgroup scheduling.
+//
+// Producer side: a workgroup's threads store a tile, meet at a barrier
+// (their stores have then reached this XCD's L2), and one thread issues an
+// agent-scope release fence -- which writes the L2's dirty lines back so the
+// tile is visible from every XCD -- before storing the epoch into the
+// tile's flag word.  Consumer side: one thread reads the flag until it
+// equals the epoch, issues an agent-scope (or, for flags written by a copy
+// engine or the command processor, system-scope) acquire fence, and the
+// workgroup meets at a barrier before reading the tile.
+//
+// The pages (SC24 abstract; mKernel, section on persistent kernels and
+// tile/chunk overlap) prescribe GPU-initiated, tile-granular publication but
+// no memory-ordering scheme; this epoch/flag protocol is this library's.
+#pragma once
+
+#include "common.hpp"
+
+namespace hocf {
+
+__device__ __forceinline__ void report_status(const SyncArgs& s, uint32_t code) {
+  if (s.status) atomicCAS(s.status, 0u, code);
+}
+
+// Called by one thread after a __syncthreads() that follows the tile stores.
+__device__ __forceinline__ void release_flag(uint32_t* flag, uint32_t epoch) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t load_flag_agent(const uint32_t* flag) {
+  return __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t load_flag_system(const uint32_t* flag) {
+  return __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void acquire_system() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, ""); }
+
+// Ticket counters live in the caller's workspace:
+//   ws[0 .. kNumQueues-1]  one claim counter per queue
+//   ws[kNumQueues]         count of workgroups that have finished
+//   ws[kNumQueues+1 ..]    operator-specific counters (reset by their users)
+constexpr int kWsDone = kNumQueues;
+constexpr int kWsExtra = kNumQueues + 1;
+
+// Queue q holds the contiguous work range [qbeg(q), qbeg(q+1)) of `total`
+// items.  A workgroup drains its home queue (blockIdx mod 8: workgroups are
+// dispatched to the XCDs round-robin, so a queue's items share one XCD's L2)
+// and then steals from the others in order.
+__device__ __forceinline__ int64_t queue_begin(int q, int64_t total) {
+  return (total * q) / kNumQueues;
+}
+
+// Claims the next item for this workgroup, or returns -1 when every queue is
+// empty.  Must be called by all threads of the workgroup (thread 0 claims,
+// the result is broadcast through LDS).  `qcur` is per-workgroup state
+// (shared memory) that starts at 0.
+__device__ __forceinline__ int64_t claim_item(uint32_t* ws, int64_t total, int* s_qcur,
+                                              int64_t* s_item) {
+  if (threadIdx.x == 0) {
+    int64_t got = -1;
+    const int home = (int)(blockIdx.x % kNumQueues);
+    while (*s_qcur < kNumQueues) {
+      const int q = (home + *s_qcur) % kNumQueues;
+      const int64_t b = queue_begin(q, total), e = queue_begin(q + 1, total);
+      const uint32_t t = __hip_atomic_fetch_add(&ws[q], 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      if ((int64_t)t < e - b) { got = b + t; break; }
+      ++*s_qcur;
+    }
+    *s_item = got;
+  }
+  __syncthreads();
+  const int64_t it = *s_item;
+  __syncthreads();
+  return it;
+}
+
+// Every workgroup calls this once when it has stopped claiming.  The last
+// one resets the queue counters and the done counter, leaving the workspace
+// zeroed for the next call (stream order makes the reset visible to it).
+__device__ __forceinline__ void finish_workgroup(uint32_t* ws) {
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&ws[kWsDone], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      for (int q = 0; q < kNumQueues; ++q)
+        __hip_atomic_store(&ws[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ws[kWsDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t now_ticks() { return (uint64_t)wall_clock64(); }
+
+// Bounded wait state: deadline in wall_clock64() ticks.
+struct Deadline {
+  uint64_t start, ticks;
+  __device__ __forceinline__ bool expired() const { return now_ticks() - start > ticks; }
+};
+
+}  // namespace hocf

@@ -1,0 +1,236 @@
+"""Python binding of libhocf.so (argument marshalling only).
+
+The functions below carry the names and arguments of the C entry points in
+``include/hocf.h``; every step of the computation runs in the library's HIP
+kernels.  Tensor arguments may be ``torch`` tensors (their device pointer is
+passed) or raw integer addresses.  PyTorch is used only to own device memory
+and streams.  Importing this module does not touch the GPU; the first call
+loads the library and fails loudly if it has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhocf.so")
+
+HOCF_OK = 0
+HOCF_ERR_INVALID_ARG = 1
+HOCF_ERR_UNSUPPORTED = 2
+HOCF_ERR_HIP = 3
+HOCF_ERR_TIMEOUT = 4
+HOCF_ERR_ABORTED = 5
+HOCF_ERR_BAD_INDEX = 6
+HOCF_ERR_PROTOCOL = 7
+HOCF_F32 = 0
+HOCF_BF16 = 1
+HOCF_MAX_P = 16
+
+EXPORTED = [
+    "hocf_gemm_rs", "hocf_gemm_rs_workspace_bytes",
+    "hocf_gemv_ar", "hocf_gemv_ar_workspace_bytes",
+    "hocf_ag_gemm", "hocf_ag_gemm_workspace_bytes",
+    "hocf_embbag_a2a", "hocf_embbag_a2a_workspace_bytes",
+    "hocf_status_string", "hocf_last_error", "hocf_abi_version",
+]
+
+
+class hocf_window(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("flags", ctypes.c_void_p)]
+
+
+class hocf_sync(ctypes.Structure):
+    _fields_ = [("epoch", ctypes.c_uint32), ("status", ctypes.c_void_p),
+                ("abort_flag", ctypes.c_void_p), ("spin_timeout_ns", ctypes.c_uint64),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class HocfError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)} ({status}): {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with computation_collective_amd/build.py "
+                               "(the fused operators have no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        i, i64, vp, sz, u32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32
+        W = ctypes.POINTER(hocf_window)
+        S = ctypes.POINTER(hocf_sync)
+        L.hocf_gemm_rs.argtypes = [i, i, i, i, i, i, i, vp, vp, W, vp, i, i, S, vp]
+        L.hocf_gemm_rs_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.hocf_gemv_ar.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, W, i, S, vp]
+        L.hocf_gemv_ar_workspace_bytes.argtypes = [i, i, i]
+        L.hocf_ag_gemm.argtypes = [i, i, i, i, i, i, vp, vp, vp, vp, i, i, S, vp]
+        L.hocf_ag_gemm_workspace_bytes.argtypes = [i]
+        L.hocf_embbag_a2a.argtypes = [i, i64, i, i, i, i, vp, vp, vp, W, i, S, vp]
+        L.hocf_embbag_a2a_workspace_bytes.argtypes = []
+        for f in ("hocf_gemm_rs", "hocf_gemv_ar", "hocf_ag_gemm", "hocf_embbag_a2a"):
+            getattr(L, f).restype = i
+        for f in ("hocf_gemm_rs_workspace_bytes", "hocf_gemv_ar_workspace_bytes",
+                  "hocf_ag_gemm_workspace_bytes", "hocf_embbag_a2a_workspace_bytes"):
+            getattr(L, f).restype = sz
+        L.hocf_status_string.argtypes = [i]
+        L.hocf_status_string.restype = ctypes.c_char_p
+        L.hocf_last_error.argtypes = []
+        L.hocf_last_error.restype = ctypes.c_char_p
+        L.hocf_abi_version.restype = i
+        _lib = L
+    return _lib
+
+
+def ptr(x) -> int | None:
+    """Device address of a torch tensor (or an int / None passed through)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def windows(pairs) -> ctypes.Array:
+    """Host array of hocf_window from [(data, flags), ...]."""
+    arr = (hocf_window * len(pairs))()
+    for k, (d, f) in enumerate(pairs):
+        arr[k].data = ptr(d)
+        arr[k].flags = ptr(f)
+    return arr
+
+
+def sync(epoch, workspace, workspace_bytes, status=None, abort_flag=None, spin_timeout_ns=0):
+    s = hocf_sync()
+    s.epoch = epoch
+    s.status = ptr(status)
+    s.abort_flag = ptr(abort_flag)
+    s.spin_timeout_ns = spin_timeout_ns
+    s.workspace = ptr(workspace)
+    s.workspace_bytes = workspace_bytes
+    return s
+
+
+def status_string(st: int) -> str:
+    return lib().hocf_status_string(st).decode()
+
+
+def last_error() -> str:
+    return lib().hocf_last_error().decode()
+
+
+def check(st: int) -> None:
+    if st != HOCF_OK:
+        raise HocfError(st, last_error())
+
+
+def hocf_abi_version() -> int:
+    return lib().hocf_abi_version()
+
+
+def hocf_gemm_rs_workspace_bytes(P, M, N, tile_m, tile_n) -> int:
+    return lib().hocf_gemm_rs_workspace_bytes(P, M, N, tile_m, tile_n)
+
+
+def hocf_gemv_ar_workspace_bytes(P, N, tile_n) -> int:
+    return lib().hocf_gemv_ar_workspace_bytes(P, N, tile_n)
+
+
+def hocf_ag_gemm_workspace_bytes(P) -> int:
+    return lib().hocf_ag_gemm_workspace_bytes(P)
+
+
+def hocf_embbag_a2a_workspace_bytes() -> int:
+    return lib().hocf_embbag_a2a_workspace_bytes()
+
+
+def hocf_gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, out, tile_m, tile_n, sync_,
+                 stream=None) -> int:
+    return lib().hocf_gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, ptr(A), ptr(W), win, ptr(out),
+                              tile_m, tile_n, ctypes.byref(sync_), _stream(stream))
+
+
+def hocf_gemv_ar(P, Mb, N, K, in_dt, slot_dt, out_dt, x, W, part, part_flags, win, tile_n, sync_,
+                 stream=None) -> int:
+    return lib().hocf_gemv_ar(P, Mb, N, K, in_dt, slot_dt, out_dt, ptr(x), ptr(W), ptr(part),
+                              ptr(part_flags), win, tile_n, ctypes.byref(sync_), _stream(stream))
+
+
+def hocf_ag_gemm(P, Mc, N, K, in_dt, out_dt, A_gathered, chunk_flags, W, out, tile_m, tile_n,
+                 sync_, stream=None) -> int:
+    return lib().hocf_ag_gemm(P, Mc, N, K, in_dt, out_dt, ptr(A_gathered), ptr(chunk_flags),
+                              ptr(W), ptr(out), tile_m, tile_n, ctypes.byref(sync_), _stream(stream))
+
+
+def hocf_embbag_a2a(T, R, D, B, L, P, tables, indices, offsets, win, tile_bags, sync_,
+                    stream=None) -> int:
+    return lib().hocf_embbag_a2a(T, R, D, B, L, P, ptr(tables), ptr(indices), ptr(offsets), win,
+                                 tile_bags, ctypes.byref(sync_), _stream(stream))
+
+
+# --------------------------------------------------------------- chunk releaser
+# The AllGather side of hocf_ag_gemm: chunk flags written by the command
+# processor of another stream (no compute unit involved), in a given order.
+
+_hip = None
+
+
+def _hip_runtime():
+    global _hip
+    if _hip is None:
+        import torch  # noqa: F401  (loads the HIP runtime torch was built with)
+        for name in ("libamdhip64.so", "libamdhip64.so.7", "libamdhip64.so.6"):
+            try:
+                _hip = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if _hip is None:
+            raise RuntimeError("HIP runtime library not found")
+        _hip.hipStreamWriteValue32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32,
+                                               ctypes.c_uint]
+        _hip.hipStreamWriteValue32.restype = ctypes.c_int
+        _hip.hipStreamWaitValue32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32,
+                                              ctypes.c_uint, ctypes.c_uint32]
+        _hip.hipStreamWaitValue32.restype = ctypes.c_int
+    return _hip
+
+
+HIP_STREAM_WAIT_VALUE_GTE = 0x0
+
+
+def stream_write_value32(stream, address: int, value: int) -> None:
+    """Enqueue a 32-bit write of `value` at device address `address` on `stream`."""
+    rc = _hip_runtime().hipStreamWriteValue32(_stream(stream), address, value, 0)
+    if rc != 0:
+        raise RuntimeError(f"hipStreamWriteValue32 failed ({rc})")
+
+
+def stream_wait_value32(stream, address: int, value: int) -> None:
+    """Enqueue a wait on `stream` until the word at `address` is >= `value`."""
+    rc = _hip_runtime().hipStreamWaitValue32(_stream(stream), address, value,
+                                             HIP_STREAM_WAIT_VALUE_GTE, 0xFFFFFFFF)
+    if rc != 0:
+        raise RuntimeError(f"hipStreamWaitValue32 failed ({rc})")
+
+
+def release_chunks(stream, chunk_flags, order, epoch) -> None:
+    """Set chunk_flags[c] = epoch for c in `order`, each after the previous, on `stream`."""
+    base = ptr(chunk_flags)
+    for c in order:
+        stream_write_value32(stream, base + 4 * int(c), epoch)

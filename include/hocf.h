@@ -1,0 +1,207 @@
+/*
+ * hocf — computations fused with their collective epilogue, on one MI355X.
+ *
+ * C ABI of libhocf.so.  Four operators, each one GPU's share of a P-way
+ * tensor-parallel (or model-parallel) step with the P logical shards'
+ * receive windows in local HBM:
+ *
+ *   hocf_gemm_rs     GEMM + ReduceScatter   (mKernel news item "GPU-vezérelt
+ *                    kommunikációval gyorsítják az AI-betanítást a kutatók",
+ *                    section on its five fused kernels)
+ *   hocf_gemv_ar     GEMV + AllReduce       ("Optimizing Distributed ML
+ *                    Communication with Fused Computation-Collective
+ *                    Operations", SC24, abstract)
+ *   hocf_ag_gemm     AllGather + GEMM       (mKernel news item, same section)
+ *   hocf_embbag_a2a  embedding bag + All-to-All (SC24 abstract)
+ *
+ * The method (SC24 abstract; mKernel, section on persistent kernels and
+ * tile/chunk overlap): the workgroups of one kernel each finish an output
+ * tile and immediately publish it to its destination's receive window with
+ * a per-tile ready flag, while other workgroups of the same kernel are still
+ * computing; the collective's consumer side (a fixed rank-order reduction,
+ * or a gather-gated GEMM) consumes tiles as their flags arrive.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every tensor, window, flag array, workspace and status pointer
+ * is a device pointer on the current HIP device, 16-byte aligned, except
+ * sync->abort_flag (device or host-pinned memory) and the hocf_window arrays
+ * themselves (host memory, read during the call).  All tensors are dense
+ * row-major.  bf16 tensors hold bfloat16 bit patterns (uint16).
+ *
+ * Streams.  A call validates its arguments, enqueues its kernel on `stream`
+ * (a hipStream_t; NULL = the null stream) and returns.  Results, windows and
+ * flags are valid once the stream has reached the kernel's end.  The library
+ * never allocates, frees or synchronises in a call, and keeps no pointer
+ * after the kernel ends.  The caller owns every buffer.
+ *
+ * Synchronous errors.  An invalid shape, an unsupported combination, a NULL
+ * or misaligned pointer, a zero epoch or a short workspace returns an error
+ * code BEFORE anything is enqueued; hocf_last_error() then describes it.
+ * A launch failure returns HOCF_ERR_HIP.
+ *
+ * Asynchronous errors.  A wait that exceeds its time limit, an abort request
+ * or an out-of-range embedding index is recorded in *sync->status (if
+ * non-NULL) by the first workgroup that meets it (compare-and-swap from 0);
+ * every workgroup still exits, and the outputs are then unspecified.  The
+ * caller zeroes *status before the call and reads it after.
+ *
+ * Flags.  Flag words are uint32 and hold an epoch: a word equals
+ * sync->epoch once the data it guards is complete and visible device-wide
+ * (release by the producer, acquire by the consumer, agent scope).  Each
+ * call must use an epoch different from the previous call on the same flag
+ * arrays, so flags never need resetting.
+ *
+ * Workspace.  Scheduler counters.  The caller allocates at least the size
+ * the matching *_workspace_bytes() query returns, zeroes it ONCE, and may
+ * then reuse it for any number of calls: every call leaves it zeroed again.
+ * Calls that may run concurrently need separate workspaces.
+ */
+#ifndef HOCF_H
+#define HOCF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HOCF_ABI_VERSION 1
+#define HOCF_MAX_P 16 /* largest shard count any operator accepts */
+
+typedef enum hocf_status {
+    HOCF_OK = 0,
+    HOCF_ERR_INVALID_ARG = 1, /* bad shape, pointer, alignment, epoch or workspace */
+    HOCF_ERR_UNSUPPORTED = 2, /* valid, but no kernel for this combination */
+    HOCF_ERR_HIP = 3,         /* a HIP runtime call failed (launch, attribute query) */
+    HOCF_ERR_TIMEOUT = 4,     /* (async) a flag wait exceeded sync->spin_timeout_ns */
+    HOCF_ERR_ABORTED = 5,     /* (async) *sync->abort_flag became nonzero during a wait */
+    HOCF_ERR_BAD_INDEX = 6,   /* (async) an embedding index outside [0, R) was skipped */
+    HOCF_ERR_PROTOCOL = 7     /* (async) a reducer found a partial's flag not set */
+} hocf_status;
+
+typedef enum hocf_dtype { HOCF_F32 = 0, HOCF_BF16 = 1 } hocf_dtype;
+
+/* One destination's receive window: its data buffer and its flag words. */
+typedef struct hocf_window {
+    void* data;
+    uint32_t* flags;
+} hocf_window;
+
+typedef struct hocf_sync {
+    uint32_t epoch;               /* nonzero; differs from the previous call on the same flags */
+    uint32_t* status;             /* nullable device word; first asynchronous error code */
+    const uint32_t* abort_flag;   /* nullable device or host-pinned word; nonzero stops waits */
+    uint64_t spin_timeout_ns;     /* bound of every flag wait; 0 = 1 second */
+    void* workspace;              /* scheduler counters, zeroed once by the caller */
+    size_t workspace_bytes;
+} hocf_sync;
+
+/* ------------------------------------------------------------------------
+ * GEMM + ReduceScatter.
+ *
+ * Computes, for every logical shard p < P, the partial C_p = A_p . W_p
+ * (M x N, fp32 accumulation) and reduce-scatters it: chunk r (rows
+ * [r*Mc, (r+1)*Mc), Mc = M/P) of every C_p goes to destination r, slot p,
+ * and destination r folds its P slots in rank order p = 0..P-1 in fp32,
+ * rounding once to out_dt.  Each workgroup that finishes a tile of C_p
+ * publishes it into win[r] (slot_dt) and releases its flag; the last of the
+ * P producers of an output tile reduces it, while other workgroups still
+ * compute.
+ *
+ *   A    [P][M][K] in_dt          W  [P][K][N] in_dt
+ *   win  host array of P windows; win[r].data = [P src][Mc][N] slot_dt,
+ *        win[r].flags = [P src][Tc] with Tc = ceil(Mc/tile_m) * ceil(N/tile_n);
+ *        flag (p, t) = epoch once tile t (row-major over the chunk's tile
+ *        grid) of C_p's chunk r is in slot p of window r
+ *   out  [M][N] out_dt  (= [P][Mc][N]: destination r's reduced chunk at rows r*Mc)
+ *
+ * Supported: (in, slot, out) = (F32, F32, F32) with tile 64x64;
+ *            (BF16, F32 or BF16, BF16 or F32) with tiles 256x256 and 128x128.
+ * Requires M % P == 0; N and K multiples of 8 (bf16) or 4 (fp32).  Tiles may
+ * be ragged at the end of a chunk, of N and of K.  M, N or K may be 0.
+ * ---------------------------------------------------------------------- */
+hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                         hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
+                         void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream);
+size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n);
+
+/* ------------------------------------------------------------------------
+ * GEMV + AllReduce.
+ *
+ * y_p = x_p . W_p (Mb x N, fp32 accumulation) for every shard p; the
+ * AllReduce folds y_0..y_{P-1} in rank order in fp32, rounds once to out_dt
+ * and writes the same bits into every one of the P receive windows.
+ *
+ *   x     [P][Mb][K] in_dt        W  [P][K][N] in_dt
+ *   part  [P][Mb][N] slot_dt: the published partials
+ *   part_flags [P][NT], NT = ceil(N/tile_n): epoch once partial tile (p, j) is in part
+ *   win   host array of P windows; win[q].data = [Mb][N] out_dt,
+ *         win[q].flags = [NT]: epoch once column tile j of the sum is in window q
+ *
+ * Supported: in BF16, slot F32 or BF16, out BF16 or F32; 1 <= Mb <= 8;
+ * tile_n in {128, 256, 512}; N and K multiples of 8.
+ * ---------------------------------------------------------------------- */
+hocf_status hocf_gemv_ar(int P, int Mb, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                         hocf_dtype out_dt, const void* x, const void* W, void* part,
+                         uint32_t* part_flags, const hocf_window* win, int tile_n,
+                         const hocf_sync* sync, void* stream);
+size_t hocf_gemv_ar_workspace_bytes(int P, int N, int tile_n);
+
+/* ------------------------------------------------------------------------
+ * AllGather + GEMM.
+ *
+ * out = A_g . W where A_g = [chunk 0; ...; chunk P-1] (rank order).  Chunk c
+ * of A_gathered (rows [c*Mc, (c+1)*Mc)) may be read only once
+ * chunk_flags[c] == epoch; chunks are released in any order (by another
+ * stream, a copy engine or a peer) and the kernel's workgroups claim output
+ * tiles of whichever chunks have arrived.  The result does not depend on the
+ * release order.  A chunk that never arrives makes the waiting workgroups
+ * give up after spin_timeout_ns with HOCF_ERR_TIMEOUT.
+ *
+ *   A_gathered [P][Mc][K] in_dt   chunk_flags [P] (device or host-pinned)
+ *   W [K][N] in_dt                out [P*Mc][N] out_dt
+ *
+ * Supported: in BF16, out BF16 or F32, tiles 256x256 and 128x128;
+ * N and K multiples of 8.
+ * ---------------------------------------------------------------------- */
+hocf_status hocf_ag_gemm(int P, int Mc, int N, int K, hocf_dtype in_dt, hocf_dtype out_dt,
+                         const void* A_gathered, const uint32_t* chunk_flags, const void* W,
+                         void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream);
+size_t hocf_ag_gemm_workspace_bytes(int P);
+
+/* ------------------------------------------------------------------------
+ * Embedding bag + All-to-All.
+ *
+ * pooled(t, b) = sum of table t's rows listed by bag (t, b), fp32, added in
+ * index order from +0.0 (an empty bag pools to zeros).  Bag b goes to
+ * destination d = b / Bd (Bd = B/P), slot s = b mod Bd.
+ *
+ *   tables  [T][R][D] fp32
+ *   indices int32: fixed-length bags [T][B][L] when offsets == NULL, else
+ *           CSR: bag (t, b) = indices[offsets[t*B+b] .. offsets[t*B+b+1])
+ *   offsets NULL or int64 [T*B + 1], non-decreasing, offsets[0] == 0
+ *   win     host array of P windows; win[d].data = [Bd][T][D] fp32,
+ *           win[d].flags = [T][NJ], NJ = ceil(Bd/tile_bags): epoch once bags
+ *           [j*tile_bags, (j+1)*tile_bags) of table t are in window d
+ *
+ * An index outside [0, R) is skipped (the bag sums its other rows) and
+ * HOCF_ERR_BAD_INDEX is recorded in *status.
+ * Supported: D a multiple of 4 up to 512; B % P == 0; tile_bags in [1, 4096].
+ * ---------------------------------------------------------------------- */
+hocf_status hocf_embbag_a2a(int T, int64_t R, int D, int B, int L, int P, const float* tables,
+                            const int32_t* indices, const int64_t* offsets,
+                            const hocf_window* win, int tile_bags, const hocf_sync* sync,
+                            void* stream);
+size_t hocf_embbag_a2a_workspace_bytes(void);
+
+/* ---------------------------------------------------------------------- */
+const char* hocf_status_string(hocf_status s); /* static string, never NULL */
+const char* hocf_last_error(void);             /* detail of this thread's last error */
+int hocf_abi_version(void);                    /* HOCF_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HOCF_H */

@@ -12,3 +12,17 @@ if TESTS not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: full-size workloads")
+
+
+def _ensure_built():
+    """Tests load what is built; they build only when nothing is there."""
+    import importlib
+    lib = os.path.join(ROOT, "computation_collective_amd", "libhocf.so")
+    if not os.path.exists(lib):
+        importlib.import_module("computation_collective_amd.build").build()
+    olib = os.path.join(ROOT, "oracle", "liboracle.so")
+    if not os.path.exists(olib):
+        importlib.import_module("oracle.build").build()
+
+
+_ensure_built()

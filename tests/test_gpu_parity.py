@@ -1,0 +1,441 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Values: normwise relative error <= 2e-2 for bf16 inputs with fp32
+accumulation, <= 1e-5 for fp32; integer-valued inputs, routing, indices,
+flags and the embedding sums: bit-exact.  Small cases span several tiles and
+a ragged tail in every dimension; the full-size workloads run in the launch
+configuration the bench times and are compared on sampled outputs plus
+properties that hold at any size.  Every output buffer is NaN-poisoned first,
+so an element the kernels fail to write cannot pass.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from computation_collective_amd import buffers as bf
+from computation_collective_amd import configs as cfgs
+from computation_collective_amd import hocf
+from computation_collective_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+F32, BF16 = 0, 1
+TOL = {F32: 1e-5, BF16: 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def val(a, dt):
+    return (gen.bf16_decode(a) if dt == BF16 else a).astype(np.float64)
+
+
+def relerr(g, o):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    assert not np.isnan(g).any(), "unwritten (NaN) elements"
+    return float(np.max(np.abs(g - o)) / max(np.max(np.abs(o)), 1e-30))
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ====================================================================== GEMM + RS
+
+def _gemm_rs(P, Mc, N, K, in_dt, slot_dt, out_dt, tm, tn, seed=0, dist=None):
+    M = P * Mc
+    if dist is None:
+        dist = dict(dist_a=("normal", 1.0), dist_w=("normal", 0.02)) if in_dt == BF16 else \
+            dict(dist_a=("uniform",), dist_w=("uniform",))
+    A, W = gen.gemm_rs_inputs(P, M, N, K, in_dt, seed=seed, **dist)
+    run = bf.GemmRS(P, M, N, K, in_dt, slot_dt, out_dt, tm, tn, A, W)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    slots, out = oracle.gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, A, W)
+    return run, slots, out
+
+
+def test_gemm_rs_tiny_config():
+    c = cfgs.GEMM_RS_TINY
+    say(f"gemm_rs {c.name}")
+    run, slots, out = _gemm_rs(c.P, c.M // c.P, c.N, c.K, F32, F32, F32, c.tile_m, c.tile_n)
+    assert relerr(bf.to_host(run.out, F32), out) <= TOL[F32]
+    assert relerr(bf.to_host(run.win_data, F32), slots) <= TOL[F32]
+    assert torch.all(run.win_flags == run.epoch)
+    assert torch.all(run.ws == 0), "workspace must be left zeroed"
+
+
+RAGGED = [
+    (3, 100, 200, 76, F32, F32, F32, 64, 64),
+    (4, 300, 328, 136, BF16, F32, BF16, 256, 256),
+    (4, 300, 328, 136, BF16, BF16, BF16, 256, 256),
+    (3, 300, 328, 136, BF16, F32, F32, 128, 128),
+    (3, 300, 328, 136, BF16, BF16, F32, 128, 128),
+    (2, 513, 1032, 72, BF16, F32, BF16, 256, 256),
+]
+
+
+@pytest.mark.parametrize("P,Mc,N,K,ind,sdt,odt,tm,tn", RAGGED)
+def test_gemm_rs_ragged(P, Mc, N, K, ind, sdt, odt, tm, tn):
+    say(f"gemm_rs ragged P={P} Mc={Mc} N={N} K={K} dt={ind}{sdt}{odt} tile={tm}x{tn}")
+    run, slots, out = _gemm_rs(P, Mc, N, K, ind, sdt, odt, tm, tn, seed=P + K)
+    assert relerr(val(bf.to_host(run.out, odt), odt), val(out, odt)) <= TOL[ind]
+    assert relerr(val(bf.to_host(run.win_data, sdt), sdt), val(slots, sdt)) <= TOL[ind]
+    assert torch.all(run.win_flags == run.epoch)
+    assert torch.all(run.ws == 0)
+
+
+@pytest.mark.parametrize("sdt,odt,tm", [(F32, BF16, 256), (BF16, BF16, 256), (F32, F32, 128)])
+def test_gemm_rs_integer_bit_exact(sdt, odt, tm):
+    """Entries in {-2..2}: every partial and fold is an exact integer, so the HIP
+    result equals the oracle bit for bit (bf16 rounding included)."""
+    say(f"gemm_rs integer P=4 Mc=300 N=328 K=392 slot={sdt} out={odt} tile={tm}")
+    ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    run, slots, out = _gemm_rs(4, 300, 328, 392, BF16, sdt, odt, tm, tm, seed=9, dist=ints)
+    np.testing.assert_array_equal(bf.to_host(run.out, odt), out)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, sdt), slots)
+
+
+def test_gemm_rs_fp32_integer_bit_exact():
+    say("gemm_rs fp32 integer P=4 256x256x256 tile 64")
+    ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    run, slots, out = _gemm_rs(4, 64, 256, 256, F32, F32, F32, 64, 64, seed=3, dist=ints)
+    np.testing.assert_array_equal(bf.to_host(run.out, F32), out)
+
+
+def test_gemm_rs_run_to_run_identical():
+    say("gemm_rs determinism: 50 calls on one buffer set, bit-identical")
+    P, Mc, N, K = 4, 512, 512, 256
+    A, W = gen.gemm_rs_inputs(P, P * Mc, N, K, BF16, seed=1)
+    run = bf.GemmRS(P, P * Mc, N, K, BF16, F32, BF16, 256, 256, A, W)
+    run.run()
+    sync()
+    ref = run.out.clone()
+    for _ in range(50):
+        run.poison()
+        run.run()
+    sync()
+    assert torch.equal(run.out, ref)
+    assert run.status_value() == 0
+
+
+@pytest.mark.parametrize("sdt", [F32, BF16])
+def test_gemm_rs_full_mlpdown(sdt):
+    c = cfgs.GEMM_RS_MLP
+    say(f"gemm_rs full {c.name} slot={sdt} (sampled)")
+    A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, BF16, seed=0)
+    run = bf.GemmRS(c.P, c.M, c.N, c.K, BF16, sdt, c.out_dt, c.tile_m, c.tile_n, A, W)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    assert torch.all(run.win_flags == run.epoch)
+    assert not torch.isnan(run.out.view(torch.bfloat16)).any()
+    rng = np.random.default_rng(123)
+    n = 3000
+    ms = rng.integers(0, c.M, n)
+    ns = rng.integers(0, c.N, n)
+    # always include tile corners
+    ms[:4] = [0, c.M - 1, 1023, 1024]
+    ns[:4] = [0, c.N - 1, 255, 256]
+    sv, ov = oracle.gemm_rs_points(c.P, c.M, c.N, c.K, BF16, sdt, c.out_dt, A, W, ms, ns)
+    out = bf.to_host(run.out, BF16)
+    assert relerr(val(out[ms, ns], BF16), val(ov, BF16)) <= TOL[BF16]
+    Mc = c.M // c.P
+    win = bf.to_host(run.win_data, sdt)       # [r][p][i][n]
+    gs = win[ms // Mc, :, ms % Mc, ns]        # [n][P]
+    assert relerr(val(gs, sdt), val(sv, sdt)) <= TOL[BF16]
+
+
+# ====================================================================== GEMV + AR
+
+def _gemv(P, Mb, N, K, sdt, odt, tn, seed=0, dist=None):
+    dist = dist or {}
+    x, W = gen.gemv_ar_inputs(P, Mb, N, K, seed=seed, **dist)
+    run = bf.GemvAR(P, Mb, N, K, BF16, sdt, odt, tn, x, W)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    part, win = oracle.gemv_ar(P, Mb, N, K, BF16, sdt, odt, x, W)
+    return run, part, win
+
+
+def test_gemv_ar_decode_config():
+    c = cfgs.GEMV_AR_DECODE
+    say(f"gemv_ar {c.name}")
+    run, part, win = _gemv(c.P, c.Mb, c.N, c.K, c.slot_dt, c.out_dt, c.tile_n)
+    got = bf.to_host(run.win_data, c.out_dt)
+    for q in range(1, c.P):
+        np.testing.assert_array_equal(got[q], got[0])     # replicas bit-identical
+    assert relerr(val(got, c.out_dt), val(win, c.out_dt)) <= TOL[BF16]
+    assert relerr(val(bf.to_host(run.part, c.slot_dt), c.slot_dt), part) <= TOL[BF16]
+    assert torch.all(run.part_flags == run.epoch) and torch.all(run.win_flags == run.epoch)
+    assert torch.all(run.ws == 0)
+
+
+@pytest.mark.parametrize("P,Mb,N,K,sdt,odt,tn", [
+    (3, 3, 328, 200, F32, BF16, 128), (5, 1, 1000, 1040, BF16, BF16, 256),
+    (2, 8, 1032, 96, F32, F32, 512), (8, 5, 2056, 520, BF16, F32, 256),
+])
+def test_gemv_ar_ragged(P, Mb, N, K, sdt, odt, tn):
+    say(f"gemv_ar ragged P={P} Mb={Mb} N={N} K={K} slot={sdt} out={odt} tile_n={tn}")
+    run, part, win = _gemv(P, Mb, N, K, sdt, odt, tn, seed=P * N)
+    got = bf.to_host(run.win_data, odt)
+    for q in range(1, P):
+        np.testing.assert_array_equal(got[q], got[0])
+    assert relerr(val(got, odt), val(win, odt)) <= TOL[BF16]
+
+
+def test_gemv_ar_integer_bit_exact():
+    say("gemv_ar integer P=8 Mb=4 N=2048 K=1024")
+    ints = dict(dist_x=("int", -2, 2), dist_w=("int", -2, 2))
+    run, part, win = _gemv(8, 4, 2048, 1024, F32, BF16, 256, seed=2, dist=ints)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, BF16), win)
+    np.testing.assert_array_equal(bf.to_host(run.part, F32), part)
+
+
+# ====================================================================== AG + GEMM
+
+def _ag_inputs(P, Mc, N, K, seed=0):
+    return gen.ag_gemm_inputs(P, Mc, N, K, seed=seed)
+
+
+@pytest.mark.parametrize("P,Mc,N,K,tm,odt", [(3, 300, 328, 136, 128, BF16), (4, 300, 520, 200, 256, F32),
+                                             (8, 128, 256, 64, 128, BF16)])
+def test_ag_gemm_release_orders(P, Mc, N, K, tm, odt):
+    say(f"ag_gemm P={P} Mc={Mc} N={N} K={K} tile={tm} out={odt}: 3 release orders")
+    chunks, W, order = _ag_inputs(P, Mc, N, K, seed=P + N)
+    run = bf.AgGemm(P, Mc, N, K, odt, tm, tm, chunks, W)
+    outs = []
+    orders = [order, np.arange(P), np.arange(P)[::-1]]
+    for k, o in enumerate(orders):
+        run.poison()
+        rs = run.run_released(o, release_first=(k == 1))
+        rs.synchronize()
+        sync()
+        assert run.status_value() == 0
+        outs.append(run.out.clone())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0]), "output depends on the release order"
+    _, want = oracle.ag_gemm(P, Mc, N, K, BF16, odt, list(chunks), W)
+    assert relerr(val(bf.to_host(outs[0], odt), odt), val(want, odt)) <= TOL[BF16]
+    assert torch.all(run.ws == 0)
+
+
+def test_ag_gemm_integer_bit_exact():
+    say("ag_gemm integer P=4 Mc=256 N=512 K=512")
+    P, Mc, N, K = 4, 256, 512, 512
+    chunks, W, order = gen.ag_gemm_inputs(P, Mc, N, K, seed=5, dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    run = bf.AgGemm(P, Mc, N, K, BF16, 256, 256, chunks, W)
+    run.poison()
+    run.run_released(order).synchronize()
+    sync()
+    _, want = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
+    np.testing.assert_array_equal(bf.to_host(run.out, BF16), want)
+
+
+def test_ag_gemm_late_release():
+    """Chunks start NaN-poisoned; a second stream first spins for ~20 ms, then
+    copies the real chunks in and sets their flags, so the kernel is already
+    running and waiting when they arrive: any read before a chunk's flag shows
+    up as NaN in the output."""
+    P, Mc, N, K = 4, 256, 384, 256
+    say(f"ag_gemm late release P={P} Mc={Mc} N={N} K={K}")
+    chunks, W, order = _ag_inputs(P, Mc, N, K, seed=11)
+    run = bf.AgGemm(P, Mc, N, K, BF16, 128, 128, chunks, W)
+    real = run.A.clone()
+    bf.nan_fill(run.A)
+    run.poison()
+    sync()
+    rel = torch.cuda.Stream()
+    s = run.next_sync(spin_timeout_ns=2_000_000_000)
+    with torch.cuda.stream(rel):
+        torch.cuda._sleep(50_000_000)
+        for c in order:
+            run.A[c].copy_(real[c])
+            hocf.stream_write_value32(rel, hocf.ptr(run.chunk_flags) + 4 * int(c), s.epoch)
+    hocf.check(run.call(s, torch.cuda.current_stream()))
+    rel.synchronize()
+    sync()
+    assert run.status_value() == 0
+    _, want = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
+    assert relerr(val(bf.to_host(run.out, BF16), BF16), val(want, BF16)) <= TOL[BF16]
+
+
+def test_ag_gemm_withheld_chunk_times_out():
+    """A chunk whose flag never arrives: the waiting workgroups give up after the
+    (tiny) time limit, record HOCF_ERR_TIMEOUT and exit; the other chunks' tiles
+    are still right, and the next call with all chunks succeeds."""
+    P, Mc, N, K = 4, 256, 256, 128
+    say(f"ag_gemm withheld chunk (timeout 20 ms) P={P}")
+    chunks, W, _ = _ag_inputs(P, Mc, N, K, seed=4)
+    run = bf.AgGemm(P, Mc, N, K, BF16, 128, 128, chunks, W)
+    run.poison()
+    rs = run.run_released([0, 2, 3], spin_timeout_ns=20_000_000)
+    rs.synchronize()
+    sync()
+    assert run.status_value() == hocf.HOCF_ERR_TIMEOUT
+    _, want = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
+    got = val(bf.to_host(run.out, BF16), BF16)
+    for c in (0, 2, 3):
+        rows = slice(c * Mc, (c + 1) * Mc)
+        assert relerr(got[rows], val(want, BF16)[rows]) <= TOL[BF16]
+    assert torch.all(run.ws == 0), "a timed-out call must still leave the workspace zeroed"
+    run.status.zero_()
+    run.poison()
+    run.run_released([3, 1, 0, 2]).synchronize()
+    sync()
+    assert run.status_value() == 0
+    assert relerr(val(bf.to_host(run.out, BF16), BF16), val(want, BF16)) <= TOL[BF16]
+
+
+def test_ag_gemm_abort():
+    P, Mc, N, K = 2, 128, 128, 64
+    say("ag_gemm abort word set, chunk withheld")
+    chunks, W, _ = _ag_inputs(P, Mc, N, K, seed=6)
+    run = bf.AgGemm(P, Mc, N, K, BF16, 128, 128, chunks, W)
+    abort = torch.ones(1, dtype=torch.int32, device="cuda")
+    run.run_released([0], abort_flag=abort, spin_timeout_ns=2_000_000_000).synchronize()
+    sync()
+    assert run.status_value() == hocf.HOCF_ERR_ABORTED
+    assert torch.all(run.ws == 0)
+
+
+def test_ag_gemm_full_colpar():
+    c = cfgs.AG_GEMM_COL
+    say(f"ag_gemm full {c.name} (sampled, 2 release orders)")
+    chunks, W, order = _ag_inputs(c.P, c.Mc, c.N, c.K, seed=0)
+    run = bf.AgGemm(c.P, c.Mc, c.N, c.K, BF16, c.tile_m, c.tile_n, chunks, W)
+    outs = []
+    for o in (order, np.arange(c.P)[::-1]):
+        run.poison()
+        run.run_released(o).synchronize()
+        sync()
+        assert run.status_value() == 0
+        outs.append(run.out.clone())
+    assert torch.equal(outs[0], outs[1])
+    rng = np.random.default_rng(7)
+    ms = rng.integers(0, c.P * c.Mc, 3000)
+    ns = rng.integers(0, c.N, 3000)
+    want = oracle.ag_gemm_points(c.P, c.Mc, c.N, c.K, BF16, BF16, list(chunks), W, ms, ns)
+    got = bf.to_host(outs[0], BF16)[ms, ns]
+    assert relerr(val(got, BF16), val(want, BF16)) <= TOL[BF16]
+    assert not torch.isnan(outs[0].view(torch.bfloat16)).any()
+
+
+# ====================================================================== emb-bag + A2A
+
+def _emb_check(run, T, R, D, B, L, P, tables, idx, off=None):
+    win = oracle.embbag_a2a(T, R, D, B, L, P, tables, idx, off)
+    got = run.win_data.cpu().numpy()
+    np.testing.assert_array_equal(got, win)      # sequential fp32 sums: bit-exact
+    assert torch.all(run.win_flags == run.epoch)
+
+
+@pytest.mark.parametrize("D,tile_bags", [(128, 16), (64, 7), (200, 32), (512, 64), (4, 1)])
+def test_embbag_values_bit_exact(D, tile_bags):
+    T, R, B, L, P = 5, 3000, 96, 13, 4
+    say(f"embbag T={T} R={R} D={D} B={B} L={L} P={P} tile_bags={tile_bags}")
+    tables = gen.embbag_tables(T, R, D, std=0.01, seed=D)
+    idx = gen.zipf_indices(T, B, L, R, seed=D)
+    run = bf.EmbbagA2A(T, R, D, B, L, P, tile_bags, tables, idx)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    _emb_check(run, T, R, D, B, L, P, tables, idx)
+    assert torch.all(run.ws == 0)
+
+
+def test_embbag_tagged_routing():
+    T, R, D, B, L, P = 6, 20000, 128, 512, 20, 8
+    say("embbag tagged tables: routing, table and index use bit-exact")
+    tables = gen.tagged_tables(T, R, D)
+    idx = gen.zipf_indices(T, B, L, R, seed=1)
+    run = bf.EmbbagA2A(T, R, D, B, L, P, 16, tables, idx)
+    run.poison()
+    run.run()
+    sync()
+    _emb_check(run, T, R, D, B, L, P, tables, idx)
+
+
+def test_embbag_csr_ragged_and_empty():
+    T, R, D, B, P = 3, 5000, 128, 200, 4
+    say("embbag CSR bags of 0..45 rows (some empty)")
+    off = gen.csr_bag_offsets(T, B, 45, seed=2, empty_frac=0.15)
+    idx = np.random.default_rng(3).integers(0, R, size=int(off[-1]), dtype=np.int32)
+    tables = gen.embbag_tables(T, R, D, std=1.0, seed=4)
+    run = bf.EmbbagA2A(T, R, D, B, 0, P, 8, tables, idx, off)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    _emb_check(run, T, R, D, B, 0, P, tables, idx, off)
+
+
+def test_embbag_bad_index_reported_and_skipped():
+    T, R, D, B, L, P = 2, 100, 128, 16, 4, 2
+    say("embbag out-of-range index")
+    tables = gen.embbag_tables(T, R, D, std=1.0, seed=5)
+    idx = gen.uniform_indices(T, B, L, R, seed=6)
+    idx[1, 3, 2] = R          # one bad index
+    idx[0, 0, 0] = -5         # and a negative one
+    run = bf.EmbbagA2A(T, R, D, B, L, P, 4, tables, idx)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == hocf.HOCF_ERR_BAD_INDEX
+    # the bags sum their valid rows: same as the oracle on the bags with the bad entries dropped
+    off = np.zeros(T * B + 1, np.int64)
+    keep = []
+    for t in range(T):
+        for b in range(B):
+            rows = [r for r in idx[t, b] if 0 <= r < R]
+            keep += rows
+            off[t * B + b + 1] = off[t * B + b] + len(rows)
+    want = oracle.embbag_a2a(T, R, D, B, 0, P, tables, np.asarray(keep, np.int32), off)
+    np.testing.assert_array_equal(run.win_data.cpu().numpy(), want)
+
+
+def test_embbag_full_dlrm():
+    c = cfgs.EMBBAG_DLRM
+    say(f"embbag full {c.name} (tables drawn on the GPU, sampled bags bit-exact)")
+    tables = gen.embbag_tables_torch(c.T, c.R, c.D, seed=0)
+    idx = gen.zipf_indices(c.T, c.B, c.L, c.R, alpha=c.alpha, seed=0)
+    run = bf.EmbbagA2A(c.T, c.R, c.D, c.B, c.L, c.P, c.tile_bags, tables, idx)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    assert torch.all(run.win_flags == run.epoch)
+    assert not torch.isnan(run.win_data).any()
+    rng = np.random.default_rng(9)
+    ts = rng.integers(0, c.T, 2048)
+    bs = rng.integers(0, c.B, 2048)
+    # the sampled bags' rows, copied back from the device tables, as one small table
+    rows = idx[ts, bs]                                        # [n][L]
+    flat = torch.from_numpy(rows.reshape(-1).astype(np.int64)).cuda()
+    tsel = torch.from_numpy(np.repeat(ts, c.L).astype(np.int64)).cuda()
+    mini = tables[tsel, flat].cpu().numpy()[None]             # [1][n*L][D]
+    n = len(ts)
+    midx = np.arange(n * c.L, dtype=np.int32).reshape(1, n, c.L)
+    want = oracle.embbag_a2a(1, n * c.L, c.D, n, c.L, 1, mini, midx)[0, :, 0]   # [n][D]
+    Bd = c.B // c.P
+    got = run.win_data[torch.from_numpy(bs // Bd).cuda(), torch.from_numpy(bs % Bd).cuda(),
+                       torch.from_numpy(ts).cuda()].cpu().numpy()
+    np.testing.assert_array_equal(got, want)
+    del tables
+    torch.cuda.empty_cache()
