@@ -53,6 +53,7 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
   Deadline dl{now_ticks(), a.sync.timeout_ticks};
 
   for (;;) {
+    __syncthreads();  // keeps the thread-0 claim region apart from the previous iteration
     if (tid == 0) {
       int chunk = -1, tile = -1;
       for (;;) {
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
       s_tile = tile;
     }
     __syncthreads();
-    const int c = s_chunk, t = s_tile;
+    const int c = uniform(s_chunk), t = uniform(s_tile);
     __syncthreads();
     if (c < 0) break;
 

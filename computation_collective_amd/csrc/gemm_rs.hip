@@ -92,7 +92,7 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
       s_last = last;
     }
     __syncthreads();
-    if (s_last) {
+    if (uniform(s_last)) {
       acquire_agent();
       if (tid < P && load_flag_agent(&a.win_flags[r][(int64_t)tid * tpc + tflag]) != a.sync.epoch)
         report_status(a.sync, kErrProtocol);

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ar_kernel(GemvArArgs a) {
       s_last = last;
     }
     __syncthreads();
-    if (s_last) {
+    if (uniform(s_last)) {
       acquire_agent();
       if (tid < P && load_flag_agent(&a.part_flags[(int64_t)tid * a.ntiles + j]) != a.sync.epoch)
         report_status(a.sync, kErrProtocol);

@@ -18,6 +18,18 @@
 
 namespace hocf {
 
+// Values broadcast through LDS are the same in every lane, but the compiler
+// cannot know it; loops and branches that depend on them must be marked
+// wave-uniform, or the control-flow structurizer may split a persistent
+// loop per lane (e.g. peel thread 0's flag release out of the loop), which
+// breaks the barriers inside it.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ void report_status(const SyncArgs& s, uint32_t code) {
   if (s.status) atomicCAS(s.status, 0u, code);
 }
@@ -58,8 +70,14 @@ __device__ __forceinline__ int64_t queue_begin(int q, int64_t total) {
 // empty.  Must be called by all threads of the workgroup (thread 0 claims,
 // the result is broadcast through LDS).  `qcur` is per-workgroup state
 // (shared memory) that starts at 0.
+//
+// The leading barrier keeps thread 0's claim from sitting next to any
+// thread-0-only code at the end of the previous item (a flag release):
+// two such regions back to back get merged across the loop edge, and the
+// structurizer then runs the rest of the loop without lane 0.
 __device__ __forceinline__ int64_t claim_item(uint32_t* ws, int64_t total, int* s_qcur,
                                               int64_t* s_item) {
+  __syncthreads();
   if (threadIdx.x == 0) {
     int64_t got = -1;
     const int home = (int)(blockIdx.x % kNumQueues);
@@ -74,7 +92,7 @@ __device__ __forceinline__ int64_t claim_item(uint32_t* ws, int64_t total, int* 
     *s_item = got;
   }
   __syncthreads();
-  const int64_t it = *s_item;
+  const int64_t it = uniform64(*s_item);
   __syncthreads();
   return it;
 }

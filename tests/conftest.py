@@ -26,3 +26,13 @@ def _ensure_built():
 
 
 _ensure_built()
+
+
+def pytest_runtest_logreport(report):
+    """On a GPU machine, write each failure's details to gpurun_out/ as it happens,
+    so they survive a run that is cut short."""
+    if report.failed and os.environ.get("GRAFT_REPO_ROOT"):
+        out = os.path.join(ROOT, "gpurun_out")
+        os.makedirs(out, exist_ok=True)
+        with open(os.path.join(out, "failures.log"), "a") as f:
+            f.write(f"==== {report.nodeid} ({report.when})\n{report.longreprtext}\n")
