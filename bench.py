@@ -6,8 +6,8 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
 
   gemm_rs     GEMM+ReduceScatter, P=8, A_p 8192x1792, W_p 1792x4096 bf16, tile 256x256
   gemv_ar     GEMV+AllReduce, P=8, x_p 4x1024, W_p 1024x8192 bf16 (4 weight replicas rotate)
-  ag_gemm     AllGather+GEMM, 8 chunks 1024x4096, W 4096x1792 bf16, chunks released in a
-              seeded random order by the command processor of a second stream
+  ag_gemm     AllGather+GEMM, 8 chunks 1024x4096, W 4096x1792 bf16, chunk flags written in a
+              seeded random order on the kernel's stream just before it
   embbag_a2a  64 tables 1e6x128 fp32, batch 16384, 20 rows per bag, Zipf(1.05), P=8
 
 `value` is the GEMM+ReduceScatter throughput (TFLOP/s, the headline kernel);
@@ -109,7 +109,6 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
-    rel_stream = torch.cuda.Stream()
     ops = [o for o in args.ops.split(",") if o]
     sdt = bf.F32 if args.slot_dtype == "f32" else bf.BF16
     runs = {}
@@ -157,7 +156,8 @@ def main():
         a = bf.AgGemm(c.P, c.Mc, c.N, c.K, bf.BF16, c.tile_m, c.tile_n, chunks, W)
 
         def ag_call(a=a, order=order):
-            a.run_released(order, stream=stream, release_stream=rel_stream)
+            # flags written in the seeded order on the kernel's own stream, then the kernel
+            a.run_prereleased(order, stream=stream)
 
         algo_bytes = 2 * (c.P * c.Mc * c.K + c.K * c.N + c.P * c.Mc * c.N)
         runs["ag_gemm"] = dict(call=ag_call, obj=a, work=c.flops, unit="TFLOP/s", bound="mfma",

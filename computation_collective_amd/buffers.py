@@ -127,14 +127,36 @@ class GemvAR(_Common):
 
 
 class AgGemm(_Common):
-    """hocf_ag_gemm: gathered chunks [P][Mc][K] gated by chunk_flags [P]; W [K][N] -> out."""
+    """hocf_ag_gemm: gathered chunks [P][Mc][K] gated by chunk_flags [P]; W [K][N] -> out.
 
-    def __init__(self, P, Mc, N, K, out_dt, tile_m, tile_n, chunks, W, device="cuda"):
+    flags="device": chunk flags in device memory, written on the kernel's own
+    stream before the kernel (all chunks present when it starts).
+    flags="host": chunk flags in coherent pinned host memory, written by the
+    host while the kernel runs (paced, any order, or withheld).
+    chunks_on_host: the gathered chunks themselves live in coherent pinned host
+    memory too, so the host can deliver them after the kernel has started."""
+
+    def __init__(self, P, Mc, N, K, out_dt, tile_m, tile_n, chunks, W, device="cuda",
+                 flags="device", chunks_on_host=False):
         self.P, self.Mc, self.N, self.K = P, Mc, N, K
         self.out_dt, self.tile_m, self.tile_n = out_dt, tile_m, tile_n
-        self.A = chunks if isinstance(chunks, torch.Tensor) else to_device(chunks, device)
+        self.flags_mode = flags
         self.W = W if isinstance(W, torch.Tensor) else to_device(W, device)
-        self.chunk_flags = torch.zeros(P, dtype=torch.int32, device=device)
+        self.host_chunks = None
+        if chunks_on_host:
+            nbytes = P * Mc * K * 2
+            addr, _ = hocf.host_coherent(nbytes)
+            self.A = addr
+            self.host_chunks = np.frombuffer((ctypes_char_array(addr, nbytes)), dtype=np.uint16).reshape(P, Mc, K)
+        else:
+            self.A = chunks if isinstance(chunks, torch.Tensor) else to_device(chunks, device)
+        if flags == "host":
+            addr, _ = hocf.host_coherent(4 * P)
+            self.chunk_flags = addr
+            self.host_flags = np.frombuffer(ctypes_char_array(addr, 4 * P), dtype=np.uint32)
+        else:
+            self.chunk_flags = torch.zeros(P, dtype=torch.int32, device=device)
+            self.host_flags = None
         self.out = torch.empty((P * Mc, N), dtype=tdtype(out_dt), device=device)
         self._alloc_sync(hocf.hocf_ag_gemm_workspace_bytes(P), device)
 
@@ -146,24 +168,34 @@ class AgGemm(_Common):
                                  self.chunk_flags, self.W, self.out, self.tile_m, self.tile_n,
                                  sync_, stream)
 
-    def run_released(self, order, stream=None, release_stream=None, release_first=False, **kw):
-        """One call whose chunks are released in `order` by the command processor of
-        `release_stream` (after the kernel is enqueued unless release_first)."""
+    def run_prereleased(self, order, stream=None, **kw):
+        """Flags written in `order` on the kernel's stream, then the kernel."""
+        assert self.flags_mode == "device"
         s = self.next_sync(**kw)
         stream = stream or torch.cuda.current_stream()
-        release_stream = release_stream or torch.cuda.Stream()
-        # the releases of this call must not overtake the previous call's kernel
-        # (it waits for the previous epoch); they may overtake this call's kernel
-        prev = torch.cuda.Event()
-        prev.record(stream)
-        release_stream.wait_event(prev)
-        if release_first:
-            hocf.release_chunks(release_stream, self.chunk_flags, order, s.epoch)
-            hocf.check(self.call(s, stream))
-        else:
-            hocf.check(self.call(s, stream))
-            hocf.release_chunks(release_stream, self.chunk_flags, order, s.epoch)
-        return release_stream
+        hocf.release_chunks(stream, self.chunk_flags, order, s.epoch)
+        hocf.check(self.call(s, stream))
+
+    def run_host_released(self, order, delay_s=0.0, deliver=None, stream=None, **kw):
+        """Kernel first; then the host sets the flags of `order` one by one (after
+        `delay_s` each), optionally delivering chunk c's data first via deliver(c)."""
+        import time
+        assert self.flags_mode == "host"
+        s = self.next_sync(**kw)
+        stream = stream or torch.cuda.current_stream()
+        hocf.check(self.call(s, stream))
+        for c in order:
+            if delay_s:
+                time.sleep(delay_s)
+            if deliver is not None:
+                deliver(int(c))
+            self.host_flags[int(c)] = s.epoch
+        return s.epoch
+
+
+def ctypes_char_array(addr, nbytes):
+    import ctypes
+    return (ctypes.c_char * nbytes).from_address(addr)
 
 
 class EmbbagA2A(_Common):

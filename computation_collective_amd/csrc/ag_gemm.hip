@@ -115,20 +115,9 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
     Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, lds, acc);
 
     const int64_t obase = ((int64_t)c * Mc + (int64_t)mt * Tile::TM) * N + (int64_t)nt * Tile::TN;
-#pragma unroll
-    for (int i = 0; i < Tile::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < Tile::FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          int row, col;
-          Tile::quad(i, j, g, lane, wave, row, col);
-          if (!RAGGED || (row < rows_valid && col < cols_valid)) {
-            const floatx4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                               acc[i][j][4 * g + 3]};
-            st4<ODT>(a.out, obase + (int64_t)row * N + col, v);
-          }
-        }
+    Tile::template store_acc<ODT, RAGGED>(
+        reinterpret_cast<char*>(a.out) + obase * (ODT == kBF16 ? 2 : 4), N, rows_valid, cols_valid,
+        acc);
   }
 
   // the last workgroup out leaves the workspace zeroed

@@ -65,20 +65,9 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
     // 1. publish the tile into window r, slot p
     void* wdata = a.win_data[r];
     const int64_t slot_off = ((int64_t)p * Mc + (int64_t)mt * Tile::TM) * N + (int64_t)nt * Tile::TN;
-#pragma unroll
-    for (int i = 0; i < Tile::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < Tile::FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          int row, col;
-          Tile::quad(i, j, g, lane, wave, row, col);
-          if (!RAGGED || (row < rows_valid && col < cols_valid)) {
-            const floatx4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                               acc[i][j][4 * g + 3]};
-            st4<SDT>(wdata, slot_off + (int64_t)row * N + col, v);
-          }
-        }
+    Tile::template store_acc<SDT, RAGGED>(
+        reinterpret_cast<char*>(wdata) + slot_off * (SDT == kBF16 ? 2 : 4), N, rows_valid,
+        cols_valid, acc);
     __syncthreads();
 
     // 2. ready flag; 3. arrival count -> the last producer reduces

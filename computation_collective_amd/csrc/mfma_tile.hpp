@@ -59,6 +59,34 @@ struct TileBf16 {
     col0 = wn * WTN + 32 * j + 8 * g + 4 * (lane >> 5);
   }
 
+  // Stores the accumulators of this lane into a row-major tile at `base`
+  // (leading dimension ld, element type DT): one base pointer per lane, the
+  // block and group offsets are compile-time constants.
+  template <int DT, bool RAGGED>
+  __device__ static __forceinline__ void store_acc(void* base, int64_t ld, int rows_valid,
+                                                   int cols_valid, const floatx16 (&acc)[FM][FN]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r0 = (wave / WN) * WTM + (lane & 31);
+    const int c0 = (wave % WN) * WTN + 4 * (lane >> 5);
+    constexpr int ES = DT == kBF16 ? 2 : 4;
+    char* p = reinterpret_cast<char*>(base) + ((int64_t)r0 * ld + c0) * ES;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      char* pi = p + (int64_t)(32 * i) * ld * ES;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (RAGGED && (r0 + 32 * i >= rows_valid || c0 + 32 * j + 8 * g >= cols_valid)) continue;
+          const floatx4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                             acc[i][j][4 * g + 3]};
+          st4<DT>(pi + (32 * j + 8 * g) * ES, 0, v);
+        }
+      // keep the scheduler from hoisting every block's conversion at once
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
   // Physical 8-byte k-slot of logical slot s in Wt row n (bit 3 flipped by bit 4 of n).
   __device__ static __forceinline__ int wslot(int n, int s) { return s ^ (((n >> 4) & 1) << 3); }
 
@@ -144,30 +172,42 @@ struct TileBf16 {
         }
     };
 
+    // MFMA operand fragments of one 16-deep k-slice
+    auto read_frags = [&](const uint16_t* As, const uint16_t* Bs, int kk, bf16x8 (&a)[FM],
+                          bf16x8 (&b)[FN]) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = wm * WTM + 32 * i + (lane & 31);
+        a[i] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(As + m * LDK + kk * 16 + (lane >> 5) * 8));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = wn * WTN + 32 * j + (lane & 31);
+        const int sl = kk * 4 + (lane >> 5) * 2;
+        b[j] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(Bs + n * LDK + wslot(n, sl) * 4));
+      }
+    };
+    auto mfmas = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    };
+    // the fragments of slice kk+1 are read while the MFMAs of slice kk run
     auto compute = [&](int stage) {
       const uint16_t* As = lds + stage * STAGE;
       const uint16_t* Bs = As + A_ELEMS;
+      bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
+      read_frags(As, Bs, 0, a0, b0);
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 a[FM], b[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int m = wm * WTM + 32 * i + (lane & 31);
-          a[i] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const uint4*>(As + m * LDK + kk * 16 + (lane >> 5) * 8));
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int n = wn * WTN + 32 * j + (lane & 31);
-          const int s = kk * 4 + (lane >> 5) * 2;
-          b[j] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const uint4*>(Bs + n * LDK + wslot(n, s) * 4));
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      for (int kk = 0; kk < BK / 16; kk += 2) {
+        read_frags(As, Bs, kk + 1, a1, b1);
+        mfmas(a0, b0);
+        if (kk + 2 < BK / 16) read_frags(As, Bs, kk + 2, a0, b0);
+        mfmas(a1, b1);
       }
     };
 
@@ -205,6 +245,34 @@ struct TileF32 {
     const int wm = wave / WN, wn = wave % WN;
     row = wm * WTM + 32 * i + (lane & 31);
     col0 = wn * WTN + 32 * j + 8 * g + 4 * (lane >> 5);
+  }
+
+  // Stores the accumulators of this lane into a row-major tile at `base`
+  // (leading dimension ld, element type DT): one base pointer per lane, the
+  // block and group offsets are compile-time constants.
+  template <int DT, bool RAGGED>
+  __device__ static __forceinline__ void store_acc(void* base, int64_t ld, int rows_valid,
+                                                   int cols_valid, const floatx16 (&acc)[FM][FN]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r0 = (wave / WN) * WTM + (lane & 31);
+    const int c0 = (wave % WN) * WTN + 4 * (lane >> 5);
+    constexpr int ES = DT == kBF16 ? 2 : 4;
+    char* p = reinterpret_cast<char*>(base) + ((int64_t)r0 * ld + c0) * ES;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      char* pi = p + (int64_t)(32 * i) * ld * ES;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (RAGGED && (r0 + 32 * i >= rows_valid || c0 + 32 * j + 8 * g >= cols_valid)) continue;
+          const floatx4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                             acc[i][j][4 * g + 3]};
+          st4<DT>(pi + (32 * j + 8 * g) * ES, 0, v);
+        }
+      // keep the scheduler from hoisting every block's conversion at once
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   template <bool RAGGED>

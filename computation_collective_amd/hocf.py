@@ -183,9 +183,13 @@ def hocf_embbag_a2a(T, R, D, B, L, P, tables, indices, offsets, win, tile_bags, 
                                  tile_bags, ctypes.byref(sync_), _stream(stream))
 
 
-# --------------------------------------------------------------- chunk releaser
-# The AllGather side of hocf_ag_gemm: chunk flags written by the command
-# processor of another stream (no compute unit involved), in a given order.
+# --------------------------------------------------------------- chunk releasers
+# The AllGather side of hocf_ag_gemm.  On ROCm a stream write-value is a tiny
+# blit kernel, ordered with the rest of its stream; a release stream that
+# shares a hardware queue with the consumer's stream would queue behind the
+# consumer kernel that waits for it.  So flags are either written on the
+# consumer's own stream before the kernel, or by the host into coherent
+# pinned memory while the kernel runs.
 
 _hip = None
 
@@ -208,10 +212,31 @@ def _hip_runtime():
         _hip.hipStreamWaitValue32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32,
                                               ctypes.c_uint, ctypes.c_uint32]
         _hip.hipStreamWaitValue32.restype = ctypes.c_int
+        _hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+        _hip.hipHostMalloc.restype = ctypes.c_int
     return _hip
 
 
 HIP_STREAM_WAIT_VALUE_GTE = 0x0
+HIP_HOST_MALLOC_MAPPED = 0x2
+HIP_HOST_MALLOC_COHERENT = 0x40000000
+_host_blocks = []   # coherent host blocks live until the process ends
+
+
+def host_coherent(nbytes: int):
+    """Pinned, device-mapped, coherent host memory (fine-grained: the GPU does not
+    cache it), e.g. for flags or chunks written by the host while a kernel runs.
+    Returns (address, ctypes buffer).  Kept until the process ends."""
+    import ctypes as C
+    hip = _hip_runtime()
+    p = C.c_void_p()
+    rc = hip.hipHostMalloc(C.byref(p), C.c_size_t(nbytes), HIP_HOST_MALLOC_COHERENT | HIP_HOST_MALLOC_MAPPED)
+    if rc != 0:
+        raise RuntimeError(f"hipHostMalloc failed ({rc})")
+    buf = (C.c_char * nbytes).from_address(p.value)
+    C.memset(p.value, 0, nbytes)
+    _host_blocks.append((p, buf))
+    return p.value, buf
 
 
 def stream_write_value32(stream, address: int, value: int) -> None:

@@ -216,23 +216,30 @@ def _ag_inputs(P, Mc, N, K, seed=0):
 @pytest.mark.parametrize("P,Mc,N,K,tm,odt", [(3, 300, 328, 136, 128, BF16), (4, 300, 520, 200, 256, F32),
                                              (8, 128, 256, 64, 128, BF16)])
 def test_ag_gemm_release_orders(P, Mc, N, K, tm, odt):
-    say(f"ag_gemm P={P} Mc={Mc} N={N} K={K} tile={tm} out={odt}: 3 release orders")
+    """Chunk flags set by the host (coherent pinned memory) while the kernel runs,
+    in three different orders, plus flags pre-released on the kernel's stream:
+    every output must be bit-identical and match the oracle."""
+    say(f"ag_gemm P={P} Mc={Mc} N={N} K={K} tile={tm} out={odt}: 3 host release orders + pre-release")
     chunks, W, order = _ag_inputs(P, Mc, N, K, seed=P + N)
-    run = bf.AgGemm(P, Mc, N, K, odt, tm, tm, chunks, W)
+    run = bf.AgGemm(P, Mc, N, K, odt, tm, tm, chunks, W, flags="host")
     outs = []
-    orders = [order, np.arange(P), np.arange(P)[::-1]]
-    for k, o in enumerate(orders):
+    for o in (order, np.arange(P), np.arange(P)[::-1]):
         run.poison()
-        rs = run.run_released(o, release_first=(k == 1))
-        rs.synchronize()
+        run.run_host_released(o, delay_s=0.0005)
         sync()
         assert run.status_value() == 0
         outs.append(run.out.clone())
+    pre = bf.AgGemm(P, Mc, N, K, odt, tm, tm, run.A, run.W, flags="device")
+    pre.poison()
+    pre.run_prereleased(order)
+    sync()
+    assert pre.status_value() == 0
+    outs.append(pre.out.clone())
     for o in outs[1:]:
         assert torch.equal(o, outs[0]), "output depends on the release order"
     _, want = oracle.ag_gemm(P, Mc, N, K, BF16, odt, list(chunks), W)
     assert relerr(val(bf.to_host(outs[0], odt), odt), val(want, odt)) <= TOL[BF16]
-    assert torch.all(run.ws == 0)
+    assert torch.all(run.ws == 0) and torch.all(pre.ws == 0)
 
 
 def test_ag_gemm_integer_bit_exact():
@@ -241,34 +248,27 @@ def test_ag_gemm_integer_bit_exact():
     chunks, W, order = gen.ag_gemm_inputs(P, Mc, N, K, seed=5, dist_a=("int", -2, 2), dist_w=("int", -2, 2))
     run = bf.AgGemm(P, Mc, N, K, BF16, 256, 256, chunks, W)
     run.poison()
-    run.run_released(order).synchronize()
+    run.run_prereleased(order)
     sync()
     _, want = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
     np.testing.assert_array_equal(bf.to_host(run.out, BF16), want)
 
 
-def test_ag_gemm_late_release():
-    """Chunks start NaN-poisoned; a second stream first spins for ~20 ms, then
-    copies the real chunks in and sets their flags, so the kernel is already
-    running and waiting when they arrive: any read before a chunk's flag shows
-    up as NaN in the output."""
+def test_ag_gemm_late_delivery():
+    """The chunks live in coherent pinned host memory and start as NaN; after the
+    kernel has started, the host writes chunk c's data and then its flag, one
+    chunk every 2 ms.  Any read of a chunk before its flag shows up as NaN."""
     P, Mc, N, K = 4, 256, 384, 256
-    say(f"ag_gemm late release P={P} Mc={Mc} N={N} K={K}")
+    say(f"ag_gemm late delivery from the host P={P} Mc={Mc} N={N} K={K}")
     chunks, W, order = _ag_inputs(P, Mc, N, K, seed=11)
-    run = bf.AgGemm(P, Mc, N, K, BF16, 128, 128, chunks, W)
-    real = run.A.clone()
-    bf.nan_fill(run.A)
+    run = bf.AgGemm(P, Mc, N, K, BF16, 128, 128, None, W, flags="host", chunks_on_host=True)
+    run.host_chunks[:] = 0x7FC0
     run.poison()
-    sync()
-    rel = torch.cuda.Stream()
-    s = run.next_sync(spin_timeout_ns=2_000_000_000)
-    with torch.cuda.stream(rel):
-        torch.cuda._sleep(50_000_000)
-        for c in order:
-            run.A[c].copy_(real[c])
-            hocf.stream_write_value32(rel, hocf.ptr(run.chunk_flags) + 4 * int(c), s.epoch)
-    hocf.check(run.call(s, torch.cuda.current_stream()))
-    rel.synchronize()
+
+    def deliver(c):
+        run.host_chunks[c] = chunks[c]
+
+    run.run_host_released(order, delay_s=0.002, deliver=deliver, spin_timeout_ns=2_000_000_000)
     sync()
     assert run.status_value() == 0
     _, want = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
@@ -282,10 +282,9 @@ def test_ag_gemm_withheld_chunk_times_out():
     P, Mc, N, K = 4, 256, 256, 128
     say(f"ag_gemm withheld chunk (timeout 20 ms) P={P}")
     chunks, W, _ = _ag_inputs(P, Mc, N, K, seed=4)
-    run = bf.AgGemm(P, Mc, N, K, BF16, 128, 128, chunks, W)
+    run = bf.AgGemm(P, Mc, N, K, BF16, 128, 128, chunks, W, flags="host")
     run.poison()
-    rs = run.run_released([0, 2, 3], spin_timeout_ns=20_000_000)
-    rs.synchronize()
+    run.run_host_released([0, 2, 3], spin_timeout_ns=20_000_000)
     sync()
     assert run.status_value() == hocf.HOCF_ERR_TIMEOUT
     _, want = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
@@ -296,19 +295,25 @@ def test_ag_gemm_withheld_chunk_times_out():
     assert torch.all(run.ws == 0), "a timed-out call must still leave the workspace zeroed"
     run.status.zero_()
     run.poison()
-    run.run_released([3, 1, 0, 2]).synchronize()
+    run.run_host_released([3, 1, 0, 2])
     sync()
     assert run.status_value() == 0
     assert relerr(val(bf.to_host(run.out, BF16), BF16), val(want, BF16)) <= TOL[BF16]
 
 
 def test_ag_gemm_abort():
+    """A withheld chunk and a host-pinned abort word set by the host 10 ms in:
+    the waiting workgroups record HOCF_ERR_ABORTED and exit."""
     P, Mc, N, K = 2, 128, 128, 64
-    say("ag_gemm abort word set, chunk withheld")
+    say("ag_gemm abort word set by the host, chunk withheld")
     chunks, W, _ = _ag_inputs(P, Mc, N, K, seed=6)
-    run = bf.AgGemm(P, Mc, N, K, BF16, 128, 128, chunks, W)
-    abort = torch.ones(1, dtype=torch.int32, device="cuda")
-    run.run_released([0], abort_flag=abort, spin_timeout_ns=2_000_000_000).synchronize()
+    run = bf.AgGemm(P, Mc, N, K, BF16, 128, 128, chunks, W, flags="host")
+    addr, _ = hocf.host_coherent(4)
+    abort = np.frombuffer(bf.ctypes_char_array(addr, 4), dtype=np.uint32)
+    run.run_host_released([0], abort_flag=addr, spin_timeout_ns=5_000_000_000)
+    import time
+    time.sleep(0.01)
+    abort[0] = 1
     sync()
     assert run.status_value() == hocf.HOCF_ERR_ABORTED
     assert torch.all(run.ws == 0)
@@ -316,24 +321,26 @@ def test_ag_gemm_abort():
 
 def test_ag_gemm_full_colpar():
     c = cfgs.AG_GEMM_COL
-    say(f"ag_gemm full {c.name} (sampled, 2 release orders)")
+    say(f"ag_gemm full {c.name} (sampled; pre-released and host-released orders)")
     chunks, W, order = _ag_inputs(c.P, c.Mc, c.N, c.K, seed=0)
     run = bf.AgGemm(c.P, c.Mc, c.N, c.K, BF16, c.tile_m, c.tile_n, chunks, W)
-    outs = []
-    for o in (order, np.arange(c.P)[::-1]):
-        run.poison()
-        run.run_released(o).synchronize()
-        sync()
-        assert run.status_value() == 0
-        outs.append(run.out.clone())
-    assert torch.equal(outs[0], outs[1])
+    run.poison()
+    run.run_prereleased(order)
+    sync()
+    assert run.status_value() == 0
+    host = bf.AgGemm(c.P, c.Mc, c.N, c.K, BF16, c.tile_m, c.tile_n, run.A, run.W, flags="host")
+    host.poison()
+    host.run_host_released(np.arange(c.P)[::-1], delay_s=0.0002)
+    sync()
+    assert host.status_value() == 0
+    assert torch.equal(run.out, host.out)
     rng = np.random.default_rng(7)
     ms = rng.integers(0, c.P * c.Mc, 3000)
     ns = rng.integers(0, c.N, 3000)
     want = oracle.ag_gemm_points(c.P, c.Mc, c.N, c.K, BF16, BF16, list(chunks), W, ms, ns)
-    got = bf.to_host(outs[0], BF16)[ms, ns]
+    got = bf.to_host(run.out, BF16)[ms, ns]
     assert relerr(val(got, BF16), val(want, BF16)) <= TOL[BF16]
-    assert not torch.isnan(outs[0].view(torch.bfloat16)).any()
+    assert not torch.isnan(run.out.view(torch.bfloat16)).any()
 
 
 # ====================================================================== emb-bag + A2A
