@@ -33,7 +33,8 @@ namespace hocf {
 
 template <class Tile, bool RAGGED, int ODT>
 __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[Tile::LDS_BYTES / 2];
+  __shared__ __attribute__((aligned(1024))) char smem0[Tile::SMEM0_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem1[Tile::SMEM1_BYTES];
   __shared__ int s_chunk, s_tile;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
     const uint16_t* At = a.A + ((int64_t)c * Mc + (int64_t)mt * Tile::TM) * K;
     const uint16_t* Wt = a.W + (int64_t)nt * Tile::TN;
     floatx16 acc[Tile::FM][Tile::FN];
-    Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, lds, acc);
+    Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, smem0, smem1, acc);
 
     const int64_t obase = ((int64_t)c * Mc + (int64_t)mt * Tile::TM) * N + (int64_t)nt * Tile::TN;
     Tile::template store_acc<ODT, RAGGED>(
@@ -130,10 +131,9 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
   }
 }
 
-template <class Tile, int ODT>
-static hipError_t launch_tile(const AgGemmArgs& a, hipStream_t s) {
-  const bool ragged = (a.Mc % Tile::TM) || (a.N % Tile::TN) || (a.K % Tile::BK);
-  auto kern = ragged ? &ag_gemm_kernel<Tile, true, ODT> : &ag_gemm_kernel<Tile, false, ODT>;
+template <class Tile, bool RAGGED, int ODT>
+static hipError_t launch_k(const AgGemmArgs& a, hipStream_t s) {
+  auto kern = &ag_gemm_kernel<Tile, RAGGED, ODT>;
   int grid = 0;
   hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), Tile::NT,
                                  (int64_t)a.P * a.mtiles * a.ntiles, &grid);
@@ -142,14 +142,23 @@ static hipError_t launch_tile(const AgGemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class Tile>
+// full tiles take the direct-to-LDS mainloop, ragged ones the register-staged one
+template <int TM, int TN, int ODT>
+static hipError_t launch_tile(const AgGemmArgs& a, hipStream_t s) {
+  using Staged = TileBf16<TM, TN, 2, 2>;
+  using Direct = TileBf16Direct<TM, TN, 2, 2>;
+  const bool ragged = (a.Mc % TM) || (a.N % TN) || (a.K % Direct::KSTEP);
+  return ragged ? launch_k<Staged, true, ODT>(a, s) : launch_k<Direct, false, ODT>(a, s);
+}
+
+template <int TM, int TN>
 static hipError_t launch_out(const AgGemmArgs& a, hipStream_t s) {
-  return a.out_dt == kBF16 ? launch_tile<Tile, kBF16>(a, s) : launch_tile<Tile, kF32>(a, s);
+  return a.out_dt == kBF16 ? launch_tile<TM, TN, kBF16>(a, s) : launch_tile<TM, TN, kF32>(a, s);
 }
 
 hipError_t launch_ag_gemm(const AgGemmArgs& a, int tm, int tn, hipStream_t s) {
-  if (tm == 256 && tn == 256) return launch_out<TileBf16<256, 256, 2, 2>>(a, s);
-  if (tm == 128 && tn == 128) return launch_out<TileBf16<128, 128, 2, 2>>(a, s);
+  if (tm == 256 && tn == 256) return launch_out<256, 256>(a, s);
+  if (tm == 128 && tn == 128) return launch_out<128, 128>(a, s);
   return hipErrorInvalidValue;
 }
 

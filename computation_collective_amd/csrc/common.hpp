@@ -19,16 +19,17 @@ enum Dt : int { kF32 = 0, kBF16 = 1 };
 // bfloat16 is the top half of a binary32 pattern.
 __device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
 
-// binary32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+// binary32 -> bfloat16 with the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const bf16x2_t r = __builtin_convertvector(floatx2_t{lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 
 // Compile-time-typed vector access: 4 consecutive elements as fp32.
 template <int DT>

@@ -34,7 +34,8 @@ namespace hocf {
 template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
 __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   using Elem = typename std::conditional<BF16IN, uint16_t, float>::type;
-  __shared__ __attribute__((aligned(16))) Elem lds[Tile::LDS_BYTES / sizeof(Elem)];
+  __shared__ __attribute__((aligned(1024))) char smem0[Tile::SMEM0_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem1[Tile::SMEM1_BYTES];
   __shared__ int s_qcur;
   __shared__ int64_t s_item;
   __shared__ int s_last;
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
                      ((int64_t)p * a.M + (int64_t)r * Mc + (int64_t)mt * Tile::TM) * K;
     const Elem* Wt = reinterpret_cast<const Elem*>(a.W) + (int64_t)p * K * N + (int64_t)nt * Tile::TN;
     floatx16 acc[Tile::FM][Tile::FN];
-    Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, lds, acc);
+    Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, smem0, smem1, acc);
 
     // 1. publish the tile into window r, slot p
     void* wdata = a.win_data[r];
@@ -124,19 +125,30 @@ static hipError_t launch_tile(const GemmRsArgs& a, hipStream_t s) {
                 : launch_one<Tile, false, BF16IN, SDT, ODT>(a, s);
 }
 
-template <class Tile>
+// bf16: full tiles take the direct-to-LDS mainloop, ragged ones the
+// register-staged mainloop that zero-fills the edges
+template <int TM, int TN, int SDT, int ODT>
+static hipError_t launch_bf16_dt(const GemmRsArgs& a, hipStream_t s) {
+  using Staged = TileBf16<TM, TN, 2, 2>;
+  using Direct = TileBf16Direct<TM, TN, 2, 2>;
+  const bool ragged = (a.Mc % TM) || (a.N % TN) || (a.K % Direct::KSTEP);
+  return ragged ? launch_one<Staged, true, true, SDT, ODT>(a, s)
+                : launch_one<Direct, false, true, SDT, ODT>(a, s);
+}
+
+template <int TM, int TN>
 static hipError_t launch_bf16(const GemmRsArgs& a, hipStream_t s) {
-  if (a.slot_dt == kF32 && a.out_dt == kBF16) return launch_tile<Tile, true, kF32, kBF16>(a, s);
-  if (a.slot_dt == kBF16 && a.out_dt == kBF16) return launch_tile<Tile, true, kBF16, kBF16>(a, s);
-  if (a.slot_dt == kF32 && a.out_dt == kF32) return launch_tile<Tile, true, kF32, kF32>(a, s);
-  if (a.slot_dt == kBF16 && a.out_dt == kF32) return launch_tile<Tile, true, kBF16, kF32>(a, s);
+  if (a.slot_dt == kF32 && a.out_dt == kBF16) return launch_bf16_dt<TM, TN, kF32, kBF16>(a, s);
+  if (a.slot_dt == kBF16 && a.out_dt == kBF16) return launch_bf16_dt<TM, TN, kBF16, kBF16>(a, s);
+  if (a.slot_dt == kF32 && a.out_dt == kF32) return launch_bf16_dt<TM, TN, kF32, kF32>(a, s);
+  if (a.slot_dt == kBF16 && a.out_dt == kF32) return launch_bf16_dt<TM, TN, kBF16, kF32>(a, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_rs(const GemmRsArgs& a, int tm, int tn, int in_dt, hipStream_t s) {
   if (in_dt == kBF16) {
-    if (tm == 256 && tn == 256) return launch_bf16<TileBf16<256, 256, 2, 2>>(a, s);
-    if (tm == 128 && tn == 128) return launch_bf16<TileBf16<128, 128, 2, 2>>(a, s);
+    if (tm == 256 && tn == 256) return launch_bf16<256, 256>(a, s);
+    if (tm == 128 && tn == 128) return launch_bf16<128, 128>(a, s);
   } else if (a.slot_dt == kF32 && a.out_dt == kF32) {
     if (tm == 64 && tn == 64) return launch_tile<TileF32<64, 64, 2, 2>, false, kF32, kF32>(a, s);
   }

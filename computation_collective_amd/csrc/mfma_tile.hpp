@@ -43,6 +43,7 @@ struct TileBf16 {
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_ELEMS = TM * LDK, B_ELEMS = TN * LDK, STAGE = A_ELEMS + B_ELEMS;
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int SMEM0_BYTES = LDS_BYTES, SMEM1_BYTES = 16;
   static constexpr int A_LD = (TM * BK / 8) / NT;  // 16-byte A pieces per thread per step
   static constexpr int NBH = TN / 64;              // W wave-blocks along n (8 lanes x 8 n)
   static constexpr int B_BLK = 2 * NBH / NW;       // 4(k) x 8(n) W blocks per thread per step
@@ -62,19 +63,20 @@ struct TileBf16 {
   // Stores the accumulators of this lane into a row-major tile at `base`
   // (leading dimension ld, element type DT): one base pointer per lane, the
   // block and group offsets are compile-time constants.
-  template <int DT, bool RAGGED>
-  __device__ static __forceinline__ void store_acc(void* base, int64_t ld, int rows_valid,
-                                                   int cols_valid, const floatx16 (&acc)[FM][FN]) {
+  template <int DT, bool RAGGED, int FM_, int FN_, int WTM_, int WTN_>
+  __device__ static __forceinline__ void store_acc_impl(void* base, int64_t ld, int rows_valid,
+                                                        int cols_valid,
+                                                        const floatx16 (&acc)[FM_][FN_]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r0 = (wave / WN) * WTM + (lane & 31);
-    const int c0 = (wave % WN) * WTN + 4 * (lane >> 5);
+    const int r0 = (wave / WN) * WTM_ + (lane & 31);
+    const int c0 = (wave % WN) * WTN_ + 4 * (lane >> 5);
     constexpr int ES = DT == kBF16 ? 2 : 4;
     char* p = reinterpret_cast<char*>(base) + ((int64_t)r0 * ld + c0) * ES;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM_; ++i) {
       char* pi = p + (int64_t)(32 * i) * ld * ES;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN_; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           if (RAGGED && (r0 + 32 * i >= rows_valid || c0 + 32 * j + 8 * g >= cols_valid)) continue;
@@ -87,6 +89,12 @@ struct TileBf16 {
     }
   }
 
+  template <int DT, bool RAGGED>
+  __device__ static __forceinline__ void store_acc(void* base, int64_t ld, int rows_valid,
+                                                   int cols_valid, const floatx16 (&acc)[FM][FN]) {
+    store_acc_impl<DT, RAGGED, FM, FN, WTM, WTN>(base, ld, rows_valid, cols_valid, acc);
+  }
+
   // Physical 8-byte k-slot of logical slot s in Wt row n (bit 3 flipped by bit 4 of n).
   __device__ static __forceinline__ int wslot(int n, int s) { return s ^ (((n >> 4) & 1) << 3); }
 
@@ -94,7 +102,8 @@ struct TileBf16 {
   __device__ static __forceinline__ void run(const uint16_t* __restrict__ A, int64_t lda,
                                              const uint16_t* __restrict__ W, int64_t ldw,
                                              int rows_valid, int cols_valid, int K,
-                                             uint16_t* lds, floatx16 (&acc)[FM][FN]) {
+                                             char* smem0, char* /*smem1*/, floatx16 (&acc)[FM][FN]) {
+    uint16_t* const lds = reinterpret_cast<uint16_t*>(smem0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 #pragma unroll
@@ -224,6 +233,178 @@ struct TileBf16 {
   }
 };
 
+// bf16 tile, full tiles only (no ragged rows, columns or K): both operand
+// slices go from global memory straight into LDS (gfx950 global_load_lds,
+// 16 bytes per lane, a wave writing 1 KB of LDS per instruction), so no
+// registers hold staged data and nothing is transposed in registers.
+//
+// LDS per stage: A as [TM][64] rows of 128 B, W as [64][TN] rows of 2*TN B,
+// both in 16-byte chunks that are XOR-swizzled (a lane may fetch any global
+// address, so the swizzle is applied on the global side):
+//   A row m, logical chunk c  -> physical chunk c ^ ((m >> 1) & 7)
+//   W row k, logical chunk c  -> physical chunk c ^ (4 * (k & 3))
+// A fragments are 16-byte ds_read_b128 (8 consecutive k of one row of A).
+// W fragments use the gfx950 transposing read ds_read_b64_tr_b16: within a
+// group of 16 lanes, lane s points at W[k0 + s/4][n0 + 4*(s%4) .. +3] and
+// lane i receives W[k0 .. k0+3][n0 + i]; two such reads give the 8
+// consecutive k of one column of W.  Both read patterns touch 16 distinct
+// 16-byte bank groups per 16 lanes (conflict-free).
+template <int TM_, int TN_, int WM_, int WN_>
+struct TileBf16Direct {
+  static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int BK = 64;
+  static constexpr int WTM = TM / WM, WTN = TN / WN;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int A_BYTES = TM * BK * 2, W_BYTES = BK * TN * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int A_BLOCKS = A_BYTES / 1024, W_BLOCKS = W_BYTES / 1024;
+  static constexpr int A_LD = A_BLOCKS / NW, W_LD = W_BLOCKS / NW;  // per wave per stage
+  static constexpr int CW = TN / 8;            // 16-byte chunks per W row
+  static constexpr int WROWS_PER_BLOCK = 512 / TN;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(A_BLOCKS % NW == 0 && W_BLOCKS % NW == 0 && TN >= 128 && TN <= 512, "layout");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+  __device__ static __forceinline__ void quad(int i, int j, int g, int lane, int wave, int& row,
+                                              int& col0) {
+    const int wm = wave / WN, wn = wave % WN;
+    row = wm * WTM + 32 * i + (lane & 31);
+    col0 = wn * WTN + 32 * j + 8 * g + 4 * (lane >> 5);
+  }
+
+  template <int DT, bool RAGGED>
+  __device__ static __forceinline__ void store_acc(void* base, int64_t ld, int rows_valid,
+                                                   int cols_valid, const floatx16 (&acc)[FM][FN]) {
+    TileBf16<TM, TN, WM, WN>::template store_acc_impl<DT, RAGGED, FM, FN, WTM, WTN>(
+        base, ld, rows_valid, cols_valid, acc);
+  }
+
+  __device__ static __forceinline__ void wait_loads() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS-bound loads have landed
+  }
+
+  // The two stages live in two separate LDS arrays and the K loop is unrolled
+  // by two, so that every LDS access names its array: the compiler then knows
+  // that the reads of one stage do not alias the in-flight direct-to-LDS
+  // loads of the other and does not wait for those loads before reading.
+  // The kernel declares the two stages as two separate __shared__ arrays.
+  static constexpr int SMEM0_BYTES = STAGE_BYTES, SMEM1_BYTES = STAGE_BYTES;
+  static constexpr int KSTEP = 2 * BK;  // K must be a multiple of this
+
+  template <bool RAGGED>
+  __device__ static __forceinline__ void run(const uint16_t* __restrict__ A, int64_t lda,
+                                             const uint16_t* __restrict__ W, int64_t ldw,
+                                             int /*rows_valid*/, int /*cols_valid*/, int K,
+                                             char* stage0, char* stage1, floatx16 (&acc)[FM][FN]) {
+    static_assert(!RAGGED, "full tiles only");
+#if defined(__HIP_DEVICE_COMPILE__)  // device-only body (the host pass only needs the declaration)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    const int nk = K / BK;
+    if (nk == 0) return;
+
+    // per-lane global sources (fixed over K; the k offset is added per stage)
+    const uint16_t* asrc[A_LD];
+    const uint16_t* wsrc[W_LD];
+#pragma unroll
+    for (int t = 0; t < A_LD; ++t) {
+      const int b = t * NW + wave;
+      const int row = b * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      asrc[t] = A + (int64_t)row * lda + c * 8;
+    }
+#pragma unroll
+    for (int t = 0; t < W_LD; ++t) {
+      const int b = t * NW + wave;
+      const int k = b * WROWS_PER_BLOCK + lane / CW;
+      const int c = (lane % CW) ^ (4 * (k & 3));
+      wsrc[t] = W + (int64_t)k * ldw + c * 8;
+    }
+    auto load_stage = [&](char* sb, int ks) {
+      const int64_t ak = (int64_t)ks * BK;
+      const int64_t wk = (int64_t)ks * BK * ldw;
+#pragma unroll
+      for (int t = 0; t < A_LD; ++t)
+        __builtin_amdgcn_global_load_lds(
+            asrc[t] + ak, (__attribute__((address_space(3))) void*)(sb + (t * NW + wave) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int t = 0; t < W_LD; ++t)
+        __builtin_amdgcn_global_load_lds(
+            wsrc[t] + wk, (__attribute__((address_space(3))) void*)(sb + A_BYTES + (t * NW + wave) * 1024),
+            16, 0, 0);
+    };
+
+    typedef short short4v __attribute__((ext_vector_type(4)));
+    auto read_frags = [&](const char* sb, int kk, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = wm * WTM + 32 * i + (lane & 31);
+        const int c = (kk * 2 + (lane >> 5)) ^ ((m >> 1) & 7);
+        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + m * 128 + c * 16));
+      }
+      const int G = lane >> 4, s = lane & 15;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = wn * WTN + 32 * j + (G & 1) * 16 + 4 * (s & 3);
+        short4v h[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = kk * 16 + (G >> 1) * 8 + 4 * hh + (s >> 2);
+          const int c = (n >> 3) ^ (4 * (k & 3));
+          const char* p = sb + A_BYTES + k * (TN * 2) + c * 16 + (n & 7) * 2;
+          h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4v*)(p));
+        }
+        const short __attribute__((ext_vector_type(8))) v8 = {h[0][0], h[0][1], h[0][2], h[0][3],
+                                                             h[1][0], h[1][1], h[1][2], h[1][3]};
+        b[j] = __builtin_bit_cast(bf16x8, v8);
+      }
+    };
+    auto mfmas = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    };
+    auto compute = [&](const char* sb) {
+      bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
+      read_frags(sb, 0, a0, b0);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; kk += 2) {
+        read_frags(sb, kk + 1, a1, b1);
+        mfmas(a0, b0);
+        if (kk + 2 < BK / 16) read_frags(sb, kk + 2, a0, b0);
+        mfmas(a1, b1);
+      }
+    };
+    auto step = [&](char* cur, char* nxt, int ks) {
+      if (ks + 1 < nk) load_stage(nxt, ks + 1);
+      compute(cur);
+      wait_loads();
+      __syncthreads();
+    };
+
+    load_stage(stage0, 0);
+    wait_loads();
+    __syncthreads();
+    // K is a multiple of 2*BK here (KSTEP): the stages alternate in pairs
+    for (int ks = 0; ks < nk; ks += 2) {
+      step(stage0, stage1, ks);
+      step(stage1, stage0, ks + 1);
+    }
+#endif
+  }
+};
+
 template <int TM_, int TN_, int WM_, int WN_>
 struct TileF32 {
   static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
@@ -234,6 +415,7 @@ struct TileF32 {
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_ELEMS = TM * LDA, B_ELEMS = BK * LDB, STAGE = A_ELEMS + B_ELEMS;
   static constexpr int LDS_BYTES = 2 * STAGE * 4;
+  static constexpr int SMEM0_BYTES = LDS_BYTES, SMEM1_BYTES = 16;
   static constexpr int A_LD = (TM * BK / 4) / NT, B_LD = (BK * TN / 4) / NT;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(A_LD >= 1 && B_LD >= 1 && (TM * BK / 4) % NT == 0 && (BK * TN / 4) % NT == 0,
@@ -278,8 +460,9 @@ struct TileF32 {
   template <bool RAGGED>
   __device__ static __forceinline__ void run(const float* __restrict__ A, int64_t lda,
                                              const float* __restrict__ W, int64_t ldw,
-                                             int rows_valid, int cols_valid, int K, float* lds,
-                                             floatx16 (&acc)[FM][FN]) {
+                                             int rows_valid, int cols_valid, int K, char* smem0,
+                                             char* /*smem1*/, floatx16 (&acc)[FM][FN]) {
+    float* const lds = reinterpret_cast<float*>(smem0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 #pragma unroll

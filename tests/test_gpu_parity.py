@@ -108,6 +108,28 @@ def test_gemm_rs_integer_bit_exact(sdt, odt, tm):
     np.testing.assert_array_equal(bf.to_host(run.win_data, sdt), slots)
 
 
+@pytest.mark.parametrize("tm,sdt,odt", [(256, F32, BF16), (256, BF16, BF16), (128, F32, F32), (128, BF16, BF16)])
+def test_gemm_rs_full_tiles_integer_bit_exact(tm, sdt, odt):
+    """Full tiles with K a multiple of 128 take the direct-to-LDS mainloop
+    (transposing LDS reads); integer inputs make it bit-exact."""
+    P, Mc, N, K = 3, 2 * tm, 2 * tm, 384
+    say(f"gemm_rs full tiles integer P={P} Mc={Mc} N={N} K={K} tile={tm} slot={sdt} out={odt}")
+    ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    run, slots, out = _gemm_rs(P, Mc, N, K, BF16, sdt, odt, tm, tm, seed=tm + sdt, dist=ints)
+    np.testing.assert_array_equal(bf.to_host(run.out, odt), out)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, sdt), slots)
+
+
+@pytest.mark.parametrize("tm", [256, 128])
+def test_gemm_rs_full_tiles_values(tm):
+    P, Mc, N, K = 4, 2 * tm, 3 * tm, 512
+    say(f"gemm_rs full tiles N(0,1) P={P} Mc={Mc} N={N} K={K} tile={tm}")
+    run, slots, out = _gemm_rs(P, Mc, N, K, BF16, F32, BF16, tm, tm, seed=tm)
+    assert relerr(val(bf.to_host(run.out, BF16), BF16), val(out, BF16)) <= TOL[BF16]
+    assert relerr(bf.to_host(run.win_data, F32), slots) <= TOL[BF16]
+    assert torch.all(run.win_flags == run.epoch)
+
+
 def test_gemm_rs_fp32_integer_bit_exact():
     say("gemm_rs fp32 integer P=4 256x256x256 tile 64")
     ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
