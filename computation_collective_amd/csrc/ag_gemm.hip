@@ -33,8 +33,12 @@ namespace hocf {
 
 template <class Tile, bool RAGGED, int ODT>
 __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem0[Tile::SMEM0_BYTES];
-  __shared__ __attribute__((aligned(1024))) char smem1[Tile::SMEM1_BYTES];
+  // LDS stages, one __shared__ array each (tiles with fewer stages leave the rest tiny)
+  __shared__ __attribute__((aligned(1024))) char smem0[Tile::SMEM_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem1[Tile::NST > 1 ? Tile::SMEM_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char smem2[Tile::NST > 2 ? Tile::SMEM_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char smem3[Tile::NST > 3 ? Tile::SMEM_BYTES : 16];
+  char* const stages[4] = {smem0, smem1, smem2, smem3};
   __shared__ int s_chunk, s_tile;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
     const uint16_t* At = a.A + ((int64_t)c * Mc + (int64_t)mt * Tile::TM) * K;
     const uint16_t* Wt = a.W + (int64_t)nt * Tile::TN;
     floatx16 acc[Tile::FM][Tile::FN];
-    Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, smem0, smem1, acc);
+    Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
 
     const int64_t obase = ((int64_t)c * Mc + (int64_t)mt * Tile::TM) * N + (int64_t)nt * Tile::TN;
     Tile::template store_acc<ODT, RAGGED>(

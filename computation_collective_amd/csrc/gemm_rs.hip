@@ -34,8 +34,12 @@ namespace hocf {
 template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
 __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   using Elem = typename std::conditional<BF16IN, uint16_t, float>::type;
-  __shared__ __attribute__((aligned(1024))) char smem0[Tile::SMEM0_BYTES];
-  __shared__ __attribute__((aligned(1024))) char smem1[Tile::SMEM1_BYTES];
+  // LDS stages, one __shared__ array each (tiles with fewer stages leave the rest tiny)
+  __shared__ __attribute__((aligned(1024))) char smem0[Tile::SMEM_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem1[Tile::NST > 1 ? Tile::SMEM_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char smem2[Tile::NST > 2 ? Tile::SMEM_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char smem3[Tile::NST > 3 ? Tile::SMEM_BYTES : 16];
+  char* const stages[4] = {smem0, smem1, smem2, smem3};
   __shared__ int s_qcur;
   __shared__ int64_t s_item;
   __shared__ int s_last;
@@ -61,7 +65,7 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
                      ((int64_t)p * a.M + (int64_t)r * Mc + (int64_t)mt * Tile::TM) * K;
     const Elem* Wt = reinterpret_cast<const Elem*>(a.W) + (int64_t)p * K * N + (int64_t)nt * Tile::TN;
     floatx16 acc[Tile::FM][Tile::FN];
-    Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, smem0, smem1, acc);
+    Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
 
     // 1. publish the tile into window r, slot p
     void* wdata = a.win_data[r];

@@ -43,7 +43,8 @@ struct TileBf16 {
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_ELEMS = TM * LDK, B_ELEMS = TN * LDK, STAGE = A_ELEMS + B_ELEMS;
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static constexpr int SMEM0_BYTES = LDS_BYTES, SMEM1_BYTES = 16;
+  static constexpr int SMEM_BYTES = LDS_BYTES;  // stage array 0 holds everything
+  static constexpr int NST = 1;
   static constexpr int A_LD = (TM * BK / 8) / NT;  // 16-byte A pieces per thread per step
   static constexpr int NBH = TN / 64;              // W wave-blocks along n (8 lanes x 8 n)
   static constexpr int B_BLK = 2 * NBH / NW;       // 4(k) x 8(n) W blocks per thread per step
@@ -102,8 +103,8 @@ struct TileBf16 {
   __device__ static __forceinline__ void run(const uint16_t* __restrict__ A, int64_t lda,
                                              const uint16_t* __restrict__ W, int64_t ldw,
                                              int rows_valid, int cols_valid, int K,
-                                             char* smem0, char* /*smem1*/, floatx16 (&acc)[FM][FN]) {
-    uint16_t* const lds = reinterpret_cast<uint16_t*>(smem0);
+                                             char* const (&stages)[4], floatx16 (&acc)[FM][FN]) {
+    uint16_t* const lds = reinterpret_cast<uint16_t*>(stages[0]);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 #pragma unroll
@@ -238,33 +239,47 @@ struct TileBf16 {
 // 16 bytes per lane, a wave writing 1 KB of LDS per instruction), so no
 // registers hold staged data and nothing is transposed in registers.
 //
-// LDS per stage: A as [TM][64] rows of 128 B, W as [64][TN] rows of 2*TN B,
-// both in 16-byte chunks that are XOR-swizzled (a lane may fetch any global
-// address, so the swizzle is applied on the global side):
-//   A row m, logical chunk c  -> physical chunk c ^ ((m >> 1) & 7)
-//   W row k, logical chunk c  -> physical chunk c ^ (4 * (k & 3))
+// NST LDS stages of a BK-deep K slice, loads issued NST-1 slices ahead: a
+// slice's loads have NST-1 slices of MFMA work to land, which hides the
+// latency of the L2 misses.  Each stage is its own __shared__ array (declared
+// by the kernel) and the K loop is unrolled by NST, so every LDS access names
+// its array; the compiler then knows that reading one stage does not alias
+// the loads still in flight into the others, and does not wait for them.
+//
+// LDS per stage: A as [TM][BK] rows, W as [BK][TN] rows, in 16-byte chunks
+// XOR-swizzled on the global side (a lane may fetch any global address):
+//   A row m, logical chunk c -> physical chunk c ^ ((m / (16/CA)) mod CA),
+//                                CA = BK/8 chunks per A row
+//   W row k, logical chunk c -> physical chunk c ^ (4 * (k mod 4))
 // A fragments are 16-byte ds_read_b128 (8 consecutive k of one row of A).
 // W fragments use the gfx950 transposing read ds_read_b64_tr_b16: within a
 // group of 16 lanes, lane s points at W[k0 + s/4][n0 + 4*(s%4) .. +3] and
 // lane i receives W[k0 .. k0+3][n0 + i]; two such reads give the 8
 // consecutive k of one column of W.  Both read patterns touch 16 distinct
 // 16-byte bank groups per 16 lanes (conflict-free).
-template <int TM_, int TN_, int WM_, int WN_>
+template <int TM_, int TN_, int WM_, int WN_, int BK_ = 32, int NST_ = 4>
 struct TileBf16Direct {
   static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
   static constexpr int NW = WM * WN, NT = 64 * NW;
-  static constexpr int BK = 64;
+  static constexpr int BK = BK_, NST = NST_;
   static constexpr int WTM = TM / WM, WTN = TN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_BYTES = TM * BK * 2, W_BYTES = BK * TN * 2;
   static constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
   static constexpr int A_BLOCKS = A_BYTES / 1024, W_BLOCKS = W_BYTES / 1024;
   static constexpr int A_LD = A_BLOCKS / NW, W_LD = W_BLOCKS / NW;  // per wave per stage
+  static constexpr int LPS = A_LD + W_LD;      // loads per wave per stage
+  static constexpr int CA = BK / 8;            // 16-byte chunks per A row
+  static constexpr int AROWS_PER_BLOCK = 1024 / (BK * 2);
   static constexpr int CW = TN / 8;            // 16-byte chunks per W row
   static constexpr int WROWS_PER_BLOCK = 512 / TN;
+  static constexpr int KSTEP = NST * BK;       // K must be a multiple of this
+  static constexpr int SMEM_BYTES = STAGE_BYTES;  // each of the NST stage arrays
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(A_BLOCKS % NW == 0 && W_BLOCKS % NW == 0 && TN >= 128 && TN <= 512, "layout");
+  static_assert((BK == 32 || BK == 64) && NST >= 2 && NST <= 4, "pipeline shape");
+  static_assert(2 * LPS <= 63 && NST <= 4, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
   __device__ static __forceinline__ void quad(int i, int j, int g, int lane, int wave, int& row,
@@ -281,23 +296,17 @@ struct TileBf16Direct {
         base, ld, rows_valid, cols_valid, acc);
   }
 
-  __device__ static __forceinline__ void wait_loads() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS-bound loads have landed
+  // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima)
+  template <int N>
+  __device__ static __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
   }
-
-  // The two stages live in two separate LDS arrays and the K loop is unrolled
-  // by two, so that every LDS access names its array: the compiler then knows
-  // that the reads of one stage do not alias the in-flight direct-to-LDS
-  // loads of the other and does not wait for those loads before reading.
-  // The kernel declares the two stages as two separate __shared__ arrays.
-  static constexpr int SMEM0_BYTES = STAGE_BYTES, SMEM1_BYTES = STAGE_BYTES;
-  static constexpr int KSTEP = 2 * BK;  // K must be a multiple of this
 
   template <bool RAGGED>
   __device__ static __forceinline__ void run(const uint16_t* __restrict__ A, int64_t lda,
                                              const uint16_t* __restrict__ W, int64_t ldw,
                                              int /*rows_valid*/, int /*cols_valid*/, int K,
-                                             char* stage0, char* stage1, floatx16 (&acc)[FM][FN]) {
+                                             char* const (&stages)[4], floatx16 (&acc)[FM][FN]) {
     static_assert(!RAGGED, "full tiles only");
 #if defined(__HIP_DEVICE_COMPILE__)  // device-only body (the host pass only needs the declaration)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -317,8 +326,8 @@ struct TileBf16Direct {
 #pragma unroll
     for (int t = 0; t < A_LD; ++t) {
       const int b = t * NW + wave;
-      const int row = b * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      const int row = b * AROWS_PER_BLOCK + lane / CA;
+      const int c = (lane % CA) ^ ((row / (16 / CA)) % CA);
       asrc[t] = A + (int64_t)row * lda + c * 8;
     }
 #pragma unroll
@@ -347,8 +356,9 @@ struct TileBf16Direct {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int m = wm * WTM + 32 * i + (lane & 31);
-        const int c = (kk * 2 + (lane >> 5)) ^ ((m >> 1) & 7);
-        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + m * 128 + c * 16));
+        const int c = (kk * 2 + (lane >> 5)) ^ ((m / (16 / CA)) % CA);
+        a[i] = __builtin_bit_cast(bf16x8,
+                                  *reinterpret_cast<const uint4*>(sb + m * (BK * 2) + c * 16));
       }
       const int G = lane >> 4, s = lane & 15;
 #pragma unroll
@@ -375,6 +385,7 @@ struct TileBf16Direct {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     };
+    // fragments of slice kk+1 are read while the MFMAs of slice kk run
     auto compute = [&](const char* sb) {
       bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
       read_frags(sb, 0, a0, b0);
@@ -386,20 +397,35 @@ struct TileBf16Direct {
         mfmas(a1, b1);
       }
     };
-    auto step = [&](char* cur, char* nxt, int ks) {
-      if (ks + 1 < nk) load_stage(nxt, ks + 1);
-      compute(cur);
-      wait_loads();
-      __syncthreads();
+    // Waits until slice ks+1 has landed in this wave's share of its stage,
+    // leaving the loads of the slices after it in flight, then meets the
+    // other waves.  A bare s_barrier, not __syncthreads(): the latter's
+    // release fence would also drain the loads still in flight.  Every LDS
+    // read of this slice has returned by now (the MFMAs consumed them).
+    auto sync_next = [&](int ks) {
+      const int later = min(NST - 2, nk - 2 - ks);  // slices issued after ks+1
+      if (later >= 2) wait_vmcnt<2 * LPS>();
+      else if (later == 1) wait_vmcnt<LPS>();
+      else wait_vmcnt<0>();
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+    };
+    // one K slice: issue the loads NST-1 slices ahead, compute this slice
+    auto step = [&](int cur, int ks) {
+      if (ks + NST - 1 < nk) load_stage(stages[(cur + NST - 1) % NST], ks + NST - 1);
+      compute(stages[cur]);
+      sync_next(ks);
     };
 
-    load_stage(stage0, 0);
-    wait_loads();
-    __syncthreads();
-    // K is a multiple of 2*BK here (KSTEP): the stages alternate in pairs
-    for (int ks = 0; ks < nk; ks += 2) {
-      step(stage0, stage1, ks);
-      step(stage1, stage0, ks + 1);
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < nk) load_stage(stages[s], s);
+    sync_next(-1);
+    // K is a multiple of NST*BK (KSTEP): the stages rotate in whole rounds
+    for (int ks = 0; ks < nk; ks += NST) {
+#pragma unroll
+      for (int s = 0; s < NST; ++s) step(s, ks + s);
     }
 #endif
   }
@@ -415,7 +441,8 @@ struct TileF32 {
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_ELEMS = TM * LDA, B_ELEMS = BK * LDB, STAGE = A_ELEMS + B_ELEMS;
   static constexpr int LDS_BYTES = 2 * STAGE * 4;
-  static constexpr int SMEM0_BYTES = LDS_BYTES, SMEM1_BYTES = 16;
+  static constexpr int SMEM_BYTES = LDS_BYTES;  // stage array 0 holds everything
+  static constexpr int NST = 1;
   static constexpr int A_LD = (TM * BK / 4) / NT, B_LD = (BK * TN / 4) / NT;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(A_LD >= 1 && B_LD >= 1 && (TM * BK / 4) % NT == 0 && (BK * TN / 4) % NT == 0,
@@ -460,9 +487,9 @@ struct TileF32 {
   template <bool RAGGED>
   __device__ static __forceinline__ void run(const float* __restrict__ A, int64_t lda,
                                              const float* __restrict__ W, int64_t ldw,
-                                             int rows_valid, int cols_valid, int K, char* smem0,
-                                             char* /*smem1*/, floatx16 (&acc)[FM][FN]) {
-    float* const lds = reinterpret_cast<float*>(smem0);
+                                             int rows_valid, int cols_valid, int K,
+                                             char* const (&stages)[4], floatx16 (&acc)[FM][FN]) {
+    float* const lds = reinterpret_cast<float*>(stages[0]);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 #pragma unroll
