@@ -184,6 +184,10 @@ hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtyp
   if (!tile_ok)
     return fail(HOCF_ERR_UNSUPPORTED, "gemm_rs: no kernel for in=%d slot=%d out=%d tile %dx%d",
                 in_dt, slot_dt, out_dt, tile_m, tile_n);
+  // published tiles are addressed with 32-bit byte offsets from their origin
+  if ((int64_t)tile_m * N * 4 >= ((int64_t)1 << 31))
+    return fail(HOCF_ERR_UNSUPPORTED, "gemm_rs: tile_m * N = %lld elements per tile row band exceeds 2^29",
+                (long long)tile_m * N);
   const size_t need = hocf_gemm_rs_workspace_bytes(P, M, N, tile_m, tile_n);
   hocf_status st = check_sync(sync, need);
   if (st != HOCF_OK) return st;

@@ -15,18 +15,21 @@
 // tiles share A row panels and W column panels in that XCD's L2.
 //
 // When a tile is done the workgroup
-//   1. stores it into destination r's window, slot p (publish),
-//   2. releases the tile's ready flag (epoch) in window r,
+//   1. stores it into destination r's window, slot p (publish), with
+//      device-coherent full-row stores, and waits for their completion,
+//   2. stores the epoch into the tile's ready flag in window r,
 //   3. counts itself in the output tile's arrival counter; the workgroup
-//      that completes the count (the last of the P producers) acquires, checks
-//      the P flags, and folds the P slots in rank order p = 0..P-1 in fp32
-//      into the destination's output chunk -- while other workgroups are
-//      still computing.
-// No workgroup ever waits on another, so the persistent grid cannot stall.
+//      that completes the count (the last of the P producers) checks the P
+//      flags and folds the P slots in rank order p = 0..P-1 in fp32 into the
+//      destination's output chunk -- while other workgroups are still
+//      computing.
+// No workgroup ever waits on another, so the persistent grid cannot stall,
+// and no step needs an L2-wide write-back or invalidate (publish.hpp).
 #include <type_traits>
 
 #include "internal.hpp"
 #include "mfma_tile.hpp"
+#include "publish.hpp"
 #include "sync.hpp"
 
 namespace hocf {
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   __shared__ int64_t s_item;
   __shared__ int s_last;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int P = a.P, N = a.N, K = a.K, Mc = a.Mc;
   const int tpc = a.mtiles * a.ntiles;
   uint32_t* grp = a.ws + kWsExtra;
@@ -68,45 +71,42 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
     Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
 
     // 1. publish the tile into window r, slot p
-    void* wdata = a.win_data[r];
-    const int64_t slot_off = ((int64_t)p * Mc + (int64_t)mt * Tile::TM) * N + (int64_t)nt * Tile::TN;
-    Tile::template store_acc<SDT, RAGGED>(
-        reinterpret_cast<char*>(wdata) + slot_off * (SDT == kBF16 ? 2 : 4), N, rows_valid,
-        cols_valid, acc);
+    constexpr int SES = SDT == kBF16 ? 2 : 4;
+    char* wdata = reinterpret_cast<char*>(a.win_data[r]);
+    const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
+    publish_tile<Tile, SDT, RAGGED>(wdata + ((int64_t)p * Mc * N + tile_off) * SES, N, rows_valid,
+                                    cols_valid, acc, stages);
     __syncthreads();
 
     // 2. ready flag; 3. arrival count -> the last producer reduces
     const int tflag = mt * a.ntiles + nt;
     if (tid == 0) {
-      release_flag(&a.win_flags[r][(int64_t)p * tpc + tflag], a.sync.epoch);
+      __hip_atomic_store(&a.win_flags[r][(int64_t)p * tpc + tflag], a.sync.epoch, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      wait_memory();  // the flag is visible before the count that announces it
       uint32_t* cnt = &grp[(int64_t)r * tpc + tflag];
-      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int last = (prev == (uint32_t)(P - 1));
       if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = last;
     }
     __syncthreads();
     if (uniform(s_last)) {
-      acquire_agent();
       if (tid < P && load_flag_agent(&a.win_flags[r][(int64_t)tid * tpc + tflag]) != a.sync.epoch)
         report_status(a.sync, kErrProtocol);
-      const int64_t slot_stride = (int64_t)Mc * N;
-      const int64_t base = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
-      const int64_t obase = (int64_t)r * Mc * N + base;
-      for (int e = tid * 4; e < Tile::TM * Tile::TN; e += Tile::NT * 4) {
-        const int row = e / Tile::TN, col = e % Tile::TN;
-        if (RAGGED && (row >= rows_valid || col >= cols_valid)) continue;
-        const int64_t off = base + (int64_t)row * N + col;
-        floatx4 v[kMaxP];
-#pragma unroll
-        for (int q = 0; q < kMaxP; ++q)
-          if (q < P) v[q] = ld4<SDT>(wdata, q * slot_stride + off);
-        floatx4 s = v[0];
-#pragma unroll
-        for (int q = 1; q < kMaxP; ++q)
-          if (q < P) s = s + v[q];
-        st4<ODT>(a.out, obase + (int64_t)row * N + col, s);
-      }
+      const char* slot0 = wdata + tile_off * SES;
+      const int64_t slot_bytes = (int64_t)Mc * N * SES;
+      char* otile = reinterpret_cast<char*>(a.out) +
+                    ((int64_t)r * Mc * N + tile_off) * (ODT == kBF16 ? 2 : 4);
+      if (P <= 4)
+        reduce_tile<Tile, SDT, ODT, RAGGED, 4, 8>(slot0, slot_bytes, P, N, otile, N, rows_valid,
+                                                  cols_valid);
+      else if (P <= 8)
+        reduce_tile<Tile, SDT, ODT, RAGGED, 8, 4>(slot0, slot_bytes, P, N, otile, N, rows_valid,
+                                                  cols_valid);
+      else
+        reduce_tile<Tile, SDT, ODT, RAGGED, kMaxP, 2>(slot0, slot_bytes, P, N, otile, N, rows_valid,
+                                                      cols_valid);
     }
   }
   finish_workgroup(a.ws);

@@ -154,6 +154,31 @@ def test_gemm_rs_run_to_run_identical():
 
 
 @pytest.mark.parametrize("sdt", [F32, BF16])
+def test_gemm_rs_alternating_inputs_no_stale_reads(sdt):
+    """Two integer input sets alternate on one buffer set with nothing cleared
+    between calls: a reducer that read a slot before its producer's stores
+    were visible would fold the previous call's (different) partial and miss
+    the bit-exact result."""
+    P, Mc, N, K = 8, 512, 512, 256
+    say(f"gemm_rs alternating inputs P={P} Mc={Mc} N={N} K={K} slot={sdt}")
+    ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    sets = []
+    for seed in (21, 22):
+        A, W = gen.gemm_rs_inputs(P, P * Mc, N, K, BF16, seed=seed, **ints)
+        slots, out = oracle.gemm_rs(P, P * Mc, N, K, BF16, sdt, BF16, A, W)
+        sets.append((bf.to_device(A), bf.to_device(W), slots, out))
+    run = bf.GemmRS(P, P * Mc, N, K, BF16, sdt, BF16, 256, 256, sets[0][0], sets[0][1])
+    for call in range(8):
+        A, W, slots, out = sets[call % 2]
+        run.A, run.W = A, W
+        run.run()
+        sync()
+        assert run.status_value() == 0
+        np.testing.assert_array_equal(bf.to_host(run.out, BF16), out, err_msg=f"call {call}")
+        np.testing.assert_array_equal(bf.to_host(run.win_data, sdt), slots, err_msg=f"call {call}")
+
+
+@pytest.mark.parametrize("sdt", [F32, BF16])
 def test_gemm_rs_full_mlpdown(sdt):
     c = cfgs.GEMM_RS_MLP
     say(f"gemm_rs full {c.name} slot={sdt} (sampled)")
