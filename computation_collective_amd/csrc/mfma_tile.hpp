@@ -25,6 +25,9 @@
 // vectors.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 
 namespace hocf {
@@ -234,6 +237,27 @@ struct TileBf16 {
   }
 };
 
+// Instruction-order hints for one k-substep: NM MFMAs, with ND LDS reads
+// front-loaded (ceil(ND/NM) after each MFMA until they run out, so the last
+// read still has MFMAs behind it) and NV global loads spread evenly.
+template <int NM, int ND, int NV, int X>
+__device__ __forceinline__ void interleave_step() {
+  constexpr int dpm = (ND + NM - 1) / NM;
+  constexpr int d = ND - X * dpm < dpm ? (ND - X * dpm > 0 ? ND - X * dpm : 0) : dpm;
+  constexpr int v = (NV * (X + 1)) / NM - (NV * X) / NM;
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
+  if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);  // global load
+  if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);  // LDS read
+}
+template <int NM, int ND, int NV, int... X>
+__device__ __forceinline__ void interleave_impl(std::integer_sequence<int, X...>) {
+  (interleave_step<NM, ND, NV, X>(), ...);
+}
+template <int NM, int ND, int NV>
+__device__ __forceinline__ void interleave() {
+  interleave_impl<NM, ND, NV>(std::make_integer_sequence<int, NM>{});
+}
+
 // bf16 tile, full tiles only (no ragged rows, columns or K): both operand
 // slices go from global memory straight into LDS (gfx950 global_load_lds,
 // 16 bytes per lane, a wave writing 1 KB of LDS per instruction), so no
@@ -318,7 +342,10 @@ struct TileBf16Direct {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     const int nk = K / BK;
-    if (nk == 0) return;
+    // precondition (checked by the launchers): K is a multiple of NST * BK.
+    // Anything else would make the slice schedule below load past row K, so
+    // it leaves the accumulators at zero instead.
+    if (nk == 0 || nk % NST != 0 || K % BK != 0) return;
 
     // per-lane global sources (fixed over K; the k offset is added per stage)
     const uint16_t* asrc[A_LD];
@@ -385,47 +412,80 @@ struct TileBf16Direct {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     };
-    // fragments of slice kk+1 are read while the MFMAs of slice kk run
-    auto compute = [&](const char* sb) {
-      bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
-      read_frags(sb, 0, a0, b0);
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; kk += 2) {
-        read_frags(sb, kk + 1, a1, b1);
-        mfmas(a0, b0);
-        if (kk + 2 < BK / 16) read_frags(sb, kk + 2, a0, b0);
-        mfmas(a1, b1);
-      }
-    };
-    // Waits until slice ks+1 has landed in this wave's share of its stage,
-    // leaving the loads of the slices after it in flight, then meets the
-    // other waves.  A bare s_barrier, not __syncthreads(): the latter's
-    // release fence would also drain the loads still in flight.  Every LDS
-    // read of this slice has returned by now (the MFMAs consumed them).
-    auto sync_next = [&](int ks) {
-      const int later = min(NST - 2, nk - 2 - ks);  // slices issued after ks+1
-      if (later >= 2) wait_vmcnt<2 * LPS>();
-      else if (later == 1) wait_vmcnt<LPS>();
-      else wait_vmcnt<0>();
+    // Schedule of one K slice j (two 16-deep k-substeps), with the
+    // fragments of substep 0 already in registers (set 0):
+    //   first half:  MFMAs of substep 0, interleaved one for one with the
+    //                LDS reads of substep 1's fragments (set 1);
+    //   sync:        this wave's share of slice j+1 has landed and its LDS
+    //                reads of slice j are done; barrier (so slice j+1 is
+    //                complete and stage j is free in every wave);
+    //   second half: loads of slice j+NST into stage j, MFMAs of substep 1,
+    //                and the LDS reads of slice j+1's substep-0 fragments
+    //                (set 0), all interleaved.
+    // Every LDS read thus has 16 MFMAs of work to hide behind, and the
+    // matrix pipe has queued work on both sides of the barrier.
+    constexpr int ND = FM + 2 * FN;  // LDS reads per substep
+    constexpr int NM = FM * FN;      // MFMAs per substep
+    static_assert(BK == 32, "the interleaved schedule covers two k-substeps per slice");
+    bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+
+    // waits for this wave's loads up to slice j+1 (LATER slices' loads may stay
+    // in flight) and for its LDS reads, then meets the other waves.  A bare
+    // s_barrier: __syncthreads() would add a release fence that drains every
+    // load in flight.
+    auto sync_slices = [&](auto later_c) {
+      constexpr int N = decltype(later_c)::value * LPS;
+      __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);  // vmcnt(N) lgkmcnt(0)
       __asm__ volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
     };
-    // one K slice: issue the loads NST-1 slices ahead, compute this slice
-    auto step = [&](int cur, int ks) {
-      if (ks + NST - 1 < nk) load_stage(stages[(cur + NST - 1) % NST], ks + NST - 1);
-      compute(stages[cur]);
-      sync_next(ks);
+    // slice j in stage ST; LOAD: issue slice j+NST into stage ST after the
+    // barrier; NEXT: read slice j+1's first fragments from stage (ST+1)%NST;
+    // LATER: slices whose loads were issued after slice j+1's
+    auto slice = [&](auto st_c, auto load_c, auto next_c, auto later_c, int j) {
+      constexpr int ST = decltype(st_c)::value;
+      char* const sb = stages[ST];
+      read_frags(sb, 1, fa1, fb1);
+      mfmas(fa0, fb0);
+      interleave<NM, ND, 0>();
+      sync_slices(later_c);
+      if constexpr (decltype(load_c)::value) load_stage(sb, j + NST);
+      if constexpr (decltype(next_c)::value) read_frags(stages[(ST + 1) % NST], 0, fa0, fb0);
+      mfmas(fa1, fb1);
+      interleave<NM, decltype(next_c)::value ? ND : 0, decltype(load_c)::value ? LPS : 0>();
     };
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
 
+    // prologue: every stage loading, slice 0 landed everywhere, its first fragments read
 #pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-      if (s < nk) load_stage(stages[s], s);
-    sync_next(-1);
-    // K is a multiple of NST*BK (KSTEP): the stages rotate in whole rounds
-    for (int ks = 0; ks < nk; ks += NST) {
-#pragma unroll
-      for (int s = 0; s < NST; ++s) step(s, ks + s);
+    for (int s = 0; s < NST; ++s) load_stage(stages[s], s);
+    sync_slices(std::integral_constant<int, NST - 1>{});
+    read_frags(stages[0], 0, fa0, fb0);
+    // K is a multiple of NST*BK: whole rounds of NST slices, the last round
+    // without loads
+    for (int j0 = 0; j0 < nk - NST; j0 += NST) {
+      slice(std::integral_constant<int, 0>{}, T_{}, T_{}, std::integral_constant<int, NST - 2>{}, j0);
+      slice(std::integral_constant<int, 1>{}, T_{}, T_{}, std::integral_constant<int, NST - 2>{}, j0 + 1);
+      if constexpr (NST > 2)
+        slice(std::integral_constant<int, 2 % NST>{}, T_{}, T_{}, std::integral_constant<int, NST - 2>{}, j0 + 2);
+      if constexpr (NST > 3)
+        slice(std::integral_constant<int, 3 % NST>{}, T_{}, T_{}, std::integral_constant<int, NST - 2>{}, j0 + 3);
+    }
+    {
+      const int j0 = nk - NST;
+      slice(std::integral_constant<int, 0>{}, F_{}, T_{}, std::integral_constant<int, NST - 2>{}, j0);
+      if constexpr (NST == 2) {
+        slice(std::integral_constant<int, 1>{}, F_{}, F_{}, std::integral_constant<int, 0>{}, j0 + 1);
+      } else if constexpr (NST == 3) {
+        slice(std::integral_constant<int, 1>{}, F_{}, T_{}, std::integral_constant<int, 0>{}, j0 + 1);
+        slice(std::integral_constant<int, 2>{}, F_{}, F_{}, std::integral_constant<int, 0>{}, j0 + 2);
+      } else {
+        slice(std::integral_constant<int, 1>{}, F_{}, T_{}, std::integral_constant<int, 1>{}, j0 + 1);
+        slice(std::integral_constant<int, 2>{}, F_{}, T_{}, std::integral_constant<int, 0>{}, j0 + 2);
+        slice(std::integral_constant<int, 3>{}, F_{}, F_{}, std::integral_constant<int, 0>{}, j0 + 3);
+      }
     }
 #endif
   }
