@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a")
+    ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     return ap.parse_args()
@@ -131,7 +132,8 @@ def main():
         c = cfgs.GEMV_AR_DECODE
         log(f"inputs {c.name}")
         x, W = gen.gemv_ar_inputs(c.P, c.Mb, c.N, c.K, seed=0)
-        g = bf.GemvAR(c.P, c.Mb, c.N, c.K, c.in_dt, c.slot_dt, c.out_dt, c.tile_n, x, W)
+        gtile = args.gemv_tile or c.tile_n
+        g = bf.GemvAR(c.P, c.Mb, c.N, c.K, c.in_dt, c.slot_dt, c.out_dt, gtile, x, W)
         # 4 replicas of the weights (537 MB > the 256 MB Infinity Cache) rotate per call
         reps = [(g.x, g.W)] + [(g.x.clone(), g.W.clone()) for _ in range(3)]
         state = {"i": 0}
@@ -147,7 +149,7 @@ def main():
                       + 2 * c.P * c.Mb * c.N)                             # P windows written
         runs["gemv_ar"] = dict(call=gemv_call, obj=g, work=algo_bytes, unit="GB/s", bound="hbm",
                                peak=PEAK_HBM_GBS, bytes=algo_bytes, flops=c.flops,
-                               config=dict(workload=c.name, P=c.P, Mb=c.Mb, N=c.N, K=c.K, tile_n=c.tile_n,
+                               config=dict(workload=c.name, P=c.P, Mb=c.Mb, N=c.N, K=c.K, tile_n=gtile,
                                            weight_replicas=4))
     if "ag_gemm" in ops:
         c = cfgs.AG_GEMM_COL

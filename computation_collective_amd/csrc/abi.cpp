@@ -233,6 +233,9 @@ hocf_status hocf_gemv_ar(int P, int Mb, int N, int K, hocf_dtype in_dt, hocf_dty
   if (tile_n != 128 && tile_n != 256 && tile_n != 512)
     return fail(HOCF_ERR_UNSUPPORTED, "gemv_ar: tile_n=%d not in {128, 256, 512}", tile_n);
   if (N % 8 || K % 8) return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: N and K must be multiples of 8");
+  // partials and windows are addressed with 32-bit byte offsets
+  if ((int64_t)Mb * N * 4 >= ((int64_t)1 << 31))
+    return fail(HOCF_ERR_UNSUPPORTED, "gemv_ar: Mb * N = %lld elements exceeds 2^29", (long long)Mb * N);
   hocf_status st = check_sync(sync, hocf_gemv_ar_workspace_bytes(P, N, tile_n));
   if (st != HOCF_OK) return st;
   if (Mb == 0 || N == 0) return ok();

@@ -15,37 +15,67 @@
 // The partial is published to part[p] with a ready flag; the last of the P
 // producers of column tile j (an arrival counter) folds the P partials in
 // rank order in fp32, rounds once, and writes the same bits into all P
-// receive windows, releasing each window's flag.
+// receive windows, releasing each window's flag.  Partials and window data
+// move with device-coherent 16- or 8-byte stores and loads, each writer
+// waiting for its stores before the flag or count that announces them
+// (publish.hpp), so no L2-wide write-back or invalidate is needed.
 #include "internal.hpp"
+#include "publish.hpp"
 #include "sync.hpp"
 
 namespace hocf {
 
 constexpr int kGemvThreads = 256;
-constexpr int kGemvKC = 512;  // rows of x staged in LDS per pass
-constexpr int kGemvUnroll = 16;
+constexpr int kGemvKC = 1024;  // rows of x staged in LDS per pass
+constexpr int kGemvU = 16;     // weight rows per load batch (two batches in flight)
+
+// 4 consecutive fp32 values as SDT at byte offset off of a device-coherent resource
+template <int DT>
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx4 v) {
+  if constexpr (DT == kBF16) {
+    const u32x2 u = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(u, r, (int)off, 0, kPolicyDevice);
+  } else {
+    st_dev16(r, off, 0, __builtin_bit_cast(u32x4, v));
+  }
+}
+template <int DT>
+__device__ __forceinline__ floatx4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (DT == kBF16) {
+    const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kPolicyDevice);
+    return floatx4{bf16_to_f32(u[0] & 0xffffu), bf16_to_f32(u[0] >> 16), bf16_to_f32(u[1] & 0xffffu),
+                   bf16_to_f32(u[1] >> 16)};
+  } else {
+    return __builtin_bit_cast(floatx4, ld_dev16(r, off, 0));
+  }
+}
 
 template <int MB, int TN, int SDT, int ODT>
-__global__ __launch_bounds__(kGemvThreads) void gemv_ar_kernel(GemvArArgs a) {
-  constexpr int NCG = TN / 8;               // column groups
+__global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) {
+  constexpr int NCG = TN / 8;               // 16-byte column groups
   constexpr int KL = kGemvThreads / NCG;    // k-lanes
+  constexpr int U = kGemvU;
+  constexpr int XS_BYTES = kGemvKC * MB * 4;
+  constexpr int RED_BYTES = KL * MB * TN * 4;
   static_assert(NCG * KL == kGemvThreads, "thread layout");
-  __shared__ float xs[MB][kGemvKC];
-  __shared__ float red[KL][MB][TN];
+  constexpr int NQ = MB * TN / 4;            // output quads (4 columns of one row) per tile
+  // x staging [k][MB] during the row loop, k-lane fold [KL][MB][TN] after it
+  __shared__ __attribute__((aligned(16))) float lds[(XS_BYTES > RED_BYTES ? XS_BYTES : RED_BYTES) / 4];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int cg = tid % NCG, kl = tid / NCG;
   const int N = a.N, K = a.K, P = a.P, Mb = a.Mb;
+  constexpr int SES = SDT == kBF16 ? 2 : 4, OES = ODT == kBF16 ? 2 : 4;
   uint32_t* grp = a.ws + kWsExtra;
 
   for (int64_t item = blockIdx.x; item < a.total; item += gridDim.x) {
     const int p = (int)(item / a.ntiles), j = (int)(item % a.ntiles);
     const int n0 = j * TN;
     const int cols_valid = min(TN, N - n0);
-    const int ncol = n0 + cg * 8;
     const bool col_ok = cg * 8 < cols_valid;
-    const uint16_t* Wp = a.W + (int64_t)p * K * N + ncol;
+    // columns of a ragged tile's idle groups are clamped to a valid one (loaded, never used)
+    const uint16_t* Wp = a.W + (int64_t)p * K * N + n0 + min(cg * 8, cols_valid - 8);
     const uint16_t* xp = a.x + (int64_t)p * Mb * K;
 
     float acc[MB][8];
@@ -56,90 +86,139 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ar_kernel(GemvArArgs a) {
 
     for (int kc = 0; kc < K; kc += kGemvKC) {
       const int kn = min(kGemvKC, K - kc);
-      __syncthreads();
-      for (int e = tid; e < MB * kGemvKC; e += kGemvThreads) {
-        const int b = e / kGemvKC, k = e % kGemvKC;
-        xs[b][k] = (b < Mb && k < kn) ? bf16_to_f32(xp[(int64_t)b * K + kc + k]) : 0.0f;
-      }
-      __syncthreads();
-      if (col_ok) {
-        // rows kl, kl + KL, ... of this pass, kGemvUnroll loads in flight
-        for (int k0 = kl; k0 < kn; k0 += KL * kGemvUnroll) {
-          uint4 w[kGemvUnroll];
+      // this thread's rows: kl, kl + KL, ..., two batches of U loads in flight
+      const int nr = (col_ok && kl < kn) ? (kn - kl + KL - 1) / KL : 0;
+      const uint16_t* w0 = Wp + (int64_t)kc * N;
+      uint4 wa[U], wb[U];
+      // unconditional loads (a guarded load becomes a branch and a full wait):
+      // rows past this thread's last are clamped to row kn-1, loaded and not used
+      auto load = [&](uint4 (&w)[U], int i0) {
 #pragma unroll
-          for (int u = 0; u < kGemvUnroll; ++u) {
-            const int k = k0 + u * KL;
-            w[u] = k < kn ? *reinterpret_cast<const uint4*>(Wp + (int64_t)(kc + k) * N)
-                          : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < U; ++u) {
+          const int k = min(kl + (i0 + u) * KL, kn - 1);
+          w[u] = *reinterpret_cast<const uint4*>(w0 + (int64_t)k * N);
+        }
+      };
+      auto consume = [&](const uint4 (&w)[U], int i0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (i0 + u >= nr) break;
+          const int k = kl + (i0 + u) * KL;
+          float xv[MB];
+          if constexpr (MB % 4 == 0) {
+#pragma unroll
+            for (int b = 0; b < MB; b += 4) {
+              const floatx4 t = *reinterpret_cast<const floatx4*>(&lds[k * MB + b]);
+              xv[b] = t[0]; xv[b + 1] = t[1]; xv[b + 2] = t[2]; xv[b + 3] = t[3];
+            }
+          } else {
+#pragma unroll
+            for (int b = 0; b < MB; ++b) xv[b] = lds[k * MB + b];
           }
+          const uint32_t wd[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
-          for (int u = 0; u < kGemvUnroll; ++u) {
-            const int k = k0 + u * KL;
-            if (k < kn) {
-              const uint32_t wd[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+          for (int c = 0; c < 4; ++c) {
+            const float lo = bf16_to_f32(wd[c] & 0xffffu), hi = bf16_to_f32(wd[c] >> 16);
 #pragma unroll
-              for (int b = 0; b < MB; ++b) {
-                const float xv = xs[b][k];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                  acc[b][2 * c] = fmaf(xv, bf16_to_f32(wd[c] & 0xffffu), acc[b][2 * c]);
-                  acc[b][2 * c + 1] = fmaf(xv, bf16_to_f32(wd[c] >> 16), acc[b][2 * c + 1]);
-                }
-              }
+            for (int b = 0; b < MB; ++b) {
+              acc[b][2 * c] = fmaf(xv[b], lo, acc[b][2 * c]);
+              acc[b][2 * c + 1] = fmaf(xv[b], hi, acc[b][2 * c + 1]);
             }
           }
         }
+      };
+      // x first (16-byte pieces x[b][k .. k+7]), then two batches of weight
+      // rows: the vector-memory counter completes in issue order, so the wait
+      // for x does not include the weight loads issued after it
+      constexpr int XL = (MB * kGemvKC / 8 + kGemvThreads - 1) / kGemvThreads;
+      const int npc = kn / 8;  // 16-byte pieces per row of x in this pass
+      uint4 xr[XL];
+#pragma unroll
+      for (int t = 0; t < XL; ++t) {  // pieces past x's end are clamped to its last piece (not used)
+        const int e = min(tid + t * kGemvThreads, Mb * npc - 1);
+        xr[t] = *reinterpret_cast<const uint4*>(xp + (int64_t)(e / npc) * K + kc + (e % npc) * 8);
+      }
+      load(wa, 0);
+      load(wb, U);
+      lds_barrier();  // the previous pass (or item) is done with lds
+#pragma unroll
+      for (int t = 0; t < XL; ++t) {
+        const int e = tid + t * kGemvThreads, b = e / npc, k0 = (e % npc) * 8;
+        if (e < MB * npc) {
+          const uint32_t wd[4] = {xr[t].x, xr[t].y, xr[t].z, xr[t].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            lds[(k0 + 2 * c) * MB + b] = b < Mb ? bf16_to_f32(wd[c] & 0xffffu) : 0.0f;
+            lds[(k0 + 2 * c + 1) * MB + b] = b < Mb ? bf16_to_f32(wd[c] >> 16) : 0.0f;
+          }
+        }
+      }
+      lds_barrier();
+      for (int i0 = 0; i0 < nr; i0 += 2 * U) {
+        consume(wa, i0);
+        load(wa, i0 + 2 * U);
+        consume(wb, i0 + U);
+        load(wb, i0 + 3 * U);
       }
     }
 
-    // fold the k-lanes in order kl = 0..KL-1
+    // fold the k-lanes in order kl = 0..KL-1, one output quad per thread
+    lds_barrier();  // every thread is done reading x from lds
 #pragma unroll
     for (int b = 0; b < MB; ++b)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) red[kl][b][cg * 8 + c] = acc[b][c];
+      for (int c = 0; c < 8; c += 4)
+        *reinterpret_cast<floatx4*>(&lds[(kl * MB + b) * TN + cg * 8 + c]) =
+            floatx4{acc[b][c], acc[b][c + 1], acc[b][c + 2], acc[b][c + 3]};
     __syncthreads();
-    const int64_t pstride = (int64_t)Mb * N;
-    for (int e = tid; e < MB * TN; e += kGemvThreads) {
-      const int b = e / TN, col = e % TN;
-      if (b < Mb && col < cols_valid) {
-        float s = red[0][b][col];
-        for (int q = 1; q < KL; ++q) s += red[q][b][col];
-        st1<SDT>(a.part, p * pstride + (int64_t)b * N + n0 + col, s);
-      }
+    const __amdgpu_buffer_rsrc_t rpart = raw_rsrc(reinterpret_cast<char*>(a.part) + (int64_t)p * Mb * N * SES);
+    for (int e = tid; e < NQ; e += kGemvThreads) {
+      const int qb = e / (TN / 4), qc = (e % (TN / 4)) * 4;  // row, first column of the quad
+      if (qb >= Mb || qc >= cols_valid) continue;
+      floatx4 s = *reinterpret_cast<const floatx4*>(&lds[qb * TN + qc]);
+      for (int q = 1; q < KL; ++q) s = s + *reinterpret_cast<const floatx4*>(&lds[(q * MB + qb) * TN + qc]);
+      st_dev4<SDT>(rpart, (uint32_t)(qb * N + n0 + qc) * SES, s);
     }
+    wait_memory();
     __syncthreads();
 
+    // ready flag; arrival count -> the last producer of tile j reduces
     if (tid == 0) {
-      release_flag(&a.part_flags[(int64_t)p * a.ntiles + j], a.sync.epoch);
+      __hip_atomic_store(&a.part_flags[(int64_t)p * a.ntiles + j], a.sync.epoch, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      wait_memory();  // the flag is visible before the count that announces it
       uint32_t* cnt = &grp[j];
-      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int last = (prev == (uint32_t)(P - 1));
       if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = last;
     }
     __syncthreads();
     if (uniform(s_last)) {
-      acquire_agent();
       if (tid < P && load_flag_agent(&a.part_flags[(int64_t)tid * a.ntiles + j]) != a.sync.epoch)
         report_status(a.sync, kErrProtocol);
-      for (int e = tid; e < Mb * TN; e += kGemvThreads) {
-        const int b = e / TN, col = e % TN;
-        if (col >= cols_valid) continue;
-        const int64_t off = (int64_t)b * N + n0 + col;
-        float v[kMaxP];
+      for (int e = tid; e < NQ; e += kGemvThreads) {
+        const int qb = e / (TN / 4), qc = (e % (TN / 4)) * 4;
+        if (qb >= Mb || qc >= cols_valid) continue;
+        const uint32_t qoff = (uint32_t)(qb * N + n0 + qc);  // element offset in a [Mb][N] array
+        floatx4 v[kMaxP];
 #pragma unroll
-        for (int q = 0; q < kMaxP; ++q)
-          if (q < P) v[q] = ld1<SDT>(a.part, q * pstride + off);
-        float s = v[0];
+        for (int q = 0; q < kMaxP; ++q) {
+          const int qq = q < P ? q : P - 1;  // loads stay unconditional; slots past P are not added
+          v[q] = ld_dev4<SDT>(raw_rsrc(reinterpret_cast<char*>(a.part) + (int64_t)qq * Mb * N * SES),
+                              qoff * SES);
+        }
+        floatx4 s = v[0];
 #pragma unroll
         for (int q = 1; q < kMaxP; ++q)
-          if (q < P) s += v[q];
-        for (int q = 0; q < P; ++q) st1<ODT>(a.win_data[q], off, s);
+          if (q < P) s = s + v[q];
+        for (int q = 0; q < P; ++q) st_dev4<ODT>(raw_rsrc(a.win_data[q]), qoff * OES, s);
       }
+      wait_memory();
       __syncthreads();
-      if (tid < P) release_flag(&a.win_flags[tid][j], a.sync.epoch);
+      if (tid < P)
+        __hip_atomic_store(&a.win_flags[tid][j], a.sync.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
   }
 }
 

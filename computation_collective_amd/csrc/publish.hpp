@@ -67,6 +67,16 @@ __device__ __forceinline__ int opaque_lane() {
 // s_waitcnt vmcnt(0): every load and store this wave issued has completed.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// accesses (lgkmcnt(0)) but not for its global loads, which stay in flight.
+// (__syncthreads() would also drain those.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // Staging geometry of one wave's 32-row accumulator block.
 template <class Tile, int DT>
 struct PublishLayout {
