@@ -127,9 +127,10 @@ __global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) 
           }
         }
       };
-      // x first (16-byte pieces x[b][k .. k+7]), then two batches of weight
-      // rows: the vector-memory counter completes in issue order, so the wait
-      // for x does not include the weight loads issued after it
+      // x first (16-byte pieces x[b][k .. k+7]), then the first batch of
+      // weight rows, the second once x is in LDS: the vector-memory counter
+      // completes in issue order, so the wait for x includes no weight load,
+      // and x does not queue behind a full double batch of them
       constexpr int XL = (MB * kGemvKC / 8 + kGemvThreads - 1) / kGemvThreads;
       const int npc = kn / 8;  // 16-byte pieces per row of x in this pass
       uint4 xr[XL];
@@ -139,7 +140,6 @@ __global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) 
         xr[t] = *reinterpret_cast<const uint4*>(xp + (int64_t)(e / npc) * K + kc + (e % npc) * 8);
       }
       load(wa, 0);
-      load(wb, U);
       lds_barrier();  // the previous pass (or item) is done with lds
 #pragma unroll
       for (int t = 0; t < XL; ++t) {
@@ -154,6 +154,7 @@ __global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) 
         }
       }
       lds_barrier();
+      load(wb, U);
       for (int i0 = 0; i0 < nr; i0 += 2 * U) {
         consume(wa, i0);
         load(wa, i0 + 2 * U);
