@@ -60,9 +60,10 @@ def cpu_baseline(target_s):
     (an exact sub-problem: same P, N, K and chunk structure)."""
     import numpy as np
 
-    cores = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16") or 16), 16)
-    os.environ["OMP_NUM_THREADS"] = str(cores)
+    want = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16") or 16), 16)
     import oracle
+    oracle.set_threads(want)
+    cores = oracle.max_threads()
     from computation_collective_amd import configs as cfgs
     from computation_collective_amd import inputs as gen
 
@@ -125,6 +126,7 @@ def main():
                       + 2 * (4 if sdt == bf.F32 else 2) * c.P * c.M * c.N  # slots written + read
                       + 2 * c.M * c.N)                                     # out written
         runs["gemm_rs"] = dict(call=lambda r=r: r.run(stream), obj=r, work=flops, unit="TFLOP/s",
+                               variant=f"slot_dtype={args.slot_dtype} tile={c.tile_m}x{c.tile_n}",
                                bound="mfma", peak=PEAK_BF16_TFLOPS, bytes=algo_bytes,
                                config=dict(workload=c.name, P=c.P, M=c.M, N=c.N, K=c.K,
                                            tile=[c.tile_m, c.tile_n], slot_dtype=args.slot_dtype))
@@ -148,6 +150,7 @@ def main():
                       + 2 * 4 * c.P * c.Mb * c.N                          # partials written + read
                       + 2 * c.P * c.Mb * c.N)                             # P windows written
         runs["gemv_ar"] = dict(call=gemv_call, obj=g, work=algo_bytes, unit="GB/s", bound="hbm",
+                               variant=f"tile_n={gtile} weight_replicas=4",
                                peak=PEAK_HBM_GBS, bytes=algo_bytes, flops=c.flops,
                                config=dict(workload=c.name, P=c.P, Mb=c.Mb, N=c.N, K=c.K, tile_n=gtile,
                                            weight_replicas=4))
@@ -163,6 +166,7 @@ def main():
 
         algo_bytes = 2 * (c.P * c.Mc * c.K + c.K * c.N + c.P * c.Mc * c.N)
         runs["ag_gemm"] = dict(call=ag_call, obj=a, work=c.flops, unit="TFLOP/s", bound="mfma",
+                               variant=f"tile={c.tile_m}x{c.tile_n} prereleased",
                                peak=PEAK_BF16_TFLOPS, bytes=algo_bytes,
                                config=dict(workload=c.name, P=c.P, Mc=c.Mc, N=c.N, K=c.K,
                                            tile=[c.tile_m, c.tile_n], release_order=[int(v) for v in order]))
@@ -176,15 +180,17 @@ def main():
                       + 4 * c.T * c.B * c.L          # indices
                       + 4 * c.T * c.B * c.D)         # pooled rows written to the buckets
         runs["embbag_a2a"] = dict(call=lambda e=e: e.run(stream), obj=e, work=algo_bytes, unit="GB/s",
+                                  variant=f"tile_bags={c.tile_bags}",
                                   bound="hbm", peak=PEAK_HBM_GBS, bytes=algo_bytes,
                                   config=dict(workload=c.name, T=c.T, R=c.R, D=c.D, B=c.B, L=c.L, P=c.P,
                                               tile_bags=c.tile_bags, zipf_alpha=c.alpha))
     if "copy" in ops:
-        # plain device copy of a known size: the calibration for the HBM byte counters
+        # a plain elementwise pass over 1 GiB (read 1 GiB, write 1 GiB; a negating copy, so its
+        # kernel is told apart from the runtime's own copies): the calibration of the HBM counters
         nbytes = 1 << 30
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
-        runs["copy"] = dict(call=lambda src=src, dst=dst: dst.copy_(src), obj=None, work=2 * nbytes,
+        runs["copy"] = dict(call=lambda src=src, dst=dst: torch.neg(src, out=dst), obj=None, work=2 * nbytes,
                             unit="GB/s", bound="hbm", peak=PEAK_HBM_GBS, bytes=2 * nbytes,
                             config=dict(workload="device copy 1 GiB (counter calibration)"))
     torch.cuda.synchronize()
@@ -224,25 +230,25 @@ def main():
         if st != 0:
             raise SystemExit(f"{n}: device status {st} ({hocf.status_string(st)})")
 
+    from computation_collective_amd import profsum
     out_ops = {}
     for n in names:
         ms = [a.elapsed_time(b) for a, b in ev[n]]
-        med = median(ms)
+        avg = sum(ms) / len(ms)
         R = runs[n]
-        if R["unit"] == "TFLOP/s":
-            v = R["work"] / (med * 1e-3) / 1e12
-        else:
-            v = R["work"] / (med * 1e-3) / 1e9
+        scale = 1e12 if R["unit"] == "TFLOP/s" else 1e9
+        v = R["work"] / (avg * 1e-3) / scale          # per launch, over the average launch duration
+        tb = profsum.traffic(n, R.get("variant"))      # scaled HBM bytes per launch, if current
         out_ops[n] = {
-            "value": round(v, 2), "unit": R["unit"], "ms_median": round(med, 4),
+            "value": round(v, 2), "unit": R["unit"], "ms_avg": round(avg, 4), "ms_median": round(median(ms), 4),
             "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4),
             "roofline": {"bound": R["bound"], "achieved": round(v, 2), "peak": R["peak"],
                          "unit": R["unit"] if R["bound"] == "mfma" else "GB/s",
-                         "frac": round(v / R["peak"], 4), "traffic": None},
+                         "frac": round(v / R["peak"], 4), "traffic": None if tb is None else int(tb)},
             "algo_bytes": R["bytes"],
             "config": R["config"],
         }
-        log(f"{n}: {v:.1f} {R['unit']} ({med:.4f} ms median, {100 * v / R['peak']:.1f}% of peak)")
+        log(f"{n}: {v:.1f} {R['unit']} ({avg:.4f} ms average, {100 * v / R['peak']:.1f}% of peak)")
 
     head = "gemm_rs" if "gemm_rs" in out_ops else names[0]
     res = {

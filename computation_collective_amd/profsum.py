@@ -1,0 +1,164 @@
+"""Summaries of rocprofv3 CSV output for the profiles/ folder, and the
+reader bench.py uses for the HBM traffic figures.
+
+  python -m computation_collective_amd.profsum STATS_DIR FETCH_DIR WRITE_DIR OUT_DIR \\
+         "STATS_COMMAND" "COUNTER_COMMAND"
+
+reads a `rocprofv3 --kernel-trace --stats --output-format csv` run and two
+`rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (COUNTER_COMMAND has
+the word COUNTER where the counter name goes) of bench.py, and writes one
+summary per operator, `OUT_DIR/<workload>.txt`:
+
+  * the kernel's call count and average / min / max duration;
+  * FETCH_SIZE and WRITE_SIZE in KiB per dispatch (median over dispatches),
+    the same counters for the 1 GiB calibration pass (a negating copy that
+    reads and writes 1 GiB), the factors known/measured they give, and the
+    scaled HBM bytes per launch;
+  * the hash of the library sources the counters were taken with, and the
+    variant (slot dtype, tile) that was profiled.
+
+`traffic(op, variant)` returns the scaled bytes, or None when there is no
+summary, it was taken for another variant, or the sources have changed.
+"""
+
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import os
+import statistics
+import sys
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 1 << 30  # the calibration pass reads and writes 1 GiB
+
+# kernel-name fragment -> operator name used by bench.py
+KERNELS = [("gemm_rs_kernel", "gemm_rs"), ("gemv_ar_kernel", "gemv_ar"),
+           ("ag_gemm_kernel", "ag_gemm"), ("embbag_kernel", "embbag_a2a"),
+           ("neg_kernel", "copy")]
+
+
+def workloads():
+    """operator -> (workload name, variant key) of bench.py's default run."""
+    from . import configs as c
+    return {
+        "gemm_rs": (c.GEMM_RS_MLP.name, f"slot_dtype=f32 tile={c.GEMM_RS_MLP.tile_m}x{c.GEMM_RS_MLP.tile_n}"),
+        "gemv_ar": (c.GEMV_AR_DECODE.name, f"tile_n={c.GEMV_AR_DECODE.tile_n} weight_replicas=4"),
+        "ag_gemm": (c.AG_GEMM_COL.name, f"tile={c.AG_GEMM_COL.tile_m}x{c.AG_GEMM_COL.tile_n} prereleased"),
+        "embbag_a2a": (c.EMBBAG_DLRM.name, f"tile_bags={c.EMBBAG_DLRM.tile_bags}"),
+    }
+
+
+def source_hash() -> str:
+    """sha256 over the library's HIP/C++ sources and the ABI header."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*"))) + [os.path.join(ROOT, "include", "hocf.h")]
+    for f in files:
+        if os.path.isfile(f):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def op_of(kernel_name: str):
+    for frag, op in KERNELS:
+        if frag in kernel_name:
+            return op
+    return None
+
+
+def _find_csv(path: str, suffix: str) -> str:
+    hits = glob.glob(os.path.join(path, "**", "*" + suffix), recursive=True)
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {path}")
+    return hits[0]
+
+
+def counter_medians(path: str, counter: str) -> dict:
+    """op -> median over dispatches of the counter summed over its instances."""
+    per = defaultdict(lambda: defaultdict(float))
+    for r in csv.DictReader(open(_find_csv(path, "counter_collection.csv"))):
+        if r["Counter_Name"] != counter:
+            continue
+        op = op_of(r["Kernel_Name"])
+        if op:
+            per[op][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {op: statistics.median(d.values()) for op, d in per.items()}
+
+
+def kernel_stats(path: str) -> dict:
+    out = {}
+    for r in csv.DictReader(open(_find_csv(path, "kernel_stats.csv"))):
+        op = op_of(r["Name"])
+        if op and op not in out:
+            out[op] = (r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                       float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3)
+    return out
+
+
+def summarize(stats_dir, fetch_dir, write_dir, out_dir, stats_cmd, counter_cmd) -> None:
+    stats = kernel_stats(stats_dir)
+    fetch = counter_medians(fetch_dir, "FETCH_SIZE")
+    write = counter_medians(write_dir, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("the calibration pass is missing from the counter runs")
+    ff = COPY_BYTES / 1024.0 / fetch["copy"]
+    fw = COPY_BYTES / 1024.0 / write["copy"]
+    src = source_hash()
+    os.makedirs(out_dir, exist_ok=True)
+    for op, (wl, variant) in workloads().items():
+        if op not in stats:
+            continue
+        name, calls, avg, mn, mx = stats[op]
+        lines = [f"# rocprofv3 summary: {op} kernel, workload {wl}",
+                 f"# kernel statistics: {stats_cmd}",
+                 f"# counters (one run per counter): {counter_cmd}",
+                 f"# calibration: a 1 GiB negating copy in the same runs reads FETCH_SIZE {fetch['copy']:.0f} KiB"
+                 f" and WRITE_SIZE {write['copy']:.0f} KiB for 1048576 KiB each",
+                 f"kernel {name}",
+                 f"variant {variant}",
+                 f"sources {src}",
+                 f"stats calls={calls} avg_us={avg:.2f} min_us={mn:.2f} max_us={mx:.2f}"]
+        if op in fetch and op in write:
+            b = fetch[op] * 1024 * ff + write[op] * 1024 * fw
+            lines.append(f"counters fetch_kib={fetch[op]:.0f} write_kib={write[op]:.0f} "
+                         f"fetch_factor={ff:.4f} write_factor={fw:.4f} hbm_bytes={b:.0f}")
+        with open(os.path.join(out_dir, wl + ".txt"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+
+
+def _fields(path):
+    d = {}
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        key, _, rest = line.rstrip("\n").partition(" ")
+        d[key] = rest
+    return d
+
+
+def traffic(op: str, variant: str | None = None):
+    """Scaled HBM bytes per launch of `op` from its committed summary, or None
+    when there is none, it covers another variant, or the sources changed."""
+    wl = workloads().get(op)
+    if wl is None:
+        return None
+    path = os.path.join(PROFILES, wl[0] + ".txt")
+    if not os.path.isfile(path):
+        return None
+    d = _fields(path)
+    if d.get("sources") != source_hash() or d.get("variant") != (variant or wl[1]) or "counters" not in d:
+        return None
+    kv = dict(x.split("=") for x in d["counters"].split())
+    return float(kv["hbm_bytes"])
+
+
+if __name__ == "__main__":
+    if len(sys.argv) != 7:
+        raise SystemExit(__doc__)
+    summarize(*sys.argv[1:7])

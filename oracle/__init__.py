@@ -38,6 +38,8 @@ def _load():
         lib.oracle_ag_gemm.argtypes = [i32] * 6 + [vp] * 4
         lib.oracle_ag_gemm_points.argtypes = [i32] * 6 + [vp, vp, i64, vp, vp, vp]
         lib.oracle_embbag_a2a.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp]
+        lib.oracle_set_threads.argtypes = [i32]
+        lib.oracle_max_threads.restype = i32
         for f in (lib.oracle_gemm_rs, lib.oracle_gemm_rs_points, lib.oracle_gemv_ar,
                   lib.oracle_ag_gemm, lib.oracle_ag_gemm_points, lib.oracle_embbag_a2a):
             f.restype = ctypes.c_int
@@ -62,8 +64,14 @@ def _check(dt, *arrays):
 
 
 def set_threads(n: int) -> None:
-    """Number of OpenMP threads the oracle uses (call before the first use)."""
+    """Number of OpenMP threads the oracle uses from now on."""
     os.environ["OMP_NUM_THREADS"] = str(int(n))
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    """Threads the oracle's parallel regions will use."""
+    return int(_load().oracle_max_threads())
 
 
 def gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, A, W, want_slots=True):

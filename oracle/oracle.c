@@ -39,6 +39,7 @@
  * Every function returns 0 on success, -1 on an invalid argument.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -281,3 +282,11 @@ int oracle_embbag_a2a(int T, int64_t R, int D, int B, int L, int P, const float*
     }
     return bad ? -2 : 0;
 }
+
+/* Thread control for the timing harness (no arithmetic): the OpenMP runtime
+   may already be initialised by the host process, so the environment
+   variable alone does not reach it. */
+void oracle_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+int oracle_max_threads(void) { return omp_get_max_threads(); }
