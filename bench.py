@@ -9,6 +9,11 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
   ag_gemm     AllGather+GEMM, 8 chunks 1024x4096, W 4096x1792 bf16, chunk flags written in a
               seeded random order on the kernel's stream just before it
   embbag_a2a  64 tables 1e6x128 fp32, batch 16384, 20 rows per bag, Zipf(1.05), P=8
+              (a 1 GiB scratch write between calls, outside the timed events)
+
+Optional extra ops (--ops): embbag_uniform (the same shapes with uniform indices:
+no reuse, a control for the Zipf figure) and copy (a 1 GiB negating copy, the
+calibration of the HBM byte counters).
 
 `value` is the GEMM+ReduceScatter throughput (TFLOP/s, the headline kernel);
 each operator's own throughput and roofline fraction are in `ops`.  Each
@@ -179,11 +184,30 @@ def main():
         algo_bytes = (4 * c.T * c.B * c.L * c.D      # every looked-up row (logical, no dedup)
                       + 4 * c.T * c.B * c.L          # indices
                       + 4 * c.T * c.B * c.D)         # pooled rows written to the buckets
+        # a 1 GiB scratch write between calls (untimed: each call has its own events) keeps the
+        # 256 MB Infinity Cache from carrying rows over from the previous call; reuse inside a
+        # call (Zipf) is the workload's own locality
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         runs["embbag_a2a"] = dict(call=lambda e=e: e.run(stream), obj=e, work=algo_bytes, unit="GB/s",
+                                  pre=lambda f=flush: f.fill_(0.0),
                                   variant=f"tile_bags={c.tile_bags}",
                                   bound="hbm", peak=PEAK_HBM_GBS, bytes=algo_bytes,
                                   config=dict(workload=c.name, T=c.T, R=c.R, D=c.D, B=c.B, L=c.L, P=c.P,
                                               tile_bags=c.tile_bags, zipf_alpha=c.alpha))
+    if "embbag_uniform" in ops:
+        # control: the same shapes with uniform indices (no reuse), so logical ~ DRAM bytes
+        c = cfgs.EMBBAG_DLRM
+        if "embbag_a2a" not in ops:
+            tables = gen.embbag_tables_torch(c.T, c.R, c.D, seed=0, device=dev)
+        uidx = gen.uniform_indices(c.T, c.B, c.L, c.R, seed=1)
+        eu = bf.EmbbagA2A(c.T, c.R, c.D, c.B, c.L, c.P, c.tile_bags, tables, uidx)
+        flush_u = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        algo_bytes = 4 * c.T * c.B * c.L * c.D + 4 * c.T * c.B * c.L + 4 * c.T * c.B * c.D
+        runs["embbag_uniform"] = dict(call=lambda e=eu: e.run(stream), obj=eu, work=algo_bytes, unit="GB/s",
+                                      pre=lambda f=flush_u: f.fill_(0.0), variant="uniform indices",
+                                      bound="hbm", peak=PEAK_HBM_GBS, bytes=algo_bytes,
+                                      config=dict(workload=c.name + "_uniform_indices", T=c.T, R=c.R, D=c.D,
+                                                  B=c.B, L=c.L, P=c.P, tile_bags=c.tile_bags))
     if "copy" in ops:
         # a plain elementwise pass over 1 GiB (read 1 GiB, write 1 GiB; a negating copy, so its
         # kernel is told apart from the runtime's own copies): the calibration of the HBM counters
@@ -200,6 +224,8 @@ def main():
 
     def step(record):
         for n in names:
+            if "pre" in runs[n]:
+                runs[n]["pre"]()
             if record:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -239,8 +265,10 @@ def main():
         scale = 1e12 if R["unit"] == "TFLOP/s" else 1e9
         v = R["work"] / (avg * 1e-3) / scale          # per launch, over the average launch duration
         tb = profsum.traffic(n, R.get("variant"))      # scaled HBM bytes per launch, if current
+        srt = sorted(ms)
         out_ops[n] = {
             "value": round(v, 2), "unit": R["unit"], "ms_avg": round(avg, 4), "ms_median": round(median(ms), 4),
+            "ms_p10": round(srt[int(0.1 * (len(srt) - 1))], 4), "ms_p90": round(srt[int(0.9 * (len(srt) - 1))], 4),
             "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4),
             "roofline": {"bound": R["bound"], "achieved": round(v, 2), "peak": R["peak"],
                          "unit": R["unit"] if R["bound"] == "mfma" else "GB/s",

@@ -47,10 +47,13 @@
  * caller zeroes *status before the call and reads it after.
  *
  * Flags.  Flag words are uint32 and hold an epoch: a word equals
- * sync->epoch once the data it guards is complete and visible device-wide
- * (release by the producer, acquire by the consumer, agent scope).  Each
- * call must use an epoch different from the previous call on the same flag
- * arrays, so flags never need resetting.
+ * sync->epoch once the data it guards is complete and visible device-wide.
+ * The library's producers write guarded data with device-coherent stores
+ * and wait for their completion before the flag store; a consumer that sees
+ * the epoch (agent-scope atomic load) and then reads the data either with
+ * device-coherent loads or after an agent-scope acquire fence sees it all.
+ * Each call must use an epoch different from the previous call on the same
+ * flag arrays, so flags never need resetting.
  *
  * Workspace.  Scheduler counters.  The caller allocates at least the size
  * the matching *_workspace_bytes() query returns, zeroes it ONCE, and may
