@@ -168,13 +168,20 @@ class AgGemm(_Common):
                                  self.chunk_flags, self.W, self.out, self.tile_m, self.tile_n,
                                  sync_, stream)
 
-    def run_prereleased(self, order, stream=None, **kw):
-        """Flags written in `order` on the kernel's stream, then the kernel."""
+    def prerelease(self, order, stream=None, **kw):
+        """Writes the chunk flags in `order` on `stream` for the next call; returns its sync."""
         assert self.flags_mode == "device"
         s = self.next_sync(**kw)
+        hocf.release_chunks(stream or torch.cuda.current_stream(), self.chunk_flags, order, s.epoch)
+        return s
+
+    def launch(self, sync_, stream=None):
+        hocf.check(self.call(sync_, stream or torch.cuda.current_stream()))
+
+    def run_prereleased(self, order, stream=None, **kw):
+        """Flags written in `order` on the kernel's stream, then the kernel."""
         stream = stream or torch.cuda.current_stream()
-        hocf.release_chunks(stream, self.chunk_flags, order, s.epoch)
-        hocf.check(self.call(s, stream))
+        self.launch(self.prerelease(order, stream, **kw), stream)
 
     def run_host_released(self, order, delay_s=0.0, deliver=None, stream=None, **kw):
         """Kernel first; then the host sets the flags of `order` one by one (after

@@ -7,26 +7,29 @@
 //
 // Chunk c of the gathered A (rows [c*Mc, (c+1)*Mc)) is written by someone
 // else -- a copy engine, another stream, a peer -- which then sets
-// chunk_flags[c] = epoch.  The kernel's persistent workgroups claim output
-// tiles only from chunks whose flag has arrived, earliest arrival first:
-// the first workgroup that sees a chunk's flag appends the chunk to an
-// arrival list in the workspace, and every workgroup walks that list in
-// order, taking the next unclaimed tile of the first chunk that still has
-// one.  A workgroup acquires (system scope: the writer may be a DMA engine)
-// the first time it uses a chunk.  Tiles are computed identically whatever
-// the order, so the output does not depend on the release order.
+// chunk_flags[c] = epoch.  Chunks are served in arrival order: the first
+// workgroup that sees a chunk's flag appends the chunk to an arrival list in
+// the workspace.  Tiles are dealt from one ticket counter: ticket t is tile
+// (t mod Tc) of the chunk at arrival position (t / Tc), Tc = tiles per chunk,
+// so a workgroup that draws a ticket waits (bounded) only for the chunk its
+// ticket names, and never for another workgroup.  A workgroup polls all
+// flags with one batch of loads and acquires (system scope: the writer may
+// be a DMA engine) once per batch of newly seen chunks, before it reads any
+// of them.  Tiles are computed identically whatever the order, so the output
+// does not depend on the release order.
 //
 // Every wait is bounded: after the time limit (or an abort request) the
 // waiting workgroup records the error and exits, so the kernel always ends.
 //
 // Workspace words after the common queue block (kWsExtra):
-//   [0, P)      per-chunk tile counters
-//   P           mask of chunks already appended to the arrival list
-//   P + 1       arrival list length
-//   [P+2, 2P+2) arrival list (chunk id + 1)
-//   2P + 2      count of finished workgroups (the last one resets all words)
+//   0           ticket counter
+//   1           mask of chunks already appended to the arrival list
+//   2           arrival list length
+//   [3, 3+P)    arrival list (chunk id + 1)
+//   3 + P       count of finished workgroups (the last one resets all words)
 #include "internal.hpp"
 #include "mfma_tile.hpp"
+#include "publish.hpp"
 #include "sync.hpp"
 
 namespace hocf {
@@ -45,63 +48,72 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
   const int P = a.P, N = a.N, K = a.K, Mc = a.Mc;
   const int tpc = a.mtiles * a.ntiles;
   uint32_t* ws = a.ws + kWsExtra;
-  uint32_t* cnt = ws;
-  uint32_t* reg_mask = ws + P;
-  uint32_t* arr_len = ws + P + 1;
-  uint32_t* arr = ws + P + 2;
-  uint32_t* done = ws + 2 * P + 2;
-  const uint32_t all = (P >= 32) ? 0xffffffffu : ((1u << P) - 1u);
+  uint32_t* ticket = ws;
+  uint32_t* reg_mask = ws + 1;
+  uint32_t* arr_len = ws + 2;
+  uint32_t* arr = ws + 3;
+  uint32_t* done = ws + 3 + P;
+  const uint32_t total = (uint32_t)P * (uint32_t)tpc;
 
   // thread 0's private state
-  uint32_t seen = 0;       // chunks whose flag this workgroup has acquired
-  uint32_t exhausted = 0;  // chunks with no tile left
+  uint32_t seen = 0;  // chunks whose flag this workgroup has acquired
   Deadline dl{now_ticks(), a.sync.timeout_ticks};
 
   for (;;) {
     __syncthreads();  // keeps the thread-0 claim region apart from the previous iteration
     if (tid == 0) {
       int chunk = -1, tile = -1;
-      for (;;) {
-        // 1. look for newly arrived chunks and append them to the arrival list
-        for (int c = 0; c < P; ++c) {
-          if (seen & (1u << c)) continue;
-          if (load_flag_system(&a.chunk_flags[c]) == a.sync.epoch) {
+      const uint32_t tk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tk < total) {
+        const uint32_t pos = tk / (uint32_t)tpc;
+        dl.start = now_ticks();  // the bound is per wait
+        for (;;) {
+          // 1. newly arrived chunks: all flags in one batch of loads, one acquire for
+          //    all of them, and the ones nobody registered yet go on the arrival list
+          uint32_t fresh = 0;
+          {
+            uint32_t fv[kMaxP];
+#pragma unroll
+            for (int q = 0; q < kMaxP; ++q)
+              if (q < P && !(seen & (1u << q))) fv[q] = load_flag_system(&a.chunk_flags[q]);
+#pragma unroll
+            for (int q = 0; q < kMaxP; ++q)
+              if (q < P && !(seen & (1u << q)) && fv[q] == a.sync.epoch) fresh |= 1u << q;
+          }
+          if (fresh) {
             acquire_system();
-            seen |= 1u << c;
-            const uint32_t old = __hip_atomic_fetch_or(reg_mask, 1u << c, __ATOMIC_RELAXED,
+            seen |= fresh;
+            const uint32_t old = __hip_atomic_fetch_or(reg_mask, fresh, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
-            if (!(old & (1u << c))) {
-              const uint32_t pos = __hip_atomic_fetch_add(arr_len, 1u, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT);
-              __hip_atomic_store(&arr[pos], (uint32_t)c + 1u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t mine = fresh & ~old;
+            if (mine) {
+              uint32_t at = __hip_atomic_fetch_add(arr_len, (uint32_t)__builtin_popcount(mine),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              for (int q = 0; q < P; ++q)
+                if (mine & (1u << q))
+                  __hip_atomic_store(&arr[at++], (uint32_t)q + 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
             }
           }
+          // 2. the chunk at this ticket's arrival position, once this workgroup has
+          //    acquired it
+          const uint32_t e = __hip_atomic_load(&arr[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (e != 0 && (seen & (1u << (e - 1)))) {
+            chunk = (int)e - 1;
+            tile = (int)(tk % (uint32_t)tpc);
+            break;
+          }
+          // 3. not there yet: bounded wait
+          if (a.sync.abort_flag && load_flag_system(a.sync.abort_flag) != 0u) {
+            report_status(a.sync, kErrAborted);
+            break;
+          }
+          if (dl.expired()) {
+            report_status(a.sync, kErrTimeout);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
         }
-        // 2. take a tile from the earliest-arrived chunk that has one
-        const uint32_t len = __hip_atomic_load(arr_len, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (uint32_t i = 0; i < len && i < (uint32_t)P; ++i) {
-          const uint32_t e = __hip_atomic_load(&arr[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (e == 0) break;  // slot claimed but not yet written
-          const int c = (int)e - 1;
-          if ((exhausted | ~seen) & (1u << c)) continue;  // only chunks this WG acquired
-          const uint32_t t = __hip_atomic_fetch_add(&cnt[c], 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-          if ((int)t < tpc) { chunk = c; tile = (int)t; break; }
-          exhausted |= 1u << c;
-        }
-        if (chunk >= 0) { dl.start = now_ticks(); break; }  // the bound is per wait
-        if (exhausted == all) break;
-        // 3. nothing to do yet: bounded wait
-        if (a.sync.abort_flag && load_flag_system(a.sync.abort_flag) != 0u) {
-          report_status(a.sync, kErrAborted);
-          break;
-        }
-        if (dl.expired()) {
-          report_status(a.sync, kErrTimeout);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
       }
       s_chunk = chunk;
       s_tile = tile;
@@ -120,16 +132,16 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
     Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
 
     const int64_t obase = ((int64_t)c * Mc + (int64_t)mt * Tile::TM) * N + (int64_t)nt * Tile::TN;
-    Tile::template store_acc<ODT, RAGGED>(
+    store_tile<Tile, ODT, RAGGED, kPolicyPlain, false>(
         reinterpret_cast<char*>(a.out) + obase * (ODT == kBF16 ? 2 : 4), N, rows_valid, cols_valid,
-        acc);
+        acc, stages);
   }
 
   // the last workgroup out leaves the workspace zeroed
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == gridDim.x - 1) {
-      for (int w = 0; w < 2 * P + 3; ++w)
+      for (int w = 0; w < P + 4; ++w)
         __hip_atomic_store(&ws[w], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

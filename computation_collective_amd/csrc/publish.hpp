@@ -33,8 +33,9 @@ namespace hocf {
 
 // Buffer resource word 3 for raw (untyped, 32-bit format) buffer accesses.
 constexpr int kRawBufferWord3 = 0x00020000;
-// Cache-policy operand: SC1 (device scope).
+// Cache-policy operands: SC1 (device scope), and none (ordinary write-back).
 constexpr int kPolicyDevice = 16;
+constexpr int kPolicyPlain = 0;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -47,9 +48,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
 
 // 16-byte device-coherent accesses at byte offset voff (per lane) + soff
 // (wave-uniform) from the resource's base.
+template <int POLICY = kPolicyDevice>
 __device__ __forceinline__ void st_dev16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                          u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, kPolicyDevice);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, POLICY);
 }
 __device__ __forceinline__ u32x4 ld_dev16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kPolicyDevice);
@@ -105,16 +107,16 @@ struct PublishLayout {
 };
 
 // Stores this workgroup's accumulators (a Tile-shaped tile) row-major at
-// `dst` (leading dimension `ld` elements of type DT; wave-uniform) with
-// device-coherent stores, and waits until they have completed.  Uses the
+// `dst` (leading dimension `ld` elements of type DT; wave-uniform) with the
+// given cache policy, and (WAIT) waits until they have completed.  Uses the
 // Tile's LDS stage arrays as staging space (begins with a barrier, so the
 // mainloop's last reads are done).  Ragged tiles store only rows <
 // rows_valid and columns < cols_valid (cols_valid a multiple of 16/ES).
 // The caller's tile must satisfy TM * ld * ES < 2^31.
-template <class Tile, int DT, bool RAGGED>
-__device__ __forceinline__ void publish_tile(char* dst, int64_t ld, int rows_valid, int cols_valid,
-                                             const floatx16 (&acc)[Tile::FM][Tile::FN],
-                                             char* const (&stages)[4]) {
+template <class Tile, int DT, bool RAGGED, int POLICY, bool WAIT>
+__device__ __forceinline__ void store_tile(char* dst, int64_t ld, int rows_valid, int cols_valid,
+                                           const floatx16 (&acc)[Tile::FM][Tile::FN],
+                                           char* const (&stages)[4]) {
   using L = PublishLayout<Tile, DT>;
   constexpr int RPI = 64 / L::NCH;       // staged rows per store instruction
   constexpr int NIT = L::NCH / 2;        // store instructions per 32-row block
@@ -164,11 +166,19 @@ __device__ __forceinline__ void publish_tile(char* dst, int64_t ld, int rows_val
         const int rb = 32 * i + (it0 + b) * RPI;  // row of lane group 0, relative to wm * WTM
         const int trow = wm * Tile::WTM + rb + sr;
         if (!RAGGED || (trow < rows_valid && tcol < cols_valid))
-          st_dev16(rs, voff, (uint32_t)((int64_t)rb * ld * L::ES), v[b]);
+          st_dev16<POLICY>(rs, voff, (uint32_t)((int64_t)rb * ld * L::ES), v[b]);
       }
     }
   }
-  wait_memory();
+  if constexpr (WAIT) wait_memory();
+}
+
+// Publication of a tile: device-coherent stores, complete when this returns.
+template <class Tile, int DT, bool RAGGED>
+__device__ __forceinline__ void publish_tile(char* dst, int64_t ld, int rows_valid, int cols_valid,
+                                             const floatx16 (&acc)[Tile::FM][Tile::FN],
+                                             char* const (&stages)[4]) {
+  store_tile<Tile, DT, RAGGED, kPolicyDevice, true>(dst, ld, rows_valid, cols_valid, acc, stages);
 }
 
 // Fixed-order reduction of one published tile: for every element,
