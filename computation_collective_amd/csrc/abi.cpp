@@ -164,7 +164,9 @@ const char* hocf_last_error(void) { return g_err; }
 size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n) {
   if (P <= 0 || M < 0 || N < 0 || tile_m <= 0 || tile_n <= 0 || M % P) return 0;
   const int64_t tpc = cdiv(M / P, tile_m) * cdiv(N, tile_n);
-  return (size_t)(hocf::kWsBaseWords + (int64_t)P * tpc) * 4;
+  // arrival counters [P][tpc], band queue heads and tails [8 + 8], band queues [8][P * tpc]
+  return (size_t)(hocf::kWsBaseWords + (int64_t)P * tpc + 2 * hocf::kNumQueues +
+                  (int64_t)hocf::kNumQueues * P * tpc) * 4;
 }
 
 hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,

@@ -72,6 +72,15 @@ __device__ __forceinline__ void st1(void* base, int64_t i, float v) {
   else reinterpret_cast<float*>(base)[i] = v;
 }
 
+// The lane index, opaque to the optimiser: addresses derived from it are
+// recomputed where they are used instead of being hoisted out of a
+// persistent loop and held in (or spilled from) registers across it.
+__device__ __forceinline__ int opaque_lane() {
+  int l = (int)(threadIdx.x & 63);
+  __asm__ volatile("" : "+v"(l));
+  return l;
+}
+
 // Status codes the kernels record (values of hocf_status).
 constexpr uint32_t kErrTimeout = 4, kErrAborted = 5, kErrBadIndex = 6, kErrProtocol = 7;
 

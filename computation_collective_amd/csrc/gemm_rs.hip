@@ -19,12 +19,23 @@
 //      device-coherent full-row stores, and waits for their completion,
 //   2. stores the epoch into the tile's ready flag in window r,
 //   3. counts itself in the output tile's arrival counter; the workgroup
-//      that completes the count (the last of the P producers) checks the P
-//      flags and folds the P slots in rank order p = 0..P-1 in fp32 into the
-//      destination's output chunk -- while other workgroups are still
-//      computing.
-// No workgroup ever waits on another, so the persistent grid cannot stall,
-// and no step needs an L2-wide write-back or invalidate (publish.hpp).
+//      that completes the count (the last of the P producers) hands the
+//      tile's reduction out as PIECES bands of rows, band k of all bands
+//      going to band queue k mod 8 (one queue per XCD),
+//   4. folds one band of a completed tile, if its band queue has one for it:
+//      checks the P flags and folds the P slots of the band's rows in rank
+//      order p = 0..P-1 in fp32 into the destination's output chunk -- while
+//      other workgroups are still computing.
+// With P = PIECES every workgroup alternates one GEMM tile and one band, so
+// the reduction traffic is spread evenly and the workgroups of an XCD stay in
+// step, which keeps their shared operand panels in L2.  A workgroup claims a
+// slot of its home band queue with one atomic add; every slot below the
+// queue's known total is filled once its tile completes, so the workgroup
+// holds the slot and checks it after each of its own tiles, never waiting
+// while tiles remain.  Without tiles it waits (bounded) for its slot, then
+// helps drain the other queues; tiles are always claimed by running
+// workgroups, so every slot is filled and the kernel ends.
+// No step needs an L2-wide write-back or invalidate (publish.hpp).
 #include <type_traits>
 
 #include "internal.hpp"
@@ -34,9 +45,39 @@
 
 namespace hocf {
 
+// Folds band `piece` of completed output tile `g` (group = (chunk r, tile)).
+template <class Tile, bool RAGGED, int SDT, int ODT>
+__device__ __forceinline__ void reduce_band(const GemmRsArgs& a, int64_t g, int piece) {
+  using RL = ReduceLayout<Tile, SDT>;
+  constexpr int SES = SDT == kBF16 ? 2 : 4;
+  const int P = a.P, N = a.N, Mc = a.Mc;
+  const int tpc = a.mtiles * a.ntiles;
+  const int r = (int)(g / tpc), tflag = (int)(g % tpc);
+  const int mt = tflag / a.ntiles, nt = tflag % a.ntiles;
+  const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
+  const int cols_valid = min(Tile::TN, N - nt * Tile::TN);
+  const int row0 = piece * RL::PIECE_ROWS;
+  if (RAGGED && row0 >= rows_valid) return;
+  if ((int)threadIdx.x < P &&
+      load_flag_agent(&a.win_flags[r][(int64_t)threadIdx.x * tpc + tflag]) != a.sync.epoch)
+    report_status(a.sync, kErrProtocol);
+  const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
+  const char* slot0 = reinterpret_cast<const char*>(a.win_data[r]) + tile_off * SES;
+  const int64_t slot_bytes = (int64_t)Mc * N * SES;
+  char* otile = reinterpret_cast<char*>(a.out) + ((int64_t)r * Mc * N + tile_off) * (ODT == kBF16 ? 2 : 4);
+  if (P <= 4)
+    reduce_piece<Tile, SDT, ODT, RAGGED, 4, 8>(slot0, slot_bytes, P, N, otile, N, row0, rows_valid, cols_valid);
+  else if (P <= 8)
+    reduce_piece<Tile, SDT, ODT, RAGGED, 8, 4>(slot0, slot_bytes, P, N, otile, N, row0, rows_valid, cols_valid);
+  else
+    reduce_piece<Tile, SDT, ODT, RAGGED, kMaxP, 2>(slot0, slot_bytes, P, N, otile, N, row0, rows_valid,
+                                                   cols_valid);
+}
+
 template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
 __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   using Elem = typename std::conditional<BF16IN, uint16_t, float>::type;
+  constexpr int S = ReduceLayout<Tile, SDT>::PIECES;
   // LDS stages, one __shared__ array each (tiles with fewer stages leave the rest tiny)
   __shared__ __attribute__((aligned(1024))) char smem0[Tile::SMEM_BYTES];
   __shared__ __attribute__((aligned(1024))) char smem1[Tile::NST > 1 ? Tile::SMEM_BYTES : 16];
@@ -46,70 +87,130 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   __shared__ int s_qcur;
   __shared__ int64_t s_item;
   __shared__ int s_last;
+  __shared__ int s_band, s_state;
 
   const int tid = threadIdx.x;
   const int P = a.P, N = a.N, K = a.K, Mc = a.Mc;
   const int tpc = a.mtiles * a.ntiles;
+  const int64_t ngroups = (int64_t)P * tpc;
+  // workspace after the queue block: arrival counters [P][tpc], band queue heads [8]
+  // and tails [8], then the band queues [8][P * tpc] (bands k = tile * S + s, plus 1)
   uint32_t* grp = a.ws + kWsExtra;
+  uint32_t* bq_head = grp + ngroups;
+  uint32_t* bq_tail = bq_head + kNumQueues;
+  uint32_t* bq = bq_tail + kNumQueues;
+  const int64_t nbands = ngroups * S;
+  auto bq_total = [&](int q) { return (uint32_t)((nbands - q + kNumQueues - 1) / kNumQueues); };
+  const int home = (int)(blockIdx.x % kNumQueues);
   if (tid == 0) s_qcur = 0;
   __syncthreads();
 
+  // thread 0's band state: a claimed slot (queue, index) not yet processed
+  int pend_q = -1;
+  uint32_t pend_i = 0;
+  bool tiles_left = true;
+  Deadline dl{now_ticks(), a.sync.timeout_ticks};
   for (;;) {
-    const int64_t item = claim_item(a.ws, a.total, &s_qcur, &s_item);
-    if (item < 0) break;
-    const int tq = (int)(item % tpc);
-    const int r = (int)((item / tpc) % P);
-    const int p = (int)(item / ((int64_t)tpc * P));
-    const int nt = tq / a.mtiles, mt = tq % a.mtiles;
-    const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
-    const int cols_valid = min(Tile::TN, N - nt * Tile::TN);
+    if (tiles_left) {
+      const int64_t item = claim_item(a.ws, a.total, &s_qcur, &s_item);
+      if (item < 0) {
+        tiles_left = false;
+      } else {
+        const int tq = (int)(item % tpc);
+        const int r = (int)((item / tpc) % P);
+        const int p = (int)(item / ((int64_t)tpc * P));
+        const int nt = tq / a.mtiles, mt = tq % a.mtiles;
+        const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
+        const int cols_valid = min(Tile::TN, N - nt * Tile::TN);
 
-    const Elem* At = reinterpret_cast<const Elem*>(a.A) +
-                     ((int64_t)p * a.M + (int64_t)r * Mc + (int64_t)mt * Tile::TM) * K;
-    const Elem* Wt = reinterpret_cast<const Elem*>(a.W) + (int64_t)p * K * N + (int64_t)nt * Tile::TN;
-    floatx16 acc[Tile::FM][Tile::FN];
-    Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
+        const Elem* At = reinterpret_cast<const Elem*>(a.A) +
+                         ((int64_t)p * a.M + (int64_t)r * Mc + (int64_t)mt * Tile::TM) * K;
+        const Elem* Wt = reinterpret_cast<const Elem*>(a.W) + (int64_t)p * K * N + (int64_t)nt * Tile::TN;
+        floatx16 acc[Tile::FM][Tile::FN];
+        Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
 
-    // 1. publish the tile into window r, slot p
-    constexpr int SES = SDT == kBF16 ? 2 : 4;
-    char* wdata = reinterpret_cast<char*>(a.win_data[r]);
-    const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
-    publish_tile<Tile, SDT, RAGGED>(wdata + ((int64_t)p * Mc * N + tile_off) * SES, N, rows_valid,
-                                    cols_valid, acc, stages);
+        // 1. publish the tile into window r, slot p
+        constexpr int SES = SDT == kBF16 ? 2 : 4;
+        char* wdata = reinterpret_cast<char*>(a.win_data[r]);
+        const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
+        publish_tile<Tile, SDT, RAGGED>(wdata + ((int64_t)p * Mc * N + tile_off) * SES, N, rows_valid,
+                                        cols_valid, acc, stages);
+        __syncthreads();
+
+        // 2. ready flag; 3. arrival count -> the last producer hands out the bands
+        const int tflag = mt * a.ntiles + nt;
+        if (tid == 0) {
+          __hip_atomic_store(&a.win_flags[r][(int64_t)p * tpc + tflag], a.sync.epoch, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+          wait_memory();  // the flag is visible before the count that announces it
+          uint32_t* cnt = &grp[(int64_t)r * tpc + tflag];
+          const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (prev == (uint32_t)(P - 1)) {
+            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int64_t g = (int64_t)r * tpc + tflag;
+            uint32_t at[S];
+#pragma unroll
+            for (int b = 0; b < S; ++b)
+              at[b] = __hip_atomic_fetch_add(&bq_tail[(g * S + b) % kNumQueues], 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int b = 0; b < S; ++b)
+              __hip_atomic_store(&bq[((g * S + b) % kNumQueues) * ngroups + at[b]], (uint32_t)(g * S + b) + 1u,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    }
+
+    // 4. a band of a completed tile (the barrier keeps this thread-0 region apart
+    //    from the one above)
     __syncthreads();
-
-    // 2. ready flag; 3. arrival count -> the last producer reduces
-    const int tflag = mt * a.ntiles + nt;
     if (tid == 0) {
-      __hip_atomic_store(&a.win_flags[r][(int64_t)p * tpc + tflag], a.sync.epoch, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      wait_memory();  // the flag is visible before the count that announces it
-      uint32_t* cnt = &grp[(int64_t)r * tpc + tflag];
-      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int last = (prev == (uint32_t)(P - 1));
-      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = last;
+      int state = 0;  // 0: none now, 1: band ready, 2: all bands taken, 3: timed out
+      int band = -1;
+      if (pend_q < 0) {
+        // claim a slot: the home queue while tiles remain, any queue after
+        for (int i = 0; i < (tiles_left ? 1 : kNumQueues); ++i) {
+          const int q = (home + i) % kNumQueues;
+          if (__hip_atomic_load(&bq_head[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= bq_total(q)) continue;
+          const uint32_t t = __hip_atomic_fetch_add(&bq_head[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (t < bq_total(q)) { pend_q = q; pend_i = t; break; }
+        }
+        if (pend_q < 0 && !tiles_left) state = 2;
+      }
+      if (pend_q >= 0) {
+        uint32_t e = __hip_atomic_load(&bq[pend_q * ngroups + pend_i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (e == 0 && !tiles_left) {
+          // nothing else to do: wait (bounded) for the slot's tile to complete
+          const Deadline wl{now_ticks(), a.sync.timeout_ticks};
+          while (e == 0 && !wl.expired()) {
+            __builtin_amdgcn_s_sleep(4);
+            e = __hip_atomic_load(&bq[pend_q * ngroups + pend_i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if (e == 0) { report_status(a.sync, kErrTimeout); state = 3; }
+        }
+        if (e != 0) {
+          band = (int)(e - 1u);
+          state = 1;
+          pend_q = -1;
+        }
+      }
+      s_state = state;
+      s_band = band;
     }
     __syncthreads();
-    if (uniform(s_last)) {
-      if (tid < P && load_flag_agent(&a.win_flags[r][(int64_t)tid * tpc + tflag]) != a.sync.epoch)
-        report_status(a.sync, kErrProtocol);
-      const char* slot0 = wdata + tile_off * SES;
-      const int64_t slot_bytes = (int64_t)Mc * N * SES;
-      char* otile = reinterpret_cast<char*>(a.out) +
-                    ((int64_t)r * Mc * N + tile_off) * (ODT == kBF16 ? 2 : 4);
-      if (P <= 4)
-        reduce_tile<Tile, SDT, ODT, RAGGED, 4, 8>(slot0, slot_bytes, P, N, otile, N, rows_valid,
-                                                  cols_valid);
-      else if (P <= 8)
-        reduce_tile<Tile, SDT, ODT, RAGGED, 8, 4>(slot0, slot_bytes, P, N, otile, N, rows_valid,
-                                                  cols_valid);
-      else
-        reduce_tile<Tile, SDT, ODT, RAGGED, kMaxP, 2>(slot0, slot_bytes, P, N, otile, N, rows_valid,
-                                                      cols_valid);
-    }
+    const int state = uniform(s_state);
+    const int band = uniform(s_band);
+    __syncthreads();
+    if (state == 1) reduce_band<Tile, RAGGED, SDT, ODT>(a, band / S, band % S);
+    else if (state >= 2) break;
   }
-  finish_workgroup(a.ws);
+
+  // the last workgroup out leaves the workspace zeroed
+  if (finish_workgroup_last(a.ws, &s_last)) {
+    for (int64_t i = tid; i < 2 * kNumQueues + kNumQueues * ngroups; i += Tile::NT)
+      __hip_atomic_store(&bq_head[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>

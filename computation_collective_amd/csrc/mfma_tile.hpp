@@ -333,7 +333,7 @@ struct TileBf16Direct {
                                              char* const (&stages)[4], floatx16 (&acc)[FM][FN]) {
     static_assert(!RAGGED, "full tiles only");
 #if defined(__HIP_DEVICE_COMPILE__)  // device-only body (the host pass only needs the declaration)
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = opaque_lane(), wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 #pragma unroll
     for (int i = 0; i < FM; ++i)

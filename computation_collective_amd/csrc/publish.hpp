@@ -57,15 +57,6 @@ __device__ __forceinline__ u32x4 ld_dev16(__amdgpu_buffer_rsrc_t r, uint32_t vof
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kPolicyDevice);
 }
 
-// The lane index, opaque to the optimiser: addresses derived from it are
-// recomputed where they are used instead of being hoisted out of the
-// persistent loop and held in registers across the mainloop.
-__device__ __forceinline__ int opaque_lane() {
-  int l = (int)(threadIdx.x & 63);
-  __asm__ volatile("" : "+v"(l));
-  return l;
-}
-
 // s_waitcnt vmcnt(0): every load and store this wave issued has completed.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -181,26 +172,40 @@ __device__ __forceinline__ void publish_tile(char* dst, int64_t ld, int rows_val
   store_tile<Tile, DT, RAGGED, kPolicyDevice, true>(dst, ld, rows_valid, cols_valid, acc, stages);
 }
 
-// Fixed-order reduction of one published tile: for every element,
-// acc = slot 0; acc += slot q for q = 1 .. P-1 (fp32, in rank order); the
-// result is rounded to ODT and stored at `out` (leading dimension ld_out).
-// Slot q's tile starts at slot0 + q * slot_bytes (leading dimension ld,
-// element type SDT); all pointers are wave-uniform.  Loads are
-// device-coherent; U chunks of 16 bytes per thread and slot (PMAX slots,
-// those past P re-reading slot P-1) are in flight together.  Requires P <= PMAX and TM * ld * ES(SDT) < 2^31.
+// Geometry of the fixed-order reduction of one Tile with slot type SDT:
+// 16-byte chunks, CPR per tile row, RPS rows per pass of the workgroup, and
+// the pieces a tile's reduction is cut into (at least 32 rows or one pass).
+template <class Tile, int SDT>
+struct ReduceLayout {
+  static constexpr int SES = SDT == kBF16 ? 2 : 4;
+  static constexpr int CE = 16 / SES;              // elements per 16-byte chunk
+  static constexpr int CPR = Tile::TN / CE;        // chunks per tile row
+  static constexpr int RPS = Tile::NT / CPR;       // rows covered by one pass of the workgroup
+  static constexpr int PIECE_ROWS = RPS > Tile::TM / 8 ? RPS : Tile::TM / 8;
+  static constexpr int PIECES = Tile::TM / PIECE_ROWS;
+  static_assert(Tile::NT % CPR == 0 && PIECE_ROWS % RPS == 0 && Tile::TM % PIECE_ROWS == 0,
+                "reduce layout");
+};
+
+// Fixed-order reduction of rows [row0, row0 + PIECE_ROWS) of one published
+// tile: for every element, acc = slot 0; acc += slot q for q = 1 .. P-1
+// (fp32, in rank order); the result is rounded to ODT and stored at `out`
+// (the output tile's origin, leading dimension ld_out).  Slot q's tile starts
+// at slot0 + q * slot_bytes (leading dimension ld, element type SDT); all
+// pointers are wave-uniform.  Loads are device-coherent; U chunks of 16
+// bytes per thread and slot (PMAX slots, those past P re-reading slot P-1)
+// are in flight together.  Requires P <= PMAX and TM * ld * ES(SDT) < 2^31.
 template <class Tile, int SDT, int ODT, bool RAGGED, int PMAX, int U>
-__device__ __forceinline__ void reduce_tile(const char* slot0, int64_t slot_bytes, int P, int64_t ld,
-                                            void* out, int64_t ld_out, int rows_valid,
-                                            int cols_valid) {
-  constexpr int SES = SDT == kBF16 ? 2 : 4;
-  constexpr int CE = 16 / SES;              // elements per 16-byte chunk
-  constexpr int CPR = Tile::TN / CE;        // chunks per tile row
-  constexpr int RPS = Tile::NT / CPR;       // rows covered by one pass of the workgroup
-  constexpr int NPASS = Tile::TM / RPS;
+__device__ __forceinline__ void reduce_piece(const char* slot0, int64_t slot_bytes, int P, int64_t ld,
+                                             void* out, int64_t ld_out, int row0, int rows_valid,
+                                             int cols_valid) {
+  using L = ReduceLayout<Tile, SDT>;
+  constexpr int SES = L::SES, CE = L::CE, CPR = L::CPR, RPS = L::RPS;
+  constexpr int NPASS = L::PIECE_ROWS / RPS;
   constexpr int UE = U < NPASS ? U : NPASS;
-  static_assert(Tile::NT % CPR == 0 && Tile::TM % RPS == 0 && NPASS % UE == 0, "reduce layout");
+  static_assert(NPASS % UE == 0, "reduce layout");
   const int tid = (int)(threadIdx.x & ~63) + opaque_lane();
-  const int r0 = tid / CPR, col = (tid % CPR) * CE;
+  const int r0 = row0 + tid / CPR, col = (tid % CPR) * CE;
   const uint32_t voff = (uint32_t)(((int64_t)r0 * ld + col) * SES);
   char* obase = reinterpret_cast<char*>(out) + ((int64_t)r0 * ld_out + col) * (ODT == kBF16 ? 2 : 4);
   for (int ps = 0; ps < NPASS; ps += UE) {

@@ -112,6 +112,26 @@ __device__ __forceinline__ void finish_workgroup(uint32_t* ws) {
   }
 }
 
+// As finish_workgroup, called by every thread; returns (wave-uniform, in
+// every thread) whether this is the last workgroup to finish, which may then
+// reset operator-specific workspace words (every other workgroup is done).
+__device__ __forceinline__ bool finish_workgroup_last(uint32_t* ws, int* s_flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&ws[kWsDone], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == gridDim.x - 1;
+    if (last) {
+      for (int q = 0; q < kNumQueues; ++q)
+        __hip_atomic_store(&ws[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ws[kWsDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *s_flag = last;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*s_flag) != 0;
+}
+
 __device__ __forceinline__ uint64_t now_ticks() { return (uint64_t)wall_clock64(); }
 
 // Bounded wait state: deadline in wall_clock64() ticks.

@@ -80,8 +80,8 @@ def test_gemm_rs_valid_reaches_device():
 
 def test_workspace_queries():
     base = (8 + 1) * 4
-    assert hocf.hocf_gemm_rs_workspace_bytes(8, 8192, 4096, 256, 256) == base + 8 * 4 * 16 * 4
-    assert hocf.hocf_gemm_rs_workspace_bytes(4, 256, 256, 64, 64) == base + 4 * 4 * 4  # Mc=64: 1x4 tiles per chunk
+    assert hocf.hocf_gemm_rs_workspace_bytes(8, 8192, 4096, 256, 256) == base + (8 * 4 * 16 + 16 + 8 * 8 * 4 * 16) * 4
+    assert hocf.hocf_gemm_rs_workspace_bytes(4, 256, 256, 64, 64) == base + (4 * 4 + 16 + 8 * 4 * 4) * 4  # Mc=64: 1x4 tiles per chunk
     assert hocf.hocf_gemv_ar_workspace_bytes(8, 8192, 256) == base + 32 * 4
     assert hocf.hocf_ag_gemm_workspace_bytes(8) == base + (2 * 8 + 3) * 4
     assert hocf.hocf_embbag_a2a_workspace_bytes() == base
