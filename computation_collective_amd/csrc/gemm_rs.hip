@@ -109,62 +109,15 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   int pend_q = -1;
   uint32_t pend_i = 0;
   bool tiles_left = true;
-  Deadline dl{now_ticks(), a.sync.timeout_ticks};
   for (;;) {
+    int64_t item = -1;
     if (tiles_left) {
-      const int64_t item = claim_item(a.ws, a.total, &s_qcur, &s_item);
-      if (item < 0) {
-        tiles_left = false;
-      } else {
-        const int tq = (int)(item % tpc);
-        const int r = (int)((item / tpc) % P);
-        const int p = (int)(item / ((int64_t)tpc * P));
-        const int nt = tq / a.mtiles, mt = tq % a.mtiles;
-        const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
-        const int cols_valid = min(Tile::TN, N - nt * Tile::TN);
-
-        const Elem* At = reinterpret_cast<const Elem*>(a.A) +
-                         ((int64_t)p * a.M + (int64_t)r * Mc + (int64_t)mt * Tile::TM) * K;
-        const Elem* Wt = reinterpret_cast<const Elem*>(a.W) + (int64_t)p * K * N + (int64_t)nt * Tile::TN;
-        floatx16 acc[Tile::FM][Tile::FN];
-        Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
-
-        // 1. publish the tile into window r, slot p
-        constexpr int SES = SDT == kBF16 ? 2 : 4;
-        char* wdata = reinterpret_cast<char*>(a.win_data[r]);
-        const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
-        publish_tile<Tile, SDT, RAGGED>(wdata + ((int64_t)p * Mc * N + tile_off) * SES, N, rows_valid,
-                                        cols_valid, acc, stages);
-        __syncthreads();
-
-        // 2. ready flag; 3. arrival count -> the last producer hands out the bands
-        const int tflag = mt * a.ntiles + nt;
-        if (tid == 0) {
-          __hip_atomic_store(&a.win_flags[r][(int64_t)p * tpc + tflag], a.sync.epoch, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-          wait_memory();  // the flag is visible before the count that announces it
-          uint32_t* cnt = &grp[(int64_t)r * tpc + tflag];
-          const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (prev == (uint32_t)(P - 1)) {
-            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int64_t g = (int64_t)r * tpc + tflag;
-            uint32_t at[S];
-#pragma unroll
-            for (int b = 0; b < S; ++b)
-              at[b] = __hip_atomic_fetch_add(&bq_tail[(g * S + b) % kNumQueues], 1u, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-            for (int b = 0; b < S; ++b)
-              __hip_atomic_store(&bq[((g * S + b) % kNumQueues) * ngroups + at[b]], (uint32_t)(g * S + b) + 1u,
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      }
+      item = claim_item(a.ws, a.total, &s_qcur, &s_item);
+      if (item < 0) tiles_left = false;
     }
 
-    // 4. a band of a completed tile (the barrier keeps this thread-0 region apart
-    //    from the one above)
-    __syncthreads();
+    // a band of a completed tile to fold in this iteration, if one is ready
+    // (thread-0 regions are kept apart by the barriers around them)
     if (tid == 0) {
       int state = 0;  // 0: none now, 1: band ready, 2: all bands taken, 3: timed out
       int band = -1;
@@ -202,8 +155,63 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
     const int state = uniform(s_state);
     const int band = uniform(s_band);
     __syncthreads();
+    if (item < 0 && state != 1) {
+      if (state >= 2 || !tiles_left) break;  // all bands taken, or a timeout was reported
+      continue;
+    }
+
+    int r = 0, p = 0, tflag = 0;
+    if (item >= 0) {
+      const int tq = (int)(item % tpc);
+      r = (int)((item / tpc) % P);
+      p = (int)(item / ((int64_t)tpc * P));
+      const int nt = tq / a.mtiles, mt = tq % a.mtiles;
+      tflag = mt * a.ntiles + nt;
+      const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
+      const int cols_valid = min(Tile::TN, N - nt * Tile::TN);
+
+      const Elem* At = reinterpret_cast<const Elem*>(a.A) +
+                       ((int64_t)p * a.M + (int64_t)r * Mc + (int64_t)mt * Tile::TM) * K;
+      const Elem* Wt = reinterpret_cast<const Elem*>(a.W) + (int64_t)p * K * N + (int64_t)nt * Tile::TN;
+      floatx16 acc[Tile::FM][Tile::FN];
+      Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
+
+      // 1. publish the tile into window r, slot p (stores issued; waited for below)
+      constexpr int SES = SDT == kBF16 ? 2 : 4;
+      char* wdata = reinterpret_cast<char*>(a.win_data[r]);
+      const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
+      store_tile<Tile, SDT, RAGGED, kPolicyDevice, false>(wdata + ((int64_t)p * Mc * N + tile_off) * SES, N,
+                                                          rows_valid, cols_valid, acc, stages);
+    }
+    // 4. the band, its loads in flight together with the tile's stores
     if (state == 1) reduce_band<Tile, RAGGED, SDT, ODT>(a, band / S, band % S);
-    else if (state >= 2) break;
+
+    if (item >= 0) {
+      wait_memory();  // this thread's stores of the tile have completed
+      __syncthreads();
+      // 2. ready flag; 3. arrival count -> the last producer hands out the bands
+      if (tid == 0) {
+        __hip_atomic_store(&a.win_flags[r][(int64_t)p * tpc + tflag], a.sync.epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        wait_memory();  // the flag is visible before the count that announces it
+        uint32_t* cnt = &grp[(int64_t)r * tpc + tflag];
+        const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == (uint32_t)(P - 1)) {
+          __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int64_t g = (int64_t)r * tpc + tflag;
+          uint32_t at[S];
+#pragma unroll
+          for (int b = 0; b < S; ++b)
+            at[b] = __hip_atomic_fetch_add(&bq_tail[(g * S + b) % kNumQueues], 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int b = 0; b < S; ++b)
+            __hip_atomic_store(&bq[((g * S + b) % kNumQueues) * ngroups + at[b]], (uint32_t)(g * S + b) + 1u,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __syncthreads();
+    }
   }
 
   // the last workgroup out leaves the workspace zeroed
