@@ -14,6 +14,8 @@
 // (the policy the compiler gives device-scope atomic stores: written
 // through to the memory side), and the reducer's loads carry SC1 as well
 // (device-scope atomic loads: never served from a possibly stale line).
+// Both also carry NT, the streaming hint: coherence is the SC bits' business,
+// NT only keeps this use-once traffic from evicting the operand panels.
 // The ordering a flag needs is then only that the data stores have
 // completed before the flag store is issued -- an s_waitcnt vmcnt(0) in
 // each thread and a barrier -- and, on the consumer side, that its data
@@ -33,8 +35,10 @@ namespace hocf {
 
 // Buffer resource word 3 for raw (untyped, 32-bit format) buffer accesses.
 constexpr int kRawBufferWord3 = 0x00020000;
-// Cache-policy operands: SC1 (device scope), and none (ordinary write-back).
-constexpr int kPolicyDevice = 16;
+// Cache-policy operands: SC1 (device scope) with NT (streaming: published
+// data is written once and read once, so it should not displace the GEMM
+// operands in the caches), and none (ordinary write-back).
+constexpr int kPolicyDevice = 16 | 2;
 constexpr int kPolicyPlain = 0;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
