@@ -78,6 +78,8 @@ template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
 __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   using Elem = typename std::conditional<BF16IN, uint16_t, float>::type;
   constexpr int S = ReduceLayout<Tile, SDT>::PIECES;
+  // tiles with a split mainloop start the next tile's loads before the band
+  constexpr bool kSplit = Tile::kSplitMainloop;
   // LDS stages, one __shared__ array each (tiles with fewer stages leave the rest tiny)
   __shared__ __attribute__((aligned(1024))) char smem0[Tile::SMEM_BYTES];
   __shared__ __attribute__((aligned(1024))) char smem1[Tile::NST > 1 ? Tile::SMEM_BYTES : 16];
@@ -160,31 +162,38 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
       continue;
     }
 
-    int r = 0, p = 0, tflag = 0;
+    int r = 0, p = 0, tflag = 0, mt = 0, nt = 0;
+    const Elem* At = nullptr;
+    const Elem* Wt = nullptr;
     if (item >= 0) {
       const int tq = (int)(item % tpc);
       r = (int)((item / tpc) % P);
       p = (int)(item / ((int64_t)tpc * P));
-      const int nt = tq / a.mtiles, mt = tq % a.mtiles;
+      nt = tq / a.mtiles;
+      mt = tq % a.mtiles;
       tflag = mt * a.ntiles + nt;
+      At = reinterpret_cast<const Elem*>(a.A) + ((int64_t)p * a.M + (int64_t)r * Mc + (int64_t)mt * Tile::TM) * K;
+      Wt = reinterpret_cast<const Elem*>(a.W) + (int64_t)p * K * N + (int64_t)nt * Tile::TN;
+      // the tile's first operand slices start loading now ...
+      if constexpr (kSplit) Tile::prologue(At, K, Wt, N, K, stages);
+    }
+    // 4. ... while the band folds (its loads do not touch the stage arrays)
+    if (state == 1) reduce_band<Tile, RAGGED, SDT, ODT>(a, band / S, band % S);
+
+    if (item >= 0) {
       const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
       const int cols_valid = min(Tile::TN, N - nt * Tile::TN);
-
-      const Elem* At = reinterpret_cast<const Elem*>(a.A) +
-                       ((int64_t)p * a.M + (int64_t)r * Mc + (int64_t)mt * Tile::TM) * K;
-      const Elem* Wt = reinterpret_cast<const Elem*>(a.W) + (int64_t)p * K * N + (int64_t)nt * Tile::TN;
       floatx16 acc[Tile::FM][Tile::FN];
-      Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
+      if constexpr (kSplit) Tile::template body<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
+      else Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
 
-      // 1. publish the tile into window r, slot p (stores issued; waited for below)
+      // 1. publish the tile into window r, slot p
       constexpr int SES = SDT == kBF16 ? 2 : 4;
       char* wdata = reinterpret_cast<char*>(a.win_data[r]);
       const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
       store_tile<Tile, SDT, RAGGED, kPolicyDevice, false>(wdata + ((int64_t)p * Mc * N + tile_off) * SES, N,
                                                           rows_valid, cols_valid, acc, stages);
     }
-    // 4. the band, its loads in flight together with the tile's stores
-    if (state == 1) reduce_band<Tile, RAGGED, SDT, ODT>(a, band / S, band % S);
 
     if (item >= 0) {
       wait_memory();  // this thread's stores of the tile have completed

@@ -39,6 +39,7 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& v, int d) {
 template <int TM_, int TN_, int WM_, int WN_>
 struct TileBf16 {
   static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr bool kSplitMainloop = false;
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int BK = 64;
   static constexpr int LDK = BK + 8;  // padded row: 72 bf16 = 144 bytes
@@ -284,6 +285,7 @@ __device__ __forceinline__ void interleave() {
 template <int TM_, int TN_, int WM_, int WN_, int BK_ = 32, int NST_ = 4>
 struct TileBf16Direct {
   static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr bool kSplitMainloop = true;
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int BK = BK_, NST = NST_;
   static constexpr int WTM = TM / WM, WTN = TN / WN;
@@ -326,21 +328,51 @@ struct TileBf16Direct {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
   }
 
+  // The whole tile: prologue (the first NST slices' loads) and body.
   template <bool RAGGED>
   __device__ static __forceinline__ void run(const uint16_t* __restrict__ A, int64_t lda,
                                              const uint16_t* __restrict__ W, int64_t ldw,
-                                             int /*rows_valid*/, int /*cols_valid*/, int K,
+                                             int rows_valid, int cols_valid, int K,
                                              char* const (&stages)[4], floatx16 (&acc)[FM][FN]) {
+    parts<RAGGED, true, true>(A, lda, W, ldw, rows_valid, cols_valid, K, stages, acc);
+  }
+  // Split use: prologue() issues the loads of the first NST-1 slices into
+  // the stage arrays and returns; body() (same arguments) then issues the
+  // last and runs the K loop.  Between the two the workgroup may do anything
+  // that leaves the stage arrays alone and keeps at most 39 vector-memory
+  // operations of its own in flight at a time, while the prologue's loads
+  // are in flight.
+  __device__ static __forceinline__ void prologue(const uint16_t* __restrict__ A, int64_t lda,
+                                                  const uint16_t* __restrict__ W, int64_t ldw, int K,
+                                                  char* const (&stages)[4]) {
+    floatx16 unused[FM][FN];
+    parts<false, true, false>(A, lda, W, ldw, TM, TN, K, stages, unused);
+  }
+  template <bool RAGGED>
+  __device__ static __forceinline__ void body(const uint16_t* __restrict__ A, int64_t lda,
+                                              const uint16_t* __restrict__ W, int64_t ldw,
+                                              int rows_valid, int cols_valid, int K,
+                                              char* const (&stages)[4], floatx16 (&acc)[FM][FN]) {
+    parts<RAGGED, false, true>(A, lda, W, ldw, rows_valid, cols_valid, K, stages, acc);
+  }
+
+  template <bool RAGGED, bool PRO, bool BODY>
+  __device__ static __forceinline__ void parts(const uint16_t* __restrict__ A, int64_t lda,
+                                               const uint16_t* __restrict__ W, int64_t ldw,
+                                               int /*rows_valid*/, int /*cols_valid*/, int K,
+                                               char* const (&stages)[4], floatx16 (&acc)[FM][FN]) {
     static_assert(!RAGGED, "full tiles only");
 #if defined(__HIP_DEVICE_COMPILE__)  // device-only body (the host pass only needs the declaration)
     const int tid = threadIdx.x, lane = opaque_lane(), wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
+    if constexpr (BODY) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    }
     const int nk = K / BK;
     // precondition (checked by the launchers): K is a multiple of NST * BK.
     // Anything else would make the slice schedule below load past row K, so
@@ -458,9 +490,18 @@ struct TileBf16Direct {
     using T_ = std::integral_constant<bool, true>;
     using F_ = std::integral_constant<bool, false>;
 
-    // prologue: every stage loading, slice 0 landed everywhere, its first fragments read
+    // prologue: every stage loading.  In split use the prologue issues the
+    // first NST-1 stages (NST-1 batches of LPS loads) and the body the last
+    // one, so that whatever runs in between can keep up to 63 - (NST-1)*LPS
+    // (= 39) more vector-memory operations of its own in flight.
+    if constexpr (PRO) {
 #pragma unroll
-    for (int s = 0; s < NST; ++s) load_stage(stages[s], s);
+      for (int s = 0; s < NST - 1; ++s) load_stage(stages[s], s);
+    }
+    if constexpr (!BODY) return;
+    load_stage(stages[NST - 1], NST - 1);
+    // slice 0 landed everywhere: the wait leaves only the NST-1 batches issued
+    // last in flight, and slice 0's were issued before them
     sync_slices(std::integral_constant<int, NST - 1>{});
     read_frags(stages[0], 0, fa0, fb0);
     // K is a multiple of NST*BK: whole rounds of NST slices, the last round
@@ -494,6 +535,7 @@ struct TileBf16Direct {
 template <int TM_, int TN_, int WM_, int WN_>
 struct TileF32 {
   static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr bool kSplitMainloop = false;
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int BK = 32;
   static constexpr int LDA = BK + 1, LDB = TN + 4;
