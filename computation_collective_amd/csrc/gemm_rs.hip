@@ -86,7 +86,6 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem2[Tile::NST > 2 ? Tile::SMEM_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char smem3[Tile::NST > 3 ? Tile::SMEM_BYTES : 16];
   char* const stages[4] = {smem0, smem1, smem2, smem3};
-  __shared__ int s_qcur;
   __shared__ int64_t s_item;
   __shared__ int s_last;
   __shared__ int s_band, s_state;
@@ -104,38 +103,42 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   const int64_t nbands = ngroups * S;
   auto bq_total = [&](int q) { return (uint32_t)((nbands - q + kNumQueues - 1) / kNumQueues); };
   const int home = (int)(blockIdx.x % kNumQueues);
-  if (tid == 0) s_qcur = 0;
-  __syncthreads();
 
-  // thread 0's band state: a claimed slot (queue, index) not yet processed
+  // thread 0's claim state: tiles and band slots are both requested one
+  // iteration ahead; a claimed band slot (queue, index) waits in pend_* until
+  // its band has been handed out
+  ClaimAhead tiles;
   int pend_q = -1;
   uint32_t pend_i = 0;
+  bool band_ahead = false;
+  uint32_t band_ticket = 0;
   bool tiles_left = true;
   for (;;) {
-    int64_t item = -1;
-    if (tiles_left) {
-      item = claim_item(a.ws, a.total, &s_qcur, &s_item);
-      if (item < 0) tiles_left = false;
-    }
-
-    // a band of a completed tile to fold in this iteration, if one is ready
-    // (thread-0 regions are kept apart by the barriers around them)
+    // the next tile, and a band of a completed tile to fold in this
+    // iteration if one is ready (one thread-0 region between two barriers)
+    __syncthreads();
     if (tid == 0) {
+      const int64_t it = tiles_left ? tiles.next(a.ws, a.total) : -1;
+      const bool tl = it >= 0;
       int state = 0;  // 0: none now, 1: band ready, 2: all bands taken, 3: timed out
       int band = -1;
+      if (band_ahead) {
+        if (band_ticket < bq_total(home)) { pend_q = home; pend_i = band_ticket; }
+        band_ahead = false;
+      }
       if (pend_q < 0) {
         // claim a slot: the home queue while tiles remain, any queue after
-        for (int i = 0; i < (tiles_left ? 1 : kNumQueues); ++i) {
+        for (int i = 0; i < (tl ? 1 : kNumQueues); ++i) {
           const int q = (home + i) % kNumQueues;
           if (__hip_atomic_load(&bq_head[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= bq_total(q)) continue;
           const uint32_t t = __hip_atomic_fetch_add(&bq_head[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (t < bq_total(q)) { pend_q = q; pend_i = t; break; }
         }
-        if (pend_q < 0 && !tiles_left) state = 2;
+        if (pend_q < 0 && !tl) state = 2;
       }
       if (pend_q >= 0) {
         uint32_t e = __hip_atomic_load(&bq[pend_q * ngroups + pend_i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (e == 0 && !tiles_left) {
+        if (e == 0 && !tl) {
           // nothing else to do: wait (bounded) for the slot's tile to complete
           const Deadline wl{now_ticks(), a.sync.timeout_ticks};
           while (e == 0 && !wl.expired()) {
@@ -148,15 +151,22 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
           band = (int)(e - 1u);
           state = 1;
           pend_q = -1;
+          if (tl) {
+            // the next slot of the home queue, its result read next iteration
+            band_ticket = __hip_atomic_fetch_add(&bq_head[home], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            band_ahead = true;
+          }
         }
       }
+      s_item = it;
       s_state = state;
       s_band = band;
     }
     __syncthreads();
+    const int64_t item = uniform64(s_item);
     const int state = uniform(s_state);
     const int band = uniform(s_band);
-    __syncthreads();
+    if (item < 0) tiles_left = false;
     if (item < 0 && state != 1) {
       if (state >= 2 || !tiles_left) break;  // all bands taken, or a timeout was reported
       continue;
@@ -219,7 +229,7 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      __syncthreads();
+      // (the barrier at the top of the loop ends this thread-0 region)
     }
   }
 

@@ -1,13 +1,17 @@
 // Flag protocol and persistent-workgroup scheduling.
 //
-// Producer side: a workgroup's threads store a tile, meet at a barrier
-// (their stores have then reached this XCD's L2), and one thread issues an
-// agent-scope release fence -- which writes the L2's dirty lines back so the
-// tile is visible from every XCD -- before storing the epoch into the
-// tile's flag word.  Consumer side: one thread reads the flag until it
-// equals the epoch, issues an agent-scope (or, for flags written by a copy
-// engine or the command processor, system-scope) acquire fence, and the
-// workgroup meets at a barrier before reading the tile.
+// Producer side: a workgroup stores a tile, the workgroup meets at a
+// barrier, and one thread stores the epoch into the tile's flag word.  For
+// the stores to be visible from every XCD by then, either they are
+// device-coherent and each thread has waited for its own (publish.hpp), or
+// they are ordinary and the flag store follows an agent-scope release fence
+// (release_flag), which writes this XCD's L2 back.  Consumer side: one
+// thread reads the flag (or an arrival count that is only advanced after
+// the flags it covers) until it equals the epoch, the workgroup meets at a
+// barrier, and the tile is read with device-coherent loads (or after an
+// acquire fence).  Flags written from outside the kernel (by the host or a
+// stream write) are read at system scope and followed by a system-scope
+// acquire before the data they announce is read.
 //
 // The pages (SC24 abstract; mKernel, section on persistent kernels and
 // tile/chunk overlap) prescribe GPU-initiated, tile-granular publication but
@@ -96,6 +100,38 @@ __device__ __forceinline__ int64_t claim_item(uint32_t* ws, int64_t total, int* 
   __syncthreads();
   return it;
 }
+
+// Thread-0 state of a workgroup that claims its items one ticket ahead:
+// when an item is handed out, the ticket for the next one is requested at
+// once, so that request's round trip overlaps the current item's work
+// instead of opening the next iteration.  Same queues and the same order of
+// queues as claim_item; a ticket requested ahead is always resolved by the
+// next call (a workgroup calls next() until it returns -1).
+struct ClaimAhead {
+  int qoff = 0;          // queues exhausted so far (home queue first)
+  bool ahead = false;    // a ticket request on queue (home + qoff) is in flight
+  uint32_t ticket = 0;
+
+  __device__ __forceinline__ int64_t next(uint32_t* ws, int64_t total) {
+    const int home = (int)(blockIdx.x % kNumQueues);
+    int64_t got = -1;
+    while (qoff < kNumQueues) {
+      const int q = (home + qoff) % kNumQueues;
+      const int64_t b = queue_begin(q, total), e = queue_begin(q + 1, total);
+      const uint32_t t = ahead ? ticket
+                               : __hip_atomic_fetch_add(&ws[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ahead = false;
+      if ((int64_t)t < e - b) { got = b + t; break; }
+      ++qoff;
+    }
+    if (got >= 0) {
+      ticket = __hip_atomic_fetch_add(&ws[(home + qoff) % kNumQueues], 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      ahead = true;
+    }
+    return got;
+  }
+};
 
 // Every workgroup calls this once when it has stopped claiming.  The last
 // one resets the queue counters and the done counter, leaving the workspace
