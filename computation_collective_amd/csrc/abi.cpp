@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <unordered_map>
@@ -132,6 +133,11 @@ hipError_t persistent_grid(const void* kernel, int threads, int64_t work, int* g
   }
   int64_t g = (int64_t)per_cu * di.cus;
   if (work < g) g = work;
+  // optional cap on the persistent grid (documented with the ABI)
+  if (const char* cap = std::getenv("HOCF_MAX_WORKGROUPS")) {
+    const long v = std::strtol(cap, nullptr, 10);
+    if (v > 0 && v < g) g = v;
+  }
   if (g < 1) g = 1;
   *grid = (int)g;
   return hipSuccess;

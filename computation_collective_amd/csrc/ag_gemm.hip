@@ -163,7 +163,9 @@ template <int TM, int TN, int ODT>
 static hipError_t launch_tile(const AgGemmArgs& a, hipStream_t s) {
   using Staged = TileBf16<TM, TN, 2, 2>;
   using Direct = TileBf16Direct<TM, TN, 2, 2>;
-  const bool ragged = (a.Mc % TM) || (a.N % TN) || (a.K % Direct::KSTEP);
+  // the direct tile takes full tiles whose operands it can address with 32-bit offsets
+  const bool ragged = (a.Mc % TM) || (a.N % TN) || (a.K % Direct::KSTEP) ||
+                      !Direct::operands_fit(a.K, a.N, a.K);
   return ragged ? launch_k<Staged, true, ODT>(a, s) : launch_k<Direct, false, ODT>(a, s);
 }
 

@@ -16,6 +16,15 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 enum Dt : int { kF32 = 0, kBF16 = 1 };
 
+// Buffer resource word 3 for raw (untyped, 32-bit format) buffer accesses.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// A raw buffer resource over [base, base + 2 GiB).  `base` must be
+// wave-uniform (it lands in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, kRawBufferWord3);
+}
+
 // bfloat16 is the top half of a binary32 pattern.
 __device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
 

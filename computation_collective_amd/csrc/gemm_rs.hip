@@ -25,7 +25,11 @@
 //   4. folds one band of a completed tile, if its band queue has one for it:
 //      checks the P flags and folds the P slots of the band's rows in rank
 //      order p = 0..P-1 in fp32 into the destination's output chunk -- while
-//      other workgroups are still computing.
+//      other workgroups are still computing.  Where the tile shape allows,
+//      the band rides along the workgroup's next GEMM tile: one row pass of
+//      slot loads is issued at the end of each K round of the mainloop and
+//      folded at the end of the next, so the band's memory latency hides
+//      behind MFMA work instead of stalling the workgroup.
 // With P = PIECES every workgroup alternates one GEMM tile and one band, so
 // the reduction traffic is spread evenly and the workgroups of an XCD stay in
 // step, which keeps their shared operand panels in L2.  A workgroup claims a
@@ -45,33 +49,61 @@
 
 namespace hocf {
 
-// Folds band `piece` of completed output tile `g` (group = (chunk r, tile)).
+// Where band `piece` of completed output tile `g` (group = (chunk r, tile))
+// lives: its tile in slot 0 of window r, its output rows, and the flags that
+// announced the tile's P contributions.
+template <class Tile, int SDT, int ODT>
+struct BandRef {
+  const char* slot0;
+  int64_t slot_bytes;
+  char* otile;
+  int row0, rows_valid, cols_valid;
+  const uint32_t* flags;  // flag of contribution q at flags[q * tiles per chunk]
+
+  __device__ __forceinline__ BandRef(const GemmRsArgs& a, int64_t g, int piece) {
+    using RL = ReduceLayout<Tile, SDT>;
+    constexpr int SES = SDT == kBF16 ? 2 : 4;
+    const int N = a.N, Mc = a.Mc;
+    const int tpc = a.mtiles * a.ntiles;
+    const int r = (int)(g / tpc), tflag = (int)(g % tpc);
+    const int mt = tflag / a.ntiles, nt = tflag % a.ntiles;
+    rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
+    cols_valid = min(Tile::TN, N - nt * Tile::TN);
+    row0 = piece * RL::PIECE_ROWS;
+    const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
+    slot0 = reinterpret_cast<const char*>(a.win_data[r]) + tile_off * SES;
+    slot_bytes = (int64_t)Mc * N * SES;
+    otile = reinterpret_cast<char*>(a.out) + ((int64_t)r * Mc * N + tile_off) * (ODT == kBF16 ? 2 : 4);
+    flags = &a.win_flags[r][tflag];
+  }
+  // the P contributions' flags must all carry this call's epoch (one thread
+  // each): the flag this thread checks (the epoch itself for threads >= P) ...
+  __device__ __forceinline__ uint32_t my_flag(const GemmRsArgs& a, int tpc) const {
+    return (int)threadIdx.x < a.P ? load_flag_agent(&flags[(int64_t)threadIdx.x * tpc]) : a.sync.epoch;
+  }
+  // ... and the check, which may come later than the load
+  __device__ __forceinline__ static void verify(const GemmRsArgs& a, uint32_t flag) {
+    if (flag != a.sync.epoch) report_status(a.sync, kErrProtocol);
+  }
+  __device__ __forceinline__ void check_flags(const GemmRsArgs& a, int tpc) const { verify(a, my_flag(a, tpc)); }
+};
+
+// Folds band `piece` of completed output tile `g` on its own.
 template <class Tile, bool RAGGED, int SDT, int ODT>
 __device__ __forceinline__ void reduce_band(const GemmRsArgs& a, int64_t g, int piece) {
-  using RL = ReduceLayout<Tile, SDT>;
-  constexpr int SES = SDT == kBF16 ? 2 : 4;
-  const int P = a.P, N = a.N, Mc = a.Mc;
-  const int tpc = a.mtiles * a.ntiles;
-  const int r = (int)(g / tpc), tflag = (int)(g % tpc);
-  const int mt = tflag / a.ntiles, nt = tflag % a.ntiles;
-  const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
-  const int cols_valid = min(Tile::TN, N - nt * Tile::TN);
-  const int row0 = piece * RL::PIECE_ROWS;
-  if (RAGGED && row0 >= rows_valid) return;
-  if ((int)threadIdx.x < P &&
-      load_flag_agent(&a.win_flags[r][(int64_t)threadIdx.x * tpc + tflag]) != a.sync.epoch)
-    report_status(a.sync, kErrProtocol);
-  const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
-  const char* slot0 = reinterpret_cast<const char*>(a.win_data[r]) + tile_off * SES;
-  const int64_t slot_bytes = (int64_t)Mc * N * SES;
-  char* otile = reinterpret_cast<char*>(a.out) + ((int64_t)r * Mc * N + tile_off) * (ODT == kBF16 ? 2 : 4);
+  const BandRef<Tile, SDT, ODT> b(a, g, piece);
+  if (RAGGED && b.row0 >= b.rows_valid) return;
+  b.check_flags(a, a.mtiles * a.ntiles);
+  const int P = a.P, N = a.N;
   if (P <= 4)
-    reduce_piece<Tile, SDT, ODT, RAGGED, 4, 8>(slot0, slot_bytes, P, N, otile, N, row0, rows_valid, cols_valid);
+    reduce_piece<Tile, SDT, ODT, RAGGED, 4, 8>(b.slot0, b.slot_bytes, P, N, b.otile, N, b.row0, b.rows_valid,
+                                               b.cols_valid);
   else if (P <= 8)
-    reduce_piece<Tile, SDT, ODT, RAGGED, 8, 4>(slot0, slot_bytes, P, N, otile, N, row0, rows_valid, cols_valid);
+    reduce_piece<Tile, SDT, ODT, RAGGED, 8, 4>(b.slot0, b.slot_bytes, P, N, b.otile, N, b.row0, b.rows_valid,
+                                               b.cols_valid);
   else
-    reduce_piece<Tile, SDT, ODT, RAGGED, kMaxP, 2>(slot0, slot_bytes, P, N, otile, N, row0, rows_valid,
-                                                   cols_valid);
+    reduce_piece<Tile, SDT, ODT, RAGGED, kMaxP, 2>(b.slot0, b.slot_bytes, P, N, b.otile, N, b.row0,
+                                                   b.rows_valid, b.cols_valid);
 }
 
 template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
@@ -80,6 +112,11 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   constexpr int S = ReduceLayout<Tile, SDT>::PIECES;
   // tiles with a split mainloop start the next tile's loads before the band
   constexpr bool kSplit = Tile::kSplitMainloop;
+  // ... and, if the band's parked rows fit in LDS beside the stages, fold the
+  // band during the tile's mainloop (full tiles, P <= 8, enough K rounds)
+  using Band = BandFold<Tile, SDT, ODT, 8>;
+  constexpr bool kBandInLoop = kSplit && !RAGGED && Tile::LDS_BYTES + Band::LDS_BYTES + 1024 <= 160 * 1024;
+  __shared__ __attribute__((aligned(16))) char band_park[kBandInLoop ? Band::LDS_BYTES : 16];
   // LDS stages, one __shared__ array each (tiles with fewer stages leave the rest tiny)
   __shared__ __attribute__((aligned(1024))) char smem0[Tile::SMEM_BYTES];
   __shared__ __attribute__((aligned(1024))) char smem1[Tile::NST > 1 ? Tile::SMEM_BYTES : 16];
@@ -103,6 +140,10 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   const int64_t nbands = ngroups * S;
   auto bq_total = [&](int q) { return (uint32_t)((nbands - q + kNumQueues - 1) / kNumQueues); };
   const int home = (int)(blockIdx.x % kNumQueues);
+  constexpr int SES = SDT == kBF16 ? 2 : 4;
+  bool loop_band_ok = false;
+  if constexpr (kBandInLoop)
+    loop_band_ok = P <= 8 && Tile::side_fits(K, Band::NPASS) && (int64_t)P * Mc * N * SES < (int64_t(1) << 31);
 
   // thread 0's claim state: tiles and band slots are both requested one
   // iteration ahead; a claimed band slot (queue, index) waits in pend_* until
@@ -184,21 +225,41 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
       tflag = mt * a.ntiles + nt;
       At = reinterpret_cast<const Elem*>(a.A) + ((int64_t)p * a.M + (int64_t)r * Mc + (int64_t)mt * Tile::TM) * K;
       Wt = reinterpret_cast<const Elem*>(a.W) + (int64_t)p * K * N + (int64_t)nt * Tile::TN;
-      // the tile's first operand slices start loading now ...
+    }
+    // 4. the band: folded during this iteration's mainloop, or on its own
+    // while the tile's first operand slices load (it does not touch the stages)
+    const bool band_in_loop = kBandInLoop && loop_band_ok && state == 1 && item >= 0;
+    // (the in-loop band's flags are loaded now and checked after the mainloop)
+    uint32_t band_flag = 0;
+    if (band_in_loop) band_flag = BandRef<Tile, SDT, ODT>(a, band / S, band % S).my_flag(a, tpc);
+    if (item >= 0) {
       if constexpr (kSplit) Tile::prologue(At, K, Wt, N, K, stages);
     }
-    // 4. ... while the band folds (its loads do not touch the stage arrays)
-    if (state == 1) reduce_band<Tile, RAGGED, SDT, ODT>(a, band / S, band % S);
+    if (state == 1 && !band_in_loop) reduce_band<Tile, RAGGED, SDT, ODT>(a, band / S, band % S);
 
     if (item >= 0) {
       const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
       const int cols_valid = min(Tile::TN, N - nt * Tile::TN);
       floatx16 acc[Tile::FM][Tile::FN];
-      if constexpr (kSplit) Tile::template body<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
-      else Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
+      if constexpr (kBandInLoop) {
+        if (band_in_loop) {
+          const BandRef<Tile, SDT, ODT> b(a, band / S, band % S);
+          Band side;
+          side.init(b.slot0, (uint32_t)b.slot_bytes, P, N, b.row0,
+                    (typename Band::lds_char*)(band_park));
+          Tile::template body_side<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc, side);
+          side.flush(b.otile, N, b.row0);
+          BandRef<Tile, SDT, ODT>::verify(a, band_flag);
+        } else {
+          Tile::template body<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
+        }
+      } else if constexpr (kSplit) {
+        Tile::template body<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
+      } else {
+        Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
+      }
 
       // 1. publish the tile into window r, slot p
-      constexpr int SES = SDT == kBF16 ? 2 : 4;
       char* wdata = reinterpret_cast<char*>(a.win_data[r]);
       const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
       store_tile<Tile, SDT, RAGGED, kPolicyDevice, false>(wdata + ((int64_t)p * Mc * N + tile_off) * SES, N,
@@ -263,7 +324,9 @@ template <int TM, int TN, int SDT, int ODT>
 static hipError_t launch_bf16_dt(const GemmRsArgs& a, hipStream_t s) {
   using Staged = TileBf16<TM, TN, 2, 2>;
   using Direct = TileBf16Direct<TM, TN, 2, 2>;
-  const bool ragged = (a.Mc % TM) || (a.N % TN) || (a.K % Direct::KSTEP);
+  // the direct tile takes full tiles whose operands it can address with 32-bit offsets
+  const bool ragged = (a.Mc % TM) || (a.N % TN) || (a.K % Direct::KSTEP) ||
+                      !Direct::operands_fit(a.K, a.N, a.K);
   return ragged ? launch_one<Staged, true, true, SDT, ODT>(a, s)
                 : launch_one<Direct, false, true, SDT, ODT>(a, s);
 }

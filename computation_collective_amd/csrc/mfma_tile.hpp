@@ -259,6 +259,16 @@ __device__ __forceinline__ void interleave() {
   interleave_impl<NM, ND, NV>(std::make_integer_sequence<int, NM>{});
 }
 
+// Work a mainloop can carry at the ends of its K rounds (see
+// TileBf16Direct::body): NPASS units, unit u's V vector-memory loads issued
+// by issue(u) at the end of round u and consumed by fold(u) at the end of
+// round u+1, where no vector-memory operation may be issued.
+struct NoSide {
+  static constexpr int NPASS = 0, V = 0;
+  __device__ void issue(int) {}
+  __device__ void fold(int) {}
+};
+
 // bf16 tile, full tiles only (no ragged rows, columns or K): both operand
 // slices go from global memory straight into LDS (gfx950 global_load_lds,
 // 16 bytes per lane, a wave writing 1 KB of LDS per instruction), so no
@@ -334,7 +344,8 @@ struct TileBf16Direct {
                                              const uint16_t* __restrict__ W, int64_t ldw,
                                              int rows_valid, int cols_valid, int K,
                                              char* const (&stages)[4], floatx16 (&acc)[FM][FN]) {
-    parts<RAGGED, true, true>(A, lda, W, ldw, rows_valid, cols_valid, K, stages, acc);
+    NoSide none;
+    parts<RAGGED, true, true>(A, lda, W, ldw, rows_valid, cols_valid, K, stages, acc, none);
   }
   // Split use: prologue() issues the loads of the first NST-1 slices into
   // the stage arrays and returns; body() (same arguments) then issues the
@@ -346,24 +357,47 @@ struct TileBf16Direct {
                                                   const uint16_t* __restrict__ W, int64_t ldw, int K,
                                                   char* const (&stages)[4]) {
     floatx16 unused[FM][FN];
-    parts<false, true, false>(A, lda, W, ldw, TM, TN, K, stages, unused);
+    NoSide none;
+    parts<false, true, false>(A, lda, W, ldw, TM, TN, K, stages, unused, none);
   }
   template <bool RAGGED>
   __device__ static __forceinline__ void body(const uint16_t* __restrict__ A, int64_t lda,
                                               const uint16_t* __restrict__ W, int64_t ldw,
                                               int rows_valid, int cols_valid, int K,
                                               char* const (&stages)[4], floatx16 (&acc)[FM][FN]) {
-    parts<RAGGED, false, true>(A, lda, W, ldw, rows_valid, cols_valid, K, stages, acc);
+    NoSide none;
+    parts<RAGGED, false, true>(A, lda, W, ldw, rows_valid, cols_valid, K, stages, acc, none);
+  }
+  // body() carrying side work at the ends of its rounds of NST slices:
+  // side.issue(u) after round u's last loads, side.fold(u) after round u+1
+  // (u < Side::NPASS).  The caller guarantees K / (NST * BK) >= NPASS + 2,
+  // so the side work ends before the last round that loads.
+  static constexpr bool side_fits(int K, int npass) { return K / (NST * BK) >= npass + 2; }
+  // the operand loads address A's TM rows and W's K rows through 2 GiB
+  // buffer resources (32-bit offsets from the tile's origin)
+  static constexpr bool operands_fit(int64_t lda, int64_t ldw, int64_t K) {
+    return ((int64_t)TM * lda + K) * 2 < (int64_t(1) << 31) && K * ldw * 2 < (int64_t(1) << 31);
+  }
+  template <bool RAGGED, class Side>
+  __device__ static __forceinline__ void body_side(const uint16_t* __restrict__ A, int64_t lda,
+                                                   const uint16_t* __restrict__ W, int64_t ldw,
+                                                   int rows_valid, int cols_valid, int K,
+                                                   char* const (&stages)[4], floatx16 (&acc)[FM][FN],
+                                                   Side& side) {
+    parts<RAGGED, false, true>(A, lda, W, ldw, rows_valid, cols_valid, K, stages, acc, side);
   }
 
-  template <bool RAGGED, bool PRO, bool BODY>
+  template <bool RAGGED, bool PRO, bool BODY, class Side = NoSide>
   __device__ static __forceinline__ void parts(const uint16_t* __restrict__ A, int64_t lda,
                                                const uint16_t* __restrict__ W, int64_t ldw,
                                                int /*rows_valid*/, int /*cols_valid*/, int K,
-                                               char* const (&stages)[4], floatx16 (&acc)[FM][FN]) {
+                                               char* const (&stages)[4], floatx16 (&acc)[FM][FN],
+                                               Side& side) {
     static_assert(!RAGGED, "full tiles only");
 #if defined(__HIP_DEVICE_COMPILE__)  // device-only body (the host pass only needs the declaration)
-    const int tid = threadIdx.x, lane = opaque_lane(), wave = tid >> 6;
+    // the wave index is wave-uniform: kept in a scalar register, so every
+    // per-wave LDS address below is scalar too
+    const int tid = threadIdx.x, lane = opaque_lane(), wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     if constexpr (BODY) {
 #pragma unroll
@@ -379,35 +413,38 @@ struct TileBf16Direct {
     // it leaves the accumulators at zero instead.
     if (nk == 0 || nk % NST != 0 || K % BK != 0) return;
 
-    // per-lane global sources (fixed over K; the k offset is added per stage)
-    const uint16_t* asrc[A_LD];
-    const uint16_t* wsrc[W_LD];
+    // operand loads go through buffer resources over the tile's A rows and W
+    // columns: a 32-bit byte offset per lane and load (fixed over K), the
+    // slice's k offset in a scalar register -- no 64-bit pointer per load and
+    // stage in vector registers
+    const __amdgpu_buffer_rsrc_t rsa = raw_rsrc(A), rsw = raw_rsrc(W);
+    uint32_t aoff[A_LD], woff[W_LD];
 #pragma unroll
     for (int t = 0; t < A_LD; ++t) {
       const int b = t * NW + wave;
       const int row = b * AROWS_PER_BLOCK + lane / CA;
       const int c = (lane % CA) ^ ((row / (16 / CA)) % CA);
-      asrc[t] = A + (int64_t)row * lda + c * 8;
+      aoff[t] = (uint32_t)(((int64_t)row * lda + c * 8) * 2);
     }
 #pragma unroll
     for (int t = 0; t < W_LD; ++t) {
       const int b = t * NW + wave;
       const int k = b * WROWS_PER_BLOCK + lane / CW;
       const int c = (lane % CW) ^ (4 * (k & 3));
-      wsrc[t] = W + (int64_t)k * ldw + c * 8;
+      woff[t] = (uint32_t)(((int64_t)k * ldw + c * 8) * 2);
     }
     auto load_stage = [&](char* sb, int ks) {
-      const int64_t ak = (int64_t)ks * BK;
-      const int64_t wk = (int64_t)ks * BK * ldw;
+      const uint32_t ak = (uint32_t)ks * (BK * 2);
+      const uint32_t wk = (uint32_t)ks * (uint32_t)(BK * ldw * 2);
 #pragma unroll
       for (int t = 0; t < A_LD; ++t)
-        __builtin_amdgcn_global_load_lds(
-            asrc[t] + ak, (__attribute__((address_space(3))) void*)(sb + (t * NW + wave) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsa, (__attribute__((address_space(3))) void*)(sb + (t * NW + wave) * 1024), 16, aoff[t], ak, 0, 0);
 #pragma unroll
       for (int t = 0; t < W_LD; ++t)
-        __builtin_amdgcn_global_load_lds(
-            wsrc[t] + wk, (__attribute__((address_space(3))) void*)(sb + A_BYTES + (t * NW + wave) * 1024),
-            16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsw, (__attribute__((address_space(3))) void*)(sb + A_BYTES + (t * NW + wave) * 1024), 16, woff[t],
+            wk, 0, 0);
     };
 
     typedef short short4v __attribute__((ext_vector_type(4)));
@@ -465,8 +502,9 @@ struct TileBf16Direct {
     // in flight) and for its LDS reads, then meets the other waves.  A bare
     // s_barrier: __syncthreads() would add a release fence that drains every
     // load in flight.
-    auto sync_slices = [&](auto later_c) {
-      constexpr int N = decltype(later_c)::value * LPS;
+    auto sync_slices = [&](auto later_c, auto extra_c) {
+      constexpr int N = decltype(later_c)::value * LPS + decltype(extra_c)::value;
+      static_assert(N <= 63, "vmcnt range");
       __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);  // vmcnt(N) lgkmcnt(0)
       __asm__ volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -474,14 +512,15 @@ struct TileBf16Direct {
     };
     // slice j in stage ST; LOAD: issue slice j+NST into stage ST after the
     // barrier; NEXT: read slice j+1's first fragments from stage (ST+1)%NST;
-    // LATER: slices whose loads were issued after slice j+1's
-    auto slice = [&](auto st_c, auto load_c, auto next_c, auto later_c, int j) {
+    // LATER: slices whose loads were issued after slice j+1's; EXTRA: other
+    // vector-memory operations issued after slice j+1's loads
+    auto slice = [&](auto st_c, auto load_c, auto next_c, auto later_c, auto extra_c, int j) {
       constexpr int ST = decltype(st_c)::value;
       char* const sb = stages[ST];
       read_frags(sb, 1, fa1, fb1);
       mfmas(fa0, fb0);
       interleave<NM, ND, 0>();
-      sync_slices(later_c);
+      sync_slices(later_c, extra_c);
       if constexpr (decltype(load_c)::value) load_stage(sb, j + NST);
       if constexpr (decltype(next_c)::value) read_frags(stages[(ST + 1) % NST], 0, fa0, fb0);
       mfmas(fa1, fb1);
@@ -499,35 +538,57 @@ struct TileBf16Direct {
       for (int s = 0; s < NST - 1; ++s) load_stage(stages[s], s);
     }
     if constexpr (!BODY) return;
+    using Z_ = std::integral_constant<int, 0>;
     load_stage(stages[NST - 1], NST - 1);
     // slice 0 landed everywhere: the wait leaves only the NST-1 batches issued
     // last in flight, and slice 0's were issued before them
-    sync_slices(std::integral_constant<int, NST - 1>{});
+    sync_slices(std::integral_constant<int, NST - 1>{}, Z_{});
     read_frags(stages[0], 0, fa0, fb0);
-    // K is a multiple of NST*BK: whole rounds of NST slices, the last round
-    // without loads
-    for (int j0 = 0; j0 < nk - NST; j0 += NST) {
-      slice(std::integral_constant<int, 0>{}, T_{}, T_{}, std::integral_constant<int, NST - 2>{}, j0);
-      slice(std::integral_constant<int, 1>{}, T_{}, T_{}, std::integral_constant<int, NST - 2>{}, j0 + 1);
-      if constexpr (NST > 2)
-        slice(std::integral_constant<int, 2 % NST>{}, T_{}, T_{}, std::integral_constant<int, NST - 2>{}, j0 + 2);
-      if constexpr (NST > 3)
-        slice(std::integral_constant<int, 3 % NST>{}, T_{}, T_{}, std::integral_constant<int, NST - 2>{}, j0 + 3);
-    }
-    {
-      const int j0 = nk - NST;
-      slice(std::integral_constant<int, 0>{}, F_{}, T_{}, std::integral_constant<int, NST - 2>{}, j0);
-      if constexpr (NST == 2) {
-        slice(std::integral_constant<int, 1>{}, F_{}, F_{}, std::integral_constant<int, 0>{}, j0 + 1);
-      } else if constexpr (NST == 3) {
-        slice(std::integral_constant<int, 1>{}, F_{}, T_{}, std::integral_constant<int, 0>{}, j0 + 1);
-        slice(std::integral_constant<int, 2>{}, F_{}, F_{}, std::integral_constant<int, 0>{}, j0 + 2);
+
+    // One round = NST slices starting at slice j0 (stage s holds slice j0+s).
+    // Every slice of a round but the last waits for loads issued in the
+    // previous round; if side work issued PV loads at that round's end, after
+    // those, the waits allow for them (PV more operations in flight).
+    static_assert(NST == 4, "round structure");
+    auto round = [&](auto pv_c, auto loads_c, int j0) {
+      using L_ = decltype(loads_c);
+      using LT_ = std::integral_constant<int, NST - 2>;
+      if constexpr (L_::value) {
+        slice(std::integral_constant<int, 0>{}, T_{}, T_{}, LT_{}, pv_c, j0);
+        slice(std::integral_constant<int, 1>{}, T_{}, T_{}, LT_{}, pv_c, j0 + 1);
+        slice(std::integral_constant<int, 2>{}, T_{}, T_{}, LT_{}, pv_c, j0 + 2);
+        slice(std::integral_constant<int, 3>{}, T_{}, T_{}, LT_{}, Z_{}, j0 + 3);
       } else {
-        slice(std::integral_constant<int, 1>{}, F_{}, T_{}, std::integral_constant<int, 1>{}, j0 + 1);
-        slice(std::integral_constant<int, 2>{}, F_{}, T_{}, std::integral_constant<int, 0>{}, j0 + 2);
-        slice(std::integral_constant<int, 3>{}, F_{}, F_{}, std::integral_constant<int, 0>{}, j0 + 3);
+        // the last round: no loads
+        slice(std::integral_constant<int, 0>{}, F_{}, T_{}, LT_{}, pv_c, j0);
+        slice(std::integral_constant<int, 1>{}, F_{}, T_{}, std::integral_constant<int, 1>{}, pv_c, j0 + 1);
+        slice(std::integral_constant<int, 2>{}, F_{}, T_{}, Z_{}, pv_c, j0 + 2);
+        slice(std::integral_constant<int, 3>{}, F_{}, F_{}, Z_{}, Z_{}, j0 + 3);
       }
+    };
+    // side work at a round's end, kept after every load of that round
+    auto side_step = [&](auto fold_c, auto issue_c, int u) {
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(fold_c)::value) side.fold(u - 1);
+      if constexpr (decltype(issue_c)::value) side.issue(u);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using PV_ = std::integral_constant<int, Side::V>;
+    const int nr = nk / NST;  // K is a multiple of NST*BK: whole rounds, the last without loads
+    int r = 0;
+    if constexpr (Side::NPASS > 0) {
+      round(Z_{}, T_{}, 0);
+      side_step(F_{}, T_{}, 0);
+      for (r = 1; r < Side::NPASS; ++r) {
+        round(PV_{}, T_{}, r * NST);
+        side_step(T_{}, T_{}, r);
+      }
+      round(PV_{}, T_{}, r * NST);
+      side_step(T_{}, F_{}, r);
+      ++r;
     }
+    for (; r < nr - 1; ++r) round(Z_{}, T_{}, r * NST);
+    round(Z_{}, F_{}, (nr - 1) * NST);
 #endif
   }
 };

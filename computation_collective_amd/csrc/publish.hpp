@@ -33,8 +33,6 @@
 
 namespace hocf {
 
-// Buffer resource word 3 for raw (untyped, 32-bit format) buffer accesses.
-constexpr int kRawBufferWord3 = 0x00020000;
 // Cache-policy operands: SC1 (device scope) with NT (streaming: published
 // data is written once and read once, so it should not displace the GEMM
 // operands in the caches), and none (ordinary write-back).
@@ -44,11 +42,6 @@ constexpr int kPolicyPlain = 0;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// A raw buffer resource over [base, base + 2 GiB).  `base` must be
-// wave-uniform (it lands in scalar registers).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, kRawBufferWord3);
-}
 
 // 16-byte device-coherent accesses at byte offset voff (per lane) + soff
 // (wave-uniform) from the resource's base.
@@ -260,5 +253,104 @@ __device__ __forceinline__ void reduce_piece(const char* slot0, int64_t slot_byt
     }
   }
 }
+
+// The fold of reduce_piece, for one band carried through a GEMM mainloop as
+// its side work (TileBf16Direct::body_side): unit u is row pass u of the
+// band, its PMAX device-coherent slot loads issued at the end of one K round
+// and folded (rank order, fp32, rounded once to ODT) at the end of the next,
+// so the loads' latency hides behind MFMA work.  Folded rows are parked in
+// LDS (the mainloop may issue no vector-memory stores of its own) and
+// written out by flush().  Same arithmetic and element order as
+// reduce_piece; requires P <= PMAX and a window below 2 GiB from the
+// band's slot 0 (P * slot_bytes < 2^31).
+template <class Tile, int SDT, int ODT, int PMAX>
+struct BandFold {
+  using L = ReduceLayout<Tile, SDT>;
+  static constexpr int NPASS = L::PIECE_ROWS / L::RPS;
+  static constexpr int V = PMAX;
+  static constexpr int OES = ODT == kBF16 ? 2 : 4;
+  static constexpr int OUT_BYTES = L::CE * OES;  // one thread's result of one pass
+  static constexpr int LDS_BYTES = NPASS * Tile::NT * OUT_BYTES;
+  typedef __attribute__((address_space(3))) char lds_char;
+
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff, slot_bytes, pass_bytes;
+  int P;
+  lds_char* park;
+  u32x4 v[PMAX];
+
+  // slot0: the band's tile in slot 0 (wave-uniform); area: LDS_BYTES of LDS
+  __device__ __forceinline__ void init(const char* slot0, uint32_t slot_bytes_, int P_, int64_t ld, int row0,
+                                       lds_char* area) {
+    const int tid = (int)(threadIdx.x & ~63) + opaque_lane();
+    const int r0 = row0 + tid / L::CPR, col = (tid % L::CPR) * L::CE;
+    rs = raw_rsrc(slot0);
+    voff = (uint32_t)(((int64_t)r0 * ld + col) * L::SES);
+    slot_bytes = slot_bytes_;
+    pass_bytes = (uint32_t)(L::RPS * ld * L::SES);
+    P = P_;
+    park = area + tid * OUT_BYTES;
+  }
+  __device__ __forceinline__ void issue(int pass) {
+#pragma unroll
+    for (int q = 0; q < PMAX; ++q) {
+      const int qq = q < P ? q : P - 1;  // past P: re-read slot P-1, never added
+      v[q] = ld_dev16(rs, voff, (uint32_t)qq * slot_bytes + (uint32_t)pass * pass_bytes);
+    }
+  }
+  __device__ __forceinline__ void fold(int pass) {
+    lds_char* o = park + pass * (Tile::NT * OUT_BYTES);
+    if constexpr (SDT == kF32) {
+      floatx4 s = __builtin_bit_cast(floatx4, v[0]);
+#pragma unroll
+      for (int q = 1; q < PMAX; ++q)
+        if (q < P) s = s + __builtin_bit_cast(floatx4, v[q]);
+      if constexpr (ODT == kBF16)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(o) =
+            u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+      else
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(o) = __builtin_bit_cast(u32x4, s);
+    } else {
+      floatx4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < PMAX; ++q) {
+        const u32x4 w = v[q];
+        const floatx4 a = {bf16_to_f32(w[0] & 0xffffu), bf16_to_f32(w[0] >> 16),
+                           bf16_to_f32(w[1] & 0xffffu), bf16_to_f32(w[1] >> 16)};
+        const floatx4 b = {bf16_to_f32(w[2] & 0xffffu), bf16_to_f32(w[2] >> 16),
+                           bf16_to_f32(w[3] & 0xffffu), bf16_to_f32(w[3] >> 16)};
+        if (q == 0) { lo = a; hi = b; }
+        else if (q < P) { lo = lo + a; hi = hi + b; }
+      }
+      if constexpr (ODT == kBF16) {
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(o) =
+            u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                  pack_bf16x2(hi[2], hi[3])};
+      } else {
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(o) = __builtin_bit_cast(u32x4, lo);
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(o + 16) = __builtin_bit_cast(u32x4, hi);
+      }
+    }
+  }
+  // the parked rows -> out (the band's output tile origin, leading dimension ld_out)
+  __device__ __forceinline__ void flush(void* out, int64_t ld_out, int row0) {
+    const int tid = (int)(threadIdx.x & ~63) + opaque_lane();
+    const int r0 = row0 + tid / L::CPR, col = (tid % L::CPR) * L::CE;
+    char* obase = reinterpret_cast<char*>(out) + ((int64_t)r0 * ld_out + col) * OES;
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+      const lds_char* src = park + pass * (Tile::NT * OUT_BYTES);
+      char* dst = obase + (int64_t)pass * L::RPS * ld_out * OES;
+      if constexpr (OUT_BYTES == 8) {
+        *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(src);
+      } else {
+#pragma unroll
+        for (int b = 0; b < OUT_BYTES; b += 16)
+          *reinterpret_cast<u32x4*>(dst + b) =
+              *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(src + b);
+      }
+    }
+  }
+};
 
 }  // namespace hocf

@@ -49,11 +49,20 @@
  * Flags.  Flag words are uint32 and hold an epoch: a word equals
  * sync->epoch once the data it guards is complete and visible device-wide.
  * The library's producers write guarded data with device-coherent stores
- * and wait for their completion before the flag store; a consumer that sees
+ * and wait for their completion before the flag store (or, for the
+ * embedding windows, with ordinary stores and an agent-scope release fence
+ * before it); a consumer that sees
  * the epoch (agent-scope atomic load) and then reads the data either with
  * device-coherent loads or after an agent-scope acquire fence sees it all.
  * Each call must use an epoch different from the previous call on the same
  * flag arrays, so flags never need resetting.
+ *
+ * Grid.  Each call launches one persistent kernel with as many workgroups
+ * as the device holds at once, capped by the number of work items.  The
+ * environment variable HOCF_MAX_WORKGROUPS (a positive integer, read at each
+ * call) caps it further, e.g. to leave CUs to other work or to have each
+ * workgroup take many items; every operator completes with any grid of one
+ * or more workgroups.
  *
  * Workspace.  Scheduler counters.  The caller allocates at least the size
  * the matching *_workspace_bytes() query returns, zeroes it ONCE, and may

@@ -178,6 +178,43 @@ def test_gemm_rs_alternating_inputs_no_stale_reads(sdt):
         np.testing.assert_array_equal(bf.to_host(run.win_data, sdt), slots, err_msg=f"call {call}")
 
 
+@pytest.mark.parametrize("P,tm,sdt", [(4, 256, F32), (8, 256, F32), (4, 256, BF16), (3, 128, F32)])
+def test_gemm_rs_band_in_mainloop_integer_bit_exact(P, tm, sdt, monkeypatch):
+    """A small grid makes every workgroup take several tiles, so the bands of
+    completed tiles are folded during later tiles' mainloops (K = 1280 leaves
+    enough K rounds for it); integer inputs make the result bit-exact."""
+    monkeypatch.setenv("HOCF_MAX_WORKGROUPS", "16")
+    Mc, N, K = (2 * tm, 2 * tm, 1280) if P <= 4 else (tm, tm, 1280)
+    say(f"gemm_rs band in mainloop P={P} Mc={Mc} N={N} K={K} tile={tm} slot={sdt} grid<=16")
+    ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    run, slots, out = _gemm_rs(P, Mc, N, K, BF16, sdt, BF16, tm, tm, seed=40 + P + sdt, dist=ints)
+    np.testing.assert_array_equal(bf.to_host(run.out, BF16), out)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, sdt), slots)
+    assert torch.all(run.win_flags == run.epoch)
+
+
+def test_gemm_rs_band_in_mainloop_values(monkeypatch):
+    monkeypatch.setenv("HOCF_MAX_WORKGROUPS", "24")
+    P, Mc, N, K = 8, 256, 512, 1536
+    say(f"gemm_rs band in mainloop N(0,1) P={P} Mc={Mc} N={N} K={K} grid<=24")
+    run, slots, out = _gemm_rs(P, Mc, N, K, BF16, F32, BF16, 256, 256, seed=77)
+    assert relerr(val(bf.to_host(run.out, BF16), BF16), val(out, BF16)) <= TOL[BF16]
+    assert relerr(bf.to_host(run.win_data, F32), slots) <= TOL[BF16]
+
+
+@pytest.mark.parametrize("grid", [1, 5, 13])
+def test_gemm_rs_small_grids_integer_bit_exact(grid, monkeypatch):
+    """Grids below the queue count (and not a multiple of it): queues without
+    a home workgroup are drained by stealing, every band still gets folded."""
+    monkeypatch.setenv("HOCF_MAX_WORKGROUPS", str(grid))
+    P, Mc, N, K = 4, 512, 512, 256
+    say(f"gemm_rs grid={grid} P={P} Mc={Mc} N={N} K={K}")
+    ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    run, slots, out = _gemm_rs(P, Mc, N, K, BF16, F32, BF16, 256, 256, seed=50 + grid, dist=ints)
+    np.testing.assert_array_equal(bf.to_host(run.out, BF16), out)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, F32), slots)
+
+
 @pytest.mark.parametrize("sdt", [F32, BF16])
 def test_gemm_rs_full_mlpdown(sdt):
     c = cfgs.GEMM_RS_MLP
