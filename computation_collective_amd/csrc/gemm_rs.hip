@@ -19,9 +19,9 @@
 //      device-coherent full-row stores, and waits for their completion,
 //   2. stores the epoch into the tile's ready flag in window r,
 //   3. counts itself in the output tile's arrival counter; the workgroup
-//      that completes the count (the last of the P producers) hands the
-//      tile's reduction out as PIECES bands of rows, band k of all bands
-//      going to band queue k mod 8 (one queue per XCD),
+//      that completes the count (the last of the P producers) marks the
+//      tile ready: its reduction is PIECES bands of rows, band q of every
+//      output tile sitting in band queue q (one queue per XCD),
 //   4. folds one band of a completed tile, if its band queue has one for it:
 //      checks the P flags and folds the P slots of the band's rows in rank
 //      order p = 0..P-1 in fp32 into the destination's output chunk -- while
@@ -32,13 +32,15 @@
 //      behind MFMA work instead of stalling the workgroup.
 // With P = PIECES every workgroup alternates one GEMM tile and one band, so
 // the reduction traffic is spread evenly and the workgroups of an XCD stay in
-// step, which keeps their shared operand panels in L2.  A workgroup claims a
-// slot of its home band queue with one atomic add; every slot below the
-// queue's known total is filled once its tile completes, so the workgroup
-// holds the slot and checks it after each of its own tiles, never waiting
-// while tiles remain.  Without tiles it waits (bounded) for its slot, then
-// helps drain the other queues; tiles are always claimed by running
-// workgroups, so every slot is filled and the kernel ends.
+// step, which keeps their shared operand panels in L2.  The slots of a band
+// queue follow the order in which output tiles complete (every shard's
+// items run in the same chunk and tile order), so a workgroup claims the
+// next slot of its home queue with one atomic add, holds it, and checks its
+// tile's ready word after each of its own tiles, never waiting while tiles
+// remain; completing an output tile costs its last producer one store.
+// Without tiles a workgroup waits (bounded) for its slot, then helps drain
+// the other queues; tiles are always claimed by running workgroups, so
+// every slot becomes ready and the kernel ends.
 // No step needs an L2-wide write-back or invalidate (publish.hpp).
 #include <type_traits>
 
@@ -131,15 +133,23 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
   const int P = a.P, N = a.N, K = a.K, Mc = a.Mc;
   const int tpc = a.mtiles * a.ntiles;
   const int64_t ngroups = (int64_t)P * tpc;
-  // workspace after the queue block: arrival counters [P][tpc], band queue heads [8]
-  // and tails [8], then the band queues [8][P * tpc] (bands k = tile * S + s, plus 1)
+  // workspace after the queue block: arrival counters [P][tpc], band queue
+  // heads [8] (and 8 spare words), then one ready word per output tile
+  // (the rest of that area is spare)
   uint32_t* grp = a.ws + kWsExtra;
   uint32_t* bq_head = grp + ngroups;
-  uint32_t* bq_tail = bq_head + kNumQueues;
-  uint32_t* bq = bq_tail + kNumQueues;
-  const int64_t nbands = ngroups * S;
-  auto bq_total = [&](int q) { return (uint32_t)((nbands - q + kNumQueues - 1) / kNumQueues); };
-  const int home = (int)(blockIdx.x % kNumQueues);
+  uint32_t* gready = bq_head + 2 * kNumQueues;
+  // Band queue q (q < S) holds band q of every output tile, in the order in
+  // which the tiles' last contributions are computed (chunk-major, then the
+  // item order within a chunk): slot t -> output tile band_tile(t).  A slot
+  // is claimed with one atomic add on the queue's head and is ready once
+  // its tile's ready word is set; producers never touch the queues.
+  auto bq_total = [&](int q) { return q < S ? (uint32_t)ngroups : 0u; };
+  auto band_tile = [&](uint32_t t) {
+    const int r = (int)(t / tpc), tq = (int)(t % tpc);
+    return (int64_t)r * tpc + (int64_t)(tq % a.mtiles) * a.ntiles + tq / a.mtiles;
+  };
+  const int home = (int)(blockIdx.x % kNumQueues) % S;
   constexpr int SES = SDT == kBF16 ? 2 : 4;
   bool loop_band_ok = false;
   if constexpr (kBandInLoop)
@@ -178,18 +188,19 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
         if (pend_q < 0 && !tl) state = 2;
       }
       if (pend_q >= 0) {
-        uint32_t e = __hip_atomic_load(&bq[pend_q * ngroups + pend_i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int64_t g = band_tile(pend_i);
+        uint32_t e = __hip_atomic_load(&gready[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (e == 0 && !tl) {
           // nothing else to do: wait (bounded) for the slot's tile to complete
           const Deadline wl{now_ticks(), a.sync.timeout_ticks};
           while (e == 0 && !wl.expired()) {
             __builtin_amdgcn_s_sleep(4);
-            e = __hip_atomic_load(&bq[pend_q * ngroups + pend_i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            e = __hip_atomic_load(&gready[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
           if (e == 0) { report_status(a.sync, kErrTimeout); state = 3; }
         }
         if (e != 0) {
-          band = (int)(e - 1u);
+          band = (int)(g * S + pend_q);
           state = 1;
           pend_q = -1;
           if (tl) {
@@ -277,17 +288,9 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
         uint32_t* cnt = &grp[(int64_t)r * tpc + tflag];
         const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (prev == (uint32_t)(P - 1)) {
+          // the last producer: the tile's bands are ready
           __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const int64_t g = (int64_t)r * tpc + tflag;
-          uint32_t at[S];
-#pragma unroll
-          for (int b = 0; b < S; ++b)
-            at[b] = __hip_atomic_fetch_add(&bq_tail[(g * S + b) % kNumQueues], 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-          for (int b = 0; b < S; ++b)
-            __hip_atomic_store(&bq[((g * S + b) % kNumQueues) * ngroups + at[b]], (uint32_t)(g * S + b) + 1u,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&gready[(int64_t)r * tpc + tflag], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
       // (the barrier at the top of the loop ends this thread-0 region)
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
 
   // the last workgroup out leaves the workspace zeroed
   if (finish_workgroup_last(a.ws, &s_last)) {
-    for (int64_t i = tid; i < 2 * kNumQueues + kNumQueues * ngroups; i += Tile::NT)
+    for (int64_t i = tid; i < 2 * kNumQueues + ngroups; i += Tile::NT)
       __hip_atomic_store(&bq_head[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
