@@ -12,17 +12,18 @@
 // the workspace.  Tiles are dealt from one ticket counter: ticket t is tile
 // (t mod Tc) of the chunk at arrival position (t / Tc), Tc = tiles per chunk,
 // so a workgroup that draws a ticket waits (bounded) only for the chunk its
-// ticket names, and never for another workgroup.  A workgroup polls all
-// flags with one batch of loads and acquires (system scope: the writer may
-// be a DMA engine) once per batch of newly seen chunks, before it reads any
-// of them.  Tiles are computed identically whatever the order, so the output
+// ticket names, and never for another workgroup.  A workgroup whose chunk is
+// already on the list only acquires it (no flag polling, no atomic on the
+// registration mask); otherwise it polls all flags with one batch of loads
+// and acquires (system scope: the writer may be a DMA engine) once per batch
+// of newly seen chunks, before it reads any of them.  Tiles are computed identically whatever the order, so the output
 // does not depend on the release order.
 //
 // Every wait is bounded: after the time limit (or an abort request) the
 // waiting workgroup records the error and exits, so the kernel always ends.
 //
 // Workspace words after the common queue block (kWsExtra):
-//   0           ticket counter
+//   0           ticket counter (tickets from gridDim.x on)
 //   1           mask of chunks already appended to the arrival list
 //   2           arrival list length
 //   [3, 3+P)    arrival list (chunk id + 1)
@@ -59,17 +60,39 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
   uint32_t seen = 0;  // chunks whose flag this workgroup has acquired
   Deadline dl{now_ticks(), a.sync.timeout_ticks};
 
+  bool first = true;
   for (;;) {
     __syncthreads();  // keeps the thread-0 claim region apart from the previous iteration
     if (tid == 0) {
       int chunk = -1, tile = -1;
-      const uint32_t tk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // the first gridDim.x tickets go to the workgroups by index (no
+      // atomic: at the start every workgroup would hit the counter at once);
+      // the counter deals the tickets after them
+      const uint32_t tk = first ? blockIdx.x
+                                : gridDim.x + __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+                                                                     __HIP_MEMORY_SCOPE_AGENT);
+      first = false;
       if (tk < total) {
         const uint32_t pos = tk / (uint32_t)tpc;
         dl.start = now_ticks();  // the bound is per wait
         for (;;) {
-          // 1. newly arrived chunks: all flags in one batch of loads, one acquire for
-          //    all of them, and the ones nobody registered yet go on the arrival list
+          // 1. the chunk at this ticket's arrival position, once someone has
+          //    registered it (after seeing its flag): acquired by this
+          //    workgroup before any of its rows is read
+          const uint32_t e = __hip_atomic_load(&arr[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (e != 0) {
+            const int q = (int)e - 1;
+            if (!(seen & (1u << q))) {
+              acquire_system();
+              seen |= 1u << q;
+            }
+            chunk = q;
+            tile = (int)(tk % (uint32_t)tpc);
+            break;
+          }
+          // 2. not registered yet: newly arrived chunks -- all flags in one
+          //    batch of loads, one acquire for all of them, and the ones
+          //    nobody registered yet go on the arrival list
           uint32_t fresh = 0;
           {
             uint32_t fv[kMaxP];
@@ -94,14 +117,7 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
                   __hip_atomic_store(&arr[at++], (uint32_t)q + 1u, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
             }
-          }
-          // 2. the chunk at this ticket's arrival position, once this workgroup has
-          //    acquired it
-          const uint32_t e = __hip_atomic_load(&arr[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (e != 0 && (seen & (1u << (e - 1)))) {
-            chunk = (int)e - 1;
-            tile = (int)(tk % (uint32_t)tpc);
-            break;
+            continue;  // look at the arrival list again
           }
           // 3. not there yet: bounded wait
           if (a.sync.abort_flag && load_flag_system(a.sync.abort_flag) != 0u) {
