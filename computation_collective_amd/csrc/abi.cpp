@@ -324,6 +324,8 @@ hocf_status hocf_embbag_a2a(int T, int64_t R, int D, int B, int L, int P, const 
   if (D > 512) return fail(HOCF_ERR_UNSUPPORTED, "embbag_a2a: D=%d > 512", D);
   if (tile_bags < 1 || tile_bags > 4096)
     return fail(HOCF_ERR_INVALID_ARG, "embbag_a2a: tile_bags=%d outside [1, 4096]", tile_bags);
+  if ((int64_t)tile_bags * T * D * 4 >= (int64_t(1) << 31))
+    return fail(HOCF_ERR_UNSUPPORTED, "embbag_a2a: a tile's window rows (tile_bags*T*D*4 bytes) reach 2 GiB");
   hocf_status st = check_sync(sync, hocf_embbag_a2a_workspace_bytes());
   if (st != HOCF_OK) return st;
   if (T == 0 || B == 0 || D == 0) return ok();

@@ -12,8 +12,9 @@
 // eight rows are kept in flight before they are added -- in index order,
 // from +0.0, so the result is bit-identical to a sequential fp32 sum.  The
 // pooled row is stored straight into destination d's window at
-// [slot][t][:] (512 contiguous bytes); when the item's bags are stored the
-// workgroup releases the (t, j) flag of window d.
+// [slot][t][:] (512 contiguous bytes) with device-coherent stores; when the
+// item's bags are stored (every thread has waited for its own) the
+// workgroup stores the (t, j) flag of window d -- no L2 write-back.
 //
 // Items are dealt from the eight per-XCD ticket queues in table-major order,
 // so each XCD works through its own eighth of the tables and keeps the
@@ -22,6 +23,7 @@
 //
 // An index outside [0, R) is skipped and HOCF_ERR_BAD_INDEX recorded.
 #include "internal.hpp"
+#include "publish.hpp"
 #include "sync.hpp"
 
 namespace hocf {
@@ -49,7 +51,9 @@ __global__ __launch_bounds__(kEmbThreads) void embbag_kernel(EmbbagArgs a) {
     const int d = rem / a.nj, j = rem % a.nj;
     const int s_end = min(a.Bd, (j + 1) * a.tile_bags);
     const float* tab = a.tables + (int64_t)t * R * D;
-    float* wd = a.win_data[d];
+    // the item's rows of window d: slots [j * tile_bags, s_end), table t
+    const __amdgpu_buffer_rsrc_t rw =
+        raw_rsrc(a.win_data[d] + ((int64_t)j * a.tile_bags * T + t) * D);
 
     for (int s = j * a.tile_bags + hw; s < s_end; s += kEmbThreads / 32) {
       const int b = d * a.Bd + s;
@@ -94,11 +98,15 @@ __global__ __launch_bounds__(kEmbThreads) void embbag_kernel(EmbbagArgs a) {
       for (int c = 0; c < CPL; ++c) {
         const int col = (c * 32 + hl) * 4;
         if (col < D)
-          *reinterpret_cast<floatx4*>(wd + ((int64_t)s * T + t) * D + col) = acc[c];
+          st_dev16(rw, (uint32_t)((((int64_t)(s - j * a.tile_bags) * T) * D + col) * 4), 0,
+                   __builtin_bit_cast(u32x4, acc[c]));
       }
     }
+    wait_memory();  // this thread's rows have completed
     __syncthreads();
-    if (tid == 0) release_flag(&a.win_flags[d][(int64_t)t * a.nj + j], a.sync.epoch);
+    if (tid == 0)
+      __hip_atomic_store(&a.win_flags[d][(int64_t)t * a.nj + j], a.sync.epoch, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
   finish_workgroup(a.ws);
 }

@@ -200,7 +200,8 @@ size_t hocf_ag_gemm_workspace_bytes(int P);
  *
  * An index outside [0, R) is skipped (the bag sums its other rows) and
  * HOCF_ERR_BAD_INDEX is recorded in *status.
- * Supported: D a multiple of 4 up to 512; B % P == 0; tile_bags in [1, 4096].
+ * Supported: D a multiple of 4 up to 512; B % P == 0; tile_bags in [1, 4096]
+ *            with tile_bags * T * D * 4 < 2^31 (else HOCF_ERR_UNSUPPORTED).
  * ---------------------------------------------------------------------- */
 hocf_status hocf_embbag_a2a(int T, int64_t R, int D, int B, int L, int P, const float* tables,
                             const int32_t* indices, const int64_t* offsets,
