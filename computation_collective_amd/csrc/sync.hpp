@@ -1,17 +1,14 @@
 // Flag protocol and persistent-workgroup scheduling.
 //
-// Producer side: a workgroup stores a tile, the workgroup meets at a
-// barrier, and one thread stores the epoch into the tile's flag word.  For
-// the stores to be visible from every XCD by then, either they are
-// device-coherent and each thread has waited for its own (publish.hpp), or
-// they are ordinary and the flag store follows an agent-scope release fence
-// (release_flag), which writes this XCD's L2 back.  Consumer side: one
-// thread reads the flag (or an arrival count that is only advanced after
-// the flags it covers) until it equals the epoch, the workgroup meets at a
-// barrier, and the tile is read with device-coherent loads (or after an
-// acquire fence).  Flags written from outside the kernel (by the host or a
-// stream write) are read at system scope and followed by a system-scope
-// acquire before the data they announce is read.
+// Producer side: a workgroup stores a tile with device-coherent stores,
+// every thread waits for its own (publish.hpp), the workgroup meets at a
+// barrier, and one thread stores the epoch into the tile's flag word -- no
+// fence, so no L2 write-back.  Consumer side: one thread reads the flag (or
+// an arrival count that is only advanced after the flags it covers) until
+// it equals the epoch, the workgroup meets at a barrier, and the tile is
+// read with device-coherent loads.  Flags written from outside the kernel
+// (by the host or a stream write) are read at system scope and followed by
+// a system-scope acquire before the data they announce is read.
 //
 // The pages (SC24 abstract; mKernel, section on persistent kernels and
 // tile/chunk overlap) prescribe GPU-initiated, tile-granular publication but
@@ -38,12 +35,6 @@ __device__ __forceinline__ void report_status(const SyncArgs& s, uint32_t code) 
   if (s.status) atomicCAS(s.status, 0u, code);
 }
 
-// Called by one thread after a __syncthreads() that follows the tile stores.
-__device__ __forceinline__ void release_flag(uint32_t* flag, uint32_t epoch) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ uint32_t load_flag_agent(const uint32_t* flag) {
   return __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -52,7 +43,6 @@ __device__ __forceinline__ uint32_t load_flag_system(const uint32_t* flag) {
   return __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void acquire_system() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, ""); }
 
 // Ticket counters live in the caller's workspace:

@@ -49,9 +49,7 @@
  * Flags.  Flag words are uint32 and hold an epoch: a word equals
  * sync->epoch once the data it guards is complete and visible device-wide.
  * The library's producers write guarded data with device-coherent stores
- * and wait for their completion before the flag store (or, for the
- * embedding windows, with ordinary stores and an agent-scope release fence
- * before it); a consumer that sees
+ * and wait for their completion before the flag store; a consumer that sees
  * the epoch (agent-scope atomic load) and then reads the data either with
  * device-coherent loads or after an agent-scope acquire fence sees it all.
  * Each call must use an epoch different from the previous call on the same
