@@ -281,6 +281,10 @@ def main():
                          "unit": R["unit"] if R["bound"] == "mfma" else "GB/s",
                          "frac": round(v / R["peak"], 4), "traffic": None if tb is None else int(tb)},
             "algo_bytes": R["bytes"],
+            # HBM-side rate from the profiled traffic (null until a current profile exists)
+            "dram": None if tb is None else {
+                "bytes": int(tb), "gbps": round(tb / (avg * 1e-3) / 1e9, 1),
+                "frac": round(tb / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
             "config": R["config"],
         }
         log(f"{n}: {v:.1f} {R['unit']} ({avg:.4f} ms average, {100 * v / R['peak']:.1f}% of peak)")
