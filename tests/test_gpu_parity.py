@@ -291,6 +291,19 @@ def test_gemv_ar_integer_bit_exact():
     np.testing.assert_array_equal(bf.to_host(run.part, F32), part)
 
 
+@pytest.mark.parametrize("grid", [1, 7])
+def test_gemv_ar_small_grids_integer_bit_exact(grid, monkeypatch):
+    """Each workgroup takes many column tiles in turn (and is the last
+    producer of some): still bit-exact, workspace left zeroed."""
+    monkeypatch.setenv("HOCF_MAX_WORKGROUPS", str(grid))
+    say(f"gemv_ar grid={grid} P=4 Mb=2 N=1024 K=512")
+    ints = dict(dist_x=("int", -2, 2), dist_w=("int", -2, 2))
+    run, part, win = _gemv(4, 2, 1024, 512, F32, BF16, 128, seed=30 + grid, dist=ints)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, BF16), win)
+    np.testing.assert_array_equal(bf.to_host(run.part, F32), part)
+    assert torch.all(run.ws == 0)
+
+
 # ====================================================================== AG + GEMM
 
 def _ag_inputs(P, Mc, N, K, seed=0):
@@ -336,6 +349,25 @@ def test_ag_gemm_integer_bit_exact():
     sync()
     _, want = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
     np.testing.assert_array_equal(bf.to_host(run.out, BF16), want)
+
+
+@pytest.mark.parametrize("grid", [1, 3])
+def test_ag_gemm_small_grids_integer_bit_exact(grid, monkeypatch):
+    """Fewer workgroups than tiles: every workgroup draws tickets after its
+    first (the counter's range), chunks are registered once; bit-exact."""
+    monkeypatch.setenv("HOCF_MAX_WORKGROUPS", str(grid))
+    P, Mc, N, K = 4, 256, 512, 512
+    say(f"ag_gemm grid={grid} P={P} Mc={Mc} N={N} K={K}")
+    chunks, W, order = gen.ag_gemm_inputs(P, Mc, N, K, seed=60 + grid, dist_a=("int", -2, 2),
+                                          dist_w=("int", -2, 2))
+    run = bf.AgGemm(P, Mc, N, K, BF16, 256, 256, chunks, W)
+    run.poison()
+    run.run_prereleased(order)
+    sync()
+    assert run.status_value() == 0
+    _, want = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
+    np.testing.assert_array_equal(bf.to_host(run.out, BF16), want)
+    assert torch.all(run.ws == 0)
 
 
 def test_ag_gemm_late_delivery():
@@ -443,6 +475,24 @@ def test_embbag_values_bit_exact(D, tile_bags):
     tables = gen.embbag_tables(T, R, D, std=0.01, seed=D)
     idx = gen.zipf_indices(T, B, L, R, seed=D)
     run = bf.EmbbagA2A(T, R, D, B, L, P, tile_bags, tables, idx)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    _emb_check(run, T, R, D, B, L, P, tables, idx)
+    assert torch.all(run.ws == 0)
+
+
+@pytest.mark.parametrize("grid", [1, 6])
+def test_embbag_small_grids_bit_exact(grid, monkeypatch):
+    """Each workgroup pools many tiles of bags (and steals from other
+    queues): every (bag, table) lands once, bit-exact, workspace zeroed."""
+    monkeypatch.setenv("HOCF_MAX_WORKGROUPS", str(grid))
+    T, R, D, B, L, P = 4, 2000, 128, 128, 9, 4
+    say(f"embbag grid={grid} T={T} R={R} D={D} B={B} L={L} P={P}")
+    tables = gen.embbag_tables(T, R, D, std=0.01, seed=70 + grid)
+    idx = gen.zipf_indices(T, B, L, R, seed=70 + grid)
+    run = bf.EmbbagA2A(T, R, D, B, L, P, 8, tables, idx)
     run.poison()
     run.run()
     sync()
