@@ -83,11 +83,16 @@ struct BandRef {
   __device__ __forceinline__ uint32_t my_flag(const GemmRsArgs& a, int tpc) const {
     return (int)threadIdx.x < a.P ? load_flag_agent(&flags[(int64_t)threadIdx.x * tpc]) : a.sync.epoch;
   }
-  // ... and the check, which may come later than the load
-  __device__ __forceinline__ static void verify(const GemmRsArgs& a, uint32_t flag) {
-    if (flag != a.sync.epoch) report_status(a.sync, kErrProtocol);
+  // ... and the check, which may come later than the load (a producer does
+  // not wait for its flag store before counting itself, so a flag read
+  // early is read again, bounded, before it counts as missing)
+  __device__ __forceinline__ void verify(const GemmRsArgs& a, int tpc, uint32_t flag) const {
+    if ((int)threadIdx.x < a.P && !flag_reaches(&flags[(int64_t)threadIdx.x * tpc], flag, a.sync))
+      report_status(a.sync, kErrProtocol);
   }
-  __device__ __forceinline__ void check_flags(const GemmRsArgs& a, int tpc) const { verify(a, my_flag(a, tpc)); }
+  __device__ __forceinline__ void check_flags(const GemmRsArgs& a, int tpc) const {
+    verify(a, tpc, my_flag(a, tpc));
+  }
 };
 
 // Folds band `piece` of completed output tile `g` on its own.
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
                     (typename Band::lds_char*)(band_park));
           Tile::template body_side<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc, side);
           side.flush(b.otile, N, b.row0);
-          BandRef<Tile, SDT, ODT>::verify(a, band_flag);
+          b.verify(a, tpc, band_flag);
         } else {
           Tile::template body<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
         }
@@ -282,9 +287,10 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
       __syncthreads();
       // 2. ready flag; 3. arrival count -> the last producer hands out the bands
       if (tid == 0) {
+        // (the tile's data is complete; readers of the flag re-read it, bounded,
+        // if they get there before the flag store has)
         __hip_atomic_store(&a.win_flags[r][(int64_t)p * tpc + tflag], a.sync.epoch, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-        wait_memory();  // the flag is visible before the count that announces it
         uint32_t* cnt = &grp[(int64_t)r * tpc + tflag];
         const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (prev == (uint32_t)(P - 1)) {

@@ -185,9 +185,10 @@ __global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) 
 
     // ready flag; arrival count -> the last producer of tile j reduces
     if (tid == 0) {
+      // (the partial is complete; the reducer re-reads the flag, bounded, if
+      // it gets there before the flag store has)
       __hip_atomic_store(&a.part_flags[(int64_t)p * a.ntiles + j], a.sync.epoch, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-      wait_memory();  // the flag is visible before the count that announces it
       uint32_t* cnt = &grp[j];
       const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int last = (prev == (uint32_t)(P - 1));
@@ -196,8 +197,10 @@ __global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) 
     }
     __syncthreads();
     if (uniform(s_last)) {
-      if (tid < P && load_flag_agent(&a.part_flags[(int64_t)tid * a.ntiles + j]) != a.sync.epoch)
-        report_status(a.sync, kErrProtocol);
+      if (tid < P) {
+        const uint32_t* f = &a.part_flags[(int64_t)tid * a.ntiles + j];
+        if (!flag_reaches(f, load_flag_agent(f), a.sync)) report_status(a.sync, kErrProtocol);
+      }
       for (int e = tid; e < NQ; e += kGemvThreads) {
         const int qb = e / (TN / 4), qc = (e % (TN / 4)) * 4;
         if (qb >= Mb || qc >= cols_valid) continue;

@@ -166,4 +166,17 @@ struct Deadline {
   __device__ __forceinline__ bool expired() const { return now_ticks() - start > ticks; }
 };
 
+// A flag that must already hold `epoch` (its producer stored it before the
+// arrival count that led here, but without waiting for that store): read
+// again, with a bounded wait, until it does; false if it never does.
+__device__ __forceinline__ bool flag_reaches(const uint32_t* flag, uint32_t seen, const SyncArgs& s) {
+  if (seen == s.epoch) return true;
+  const Deadline dl{now_ticks(), s.timeout_ticks};
+  while (!dl.expired()) {
+    __builtin_amdgcn_s_sleep(2);
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == s.epoch) return true;
+  }
+  return false;
+}
+
 }  // namespace hocf
