@@ -2,12 +2,14 @@
 reader bench.py uses for the HBM traffic figures.
 
   python -m computation_collective_amd.profsum STATS_DIR FETCH_DIR WRITE_DIR OUT_DIR \\
-         "STATS_COMMAND" "COUNTER_COMMAND"
+         "STATS_COMMAND" "COUNTER_COMMAND" [MFMA_DIR "MFMA_COMMAND"]
 
 reads a `rocprofv3 --kernel-trace --stats --output-format csv` run and two
 `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (COUNTER_COMMAND has
-the word COUNTER where the counter name goes) of bench.py, and writes one
-summary per operator, `OUT_DIR/<workload>.txt`:
+the word COUNTER where the counter name goes) of bench.py -- and, if given,
+a run with `--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
+GRBM_GUI_ACTIVE` -- and writes one summary per operator,
+`OUT_DIR/<workload>.txt`:
 
   * the kernel's call count and average / min / max duration;
   * FETCH_SIZE and WRITE_SIZE in KiB per dispatch (median over dispatches),
@@ -15,7 +17,12 @@ summary per operator, `OUT_DIR/<workload>.txt`:
     reads and writes 1 GiB), the factors known/measured they give, and the
     scaled HBM bytes per launch;
   * the hash of the library sources the counters were taken with, and the
-    variant (slot dtype, tile) that was profiled.
+    variant (slot dtype, tile) that was profiled;
+  * with the MFMA run: matrix-core busy cycles summed over all SIMDs,
+    GRBM_GUI_ACTIVE (reported summed over the 8 XCDs, so divided by 8 for
+    one XCD's busy cycles), the MFMA utilisation busy / (XCD cycles *
+    SIMDs), the bf16 MFMA flops the kernel issued (MOPS * 512), and the
+    clock it ran at (XCD cycles / the dispatch's counter window).
 
 `traffic(op, variant)` returns the scaled bytes, or None when there is no
 summary, it was taken for another variant, or the sources have changed.
@@ -79,6 +86,10 @@ def _find_csv(path: str, suffix: str) -> str:
     return hits[0]
 
 
+SIMDS = 256 * 4  # MI355X: 256 CUs of 4 SIMDs
+XCDS = 8
+
+
 def counter_medians(path: str, counter: str) -> dict:
     """op -> median over dispatches of the counter summed over its instances."""
     per = defaultdict(lambda: defaultdict(float))
@@ -91,6 +102,16 @@ def counter_medians(path: str, counter: str) -> dict:
     return {op: statistics.median(d.values()) for op, d in per.items()}
 
 
+def counter_windows_us(path: str, counter: str) -> dict:
+    """op -> median over dispatches of the counter row's own time window."""
+    per = defaultdict(list)
+    for r in csv.DictReader(open(_find_csv(path, "counter_collection.csv"))):
+        op = op_of(r["Kernel_Name"])
+        if r["Counter_Name"] == counter and op:
+            per[op].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {op: statistics.median(v) for op, v in per.items()}
+
+
 def kernel_stats(path: str) -> dict:
     out = {}
     for r in csv.DictReader(open(_find_csv(path, "kernel_stats.csv"))):
@@ -101,10 +122,15 @@ def kernel_stats(path: str) -> dict:
     return out
 
 
-def summarize(stats_dir, fetch_dir, write_dir, out_dir, stats_cmd, counter_cmd) -> None:
+def summarize(stats_dir, fetch_dir, write_dir, out_dir, stats_cmd, counter_cmd, mfma_dir=None,
+              mfma_cmd=None) -> None:
     stats = kernel_stats(stats_dir)
     fetch = counter_medians(fetch_dir, "FETCH_SIZE")
     write = counter_medians(write_dir, "WRITE_SIZE")
+    busy = counter_medians(mfma_dir, "SQ_VALU_MFMA_BUSY_CYCLES") if mfma_dir else {}
+    mops = counter_medians(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16") if mfma_dir else {}
+    active = counter_medians(mfma_dir, "GRBM_GUI_ACTIVE") if mfma_dir else {}
+    window = counter_windows_us(mfma_dir, "GRBM_GUI_ACTIVE") if mfma_dir else {}
     if "copy" not in fetch or "copy" not in write:
         raise SystemExit("the calibration pass is missing from the counter runs")
     ff = COPY_BYTES / 1024.0 / fetch["copy"]
@@ -119,7 +145,10 @@ def summarize(stats_dir, fetch_dir, write_dir, out_dir, stats_cmd, counter_cmd) 
                  f"# kernel statistics: {stats_cmd}",
                  f"# counters (one run per counter): {counter_cmd}",
                  f"# calibration: a 1 GiB negating copy in the same runs reads FETCH_SIZE {fetch['copy']:.0f} KiB"
-                 f" and WRITE_SIZE {write['copy']:.0f} KiB for 1048576 KiB each",
+                 f" and WRITE_SIZE {write['copy']:.0f} KiB for 1048576 KiB each"]
+        if mfma_cmd:
+            lines.append(f"# matrix cores: {mfma_cmd}")
+        lines += [
                  f"kernel {name}",
                  f"variant {variant}",
                  f"sources {src}",
@@ -128,6 +157,12 @@ def summarize(stats_dir, fetch_dir, write_dir, out_dir, stats_cmd, counter_cmd) 
             b = fetch[op] * 1024 * ff + write[op] * 1024 * fw
             lines.append(f"counters fetch_kib={fetch[op]:.0f} write_kib={write[op]:.0f} "
                          f"fetch_factor={ff:.4f} write_factor={fw:.4f} hbm_bytes={b:.0f}")
+        if op in busy and op in active and active[op] > 0:
+            xcd_cycles = active[op] / XCDS
+            util = busy[op] / (xcd_cycles * SIMDS)
+            lines.append(f"mfma busy_cycles={busy[op]:.0f} gui_active_cycles={active[op]:.0f} xcds={XCDS} "
+                         f"simds={SIMDS} util={util:.4f} bf16_flops={mops.get(op, 0) * 512:.0f} "
+                         f"window_us={window[op]:.1f} clock_mhz={xcd_cycles / window[op]:.0f}")
         with open(os.path.join(out_dir, wl + ".txt"), "w") as fh:
             fh.write("\n".join(lines) + "\n")
 
@@ -159,6 +194,6 @@ def traffic(op: str, variant: str | None = None):
 
 
 if __name__ == "__main__":
-    if len(sys.argv) != 7:
+    if len(sys.argv) not in (7, 9):
         raise SystemExit(__doc__)
-    summarize(*sys.argv[1:7])
+    summarize(*sys.argv[1:])
