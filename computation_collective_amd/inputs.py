@@ -51,7 +51,11 @@ def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
 
 
 def _draw(rng, shape, dist, dtype):
-    """Draw one tensor.  dist: ('normal', std) | ('uniform',) | ('int', lo, hi)."""
+    """Draw one tensor.  dist: ('normal', std) | ('uniform',) | ('int', lo, hi)
+    | ('wide', lo, hi): sign * 2**e * (1 + u), e an integer in [lo, hi], u in
+    [0, 1) -- magnitudes spread over many binades | ('selector',): a
+    [..][rows][cols] 0/1 matrix with a single 1 per row, at column row mod
+    cols (drawn from nothing)."""
     kind = dist[0]
     if kind == "normal":
         v = _normal(rng, shape, dist[1])
@@ -59,6 +63,15 @@ def _draw(rng, shape, dist, dtype):
         v = rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
     elif kind == "int":
         v = rng.integers(dist[1], dist[2] + 1, size=shape).astype(np.float32)
+    elif kind == "wide":
+        e = rng.integers(dist[1], dist[2] + 1, size=shape)
+        u = rng.uniform(0.0, 1.0, size=shape)
+        sign = np.where(rng.integers(0, 2, size=shape) == 1, -1.0, 1.0)
+        v = (sign * np.ldexp(1.0 + u, e)).astype(np.float32)
+    elif kind == "selector":
+        rows, cols = shape[-2], shape[-1]
+        v = np.zeros(shape, dtype=np.float32)
+        v[..., np.arange(rows), np.arange(rows) % cols] = 1.0
     else:
         raise ValueError(f"unknown distribution {dist!r}")
     return bf16_encode(v) if dtype == BF16 else v

@@ -215,6 +215,34 @@ def test_gemm_rs_small_grids_integer_bit_exact(grid, monkeypatch):
     np.testing.assert_array_equal(bf.to_host(run.win_data, F32), slots)
 
 
+def _reversed_fold_differs(slots_f32_by_p, out_f32):
+    """The inputs are discriminative: folding the same partials in reverse
+    rank order gives a different fp32 result somewhere."""
+    acc = slots_f32_by_p[-1].astype(np.float32)
+    for q in range(len(slots_f32_by_p) - 2, -1, -1):
+        acc = (acc + slots_f32_by_p[q].astype(np.float32)).astype(np.float32)
+    return bool(np.any(acc != out_f32))
+
+
+@pytest.mark.parametrize("odt", [F32, BF16])
+def test_gemm_rs_reducer_isolation_bit_exact(odt, monkeypatch):
+    """Reducer isolation: A_p selects one row of W_p per output row, so every
+    partial is an exact bf16 value spread over 2^-20 .. 2^21; the fold is
+    then the only rounding, and the GPU's rank-order fp32 fold must equal the
+    oracle's bit for bit (a reversed order would not).  A small grid puts
+    most folds inside the mainloop."""
+    monkeypatch.setenv("HOCF_MAX_WORKGROUPS", "16")
+    P, Mc, N, K = 8, 256, 512, 1280
+    say(f"gemm_rs reducer isolation P={P} Mc={Mc} N={N} K={K} out={odt}")
+    dist = dict(dist_a=("selector",), dist_w=("wide", -20, 20))
+    run, slots, out = _gemm_rs(P, Mc, N, K, BF16, F32, odt, 256, 256, seed=90 + odt, dist=dist)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, F32), slots)
+    np.testing.assert_array_equal(bf.to_host(run.out, odt), out)
+    if odt == F32:
+        # slots [r][p][Mc][N]: fold destination 0's P partials the other way round
+        assert _reversed_fold_differs([slots[0][q] for q in range(P)], out[:Mc])
+
+
 @pytest.mark.parametrize("sdt", [F32, BF16])
 def test_gemm_rs_full_mlpdown(sdt):
     c = cfgs.GEMM_RS_MLP
@@ -302,6 +330,19 @@ def test_gemv_ar_small_grids_integer_bit_exact(grid, monkeypatch):
     np.testing.assert_array_equal(bf.to_host(run.win_data, BF16), win)
     np.testing.assert_array_equal(bf.to_host(run.part, F32), part)
     assert torch.all(run.ws == 0)
+
+
+def test_gemv_ar_reducer_isolation_bit_exact():
+    """x_p selects row b of W_p for output row b: every partial is an exact
+    bf16 value of wide magnitude spread, so the rank-order fp32 fold is the
+    only rounding and must match the oracle bit for bit."""
+    P, Mb, N, K = 8, 4, 2048, 512
+    say(f"gemv_ar reducer isolation P={P} Mb={Mb} N={N} K={K}")
+    dist = dict(dist_x=("selector",), dist_w=("wide", -20, 20))
+    run, part, win = _gemv(P, Mb, N, K, F32, F32, 256, seed=91, dist=dist)
+    np.testing.assert_array_equal(bf.to_host(run.part, F32), part)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, F32), win)
+    assert _reversed_fold_differs([part[q] for q in range(P)], win[0])
 
 
 # ====================================================================== AG + GEMM
