@@ -25,7 +25,7 @@
 // Workspace words after the common queue block (kWsExtra):
 //   0           ticket counter (tickets from gridDim.x on)
 //   1           mask of chunks already appended to the arrival list
-//   2           arrival list length
+//   2           (unused)
 //   [3, 3+P)    arrival list (chunk id + 1)
 //   3 + P       count of finished workgroups (the last one resets all words)
 #include "internal.hpp"
@@ -51,7 +51,6 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
   uint32_t* ws = a.ws + kWsExtra;
   uint32_t* ticket = ws;
   uint32_t* reg_mask = ws + 1;
-  uint32_t* arr_len = ws + 2;
   uint32_t* arr = ws + 3;
   uint32_t* done = ws + 3 + P;
   const uint32_t total = (uint32_t)P * (uint32_t)tpc;
@@ -76,10 +75,16 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
         const uint32_t pos = tk / (uint32_t)tpc;
         dl.start = now_ticks();  // the bound is per wait
         for (;;) {
+          // one batch of loads: the arrival list entry for this ticket and
+          // every flag not yet seen by this workgroup
+          const uint32_t e = __hip_atomic_load(&arr[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          uint32_t fv[kMaxP];
+#pragma unroll
+          for (int q = 0; q < kMaxP; ++q)
+            if (q < P && !(seen & (1u << q))) fv[q] = load_flag_system(&a.chunk_flags[q]);
           // 1. the chunk at this ticket's arrival position, once someone has
           //    registered it (after seeing its flag): acquired by this
           //    workgroup before any of its rows is read
-          const uint32_t e = __hip_atomic_load(&arr[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (e != 0) {
             const int q = (int)e - 1;
             if (!(seen & (1u << q))) {
@@ -90,34 +95,30 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
             tile = (int)(tk % (uint32_t)tpc);
             break;
           }
-          // 2. not registered yet: newly arrived chunks -- all flags in one
-          //    batch of loads, one acquire for all of them, and the ones
-          //    nobody registered yet go on the arrival list
+          // 2. not registered yet: the newly arrived chunks, acquired at once;
+          //    the ones nobody registered yet go on the arrival list.  One
+          //    atomic OR on the registration mask orders registrations: the
+          //    chunks this one adds take the next positions after those
+          //    already registered (popcount of the old mask), in index order.
           uint32_t fresh = 0;
-          {
-            uint32_t fv[kMaxP];
 #pragma unroll
-            for (int q = 0; q < kMaxP; ++q)
-              if (q < P && !(seen & (1u << q))) fv[q] = load_flag_system(&a.chunk_flags[q]);
-#pragma unroll
-            for (int q = 0; q < kMaxP; ++q)
-              if (q < P && !(seen & (1u << q)) && fv[q] == a.sync.epoch) fresh |= 1u << q;
-          }
+          for (int q = 0; q < kMaxP; ++q)
+            if (q < P && !(seen & (1u << q)) && fv[q] == a.sync.epoch) fresh |= 1u << q;
           if (fresh) {
             acquire_system();
             seen |= fresh;
             const uint32_t old = __hip_atomic_fetch_or(reg_mask, fresh, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
             const uint32_t mine = fresh & ~old;
-            if (mine) {
-              uint32_t at = __hip_atomic_fetch_add(arr_len, (uint32_t)__builtin_popcount(mine),
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              for (int q = 0; q < P; ++q)
-                if (mine & (1u << q))
-                  __hip_atomic_store(&arr[at++], (uint32_t)q + 1u, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t at = (uint32_t)__builtin_popcount(old);
+            for (int q = 0; q < P; ++q) {
+              if (!(mine & (1u << q))) continue;
+              __hip_atomic_store(&arr[at], (uint32_t)q + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if (at == pos) { chunk = q; tile = (int)(tk % (uint32_t)tpc); }
+              ++at;
             }
-            continue;  // look at the arrival list again
+            if (chunk >= 0) break;  // this workgroup registered its own ticket's chunk
+            continue;               // look at the arrival list again
           }
           // 3. not there yet: bounded wait
           if (a.sync.abort_flag && load_flag_system(a.sync.abort_flag) != 0u) {
