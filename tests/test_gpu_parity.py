@@ -243,6 +243,17 @@ def test_gemm_rs_reducer_isolation_bit_exact(odt, monkeypatch):
         assert _reversed_fold_differs([slots[0][q] for q in range(P)], out[:Mc])
 
 
+@pytest.mark.parametrize("P,tm", [(16, 256), (12, 128), (9, 256)])
+def test_gemm_rs_many_shards_integer_bit_exact(P, tm):
+    """More than 8 shards (up to the ABI's 16): the reducer's wide-P path."""
+    Mc, N, K = tm, 2 * tm, 256
+    say(f"gemm_rs many shards P={P} Mc={Mc} N={N} K={K} tile={tm}")
+    ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    run, slots, out = _gemm_rs(P, Mc, N, K, BF16, F32, BF16, tm, tm, seed=100 + P, dist=ints)
+    np.testing.assert_array_equal(bf.to_host(run.out, BF16), out)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, F32), slots)
+
+
 @pytest.mark.parametrize("sdt", [F32, BF16])
 def test_gemm_rs_full_mlpdown(sdt):
     c = cfgs.GEMM_RS_MLP
@@ -345,6 +356,15 @@ def test_gemv_ar_reducer_isolation_bit_exact():
     assert _reversed_fold_differs([part[q] for q in range(P)], win[0])
 
 
+@pytest.mark.parametrize("P", [16, 11])
+def test_gemv_ar_many_shards_integer_bit_exact(P):
+    say(f"gemv_ar many shards P={P} Mb=3 N=1024 K=256")
+    ints = dict(dist_x=("int", -2, 2), dist_w=("int", -2, 2))
+    run, part, win = _gemv(P, 3, 1024, 256, F32, BF16, 256, seed=110 + P, dist=ints)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, BF16), win)
+    np.testing.assert_array_equal(bf.to_host(run.part, F32), part)
+
+
 # ====================================================================== AG + GEMM
 
 def _ag_inputs(P, Mc, N, K, seed=0):
@@ -402,6 +422,20 @@ def test_ag_gemm_small_grids_integer_bit_exact(grid, monkeypatch):
     chunks, W, order = gen.ag_gemm_inputs(P, Mc, N, K, seed=60 + grid, dist_a=("int", -2, 2),
                                           dist_w=("int", -2, 2))
     run = bf.AgGemm(P, Mc, N, K, BF16, 256, 256, chunks, W)
+    run.poison()
+    run.run_prereleased(order)
+    sync()
+    assert run.status_value() == 0
+    _, want = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
+    np.testing.assert_array_equal(bf.to_host(run.out, BF16), want)
+    assert torch.all(run.ws == 0)
+
+
+def test_ag_gemm_sixteen_chunks_integer_bit_exact():
+    P, Mc, N, K = 16, 128, 256, 256
+    say(f"ag_gemm P={P} Mc={Mc} N={N} K={K}")
+    chunks, W, order = gen.ag_gemm_inputs(P, Mc, N, K, seed=120, dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    run = bf.AgGemm(P, Mc, N, K, BF16, 128, 128, chunks, W)
     run.poison()
     run.run_prereleased(order)
     sync()
@@ -540,6 +574,19 @@ def test_embbag_small_grids_bit_exact(grid, monkeypatch):
     assert run.status_value() == 0
     _emb_check(run, T, R, D, B, L, P, tables, idx)
     assert torch.all(run.ws == 0)
+
+
+def test_embbag_sixteen_destinations_bit_exact():
+    T, R, D, B, L, P = 3, 4000, 128, 256, 11, 16
+    say(f"embbag P={P} T={T} R={R} D={D} B={B} L={L}")
+    tables = gen.embbag_tables(T, R, D, std=0.01, seed=130)
+    idx = gen.zipf_indices(T, B, L, R, seed=130)
+    run = bf.EmbbagA2A(T, R, D, B, L, P, 8, tables, idx)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    _emb_check(run, T, R, D, B, L, P, tables, idx)
 
 
 def test_embbag_tagged_routing():
