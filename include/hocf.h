@@ -116,9 +116,10 @@ typedef struct hocf_sync {
  * [r*Mc, (r+1)*Mc), Mc = M/P) of every C_p goes to destination r, slot p,
  * and destination r folds its P slots in rank order p = 0..P-1 in fp32,
  * rounding once to out_dt.  Each workgroup that finishes a tile of C_p
- * publishes it into win[r] (slot_dt) and releases its flag; the last of the
- * P producers of an output tile reduces it, while other workgroups still
- * compute.
+ * publishes it into win[r] (slot_dt) and sets its flag; once all P
+ * producers of an output tile have published, the tile's fold (in bands of
+ * rows) is taken up by workgroups of the same kernel, mostly during their
+ * next tile's mainloop, while other workgroups still compute.
  *
  *   A    [P][M][K] in_dt          W  [P][K][N] in_dt
  *   win  host array of P windows; win[r].data = [P src][Mc][N] slot_dt,
@@ -131,6 +132,8 @@ typedef struct hocf_sync {
  *            (BF16, F32 or BF16, BF16 or F32) with tiles 256x256 and 128x128.
  * Requires M % P == 0; N and K multiples of 8 (bf16) or 4 (fp32).  Tiles may
  * be ragged at the end of a chunk, of N and of K.  M, N or K may be 0.
+ * HOCF_ERR_UNSUPPORTED when tile_m * N reaches 2^29 elements (a tile's row
+ * band is addressed with 32-bit byte offsets).
  * ---------------------------------------------------------------------- */
 hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
                          hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
@@ -151,7 +154,7 @@ size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n)
  *         win[q].flags = [NT]: epoch once column tile j of the sum is in window q
  *
  * Supported: in BF16, slot F32 or BF16, out BF16 or F32; 1 <= Mb <= 8;
- * tile_n in {128, 256, 512}; N and K multiples of 8.
+ * tile_n in {128, 256, 512}; N and K multiples of 8; Mb * N below 2^29.
  * ---------------------------------------------------------------------- */
 hocf_status hocf_gemv_ar(int P, int Mb, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
                          hocf_dtype out_dt, const void* x, const void* W, void* part,
