@@ -35,6 +35,7 @@ def _load():
         lib.oracle_gemm_rs.argtypes = [i32] * 7 + [vp] * 4
         lib.oracle_gemm_rs_points.argtypes = [i32] * 7 + [vp, vp, i64, vp, vp, vp, vp]
         lib.oracle_gemv_ar.argtypes = [i32] * 7 + [vp] * 4
+        lib.oracle_gemm_ar.argtypes = [i32] * 7 + [vp] * 4
         lib.oracle_ag_gemm.argtypes = [i32] * 6 + [vp] * 4
         lib.oracle_ag_gemm_points.argtypes = [i32] * 6 + [vp, vp, i64, vp, vp, vp]
         lib.oracle_embbag_a2a.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -100,6 +101,20 @@ def gemm_rs_points(P, M, N, K, in_dt, slot_dt, out_dt, A, W, ms, ns):
     if rc != 0:
         raise ValueError(f"oracle_gemm_rs_points rejected its arguments (rc={rc})")
     return sv, ov
+
+
+def gemm_ar(P, M, N, K, in_dt, slot_dt, out_dt, A, W, want_slots=True):
+    """GEMM + AllReduce.  Returns (slots [P][P][Mc][N] or None, win [P][M][N])."""
+    _check(in_dt, A, W)
+    assert A.shape == (P, M, K) and W.shape == (P, K, N)
+    Mc = M // P
+    slots = np.empty((P, P, Mc, N), dtype=_np_dt(slot_dt)) if want_slots else None
+    win = np.empty((P, M, N), dtype=_np_dt(out_dt))
+    rc = _load().oracle_gemm_ar(P, M, N, K, in_dt, slot_dt, out_dt, _ptr(A), _ptr(W),
+                                _ptr(slots), _ptr(win))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_ar rejected its arguments (rc={rc})")
+    return slots, win
 
 
 def gemv_ar(P, Mb, N, K, in_dt, slot_dt, out_dt, x, W):

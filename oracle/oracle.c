@@ -169,6 +169,64 @@ int oracle_gemm_rs_points(int P, int M, int N, int K, int in_dt, int slot_dt, in
     return 0;
 }
 
+/* ---- GEMM + AllReduce -----------------------------------------------------
+ * The mKernel news item lists GEMM + AllReduce among its five fused kernels
+ * (section on the fused kernels).  A [P][M][K], W [P][K][N].  Shard p
+ * computes C_p = A_p . W_p (M x N), carried in slot_dt.  The AllReduce
+ * leaves the sum of the P partials -- folded in rank order in fp32, rounded
+ * once to out_dt -- in every one of the P receive windows.  It is carried out
+ * in two phases: a ReduceScatter (chunk r of every C_p to destination r,
+ * slot p, folded there) and an AllGather of the reduced chunks, so every
+ * window ends up holding all M rows with the same bits.
+ *   slots: [P dst r][P src p][Mc][N] of slot_dt (may be NULL): C_p chunk r
+ *   win:   [P dst q][M][N] of out_dt: the full reduced result, once per q
+ */
+int oracle_gemm_ar(int P, int M, int N, int K, int in_dt, int slot_dt, int out_dt,
+                   const void* A, const void* W, void* slots, void* win) {
+    if (P <= 0 || M < 0 || N < 0 || K < 0 || M % P != 0) return -1;
+    if (!dt_ok(in_dt) || !dt_ok(slot_dt) || !dt_ok(out_dt)) return -1;
+    const int64_t Mc = M / P;
+    float* C = (float*)malloc(sizeof(float) * (size_t)P * (size_t)M * (size_t)(N > 0 ? N : 1));
+    if (!C) return -1;
+
+    /* 1. per-shard GEMM, fp64, k ascending, carried in slot_dt */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t pm = 0; pm < (int64_t)P * M; ++pm) {
+        const int64_t p = pm / M, m = pm % M;
+        double* acc = (double*)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = load_in(A, in_dt, (p * M + m) * K + k);
+            const int64_t wrow = (p * K + k) * N;
+            for (int64_t n = 0; n < N; ++n) acc[n] += a * load_in(W, in_dt, wrow + n);
+        }
+        for (int64_t n = 0; n < N; ++n) C[(p * M + m) * N + n] = carried(acc[n], slot_dt);
+        free(acc);
+    }
+
+    /* 2. ReduceScatter phase: chunk r of C_p -> destination r, slot p */
+    if (slots) {
+        for (int64_t r = 0; r < P; ++r)
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t i = 0; i < Mc; ++i)
+                    for (int64_t n = 0; n < N; ++n)
+                        store_f32_as(slots, slot_dt, ((r * P + p) * Mc + i) * N + n,
+                                     C[(p * M + r * Mc + i) * N + n]);
+    }
+
+    /* 3. destination r folds its chunk in rank order; 4. AllGather phase:
+     * the reduced chunk r lands at rows r*Mc.. of every window q */
+    for (int64_t r = 0; r < P; ++r)
+        for (int64_t i = 0; i < Mc; ++i)
+            for (int64_t n = 0; n < N; ++n) {
+                const int64_t m = r * Mc + i;
+                float acc = C[(0 * M + m) * N + n];
+                for (int64_t p = 1; p < P; ++p) acc = acc + C[(p * M + m) * N + n];
+                for (int64_t q = 0; q < P; ++q) store_f32_as(win, out_dt, (q * M + m) * N + n, acc);
+            }
+    free(C);
+    return 0;
+}
+
 /* ---- GEMV + AllReduce -----------------------------------------------------
  * x [P][Mb][K], W [P][K][N].  Shard p computes y_p = x_p . W_p (Mb x N),
  * carried in slot_dt; the AllReduce folds y_0..y_{P-1} in rank order in fp32,

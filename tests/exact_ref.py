@@ -82,6 +82,13 @@ def gemm_rs(P, M, N, K, A, W, slot_fmt, out_fmt):
     return slots, out
 
 
+def gemm_ar(P, M, N, K, A, W, slot_fmt, out_fmt):
+    """Returns (slots[r][p][i][n], win[q][m][n]): every window q holds the full
+    rank-order sum (the reduced chunks gathered in destination order)."""
+    slots, out = gemm_rs(P, M, N, K, A, W, slot_fmt, out_fmt)
+    return slots, [[list(out[m]) for m in range(M)] for _ in range(P)]
+
+
 def gemv_ar(P, Mb, N, K, x, W, slot_fmt, out_fmt):
     """Returns (part[p][b][n], win[q][b][n])."""
     part = [[[None] * N for _ in range(Mb)] for _ in range(P)]

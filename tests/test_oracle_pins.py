@@ -63,6 +63,15 @@ def test_gemm_rs_golden(g):
                                       np.asarray(g["slots"], dtype=np.float64))
 
 
+@pytest.mark.parametrize("g", _golden("gemm_ar"))
+def test_gemm_ar_golden(g):
+    A, W = _arr(g["A"], g["in_dt"]), _arr(g["W"], g["in_dt"])
+    slots, win = oracle.gemm_ar(g["P"], g["M"], g["N"], g["K"], g["in_dt"], g["slot_dt"],
+                                g["out_dt"], A, W)
+    np.testing.assert_array_equal(_val(slots, g["slot_dt"]), np.asarray(g["slots"], dtype=np.float64))
+    np.testing.assert_array_equal(_val(win, g["out_dt"]), np.asarray(g["win"], dtype=np.float64))
+
+
 @pytest.mark.parametrize("g", _golden("gemv_ar"))
 def test_gemv_ar_golden(g):
     x, W = _arr(g["x"], g["in_dt"]), _arr(g["W"], g["in_dt"])
@@ -275,6 +284,60 @@ def test_bf16_rounding_matches_torch():
     slots, out = oracle.gemm_rs(1, M, 1, 1, F32, BF16, F32, A, W)
     want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(slots.reshape(-1), want)
+
+
+@pytest.mark.parametrize("P,Mc,N,K", CASES)
+@pytest.mark.parametrize("in_dt,slot_dt,out_dt", [(F32, F32, F32), (BF16, F32, BF16), (BF16, BF16, F32)])
+def test_gemm_ar_bruteforce(P, Mc, N, K, in_dt, slot_dt, out_dt):
+    M = P * Mc
+    seed = 2000 * P + 100 * Mc + 10 * N + K + 7 * in_dt
+    A, W = gen.gemm_rs_inputs(P, M, N, K, in_dt, seed=seed)
+    slots, win = oracle.gemm_ar(P, M, N, K, in_dt, slot_dt, out_dt, A, W)
+    Av, Wv = _val(A, in_dt), _val(W, in_dt)
+    es, ew = ex.gemm_ar(P, M, N, K, Av.tolist(), Wv.tolist(),
+                        ex.BF16 if slot_dt == BF16 else ex.FP32,
+                        ex.BF16 if out_dt == BF16 else ex.FP32)
+    if in_dt == BF16:
+        _exact_check(slots, es, slot_dt)
+        _exact_check(win, ew, out_dt)
+    else:
+        # fp32 inputs: the fp64 dot product may round once before fp32 (<= 1 ulp per partial)
+        _exact_check(slots, es, slot_dt, ulps=1)
+        _exact_check(win, ew, out_dt, ulps=P)
+
+
+@pytest.mark.parametrize("slot_dt,out_dt,tol", [(F32, BF16, 8e-3), (BF16, BF16, 2e-2), (F32, F32, 1e-5)])
+def test_gemm_ar_closed_form_and_replicas(slot_dt, out_dt, tol):
+    """Every window holds hcat_p(A_p) . vcat_p(W_p) (numpy fp64), bit-identical
+    across windows; the slots are the ReduceScatter phase's chunks of each C_p."""
+    P, M, N, K = 4, 24, 40, 56
+    A, W = gen.gemm_rs_inputs(P, M, N, K, BF16, seed=31)
+    slots, win = oracle.gemm_ar(P, M, N, K, BF16, slot_dt, out_dt, A, W)
+    Av, Wv = _val(A, BF16), _val(W, BF16)
+    full = np.concatenate(list(Av), axis=1) @ np.concatenate(list(Wv), axis=0)
+    for q in range(P):
+        np.testing.assert_array_equal(win[q], win[0])
+        assert _normwise(_val(win[q], out_dt), full) <= tol
+    Mc = M // P
+    sv = _val(slots, slot_dt)
+    for r in range(P):
+        for p in range(P):
+            prod = Av[p, r * Mc:(r + 1) * Mc] @ Wv[p]
+            assert _normwise(sv[r, p], prod) <= (8e-3 if slot_dt == BF16 else 1e-6)
+
+
+def test_gemm_ar_integer_inputs_exact():
+    """Integer-valued operands: every partial and sum is an exact integer, so the
+    windows equal the int64 product bit for bit."""
+    P, M, N, K = 3, 12, 16, 24
+    rng = np.random.default_rng(5)
+    Ai = rng.integers(-2, 3, size=(P, M, K))
+    Wi = rng.integers(-2, 3, size=(P, K, N))
+    A, W = _arr(Ai, BF16), _arr(Wi, BF16)
+    _, win = oracle.gemm_ar(P, M, N, K, BF16, F32, F32, A, W)
+    want = sum(Ai[p] @ Wi[p] for p in range(P)).astype(np.float32)
+    for q in range(P):
+        np.testing.assert_array_equal(win[q], want)
 
 
 @pytest.mark.parametrize("slot_dt,out_dt", [(F32, BF16), (BF16, BF16)])
