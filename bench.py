@@ -11,6 +11,8 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
               events: the kernel's span is timed)
   embbag_a2a  64 tables 1e6x128 fp32, batch 16384, 20 rows per bag, Zipf(1.05), P=8
               (a 1 GiB scratch write between calls, outside the timed events)
+  gemm_ar     GEMM+AllReduce, the gemm_rs shapes; the folded chunks land in all 8 windows
+              (last in the step, so its 537 MB of window writes precede only the next step)
 
 Optional extra ops (--ops): embbag_uniform (the same shapes with uniform indices:
 no reuse, a control for the Zipf figure) and copy (a 1 GiB negating copy, the
@@ -47,7 +49,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)  # >= 200 timed calls of each operator
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
-    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a")
+    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a,gemm_ar")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
@@ -201,6 +203,20 @@ def main():
                                   bound="hbm", peak=PEAK_HBM_GBS, bytes=algo_bytes,
                                   config=dict(workload=c.name, T=c.T, R=c.R, D=c.D, B=c.B, L=c.L, P=c.P,
                                               tile_bags=c.tile_bags, zipf_alpha=c.alpha))
+    if "gemm_ar" in ops:
+        c = cfgs.GEMM_AR_MLP
+        log(f"inputs {c.name}")
+        A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, c.in_dt, seed=0)
+        ar = bf.GemmAR(c.P, c.M, c.N, c.K, c.in_dt, sdt, c.out_dt, c.tile_m, c.tile_n, A, W)
+        del A, W
+        algo_bytes = (2 * (c.P * c.M * c.K + c.P * c.K * c.N)            # A, W read
+                      + 2 * (4 if sdt == bf.F32 else 2) * c.P * c.M * c.N  # slots written + read
+                      + 2 * c.P * c.M * c.N)                               # P full windows written
+        runs["gemm_ar"] = dict(call=lambda r=ar: r.run(stream), obj=ar, work=c.flops, unit="TFLOP/s",
+                               variant=f"slot_dtype={args.slot_dtype} tile={c.tile_m}x{c.tile_n}",
+                               bound="mfma", peak=PEAK_BF16_TFLOPS, bytes=algo_bytes,
+                               config=dict(workload=c.name, P=c.P, M=c.M, N=c.N, K=c.K,
+                                           tile=[c.tile_m, c.tile_n], slot_dtype=args.slot_dtype))
     if "embbag_uniform" in ops:
         # control: the same shapes with uniform indices (no reuse), so logical ~ DRAM bytes
         c = cfgs.EMBBAG_DLRM

@@ -93,6 +93,27 @@ class GemmRS(_Common):
         hocf.check(self.call(stream, **kw))
 
 
+class GemmAR(GemmRS):
+    """hocf_gemm_ar: as GemmRS, and every destination q gets the whole reduced
+    result in outs[q] = [M][N] (held together as out_all [P][M][N])."""
+
+    def __init__(self, P, M, N, K, in_dt, slot_dt, out_dt, tile_m, tile_n, A, W, device="cuda"):
+        super().__init__(P, M, N, K, in_dt, slot_dt, out_dt, tile_m, tile_n, A, W, device)
+        del self.out
+        self.out_all = torch.empty((P, M, N), dtype=tdtype(out_dt), device=device)
+        self.outs = hocf.pointers([self.out_all[q] for q in range(P)])
+
+    def poison(self):
+        nan_fill(self.win_data)
+        nan_fill(self.out_all)
+
+    def call(self, stream=None, **kw) -> int:
+        s = self.next_sync(**kw)
+        return hocf.hocf_gemm_ar(self.P, self.M, self.N, self.K, self.in_dt, self.slot_dt,
+                                 self.out_dt, self.A, self.W, self.win, self.outs, self.tile_m,
+                                 self.tile_n, s, stream)
+
+
 class GemvAR(_Common):
     """hocf_gemv_ar: x [P][Mb][K], W [P][K][N] -> part [P][Mb][N], windows [P][Mb][N]."""
 

@@ -98,4 +98,9 @@ AG_GEMM_COL = AgGemm("ag_gemm_colpar_p8_1024x4096x1792_bf16", P=8, Mc=1024, N=17
 EMBBAG_DLRM = EmbbagA2A("embbag_a2a_t64_r1e6_d128_b16384_l20_p8", T=64, R=1_000_000, D=128,
                         B=16384, L=20, P=8, tile_bags=64)
 
+# GEMM+AllReduce at the same row-parallel MLP-down shape: the ReduceScatter's
+# folded chunks are gathered into all 8 destinations' 8192x4096 bf16 windows.
+GEMM_AR_MLP = GemmRS("gemm_ar_mlpdown_p8_8192x4096x1792_bf16", P=8, M=8192, N=4096, K=1792,
+                     in_dt=BF16, slot_dt=F32, out_dt=BF16, tile_m=256, tile_n=256)
+
 ALL = [GEMM_RS_TINY, GEMV_AR_DECODE, GEMM_RS_MLP, AG_GEMM_COL, EMBBAG_DLRM]

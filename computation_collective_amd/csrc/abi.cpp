@@ -175,40 +175,57 @@ size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n)
                   (int64_t)hocf::kNumQueues * P * tpc) * 4;
 }
 
-hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
-                         hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
-                         void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
-  if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: P=%d outside [1, %d]", P, HOCF_MAX_P);
-  if (M < 0 || N < 0 || K < 0) return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: negative dimension");
-  if (M % P) return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: M=%d not divisible by P=%d", M, P);
+// Checks and launch shared by GEMM + ReduceScatter (one output) and GEMM +
+// AllReduce (nout = P outputs, every one receiving all M rows).
+static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, hocf_dtype in_dt,
+                                   hocf_dtype slot_dt, hocf_dtype out_dt, const void* A, const void* W,
+                                   const hocf_window* win, void* const* outs, int nout, bool allreduce,
+                                   int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
+  if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "%s: P=%d outside [1, %d]", op, P, HOCF_MAX_P);
+  if (M < 0 || N < 0 || K < 0) return fail(HOCF_ERR_INVALID_ARG, "%s: negative dimension", op);
+  if (M % P) return fail(HOCF_ERR_INVALID_ARG, "%s: M=%d not divisible by P=%d", op, M, P);
   if (!dt_ok(in_dt) || !dt_ok(slot_dt) || !dt_ok(out_dt))
-    return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: unknown dtype");
+    return fail(HOCF_ERR_INVALID_ARG, "%s: unknown dtype", op);
   const int vec = in_dt == HOCF_BF16 ? 8 : 4;
   if (N % vec || K % vec)
-    return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: N=%d and K=%d must be multiples of %d", N, K, vec);
+    return fail(HOCF_ERR_INVALID_ARG, "%s: N=%d and K=%d must be multiples of %d", op, N, K, vec);
   bool tile_ok;
   if (in_dt == HOCF_BF16) tile_ok = (tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128);
   else tile_ok = (tile_m == 64 && tile_n == 64) && slot_dt == HOCF_F32 && out_dt == HOCF_F32;
   if (!tile_ok)
-    return fail(HOCF_ERR_UNSUPPORTED, "gemm_rs: no kernel for in=%d slot=%d out=%d tile %dx%d",
+    return fail(HOCF_ERR_UNSUPPORTED, "%s: no kernel for in=%d slot=%d out=%d tile %dx%d", op,
                 in_dt, slot_dt, out_dt, tile_m, tile_n);
   // published tiles are addressed with 32-bit byte offsets from their origin
   if ((int64_t)tile_m * N * 4 >= ((int64_t)1 << 31))
-    return fail(HOCF_ERR_UNSUPPORTED, "gemm_rs: tile_m * N = %lld elements per tile row band exceeds 2^29",
+    return fail(HOCF_ERR_UNSUPPORTED, "%s: tile_m * N = %lld elements per tile row band exceeds 2^29", op,
                 (long long)tile_m * N);
   const size_t need = hocf_gemm_rs_workspace_bytes(P, M, N, tile_m, tile_n);
   hocf_status st = check_sync(sync, need);
   if (st != HOCF_OK) return st;
   if (M == 0 || N == 0) return ok();
-  if (!A || !W || !out) return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: NULL tensor");
-  if ((K && (!aligned16(A) || !aligned16(W))) || !aligned16(out))
-    return fail(HOCF_ERR_INVALID_ARG, "gemm_rs: tensors must be 16-byte aligned");
-  if ((st = check_windows(win, P, "gemm_rs")) != HOCF_OK) return st;
+  if (!A || !W || !outs) return fail(HOCF_ERR_INVALID_ARG, "%s: NULL tensor", op);
+  if (K && (!aligned16(A) || !aligned16(W)))
+    return fail(HOCF_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", op);
+  const int64_t out_bytes = (int64_t)M * N * (out_dt == HOCF_BF16 ? 2 : 4);
+  for (int q = 0; q < nout; ++q) {
+    if (!outs[q]) return fail(HOCF_ERR_INVALID_ARG, "%s: NULL output %d", op, q);
+    if (!aligned16(outs[q])) return fail(HOCF_ERR_INVALID_ARG, "%s: output %d not 16-byte aligned", op, q);
+    for (int d = 0; d < q; ++d) {
+      const char* x = static_cast<const char*>(outs[q]);
+      const char* y = static_cast<const char*>(outs[d]);
+      if (x < y + out_bytes && y < x + out_bytes)
+        return fail(HOCF_ERR_INVALID_ARG, "%s: outputs %d and %d overlap", op, d, q);
+    }
+  }
+  if ((st = check_windows(win, P, op)) != HOCF_OK) return st;
 
   hocf::SyncArgs sa;
   if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
   hocf::GemmRsArgs a{};
-  a.A = A; a.W = W; a.out = out;
+  a.A = A; a.W = W;
+  for (int q = 0; q < nout; ++q) a.outs[q] = outs[q];
+  a.nout = nout;
+  a.allreduce = allreduce;
   for (int r = 0; r < P; ++r) { a.win_data[r] = win[r].data; a.win_flags[r] = win[r].flags; }
   a.ws = static_cast<uint32_t*>(sync->workspace);
   a.P = P; a.M = M; a.N = N; a.K = K; a.Mc = M / P;
@@ -217,8 +234,28 @@ hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtyp
   a.ntiles = (int)cdiv(N, tile_n);
   a.total = (int64_t)P * P * a.mtiles * a.ntiles;
   a.sync = sa;
-  return launched(hocf::launch_gemm_rs(a, tile_m, tile_n, in_dt, static_cast<hipStream_t>(stream)),
-                  "gemm_rs");
+  return launched(hocf::launch_gemm_rs(a, tile_m, tile_n, in_dt, static_cast<hipStream_t>(stream)), op);
+}
+
+hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                         hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
+                         void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
+  void* const outs[1] = {out};
+  return gemm_collective("gemm_rs", P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, 1, false, tile_m, tile_n,
+                         sync, stream);
+}
+
+/* ------------------------------------------------------------ GEMM + AR */
+
+size_t hocf_gemm_ar_workspace_bytes(int P, int M, int N, int tile_m, int tile_n) {
+  return hocf_gemm_rs_workspace_bytes(P, M, N, tile_m, tile_n);
+}
+
+hocf_status hocf_gemm_ar(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                         hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
+                         void* const* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
+  return gemm_collective("gemm_ar", P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, out, P, true, tile_m, tile_n,
+                         sync, stream);
 }
 
 /* ------------------------------------------------------------ GEMV + AR */

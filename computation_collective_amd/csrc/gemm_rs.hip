@@ -58,7 +58,7 @@ template <class Tile, int SDT, int ODT>
 struct BandRef {
   const char* slot0;
   int64_t slot_bytes;
-  char* otile;
+  int64_t otile_off;  // byte offset of the band's output tile in every output
   int row0, rows_valid, cols_valid;
   const uint32_t* flags;  // flag of contribution q at flags[q * tiles per chunk]
 
@@ -75,7 +75,7 @@ struct BandRef {
     const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
     slot0 = reinterpret_cast<const char*>(a.win_data[r]) + tile_off * SES;
     slot_bytes = (int64_t)Mc * N * SES;
-    otile = reinterpret_cast<char*>(a.out) + ((int64_t)r * Mc * N + tile_off) * (ODT == kBF16 ? 2 : 4);
+    otile_off = ((int64_t)r * Mc * N + tile_off) * (ODT == kBF16 ? 2 : 4);
     flags = &a.win_flags[r][tflag];
   }
   // the P contributions' flags must all carry this call's epoch (one thread
@@ -93,28 +93,34 @@ struct BandRef {
   __device__ __forceinline__ void check_flags(const GemmRsArgs& a, int tpc) const {
     verify(a, tpc, my_flag(a, tpc));
   }
+  // the outputs the band goes to: the first `n` of a.outs
+  __device__ __forceinline__ OutSet outs(const GemmRsArgs& a, int n) const { return OutSet{a.outs, n, otile_off}; }
 };
 
-// Folds band `piece` of completed output tile `g` on its own.
+// Folds band `piece` of completed output tile `g` on its own, into the
+// first `nout` outputs.
 template <class Tile, bool RAGGED, int SDT, int ODT>
-__device__ __forceinline__ void reduce_band(const GemmRsArgs& a, int64_t g, int piece) {
+__device__ __forceinline__ void reduce_band(const GemmRsArgs& a, int64_t g, int piece, int nout) {
   const BandRef<Tile, SDT, ODT> b(a, g, piece);
   if (RAGGED && b.row0 >= b.rows_valid) return;
   b.check_flags(a, a.mtiles * a.ntiles);
   const int P = a.P, N = a.N;
   if (P <= 4)
-    reduce_piece<Tile, SDT, ODT, RAGGED, 4, 8>(b.slot0, b.slot_bytes, P, N, b.otile, N, b.row0, b.rows_valid,
+    reduce_piece<Tile, SDT, ODT, RAGGED, 4, 8>(b.slot0, b.slot_bytes, P, N, b.outs(a, nout), N, b.row0, b.rows_valid,
                                                b.cols_valid);
   else if (P <= 8)
-    reduce_piece<Tile, SDT, ODT, RAGGED, 8, 4>(b.slot0, b.slot_bytes, P, N, b.otile, N, b.row0, b.rows_valid,
+    reduce_piece<Tile, SDT, ODT, RAGGED, 8, 4>(b.slot0, b.slot_bytes, P, N, b.outs(a, nout), N, b.row0, b.rows_valid,
                                                b.cols_valid);
   else
-    reduce_piece<Tile, SDT, ODT, RAGGED, kMaxP, 2>(b.slot0, b.slot_bytes, P, N, b.otile, N, b.row0,
+    reduce_piece<Tile, SDT, ODT, RAGGED, kMaxP, 2>(b.slot0, b.slot_bytes, P, N, b.outs(a, nout), N, b.row0,
                                                    b.rows_valid, b.cols_valid);
 }
 
-template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
-__global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
+// The kernel body shared by GEMM + ReduceScatter (AR = false: each folded
+// band goes to the one output) and GEMM + AllReduce (AR = true: each folded
+// band goes to all a.nout destination windows).
+template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT, bool AR>
+__device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
   using Elem = typename std::conditional<BF16IN, uint16_t, float>::type;
   constexpr int S = ReduceLayout<Tile, SDT>::PIECES;
   // tiles with a split mainloop start the next tile's loads before the band
@@ -136,6 +142,7 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
 
   const int tid = threadIdx.x;
   const int P = a.P, N = a.N, K = a.K, Mc = a.Mc;
+  const int nout = AR ? a.nout : 1;
   const int tpc = a.mtiles * a.ntiles;
   const int64_t ngroups = (int64_t)P * tpc;
   // workspace after the queue block: arrival counters [P][tpc], band queue
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
     if (item >= 0) {
       if constexpr (kSplit) Tile::prologue(At, K, Wt, N, K, stages);
     }
-    if (state == 1 && !band_in_loop) reduce_band<Tile, RAGGED, SDT, ODT>(a, band / S, band % S);
+    if (state == 1 && !band_in_loop) reduce_band<Tile, RAGGED, SDT, ODT>(a, band / S, band % S, nout);
 
     if (item >= 0) {
       const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
@@ -264,7 +271,7 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
           side.init(b.slot0, (uint32_t)b.slot_bytes, P, N, b.row0,
                     (typename Band::lds_char*)(band_park));
           Tile::template body_side<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc, side);
-          side.flush(b.otile, N, b.row0);
+          side.flush(b.outs(a, nout), N, b.row0);
           b.verify(a, tpc, band_flag);
         } else {
           Tile::template body<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
@@ -311,8 +318,19 @@ __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
 }
 
 template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
+__global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
+  gemm_collective<Tile, RAGGED, BF16IN, SDT, ODT, false>(a);
+}
+
+template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
+__global__ __launch_bounds__(Tile::NT) void gemm_ar_kernel(GemmRsArgs a) {
+  gemm_collective<Tile, RAGGED, BF16IN, SDT, ODT, true>(a);
+}
+
+template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
 static hipError_t launch_one(const GemmRsArgs& a, hipStream_t s) {
-  auto kern = &gemm_rs_kernel<Tile, RAGGED, BF16IN, SDT, ODT>;
+  auto kern = a.allreduce ? &gemm_ar_kernel<Tile, RAGGED, BF16IN, SDT, ODT>
+                          : &gemm_rs_kernel<Tile, RAGGED, BF16IN, SDT, ODT>;
   int grid = 0;
   hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), Tile::NT, a.total, &grid);
   if (e != hipSuccess) return e;

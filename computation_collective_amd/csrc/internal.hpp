@@ -12,7 +12,11 @@ namespace hocf {
 struct GemmRsArgs {
   const void* A;
   const void* W;
-  void* out;
+  // the reduced chunks go to every one of outs[0 .. nout): one output
+  // [M][N] for a ReduceScatter, the P receive windows for an AllReduce
+  void* outs[kMaxP];
+  int nout;
+  bool allreduce;  // GEMM + AllReduce (nout == P) rather than ReduceScatter (nout == 1)
   void* win_data[kMaxP];
   uint32_t* win_flags[kMaxP];
   uint32_t* ws;

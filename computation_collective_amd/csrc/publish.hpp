@@ -169,6 +169,17 @@ __device__ __forceinline__ void publish_tile(char* dst, int64_t ld, int rows_val
   store_tile<Tile, DT, RAGGED, kPolicyDevice, true>(dst, ld, rows_valid, cols_valid, acc, stages);
 }
 
+// Where a reduced band goes: the same bytes at byte offset `off` from each
+// of the `n` output bases -- one for a ReduceScatter (the destination's
+// chunk), all P receive windows for an AllReduce.  `base` points at the
+// kernel's argument array, so the addresses are wave-uniform.
+struct OutSet {
+  void* const* base;
+  int n;
+  int64_t off;
+  __device__ __forceinline__ char* at(int d) const { return reinterpret_cast<char*>(base[d]) + off; }
+};
+
 // Geometry of the fixed-order reduction of one Tile with slot type SDT:
 // 16-byte chunks, CPR per tile row, RPS rows per pass of the workgroup, and
 // the pieces a tile's reduction is cut into (at least 32 rows or one pass).
@@ -194,7 +205,7 @@ struct ReduceLayout {
 // are in flight together.  Requires P <= PMAX and TM * ld * ES(SDT) < 2^31.
 template <class Tile, int SDT, int ODT, bool RAGGED, int PMAX, int U>
 __device__ __forceinline__ void reduce_piece(const char* slot0, int64_t slot_bytes, int P, int64_t ld,
-                                             void* out, int64_t ld_out, int row0, int rows_valid,
+                                             const OutSet& outs, int64_t ld_out, int row0, int rows_valid,
                                              int cols_valid) {
   using L = ReduceLayout<Tile, SDT>;
   constexpr int SES = L::SES, CE = L::CE, CPR = L::CPR, RPS = L::RPS;
@@ -204,7 +215,7 @@ __device__ __forceinline__ void reduce_piece(const char* slot0, int64_t slot_byt
   const int tid = (int)(threadIdx.x & ~63) + opaque_lane();
   const int r0 = row0 + tid / CPR, col = (tid % CPR) * CE;
   const uint32_t voff = (uint32_t)(((int64_t)r0 * ld + col) * SES);
-  char* obase = reinterpret_cast<char*>(out) + ((int64_t)r0 * ld_out + col) * (ODT == kBF16 ? 2 : 4);
+  const int64_t orel = ((int64_t)r0 * ld_out + col) * (ODT == kBF16 ? 2 : 4);
   for (int ps = 0; ps < NPASS; ps += UE) {
     u32x4 v[UE][PMAX];
 #pragma unroll
@@ -228,13 +239,13 @@ __device__ __forceinline__ void reduce_piece(const char* slot0, int64_t slot_byt
     for (int u = 0; u < UE; ++u) {
       const int row = (ps + u) * RPS + r0;
       if (RAGGED && (row >= rows_valid || col >= cols_valid)) continue;
-      char* o = obase + (int64_t)(ps + u) * RPS * ld_out * (ODT == kBF16 ? 2 : 4);
+      const int64_t o = orel + (int64_t)(ps + u) * RPS * ld_out * (ODT == kBF16 ? 2 : 4);
       if constexpr (SDT == kF32) {
         floatx4 s = __builtin_bit_cast(floatx4, v[u][0]);
 #pragma unroll
         for (int q = 1; q < PMAX; ++q)
           if (q < P) s = s + __builtin_bit_cast(floatx4, v[u][q]);
-        st4<ODT>(o, 0, s);
+        for (int d = 0; d < outs.n; ++d) st4<ODT>(outs.at(d) + o, 0, s);
       } else {
         floatx4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -247,8 +258,10 @@ __device__ __forceinline__ void reduce_piece(const char* slot0, int64_t slot_byt
           if (q == 0) { lo = a; hi = b; }
           else if (q < P) { lo = lo + a; hi = hi + b; }
         }
-        st4<ODT>(o, 0, lo);
-        st4<ODT>(o, 4, hi);
+        for (int d = 0; d < outs.n; ++d) {
+          st4<ODT>(outs.at(d) + o, 0, lo);
+          st4<ODT>(outs.at(d) + o, 4, hi);
+        }
       }
     }
   }
@@ -332,22 +345,27 @@ struct BandFold {
       }
     }
   }
-  // the parked rows -> out (the band's output tile origin, leading dimension ld_out)
-  __device__ __forceinline__ void flush(void* out, int64_t ld_out, int row0) {
+  // the parked rows -> every output of `outs` (the band's output tile
+  // origins, leading dimension ld_out)
+  __device__ __forceinline__ void flush(const OutSet& outs, int64_t ld_out, int row0) {
     const int tid = (int)(threadIdx.x & ~63) + opaque_lane();
     const int r0 = row0 + tid / L::CPR, col = (tid % L::CPR) * L::CE;
-    char* obase = reinterpret_cast<char*>(out) + ((int64_t)r0 * ld_out + col) * OES;
+    const int64_t orel = ((int64_t)r0 * ld_out + col) * OES;
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
       const lds_char* src = park + pass * (Tile::NT * OUT_BYTES);
-      char* dst = obase + (int64_t)pass * L::RPS * ld_out * OES;
+      const int64_t o = orel + (int64_t)pass * L::RPS * ld_out * OES;
       if constexpr (OUT_BYTES == 8) {
-        *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(src);
+        const u32x2 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(src);
+        for (int d = 0; d < outs.n; ++d) *reinterpret_cast<u32x2*>(outs.at(d) + o) = w;
       } else {
+        u32x4 w[OUT_BYTES / 16];
 #pragma unroll
-        for (int b = 0; b < OUT_BYTES; b += 16)
-          *reinterpret_cast<u32x4*>(dst + b) =
-              *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(src + b);
+        for (int b = 0; b < OUT_BYTES / 16; ++b)
+          w[b] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(src + 16 * b);
+        for (int d = 0; d < outs.n; ++d)
+#pragma unroll
+          for (int b = 0; b < OUT_BYTES / 16; ++b) *reinterpret_cast<u32x4*>(outs.at(d) + o + 16 * b) = w[b];
       }
     }
   }

@@ -30,6 +30,7 @@ HOCF_MAX_P = 16
 
 EXPORTED = [
     "hocf_gemm_rs", "hocf_gemm_rs_workspace_bytes",
+    "hocf_gemm_ar", "hocf_gemm_ar_workspace_bytes",
     "hocf_gemv_ar", "hocf_gemv_ar_workspace_bytes",
     "hocf_ag_gemm", "hocf_ag_gemm_workspace_bytes",
     "hocf_embbag_a2a", "hocf_embbag_a2a_workspace_bytes",
@@ -69,15 +70,17 @@ def lib():
         S = ctypes.POINTER(hocf_sync)
         L.hocf_gemm_rs.argtypes = [i, i, i, i, i, i, i, vp, vp, W, vp, i, i, S, vp]
         L.hocf_gemm_rs_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.hocf_gemm_ar.argtypes = [i, i, i, i, i, i, i, vp, vp, W, ctypes.POINTER(vp), i, i, S, vp]
+        L.hocf_gemm_ar_workspace_bytes.argtypes = [i, i, i, i, i]
         L.hocf_gemv_ar.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, W, i, S, vp]
         L.hocf_gemv_ar_workspace_bytes.argtypes = [i, i, i]
         L.hocf_ag_gemm.argtypes = [i, i, i, i, i, i, vp, vp, vp, vp, i, i, S, vp]
         L.hocf_ag_gemm_workspace_bytes.argtypes = [i]
         L.hocf_embbag_a2a.argtypes = [i, i64, i, i, i, i, vp, vp, vp, W, i, S, vp]
         L.hocf_embbag_a2a_workspace_bytes.argtypes = []
-        for f in ("hocf_gemm_rs", "hocf_gemv_ar", "hocf_ag_gemm", "hocf_embbag_a2a"):
+        for f in ("hocf_gemm_rs", "hocf_gemm_ar", "hocf_gemv_ar", "hocf_ag_gemm", "hocf_embbag_a2a"):
             getattr(L, f).restype = i
-        for f in ("hocf_gemm_rs_workspace_bytes", "hocf_gemv_ar_workspace_bytes",
+        for f in ("hocf_gemm_rs_workspace_bytes", "hocf_gemm_ar_workspace_bytes", "hocf_gemv_ar_workspace_bytes",
                   "hocf_ag_gemm_workspace_bytes", "hocf_embbag_a2a_workspace_bytes"):
             getattr(L, f).restype = sz
         L.hocf_status_string.argtypes = [i]
@@ -115,6 +118,13 @@ def windows(pairs) -> ctypes.Array:
     return arr
 
 
+def pointers(xs) -> ctypes.Array | None:
+    """Host array of device pointers from [tensor or int, ...] (None passes through)."""
+    if xs is None:
+        return None
+    return (ctypes.c_void_p * len(xs))(*[ptr(x) for x in xs])
+
+
 def sync(epoch, workspace, workspace_bytes, status=None, abort_flag=None, spin_timeout_ns=0):
     s = hocf_sync()
     s.epoch = epoch
@@ -147,6 +157,10 @@ def hocf_gemm_rs_workspace_bytes(P, M, N, tile_m, tile_n) -> int:
     return lib().hocf_gemm_rs_workspace_bytes(P, M, N, tile_m, tile_n)
 
 
+def hocf_gemm_ar_workspace_bytes(P, M, N, tile_m, tile_n) -> int:
+    return lib().hocf_gemm_ar_workspace_bytes(P, M, N, tile_m, tile_n)
+
+
 def hocf_gemv_ar_workspace_bytes(P, N, tile_n) -> int:
     return lib().hocf_gemv_ar_workspace_bytes(P, N, tile_n)
 
@@ -162,6 +176,14 @@ def hocf_embbag_a2a_workspace_bytes() -> int:
 def hocf_gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, out, tile_m, tile_n, sync_,
                  stream=None) -> int:
     return lib().hocf_gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, ptr(A), ptr(W), win, ptr(out),
+                              tile_m, tile_n, ctypes.byref(sync_), _stream(stream))
+
+
+def hocf_gemm_ar(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, tile_m, tile_n, sync_,
+                 stream=None) -> int:
+    """outs: P device buffers (or a host pointer array from pointers())."""
+    arr = outs if outs is None or isinstance(outs, ctypes.Array) else pointers(outs)
+    return lib().hocf_gemm_ar(P, M, N, K, in_dt, slot_dt, out_dt, ptr(A), ptr(W), win, arr,
                               tile_m, tile_n, ctypes.byref(sync_), _stream(stream))
 
 

@@ -44,7 +44,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30  # the calibration pass reads and writes 1 GiB
 
 # kernel-name fragment -> operator name used by bench.py
-KERNELS = [("gemm_rs_kernel", "gemm_rs"), ("gemv_ar_kernel", "gemv_ar"),
+KERNELS = [("gemm_rs_kernel", "gemm_rs"), ("gemm_ar_kernel", "gemm_ar"), ("gemv_ar_kernel", "gemv_ar"),
            ("ag_gemm_kernel", "ag_gemm"), ("embbag_kernel", "embbag_a2a"),
            ("neg_kernel", "copy")]
 
@@ -54,6 +54,7 @@ def workloads():
     from . import configs as c
     return {
         "gemm_rs": (c.GEMM_RS_MLP.name, f"slot_dtype=f32 tile={c.GEMM_RS_MLP.tile_m}x{c.GEMM_RS_MLP.tile_n}"),
+        "gemm_ar": (c.GEMM_AR_MLP.name, f"slot_dtype=f32 tile={c.GEMM_AR_MLP.tile_m}x{c.GEMM_AR_MLP.tile_n}"),
         "gemv_ar": (c.GEMV_AR_DECODE.name, f"tile_n={c.GEMV_AR_DECODE.tile_n} weight_replicas=4"),
         "ag_gemm": (c.AG_GEMM_COL.name, f"tile={c.AG_GEMM_COL.tile_m}x{c.AG_GEMM_COL.tile_n} prereleased"),
         "embbag_a2a": (c.EMBBAG_DLRM.name, f"tile_bags={c.EMBBAG_DLRM.tile_bags}"),

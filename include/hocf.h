@@ -1,13 +1,14 @@
 /*
  * hocf — computations fused with their collective epilogue, on one MI355X.
  *
- * C ABI of libhocf.so.  Four operators, each one GPU's share of a P-way
+ * C ABI of libhocf.so.  Five operators, each one GPU's share of a P-way
  * tensor-parallel (or model-parallel) step with the P logical shards'
  * receive windows in local HBM:
  *
  *   hocf_gemm_rs     GEMM + ReduceScatter   (mKernel news item "GPU-vezérelt
  *                    kommunikációval gyorsítják az AI-betanítást a kutatók",
  *                    section on its five fused kernels)
+ *   hocf_gemm_ar     GEMM + AllReduce       (mKernel news item, same section)
  *   hocf_gemv_ar     GEMV + AllReduce       ("Optimizing Distributed ML
  *                    Communication with Fused Computation-Collective
  *                    Operations", SC24, abstract)
@@ -139,6 +140,35 @@ hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtyp
                          hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
                          void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream);
 size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n);
+
+/* ------------------------------------------------------------------------
+ * GEMM + AllReduce.
+ *
+ * The mKernel news item ("GPU-vezérelt kommunikációval gyorsítják az
+ * AI-betanítást a kutatók", section on the five fused kernels) lists GEMM +
+ * AllReduce among its fused kernels.  Same computation and ReduceScatter
+ * phase as hocf_gemm_rs -- C_p = A_p . W_p for every shard p, chunk r of
+ * every C_p published into win[r], slot p, with its tile flags, and folded
+ * there in rank order p = 0..P-1 in fp32 by workgroups of the same kernel
+ * while others still compute -- and then each folded band is stored into
+ * every one of the P output windows (the AllGather phase), so every
+ * destination holds the whole sum, the same bits in all P.
+ *
+ *   A, W, win      as for hocf_gemm_rs
+ *   out            host array of P device pointers; out[q] = [M][N] out_dt,
+ *                  destination q's copy of the full result (rows r*Mc.. are
+ *                  the fold of chunk r); the P ranges must not overlap
+ *
+ * Supported combinations, limits and errors as for hocf_gemm_rs; the
+ * workspace is the same size (hocf_gemm_ar_workspace_bytes).  The outputs
+ * carry no flags: they are complete when the stream reaches the end of the
+ * call.  The library keeps no pointer from `out` after the call returns (the
+ * P pointers are copied into the launch's arguments).
+ * ---------------------------------------------------------------------- */
+hocf_status hocf_gemm_ar(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                         hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
+                         void* const* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream);
+size_t hocf_gemm_ar_workspace_bytes(int P, int M, int N, int tile_m, int tile_n);
 
 /* ------------------------------------------------------------------------
  * GEMV + AllReduce.

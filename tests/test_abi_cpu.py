@@ -88,6 +88,34 @@ def test_workspace_queries():
     assert hocf.hocf_gemm_rs_workspace_bytes(3, 256, 256, 64, 64) == 0   # M % P != 0
 
 
+def gemm_ar(P=4, M=256, N=256, K=256, dts=(F32, F32, F32), tile=(64, 64), outs="ok"):
+    if outs == "ok":
+        outs = [FAKE + q * M * N * 4 for q in range(P)]
+    return hocf.hocf_gemm_ar(P, M, N, K, *dts, FAKE, FAKE, _win(P), outs, *tile, _sync())
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(P=0), INVALID), (dict(M=254), INVALID), (dict(tile=(128, 64)), UNSUPPORTED),
+    (dict(outs=None), INVALID),
+    (dict(outs=[FAKE, 0, FAKE + 2 * 262144, FAKE + 3 * 262144]), INVALID),        # NULL output
+    (dict(outs=[FAKE, FAKE + 262144 + 8, FAKE + 2 * 262144 + 16, FAKE + 4 * 262144]), INVALID),  # misaligned
+    (dict(outs=[FAKE, FAKE + 262144 - 16, FAKE + 2 * 262144, FAKE + 3 * 262144]), INVALID),  # overlap
+])
+def test_gemm_ar_rejects(kw, expect):
+    assert gemm_ar(**kw) == expect
+    assert hocf.last_error()
+
+
+def test_gemm_ar_valid_reaches_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    assert gemm_ar() == HIP
+    assert gemm_ar(M=0, outs=None) == hocf.HOCF_OK
+    assert hocf.hocf_gemm_ar_workspace_bytes(8, 8192, 4096, 256, 256) == \
+        hocf.hocf_gemm_rs_workspace_bytes(8, 8192, 4096, 256, 256)
+
+
 @pytest.mark.parametrize("kw,expect", [
     (dict(P=0), INVALID), (dict(Mb=9), UNSUPPORTED), (dict(tile_n=64), UNSUPPORTED),
     (dict(N=8190), INVALID), (dict(in_dt=F32), UNSUPPORTED), (dict(part=0), INVALID),

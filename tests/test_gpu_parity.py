@@ -282,6 +282,110 @@ def test_gemm_rs_full_mlpdown(sdt):
     assert relerr(val(gs, sdt), val(sv, sdt)) <= TOL[BF16]
 
 
+# ====================================================================== GEMM + AR
+
+def _gemm_ar(P, Mc, N, K, in_dt, slot_dt, out_dt, tm, tn, seed=0, dist=None):
+    M = P * Mc
+    if dist is None:
+        dist = dict(dist_a=("normal", 1.0), dist_w=("normal", 0.02)) if in_dt == BF16 else \
+            dict(dist_a=("uniform",), dist_w=("uniform",))
+    A, W = gen.gemm_rs_inputs(P, M, N, K, in_dt, seed=seed, **dist)
+    run = bf.GemmAR(P, M, N, K, in_dt, slot_dt, out_dt, tm, tn, A, W)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    slots, win = oracle.gemm_ar(P, M, N, K, in_dt, slot_dt, out_dt, A, W)
+    return run, slots, win
+
+
+def _replicas_identical(run):
+    """AllReduce: every destination's window holds the same bits."""
+    for q in range(1, run.P):
+        assert torch.equal(run.out_all[q], run.out_all[0]), f"window {q} differs from window 0"
+
+
+GEMM_AR_CASES = [
+    (4, 64, 256, 256, F32, F32, F32, 64, 64),        # the tiny workload's shapes, fp32
+    (3, 100, 200, 76, F32, F32, F32, 64, 64),
+    (4, 300, 328, 136, BF16, F32, BF16, 256, 256),
+    (3, 300, 328, 136, BF16, BF16, F32, 128, 128),
+    (2, 513, 1032, 72, BF16, F32, BF16, 256, 256),
+]
+
+
+@pytest.mark.parametrize("P,Mc,N,K,ind,sdt,odt,tm,tn", GEMM_AR_CASES)
+def test_gemm_ar_values(P, Mc, N, K, ind, sdt, odt, tm, tn):
+    say(f"gemm_ar P={P} Mc={Mc} N={N} K={K} dt={ind}{sdt}{odt} tile={tm}x{tn}")
+    run, slots, win = _gemm_ar(P, Mc, N, K, ind, sdt, odt, tm, tn, seed=3 * P + K)
+    assert relerr(val(bf.to_host(run.out_all, odt), odt), val(win, odt)) <= TOL[ind]
+    assert relerr(val(bf.to_host(run.win_data, sdt), sdt), val(slots, sdt)) <= TOL[ind]
+    _replicas_identical(run)
+    assert torch.all(run.win_flags == run.epoch)
+    assert torch.all(run.ws == 0)
+
+
+@pytest.mark.parametrize("P,Mc,N,K,tm,sdt,grid", [
+    (4, 300, 328, 392, 256, F32, 0),        # ragged tiles, register-staged mainloop
+    (4, 512, 512, 1280, 256, F32, 16),      # bands folded inside later tiles' mainloops
+    (8, 256, 256, 1280, 256, BF16, 16),
+    (3, 256, 256, 1280, 128, F32, 16),
+    (4, 512, 512, 256, 256, F32, 5),        # a grid below the queue count: stealing
+    (16, 256, 512, 256, 256, F32, 0),       # the ABI's largest shard count
+])
+def test_gemm_ar_integer_bit_exact(P, Mc, N, K, tm, sdt, grid, monkeypatch):
+    """Integer-valued operands: every partial and fold is exact, so all P
+    windows equal the oracle bit for bit, whichever path folds the band."""
+    if grid:
+        monkeypatch.setenv("HOCF_MAX_WORKGROUPS", str(grid))
+    say(f"gemm_ar integer P={P} Mc={Mc} N={N} K={K} tile={tm} slot={sdt} grid={grid or 'full'}")
+    ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    run, slots, win = _gemm_ar(P, Mc, N, K, BF16, sdt, BF16, tm, tm, seed=200 + P + grid, dist=ints)
+    np.testing.assert_array_equal(bf.to_host(run.out_all, BF16), win)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, sdt), slots)
+
+
+def test_gemm_ar_reducer_isolation_bit_exact(monkeypatch):
+    """Selector operands make every partial an exact bf16 value over 2^-20 ..
+    2^21, so the rank-order fp32 fold is the only rounding: all P windows
+    must equal the oracle's fold bit for bit (a reversed order would not)."""
+    monkeypatch.setenv("HOCF_MAX_WORKGROUPS", "16")
+    P, Mc, N, K = 8, 256, 512, 1280
+    say(f"gemm_ar reducer isolation P={P} Mc={Mc} N={N} K={K}")
+    dist = dict(dist_a=("selector",), dist_w=("wide", -20, 20))
+    run, slots, win = _gemm_ar(P, Mc, N, K, BF16, F32, F32, 256, 256, seed=95, dist=dist)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, F32), slots)
+    np.testing.assert_array_equal(bf.to_host(run.out_all, F32), win)
+    assert _reversed_fold_differs([slots[0][q] for q in range(P)], win[0][:Mc])
+
+
+def test_gemm_ar_full_mlpdown():
+    """GEMM + AllReduce at the row-parallel MLP-down shape (P=8, 8192x4096x1792):
+    sampled windows against the oracle's fold at those points, all P windows
+    bit-identical, every flag set."""
+    c = cfgs.GEMM_RS_MLP
+    say(f"gemm_ar full {c.name} (sampled)")
+    A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, BF16, seed=0)
+    run = bf.GemmAR(c.P, c.M, c.N, c.K, BF16, F32, c.out_dt, c.tile_m, c.tile_n, A, W)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    assert torch.all(run.win_flags == run.epoch)
+    _replicas_identical(run)
+    assert not torch.isnan(run.out_all[0].view(torch.bfloat16)).any()
+    rng = np.random.default_rng(321)
+    n = 3000
+    ms = rng.integers(0, c.M, n)
+    ns = rng.integers(0, c.N, n)
+    ms[:4] = [0, c.M - 1, 1023, 1024]
+    ns[:4] = [0, c.N - 1, 255, 256]
+    # the AllReduce's value at (m, n) is the rank-order fold of the P partials there
+    _, ov = oracle.gemm_rs_points(c.P, c.M, c.N, c.K, BF16, F32, c.out_dt, A, W, ms, ns)
+    out = bf.to_host(run.out_all[c.P - 1], BF16)
+    assert relerr(val(out[ms, ns], BF16), val(ov, BF16)) <= TOL[BF16]
+
+
 # ====================================================================== GEMV + AR
 
 def _gemv(P, Mb, N, K, sdt, odt, tn, seed=0, dist=None):
