@@ -12,7 +12,9 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
   embbag_a2a  64 tables 1e6x128 fp32, batch 16384, 20 rows per bag, Zipf(1.05), P=8
               (a 1 GiB scratch write between calls, outside the timed events)
   gemm_ar     GEMM+AllReduce, the gemm_rs shapes; the folded chunks land in all 8 windows
-              (last in the step, so its 537 MB of window writes precede only the next step)
+  gemm_rs_unfused  the gemm_rs workload as two kernels (the GEMM publishing its tiles, then the
+              fold): the bulk-synchronous baseline; `fusion` reports the time the fused
+              operator saves against it
 
 Optional extra ops (--ops): embbag_uniform (the same shapes with uniform indices:
 no reuse, a control for the Zipf figure) and copy (a 1 GiB negating copy, the
@@ -49,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)  # >= 200 timed calls of each operator
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
-    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a,gemm_ar")
+    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a,gemm_ar,gemm_rs_unfused")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
@@ -217,6 +219,21 @@ def main():
                                bound="mfma", peak=PEAK_BF16_TFLOPS, bytes=algo_bytes,
                                config=dict(workload=c.name, P=c.P, M=c.M, N=c.N, K=c.K,
                                            tile=[c.tile_m, c.tile_n], slot_dtype=args.slot_dtype))
+    if "gemm_rs_unfused" in ops:
+        # the baseline of the fused operator: the same GEMM, then a separate fold kernel
+        c = cfgs.GEMM_RS_MLP
+        log(f"inputs {c.name} (unfused)")
+        A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, c.in_dt, seed=0)
+        u = bf.GemmRS(c.P, c.M, c.N, c.K, c.in_dt, sdt, c.out_dt, c.tile_m, c.tile_n, A, W, unfused=True)
+        del A, W
+        algo_bytes = (2 * (c.P * c.M * c.K + c.P * c.K * c.N)
+                      + 2 * (4 if sdt == bf.F32 else 2) * c.P * c.M * c.N + 2 * c.M * c.N)
+        runs["gemm_rs_unfused"] = dict(call=lambda r=u: r.run(stream), obj=u, work=c.flops, unit="TFLOP/s",
+                                       variant=f"slot_dtype={args.slot_dtype} tile={c.tile_m}x{c.tile_n}",
+                                       bound="mfma", peak=PEAK_BF16_TFLOPS, bytes=algo_bytes,
+                                       config=dict(workload=c.name + "_unfused", P=c.P, M=c.M, N=c.N, K=c.K,
+                                                   tile=[c.tile_m, c.tile_n], slot_dtype=args.slot_dtype,
+                                                   kernels="GEMM (tiles published), then the fold"))
     if "embbag_uniform" in ops:
         # control: the same shapes with uniform indices (no reuse), so logical ~ DRAM bytes
         c = cfgs.EMBBAG_DLRM
@@ -325,6 +342,11 @@ def main():
         "roofline": out_ops[head]["roofline"],
         "ops": out_ops,
     }
+    if "gemm_rs" in out_ops and "gemm_rs_unfused" in out_ops:
+        # fused against unfused (the computation, then the collective) on the same GPU
+        f, u = out_ops["gemm_rs"]["ms_avg"], out_ops["gemm_rs_unfused"]["ms_avg"]
+        res["fusion"] = {"op": "gemm_rs", "fused_ms": f, "unfused_ms": u, "time_saved": round(1.0 - f / u, 4)}
+        log(f"fusion: gemm_rs fused {f:.4f} ms, unfused {u:.4f} ms ({100 * (1 - f / u):.1f}% less time)")
     if not args.no_cpu_baseline and "gemm_rs" in out_ops:
         log("cpu baseline (oracle on a bounded sample)")
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

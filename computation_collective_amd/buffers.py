@@ -65,7 +65,9 @@ class _Common:
 class GemmRS(_Common):
     """hocf_gemm_rs: A [P][M][K], W [P][K][N] -> windows [P dst][P src][Mc][N], out [M][N]."""
 
-    def __init__(self, P, M, N, K, in_dt, slot_dt, out_dt, tile_m, tile_n, A, W, device="cuda"):
+    def __init__(self, P, M, N, K, in_dt, slot_dt, out_dt, tile_m, tile_n, A, W, device="cuda",
+                 unfused=False):
+        self.unfused = unfused   # hocf_gemm_rs_unfused: the GEMM kernel, then the fold kernel
         self.P, self.M, self.N, self.K = P, M, N, K
         self.in_dt, self.slot_dt, self.out_dt = in_dt, slot_dt, out_dt
         self.tile_m, self.tile_n = tile_m, tile_n
@@ -85,9 +87,9 @@ class GemmRS(_Common):
 
     def call(self, stream=None, **kw) -> int:
         s = self.next_sync(**kw)
-        return hocf.hocf_gemm_rs(self.P, self.M, self.N, self.K, self.in_dt, self.slot_dt,
-                                 self.out_dt, self.A, self.W, self.win, self.out, self.tile_m,
-                                 self.tile_n, s, stream)
+        fn = hocf.hocf_gemm_rs_unfused if self.unfused else hocf.hocf_gemm_rs
+        return fn(self.P, self.M, self.N, self.K, self.in_dt, self.slot_dt, self.out_dt, self.A, self.W,
+                  self.win, self.out, self.tile_m, self.tile_n, s, stream)
 
     def run(self, stream=None, **kw):
         hocf.check(self.call(stream, **kw))
@@ -99,6 +101,7 @@ class GemmAR(GemmRS):
 
     def __init__(self, P, M, N, K, in_dt, slot_dt, out_dt, tile_m, tile_n, A, W, device="cuda"):
         super().__init__(P, M, N, K, in_dt, slot_dt, out_dt, tile_m, tile_n, A, W, device)
+        del self.unfused
         del self.out
         self.out_all = torch.empty((P, M, N), dtype=tdtype(out_dt), device=device)
         self.outs = hocf.pointers([self.out_all[q] for q in range(P)])

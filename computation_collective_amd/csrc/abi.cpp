@@ -179,7 +179,7 @@ size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n)
 // AllReduce (nout = P outputs, every one receiving all M rows).
 static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, hocf_dtype in_dt,
                                    hocf_dtype slot_dt, hocf_dtype out_dt, const void* A, const void* W,
-                                   const hocf_window* win, void* const* outs, int nout, bool allreduce,
+                                   const hocf_window* win, void* const* outs, int nout, int mode,
                                    int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
   if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "%s: P=%d outside [1, %d]", op, P, HOCF_MAX_P);
   if (M < 0 || N < 0 || K < 0) return fail(HOCF_ERR_INVALID_ARG, "%s: negative dimension", op);
@@ -225,7 +225,7 @@ static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, h
   a.A = A; a.W = W;
   for (int q = 0; q < nout; ++q) a.outs[q] = outs[q];
   a.nout = nout;
-  a.allreduce = allreduce;
+  a.mode = mode;
   for (int r = 0; r < P; ++r) { a.win_data[r] = win[r].data; a.win_flags[r] = win[r].flags; }
   a.ws = static_cast<uint32_t*>(sync->workspace);
   a.P = P; a.M = M; a.N = N; a.K = K; a.Mc = M / P;
@@ -241,8 +241,16 @@ hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtyp
                          hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
                          void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
   void* const outs[1] = {out};
-  return gemm_collective("gemm_rs", P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, 1, false, tile_m, tile_n,
+  return gemm_collective("gemm_rs", P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, 1, 0, tile_m, tile_n,
                          sync, stream);
+}
+
+hocf_status hocf_gemm_rs_unfused(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                                 hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
+                                 void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
+  void* const outs[1] = {out};
+  return gemm_collective("gemm_rs_unfused", P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, 1, 2, tile_m,
+                         tile_n, sync, stream);
 }
 
 /* ------------------------------------------------------------ GEMM + AR */
@@ -254,7 +262,7 @@ size_t hocf_gemm_ar_workspace_bytes(int P, int M, int N, int tile_m, int tile_n)
 hocf_status hocf_gemm_ar(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
                          hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
                          void* const* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
-  return gemm_collective("gemm_ar", P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, out, P, true, tile_m, tile_n,
+  return gemm_collective("gemm_ar", P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, out, P, 1, tile_m, tile_n,
                          sync, stream);
 }
 

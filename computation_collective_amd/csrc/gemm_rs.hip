@@ -98,12 +98,13 @@ struct BandRef {
 };
 
 // Folds band `piece` of completed output tile `g` on its own, into the
-// first `nout` outputs.
-template <class Tile, bool RAGGED, int SDT, int ODT>
+// first `nout` outputs (checking the P contributions' flags first, unless
+// the partials are known complete: the unfused fold kernel).
+template <class Tile, bool RAGGED, int SDT, int ODT, bool CHECK = true>
 __device__ __forceinline__ void reduce_band(const GemmRsArgs& a, int64_t g, int piece, int nout) {
   const BandRef<Tile, SDT, ODT> b(a, g, piece);
   if (RAGGED && b.row0 >= b.rows_valid) return;
-  b.check_flags(a, a.mtiles * a.ntiles);
+  if constexpr (CHECK) b.check_flags(a, a.mtiles * a.ntiles);
   const int P = a.P, N = a.N;
   if (P <= 4)
     reduce_piece<Tile, SDT, ODT, RAGGED, 4, 8>(b.slot0, b.slot_bytes, P, N, b.outs(a, nout), N, b.row0, b.rows_valid,
@@ -116,11 +117,18 @@ __device__ __forceinline__ void reduce_band(const GemmRsArgs& a, int64_t g, int 
                                                    b.rows_valid, b.cols_valid);
 }
 
-// The kernel body shared by GEMM + ReduceScatter (AR = false: each folded
-// band goes to the one output) and GEMM + AllReduce (AR = true: each folded
-// band goes to all a.nout destination windows).
-template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT, bool AR>
+// What the kernel body does with a finished tile.
+enum GemmMode {
+  kFusedRS = 0,  // GEMM + ReduceScatter: publish, flag, fold bands into the one output
+  kFusedAR = 1,  // GEMM + AllReduce: the same, each folded band stored to all a.nout windows
+  kGemmOnly = 2  // the unfused baseline's first kernel: publish the tile, nothing else
+};
+
+// The kernel body shared by the fused operators and the unfused baseline's
+// GEMM kernel (MODE above).
+template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT, int MODE>
 __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
+  constexpr bool AR = MODE == kFusedAR, FUSED = MODE != kGemmOnly;
   using Elem = typename std::conditional<BF16IN, uint16_t, float>::type;
   constexpr int S = ReduceLayout<Tile, SDT>::PIECES;
   // tiles with a split mainloop start the next tile's loads before the band
@@ -180,7 +188,13 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
     // the next tile, and a band of a completed tile to fold in this
     // iteration if one is ready (one thread-0 region between two barriers)
     __syncthreads();
-    if (tid == 0) {
+    if (tid == 0 && !FUSED) {
+      // unfused: tiles only; the folds are a separate kernel
+      const int64_t it = tiles_left ? tiles.next(a.ws, a.total) : -1;
+      s_item = it;
+      s_state = it >= 0 ? 0 : 2;
+      s_band = -1;
+    } else if (tid == 0) {
       const int64_t it = tiles_left ? tiles.next(a.ws, a.total) : -1;
       const bool tl = it >= 0;
       int state = 0;  // 0: none now, 1: band ready, 2: all bands taken, 3: timed out
@@ -289,7 +303,7 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
                                                           rows_valid, cols_valid, acc, stages);
     }
 
-    if (item >= 0) {
+    if (FUSED && item >= 0) {
       wait_memory();  // this thread's stores of the tile have completed
       __syncthreads();
       // 2. ready flag; 3. arrival count -> the last producer hands out the bands
@@ -319,22 +333,45 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
 
 template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
 __global__ __launch_bounds__(Tile::NT) void gemm_rs_kernel(GemmRsArgs a) {
-  gemm_collective<Tile, RAGGED, BF16IN, SDT, ODT, false>(a);
+  gemm_collective<Tile, RAGGED, BF16IN, SDT, ODT, kFusedRS>(a);
 }
 
 template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
 __global__ __launch_bounds__(Tile::NT) void gemm_ar_kernel(GemmRsArgs a) {
-  gemm_collective<Tile, RAGGED, BF16IN, SDT, ODT, true>(a);
+  gemm_collective<Tile, RAGGED, BF16IN, SDT, ODT, kFusedAR>(a);
+}
+
+// The unfused baseline: the same GEMM, every tile published into its slot and
+// nothing else (no flags, no counts, no folds) ...
+template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
+__global__ __launch_bounds__(Tile::NT) void unfused_gemm_kernel(GemmRsArgs a) {
+  gemm_collective<Tile, RAGGED, BF16IN, SDT, ODT, kGemmOnly>(a);
+}
+
+// ... then, once that kernel has ended (stream order), one workgroup per band
+// of every output tile folds the P slots in rank order into the output.
+template <class Tile, bool RAGGED, int SDT, int ODT>
+__global__ __launch_bounds__(Tile::NT) void unfused_fold_kernel(GemmRsArgs a) {
+  constexpr int S = ReduceLayout<Tile, SDT>::PIECES;
+  reduce_band<Tile, RAGGED, SDT, ODT, false>(a, (int64_t)blockIdx.x / S, (int)(blockIdx.x % S), 1);
 }
 
 template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
 static hipError_t launch_one(const GemmRsArgs& a, hipStream_t s) {
-  auto kern = a.allreduce ? &gemm_ar_kernel<Tile, RAGGED, BF16IN, SDT, ODT>
-                          : &gemm_rs_kernel<Tile, RAGGED, BF16IN, SDT, ODT>;
+  auto kern = a.mode == kFusedAR ? &gemm_ar_kernel<Tile, RAGGED, BF16IN, SDT, ODT>
+            : a.mode == kGemmOnly ? &unfused_gemm_kernel<Tile, RAGGED, BF16IN, SDT, ODT>
+                                  : &gemm_rs_kernel<Tile, RAGGED, BF16IN, SDT, ODT>;
   int grid = 0;
   hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), Tile::NT, a.total, &grid);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(Tile::NT), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.mode != kGemmOnly) return e;
+  // the fold kernel: P chunks x tiles per chunk x bands per tile workgroups
+  const int64_t folds = (int64_t)a.P * a.mtiles * a.ntiles * ReduceLayout<Tile, SDT>::PIECES;
+  if (folds > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((unfused_fold_kernel<Tile, RAGGED, SDT, ODT>), dim3((unsigned)folds), dim3(Tile::NT), 0, s,
+                     a);
   return hipGetLastError();
 }
 

@@ -16,7 +16,8 @@ struct GemmRsArgs {
   // [M][N] for a ReduceScatter, the P receive windows for an AllReduce
   void* outs[kMaxP];
   int nout;
-  bool allreduce;  // GEMM + AllReduce (nout == P) rather than ReduceScatter (nout == 1)
+  int mode;  // 0: fused ReduceScatter (nout == 1); 1: fused AllReduce (nout == P);
+             // 2: unfused ReduceScatter (a GEMM kernel, then a fold kernel; nout == 1)
   void* win_data[kMaxP];
   uint32_t* win_flags[kMaxP];
   uint32_t* ws;

@@ -30,7 +30,7 @@ HOCF_MAX_P = 16
 
 EXPORTED = [
     "hocf_gemm_rs", "hocf_gemm_rs_workspace_bytes",
-    "hocf_gemm_ar", "hocf_gemm_ar_workspace_bytes",
+    "hocf_gemm_ar", "hocf_gemm_ar_workspace_bytes", "hocf_gemm_rs_unfused",
     "hocf_gemv_ar", "hocf_gemv_ar_workspace_bytes",
     "hocf_ag_gemm", "hocf_ag_gemm_workspace_bytes",
     "hocf_embbag_a2a", "hocf_embbag_a2a_workspace_bytes",
@@ -70,6 +70,7 @@ def lib():
         S = ctypes.POINTER(hocf_sync)
         L.hocf_gemm_rs.argtypes = [i, i, i, i, i, i, i, vp, vp, W, vp, i, i, S, vp]
         L.hocf_gemm_rs_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.hocf_gemm_rs_unfused.argtypes = [i, i, i, i, i, i, i, vp, vp, W, vp, i, i, S, vp]
         L.hocf_gemm_ar.argtypes = [i, i, i, i, i, i, i, vp, vp, W, ctypes.POINTER(vp), i, i, S, vp]
         L.hocf_gemm_ar_workspace_bytes.argtypes = [i, i, i, i, i]
         L.hocf_gemv_ar.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, W, i, S, vp]
@@ -78,7 +79,7 @@ def lib():
         L.hocf_ag_gemm_workspace_bytes.argtypes = [i]
         L.hocf_embbag_a2a.argtypes = [i, i64, i, i, i, i, vp, vp, vp, W, i, S, vp]
         L.hocf_embbag_a2a_workspace_bytes.argtypes = []
-        for f in ("hocf_gemm_rs", "hocf_gemm_ar", "hocf_gemv_ar", "hocf_ag_gemm", "hocf_embbag_a2a"):
+        for f in ("hocf_gemm_rs", "hocf_gemm_rs_unfused", "hocf_gemm_ar", "hocf_gemv_ar", "hocf_ag_gemm", "hocf_embbag_a2a"):
             getattr(L, f).restype = i
         for f in ("hocf_gemm_rs_workspace_bytes", "hocf_gemm_ar_workspace_bytes", "hocf_gemv_ar_workspace_bytes",
                   "hocf_ag_gemm_workspace_bytes", "hocf_embbag_a2a_workspace_bytes"):
@@ -177,6 +178,12 @@ def hocf_gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, out, tile_m, til
                  stream=None) -> int:
     return lib().hocf_gemm_rs(P, M, N, K, in_dt, slot_dt, out_dt, ptr(A), ptr(W), win, ptr(out),
                               tile_m, tile_n, ctypes.byref(sync_), _stream(stream))
+
+
+def hocf_gemm_rs_unfused(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, out, tile_m, tile_n, sync_,
+                         stream=None) -> int:
+    return lib().hocf_gemm_rs_unfused(P, M, N, K, in_dt, slot_dt, out_dt, ptr(A), ptr(W), win, ptr(out),
+                                      tile_m, tile_n, ctypes.byref(sync_), _stream(stream))
 
 
 def hocf_gemm_ar(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, tile_m, tile_n, sync_,

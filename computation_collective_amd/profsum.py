@@ -44,7 +44,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30  # the calibration pass reads and writes 1 GiB
 
 # kernel-name fragment -> operator name used by bench.py
-KERNELS = [("gemm_rs_kernel", "gemm_rs"), ("gemm_ar_kernel", "gemm_ar"), ("gemv_ar_kernel", "gemv_ar"),
+KERNELS = [("gemm_rs_kernel", "gemm_rs"), ("gemm_ar_kernel", "gemm_ar"),
+           ("unfused_gemm_kernel", "gemm_rs_unfused_gemm"), ("unfused_fold_kernel", "gemm_rs_unfused_fold"), ("gemv_ar_kernel", "gemv_ar"),
            ("ag_gemm_kernel", "ag_gemm"), ("embbag_kernel", "embbag_a2a"),
            ("neg_kernel", "copy")]
 
@@ -54,6 +55,10 @@ def workloads():
     from . import configs as c
     return {
         "gemm_rs": (c.GEMM_RS_MLP.name, f"slot_dtype=f32 tile={c.GEMM_RS_MLP.tile_m}x{c.GEMM_RS_MLP.tile_n}"),
+        "gemm_rs_unfused_gemm": (c.GEMM_RS_MLP.name + "_unfused_gemm",
+                                 f"slot_dtype=f32 tile={c.GEMM_RS_MLP.tile_m}x{c.GEMM_RS_MLP.tile_n}"),
+        "gemm_rs_unfused_fold": (c.GEMM_RS_MLP.name + "_unfused_fold",
+                                 f"slot_dtype=f32 tile={c.GEMM_RS_MLP.tile_m}x{c.GEMM_RS_MLP.tile_n}"),
         "gemm_ar": (c.GEMM_AR_MLP.name, f"slot_dtype=f32 tile={c.GEMM_AR_MLP.tile_m}x{c.GEMM_AR_MLP.tile_n}"),
         "gemv_ar": (c.GEMV_AR_DECODE.name, f"tile_n={c.GEMV_AR_DECODE.tile_n} weight_replicas=4"),
         "ag_gemm": (c.AG_GEMM_COL.name, f"tile={c.AG_GEMM_COL.tile_m}x{c.AG_GEMM_COL.tile_n} prereleased"),
@@ -178,9 +183,17 @@ def _fields(path):
     return d
 
 
+# bench operators whose timed call launches several kernels
+COMPOSITE = {"gemm_rs_unfused": ("gemm_rs_unfused_gemm", "gemm_rs_unfused_fold")}
+
+
 def traffic(op: str, variant: str | None = None):
     """Scaled HBM bytes per launch of `op` from its committed summary, or None
-    when there is none, it covers another variant, or the sources changed."""
+    when there is none, it covers another variant, or the sources changed
+    (for an operator of several kernels: their sum, if every one is known)."""
+    if op in COMPOSITE:
+        parts = [traffic(k, variant) for k in COMPOSITE[op]]
+        return None if any(x is None for x in parts) else float(sum(parts))
     wl = workloads().get(op)
     if wl is None:
         return None

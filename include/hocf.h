@@ -9,6 +9,9 @@
  *                    kommunikációval gyorsítják az AI-betanítást a kutatók",
  *                    section on its five fused kernels)
  *   hocf_gemm_ar     GEMM + AllReduce       (mKernel news item, same section)
+ *   hocf_gemm_rs_unfused  the same GEMM + ReduceScatter as two kernels, the
+ *                    computation then the collective (the baseline SC24
+ *                    measures its fused operators against)
  *   hocf_gemv_ar     GEMV + AllReduce       ("Optimizing Distributed ML
  *                    Communication with Fused Computation-Collective
  *                    Operations", SC24, abstract)
@@ -140,6 +143,27 @@ hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtyp
                          hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
                          void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream);
 size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n);
+
+/* ------------------------------------------------------------------------
+ * GEMM + ReduceScatter, unfused (the baseline the fused operator is
+ * measured against).
+ *
+ * SC24 (abstract) reports its fused operators against running the
+ * computation and then the collective; the mKernel item contrasts its
+ * in-kernel tile overlap with the same.  This entry point is that
+ * bulk-synchronous form on one GPU: the same arguments, arithmetic and
+ * results as hocf_gemm_rs (bit for bit: the same per-tile products and the
+ * same rank-order fold), computed by two kernels enqueued back to back on
+ * `stream` -- the GEMM, which publishes every tile of every C_p into its
+ * slot of win[r] and does nothing else, and then a fold kernel that reduces
+ * every destination's P slots in rank order into `out` once the GEMM kernel
+ * has ended.  No tile flag is written (win[r].flags is left as it was) and
+ * no fold overlaps the GEMM.  Supported combinations, limits, workspace
+ * (hocf_gemm_rs_workspace_bytes) and errors as for hocf_gemm_rs.
+ * ---------------------------------------------------------------------- */
+hocf_status hocf_gemm_rs_unfused(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                                 hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
+                                 void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream);
 
 /* ------------------------------------------------------------------------
  * GEMM + AllReduce.

@@ -68,6 +68,16 @@ def test_gemm_rs_rejects(kw, expect):
     assert hocf.last_error()
 
 
+@pytest.mark.parametrize("kw,expect", [(dict(P=0), INVALID), (dict(tile=(128, 64)), UNSUPPORTED),
+                                       (dict(A=FAKE + 8), INVALID), (dict(win=False), INVALID)])
+def test_gemm_rs_unfused_rejects(kw, expect):
+    a = dict(P=4, M=256, N=256, K=256, tile=(64, 64), A=FAKE, win=True)
+    a.update(kw)
+    st = hocf.hocf_gemm_rs_unfused(a["P"], a["M"], a["N"], a["K"], F32, F32, F32, a["A"], FAKE,
+                                   _win(a["P"]) if a["win"] else None, FAKE, *a["tile"], _sync())
+    assert st == expect
+
+
 def test_gemm_rs_valid_reaches_device():
     """A valid call gets past validation; here no GPU is present, so it stops at
     the device query (HOCF_ERR_HIP) -- on a GPU machine the same call launches."""

@@ -282,6 +282,86 @@ def test_gemm_rs_full_mlpdown(sdt):
     assert relerr(val(gs, sdt), val(sv, sdt)) <= TOL[BF16]
 
 
+# ====================================================================== GEMM + RS, unfused baseline
+
+UNFUSED_CASES = [
+    (4, 64, 256, 256, F32, F32, F32, 64, 64),        # the tiny workload's shapes, fp32
+    (4, 300, 328, 136, BF16, F32, BF16, 256, 256),   # ragged, register-staged mainloop
+    (3, 300, 328, 136, BF16, BF16, F32, 128, 128),
+    (4, 512, 768, 512, BF16, F32, BF16, 256, 256),   # full tiles, direct-to-LDS mainloop
+    (8, 256, 512, 1280, BF16, BF16, BF16, 256, 256),
+]
+
+
+@pytest.mark.parametrize("P,Mc,N,K,ind,sdt,odt,tm,tn", UNFUSED_CASES)
+def test_gemm_rs_unfused_matches_oracle_and_fused(P, Mc, N, K, ind, sdt, odt, tm, tn):
+    """The two-kernel baseline (GEMM, then the fold) gives the oracle's result
+    within tolerance and the fused operator's bits exactly: the same tile
+    products and the same rank-order fold, only the timing differs.  It
+    writes no flags."""
+    say(f"gemm_rs unfused P={P} Mc={Mc} N={N} K={K} dt={ind}{sdt}{odt} tile={tm}x{tn}")
+    M = P * Mc
+    dist = dict(dist_a=("normal", 1.0), dist_w=("normal", 0.02)) if ind == BF16 else \
+        dict(dist_a=("uniform",), dist_w=("uniform",))
+    A, W = gen.gemm_rs_inputs(P, M, N, K, ind, seed=11 * P + K, **dist)
+    u = bf.GemmRS(P, M, N, K, ind, sdt, odt, tm, tn, A, W, unfused=True)
+    f = bf.GemmRS(P, M, N, K, ind, sdt, odt, tm, tn, u.A, u.W)
+    u.poison()
+    f.poison()
+    u.run()
+    f.run()
+    sync()
+    assert u.status_value() == 0 and f.status_value() == 0
+    slots, out = oracle.gemm_rs(P, M, N, K, ind, sdt, odt, A, W)
+    assert relerr(val(bf.to_host(u.out, odt), odt), val(out, odt)) <= TOL[ind]
+    assert relerr(val(bf.to_host(u.win_data, sdt), sdt), val(slots, sdt)) <= TOL[ind]
+    assert torch.equal(u.out, f.out)
+    assert torch.equal(u.win_data, f.win_data)
+    assert torch.all(u.win_flags == 0), "the unfused baseline writes no flags"
+    assert torch.all(u.ws == 0)
+
+
+def test_gemm_rs_unfused_integer_bit_exact():
+    P, Mc, N, K = 4, 300, 328, 392
+    say(f"gemm_rs unfused integer P={P} Mc={Mc} N={N} K={K}")
+    M = P * Mc
+    A, W = gen.gemm_rs_inputs(P, M, N, K, BF16, seed=12, dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    u = bf.GemmRS(P, M, N, K, BF16, F32, BF16, 256, 256, A, W, unfused=True)
+    u.poison()
+    u.run()
+    sync()
+    assert u.status_value() == 0
+    slots, out = oracle.gemm_rs(P, M, N, K, BF16, F32, BF16, A, W)
+    np.testing.assert_array_equal(bf.to_host(u.out, BF16), out)
+    np.testing.assert_array_equal(bf.to_host(u.win_data, F32), slots)
+
+
+def test_gemm_rs_unfused_full_mlpdown():
+    """At the MLP-down workload: bit-identical to the fused operator, and
+    sampled outputs against the oracle."""
+    c = cfgs.GEMM_RS_MLP
+    say(f"gemm_rs unfused full {c.name}")
+    A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, BF16, seed=0)
+    u = bf.GemmRS(c.P, c.M, c.N, c.K, BF16, F32, c.out_dt, c.tile_m, c.tile_n, A, W, unfused=True)
+    u.poison()
+    u.run()
+    sync()
+    assert u.status_value() == 0
+    out_u = u.out.clone()
+    f = bf.GemmRS(c.P, c.M, c.N, c.K, BF16, F32, c.out_dt, c.tile_m, c.tile_n, u.A, u.W)
+    del u
+    f.poison()
+    f.run()
+    sync()
+    assert f.status_value() == 0
+    assert torch.equal(out_u, f.out)
+    rng = np.random.default_rng(7)
+    ms = rng.integers(0, c.M, 2000)
+    ns = rng.integers(0, c.N, 2000)
+    _, ov = oracle.gemm_rs_points(c.P, c.M, c.N, c.K, BF16, F32, c.out_dt, A, W, ms, ns)
+    assert relerr(val(bf.to_host(out_u, BF16)[ms, ns], BF16), val(ov, BF16)) <= TOL[BF16]
+
+
 # ====================================================================== GEMM + AR
 
 def _gemm_ar(P, Mc, N, K, in_dt, slot_dt, out_dt, tm, tn, seed=0, dist=None):
