@@ -12,9 +12,9 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
   embbag_a2a  64 tables 1e6x128 fp32, batch 16384, 20 rows per bag, Zipf(1.05), P=8
               (a 1 GiB scratch write between calls, outside the timed events)
   gemm_ar     GEMM+AllReduce, the gemm_rs shapes; the folded chunks land in all 8 windows
-  gemm_rs_unfused  the gemm_rs workload as two kernels (the GEMM publishing its tiles, then the
-              fold): the bulk-synchronous baseline; `fusion` reports the time the fused
-              operator saves against it
+  gemm_rs_unfused, gemv_ar_unfused  the gemm_rs / gemv_ar workloads as two kernels (the
+              computation publishing its partials, then the fold): the bulk-synchronous
+              baseline; `fusion` reports the time each fused operator saves against it
 
 Optional extra ops (--ops): embbag_uniform (the same shapes with uniform indices:
 no reuse, a control for the Zipf figure) and copy (a 1 GiB negating copy, the
@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)  # >= 200 timed calls of each operator
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
-    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a,gemm_ar,gemm_rs_unfused")
+    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a,gemm_ar,gemm_rs_unfused,gemv_ar_unfused")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
@@ -234,6 +234,30 @@ def main():
                                        config=dict(workload=c.name + "_unfused", P=c.P, M=c.M, N=c.N, K=c.K,
                                                    tile=[c.tile_m, c.tile_n], slot_dtype=args.slot_dtype,
                                                    kernels="GEMM (tiles published), then the fold"))
+    if "gemv_ar_unfused" in ops:
+        # the baseline of the fused GEMV + AllReduce: the GEMV, then a separate fold kernel
+        c = cfgs.GEMV_AR_DECODE
+        log(f"inputs {c.name} (unfused)")
+        x, W = gen.gemv_ar_inputs(c.P, c.Mb, c.N, c.K, seed=0)
+        gtile = args.gemv_tile or c.tile_n
+        gu = bf.GemvAR(c.P, c.Mb, c.N, c.K, c.in_dt, c.slot_dt, c.out_dt, gtile, x, W, unfused=True)
+        ureps = [(gu.x, gu.W)] + [(gu.x.clone(), gu.W.clone()) for _ in range(3)]
+        ustate = {"i": 0}
+
+        def gemv_u_call(g=gu, reps=ureps, state=ustate):
+            xr, Wr = reps[state["i"] % len(reps)]
+            state["i"] += 1
+            g.set_weights(xr, Wr)
+            g.run(stream)
+
+        algo_bytes = (2 * c.P * c.K * c.N + 2 * c.P * c.Mb * c.K + 2 * 4 * c.P * c.Mb * c.N
+                      + 2 * c.P * c.Mb * c.N)
+        runs["gemv_ar_unfused"] = dict(call=gemv_u_call, obj=gu, work=algo_bytes, unit="GB/s", bound="hbm",
+                                       variant=f"tile_n={gtile} weight_replicas=4",
+                                       peak=PEAK_HBM_GBS, bytes=algo_bytes,
+                                       config=dict(workload=c.name + "_unfused", P=c.P, Mb=c.Mb, N=c.N, K=c.K,
+                                                   tile_n=gtile, weight_replicas=4,
+                                                   kernels="GEMV (partials published), then the fold"))
     if "embbag_uniform" in ops:
         # control: the same shapes with uniform indices (no reuse), so logical ~ DRAM bytes
         c = cfgs.EMBBAG_DLRM
@@ -342,11 +366,15 @@ def main():
         "roofline": out_ops[head]["roofline"],
         "ops": out_ops,
     }
-    if "gemm_rs" in out_ops and "gemm_rs_unfused" in out_ops:
-        # fused against unfused (the computation, then the collective) on the same GPU
-        f, u = out_ops["gemm_rs"]["ms_avg"], out_ops["gemm_rs_unfused"]["ms_avg"]
-        res["fusion"] = {"op": "gemm_rs", "fused_ms": f, "unfused_ms": u, "time_saved": round(1.0 - f / u, 4)}
-        log(f"fusion: gemm_rs fused {f:.4f} ms, unfused {u:.4f} ms ({100 * (1 - f / u):.1f}% less time)")
+    # fused against unfused (the computation, then the collective) on the same GPU
+    fusion = {}
+    for op in ("gemm_rs", "gemv_ar"):
+        if op in out_ops and op + "_unfused" in out_ops:
+            f, u = out_ops[op]["ms_avg"], out_ops[op + "_unfused"]["ms_avg"]
+            fusion[op] = {"fused_ms": f, "unfused_ms": u, "time_saved": round(1.0 - f / u, 4)}
+            log(f"fusion: {op} fused {f:.4f} ms, unfused {u:.4f} ms ({100 * (1 - f / u):.1f}% less time)")
+    if fusion:
+        res["fusion"] = fusion
     if not args.no_cpu_baseline and "gemm_rs" in out_ops:
         log("cpu baseline (oracle on a bounded sample)")
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

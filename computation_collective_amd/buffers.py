@@ -120,7 +120,8 @@ class GemmAR(GemmRS):
 class GemvAR(_Common):
     """hocf_gemv_ar: x [P][Mb][K], W [P][K][N] -> part [P][Mb][N], windows [P][Mb][N]."""
 
-    def __init__(self, P, Mb, N, K, in_dt, slot_dt, out_dt, tile_n, x, W, device="cuda"):
+    def __init__(self, P, Mb, N, K, in_dt, slot_dt, out_dt, tile_n, x, W, device="cuda", unfused=False):
+        self.unfused = unfused   # hocf_gemv_ar_unfused: the GEMV kernel, then the fold kernel
         self.P, self.Mb, self.N, self.K = P, Mb, N, K
         self.in_dt, self.slot_dt, self.out_dt, self.tile_n = in_dt, slot_dt, out_dt, tile_n
         self.x = x if isinstance(x, torch.Tensor) else to_device(x, device)
@@ -142,9 +143,9 @@ class GemvAR(_Common):
 
     def call(self, stream=None, **kw) -> int:
         s = self.next_sync(**kw)
-        return hocf.hocf_gemv_ar(self.P, self.Mb, self.N, self.K, self.in_dt, self.slot_dt,
-                                 self.out_dt, self.x, self.W, self.part, self.part_flags, self.win,
-                                 self.tile_n, s, stream)
+        fn = hocf.hocf_gemv_ar_unfused if self.unfused else hocf.hocf_gemv_ar
+        return fn(self.P, self.Mb, self.N, self.K, self.in_dt, self.slot_dt, self.out_dt, self.x, self.W,
+                  self.part, self.part_flags, self.win, self.tile_n, s, stream)
 
     def run(self, stream=None, **kw):
         hocf.check(self.call(stream, **kw))

@@ -273,29 +273,30 @@ size_t hocf_gemv_ar_workspace_bytes(int P, int N, int tile_n) {
   return (size_t)(hocf::kWsBaseWords + cdiv(N, tile_n)) * 4;
 }
 
-hocf_status hocf_gemv_ar(int P, int Mb, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
-                         hocf_dtype out_dt, const void* x, const void* W, void* part,
-                         uint32_t* part_flags, const hocf_window* win, int tile_n,
-                         const hocf_sync* sync, void* stream) {
-  if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: P=%d outside [1, %d]", P, HOCF_MAX_P);
-  if (Mb < 0 || N < 0 || K < 0) return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: negative dimension");
+// Checks and launch shared by the fused GEMV + AllReduce and its unfused baseline.
+static hocf_status gemv_collective(const char* op, bool fused, int P, int Mb, int N, int K, hocf_dtype in_dt,
+                                   hocf_dtype slot_dt, hocf_dtype out_dt, const void* x, const void* W,
+                                   void* part, uint32_t* part_flags, const hocf_window* win, int tile_n,
+                                   const hocf_sync* sync, void* stream) {
+  if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "%s: P=%d outside [1, %d]", op, P, HOCF_MAX_P);
+  if (Mb < 0 || N < 0 || K < 0) return fail(HOCF_ERR_INVALID_ARG, "%s: negative dimension", op);
   if (!dt_ok(in_dt) || !dt_ok(slot_dt) || !dt_ok(out_dt))
-    return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: unknown dtype");
-  if (in_dt != HOCF_BF16) return fail(HOCF_ERR_UNSUPPORTED, "gemv_ar: inputs must be bf16");
-  if (Mb > 8) return fail(HOCF_ERR_UNSUPPORTED, "gemv_ar: Mb=%d > 8", Mb);
+    return fail(HOCF_ERR_INVALID_ARG, "%s: unknown dtype", op);
+  if (in_dt != HOCF_BF16) return fail(HOCF_ERR_UNSUPPORTED, "%s: inputs must be bf16", op);
+  if (Mb > 8) return fail(HOCF_ERR_UNSUPPORTED, "%s: Mb=%d > 8", op, Mb);
   if (tile_n != 128 && tile_n != 256 && tile_n != 512)
-    return fail(HOCF_ERR_UNSUPPORTED, "gemv_ar: tile_n=%d not in {128, 256, 512}", tile_n);
-  if (N % 8 || K % 8) return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: N and K must be multiples of 8");
+    return fail(HOCF_ERR_UNSUPPORTED, "%s: tile_n=%d not in {128, 256, 512}", op, tile_n);
+  if (N % 8 || K % 8) return fail(HOCF_ERR_INVALID_ARG, "%s: N and K must be multiples of 8", op);
   // partials and windows are addressed with 32-bit byte offsets
   if ((int64_t)Mb * N * 4 >= ((int64_t)1 << 31))
-    return fail(HOCF_ERR_UNSUPPORTED, "gemv_ar: Mb * N = %lld elements exceeds 2^29", (long long)Mb * N);
+    return fail(HOCF_ERR_UNSUPPORTED, "%s: Mb * N = %lld elements exceeds 2^29", op, (long long)Mb * N);
   hocf_status st = check_sync(sync, hocf_gemv_ar_workspace_bytes(P, N, tile_n));
   if (st != HOCF_OK) return st;
   if (Mb == 0 || N == 0) return ok();
-  if (!x || !W || !part || !part_flags) return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: NULL tensor");
+  if (!x || !W || !part || !part_flags) return fail(HOCF_ERR_INVALID_ARG, "%s: NULL tensor", op);
   if (!aligned16(x) || !aligned16(W) || !aligned16(part))
-    return fail(HOCF_ERR_INVALID_ARG, "gemv_ar: tensors must be 16-byte aligned");
-  if ((st = check_windows(win, P, "gemv_ar")) != HOCF_OK) return st;
+    return fail(HOCF_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", op);
+  if ((st = check_windows(win, P, op)) != HOCF_OK) return st;
 
   hocf::SyncArgs sa;
   if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
@@ -310,7 +311,24 @@ hocf_status hocf_gemv_ar(int P, int Mb, int N, int K, hocf_dtype in_dt, hocf_dty
   a.slot_dt = slot_dt; a.out_dt = out_dt;
   a.total = (int64_t)P * a.ntiles;
   a.sync = sa;
-  return launched(hocf::launch_gemv_ar(a, static_cast<hipStream_t>(stream)), "gemv_ar");
+  a.fused = fused;
+  return launched(hocf::launch_gemv_ar(a, static_cast<hipStream_t>(stream)), op);
+}
+
+hocf_status hocf_gemv_ar(int P, int Mb, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                         hocf_dtype out_dt, const void* x, const void* W, void* part,
+                         uint32_t* part_flags, const hocf_window* win, int tile_n,
+                         const hocf_sync* sync, void* stream) {
+  return gemv_collective("gemv_ar", true, P, Mb, N, K, in_dt, slot_dt, out_dt, x, W, part, part_flags, win,
+                         tile_n, sync, stream);
+}
+
+hocf_status hocf_gemv_ar_unfused(int P, int Mb, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                                 hocf_dtype out_dt, const void* x, const void* W, void* part,
+                                 uint32_t* part_flags, const hocf_window* win, int tile_n,
+                                 const hocf_sync* sync, void* stream) {
+  return gemv_collective("gemv_ar_unfused", false, P, Mb, N, K, in_dt, slot_dt, out_dt, x, W, part, part_flags,
+                         win, tile_n, sync, stream);
 }
 
 /* ------------------------------------------------------------ AG + GEMM */

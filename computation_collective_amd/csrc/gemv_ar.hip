@@ -50,8 +50,38 @@ __device__ __forceinline__ floatx4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t of
   }
 }
 
+// Folds the P partials of column tile j in rank order in fp32, rounds once
+// and stores the same bits into all P windows (device-coherent stores; the
+// caller waits for them before announcing the tile).
 template <int MB, int TN, int SDT, int ODT>
-__global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) {
+__device__ __forceinline__ void fold_column_tile(const GemvArArgs& a, int j) {
+  constexpr int NQ = MB * TN / 4;
+  constexpr int SES = SDT == kBF16 ? 2 : 4, OES = ODT == kBF16 ? 2 : 4;
+  const int tid = threadIdx.x, N = a.N, P = a.P, Mb = a.Mb;
+  const int n0 = j * TN, cols_valid = min(TN, N - n0);
+  for (int e = tid; e < NQ; e += kGemvThreads) {
+    const int qb = e / (TN / 4), qc = (e % (TN / 4)) * 4;
+    if (qb >= Mb || qc >= cols_valid) continue;
+    const uint32_t qoff = (uint32_t)(qb * N + n0 + qc);  // element offset in a [Mb][N] array
+    floatx4 v[kMaxP];
+#pragma unroll
+    for (int q = 0; q < kMaxP; ++q) {
+      const int qq = q < P ? q : P - 1;  // loads stay unconditional; slots past P are not added
+      v[q] = ld_dev4<SDT>(raw_rsrc(reinterpret_cast<char*>(a.part) + (int64_t)qq * Mb * N * SES), qoff * SES);
+    }
+    floatx4 s = v[0];
+#pragma unroll
+    for (int q = 1; q < kMaxP; ++q)
+      if (q < P) s = s + v[q];
+    for (int q = 0; q < P; ++q) st_dev4<ODT>(raw_rsrc(a.win_data[q]), qoff * OES, s);
+  }
+}
+
+// FUSED: the operator (publish the partial with its flag; the last producer
+// of a column tile folds it).  Not FUSED: the unfused baseline's first
+// kernel, which only publishes the partials.
+template <int MB, int TN, int SDT, int ODT, bool FUSED>
+__device__ __forceinline__ void gemv_body(const GemvArArgs& a) {
   constexpr int NCG = TN / 8;               // 16-byte column groups
   constexpr int KL = kGemvThreads / NCG;    // k-lanes
   constexpr int U = kGemvU;
@@ -180,6 +210,10 @@ __global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) 
       for (int q = 1; q < KL; ++q) s = s + *reinterpret_cast<const floatx4*>(&lds[(q * MB + qb) * TN + qc]);
       st_dev4<SDT>(rpart, (uint32_t)(qb * N + n0 + qc) * SES, s);
     }
+    if constexpr (!FUSED) {
+      __syncthreads();  // the fold's lds reads are done before the next item stages x
+      continue;
+    }
     wait_memory();
     __syncthreads();
 
@@ -201,23 +235,7 @@ __global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) 
         const uint32_t* f = &a.part_flags[(int64_t)tid * a.ntiles + j];
         if (!flag_reaches(f, load_flag_agent(f), a.sync)) report_status(a.sync, kErrProtocol);
       }
-      for (int e = tid; e < NQ; e += kGemvThreads) {
-        const int qb = e / (TN / 4), qc = (e % (TN / 4)) * 4;
-        if (qb >= Mb || qc >= cols_valid) continue;
-        const uint32_t qoff = (uint32_t)(qb * N + n0 + qc);  // element offset in a [Mb][N] array
-        floatx4 v[kMaxP];
-#pragma unroll
-        for (int q = 0; q < kMaxP; ++q) {
-          const int qq = q < P ? q : P - 1;  // loads stay unconditional; slots past P are not added
-          v[q] = ld_dev4<SDT>(raw_rsrc(reinterpret_cast<char*>(a.part) + (int64_t)qq * Mb * N * SES),
-                              qoff * SES);
-        }
-        floatx4 s = v[0];
-#pragma unroll
-        for (int q = 1; q < kMaxP; ++q)
-          if (q < P) s = s + v[q];
-        for (int q = 0; q < P; ++q) st_dev4<ODT>(raw_rsrc(a.win_data[q]), qoff * OES, s);
-      }
+      fold_column_tile<MB, TN, SDT, ODT>(a, j);
       wait_memory();
       __syncthreads();
       if (tid < P)
@@ -227,12 +245,33 @@ __global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) 
 }
 
 template <int MB, int TN, int SDT, int ODT>
+__global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) {
+  gemv_body<MB, TN, SDT, ODT, true>(a);
+}
+
+// The unfused baseline: the GEMV publishing its partials and nothing else ...
+template <int MB, int TN, int SDT, int ODT>
+__global__ __launch_bounds__(kGemvThreads, 2) void unfused_gemv_kernel(GemvArArgs a) {
+  gemv_body<MB, TN, SDT, ODT, false>(a);
+}
+
+// ... then, after it (stream order), one workgroup per column tile folds the
+// P partials and writes the result into all P windows.
+template <int MB, int TN, int SDT, int ODT>
+__global__ __launch_bounds__(kGemvThreads) void unfused_gemv_fold_kernel(GemvArArgs a) {
+  fold_column_tile<MB, TN, SDT, ODT>(a, (int)blockIdx.x);
+}
+
+template <int MB, int TN, int SDT, int ODT>
 static hipError_t launch_k(const GemvArArgs& a, hipStream_t s) {
-  auto kern = &gemv_ar_kernel<MB, TN, SDT, ODT>;
+  auto kern = a.fused ? &gemv_ar_kernel<MB, TN, SDT, ODT> : &unfused_gemv_kernel<MB, TN, SDT, ODT>;
   int grid = 0;
   hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), kGemvThreads, a.total, &grid);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemvThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.fused) return e;
+  hipLaunchKernelGGL((unfused_gemv_fold_kernel<MB, TN, SDT, ODT>), dim3(a.ntiles), dim3(kGemvThreads), 0, s, a);
   return hipGetLastError();
 }
 

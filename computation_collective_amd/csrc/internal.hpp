@@ -39,6 +39,7 @@ struct GemvArArgs {
   int P, Mb, N, K, tile_n, ntiles;
   int slot_dt, out_dt;
   int64_t total;  // P * ntiles
+  bool fused;     // false: the unfused baseline (a GEMV kernel, then a fold kernel)
   SyncArgs sync;
 };
 

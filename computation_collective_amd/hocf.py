@@ -31,7 +31,7 @@ HOCF_MAX_P = 16
 EXPORTED = [
     "hocf_gemm_rs", "hocf_gemm_rs_workspace_bytes",
     "hocf_gemm_ar", "hocf_gemm_ar_workspace_bytes", "hocf_gemm_rs_unfused",
-    "hocf_gemv_ar", "hocf_gemv_ar_workspace_bytes",
+    "hocf_gemv_ar", "hocf_gemv_ar_workspace_bytes", "hocf_gemv_ar_unfused",
     "hocf_ag_gemm", "hocf_ag_gemm_workspace_bytes",
     "hocf_embbag_a2a", "hocf_embbag_a2a_workspace_bytes",
     "hocf_status_string", "hocf_last_error", "hocf_abi_version",
@@ -75,11 +75,13 @@ def lib():
         L.hocf_gemm_ar_workspace_bytes.argtypes = [i, i, i, i, i]
         L.hocf_gemv_ar.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, W, i, S, vp]
         L.hocf_gemv_ar_workspace_bytes.argtypes = [i, i, i]
+        L.hocf_gemv_ar_unfused.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, W, i, S, vp]
         L.hocf_ag_gemm.argtypes = [i, i, i, i, i, i, vp, vp, vp, vp, i, i, S, vp]
         L.hocf_ag_gemm_workspace_bytes.argtypes = [i]
         L.hocf_embbag_a2a.argtypes = [i, i64, i, i, i, i, vp, vp, vp, W, i, S, vp]
         L.hocf_embbag_a2a_workspace_bytes.argtypes = []
-        for f in ("hocf_gemm_rs", "hocf_gemm_rs_unfused", "hocf_gemm_ar", "hocf_gemv_ar", "hocf_ag_gemm", "hocf_embbag_a2a"):
+        for f in ("hocf_gemm_rs", "hocf_gemm_rs_unfused", "hocf_gemm_ar", "hocf_gemv_ar", "hocf_gemv_ar_unfused", "hocf_ag_gemm",
+                  "hocf_embbag_a2a"):
             getattr(L, f).restype = i
         for f in ("hocf_gemm_rs_workspace_bytes", "hocf_gemm_ar_workspace_bytes", "hocf_gemv_ar_workspace_bytes",
                   "hocf_ag_gemm_workspace_bytes", "hocf_embbag_a2a_workspace_bytes"):
@@ -198,6 +200,12 @@ def hocf_gemv_ar(P, Mb, N, K, in_dt, slot_dt, out_dt, x, W, part, part_flags, wi
                  stream=None) -> int:
     return lib().hocf_gemv_ar(P, Mb, N, K, in_dt, slot_dt, out_dt, ptr(x), ptr(W), ptr(part),
                               ptr(part_flags), win, tile_n, ctypes.byref(sync_), _stream(stream))
+
+
+def hocf_gemv_ar_unfused(P, Mb, N, K, in_dt, slot_dt, out_dt, x, W, part, part_flags, win, tile_n, sync_,
+                         stream=None) -> int:
+    return lib().hocf_gemv_ar_unfused(P, Mb, N, K, in_dt, slot_dt, out_dt, ptr(x), ptr(W), ptr(part),
+                                      ptr(part_flags), win, tile_n, ctypes.byref(sync_), _stream(stream))
 
 
 def hocf_ag_gemm(P, Mc, N, K, in_dt, out_dt, A_gathered, chunk_flags, W, out, tile_m, tile_n,

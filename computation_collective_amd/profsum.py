@@ -45,7 +45,8 @@ COPY_BYTES = 1 << 30  # the calibration pass reads and writes 1 GiB
 
 # kernel-name fragment -> operator name used by bench.py
 KERNELS = [("gemm_rs_kernel", "gemm_rs"), ("gemm_ar_kernel", "gemm_ar"),
-           ("unfused_gemm_kernel", "gemm_rs_unfused_gemm"), ("unfused_fold_kernel", "gemm_rs_unfused_fold"), ("gemv_ar_kernel", "gemv_ar"),
+           ("unfused_gemm_kernel", "gemm_rs_unfused_gemm"), ("unfused_fold_kernel", "gemm_rs_unfused_fold"),
+           ("unfused_gemv_kernel", "gemv_ar_unfused_gemv"), ("unfused_gemv_fold_kernel", "gemv_ar_unfused_fold"), ("gemv_ar_kernel", "gemv_ar"),
            ("ag_gemm_kernel", "ag_gemm"), ("embbag_kernel", "embbag_a2a"),
            ("neg_kernel", "copy")]
 
@@ -59,6 +60,10 @@ def workloads():
                                  f"slot_dtype=f32 tile={c.GEMM_RS_MLP.tile_m}x{c.GEMM_RS_MLP.tile_n}"),
         "gemm_rs_unfused_fold": (c.GEMM_RS_MLP.name + "_unfused_fold",
                                  f"slot_dtype=f32 tile={c.GEMM_RS_MLP.tile_m}x{c.GEMM_RS_MLP.tile_n}"),
+        "gemv_ar_unfused_gemv": (c.GEMV_AR_DECODE.name + "_unfused_gemv",
+                                 f"tile_n={c.GEMV_AR_DECODE.tile_n} weight_replicas=4"),
+        "gemv_ar_unfused_fold": (c.GEMV_AR_DECODE.name + "_unfused_fold",
+                                 f"tile_n={c.GEMV_AR_DECODE.tile_n} weight_replicas=4"),
         "gemm_ar": (c.GEMM_AR_MLP.name, f"slot_dtype=f32 tile={c.GEMM_AR_MLP.tile_m}x{c.GEMM_AR_MLP.tile_n}"),
         "gemv_ar": (c.GEMV_AR_DECODE.name, f"tile_n={c.GEMV_AR_DECODE.tile_n} weight_replicas=4"),
         "ag_gemm": (c.AG_GEMM_COL.name, f"tile={c.AG_GEMM_COL.tile_m}x{c.AG_GEMM_COL.tile_n} prereleased"),
@@ -184,7 +189,8 @@ def _fields(path):
 
 
 # bench operators whose timed call launches several kernels
-COMPOSITE = {"gemm_rs_unfused": ("gemm_rs_unfused_gemm", "gemm_rs_unfused_fold")}
+COMPOSITE = {"gemm_rs_unfused": ("gemm_rs_unfused_gemm", "gemm_rs_unfused_fold"),
+             "gemv_ar_unfused": ("gemv_ar_unfused_gemv", "gemv_ar_unfused_fold")}
 
 
 def traffic(op: str, variant: str | None = None):

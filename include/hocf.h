@@ -9,9 +9,10 @@
  *                    kommunikációval gyorsítják az AI-betanítást a kutatók",
  *                    section on its five fused kernels)
  *   hocf_gemm_ar     GEMM + AllReduce       (mKernel news item, same section)
- *   hocf_gemm_rs_unfused  the same GEMM + ReduceScatter as two kernels, the
- *                    computation then the collective (the baseline SC24
- *                    measures its fused operators against)
+ *   hocf_gemm_rs_unfused, hocf_gemv_ar_unfused
+ *                    the same GEMM + ReduceScatter / GEMV + AllReduce as two
+ *                    kernels, the computation then the collective (the
+ *                    baseline SC24 measures its fused operators against)
  *   hocf_gemv_ar     GEMV + AllReduce       ("Optimizing Distributed ML
  *                    Communication with Fused Computation-Collective
  *                    Operations", SC24, abstract)
@@ -215,6 +216,26 @@ hocf_status hocf_gemv_ar(int P, int Mb, int N, int K, hocf_dtype in_dt, hocf_dty
                          uint32_t* part_flags, const hocf_window* win, int tile_n,
                          const hocf_sync* sync, void* stream);
 size_t hocf_gemv_ar_workspace_bytes(int P, int N, int tile_n);
+
+/* ------------------------------------------------------------------------
+ * GEMV + AllReduce, unfused (the baseline the fused operator is measured
+ * against: SC24's abstract compares its fused GEMV + AllReduce with running
+ * the computation and then the collective).
+ *
+ * Same arguments, arithmetic and results as hocf_gemv_ar (the windows get
+ * the same bits), computed by two kernels enqueued back to back on
+ * `stream`: the GEMV, which publishes every partial into `part`, and then a
+ * fold kernel (one workgroup per column tile) that folds the P partials in
+ * rank order and writes the result into all P windows once the GEMV kernel
+ * has ended.  Neither part_flags nor the windows' flags are written (they
+ * are left as they were); part_flags must still be a valid pointer.
+ * Supported combinations, limits, workspace (hocf_gemv_ar_workspace_bytes)
+ * and errors as for hocf_gemv_ar.
+ * ---------------------------------------------------------------------- */
+hocf_status hocf_gemv_ar_unfused(int P, int Mb, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                                 hocf_dtype out_dt, const void* x, const void* W, void* part,
+                                 uint32_t* part_flags, const hocf_window* win, int tile_n,
+                                 const hocf_sync* sync, void* stream);
 
 /* ------------------------------------------------------------------------
  * AllGather + GEMM.

@@ -139,6 +139,17 @@ def test_gemv_ar_rejects(kw, expect):
 
 
 @pytest.mark.parametrize("kw,expect", [
+    (dict(P=0), INVALID), (dict(Mb=9), UNSUPPORTED), (dict(part=0), INVALID), (dict(N=8190), INVALID),
+])
+def test_gemv_ar_unfused_rejects(kw, expect):
+    a = dict(P=8, Mb=4, N=8192, part=FAKE)
+    a.update(kw)
+    st = hocf.hocf_gemv_ar_unfused(a["P"], a["Mb"], a["N"], 1024, BF16, F32, BF16, FAKE, FAKE, a["part"], FAKE,
+                                   _win(max(a["P"], 1)), 256, _sync())
+    assert st == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
     (dict(P=0), INVALID), (dict(tile=(256, 128)), UNSUPPORTED), (dict(K=100), INVALID),
     (dict(flags=FAKE + 2), INVALID), (dict(flags=0), INVALID),
 ])

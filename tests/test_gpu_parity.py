@@ -549,6 +549,45 @@ def test_gemv_ar_many_shards_integer_bit_exact(P):
     np.testing.assert_array_equal(bf.to_host(run.part, F32), part)
 
 
+@pytest.mark.parametrize("P,Mb,N,K,sdt,odt,tn", [
+    (8, 4, 8192, 1024, F32, BF16, 256),      # the decode workload
+    (3, 3, 328, 200, F32, BF16, 128), (8, 5, 2056, 520, BF16, F32, 256), (16, 2, 1032, 96, F32, F32, 512),
+])
+def test_gemv_ar_unfused_matches_oracle_and_fused(P, Mb, N, K, sdt, odt, tn):
+    """The two-kernel baseline (GEMV, then the fold) gives the oracle's result
+    within tolerance and the fused operator's bits exactly, in every window;
+    it writes no flags."""
+    say(f"gemv_ar unfused P={P} Mb={Mb} N={N} K={K} slot={sdt} out={odt} tile_n={tn}")
+    x, W = gen.gemv_ar_inputs(P, Mb, N, K, seed=P + Mb)
+    u = bf.GemvAR(P, Mb, N, K, BF16, sdt, odt, tn, x, W, unfused=True)
+    f = bf.GemvAR(P, Mb, N, K, BF16, sdt, odt, tn, u.x, u.W)
+    u.poison()
+    f.poison()
+    u.run()
+    f.run()
+    sync()
+    assert u.status_value() == 0 and f.status_value() == 0
+    part, win = oracle.gemv_ar(P, Mb, N, K, BF16, sdt, odt, x, W)
+    assert relerr(val(bf.to_host(u.win_data, odt), odt), val(win, odt)) <= TOL[BF16]
+    assert relerr(val(bf.to_host(u.part, sdt), sdt), val(part, sdt)) <= TOL[BF16]
+    assert torch.equal(u.win_data, f.win_data) and torch.equal(u.part, f.part)
+    assert torch.all(u.part_flags == 0) and torch.all(u.win_flags == 0)
+
+
+def test_gemv_ar_unfused_integer_bit_exact():
+    P, Mb, N, K = 8, 4, 2048, 1024
+    say(f"gemv_ar unfused integer P={P} Mb={Mb} N={N} K={K}")
+    x, W = gen.gemv_ar_inputs(P, Mb, N, K, seed=5, dist_x=("int", -2, 2), dist_w=("int", -2, 2))
+    u = bf.GemvAR(P, Mb, N, K, BF16, F32, F32, 256, x, W, unfused=True)
+    u.poison()
+    u.run()
+    sync()
+    assert u.status_value() == 0
+    part, win = oracle.gemv_ar(P, Mb, N, K, BF16, F32, F32, x, W)
+    np.testing.assert_array_equal(bf.to_host(u.win_data, F32), win)
+    np.testing.assert_array_equal(bf.to_host(u.part, F32), part)
+
+
 # ====================================================================== AG + GEMM
 
 def _ag_inputs(P, Mc, N, K, seed=0):
