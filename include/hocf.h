@@ -34,7 +34,8 @@
  * themselves (host memory, read during the call).  All tensors are dense
  * row-major.  bf16 tensors hold bfloat16 bit patterns (uint16).
  *
- * Streams.  A call validates its arguments, enqueues its kernel on `stream`
+ * Streams.  A call validates its arguments, enqueues its kernel (the
+ * unfused baselines: its two kernels) on `stream`
  * (a hipStream_t; NULL = the null stream) and returns.  Results, windows and
  * flags are valid once the stream has reached the kernel's end.  The library
  * never allocates, frees or synchronises in a call, and keeps no pointer
