@@ -171,3 +171,56 @@ def csr_bag_offsets(T, B, max_len, seed=0, empty_frac=0.1) -> np.ndarray:
     off = np.zeros(T * B + 1, dtype=np.int64)
     np.cumsum(lens, out=off[1:])
     return off
+
+
+def moe_routing(P, E, B, topk, tile_m, seed=0):
+    """Top-k routing of an expert-parallel MoE layer, seen from rank 0.
+
+    P ranks each hold B tokens and E experts (P*E experts in all; rank 0 owns
+    experts 0..E-1).  Every token picks `topk` distinct experts uniformly at
+    random.  Rank 0 computes the pairs (rank d, token t, choice k) whose
+    expert is one of its own, grouped by expert, each group in (d, t, k)
+    order and padded with empty rows to a multiple of `tile_m` (the
+    block-aligned layout of a grouped GEMM).  Each real row goes back to its
+    token's rank d, at slot = its position among the pairs rank 0 sends to d,
+    in (t, k) order.
+
+    Returns (offsets int64 [E+1] (row ranges of the expert groups), dest int32
+    [T] (-1 for a padding row), slot int32 [T] (-1 for padding), send_counts
+    int64 [P]), T = offsets[-1]."""
+    rng = np.random.default_rng(seed)
+    choice = np.argsort(rng.random((P, B, P * E)), axis=2)[:, :, :topk]   # [d][t][k] expert ids
+    local = choice < E
+    d_idx, t_idx, k_idx = np.nonzero(local)            # (d, t, k) order
+    experts = choice[d_idx, t_idx, k_idx]
+    send_counts = np.bincount(d_idx, minlength=P).astype(np.int64)
+    # slot of each pair inside its destination: running count per d in (t, k) order
+    slot_of = np.empty(len(d_idx), dtype=np.int64)
+    for d in range(P):
+        m = d_idx == d
+        slot_of[m] = np.arange(int(m.sum()))
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    dest_rows, slot_rows = [], []
+    for e in range(E):
+        m = experts == e
+        n = int(m.sum())
+        padded = -(-n // tile_m) * tile_m
+        dest_e = np.full(padded, -1, dtype=np.int32)
+        slot_e = np.full(padded, -1, dtype=np.int32)
+        dest_e[:n] = d_idx[m]
+        slot_e[:n] = slot_of[m]
+        dest_rows.append(dest_e)
+        slot_rows.append(slot_e)
+        offsets[e + 1] = offsets[e] + padded
+    dest = np.concatenate(dest_rows) if dest_rows else np.zeros(0, np.int32)
+    slot = np.concatenate(slot_rows) if slot_rows else np.zeros(0, np.int32)
+    return offsets, dest, slot, send_counts
+
+
+def gemm_a2a_inputs(E, T, N, K, dest, dtype=BF16, seed=0, dist_x=("normal", 1.0), dist_w=("normal", 0.02)):
+    """X [T][K] (padding rows, dest < 0, are zero) then W [E][K][N]."""
+    rng = np.random.default_rng(seed)
+    X = _draw(rng, (T, K), dist_x, dtype)
+    W = _draw(rng, (E, K, N), dist_w, dtype)
+    X[np.asarray(dest) < 0] = 0
+    return X, W

@@ -36,6 +36,7 @@ def _load():
         lib.oracle_gemm_rs_points.argtypes = [i32] * 7 + [vp, vp, i64, vp, vp, vp, vp]
         lib.oracle_gemv_ar.argtypes = [i32] * 7 + [vp] * 4
         lib.oracle_gemm_ar.argtypes = [i32] * 7 + [vp] * 4
+        lib.oracle_gemm_a2a.argtypes = [i32, i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64, vp]
         lib.oracle_ag_gemm.argtypes = [i32] * 6 + [vp] * 4
         lib.oracle_ag_gemm_points.argtypes = [i32] * 6 + [vp, vp, i64, vp, vp, vp]
         lib.oracle_embbag_a2a.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -115,6 +116,26 @@ def gemm_ar(P, M, N, K, in_dt, slot_dt, out_dt, A, W, want_slots=True):
     if rc != 0:
         raise ValueError(f"oracle_gemm_ar rejected its arguments (rc={rc})")
     return slots, win
+
+
+def gemm_a2a(P, E, N, K, in_dt, out_dt, X, W, offsets, dest, slot, cap, win=None):
+    """GEMM + All-to-All.  Returns win [P][cap][N]: row i of the expert GEMM at
+    [dest[i]][slot[i]]; entries no row names keep their previous contents
+    (`win`, or zeros)."""
+    _check(in_dt, X, W)
+    T = X.shape[0]
+    assert X.shape == (T, K) and W.shape == (E, K, N)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    dest = np.ascontiguousarray(dest, dtype=np.int32)
+    slot = np.ascontiguousarray(slot, dtype=np.int32)
+    assert offsets.shape == (E + 1,) and dest.shape == (T,) and slot.shape == (T,)
+    if win is None:
+        win = np.zeros((P, cap, N), dtype=_np_dt(out_dt))
+    rc = _load().oracle_gemm_a2a(P, E, T, N, K, in_dt, out_dt, _ptr(X), _ptr(W), _ptr(offsets), _ptr(dest),
+                                 _ptr(slot), cap, _ptr(win))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_a2a rejected its arguments (rc={rc})")
+    return win
 
 
 def gemv_ar(P, Mb, N, K, in_dt, slot_dt, out_dt, x, W):

@@ -227,6 +227,59 @@ int oracle_gemm_ar(int P, int M, int N, int K, int in_dt, int slot_dt, int out_d
     return 0;
 }
 
+/* ---- GEMM + All-to-All ----------------------------------------------------
+ * SC24 (abstract) names GEMM + All-to-All, for mixture-of-experts layers,
+ * among its three fused prototypes.  This rank holds E experts and has
+ * received, for each expert e, a group of token rows X[offsets[e] ..
+ * offsets[e+1]) (rows of expert e, [K] each).  Each row is multiplied by its
+ * expert's W_e [K][N] (fp64, k ascending, rounded once to out_dt), and the
+ * All-to-All sends the result row back to the token's rank: row i lands in
+ * window dest[i] at slot slot[i].  A row with dest[i] < 0 is padding and
+ * goes nowhere.
+ *   X [T][K], W [E][K][N] of in_dt; offsets [E+1] int64 non-decreasing from
+ *   0 to T; dest, slot [T] int32; win [P][cap][N] of out_dt.
+ * Every (dest, slot) pair may be written at most once: a repeated pair, a
+ * dest >= P or a slot outside [0, cap) is an error (-1). */
+int oracle_gemm_a2a(int P, int E, int64_t T, int N, int K, int in_dt, int out_dt, const void* X,
+                    const void* W, const int64_t* offsets, const int32_t* dest, const int32_t* slot,
+                    int64_t cap, void* win) {
+    if (P <= 0 || E <= 0 || T < 0 || N < 0 || K < 0 || cap < 0) return -1;
+    if (!dt_ok(in_dt) || !dt_ok(out_dt)) return -1;
+    if (offsets[0] != 0 || offsets[E] != T) return -1;
+    for (int e = 0; e < E; ++e)
+        if (offsets[e + 1] < offsets[e]) return -1;
+    /* routing: each real row names one (dest, slot), and no pair is named twice */
+    unsigned char* used = (unsigned char*)calloc((size_t)(P * cap > 0 ? P * cap : 1), 1);
+    if (!used) return -1;
+    for (int64_t i = 0; i < T; ++i) {
+        if (dest[i] < 0) continue;
+        if (dest[i] >= P || slot[i] < 0 || slot[i] >= cap || used[dest[i] * cap + slot[i]]) {
+            free(used);
+            return -1;
+        }
+        used[dest[i] * cap + slot[i]] = 1;
+    }
+    free(used);
+
+    /* expert GEMM per row, then the row goes to its (dest, slot) */
+    for (int e = 0; e < E; ++e) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t i = offsets[e]; i < offsets[e + 1]; ++i) {
+            if (dest[i] < 0) continue;
+            double* acc = (double*)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+            for (int64_t k = 0; k < K; ++k) {
+                const double a = load_in(X, in_dt, i * K + k);
+                const int64_t wrow = ((int64_t)e * K + k) * N;
+                for (int64_t n = 0; n < N; ++n) acc[n] += a * load_in(W, in_dt, wrow + n);
+            }
+            const int64_t base = ((int64_t)dest[i] * cap + slot[i]) * N;
+            for (int64_t n = 0; n < N; ++n) store_f32_as(win, out_dt, base + n, (float)acc[n]);
+            free(acc);
+        }
+    }
+    return 0;
+}
+
 /* ---- GEMV + AllReduce -----------------------------------------------------
  * x [P][Mb][K], W [P][K][N].  Shard p computes y_p = x_p . W_p (Mb x N),
  * carried in slot_dt; the AllReduce folds y_0..y_{P-1} in rank order in fp32,

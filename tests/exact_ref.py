@@ -89,6 +89,20 @@ def gemm_ar(P, M, N, K, A, W, slot_fmt, out_fmt):
     return slots, [[list(out[m]) for m in range(M)] for _ in range(P)]
 
 
+def gemm_a2a(P, E, N, K, X, W, offsets, dest, slot, cap, out_fmt):
+    """Returns win[d][s][n] (None where no row lands) as Fractions."""
+    win = [[[None] * N for _ in range(cap)] for _ in range(P)]
+    for e in range(E):
+        for i in range(offsets[e], offsets[e + 1]):
+            if dest[i] < 0:
+                continue
+            for n in range(N):
+                s = sum((fr(X[i][k]) * fr(W[e][k][n]) for k in range(K)), Fraction(0))
+                v = round_to(s, FP32)
+                win[dest[i]][slot[i]][n] = round_to(v, out_fmt) if out_fmt is BF16 else v
+    return win
+
+
 def gemv_ar(P, Mb, N, K, x, W, slot_fmt, out_fmt):
     """Returns (part[p][b][n], win[q][b][n])."""
     part = [[[None] * N for _ in range(Mb)] for _ in range(P)]

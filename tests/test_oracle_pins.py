@@ -72,6 +72,14 @@ def test_gemm_ar_golden(g):
     np.testing.assert_array_equal(_val(win, g["out_dt"]), np.asarray(g["win"], dtype=np.float64))
 
 
+@pytest.mark.parametrize("g", _golden("gemm_a2a"))
+def test_gemm_a2a_golden(g):
+    X, W = _arr(g["X"], g["in_dt"]), _arr(g["W"], g["in_dt"])
+    win = oracle.gemm_a2a(g["P"], g["E"], g["N"], g["K"], g["in_dt"], g["out_dt"], X, W, g["offsets"],
+                          g["dest"], g["slot"], g["cap"])
+    np.testing.assert_array_equal(_val(win, g["out_dt"]), np.asarray(g["win"], dtype=np.float64))
+
+
 @pytest.mark.parametrize("g", _golden("gemv_ar"))
 def test_gemv_ar_golden(g):
     x, W = _arr(g["x"], g["in_dt"]), _arr(g["W"], g["in_dt"])
@@ -338,6 +346,74 @@ def test_gemm_ar_integer_inputs_exact():
     want = sum(Ai[p] @ Wi[p] for p in range(P)).astype(np.float32)
     for q in range(P):
         np.testing.assert_array_equal(win[q], want)
+
+
+def _moe(P, E, B, topk, tile_m, N, K, in_dt, seed, **dist):
+    off, dest, slot, counts = gen.moe_routing(P, E, B, topk, tile_m, seed=seed)
+    X, W = gen.gemm_a2a_inputs(E, int(off[-1]), N, K, dest, dtype=in_dt, seed=seed, **dist)
+    return off, dest, slot, counts, X, W
+
+
+@pytest.mark.parametrize("P,E,B,topk,tile_m,N,K", [(2, 1, 3, 1, 2, 2, 3), (3, 2, 4, 2, 2, 3, 2),
+                                                   (2, 3, 5, 2, 4, 1, 4), (4, 1, 2, 3, 1, 2, 2)])
+@pytest.mark.parametrize("in_dt,out_dt", [(F32, F32), (BF16, BF16), (BF16, F32)])
+def test_gemm_a2a_bruteforce(P, E, B, topk, tile_m, N, K, in_dt, out_dt):
+    off, dest, slot, counts, X, W = _moe(P, E, B, topk, tile_m, N, K, in_dt, seed=P * 10 + E + B)
+    cap = int(counts.max()) + 1
+    win = oracle.gemm_a2a(P, E, N, K, in_dt, out_dt, X, W, off, dest, slot, cap)
+    ew = ex.gemm_a2a(P, E, N, K, _val(X, in_dt).tolist(), _val(W, in_dt).tolist(), off.tolist(),
+                     dest.tolist(), slot.tolist(), cap, ex.BF16 if out_dt == BF16 else ex.FP32)
+    got = _val(win, out_dt)
+    for d in range(P):
+        for s_ in range(cap):
+            for n in range(N):
+                want = ew[d][s_][n]
+                if want is None:
+                    assert got[d, s_, n] == 0.0          # untouched (zero-initialised)
+                elif in_dt == BF16:
+                    assert got[d, s_, n] == float(want)
+                else:  # fp32 inputs: the fp64 sum may round once before fp32 (<= 1 ulp)
+                    assert abs(got[d, s_, n] - float(want)) <= np.spacing(np.float32(abs(float(want))))
+
+
+def test_gemm_a2a_closed_form_and_buckets():
+    """Each window row equals its token row times its expert's W (numpy fp64,
+    one matmul per expert); every (dest, slot < send_count) is written exactly
+    once and nothing else is (NaN prefill)."""
+    P, E, B, topk, tile_m, N, K = 8, 4, 64, 2, 16, 24, 40
+    off, dest, slot, counts, X, W = _moe(P, E, B, topk, tile_m, N, K, BF16, seed=17)
+    cap = int(counts.max()) + 3
+    pre = np.full((P, cap, N), np.nan, dtype=np.float32)
+    win = oracle.gemm_a2a(P, E, N, K, BF16, F32, X, W, off, dest, slot, cap, win=pre)
+    Xv, Wv = _val(X, BF16), _val(W, BF16)
+    written = np.zeros((P, cap), dtype=np.int64)
+    for e in range(E):
+        Y = Xv[off[e]:off[e + 1]] @ Wv[e]
+        for r, i in enumerate(range(off[e], off[e + 1])):
+            if dest[i] < 0:
+                continue
+            written[dest[i], slot[i]] += 1
+            assert _normwise(win[dest[i], slot[i]].astype(np.float64), Y[r]) <= 1e-6
+    for d in range(P):
+        assert np.all(written[d, :counts[d]] == 1) and np.all(written[d, counts[d]:] == 0)
+        assert not np.isnan(win[d, :counts[d]]).any() and np.isnan(win[d, counts[d]:]).all()
+
+
+def test_gemm_a2a_routing_errors_rejected():
+    P, E, B, topk, tile_m, N, K = 2, 2, 4, 2, 2, 2, 2
+    off, dest, slot, counts, X, W = _moe(P, E, B, topk, tile_m, N, K, F32, seed=3)
+    cap = int(counts.max())
+    real = np.nonzero(dest >= 0)[0]
+    bad = slot.copy()
+    bad[real[1]] = slot[real[0]]
+    dup = dest.copy()
+    dup[real[1]] = dest[real[0]]
+    with pytest.raises(ValueError):                   # the same (dest, slot) twice
+        oracle.gemm_a2a(P, E, N, K, F32, F32, X, W, off, dup, bad, cap)
+    big = dest.copy()
+    big[real[0]] = P
+    with pytest.raises(ValueError):                   # a destination that does not exist
+        oracle.gemm_a2a(P, E, N, K, F32, F32, X, W, off, big, slot, cap)
 
 
 @pytest.mark.parametrize("slot_dt,out_dt", [(F32, BF16), (BF16, BF16)])
