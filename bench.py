@@ -12,6 +12,8 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
   embbag_a2a  64 tables 1e6x128 fp32, batch 16384, 20 rows per bag, Zipf(1.05), P=8
               (a 1 GiB scratch write between calls, outside the timed events)
   gemm_ar     GEMM+AllReduce, the gemm_rs shapes; the folded chunks land in all 8 windows
+  gemm_a2a    GEMM+All-to-All (MoE combine): 8 ranks x 4096 tokens, top-2 of 32 experts, this
+              rank's 4 experts 1792 -> 4096 bf16, each result row sent to its token's rank
   gemm_rs_unfused, gemv_ar_unfused  the gemm_rs / gemv_ar workloads as two kernels (the
               computation publishing its partials, then the fold): the bulk-synchronous
               baseline; `fusion` reports the time each fused operator saves against it
@@ -51,7 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)  # >= 200 timed calls of each operator
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
-    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a,gemm_ar,gemm_rs_unfused,gemv_ar_unfused")
+    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a,gemm_ar,gemm_a2a,gemm_rs_unfused,"
+                                     "gemv_ar_unfused")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
@@ -219,6 +222,24 @@ def main():
                                bound="mfma", peak=PEAK_BF16_TFLOPS, bytes=algo_bytes,
                                config=dict(workload=c.name, P=c.P, M=c.M, N=c.N, K=c.K,
                                            tile=[c.tile_m, c.tile_n], slot_dtype=args.slot_dtype))
+    if "gemm_a2a" in ops:
+        c = cfgs.GEMM_A2A_MOE
+        log(f"inputs {c.name}")
+        off, dest, slot, counts = gen.moe_routing(c.P, c.E, c.B, c.topk, c.tile_m, seed=0)
+        X, W = gen.gemm_a2a_inputs(c.E, int(off[-1]), c.N, c.K, dest, seed=0)
+        ga = bf.GemmA2A(c.P, c.E, c.N, c.K, bf.BF16, X, W, off, dest, slot, counts, c.cap)
+        rows = int(counts.sum())
+        del X, W
+        flops = 2.0 * rows * c.N * c.K                    # the routed rows (padding rows excluded)
+        algo_bytes = (2 * int(off[-1]) * c.K + 2 * c.E * c.K * c.N   # X, W read
+                      + 8 * int(off[-1])                            # dest, slot
+                      + 2 * rows * c.N)                             # result rows written
+        runs["gemm_a2a"] = dict(call=lambda r=ga: r.run(stream), obj=ga, work=flops, unit="TFLOP/s",
+                                variant=f"tile={c.tile_m}x{c.tile_n}", bound="mfma", peak=PEAK_BF16_TFLOPS,
+                                bytes=algo_bytes,
+                                config=dict(workload=c.name, P=c.P, E=c.E, B=c.B, topk=c.topk, N=c.N, K=c.K,
+                                            cap=c.cap, rows=rows, padded_rows=int(off[-1]),
+                                            tile=[c.tile_m, c.tile_n]))
     if "gemm_rs_unfused" in ops:
         # the baseline of the fused operator: the same GEMM, then a separate fold kernel
         c = cfgs.GEMM_RS_MLP

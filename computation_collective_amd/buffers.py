@@ -259,3 +259,34 @@ class EmbbagA2A(_Common):
 
     def run(self, stream=None, **kw):
         hocf.check(self.call(stream, **kw))
+
+
+class GemmA2A(_Common):
+    """hocf_gemm_a2a: X [T][K] grouped by expert (offsets), W [E][K][N], routing
+    dest/slot [T] -> windows [P][cap][N] with one flag word each."""
+
+    def __init__(self, P, E, N, K, out_dt, X, W, offsets, dest, slot, send_counts, cap, device="cuda"):
+        self.P, self.E, self.N, self.K, self.out_dt, self.cap = P, E, N, K, out_dt, cap
+        self.offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+        self.send_counts = np.ascontiguousarray(send_counts, dtype=np.int64)
+        self.T = int(self.offsets[-1])
+        self.X = X if isinstance(X, torch.Tensor) else to_device(X, device)
+        self.W = W if isinstance(W, torch.Tensor) else to_device(W, device)
+        self.dest = to_device(np.ascontiguousarray(dest, dtype=np.int32), device)
+        self.slot = to_device(np.ascontiguousarray(slot, dtype=np.int32), device)
+        self.win_data = torch.empty((P, cap, N), dtype=tdtype(out_dt), device=device)
+        self.win_flags = torch.zeros((P, 4), dtype=torch.int32, device=device)  # word 0 used; 16-byte rows
+        self.win = hocf.windows([(self.win_data[d], self.win_flags[d]) for d in range(P)])
+        self._alloc_sync(hocf.hocf_gemm_a2a_workspace_bytes(P), device)
+
+    def poison(self):
+        nan_fill(self.win_data)
+
+    def call(self, stream=None, **kw) -> int:
+        s = self.next_sync(**kw)
+        return hocf.hocf_gemm_a2a(self.P, self.E, self.T, self.N, self.K, BF16, self.out_dt, self.X, self.W,
+                                  self.offsets, self.dest, self.slot, self.send_counts, self.win, self.cap,
+                                  256, 256, s, stream)
+
+    def run(self, stream=None, **kw):
+        hocf.check(self.call(stream, **kw))

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhocf.so")
-SOURCES = ["abi.cpp", "gemm_rs.hip", "gemv_ar.hip", "ag_gemm.hip", "embbag_a2a.hip"]
+SOURCES = ["abi.cpp", "gemm_rs.hip", "gemv_ar.hip", "ag_gemm.hip", "embbag_a2a.hip", "gemm_a2a.hip"]
 ARCH = "gfx950"
 
 

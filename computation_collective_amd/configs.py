@@ -103,4 +103,26 @@ EMBBAG_DLRM = EmbbagA2A("embbag_a2a_t64_r1e6_d128_b16384_l20_p8", T=64, R=1_000_
 GEMM_AR_MLP = GemmRS("gemm_ar_mlpdown_p8_8192x4096x1792_bf16", P=8, M=8192, N=4096, K=1792,
                      in_dt=BF16, slot_dt=F32, out_dt=BF16, tile_m=256, tile_n=256)
 
+
+
+@dataclass(frozen=True)
+class GemmA2A:
+    name: str
+    P: int          # ranks
+    E: int          # experts per rank (P * E in all)
+    B: int          # tokens per rank
+    topk: int       # experts per token
+    N: int          # model width (output of the expert's down projection)
+    K: int          # expert hidden width
+    cap: int        # rows of each destination window
+    tile_m: int = 256
+    tile_n: int = 256
+
+
+# GEMM+All-to-All, the MoE combine: 8 ranks x 4096 tokens, top-2 of 32 experts;
+# this rank's 4 experts project 1792 -> 4096 and send each row to its token's rank
+# (about 1024 rows per destination; windows hold twice that).
+GEMM_A2A_MOE = GemmA2A("gemm_a2a_moe_p8_e4_b4096_top2_1792x4096_bf16", P=8, E=4, B=4096, topk=2,
+                       N=4096, K=1792, cap=2048)
+
 ALL = [GEMM_RS_TINY, GEMV_AR_DECODE, GEMM_RS_MLP, AG_GEMM_COL, EMBBAG_DLRM]

@@ -266,6 +266,81 @@ hocf_status hocf_gemm_ar(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtyp
                          sync, stream);
 }
 
+/* ------------------------------------------------------------ GEMM + A2A */
+
+size_t hocf_gemm_a2a_workspace_bytes(int P) {
+  if (P <= 0 || P > HOCF_MAX_P) return 0;
+  return (size_t)(hocf::kWsBaseWords + P) * 4;
+}
+
+hocf_status hocf_gemm_a2a(int P, int E, int64_t T, int N, int K, hocf_dtype in_dt, hocf_dtype out_dt,
+                          const void* X, const void* W, const int64_t* expert_offsets, const int32_t* dest,
+                          const int32_t* slot, const int64_t* send_counts, const hocf_window* win, int64_t cap,
+                          int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
+  if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: P=%d outside [1, %d]", P, HOCF_MAX_P);
+  if (E < 1 || E > hocf::kMaxExperts)
+    return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: E=%d outside [1, %d]", E, hocf::kMaxExperts);
+  if (T < 0 || N < 0 || K < 0 || cap < 0) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: negative size");
+  if (!dt_ok(in_dt) || !dt_ok(out_dt)) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: unknown dtype");
+  if (in_dt != HOCF_BF16) return fail(HOCF_ERR_UNSUPPORTED, "gemm_a2a: inputs must be bf16");
+  if (tile_m != 256 || tile_n != 256)
+    return fail(HOCF_ERR_UNSUPPORTED, "gemm_a2a: tile %dx%d (256x256 only)", tile_m, tile_n);
+  if (N % 256 || K % 128)
+    return fail(HOCF_ERR_UNSUPPORTED, "gemm_a2a: N=%d must be a multiple of 256 and K=%d of 128", N, K);
+  if ((int64_t)K * N * 2 >= ((int64_t)1 << 31) || ((int64_t)tile_m * K + K) * 2 >= ((int64_t)1 << 31))
+    return fail(HOCF_ERR_UNSUPPORTED, "gemm_a2a: an expert's W or a row tile exceeds 2 GiB");
+  if (!expert_offsets || !send_counts) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: NULL host array");
+  if (expert_offsets[0] != 0 || expert_offsets[E] != T)
+    return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: expert offsets must run from 0 to T=%lld", (long long)T);
+  const int ntiles = N / tile_n;
+  int64_t items = 0;
+  for (int e = 0; e < E; ++e) {
+    const int64_t n = expert_offsets[e + 1] - expert_offsets[e];
+    if (n < 0 || n % tile_m)
+      return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: expert %d has %lld rows (must be a non-negative multiple of %d)",
+                  e, (long long)n, tile_m);
+    items += n / tile_m * ntiles;
+  }
+  if (items >= ((int64_t)1 << 31)) return fail(HOCF_ERR_UNSUPPORTED, "gemm_a2a: too many tiles");
+  for (int d = 0; d < P; ++d)
+    if (send_counts[d] < 0 || send_counts[d] > cap || send_counts[d] * ntiles >= ((int64_t)1 << 32))
+      return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: send_counts[%d]=%lld outside [0, cap=%lld]", d,
+                  (long long)send_counts[d], (long long)cap);
+  hocf_status st = check_sync(sync, hocf_gemm_a2a_workspace_bytes(P));
+  if (st != HOCF_OK) return st;
+  if ((st = check_windows(win, P, "gemm_a2a")) != HOCF_OK) return st;
+  for (int d = 0; d < P; ++d)
+    if (!win[d].flags) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: window %d has no flag word", d);
+  if (T > 0 && N > 0) {
+    if (!X || !W || !dest || !slot) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: NULL tensor");
+    if (!aligned16(X) || !aligned16(W)) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: tensors must be 16-byte aligned");
+  }
+
+  hocf::SyncArgs sa;
+  if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
+  hocf::GemmA2aArgs a{};
+  a.X = static_cast<const uint16_t*>(X);
+  a.W = static_cast<const uint16_t*>(W);
+  a.dest = dest; a.slot = slot;
+  for (int d = 0; d < P; ++d) {
+    a.win_data[d] = win[d].data;
+    a.win_flags[d] = win[d].flags;
+    a.expected[d] = (uint32_t)(N > 0 ? send_counts[d] * ntiles : 0);
+  }
+  int64_t t = 0;
+  for (int e = 0; e <= E; ++e) {
+    a.row_off[e] = expert_offsets[e];
+    a.tile_off[e] = (int)t;
+    if (e < E) t += (expert_offsets[e + 1] - expert_offsets[e]) / tile_m * ntiles;
+  }
+  a.ws = static_cast<uint32_t*>(sync->workspace);
+  a.T = T; a.cap = cap;
+  a.P = P; a.E = E; a.N = N; a.K = K; a.ntiles = ntiles; a.out_dt = out_dt;
+  a.total = (int)items;
+  a.sync = sa;
+  return launched(hocf::launch_gemm_a2a(a, static_cast<hipStream_t>(stream)), "gemm_a2a");
+}
+
 /* ------------------------------------------------------------ GEMV + AR */
 
 size_t hocf_gemv_ar_workspace_bytes(int P, int N, int tile_n) {

@@ -1,0 +1,156 @@
+// GEMM + All-to-All (the mixture-of-experts combine), fused in one kernel.
+//
+// SC24 ("Optimizing Distributed ML Communication with Fused
+// Computation-Collective Operations", abstract) names GEMM + All-to-All, for
+// MoE layers, among its three fused prototypes: the expert GEMM's result
+// rows go back to the ranks their tokens came from as soon as a workgroup
+// has computed them, while other workgroups still compute.
+//
+// This rank holds E experts.  The token rows it received are grouped by
+// expert, each group padded to whole 256-row tiles (the block-aligned layout
+// of a grouped GEMM; padding rows carry dest = -1).  Work item = one 256x256
+// tile (expert e, row tile, column tile) of Y_e = X_e . W_e, computed with
+// the direct-to-LDS MFMA mainloop; items are dealt statically (every tile
+// costs the same).  The epilogue scatters the tile's rows: row i goes to
+// window dest[i], row slot[i] -- a data-dependent destination per row, so
+// each wave stages a 32-row block in LDS and stores it with per-lane 8-byte
+// device-coherent stores, each store instruction covering whole 128-byte
+// lines of one or two destination rows.  The workgroup counts the rows it
+// delivered per destination (in LDS), waits for its stores, and adds the
+// counts to one arrival counter per destination; the workgroup whose add
+// completes a destination's expected count (its send count x column tiles)
+// stores the epoch into that window's flag.  A destination that receives
+// nothing gets its flag from the last workgroup to finish.  Rows naming a
+// destination or slot out of range are skipped and reported
+// (HOCF_ERR_BAD_INDEX); their destination's flag is then never set.
+#include "internal.hpp"
+#include "mfma_tile.hpp"
+#include "publish.hpp"
+#include "sync.hpp"
+
+namespace hocf {
+
+// The tile's rows -> their destination windows.  Begins with a barrier (the
+// mainloop's last LDS reads are done) and uses the stage arrays for staging.
+template <class Tile, int ODT>
+__device__ __forceinline__ void scatter_rows(const GemmA2aArgs& a, int64_t row0, int col0,
+                                             const floatx16 (&acc)[Tile::FM][Tile::FN],
+                                             char* const (&stages)[4], uint32_t* s_cnt) {
+  using L = PublishLayout<Tile, ODT>;
+  constexpr int PPR = L::RB / 8;   // 8-byte pieces per staged row
+  constexpr int RPI = 64 / PPR;    // rows per store instruction
+  constexpr int NIT = 32 / RPI;    // store instructions per 32-row block
+  static_assert(64 % PPR == 0 && RPI >= 1, "scatter layout");
+  const int wave = threadIdx.x >> 6;
+  const int lane = opaque_lane();
+  const int wm = wave / Tile::WN, wn = wave % Tile::WN;
+  const int lr = lane & 31, half = lane >> 5;
+  const int sr = lane / PPR, pc = lane % PPR;  // staged row (within an instruction) and piece
+  const int tcol = col0 + wn * Tile::WTN + pc * (8 / L::ES);  // first output column of this lane
+  __syncthreads();
+  char* area = L::area(stages, wave);
+#pragma unroll
+  for (int i = 0; i < Tile::FM; ++i) {
+    // accumulator block row i -> staging rows 0..31 (row lr of this lane)
+#pragma unroll
+    for (int j = 0; j < Tile::FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * j + 8 * g + 4 * half;  // wave-local column
+        const int byte = col * L::ES;
+        char* p = area + L::at(lr, byte >> 4) + (byte & 15);
+        if constexpr (ODT == kBF16) {
+          *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                                               pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+        } else {
+          *reinterpret_cast<floatx4*>(p) =
+              floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        }
+      }
+    // staged rows -> their destinations; LDS operations of one wave complete
+    // in order, so no barrier is needed between the staging and the reads
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int r = it * RPI + sr;  // staged row
+      const u32x2 v = *reinterpret_cast<const u32x2*>(area + L::at(r, pc >> 1) + (pc & 1) * 8);
+      const int64_t g = row0 + wm * Tile::WTM + 32 * i + r;  // row of X
+      const int d = a.dest[g];
+      if (d < 0) continue;  // padding row
+      const int s = a.slot[g];
+      if (d >= a.P || s < 0 || s >= a.cap) {
+        if (pc == 0) report_status(a.sync, kErrBadIndex);
+        continue;
+      }
+      uint64_t* p = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(a.win_data[d]) +
+                                                ((int64_t)s * a.N + tcol) * L::ES);
+      // relaxed device-scope store: written through to the memory side (no L2-wide fence needed)
+      __hip_atomic_store(p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (pc == 0 && wn == 0) atomicAdd(&s_cnt[d], 1u);  // one piece per row and column tile
+    }
+  }
+}
+
+template <class Tile, int ODT>
+__global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem0[Tile::SMEM_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem1[Tile::NST > 1 ? Tile::SMEM_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char smem2[Tile::NST > 2 ? Tile::SMEM_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char smem3[Tile::NST > 3 ? Tile::SMEM_BYTES : 16];
+  char* const stages[4] = {smem0, smem1, smem2, smem3};
+  __shared__ uint32_t s_cnt[kMaxP];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  uint32_t* arrived = a.ws + kWsExtra;  // [P] pieces delivered per destination
+  if (tid < kMaxP) s_cnt[tid] = 0;
+
+  for (int item = blockIdx.x; item < a.total; item += gridDim.x) {
+    int e = 0;
+    while (e + 1 < a.E && item >= a.tile_off[e + 1]) ++e;
+    const int local = item - a.tile_off[e];
+    const int mt = local / a.ntiles, nt = local % a.ntiles;
+    const int64_t row0 = a.row_off[e] + (int64_t)mt * Tile::TM;
+    const uint16_t* At = a.X + row0 * a.K;
+    const uint16_t* Wt = a.W + (int64_t)e * a.K * a.N + (int64_t)nt * Tile::TN;
+    floatx16 acc[Tile::FM][Tile::FN];
+    Tile::template run<false>(At, a.K, Wt, a.N, Tile::TM, Tile::TN, a.K, stages, acc);
+    scatter_rows<Tile, ODT>(a, row0, nt * Tile::TN, acc, stages, s_cnt);
+    wait_memory();  // this thread's row stores have completed
+    __syncthreads();
+    if (tid < a.P) {
+      const uint32_t c = s_cnt[tid];
+      s_cnt[tid] = 0;  // (the next tile's counts start after the next scatter's first barrier)
+      if (c) {
+        const uint32_t prev = __hip_atomic_fetch_add(&arrived[tid], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev + c == a.expected[tid]) {
+          // every row this rank sends to destination tid is in its window
+          __hip_atomic_store(&arrived[tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&a.win_flags[tid][0], a.sync.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+
+  // the last workgroup out flags the destinations that receive no rows
+  if (finish_workgroup_last(a.ws, &s_last)) {
+    if (tid < a.P && a.expected[tid] == 0)
+      __hip_atomic_store(&a.win_flags[tid][0], a.sync.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <class Tile, int ODT>
+static hipError_t launch_k(const GemmA2aArgs& a, hipStream_t s) {
+  auto kern = &gemm_a2a_kernel<Tile, ODT>;
+  int grid = 0;
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), Tile::NT, a.total, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(Tile::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_a2a(const GemmA2aArgs& a, hipStream_t s) {
+  using Tile = TileBf16Direct<256, 256, 2, 2>;
+  return a.out_dt == kBF16 ? launch_k<Tile, kBF16>(a, s) : launch_k<Tile, kF32>(a, s);
+}
+
+}  // namespace hocf

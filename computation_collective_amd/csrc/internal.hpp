@@ -67,6 +67,25 @@ struct EmbbagArgs {
   SyncArgs sync;
 };
 
+constexpr int kMaxExperts = 64;  // local experts of one GEMM + All-to-All call
+
+struct GemmA2aArgs {
+  const uint16_t* X;     // [T][K] token rows, grouped by expert
+  const uint16_t* W;     // [E][K][N]
+  const int32_t* dest;   // [T] destination rank of each row (-1: padding)
+  const int32_t* slot;   // [T] row of the destination's window
+  void* win_data[kMaxP];       // [cap][N] out_dt each
+  uint32_t* win_flags[kMaxP];  // [1] each
+  uint32_t expected[kMaxP];    // pieces (row x column tile) each destination receives
+  int64_t row_off[kMaxExperts + 1];  // expert row ranges (whole row tiles)
+  int tile_off[kMaxExperts + 1];     // first work item of each expert
+  uint32_t* ws;
+  int64_t T, cap;
+  int P, E, N, K, ntiles, out_dt;
+  int total;  // work items: row tiles x column tiles over all experts
+  SyncArgs sync;
+};
+
 // Device properties the launches need, cached per device.
 struct DeviceInfo {
   int cus = 0;
@@ -83,6 +102,7 @@ hipError_t launch_gemm_rs(const GemmRsArgs& a, int tile_m, int tile_n, int in_dt
 hipError_t launch_gemv_ar(const GemvArArgs& a, hipStream_t s);
 hipError_t launch_ag_gemm(const AgGemmArgs& a, int tile_m, int tile_n, hipStream_t s);
 hipError_t launch_embbag_a2a(const EmbbagArgs& a, hipStream_t s);
+hipError_t launch_gemm_a2a(const GemmA2aArgs& a, hipStream_t s);
 
 // Workspace words each operator needs.
 constexpr int64_t kWsBaseWords = kNumQueues + 1;

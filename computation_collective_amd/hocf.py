@@ -34,6 +34,7 @@ EXPORTED = [
     "hocf_gemv_ar", "hocf_gemv_ar_workspace_bytes", "hocf_gemv_ar_unfused",
     "hocf_ag_gemm", "hocf_ag_gemm_workspace_bytes",
     "hocf_embbag_a2a", "hocf_embbag_a2a_workspace_bytes",
+    "hocf_gemm_a2a", "hocf_gemm_a2a_workspace_bytes",
     "hocf_status_string", "hocf_last_error", "hocf_abi_version",
 ]
 
@@ -80,11 +81,14 @@ def lib():
         L.hocf_ag_gemm_workspace_bytes.argtypes = [i]
         L.hocf_embbag_a2a.argtypes = [i, i64, i, i, i, i, vp, vp, vp, W, i, S, vp]
         L.hocf_embbag_a2a_workspace_bytes.argtypes = []
+        L.hocf_gemm_a2a.argtypes = [i, i, i64, i, i, i, i, vp, vp, vp, vp, vp, vp, W, i64, i, i, S, vp]
+        L.hocf_gemm_a2a_workspace_bytes.argtypes = [i]
         for f in ("hocf_gemm_rs", "hocf_gemm_rs_unfused", "hocf_gemm_ar", "hocf_gemv_ar", "hocf_gemv_ar_unfused", "hocf_ag_gemm",
-                  "hocf_embbag_a2a"):
+                  "hocf_embbag_a2a", "hocf_gemm_a2a"):
             getattr(L, f).restype = i
         for f in ("hocf_gemm_rs_workspace_bytes", "hocf_gemm_ar_workspace_bytes", "hocf_gemv_ar_workspace_bytes",
-                  "hocf_ag_gemm_workspace_bytes", "hocf_embbag_a2a_workspace_bytes"):
+                  "hocf_ag_gemm_workspace_bytes", "hocf_embbag_a2a_workspace_bytes",
+                  "hocf_gemm_a2a_workspace_bytes"):
             getattr(L, f).restype = sz
         L.hocf_status_string.argtypes = [i]
         L.hocf_status_string.restype = ctypes.c_char_p
@@ -220,6 +224,30 @@ def hocf_embbag_a2a(T, R, D, B, L, P, tables, indices, offsets, win, tile_bags, 
                                  tile_bags, ctypes.byref(sync_), _stream(stream))
 
 
+def hocf_gemm_a2a_workspace_bytes(P) -> int:
+    return lib().hocf_gemm_a2a_workspace_bytes(P)
+
+
+def _host_i64(a):
+    """A host int64 array for the call (kept alive by the caller's reference)."""
+    import numpy as np
+    if a is None:
+        return None
+    arr = np.ascontiguousarray(a, dtype=np.int64)
+    return arr
+
+
+def hocf_gemm_a2a(P, E, T, N, K, in_dt, out_dt, X, W, expert_offsets, dest, slot, send_counts, win, cap,
+                  tile_m, tile_n, sync_, stream=None) -> int:
+    """expert_offsets, send_counts: host int64 sequences; the rest device buffers."""
+    off = _host_i64(expert_offsets)
+    cnt = _host_i64(send_counts)
+    return lib().hocf_gemm_a2a(P, E, T, N, K, in_dt, out_dt, ptr(X), ptr(W),
+                               None if off is None else off.ctypes.data, ptr(dest), ptr(slot),
+                               None if cnt is None else cnt.ctypes.data, win, cap, tile_m, tile_n,
+                               ctypes.byref(sync_), _stream(stream))
+
+
 # --------------------------------------------------------------- chunk releasers
 # The AllGather side of hocf_ag_gemm.  On ROCm a stream write-value is a tiny
 # blit kernel, ordered with the rest of its stream; a release stream that
@@ -296,3 +324,4 @@ def release_chunks(stream, chunk_flags, order, epoch) -> None:
     base = ptr(chunk_flags)
     for c in order:
         stream_write_value32(stream, base + 4 * int(c), epoch)
+

@@ -44,7 +44,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30  # the calibration pass reads and writes 1 GiB
 
 # kernel-name fragment -> operator name used by bench.py
-KERNELS = [("gemm_rs_kernel", "gemm_rs"), ("gemm_ar_kernel", "gemm_ar"),
+KERNELS = [("gemm_rs_kernel", "gemm_rs"), ("gemm_ar_kernel", "gemm_ar"), ("gemm_a2a_kernel", "gemm_a2a"),
            ("unfused_gemm_kernel", "gemm_rs_unfused_gemm"), ("unfused_fold_kernel", "gemm_rs_unfused_fold"),
            ("unfused_gemv_kernel", "gemv_ar_unfused_gemv"), ("unfused_gemv_fold_kernel", "gemv_ar_unfused_fold"), ("gemv_ar_kernel", "gemv_ar"),
            ("ag_gemm_kernel", "ag_gemm"), ("embbag_kernel", "embbag_a2a"),
@@ -64,6 +64,7 @@ def workloads():
                                  f"tile_n={c.GEMV_AR_DECODE.tile_n} weight_replicas=4"),
         "gemv_ar_unfused_fold": (c.GEMV_AR_DECODE.name + "_unfused_fold",
                                  f"tile_n={c.GEMV_AR_DECODE.tile_n} weight_replicas=4"),
+        "gemm_a2a": (c.GEMM_A2A_MOE.name, f"tile={c.GEMM_A2A_MOE.tile_m}x{c.GEMM_A2A_MOE.tile_n}"),
         "gemm_ar": (c.GEMM_AR_MLP.name, f"slot_dtype=f32 tile={c.GEMM_AR_MLP.tile_m}x{c.GEMM_AR_MLP.tile_n}"),
         "gemv_ar": (c.GEMV_AR_DECODE.name, f"tile_n={c.GEMV_AR_DECODE.tile_n} weight_replicas=4"),
         "ag_gemm": (c.AG_GEMM_COL.name, f"tile={c.AG_GEMM_COL.tile_m}x{c.AG_GEMM_COL.tile_n} prereleased"),

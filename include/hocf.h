@@ -1,7 +1,7 @@
 /*
  * hocf — computations fused with their collective epilogue, on one MI355X.
  *
- * C ABI of libhocf.so.  Five operators, each one GPU's share of a P-way
+ * C ABI of libhocf.so.  Six operators, each one GPU's share of a P-way
  * tensor-parallel (or model-parallel) step with the P logical shards'
  * receive windows in local HBM:
  *
@@ -18,6 +18,7 @@
  *                    Operations", SC24, abstract)
  *   hocf_ag_gemm     AllGather + GEMM       (mKernel news item, same section)
  *   hocf_embbag_a2a  embedding bag + All-to-All (SC24 abstract)
+ *   hocf_gemm_a2a    GEMM + All-to-All, the MoE combine (SC24 abstract)
  *
  * The method (SC24 abstract; mKernel, section on persistent kernels and
  * tile/chunk overlap): the workgroups of one kernel each finish an output
@@ -259,6 +260,45 @@ hocf_status hocf_ag_gemm(int P, int Mc, int N, int K, hocf_dtype in_dt, hocf_dty
                          const void* A_gathered, const uint32_t* chunk_flags, const void* W,
                          void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream);
 size_t hocf_ag_gemm_workspace_bytes(int P);
+
+/* ------------------------------------------------------------------------
+ * GEMM + All-to-All (the mixture-of-experts combine).
+ *
+ * SC24 (abstract) names GEMM + All-to-All, for MoE layers, among its three
+ * fused prototypes.  This rank holds E experts and has received token rows
+ * grouped by expert: rows [expert_offsets[e], expert_offsets[e+1]) of X
+ * belong to expert e, each group a whole number of tile_m-row tiles (pad a
+ * group with rows whose dest is -1; their results go nowhere).  Every row i
+ * is multiplied by its expert's W_e (fp32 accumulation, rounded once to
+ * out_dt) and the result row is sent back to its token's rank: it lands in
+ * win[dest[i]].data at row slot[i].  Tiles are scattered by the workgroup
+ * that computed them while other workgroups still compute; win[d].flags[0]
+ * becomes epoch once all send_counts[d] rows for destination d are there
+ * (immediately, at the end of the kernel, when send_counts[d] == 0).
+ *
+ *   X              [T][K] in_dt (device)
+ *   W              [E][K][N] in_dt (device)
+ *   expert_offsets host int64 [E+1]: 0 = o_0 <= o_1 <= ... <= o_E = T, each
+ *                  o_{e+1} - o_e a multiple of tile_m (read during the call)
+ *   dest, slot     device int32 [T]: destination rank in [0, P) (or -1:
+ *                  padding) and row in [0, cap) of each row; every (dest,
+ *                  slot) pair at most once
+ *   send_counts    host int64 [P]: rows with dest == d (read during the call);
+ *                  each in [0, cap]
+ *   win            host array of P windows; win[d].data = [cap][N] out_dt,
+ *                  win[d].flags = [1]
+ *
+ * Supported: in BF16, out BF16 or F32; tile 256x256; N a multiple of 256,
+ * K of 128; 1 <= E <= 64.  A row naming a destination or slot out of range
+ * is skipped and HOCF_ERR_BAD_INDEX goes to the status word (that
+ * destination's flag is then not set).  Rows of the windows that no row
+ * names are left as they were.
+ * ---------------------------------------------------------------------- */
+hocf_status hocf_gemm_a2a(int P, int E, int64_t T, int N, int K, hocf_dtype in_dt, hocf_dtype out_dt,
+                          const void* X, const void* W, const int64_t* expert_offsets, const int32_t* dest,
+                          const int32_t* slot, const int64_t* send_counts, const hocf_window* win,
+                          int64_t cap, int tile_m, int tile_n, const hocf_sync* sync, void* stream);
+size_t hocf_gemm_a2a_workspace_bytes(int P);
 
 /* ------------------------------------------------------------------------
  * Embedding bag + All-to-All.

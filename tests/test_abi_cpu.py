@@ -175,6 +175,33 @@ def test_embbag_rejects(kw, expect):
     assert st == expect
 
 
+def _a2a(P=2, E=2, T=512, N=256, K=256, off=(0, 256, 512), counts=(3, 4), cap=8, tile=(256, 256),
+         in_dt=BF16, win=True, X=FAKE):
+    return hocf.hocf_gemm_a2a(P, E, T, N, K, in_dt, BF16, X, FAKE, off, FAKE, FAKE, counts,
+                              _win(P) if win else None, cap, *tile, _sync())
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(P=0, counts=()), INVALID), (dict(E=0, off=(0,)), INVALID), (dict(E=65, off=(0,) * 66), INVALID),
+    (dict(in_dt=F32), UNSUPPORTED), (dict(tile=(128, 128)), UNSUPPORTED), (dict(N=200), UNSUPPORTED),
+    (dict(K=100), UNSUPPORTED), (dict(off=(0, 200, 512)), INVALID), (dict(off=(0, 256, 256)), INVALID),
+    (dict(off=(0, 512, 256)), INVALID), (dict(counts=(3, 9)), INVALID), (dict(counts=(-1, 4)), INVALID),
+    (dict(off=None), INVALID), (dict(counts=None), INVALID), (dict(win=False), INVALID),
+    (dict(X=0), INVALID), (dict(X=FAKE + 8), INVALID),
+])
+def test_gemm_a2a_rejects(kw, expect):
+    assert _a2a(**kw) == expect
+    assert hocf.last_error()
+
+
+def test_gemm_a2a_valid_reaches_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    assert _a2a() == HIP
+    assert hocf.hocf_gemm_a2a_workspace_bytes(8) == (8 + 1 + 8) * 4
+
+
 def test_null_sync_rejected():
     L = hocf.lib()
     st = L.hocf_gemm_rs(4, 256, 256, 256, F32, F32, F32, FAKE, FAKE, _win(4), FAKE, 64, 64, None, None)

@@ -588,6 +588,139 @@ def test_gemv_ar_unfused_integer_bit_exact():
     np.testing.assert_array_equal(bf.to_host(u.part, F32), part)
 
 
+# ====================================================================== GEMM + A2A
+
+def _moe_case(P, E, B, topk, N, K, seed, dist_x=("normal", 1.0), dist_w=("normal", 0.02)):
+    off, dest, slot, counts = gen.moe_routing(P, E, B, topk, 256, seed=seed)
+    X, W = gen.gemm_a2a_inputs(E, int(off[-1]), N, K, dest, seed=seed, dist_x=dist_x, dist_w=dist_w)
+    return off, dest, slot, counts, X, W
+
+
+def _check_a2a(run, want, counts):
+    """Rows [0, send_count) of every window hold the oracle's rows; the rest
+    was never written (still NaN); every window's flag carries the epoch."""
+    got = bf.to_host(run.win_data, run.out_dt)
+    for d in range(run.P):
+        c = int(counts[d])
+        g = val(got[d, :c], run.out_dt)
+        assert not np.isnan(g).any(), f"window {d}: unwritten rows"
+        if c:
+            assert relerr(g, val(want[d, :c], run.out_dt)) <= TOL[BF16]
+        assert np.isnan(val(got[d, c:], run.out_dt)).all(), f"window {d}: rows past its count written"
+    assert torch.all(run.win_flags[:, 0] == run.epoch)
+    assert torch.all(run.ws == 0)
+
+
+@pytest.mark.parametrize("P,E,B,topk,N,K,odt", [
+    (4, 3, 96, 2, 512, 256, BF16), (8, 4, 256, 2, 768, 384, F32), (2, 1, 200, 1, 256, 128, BF16),
+    (16, 2, 64, 4, 512, 256, BF16),
+])
+def test_gemm_a2a_values(P, E, B, topk, N, K, odt):
+    say(f"gemm_a2a P={P} E={E} B={B} top{topk} N={N} K={K} out={odt}")
+    off, dest, slot, counts, X, W = _moe_case(P, E, B, topk, N, K, seed=P + E + B)
+    cap = int(counts.max()) + 8
+    run = bf.GemmA2A(P, E, N, K, odt, X, W, off, dest, slot, counts, cap)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    want = oracle.gemm_a2a(P, E, N, K, BF16, odt, X, W, off, dest, slot, cap)
+    _check_a2a(run, want, counts)
+
+
+def test_gemm_a2a_integer_bit_exact_and_repeatable():
+    """Integer-valued operands: every row is exact, so the windows equal the
+    oracle bit for bit; a second call (new epoch) gives the same bits and
+    sets the flags again."""
+    P, E, B, topk, N, K = 8, 4, 512, 2, 512, 512
+    say(f"gemm_a2a integer P={P} E={E} B={B} N={N} K={K}")
+    off, dest, slot, counts, X, W = _moe_case(P, E, B, topk, N, K, seed=21, dist_x=("int", -2, 2),
+                                              dist_w=("int", -2, 2))
+    cap = int(counts.max())
+    run = bf.GemmA2A(P, E, N, K, F32, X, W, off, dest, slot, counts, cap)
+    want = oracle.gemm_a2a(P, E, N, K, BF16, F32, X, W, off, dest, slot, cap)
+    for call in range(2):
+        run.poison()
+        run.run()
+        sync()
+        assert run.status_value() == 0
+        got = bf.to_host(run.win_data, F32)
+        for d in range(P):
+            np.testing.assert_array_equal(got[d, :counts[d]], want[d, :counts[d]], err_msg=f"call {call}")
+        assert torch.all(run.win_flags[:, 0] == run.epoch)
+
+
+def test_gemm_a2a_empty_destination_and_small_grid(monkeypatch):
+    """A destination that receives no rows still gets its flag; a grid of a
+    few workgroups takes many tiles each."""
+    monkeypatch.setenv("HOCF_MAX_WORKGROUPS", "3")
+    P, E, N, K = 3, 2, 512, 256
+    say(f"gemm_a2a empty destination P={P} E={E} grid<=3")
+    rng = np.random.default_rng(4)
+    n0, n1 = 300, 140                                # real rows of expert 0 and 1
+    off = np.array([0, 512, 768], dtype=np.int64)      # padded to whole 256-row tiles
+    dest = np.full(768, -1, dtype=np.int32)
+    slot = np.full(768, -1, dtype=np.int32)
+    d_real = rng.integers(0, 2, n0 + n1).astype(np.int32)   # destinations 0 and 1 only
+    rows = np.concatenate([np.arange(n0), 512 + np.arange(n1)])
+    dest[rows] = d_real
+    counts = np.bincount(d_real, minlength=P).astype(np.int64)
+    for d in range(P):
+        m = rows[d_real == d]
+        slot[m] = rng.permutation(int(counts[d])).astype(np.int32)
+    X, W = gen.gemm_a2a_inputs(E, 768, N, K, dest, seed=4)
+    cap = int(counts.max())
+    run = bf.GemmA2A(P, E, N, K, BF16, X, W, off, dest, slot, counts, cap)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0 and counts[2] == 0
+    want = oracle.gemm_a2a(P, E, N, K, BF16, BF16, X, W, off, dest, slot, cap)
+    _check_a2a(run, want, counts)
+
+
+def test_gemm_a2a_bad_slot_reported_and_skipped():
+    P, E, B, topk, N, K = 4, 2, 128, 2, 256, 256
+    say(f"gemm_a2a bad slot P={P} E={E} B={B}")
+    off, dest, slot, counts, X, W = _moe_case(P, E, B, topk, N, K, seed=8)
+    cap = int(counts.max())
+    real = np.nonzero(dest >= 0)[0]
+    bad = slot.copy()
+    victim = int(real[5])
+    bad[victim] = cap + 3                       # outside the window: skipped and reported
+    run = bf.GemmA2A(P, E, N, K, BF16, X, W, off, dest, bad, counts, cap)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == hocf.HOCF_ERR_BAD_INDEX
+    want = oracle.gemm_a2a(P, E, N, K, BF16, BF16, X, W, off, dest, slot, cap)
+    got = bf.to_host(run.win_data, BF16)
+    d_v, s_v = int(dest[victim]), int(slot[victim])
+    ok = np.ones(cap, dtype=bool)
+    ok[s_v] = False
+    assert np.isnan(val(got[d_v, s_v], BF16)).all()           # the skipped row was not written
+    for d in range(P):
+        rows_ok = np.arange(int(counts[d])) if d != d_v else np.nonzero(ok[:counts[d]])[0]
+        assert relerr(val(got[d, rows_ok], BF16), val(want[d, rows_ok], BF16)) <= TOL[BF16]
+    assert int(run.win_flags[d_v, 0]) != run.epoch                # its destination is incomplete
+
+
+def test_gemm_a2a_full_moe():
+    """The MoE combine workload: 8 ranks x 4096 tokens, top-2 of 32 experts,
+    this rank's 4 experts (K=1792 -> N=4096): every window row against the
+    oracle."""
+    c = cfgs.GEMM_A2A_MOE
+    say(f"gemm_a2a full {c.name}")
+    off, dest, slot, counts, X, W = _moe_case(c.P, c.E, c.B, c.topk, c.N, c.K, seed=0)
+    run = bf.GemmA2A(c.P, c.E, c.N, c.K, BF16, X, W, off, dest, slot, counts, c.cap)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    want = oracle.gemm_a2a(c.P, c.E, c.N, c.K, BF16, BF16, X, W, off, dest, slot, c.cap)
+    _check_a2a(run, want, counts)
+
+
 # ====================================================================== AG + GEMM
 
 def _ag_inputs(P, Mc, N, K, seed=0):
