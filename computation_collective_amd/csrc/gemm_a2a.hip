@@ -31,11 +31,16 @@
 namespace hocf {
 
 // The tile's rows -> their destination windows.  Begins with a barrier (the
-// mainloop's last LDS reads are done) and uses the stage arrays for staging.
+// mainloop's last LDS reads are done) and uses the stage arrays for staging;
+// s_route[r] holds tile row r's (dest, slot), loaded before the mainloop, and
+// s_win the P window bases (so that the store loop waits on nothing but LDS:
+// a per-lane read of the kernel's argument array would be a global load, and
+// its wait would also wait for every store issued before it).
 template <class Tile, int ODT>
-__device__ __forceinline__ void scatter_rows(const GemmA2aArgs& a, int64_t row0, int col0,
+__device__ __forceinline__ void scatter_rows(const GemmA2aArgs& a, int col0,
                                              const floatx16 (&acc)[Tile::FM][Tile::FN],
-                                             char* const (&stages)[4], uint32_t* s_cnt) {
+                                             char* const (&stages)[4], const int2* s_route, const uint64_t* s_win,
+                                             uint32_t* s_cnt) {
   using L = PublishLayout<Tile, ODT>;
   constexpr int PPR = L::RB / 8;   // 8-byte pieces per staged row
   constexpr int RPI = 64 / PPR;    // rows per store instruction
@@ -73,16 +78,16 @@ __device__ __forceinline__ void scatter_rows(const GemmA2aArgs& a, int64_t row0,
     for (int it = 0; it < NIT; ++it) {
       const int r = it * RPI + sr;  // staged row
       const u32x2 v = *reinterpret_cast<const u32x2*>(area + L::at(r, pc >> 1) + (pc & 1) * 8);
-      const int64_t g = row0 + wm * Tile::WTM + 32 * i + r;  // row of X
-      const int d = a.dest[g];
+      const int2 route = s_route[wm * Tile::WTM + 32 * i + r];
+      const int d = route.x, s = route.y;
       if (d < 0) continue;  // padding row
-      const int s = a.slot[g];
       if (d >= a.P || s < 0 || s >= a.cap) {
         if (pc == 0) report_status(a.sync, kErrBadIndex);
         continue;
       }
-      uint64_t* p = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(a.win_data[d]) +
-                                                ((int64_t)s * a.N + tcol) * L::ES);
+      // a global (not flat) address: a flat store would also count against the LDS counter
+      typedef __attribute__((address_space(1))) uint64_t gu64;
+      gu64* p = (gu64*)(s_win[d] + (uint64_t)(((int64_t)s * a.N + tcol) * L::ES));
       // relaxed device-scope store: written through to the memory side (no L2-wide fence needed)
       __hip_atomic_store(p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (pc == 0 && wn == 0) atomicAdd(&s_cnt[d], 1u);  // one piece per row and column tile
@@ -98,11 +103,15 @@ __global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem3[Tile::NST > 3 ? Tile::SMEM_BYTES : 16];
   char* const stages[4] = {smem0, smem1, smem2, smem3};
   __shared__ uint32_t s_cnt[kMaxP];
+  __shared__ int2 s_route[Tile::TM];  // (dest, slot) of the current tile's rows
+  __shared__ uint64_t s_win[kMaxP];    // window bases
   __shared__ int s_last;
+  static_assert(Tile::NT >= Tile::TM, "one thread per tile row loads its route");
 
   const int tid = threadIdx.x;
   uint32_t* arrived = a.ws + kWsExtra;  // [P] pieces delivered per destination
   if (tid < kMaxP) s_cnt[tid] = 0;
+  if (tid < a.P) s_win[tid] = reinterpret_cast<uint64_t>(a.win_data[tid]);  // (read after the scatter's barrier)
 
   for (int item = blockIdx.x; item < a.total; item += gridDim.x) {
     int e = 0;
@@ -112,9 +121,14 @@ __global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
     const int64_t row0 = a.row_off[e] + (int64_t)mt * Tile::TM;
     const uint16_t* At = a.X + row0 * a.K;
     const uint16_t* Wt = a.W + (int64_t)e * a.K * a.N + (int64_t)nt * Tile::TN;
+    // the rows' routes, loaded now so that their latency hides behind the mainloop
+    int2 route = {-1, -1};
+    if (tid < Tile::TM) route = int2{a.dest[row0 + tid], a.slot[row0 + tid]};
     floatx16 acc[Tile::FM][Tile::FN];
     Tile::template run<false>(At, a.K, Wt, a.N, Tile::TM, Tile::TN, a.K, stages, acc);
-    scatter_rows<Tile, ODT>(a, row0, nt * Tile::TN, acc, stages, s_cnt);
+    // (the previous tile's scatter read s_route before the barrier that ended it)
+    if (tid < Tile::TM) s_route[tid] = route;
+    scatter_rows<Tile, ODT>(a, nt * Tile::TN, acc, stages, s_route, s_win, s_cnt);
     wait_memory();  // this thread's row stores have completed
     __syncthreads();
     if (tid < a.P) {
