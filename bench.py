@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a,gemm_ar,gemm_a2a,gemm_rs_unfused,"
                                      "gemv_ar_unfused")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
+    ap.add_argument("--a2a-tile-m", type=int, default=0, help="GEMM+A2A tile rows (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     return ap.parse_args()
@@ -225,9 +226,10 @@ def main():
     if "gemm_a2a" in ops:
         c = cfgs.GEMM_A2A_MOE
         log(f"inputs {c.name}")
-        off, dest, slot, counts = gen.moe_routing(c.P, c.E, c.B, c.topk, c.tile_m, seed=0)
+        atm = args.a2a_tile_m or c.tile_m
+        off, dest, slot, counts = gen.moe_routing(c.P, c.E, c.B, c.topk, atm, seed=0)
         X, W = gen.gemm_a2a_inputs(c.E, int(off[-1]), c.N, c.K, dest, seed=0)
-        ga = bf.GemmA2A(c.P, c.E, c.N, c.K, bf.BF16, X, W, off, dest, slot, counts, c.cap)
+        ga = bf.GemmA2A(c.P, c.E, c.N, c.K, bf.BF16, X, W, off, dest, slot, counts, c.cap, tile_m=atm)
         rows = int(counts.sum())
         del X, W
         flops = 2.0 * rows * c.N * c.K                    # the routed rows (padding rows excluded)
@@ -235,11 +237,11 @@ def main():
                       + 8 * int(off[-1])                            # dest, slot
                       + 2 * rows * c.N)                             # result rows written
         runs["gemm_a2a"] = dict(call=lambda r=ga: r.run(stream), obj=ga, work=flops, unit="TFLOP/s",
-                                variant=f"tile={c.tile_m}x{c.tile_n}", bound="mfma", peak=PEAK_BF16_TFLOPS,
+                                variant=f"tile={atm}x{c.tile_n}", bound="mfma", peak=PEAK_BF16_TFLOPS,
                                 bytes=algo_bytes,
                                 config=dict(workload=c.name, P=c.P, E=c.E, B=c.B, topk=c.topk, N=c.N, K=c.K,
                                             cap=c.cap, rows=rows, padded_rows=int(off[-1]),
-                                            tile=[c.tile_m, c.tile_n]))
+                                            tile=[atm, c.tile_n]))
     if "gemm_rs_unfused" in ops:
         # the baseline of the fused operator: the same GEMM, then a separate fold kernel
         c = cfgs.GEMM_RS_MLP

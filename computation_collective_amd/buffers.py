@@ -265,8 +265,10 @@ class GemmA2A(_Common):
     """hocf_gemm_a2a: X [T][K] grouped by expert (offsets), W [E][K][N], routing
     dest/slot [T] -> windows [P][cap][N] with one flag word each."""
 
-    def __init__(self, P, E, N, K, out_dt, X, W, offsets, dest, slot, send_counts, cap, device="cuda"):
+    def __init__(self, P, E, N, K, out_dt, X, W, offsets, dest, slot, send_counts, cap, device="cuda",
+                 tile_m=256):
         self.P, self.E, self.N, self.K, self.out_dt, self.cap = P, E, N, K, out_dt, cap
+        self.tile_m = tile_m
         self.offsets = np.ascontiguousarray(offsets, dtype=np.int64)
         self.send_counts = np.ascontiguousarray(send_counts, dtype=np.int64)
         self.T = int(self.offsets[-1])
@@ -286,7 +288,7 @@ class GemmA2A(_Common):
         s = self.next_sync(**kw)
         return hocf.hocf_gemm_a2a(self.P, self.E, self.T, self.N, self.K, BF16, self.out_dt, self.X, self.W,
                                   self.offsets, self.dest, self.slot, self.send_counts, self.win, self.cap,
-                                  256, 256, s, stream)
+                                  self.tile_m, 256, s, stream)
 
     def run(self, stream=None, **kw):
         hocf.check(self.call(stream, **kw))

@@ -283,8 +283,10 @@ hocf_status hocf_gemm_a2a(int P, int E, int64_t T, int N, int K, hocf_dtype in_d
   if (T < 0 || N < 0 || K < 0 || cap < 0) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: negative size");
   if (!dt_ok(in_dt) || !dt_ok(out_dt)) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: unknown dtype");
   if (in_dt != HOCF_BF16) return fail(HOCF_ERR_UNSUPPORTED, "gemm_a2a: inputs must be bf16");
-  if (tile_m != 256 || tile_n != 256)
-    return fail(HOCF_ERR_UNSUPPORTED, "gemm_a2a: tile %dx%d (256x256 only)", tile_m, tile_n);
+  if ((tile_m != 256 && tile_m != 128) || tile_n != 256)
+    return fail(HOCF_ERR_UNSUPPORTED, "gemm_a2a: tile %dx%d (256x256 or 128x256 only)", tile_m, tile_n);
+  if (tile_m == 128 && out_dt != HOCF_BF16)
+    return fail(HOCF_ERR_UNSUPPORTED, "gemm_a2a: 128-row tiles take bf16 output only");
   if (N % 256 || K % 128)
     return fail(HOCF_ERR_UNSUPPORTED, "gemm_a2a: N=%d must be a multiple of 256 and K=%d of 128", N, K);
   if ((int64_t)K * N * 2 >= ((int64_t)1 << 31) || ((int64_t)tile_m * K + K) * 2 >= ((int64_t)1 << 31))
@@ -338,7 +340,7 @@ hocf_status hocf_gemm_a2a(int P, int E, int64_t T, int N, int K, hocf_dtype in_d
   a.P = P; a.E = E; a.N = N; a.K = K; a.ntiles = ntiles; a.out_dt = out_dt;
   a.total = (int)items;
   a.sync = sa;
-  return launched(hocf::launch_gemm_a2a(a, static_cast<hipStream_t>(stream)), "gemm_a2a");
+  return launched(hocf::launch_gemm_a2a(a, tile_m, static_cast<hipStream_t>(stream)), "gemm_a2a");
 }
 
 /* ------------------------------------------------------------ GEMV + AR */

@@ -7,9 +7,10 @@
 // has computed them, while other workgroups still compute.
 //
 // This rank holds E experts.  The token rows it received are grouped by
-// expert, each group padded to whole 256-row tiles (the block-aligned layout
-// of a grouped GEMM; padding rows carry dest = -1).  Work item = one 256x256
-// tile (expert e, row tile, column tile) of Y_e = X_e . W_e, computed with
+// expert, each group padded to whole tiles of tile_m rows (the block-aligned
+// layout of a grouped GEMM; padding rows carry dest = -1).  Work item = one
+// tile_m x 256 tile (expert e, row tile, column tile) of Y_e = X_e . W_e
+// (tile_m = 256 or 128), computed with
 // the direct-to-LDS MFMA mainloop; items are dealt statically (every tile
 // costs the same).  The epilogue scatters the tile's rows: row i goes to
 // window dest[i], row slot[i] -- a data-dependent destination per row, so
@@ -162,9 +163,16 @@ static hipError_t launch_k(const GemmA2aArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_a2a(const GemmA2aArgs& a, hipStream_t s) {
-  using Tile = TileBf16Direct<256, 256, 2, 2>;
+template <class Tile>
+static hipError_t launch_tile(const GemmA2aArgs& a, hipStream_t s) {
   return a.out_dt == kBF16 ? launch_k<Tile, kBF16>(a, s) : launch_k<Tile, kF32>(a, s);
+}
+
+hipError_t launch_gemm_a2a(const GemmA2aArgs& a, int tile_m, hipStream_t s) {
+  if (tile_m == 256) return launch_tile<TileBf16Direct<256, 256, 2, 2>>(a, s);
+  // (128-row tiles: bf16 output only -- an fp32 staging row block does not fit their stage arrays)
+  if (tile_m == 128 && a.out_dt == kBF16) return launch_k<TileBf16Direct<128, 256, 2, 2>, kBF16>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace hocf

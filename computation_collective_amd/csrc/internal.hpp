@@ -102,7 +102,7 @@ hipError_t launch_gemm_rs(const GemmRsArgs& a, int tile_m, int tile_n, int in_dt
 hipError_t launch_gemv_ar(const GemvArArgs& a, hipStream_t s);
 hipError_t launch_ag_gemm(const AgGemmArgs& a, int tile_m, int tile_n, hipStream_t s);
 hipError_t launch_embbag_a2a(const EmbbagArgs& a, hipStream_t s);
-hipError_t launch_gemm_a2a(const GemmA2aArgs& a, hipStream_t s);
+hipError_t launch_gemm_a2a(const GemmA2aArgs& a, int tile_m, hipStream_t s);
 
 // Workspace words each operator needs.
 constexpr int64_t kWsBaseWords = kNumQueues + 1;

@@ -288,8 +288,8 @@ size_t hocf_ag_gemm_workspace_bytes(int P);
  *   win            host array of P windows; win[d].data = [cap][N] out_dt,
  *                  win[d].flags = [1]
  *
- * Supported: in BF16, out BF16 or F32; tile 256x256; N a multiple of 256,
- * K of 128; 1 <= E <= 64.  A row naming a destination or slot out of range
+ * Supported: in BF16; tile 256x256 with out BF16 or F32, tile 128x256 with
+ * out BF16; N a multiple of 256, K of 128; 1 <= E <= 64.  A row naming a destination or slot out of range
  * is skipped and HOCF_ERR_BAD_INDEX goes to the status word (that
  * destination's flag is then not set).  Rows of the windows that no row
  * names are left as they were.

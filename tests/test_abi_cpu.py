@@ -176,14 +176,15 @@ def test_embbag_rejects(kw, expect):
 
 
 def _a2a(P=2, E=2, T=512, N=256, K=256, off=(0, 256, 512), counts=(3, 4), cap=8, tile=(256, 256),
-         in_dt=BF16, win=True, X=FAKE):
-    return hocf.hocf_gemm_a2a(P, E, T, N, K, in_dt, BF16, X, FAKE, off, FAKE, FAKE, counts,
+         in_dt=BF16, out_dt=BF16, win=True, X=FAKE):
+    return hocf.hocf_gemm_a2a(P, E, T, N, K, in_dt, out_dt, X, FAKE, off, FAKE, FAKE, counts,
                               _win(P) if win else None, cap, *tile, _sync())
 
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(P=0, counts=()), INVALID), (dict(E=0, off=(0,)), INVALID), (dict(E=65, off=(0,) * 66), INVALID),
-    (dict(in_dt=F32), UNSUPPORTED), (dict(tile=(128, 128)), UNSUPPORTED), (dict(N=200), UNSUPPORTED),
+    (dict(in_dt=F32), UNSUPPORTED), (dict(tile=(128, 128)), UNSUPPORTED), (dict(tile=(64, 256)), UNSUPPORTED),
+    (dict(tile=(128, 256), off=(0, 128, 500)), INVALID), (dict(tile=(128, 256), out_dt=F32), UNSUPPORTED), (dict(N=200), UNSUPPORTED),
     (dict(K=100), UNSUPPORTED), (dict(off=(0, 200, 512)), INVALID), (dict(off=(0, 256, 256)), INVALID),
     (dict(off=(0, 512, 256)), INVALID), (dict(counts=(3, 9)), INVALID), (dict(counts=(-1, 4)), INVALID),
     (dict(off=None), INVALID), (dict(counts=None), INVALID), (dict(win=False), INVALID),

@@ -590,8 +590,8 @@ def test_gemv_ar_unfused_integer_bit_exact():
 
 # ====================================================================== GEMM + A2A
 
-def _moe_case(P, E, B, topk, N, K, seed, dist_x=("normal", 1.0), dist_w=("normal", 0.02)):
-    off, dest, slot, counts = gen.moe_routing(P, E, B, topk, 256, seed=seed)
+def _moe_case(P, E, B, topk, N, K, seed, dist_x=("normal", 1.0), dist_w=("normal", 0.02), tile_m=256):
+    off, dest, slot, counts = gen.moe_routing(P, E, B, topk, tile_m, seed=seed)
     X, W = gen.gemm_a2a_inputs(E, int(off[-1]), N, K, dest, seed=seed, dist_x=dist_x, dist_w=dist_w)
     return off, dest, slot, counts, X, W
 
@@ -626,6 +626,27 @@ def test_gemm_a2a_values(P, E, B, topk, N, K, odt):
     assert run.status_value() == 0
     want = oracle.gemm_a2a(P, E, N, K, BF16, odt, X, W, off, dest, slot, cap)
     _check_a2a(run, want, counts)
+
+
+@pytest.mark.parametrize("tile_m", [128, 256])
+def test_gemm_a2a_tile_rows_integer_bit_exact(tile_m):
+    """Both row-tile heights (groups padded to 128 or 256 rows) give the
+    oracle's bits on integer-valued operands."""
+    P, E, B, topk, N, K = 8, 3, 300, 2, 512, 384
+    say(f"gemm_a2a tile_m={tile_m} integer P={P} E={E} B={B}")
+    off, dest, slot, counts, X, W = _moe_case(P, E, B, topk, N, K, seed=31 + tile_m, dist_x=("int", -2, 2),
+                                              dist_w=("int", -2, 2), tile_m=tile_m)
+    cap = int(counts.max())
+    run = bf.GemmA2A(P, E, N, K, BF16, X, W, off, dest, slot, counts, cap, tile_m=tile_m)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    want = oracle.gemm_a2a(P, E, N, K, BF16, BF16, X, W, off, dest, slot, cap)
+    got = bf.to_host(run.win_data, BF16)
+    for d in range(P):
+        np.testing.assert_array_equal(got[d, :counts[d]], want[d, :counts[d]])
+    assert torch.all(run.win_flags[:, 0] == run.epoch)
 
 
 def test_gemm_a2a_integer_bit_exact_and_repeatable():
@@ -710,9 +731,9 @@ def test_gemm_a2a_full_moe():
     this rank's 4 experts (K=1792 -> N=4096): every window row against the
     oracle."""
     c = cfgs.GEMM_A2A_MOE
-    say(f"gemm_a2a full {c.name}")
-    off, dest, slot, counts, X, W = _moe_case(c.P, c.E, c.B, c.topk, c.N, c.K, seed=0)
-    run = bf.GemmA2A(c.P, c.E, c.N, c.K, BF16, X, W, off, dest, slot, counts, c.cap)
+    say(f"gemm_a2a full {c.name} tile {c.tile_m}x{c.tile_n}")
+    off, dest, slot, counts, X, W = _moe_case(c.P, c.E, c.B, c.topk, c.N, c.K, seed=0, tile_m=c.tile_m)
+    run = bf.GemmA2A(c.P, c.E, c.N, c.K, BF16, X, W, off, dest, slot, counts, c.cap, tile_m=c.tile_m)
     run.poison()
     run.run()
     sync()
