@@ -726,6 +726,49 @@ def test_gemm_a2a_bad_slot_reported_and_skipped():
     assert int(run.win_flags[d_v, 0]) != run.epoch                # its destination is incomplete
 
 
+def test_gemm_a2a_expert_without_rows_and_no_rows_at_all():
+    """An expert that received no token (an empty group) is skipped; a call
+    with no rows at all still sets every destination's flag and writes
+    nothing."""
+    P, E, N, K = 4, 3, 256, 256
+    say("gemm_a2a empty expert group, then T = 0")
+    off, dest, slot, counts = gen.moe_routing(P, 2, 64, 2, 128, seed=6)   # experts 0, 1 ...
+    off = np.concatenate([off[:2], off[1:2], off[2:]])                      # ... and an empty expert 1
+    X, W = gen.gemm_a2a_inputs(E, int(off[-1]), N, K, dest, seed=6)
+    # routing generated for 2 experts: expert 1's rows now belong to expert 2 (its W differs)
+    cap = int(counts.max())
+    run = bf.GemmA2A(P, E, N, K, BF16, X, W, off, dest, slot, counts, cap, tile_m=128)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    want = oracle.gemm_a2a(P, E, N, K, BF16, BF16, X, W, off, dest, slot, cap)
+    _check_a2a(run, want, counts)
+
+    empty = bf.GemmA2A(P, E, N, K, BF16, X[:0], W, np.zeros(E + 1, np.int64), dest[:0], slot[:0],
+                       np.zeros(P, np.int64), cap, tile_m=128)
+    empty.poison()
+    empty.run()
+    sync()
+    assert empty.status_value() == 0
+    assert torch.all(empty.win_flags[:, 0] == empty.epoch)
+    assert torch.isnan(empty.win_data.view(torch.bfloat16).float()).all()
+
+
+def test_gemm_ar_single_shard_and_empty():
+    """P = 1: the AllReduce of one partial is the GEMM itself (one window);
+    M = 0: nothing is launched, the call succeeds."""
+    say("gemm_ar P=1 and M=0")
+    ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    run, slots, win = _gemm_ar(1, 512, 512, 256, BF16, F32, F32, 256, 256, seed=3, dist=ints)
+    A = bf.to_host(run.A, BF16)
+    Wm = bf.to_host(run.W, BF16)
+    plain = (val(A[0], BF16) @ val(Wm[0], BF16)).astype(np.float32)
+    np.testing.assert_array_equal(bf.to_host(run.out_all, F32)[0], plain)
+    e = bf.GemmAR(2, 0, 256, 256, BF16, F32, BF16, 256, 256, A[:, :0].repeat(2, 0)[:2], Wm.repeat(2, 0))
+    assert e.call() == hocf.HOCF_OK
+
+
 def test_gemm_a2a_full_moe():
     """The MoE combine workload: 8 ranks x 4096 tokens, top-2 of 32 experts,
     this rank's 4 experts (K=1792 -> N=4096): every window row against the
