@@ -115,7 +115,7 @@ class GemmA2A:
     N: int          # model width (output of the expert's down projection)
     K: int          # expert hidden width
     cap: int        # rows of each destination window
-    tile_m: int = 128   # expert groups are padded to whole tiles of this many rows
+    tile_m: int = 256   # expert groups are padded to whole tiles of this many rows
     tile_n: int = 256
 
 
