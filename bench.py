@@ -51,7 +51,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)  # >= 200 timed calls of each operator
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)  # untimed steps first (10 calls of each operator)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a,gemm_ar,gemm_a2a,gemm_rs_unfused,"
                                      "gemv_ar_unfused")
