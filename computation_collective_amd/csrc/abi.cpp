@@ -311,11 +311,11 @@ hocf_status hocf_gemm_a2a(int P, int E, int64_t T, int N, int K, hocf_dtype in_d
   hocf_status st = check_sync(sync, hocf_gemm_a2a_workspace_bytes(P));
   if (st != HOCF_OK) return st;
   if ((st = check_windows(win, P, "gemm_a2a")) != HOCF_OK) return st;
-  for (int d = 0; d < P; ++d)
-    if (!win[d].flags) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: window %d has no flag word", d);
   if (T > 0 && N > 0) {
     if (!X || !W || !dest || !slot) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: NULL tensor");
     if (!aligned16(X) || !aligned16(W)) return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: tensors must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(dest) | reinterpret_cast<uintptr_t>(slot)) & 3u)
+      return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: dest and slot must be 4-byte aligned");
   }
 
   hocf::SyncArgs sa;

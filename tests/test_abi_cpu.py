@@ -176,8 +176,8 @@ def test_embbag_rejects(kw, expect):
 
 
 def _a2a(P=2, E=2, T=512, N=256, K=256, off=(0, 256, 512), counts=(3, 4), cap=8, tile=(256, 256),
-         in_dt=BF16, out_dt=BF16, win=True, X=FAKE):
-    return hocf.hocf_gemm_a2a(P, E, T, N, K, in_dt, out_dt, X, FAKE, off, FAKE, FAKE, counts,
+         in_dt=BF16, out_dt=BF16, win=True, X=FAKE, dest=FAKE):
+    return hocf.hocf_gemm_a2a(P, E, T, N, K, in_dt, out_dt, X, FAKE, off, dest, FAKE, counts,
                               _win(P) if win else None, cap, *tile, _sync())
 
 
@@ -188,7 +188,7 @@ def _a2a(P=2, E=2, T=512, N=256, K=256, off=(0, 256, 512), counts=(3, 4), cap=8,
     (dict(K=100), UNSUPPORTED), (dict(off=(0, 200, 512)), INVALID), (dict(off=(0, 256, 256)), INVALID),
     (dict(off=(0, 512, 256)), INVALID), (dict(counts=(3, 9)), INVALID), (dict(counts=(-1, 4)), INVALID),
     (dict(off=None), INVALID), (dict(counts=None), INVALID), (dict(win=False), INVALID),
-    (dict(X=0), INVALID), (dict(X=FAKE + 8), INVALID),
+    (dict(X=0), INVALID), (dict(X=FAKE + 8), INVALID), (dict(dest=FAKE + 2), INVALID), (dict(dest=0), INVALID),
 ])
 def test_gemm_a2a_rejects(kw, expect):
     assert _a2a(**kw) == expect
