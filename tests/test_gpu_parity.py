@@ -769,6 +769,26 @@ def test_gemm_ar_single_shard_and_empty():
     assert e.call() == hocf.HOCF_OK
 
 
+def test_gemm_a2a_most_experts_and_destinations():
+    """The ABI's limits: 64 local experts (64 groups of one mostly padded
+    tile each) and 16 destination ranks; integer operands, bit-exact."""
+    P, E, B, topk, N, K = 16, 64, 96, 4, 256, 128
+    say(f"gemm_a2a limits P={P} E={E} B={B} top{topk}")
+    off, dest, slot, counts, X, W = _moe_case(P, E, B, topk, N, K, seed=64, dist_x=("int", -2, 2),
+                                              dist_w=("int", -2, 2))
+    cap = int(counts.max())
+    run = bf.GemmA2A(P, E, N, K, F32, X, W, off, dest, slot, counts, cap)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    want = oracle.gemm_a2a(P, E, N, K, BF16, F32, X, W, off, dest, slot, cap)
+    got = bf.to_host(run.win_data, F32)
+    for d in range(P):
+        np.testing.assert_array_equal(got[d, :counts[d]], want[d, :counts[d]])
+    assert torch.all(run.win_flags[:, 0] == run.epoch)
+
+
 def test_gemm_a2a_full_moe():
     """The MoE combine workload: 8 ranks x 4096 tokens, top-2 of 32 experts,
     this rank's 4 experts (K=1792 -> N=4096): every window row against the
