@@ -1108,3 +1108,68 @@ def test_embbag_full_dlrm():
     np.testing.assert_array_equal(got, want)
     del tables
     torch.cuda.empty_cache()
+
+
+# ====================================================================== determinism
+
+def _repeat_identical(run_call, outs, n=1000):
+    """n calls, each output compared on the device with the first call's: every
+    call must give the same bits (fixed reduction order, no arrival dependence)."""
+    run_call(0)
+    sync()
+    refs = [o.clone() for o in outs()]
+    bad = torch.zeros((), dtype=torch.int64, device="cuda")
+    for i in range(1, n):
+        run_call(i)
+        for o, r in zip(outs(), refs):
+            bad += (o.view(torch.int32 if o.element_size() == 4 else torch.int16) !=
+                    r.view(torch.int32 if r.element_size() == 4 else torch.int16)).any()
+    sync()
+    return int(bad.item())
+
+
+@pytest.mark.parametrize("op", ["gemm_rs", "gemm_ar", "gemm_rs_unfused", "gemv_ar", "ag_gemm", "embbag_a2a",
+                                "gemm_a2a"])
+def test_thousand_calls_bit_identical(op, monkeypatch):
+    """1000 calls of each operator on one buffer set give bit-identical results
+    (outputs NaN-poisoned before every call).  A small grid makes the GEMM
+    reductions fold bands inside later tiles' mainloops, in whichever order
+    the workgroups happen to run; AllGather+GEMM cycles through six chunk
+    release orders."""
+    monkeypatch.setenv("HOCF_MAX_WORKGROUPS", "24")
+    say(f"{op}: 1000 calls bit-identical")
+    if op in ("gemm_rs", "gemm_ar", "gemm_rs_unfused"):
+        P, Mc, N, K = 4, 512, 512, 1280
+        A, W = gen.gemm_rs_inputs(P, P * Mc, N, K, BF16, seed=13)
+        if op == "gemm_ar":
+            r = bf.GemmAR(P, P * Mc, N, K, BF16, F32, BF16, 256, 256, A, W)
+            outs = lambda: [r.out_all]
+        else:
+            r = bf.GemmRS(P, P * Mc, N, K, BF16, F32, BF16, 256, 256, A, W, unfused=op == "gemm_rs_unfused")
+            outs = lambda: [r.out]
+        call = lambda i: (r.poison(), r.run())
+    elif op == "gemv_ar":
+        x, W = gen.gemv_ar_inputs(8, 4, 2048, 1024, seed=13)
+        r = bf.GemvAR(8, 4, 2048, 1024, BF16, F32, BF16, 256, x, W)
+        outs = lambda: [r.win_data]
+        call = lambda i: (r.poison(), r.run())
+    elif op == "ag_gemm":
+        chunks, W, _ = gen.ag_gemm_inputs(4, 256, 512, 512, seed=13)
+        r = bf.AgGemm(4, 256, 512, 512, BF16, 256, 256, chunks, W)
+        orders = [np.random.default_rng(k).permutation(4) for k in range(6)]
+        outs = lambda: [r.out]
+        call = lambda i: (r.poison(), r.run_prereleased(orders[i % 6]))
+    elif op == "embbag_a2a":
+        T, R, D, B, L = 4, 5000, 128, 512, 20
+        tab = gen.embbag_tables(T, R, D, seed=13)
+        idx = gen.zipf_indices(T, B, L, R, seed=13)
+        r = bf.EmbbagA2A(T, R, D, B, L, 8, 16, tab, idx)
+        outs = lambda: [r.win_data]
+        call = lambda i: (r.poison(), r.run())
+    else:
+        off, dest, slot, counts, X, W = _moe_case(8, 4, 256, 2, 512, 512, seed=13)
+        r = bf.GemmA2A(8, 4, 512, 512, BF16, X, W, off, dest, slot, counts, int(counts.max()))
+        outs = lambda: [r.win_data]
+        call = lambda i: (r.poison(), r.run())
+    assert _repeat_identical(call, outs) == 0
+    assert r.status_value() == 0
