@@ -65,9 +65,11 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
     if (tid == 0) {
       int chunk = -1, tile = -1;
       // the first gridDim.x tickets go to the workgroups by index (no
-      // atomic: at the start every workgroup would hit the counter at once);
-      // the counter deals the tickets after them
-      const uint32_t tk = first ? blockIdx.x
+      // atomic: at the start every workgroup would hit the counter at once),
+      // each XCD's workgroups taking a contiguous run of them (tiles of the
+      // same chunk share its A rows in that XCD's L2); the counter deals the
+      // tickets after them
+      const uint32_t tk = first ? xcd_contiguous(blockIdx.x, gridDim.x)
                                 : gridDim.x + __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
                                                                      __HIP_MEMORY_SCOPE_AGENT);
       first = false;

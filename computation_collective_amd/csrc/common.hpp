@@ -10,6 +10,16 @@ namespace hocf {
 constexpr int kMaxP = 16;      // largest shard count (matches HOCF_MAX_P)
 constexpr int kNumQueues = 8;  // one ticket queue per XCD (MI355X has 8)
 
+// A permutation of the workgroup indices [0, grid) that gives the
+// workgroups of one XCD (dispatched round-robin: XCD = index mod 8) one
+// contiguous run of positions, so the work they take first is adjacent and
+// shares operands in that XCD's L2.  Identity when grid is not a multiple
+// of 8 (still a permutation: correctness never depends on the placement).
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t grid) {
+  if (grid % kNumQueues) return b;
+  return (b % kNumQueues) * (grid / kNumQueues) + b / kNumQueues;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));

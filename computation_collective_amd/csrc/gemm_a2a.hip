@@ -114,11 +114,21 @@ __global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
   if (tid < kMaxP) s_cnt[tid] = 0;
   if (tid < a.P) s_win[tid] = reinterpret_cast<uint64_t>(a.win_data[tid]);  // (read after the scatter's barrier)
 
-  for (int item = blockIdx.x; item < a.total; item += gridDim.x) {
+  // round k of the static schedule: the workgroups of one XCD take a
+  // contiguous run of items, and within an expert the items run in blocks of
+  // (up to) 8 column tiles, row tile by row tile, so such a run covers a few
+  // row tiles by 8 column tiles, sharing their X and W panels in that XCD's L2
+  constexpr int kColBlock = 8;
+  const int first = (int)xcd_contiguous(blockIdx.x, gridDim.x);
+  for (int item = first; item < a.total; item += gridDim.x) {
     int e = 0;
     while (e + 1 < a.E && item >= a.tile_off[e + 1]) ++e;
     const int local = item - a.tile_off[e];
-    const int mt = local / a.ntiles, nt = local % a.ntiles;
+    const int mtiles = (a.tile_off[e + 1] - a.tile_off[e]) / a.ntiles;
+    const int nb = local / (mtiles * kColBlock);               // column block
+    const int width = min(kColBlock, a.ntiles - nb * kColBlock);
+    const int j = local - nb * mtiles * kColBlock;
+    const int mt = j / width, nt = nb * kColBlock + j % width;
     const int64_t row0 = a.row_off[e] + (int64_t)mt * Tile::TM;
     const uint16_t* At = a.X + row0 * a.K;
     const uint16_t* Wt = a.W + (int64_t)e * a.K * a.N + (int64_t)nt * Tile::TN;
