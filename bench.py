@@ -19,6 +19,9 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
               computation publishing its partials, then the fold): the bulk-synchronous
               baseline; `fusion` reports the time each fused operator saves against it
 
+hipblaslt_bmm: context, not an operator of this library -- torch.bmm (hipBLASLt) on the same
+eight shard GEMMs as gemm_rs, with no collective.
+
 Optional extra ops (--ops): embbag_uniform (the same shapes with uniform indices:
 no reuse, a control for the Zipf figure) and copy (a 1 GiB negating copy, the
 calibration of the HBM byte counters).
@@ -55,7 +58,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)  # untimed steps first (10 calls of each operator)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a,gemm_ar,gemm_a2a,gemm_rs_unfused,"
-                                     "gemv_ar_unfused")
+                                     "gemv_ar_unfused,hipblaslt_bmm")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
     ap.add_argument("--a2a-tile-m", type=int, default=0, help="GEMM+A2A tile rows (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -294,6 +297,35 @@ def main():
                                        config=dict(workload=c.name + "_unfused", P=c.P, Mb=c.Mb, N=c.N, K=c.K,
                                                    tile_n=gtile, weight_replicas=4,
                                                    kernels="GEMV (partials published), then the fold"))
+    if "hipblaslt_bmm" in ops:
+        # context, not a fused operator: the vendor library (torch.bmm -> hipBLASLt) on the same
+        # eight shard GEMMs as gemm_rs, bf16 in, bf16 out, with no collective at all; both
+        # operands contiguous (a transposed view as the right operand is avoided)
+        c = cfgs.GEMM_RS_MLP
+        log(f"inputs {c.name} (hipBLASLt context)")
+        A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, c.in_dt, seed=0)
+        At = bf.to_device(A, dev).view(torch.bfloat16).contiguous()
+        Wt = bf.to_device(W, dev).view(torch.bfloat16).contiguous()
+        Ct = torch.empty((c.P, c.M, c.N), dtype=torch.bfloat16, device=dev)
+        del A, W
+        runs["hipblaslt_bmm"] = dict(call=lambda a=At, w=Wt, o=Ct: torch.bmm(a, w, out=o), obj=None, work=c.flops,
+                                     unit="TFLOP/s", bound="mfma", peak=PEAK_BF16_TFLOPS,
+                                     bytes=2 * (c.P * c.M * c.K + c.P * c.K * c.N + c.P * c.M * c.N),
+                                     config=dict(workload=c.name + "_hipblaslt_bmm", P=c.P, M=c.M, N=c.N, K=c.K,
+                                                 note="torch.bmm on the 8 shard GEMMs, no collective (context)"))
+        # the same with fp32 output (the partials gemm_rs carries), where this torch build has it
+        try:
+            Cf = torch.bmm(At, Wt, out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            runs["hipblaslt_bmm_f32out"] = dict(
+                call=lambda a=At, w=Wt: torch.bmm(a, w, out_dtype=torch.float32), obj=None, work=c.flops,
+                unit="TFLOP/s", bound="mfma", peak=PEAK_BF16_TFLOPS,
+                bytes=2 * (c.P * c.M * c.K + c.P * c.K * c.N) + 4 * c.P * c.M * c.N,
+                config=dict(workload=c.name + "_hipblaslt_bmm_f32out", P=c.P, M=c.M, N=c.N, K=c.K,
+                            note="torch.bmm, fp32 output, on the 8 shard GEMMs, no collective (context)"))
+            del Cf
+        except (RuntimeError, TypeError, NotImplementedError) as ex:
+            log(f"hipBLASLt fp32-output context skipped: {type(ex).__name__}")
     if "embbag_uniform" in ops:
         # control: the same shapes with uniform indices (no reuse), so logical ~ DRAM bytes
         c = cfgs.EMBBAG_DLRM
