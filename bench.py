@@ -10,6 +10,9 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
   ag_gemm     AllGather+GEMM, 8 chunks 1024x4096, W 4096x1792 bf16, chunk flags written in a
               seeded random order on the kernel's stream just before it (outside the timed
               events: the kernel's span is timed)
+  ag_gemm_paced  the same with the chunks arriving over time, as over xGMI: the host sets
+              the flags (host-coherent memory) 55 us apart after the launch (--chunk-gap-us);
+              after_last_arrival_us = the kernel's span minus the 385 us arrival span
   embbag_a2a  64 tables 1e6x128 fp32, batch 16384, 20 rows per bag, Zipf(1.05), P=8
               (a 1 GiB scratch read before each call, outside the timed events)
   gemm_ar     GEMM+AllReduce, the gemm_rs shapes; the folded chunks land in all 8 windows
@@ -57,10 +60,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)  # >= 200 timed calls of each operator
     ap.add_argument("--warmup", type=int, default=10)  # untimed steps first (10 calls of each operator)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
-    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,embbag_a2a,gemm_ar,gemm_a2a,gemm_rs_unfused,"
-                                     "gemv_ar_unfused,hipblaslt_bmm")
+    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,ag_gemm_paced,embbag_a2a,gemm_ar,gemm_a2a,"
+                                     "gemm_rs_unfused,gemv_ar_unfused,hipblaslt_bmm")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
     ap.add_argument("--a2a-tile-m", type=int, default=0, help="GEMM+A2A tile rows (default: the config's)")
+    ap.add_argument("--chunk-gap-us", type=float, default=55.0,
+                    help="ag_gemm_paced: time between chunk arrivals (8 MB over one ~153 GB/s xGMI link)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     return ap.parse_args()
@@ -206,6 +211,32 @@ def main():
                                peak=PEAK_BF16_TFLOPS, bytes=algo_bytes,
                                config=dict(workload=c.name, P=c.P, Mc=c.Mc, N=c.N, K=c.K,
                                            tile=[c.tile_m, c.tile_n], release_order=[int(v) for v in order]))
+    if "ag_gemm_paced" in ops:
+        # context: the chunks arrive over time, as over xGMI (8 MB per chunk at ~153 GB/s per
+        # link: one every ~55 us), the first (the local one) at the start; chunk data resident,
+        # flags in host-coherent memory written by the host on a busy-wait clock after the launch
+        c = cfgs.AG_GEMM_COL
+        log(f"inputs {c.name} (paced arrival)")
+        chunks, W, order = gen.ag_gemm_inputs(c.P, c.Mc, c.N, c.K, seed=0)
+        ap_ = bf.AgGemm(c.P, c.Mc, c.N, c.K, bf.BF16, c.tile_m, c.tile_n, chunks, W, flags="host")
+        gap_s = args.chunk_gap_us * 1e-6
+
+        def ag_paced_call(a=ap_, order=order):
+            sy = a.next_sync(spin_timeout_ns=2_000_000_000)
+            hocf.check(a.call(sy, stream))
+            t0 = time.perf_counter()
+            for k, ch in enumerate(order):
+                while time.perf_counter() - t0 < k * gap_s:
+                    pass
+                a.host_flags[int(ch)] = sy.epoch
+
+        runs["ag_gemm_paced"] = dict(call=ag_paced_call, pre=torch.cuda.synchronize, obj=ap_, work=c.flops,
+                                     unit="TFLOP/s", bound="mfma", peak=PEAK_BF16_TFLOPS,
+                                     bytes=2 * (c.P * c.Mc * c.K + c.K * c.N + c.P * c.Mc * c.N),
+                                     config=dict(workload=c.name + "_paced", P=c.P, Mc=c.Mc, N=c.N, K=c.K,
+                                                 tile=[c.tile_m, c.tile_n], chunk_gap_us=args.chunk_gap_us,
+                                                 arrival_span_us=(c.P - 1) * args.chunk_gap_us,
+                                                 release_order=[int(v) for v in order]))
     if "embbag_a2a" in ops:
         c = cfgs.EMBBAG_DLRM
         log(f"inputs {c.name} (tables on the device)")
@@ -412,6 +443,9 @@ def main():
                 "frac": round(tb / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
             "config": R["config"],
         }
+        if n == "ag_gemm_paced":
+            # how long the kernel runs on after the last chunk has arrived
+            out_ops[n]["after_last_arrival_us"] = round(avg * 1e3 - R["config"]["arrival_span_us"], 1)
         log(f"{n}: {v:.1f} {R['unit']} ({avg:.4f} ms average, {100 * v / R['peak']:.1f}% of peak)")
 
     head = "gemm_rs" if "gemm_rs" in out_ops else names[0]
