@@ -96,6 +96,28 @@ __device__ __forceinline__ void scatter_rows(const GemmA2aArgs& a, int col0,
   }
 }
 
+// One tile (or the half-height tile `half` = 0/1 of it, with the Half
+// tile shape) of the grouped GEMM, scattered; returns after the barrier that
+// follows its stores.
+template <class T, int ODT>
+__device__ __forceinline__ void a2a_tile(const GemmA2aArgs& a, int64_t row0, int e, int nt,
+                                         char* const (&stages)[4], int2* s_route, const uint64_t* s_win,
+                                         uint32_t* s_cnt) {
+  const int tid = threadIdx.x;
+  const uint16_t* At = a.X + row0 * a.K;
+  const uint16_t* Wt = a.W + (int64_t)e * a.K * a.N + (int64_t)nt * T::TN;
+  // the rows' routes, loaded now so that their latency hides behind the mainloop
+  int2 route = {-1, -1};
+  if (tid < T::TM) route = int2{a.dest[row0 + tid], a.slot[row0 + tid]};
+  floatx16 acc[T::FM][T::FN];
+  T::template run<false>(At, a.K, Wt, a.N, T::TM, T::TN, a.K, stages, acc);
+  // (the previous tile's scatter read s_route before the barrier that ended it)
+  if (tid < T::TM) s_route[tid] = route;
+  scatter_rows<T, ODT>(a, nt * T::TN, acc, stages, s_route, s_win, s_cnt);
+  wait_memory();  // this thread's row stores have completed
+  __syncthreads();
+}
+
 template <class Tile, int ODT>
 __global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem0[Tile::SMEM_BYTES];
@@ -119,8 +141,18 @@ __global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
   // (up to) 8 column tiles, row tile by row tile, so such a run covers a few
   // row tiles by 8 column tiles, sharing their X and W panels in that XCD's L2
   constexpr int kColBlock = 8;
+  //
+  // Tiles [keep, total) -- the last, partial round of whole tiles -- run as
+  // two half-height tiles each, so that round takes half as long (the same
+  // rows, each computed once; only 256-row tiles with bf16 output split).
+  using Half = TileBf16Direct<Tile::TM / 2, Tile::TN, 2, 2>;
+  constexpr bool kHalves = ODT == kBF16 && Tile::TM == 256;
+  static_assert(!kHalves || (Half::SMEM_BYTES <= Tile::SMEM_BYTES && Half::NT == Tile::NT), "half tile");
+  const int nwork = kHalves ? a.keep + 2 * (a.total - a.keep) : a.total;
   const int first = (int)xcd_contiguous(blockIdx.x, gridDim.x);
-  for (int item = first; item < a.total; item += gridDim.x) {
+  for (int w = first; w < nwork; w += gridDim.x) {
+    const bool split = kHalves && w >= a.keep;
+    const int item = split ? a.keep + (w - a.keep) / 2 : w;
     int e = 0;
     while (e + 1 < a.E && item >= a.tile_off[e + 1]) ++e;
     const int local = item - a.tile_off[e];
@@ -130,18 +162,14 @@ __global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
     const int j = local - nb * mtiles * kColBlock;
     const int mt = j / width, nt = nb * kColBlock + j % width;
     const int64_t row0 = a.row_off[e] + (int64_t)mt * Tile::TM;
-    const uint16_t* At = a.X + row0 * a.K;
-    const uint16_t* Wt = a.W + (int64_t)e * a.K * a.N + (int64_t)nt * Tile::TN;
-    // the rows' routes, loaded now so that their latency hides behind the mainloop
-    int2 route = {-1, -1};
-    if (tid < Tile::TM) route = int2{a.dest[row0 + tid], a.slot[row0 + tid]};
-    floatx16 acc[Tile::FM][Tile::FN];
-    Tile::template run<false>(At, a.K, Wt, a.N, Tile::TM, Tile::TN, a.K, stages, acc);
-    // (the previous tile's scatter read s_route before the barrier that ended it)
-    if (tid < Tile::TM) s_route[tid] = route;
-    scatter_rows<Tile, ODT>(a, nt * Tile::TN, acc, stages, s_route, s_win, s_cnt);
-    wait_memory();  // this thread's row stores have completed
-    __syncthreads();
+    if constexpr (kHalves) {
+      if (split)
+        a2a_tile<Half, ODT>(a, row0 + (int64_t)((w - a.keep) % 2) * Half::TM, e, nt, stages, s_route, s_win, s_cnt);
+      else
+        a2a_tile<Tile, ODT>(a, row0, e, nt, stages, s_route, s_win, s_cnt);
+    } else {
+      a2a_tile<Tile, ODT>(a, row0, e, nt, stages, s_route, s_win, s_cnt);
+    }
     if (tid < a.P) {
       const uint32_t c = s_cnt[tid];
       s_cnt[tid] = 0;  // (the next tile's counts start after the next scatter's first barrier)
@@ -164,11 +192,19 @@ __global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
 }
 
 template <class Tile, int ODT>
-static hipError_t launch_k(const GemmA2aArgs& a, hipStream_t s) {
+static hipError_t launch_k(const GemmA2aArgs& a0, hipStream_t s) {
   auto kern = &gemm_a2a_kernel<Tile, ODT>;
+  constexpr bool kHalves = ODT == kBF16 && Tile::TM == 256;  // (as in the kernel)
   int grid = 0;
-  hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), Tile::NT, a.total, &grid);
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), Tile::NT,
+                                 kHalves ? 2 * (int64_t)a0.total : a0.total, &grid);
   if (e != hipSuccess) return e;
+  // split the last, partial round of whole tiles into half-height tiles when
+  // the halves still fit in one round of the grid (the kernel splits only
+  // 256-row tiles with bf16 output; elsewhere keep is ignored)
+  GemmA2aArgs a = a0;
+  const int rem = a.total % grid;
+  a.keep = (rem != 0 && 2 * rem <= grid) ? a.total - rem : a.total;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(Tile::NT), 0, s, a);
   return hipGetLastError();
 }

@@ -82,7 +82,8 @@ struct GemmA2aArgs {
   uint32_t* ws;
   int64_t T, cap;
   int P, E, N, K, ntiles, out_dt;
-  int total;  // work items: row tiles x column tiles over all experts
+  int total;  // tiles: row tiles x column tiles over all experts
+  int keep;   // tiles [0, keep) run whole; each later tile runs as two half-height tiles
   SyncArgs sync;
 };
 

@@ -789,6 +789,31 @@ def test_gemm_a2a_most_experts_and_destinations():
     assert torch.all(run.win_flags[:, 0] == run.epoch)
 
 
+@pytest.mark.parametrize("grid", [8, 16, 32])
+def test_gemm_a2a_last_round_in_half_tiles_bit_exact(grid, monkeypatch):
+    """A grid that leaves a partial last round: those tiles run as two
+    half-height tiles each (every row still computed once); integer
+    operands, bit-exact, every flag set."""
+    monkeypatch.setenv("HOCF_MAX_WORKGROUPS", str(grid))
+    P, E, B, topk, N, K = 8, 3, 400, 2, 1024, 256
+    off, dest, slot, counts, X, W = _moe_case(P, E, B, topk, N, K, seed=70 + grid, dist_x=("int", -2, 2),
+                                              dist_w=("int", -2, 2))
+    tiles = int(off[-1]) // 256 * (N // 256)
+    say(f"gemm_a2a half tiles: {tiles} tiles on a grid of {grid} (remainder {tiles % grid})")
+    assert 0 < tiles % grid <= grid // 2          # the case where the last round splits
+    cap = int(counts.max())
+    run = bf.GemmA2A(P, E, N, K, BF16, X, W, off, dest, slot, counts, cap)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    want = oracle.gemm_a2a(P, E, N, K, BF16, BF16, X, W, off, dest, slot, cap)
+    got = bf.to_host(run.win_data, BF16)
+    for d in range(P):
+        np.testing.assert_array_equal(got[d, :counts[d]], want[d, :counts[d]])
+    assert torch.all(run.win_flags[:, 0] == run.epoch)
+
+
 def test_gemm_a2a_full_moe():
     """The MoE combine workload: 8 ranks x 4096 tokens, top-2 of 32 experts,
     this rank's 4 experts (K=1792 -> N=4096): every window row against the
