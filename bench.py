@@ -364,10 +364,9 @@ def main():
             tables = gen.embbag_tables_torch(c.T, c.R, c.D, seed=0, device=dev)
         uidx = gen.uniform_indices(c.T, c.B, c.L, c.R, seed=1)
         eu = bf.EmbbagA2A(c.T, c.R, c.D, c.B, c.L, c.P, c.tile_bags, tables, uidx)
-        flush_u = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         algo_bytes = 4 * c.T * c.B * c.L * c.D + 4 * c.T * c.B * c.L + 4 * c.T * c.B * c.D
         runs["embbag_uniform"] = dict(call=lambda e=eu: e.run(stream), obj=eu, work=algo_bytes, unit="GB/s",
-                                      pre=lambda f=flush_u: f.fill_(0.0), variant="uniform indices",
+                                      pre=mall_flush, variant="uniform indices",
                                       bound="hbm", peak=PEAK_HBM_GBS, bytes=algo_bytes,
                                       config=dict(workload=c.name + "_uniform_indices", T=c.T, R=c.R, D=c.D,
                                                   B=c.B, L=c.L, P=c.P, tile_bags=c.tile_bags))
