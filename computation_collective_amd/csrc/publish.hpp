@@ -355,9 +355,11 @@ struct BandFold {
     for (int pass = 0; pass < NPASS; ++pass) {
       const lds_char* src = park + pass * (Tile::NT * OUT_BYTES);
       const int64_t o = orel + (int64_t)pass * L::RPS * ld_out * OES;
+      // (streaming stores: the folded rows are written once and not read
+      // back by this kernel, so they should not displace operand panels)
       if constexpr (OUT_BYTES == 8) {
         const u32x2 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(src);
-        for (int d = 0; d < outs.n; ++d) *reinterpret_cast<u32x2*>(outs.at(d) + o) = w;
+        for (int d = 0; d < outs.n; ++d) __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(outs.at(d) + o));
       } else {
         u32x4 w[OUT_BYTES / 16];
 #pragma unroll
@@ -365,7 +367,8 @@ struct BandFold {
           w[b] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(src + 16 * b);
         for (int d = 0; d < outs.n; ++d)
 #pragma unroll
-          for (int b = 0; b < OUT_BYTES / 16; ++b) *reinterpret_cast<u32x4*>(outs.at(d) + o + 16 * b) = w[b];
+          for (int b = 0; b < OUT_BYTES / 16; ++b)
+            __builtin_nontemporal_store(w[b], reinterpret_cast<u32x4*>(outs.at(d) + o + 16 * b));
       }
     }
   }
