@@ -78,9 +78,54 @@ hocf_status check_windows(const hocf_window* win, int P, const char* what) {
 
 bool dt_ok(hocf_dtype d) { return d == HOCF_F32 || d == HOCF_BF16; }
 
-hocf_status launched(hipError_t e, const char* what) {
-  if (e == hipErrorInvalidValue) return fail(HOCF_ERR_UNSUPPORTED, "%s: no kernel for this shape", what);
-  if (e != hipSuccess) return fail(HOCF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+// Byte ranges a call reads (inputs) and writes (outputs).  A written range
+// may overlap no other range of the call: the kernels read their inputs
+// while other workgroups already write, and publish into windows that others
+// read, so any aliasing gives unspecified results.  Read-only ranges may
+// overlap each other.  Empty ranges and NULL pointers are skipped.
+class Ranges {
+ public:
+  void in(const char* what, int idx, const void* p, int64_t bytes) { add(what, idx, p, bytes, false); }
+  void out(const char* what, int idx, const void* p, int64_t bytes) { add(what, idx, p, bytes, true); }
+  hocf_status check(const char* op) const {
+    for (int i = 0; i < n_; ++i)
+      for (int j = i + 1; j < n_; ++j) {
+        const R& a = r_[i];
+        const R& b = r_[j];
+        if (!a.out && !b.out) continue;
+        if (a.lo < b.hi && b.lo < a.hi)
+          return fail(HOCF_ERR_INVALID_ARG, "%s: %s[%d] and %s[%d] overlap (an output may alias nothing else)",
+                      op, a.what, a.idx, b.what, b.idx);
+      }
+    return HOCF_OK;
+  }
+
+ private:
+  struct R {
+    const char* what;
+    int idx;
+    uintptr_t lo, hi;
+    bool out;
+  };
+  void add(const char* what, int idx, const void* p, int64_t bytes, bool out) {
+    if (!p || bytes <= 0 || n_ >= kMax) return;
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    r_[n_++] = R{what, idx, lo, lo + (uintptr_t)bytes, out};
+  }
+  static constexpr int kMax = 4 * HOCF_MAX_P + 16;
+  R r_[kMax];
+  int n_ = 0;
+};
+
+// The sync block's own ranges: the status word and the workspace (both written).
+void add_sync(Ranges& rg, const hocf_sync* s, size_t ws_bytes) {
+  rg.out("status", 0, s->status, 4);
+  rg.out("workspace", 0, s->workspace, (int64_t)ws_bytes);
+}
+
+hocf_status launched(int e, const char* what) {
+  if (e == hocf::kNoKernel) return fail(HOCF_ERR_UNSUPPORTED, "%s: no kernel for this shape", what);
+  if (e != hipSuccess) return fail(HOCF_ERR_HIP, "%s: %s", what, hipGetErrorString(static_cast<hipError_t>(e)));
   return ok();
 }
 
@@ -210,14 +255,22 @@ static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, h
   for (int q = 0; q < nout; ++q) {
     if (!outs[q]) return fail(HOCF_ERR_INVALID_ARG, "%s: NULL output %d", op, q);
     if (!aligned16(outs[q])) return fail(HOCF_ERR_INVALID_ARG, "%s: output %d not 16-byte aligned", op, q);
-    for (int d = 0; d < q; ++d) {
-      const char* x = static_cast<const char*>(outs[q]);
-      const char* y = static_cast<const char*>(outs[d]);
-      if (x < y + out_bytes && y < x + out_bytes)
-        return fail(HOCF_ERR_INVALID_ARG, "%s: outputs %d and %d overlap", op, d, q);
-    }
   }
   if ((st = check_windows(win, P, op)) != HOCF_OK) return st;
+  {
+    const int ies = in_dt == HOCF_BF16 ? 2 : 4, ses = slot_dt == HOCF_BF16 ? 2 : 4;
+    const int64_t tpc = cdiv(M / P, tile_m) * cdiv(N, tile_n);
+    Ranges rg;
+    rg.in("A", 0, A, (int64_t)P * M * K * ies);
+    rg.in("W", 0, W, (int64_t)P * K * N * ies);
+    for (int q = 0; q < nout; ++q) rg.out("out", q, outs[q], out_bytes);
+    for (int r = 0; r < P; ++r) {
+      rg.out("win.data", r, win[r].data, (int64_t)M * N * ses);  // [P src][Mc][N]
+      rg.out("win.flags", r, win[r].flags, (int64_t)P * tpc * 4);
+    }
+    add_sync(rg, sync, need);
+    if ((st = rg.check(op)) != HOCF_OK) return st;
+  }
 
   hocf::SyncArgs sa;
   if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
@@ -317,6 +370,20 @@ hocf_status hocf_gemm_a2a(int P, int E, int64_t T, int N, int K, hocf_dtype in_d
     if ((reinterpret_cast<uintptr_t>(dest) | reinterpret_cast<uintptr_t>(slot)) & 3u)
       return fail(HOCF_ERR_INVALID_ARG, "gemm_a2a: dest and slot must be 4-byte aligned");
   }
+  {
+    const int oes = out_dt == HOCF_BF16 ? 2 : 4;
+    Ranges rg;
+    rg.in("X", 0, X, T * K * 2);
+    rg.in("W", 0, W, (int64_t)E * K * N * 2);
+    rg.in("dest", 0, dest, T * 4);
+    rg.in("slot", 0, slot, T * 4);
+    for (int d = 0; d < P; ++d) {
+      rg.out("win.data", d, win[d].data, cap * N * oes);
+      rg.out("win.flags", d, win[d].flags, 4);
+    }
+    add_sync(rg, sync, hocf_gemm_a2a_workspace_bytes(P));
+    if ((st = rg.check("gemm_a2a")) != HOCF_OK) return st;
+  }
 
   hocf::SyncArgs sa;
   if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
@@ -374,6 +441,21 @@ static hocf_status gemv_collective(const char* op, bool fused, int P, int Mb, in
   if (!aligned16(x) || !aligned16(W) || !aligned16(part))
     return fail(HOCF_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", op);
   if ((st = check_windows(win, P, op)) != HOCF_OK) return st;
+  {
+    const int ses = slot_dt == HOCF_BF16 ? 2 : 4, oes = out_dt == HOCF_BF16 ? 2 : 4;
+    const int64_t nt = cdiv(N, tile_n);
+    Ranges rg;
+    rg.in("x", 0, x, (int64_t)P * Mb * K * 2);
+    rg.in("W", 0, W, (int64_t)P * K * N * 2);
+    rg.out("part", 0, part, (int64_t)P * Mb * N * ses);
+    rg.out("part_flags", 0, part_flags, (int64_t)P * nt * 4);
+    for (int q = 0; q < P; ++q) {
+      rg.out("win.data", q, win[q].data, (int64_t)Mb * N * oes);
+      rg.out("win.flags", q, win[q].flags, nt * 4);
+    }
+    add_sync(rg, sync, hocf_gemv_ar_workspace_bytes(P, N, tile_n));
+    if ((st = rg.check(op)) != HOCF_OK) return st;
+  }
 
   hocf::SyncArgs sa;
   if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
@@ -425,6 +507,10 @@ hocf_status hocf_ag_gemm(int P, int Mc, int N, int K, hocf_dtype in_dt, hocf_dty
   if (!((tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128)))
     return fail(HOCF_ERR_UNSUPPORTED, "ag_gemm: no kernel for tile %dx%d", tile_m, tile_n);
   if (N % 8 || K % 8) return fail(HOCF_ERR_INVALID_ARG, "ag_gemm: N and K must be multiples of 8");
+  // output tiles are stored with 32-bit byte offsets from their origin
+  if ((int64_t)tile_m * N * (out_dt == HOCF_BF16 ? 2 : 4) >= ((int64_t)1 << 31))
+    return fail(HOCF_ERR_UNSUPPORTED, "ag_gemm: tile_m * N * %d bytes per tile row band reach 2 GiB",
+                out_dt == HOCF_BF16 ? 2 : 4);
   hocf_status st = check_sync(sync, hocf_ag_gemm_workspace_bytes(P));
   if (st != HOCF_OK) return st;
   if (Mc == 0 || N == 0) return ok();
@@ -432,6 +518,15 @@ hocf_status hocf_ag_gemm(int P, int Mc, int N, int K, hocf_dtype in_dt, hocf_dty
   if ((K && (!aligned16(A_gathered) || !aligned16(W))) || !aligned16(out) ||
       (reinterpret_cast<uintptr_t>(chunk_flags) & 3u))
     return fail(HOCF_ERR_INVALID_ARG, "ag_gemm: misaligned tensor");
+  {
+    Ranges rg;
+    rg.in("A_gathered", 0, A_gathered, (int64_t)P * Mc * K * 2);
+    rg.in("chunk_flags", 0, chunk_flags, (int64_t)P * 4);
+    rg.in("W", 0, W, (int64_t)K * N * 2);
+    rg.out("out", 0, out, (int64_t)P * Mc * N * (out_dt == HOCF_BF16 ? 2 : 4));
+    add_sync(rg, sync, hocf_ag_gemm_workspace_bytes(P));
+    if ((st = rg.check("ag_gemm")) != HOCF_OK) return st;
+  }
 
   hocf::SyncArgs sa;
   if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
@@ -474,6 +569,20 @@ hocf_status hocf_embbag_a2a(int T, int64_t R, int D, int B, int L, int P, const 
   if ((tables && !aligned16(tables)) || (offsets && (reinterpret_cast<uintptr_t>(offsets) & 7u)))
     return fail(HOCF_ERR_INVALID_ARG, "embbag_a2a: misaligned tensor");
   if ((st = check_windows(win, P, "embbag_a2a")) != HOCF_OK) return st;
+  {
+    const int64_t Bd = B / P, nj = cdiv(Bd, tile_bags);
+    Ranges rg;
+    rg.in("tables", 0, tables, (int64_t)T * R * D * 4);
+    // (with CSR offsets the extent of `indices` is only known on the device)
+    if (!offsets) rg.in("indices", 0, indices, (int64_t)T * B * L * 4);
+    rg.in("offsets", 0, offsets, offsets ? ((int64_t)T * B + 1) * 8 : 0);
+    for (int d = 0; d < P; ++d) {
+      rg.out("win.data", d, win[d].data, Bd * T * D * 4);
+      rg.out("win.flags", d, win[d].flags, (int64_t)T * nj * 4);
+    }
+    add_sync(rg, sync, hocf_embbag_a2a_workspace_bytes());
+    if ((st = rg.check("embbag_a2a")) != HOCF_OK) return st;
+  }
 
   hocf::SyncArgs sa;
   if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;

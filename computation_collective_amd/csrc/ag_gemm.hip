@@ -45,7 +45,7 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
   char* const stages[4] = {smem0, smem1, smem2, smem3};
   __shared__ int s_chunk, s_tile;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int P = a.P, N = a.N, K = a.K, Mc = a.Mc;
   const int tpc = a.mtiles * a.ntiles;
   uint32_t* ws = a.ws + kWsExtra;
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
             continue;               // look at the arrival list again
           }
           // 3. not there yet: bounded wait
-          if (a.sync.abort_flag && load_flag_system(a.sync.abort_flag) != 0u) {
+          if (abort_requested(a.sync)) {
             report_status(a.sync, kErrAborted);
             break;
           }
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(Tile::NT) void ag_gemm_kernel(AgGemmArgs a) {
 }
 
 template <class Tile, bool RAGGED, int ODT>
-static hipError_t launch_k(const AgGemmArgs& a, hipStream_t s) {
+static int launch_k(const AgGemmArgs& a, hipStream_t s) {
   auto kern = &ag_gemm_kernel<Tile, RAGGED, ODT>;
   int grid = 0;
   hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), Tile::NT,
@@ -179,24 +179,24 @@ static hipError_t launch_k(const AgGemmArgs& a, hipStream_t s) {
 
 // full tiles take the direct-to-LDS mainloop, ragged ones the register-staged one
 template <int TM, int TN, int ODT>
-static hipError_t launch_tile(const AgGemmArgs& a, hipStream_t s) {
+static int launch_tile(const AgGemmArgs& a, hipStream_t s) {
   using Staged = TileBf16<TM, TN, 2, 2>;
   using Direct = TileBf16Direct<TM, TN, 2, 2>;
   // the direct tile takes full tiles whose operands it can address with 32-bit offsets
-  const bool ragged = (a.Mc % TM) || (a.N % TN) || (a.K % Direct::KSTEP) ||
+  const bool ragged = (a.Mc % TM) || (a.N % TN) || !Direct::k_fits(a.K) ||
                       !Direct::operands_fit(a.K, a.N, a.K);
   return ragged ? launch_k<Staged, true, ODT>(a, s) : launch_k<Direct, false, ODT>(a, s);
 }
 
 template <int TM, int TN>
-static hipError_t launch_out(const AgGemmArgs& a, hipStream_t s) {
+static int launch_out(const AgGemmArgs& a, hipStream_t s) {
   return a.out_dt == kBF16 ? launch_tile<TM, TN, kBF16>(a, s) : launch_tile<TM, TN, kF32>(a, s);
 }
 
-hipError_t launch_ag_gemm(const AgGemmArgs& a, int tm, int tn, hipStream_t s) {
+int launch_ag_gemm(const AgGemmArgs& a, int tm, int tn, hipStream_t s) {
   if (tm == 256 && tn == 256) return launch_out<256, 256>(a, s);
   if (tm == 128 && tn == 128) return launch_out<128, 128>(a, s);
-  return hipErrorInvalidValue;
+  return kNoKernel;
 }
 
 }  // namespace hocf

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kEmbThreads) void embbag_kernel(EmbbagArgs a) {
 }
 
 template <int CPL>
-static hipError_t launch_cpl(const EmbbagArgs& a, hipStream_t s) {
+static int launch_cpl(const EmbbagArgs& a, hipStream_t s) {
   const void* k = reinterpret_cast<const void*>(&embbag_kernel<CPL>);
   int grid = 0;
   hipError_t e = persistent_grid(k, kEmbThreads, a.total, &grid);
@@ -124,11 +124,11 @@ static hipError_t launch_cpl(const EmbbagArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_embbag_a2a(const EmbbagArgs& a, hipStream_t s) {
+int launch_embbag_a2a(const EmbbagArgs& a, hipStream_t s) {
   if (a.D <= 128) return launch_cpl<1>(a, s);
   if (a.D <= 256) return launch_cpl<2>(a, s);
   if (a.D <= 512) return launch_cpl<4>(a, s);
-  return hipErrorInvalidValue;
+  return kNoKernel;
 }
 
 }  // namespace hocf

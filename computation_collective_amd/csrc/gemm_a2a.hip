@@ -184,15 +184,19 @@ __global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
     }
   }
 
-  // the last workgroup out flags the destinations that receive no rows
+  // the last workgroup out flags the destinations that receive no rows, and
+  // clears every arrival counter: a destination whose rows were not all
+  // delivered (a row skipped for a bad destination or slot) never reached
+  // its expected count, so its counter still holds what did arrive
   if (finish_workgroup_last(a.ws, &s_last)) {
     if (tid < a.P && a.expected[tid] == 0)
       __hip_atomic_store(&a.win_flags[tid][0], a.sync.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < a.P) __hip_atomic_store(&arrived[tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 template <class Tile, int ODT>
-static hipError_t launch_k(const GemmA2aArgs& a0, hipStream_t s) {
+static int launch_k(const GemmA2aArgs& a0, hipStream_t s) {
   auto kern = &gemm_a2a_kernel<Tile, ODT>;
   constexpr bool kHalves = ODT == kBF16 && Tile::TM == 256;  // (as in the kernel)
   int grid = 0;
@@ -210,15 +214,15 @@ static hipError_t launch_k(const GemmA2aArgs& a0, hipStream_t s) {
 }
 
 template <class Tile>
-static hipError_t launch_tile(const GemmA2aArgs& a, hipStream_t s) {
+static int launch_tile(const GemmA2aArgs& a, hipStream_t s) {
   return a.out_dt == kBF16 ? launch_k<Tile, kBF16>(a, s) : launch_k<Tile, kF32>(a, s);
 }
 
-hipError_t launch_gemm_a2a(const GemmA2aArgs& a, int tile_m, hipStream_t s) {
+int launch_gemm_a2a(const GemmA2aArgs& a, int tile_m, hipStream_t s) {
   if (tile_m == 256) return launch_tile<TileBf16Direct<256, 256, 2, 2>>(a, s);
   // (128-row tiles: bf16 output only -- an fp32 staging row block does not fit their stage arrays)
   if (tile_m == 128 && a.out_dt == kBF16) return launch_k<TileBf16Direct<128, 256, 2, 2>, kBF16>(a, s);
-  return hipErrorInvalidValue;
+  return kNoKernel;
 }
 
 }  // namespace hocf

@@ -87,8 +87,7 @@ struct BandRef {
   // not wait for its flag store before counting itself, so a flag read
   // early is read again, bounded, before it counts as missing)
   __device__ __forceinline__ void verify(const GemmRsArgs& a, int tpc, uint32_t flag) const {
-    if ((int)threadIdx.x < a.P && !flag_reaches(&flags[(int64_t)threadIdx.x * tpc], flag, a.sync))
-      report_status(a.sync, kErrProtocol);
+    if ((int)threadIdx.x < a.P) expect_flag(&flags[(int64_t)threadIdx.x * tpc], flag, a.sync);
   }
   __device__ __forceinline__ void check_flags(const GemmRsArgs& a, int tpc) const {
     verify(a, tpc, my_flag(a, tpc));
@@ -217,13 +216,18 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
         const int64_t g = band_tile(pend_i);
         uint32_t e = __hip_atomic_load(&gready[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (e == 0 && !tl) {
-          // nothing else to do: wait (bounded) for the slot's tile to complete
+          // nothing else to do: wait (bounded; an abort request ends it) for
+          // the slot's tile to complete
           const Deadline wl{now_ticks(), a.sync.timeout_ticks};
-          while (e == 0 && !wl.expired()) {
+          int w = kWaitOk;
+          while (e == 0) {
             __builtin_amdgcn_s_sleep(4);
             e = __hip_atomic_load(&gready[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (e != 0) break;
+            if (abort_requested(a.sync)) { w = kWaitAborted; break; }
+            if (wl.expired()) { w = kWaitTimeout; break; }
           }
-          if (e == 0) { report_status(a.sync, kErrTimeout); state = 3; }
+          if (e == 0) { report_wait(a.sync, w); state = 3; }
         }
         if (e != 0) {
           band = (int)(g * S + pend_q);
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(Tile::NT) void unfused_fold_kernel(GemmRsArgs a) {
 }
 
 template <class Tile, bool RAGGED, bool BF16IN, int SDT, int ODT>
-static hipError_t launch_one(const GemmRsArgs& a, hipStream_t s) {
+static int launch_one(const GemmRsArgs& a, hipStream_t s) {
   auto kern = a.mode == kFusedAR ? &gemm_ar_kernel<Tile, RAGGED, BF16IN, SDT, ODT>
             : a.mode == kGemmOnly ? &unfused_gemm_kernel<Tile, RAGGED, BF16IN, SDT, ODT>
                                   : &gemm_rs_kernel<Tile, RAGGED, BF16IN, SDT, ODT>;
@@ -369,14 +373,14 @@ static hipError_t launch_one(const GemmRsArgs& a, hipStream_t s) {
   if (e != hipSuccess || a.mode != kGemmOnly) return e;
   // the fold kernel: P chunks x tiles per chunk x bands per tile workgroups
   const int64_t folds = (int64_t)a.P * a.mtiles * a.ntiles * ReduceLayout<Tile, SDT>::PIECES;
-  if (folds > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (folds > 0x7FFFFFFF) return kNoKernel;
   hipLaunchKernelGGL((unfused_fold_kernel<Tile, RAGGED, SDT, ODT>), dim3((unsigned)folds), dim3(Tile::NT), 0, s,
                      a);
   return hipGetLastError();
 }
 
 template <class Tile, bool BF16IN, int SDT, int ODT>
-static hipError_t launch_tile(const GemmRsArgs& a, hipStream_t s) {
+static int launch_tile(const GemmRsArgs& a, hipStream_t s) {
   const bool ragged = (a.Mc % Tile::TM) || (a.N % Tile::TN) || (a.K % Tile::BK);
   return ragged ? launch_one<Tile, true, BF16IN, SDT, ODT>(a, s)
                 : launch_one<Tile, false, BF16IN, SDT, ODT>(a, s);
@@ -385,33 +389,33 @@ static hipError_t launch_tile(const GemmRsArgs& a, hipStream_t s) {
 // bf16: full tiles take the direct-to-LDS mainloop, ragged ones the
 // register-staged mainloop that zero-fills the edges
 template <int TM, int TN, int SDT, int ODT>
-static hipError_t launch_bf16_dt(const GemmRsArgs& a, hipStream_t s) {
+static int launch_bf16_dt(const GemmRsArgs& a, hipStream_t s) {
   using Staged = TileBf16<TM, TN, 2, 2>;
   using Direct = TileBf16Direct<TM, TN, 2, 2>;
   // the direct tile takes full tiles whose operands it can address with 32-bit offsets
-  const bool ragged = (a.Mc % TM) || (a.N % TN) || (a.K % Direct::KSTEP) ||
+  const bool ragged = (a.Mc % TM) || (a.N % TN) || !Direct::k_fits(a.K) ||
                       !Direct::operands_fit(a.K, a.N, a.K);
   return ragged ? launch_one<Staged, true, true, SDT, ODT>(a, s)
                 : launch_one<Direct, false, true, SDT, ODT>(a, s);
 }
 
 template <int TM, int TN>
-static hipError_t launch_bf16(const GemmRsArgs& a, hipStream_t s) {
+static int launch_bf16(const GemmRsArgs& a, hipStream_t s) {
   if (a.slot_dt == kF32 && a.out_dt == kBF16) return launch_bf16_dt<TM, TN, kF32, kBF16>(a, s);
   if (a.slot_dt == kBF16 && a.out_dt == kBF16) return launch_bf16_dt<TM, TN, kBF16, kBF16>(a, s);
   if (a.slot_dt == kF32 && a.out_dt == kF32) return launch_bf16_dt<TM, TN, kF32, kF32>(a, s);
   if (a.slot_dt == kBF16 && a.out_dt == kF32) return launch_bf16_dt<TM, TN, kBF16, kF32>(a, s);
-  return hipErrorInvalidValue;
+  return kNoKernel;
 }
 
-hipError_t launch_gemm_rs(const GemmRsArgs& a, int tm, int tn, int in_dt, hipStream_t s) {
+int launch_gemm_rs(const GemmRsArgs& a, int tm, int tn, int in_dt, hipStream_t s) {
   if (in_dt == kBF16) {
     if (tm == 256 && tn == 256) return launch_bf16<256, 256>(a, s);
     if (tm == 128 && tn == 128) return launch_bf16<128, 128>(a, s);
   } else if (a.slot_dt == kF32 && a.out_dt == kF32) {
     if (tm == 64 && tn == 64) return launch_tile<TileF32<64, 64, 2, 2>, false, kF32, kF32>(a, s);
   }
-  return hipErrorInvalidValue;
+  return kNoKernel;
 }
 
 }  // namespace hocf

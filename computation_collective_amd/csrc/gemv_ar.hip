@@ -96,7 +96,7 @@ __device__ __forceinline__ void gemv_body(const GemvArArgs& a) {
   const int tid = threadIdx.x;
   const int cg = tid % NCG, kl = tid / NCG;
   const int N = a.N, K = a.K, P = a.P, Mb = a.Mb;
-  constexpr int SES = SDT == kBF16 ? 2 : 4, OES = ODT == kBF16 ? 2 : 4;
+  constexpr int SES = SDT == kBF16 ? 2 : 4;
   uint32_t* grp = a.ws + kWsExtra;
 
   for (int64_t item = blockIdx.x; item < a.total; item += gridDim.x) {
@@ -233,7 +233,7 @@ __device__ __forceinline__ void gemv_body(const GemvArArgs& a) {
     if (uniform(s_last)) {
       if (tid < P) {
         const uint32_t* f = &a.part_flags[(int64_t)tid * a.ntiles + j];
-        if (!flag_reaches(f, load_flag_agent(f), a.sync)) report_status(a.sync, kErrProtocol);
+        expect_flag(f, load_flag_agent(f), a.sync);
       }
       fold_column_tile<MB, TN, SDT, ODT>(a, j);
       wait_memory();
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kGemvThreads) void unfused_gemv_fold_kernel(GemvArA
 }
 
 template <int MB, int TN, int SDT, int ODT>
-static hipError_t launch_k(const GemvArArgs& a, hipStream_t s) {
+static int launch_k(const GemvArArgs& a, hipStream_t s) {
   auto kern = a.fused ? &gemv_ar_kernel<MB, TN, SDT, ODT> : &unfused_gemv_kernel<MB, TN, SDT, ODT>;
   int grid = 0;
   hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), kGemvThreads, a.total, &grid);
@@ -276,7 +276,7 @@ static hipError_t launch_k(const GemvArArgs& a, hipStream_t s) {
 }
 
 template <int MB, int TN>
-static hipError_t launch_dt(const GemvArArgs& a, hipStream_t s) {
+static int launch_dt(const GemvArArgs& a, hipStream_t s) {
   if (a.slot_dt == kF32 && a.out_dt == kBF16) return launch_k<MB, TN, kF32, kBF16>(a, s);
   if (a.slot_dt == kBF16 && a.out_dt == kBF16) return launch_k<MB, TN, kBF16, kBF16>(a, s);
   if (a.slot_dt == kF32 && a.out_dt == kF32) return launch_k<MB, TN, kF32, kF32>(a, s);
@@ -284,20 +284,20 @@ static hipError_t launch_dt(const GemvArArgs& a, hipStream_t s) {
 }
 
 template <int TN>
-static hipError_t launch_tn(const GemvArArgs& a, hipStream_t s) {
+static int launch_tn(const GemvArArgs& a, hipStream_t s) {
   if (a.Mb <= 1) return launch_dt<1, TN>(a, s);
   if (a.Mb <= 2) return launch_dt<2, TN>(a, s);
   if (a.Mb <= 4) return launch_dt<4, TN>(a, s);
   return launch_dt<8, TN>(a, s);
 }
 
-hipError_t launch_gemv_ar(const GemvArArgs& a, hipStream_t s) {
+int launch_gemv_ar(const GemvArArgs& a, hipStream_t s) {
   switch (a.tile_n) {
     case 128: return launch_tn<128>(a, s);
     case 256: return launch_tn<256>(a, s);
     case 512: return launch_tn<512>(a, s);
   }
-  return hipErrorInvalidValue;
+  return kNoKernel;
 }
 
 }  // namespace hocf

@@ -98,12 +98,15 @@ hipError_t device_info(DeviceInfo* out);
 // (occupancy x CUs), capped by the work available.
 hipError_t persistent_grid(const void* kernel, int threads, int64_t work, int* grid);
 
-// Each returns hipErrorInvalidValue for a tile shape it has no kernel for.
-hipError_t launch_gemm_rs(const GemmRsArgs& a, int tile_m, int tile_n, int in_dt, hipStream_t s);
-hipError_t launch_gemv_ar(const GemvArArgs& a, hipStream_t s);
-hipError_t launch_ag_gemm(const AgGemmArgs& a, int tile_m, int tile_n, hipStream_t s);
-hipError_t launch_embbag_a2a(const EmbbagArgs& a, hipStream_t s);
-hipError_t launch_gemm_a2a(const GemmA2aArgs& a, int tile_m, hipStream_t s);
+// Each returns hipSuccess, the HIP error a runtime call gave (a hipError_t
+// value), or kNoKernel when it has no kernel for the shape (found before
+// anything is enqueued).
+constexpr int kNoKernel = -1;
+int launch_gemm_rs(const GemmRsArgs& a, int tile_m, int tile_n, int in_dt, hipStream_t s);
+int launch_gemv_ar(const GemvArArgs& a, hipStream_t s);
+int launch_ag_gemm(const AgGemmArgs& a, int tile_m, int tile_n, hipStream_t s);
+int launch_embbag_a2a(const EmbbagArgs& a, hipStream_t s);
+int launch_gemm_a2a(const GemmA2aArgs& a, int tile_m, hipStream_t s);
 
 // Workspace words each operator needs.
 constexpr int64_t kWsBaseWords = kNumQueues + 1;

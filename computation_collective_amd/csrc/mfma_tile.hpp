@@ -373,6 +373,8 @@ struct TileBf16Direct {
   // (u < Side::NPASS).  The caller guarantees K / (NST * BK) >= NPASS + 2,
   // so the side work ends before the last round that loads.
   static constexpr bool side_fits(int K, int npass) { return K / (NST * BK) >= npass + 2; }
+  // K values the slice schedule covers exactly (whole rounds of NST slices)
+  static constexpr bool k_fits(int64_t K) { return K > 0 && K % KSTEP == 0; }
   // the operand loads address A's TM rows and W's K rows through 2 GiB
   // buffer resources (32-bit offsets from the tile's origin)
   static constexpr bool operands_fit(int64_t lda, int64_t ldw, int64_t K) {
@@ -408,10 +410,24 @@ struct TileBf16Direct {
           for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     }
     const int nk = K / BK;
-    // precondition (checked by the launchers): K is a multiple of NST * BK.
-    // Anything else would make the slice schedule below load past row K, so
-    // it leaves the accumulators at zero instead.
-    if (nk == 0 || nk % NST != 0 || K % BK != 0) return;
+    // precondition (every launcher checks k_fits(K) before choosing this
+    // tile): K is a multiple of NST * BK.  Anything else would make the slice
+    // schedule below load past row K; should it ever get here, nothing is
+    // loaded and the accumulators are NaN, so the result cannot pass for a
+    // product (K == 0 is the empty product: zeros).
+    if (nk == 0 || nk % NST != 0 || K % BK != 0) {
+      if constexpr (BODY) {
+        if (K != 0) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_nanf("");
+        }
+      }
+      return;
+    }
 
     // operand loads go through buffer resources over the tile's A rows and W
     // columns: a 32-bit byte offset per lane and load (fixed over K), the

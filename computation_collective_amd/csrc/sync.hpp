@@ -166,17 +166,43 @@ struct Deadline {
   __device__ __forceinline__ bool expired() const { return now_ticks() - start > ticks; }
 };
 
+// Whether the caller has asked every wait to stop (the abort word, read at
+// system scope: the host may write it while the kernel runs).
+__device__ __forceinline__ bool abort_requested(const SyncArgs& s) {
+  return s.abort_flag && load_flag_system(s.abort_flag) != 0u;
+}
+
+// Outcome of a bounded wait.
+enum WaitResult : int { kWaitOk = 0, kWaitTimeout = 1, kWaitAborted = 2 };
+
+// Records the error a failed wait stands for (first writer wins).
+__device__ __forceinline__ void report_wait(const SyncArgs& s, int w) {
+  if (w == kWaitTimeout) report_status(s, kErrTimeout);
+  else if (w == kWaitAborted) report_status(s, kErrAborted);
+}
+
 // A flag that must already hold `epoch` (its producer stored it before the
 // arrival count that led here, but without waiting for that store): read
-// again, with a bounded wait, until it does; false if it never does.
-__device__ __forceinline__ bool flag_reaches(const uint32_t* flag, uint32_t seen, const SyncArgs& s) {
-  if (seen == s.epoch) return true;
+// again, with a bounded wait that also stops on an abort request, until it
+// does.  kWaitOk once it does; otherwise why the wait ended.
+__device__ __forceinline__ int flag_reaches(const uint32_t* flag, uint32_t seen, const SyncArgs& s) {
+  if (seen == s.epoch) return kWaitOk;
   const Deadline dl{now_ticks(), s.timeout_ticks};
-  while (!dl.expired()) {
+  for (;;) {
     __builtin_amdgcn_s_sleep(2);
-    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == s.epoch) return true;
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == s.epoch) return kWaitOk;
+    if (abort_requested(s)) return kWaitAborted;
+    if (dl.expired()) return kWaitTimeout;
   }
-  return false;
+}
+
+// As flag_reaches, reporting a flag that never arrives: a producer counted
+// itself without storing its flag is a protocol error (on a timeout), an
+// abort request is reported as such.
+__device__ __forceinline__ void expect_flag(const uint32_t* flag, uint32_t seen, const SyncArgs& s) {
+  const int w = flag_reaches(flag, seen, s);
+  if (w == kWaitTimeout) report_status(s, kErrProtocol);
+  else if (w == kWaitAborted) report_status(s, kErrAborted);
 }
 
 }  // namespace hocf

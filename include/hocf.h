@@ -43,15 +43,23 @@
  * after the kernel ends.  The caller owns every buffer.
  *
  * Synchronous errors.  An invalid shape, an unsupported combination, a NULL
- * or misaligned pointer, a zero epoch or a short workspace returns an error
- * code BEFORE anything is enqueued; hocf_last_error() then describes it.
- * A launch failure returns HOCF_ERR_HIP.
+ * or misaligned pointer, a zero epoch, a short workspace, or aliasing
+ * returns an error code BEFORE anything is enqueued; hocf_last_error() then
+ * describes it.  Aliasing: every byte range a call writes (outputs, windows
+ * and their flags, partials, the workspace, the status word) may overlap no
+ * other range of the same call, read or written (HOCF_ERR_INVALID_ARG);
+ * ranges that are only read may overlap each other.  A launch failure
+ * returns HOCF_ERR_HIP.
  *
  * Asynchronous errors.  A wait that exceeds its time limit, an abort request
  * or an out-of-range embedding index is recorded in *sync->status (if
  * non-NULL) by the first workgroup that meets it (compare-and-swap from 0);
  * every workgroup still exits, and the outputs are then unspecified.  The
- * caller zeroes *status before the call and reads it after.
+ * caller zeroes *status before the call and reads it after.  Every wait of
+ * every operator (a flag or ready word that has not arrived yet) polls the
+ * abort word too and ends with HOCF_ERR_ABORTED once it is nonzero; a call
+ * that happens not to wait completes normally whatever the abort word
+ * holds.
  *
  * Flags.  Flag words are uint32 and hold an epoch: a word equals
  * sync->epoch once the data it guards is complete and visible device-wide.
@@ -109,7 +117,7 @@ typedef struct hocf_window {
 typedef struct hocf_sync {
     uint32_t epoch;               /* nonzero; differs from the previous call on the same flags */
     uint32_t* status;             /* nullable device word; first asynchronous error code */
-    const uint32_t* abort_flag;   /* nullable device or host-pinned word; nonzero stops waits */
+    const uint32_t* abort_flag;   /* nullable device or host-pinned word; nonzero ends every wait */
     uint64_t spin_timeout_ns;     /* bound of every flag wait; 0 = 1 second */
     void* workspace;              /* scheduler counters, zeroed once by the caller */
     size_t workspace_bytes;
@@ -254,7 +262,9 @@ hocf_status hocf_gemv_ar_unfused(int P, int Mb, int N, int K, hocf_dtype in_dt, 
  *   W [K][N] in_dt                out [P*Mc][N] out_dt
  *
  * Supported: in BF16, out BF16 or F32, tiles 256x256 and 128x128;
- * N and K multiples of 8.
+ * N and K multiples of 8.  HOCF_ERR_UNSUPPORTED when tile_m * N * (bytes
+ * per output element) reaches 2^31 (an output tile's row band is stored
+ * with 32-bit byte offsets).
  * ---------------------------------------------------------------------- */
 hocf_status hocf_ag_gemm(int P, int Mc, int N, int K, hocf_dtype in_dt, hocf_dtype out_dt,
                          const void* A_gathered, const uint32_t* chunk_flags, const void* W,

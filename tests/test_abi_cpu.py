@@ -14,7 +14,19 @@ HEADER = os.path.join(ROOT, "include", "hocf.h")
 
 INVALID, UNSUPPORTED, HIP = hocf.HOCF_ERR_INVALID_ARG, hocf.HOCF_ERR_UNSUPPORTED, hocf.HOCF_ERR_HIP
 F32, BF16 = hocf.HOCF_F32, hocf.HOCF_BF16
-FAKE = 0x100000          # never dereferenced: every call below fails validation first
+# Fake device addresses, never dereferenced (every call below fails validation
+# or, with no GPU, the device query that follows it): each named buffer gets
+# its own 1 TiB region, so the calls that are meant to be valid alias nothing.
+_REGIONS = {}
+
+
+def addr(name):
+    if name not in _REGIONS:
+        _REGIONS[name] = (1 << 44) + (len(_REGIONS) << 40)
+    return _REGIONS[name]
+
+
+FAKE = addr("A")         # the first operand of most calls
 
 
 def declared_functions():
@@ -39,17 +51,18 @@ def test_abi_version_and_strings():
     assert hocf.status_string(99) == "unknown status"
 
 
-def _sync(epoch=1, ws=FAKE, nbytes=1 << 20, status=None):
-    return hocf.sync(epoch, ws, nbytes, status=status)
+def _sync(epoch=1, ws=None, nbytes=1 << 20, status=None):
+    return hocf.sync(epoch, addr("ws") if ws is None else ws, nbytes, status=status)
 
 
 def _win(P):
-    return hocf.windows([(FAKE, FAKE)] * P)
+    return hocf.windows([(addr(f"win{r}"), addr(f"flags{r}")) for r in range(P)])
 
 
-def gemm(P=4, M=256, N=256, K=256, dts=(F32, F32, F32), tile=(64, 64), s=None, win=True, A=FAKE):
-    return hocf.hocf_gemm_rs(P, M, N, K, *dts, A, FAKE, _win(P) if win else None, FAKE, *tile,
-                             s if s is not None else _sync())
+def gemm(P=4, M=256, N=256, K=256, dts=(F32, F32, F32), tile=(64, 64), s=None, win=True, A=FAKE, W=None,
+         out=None):
+    return hocf.hocf_gemm_rs(P, M, N, K, *dts, A, addr("W") if W is None else W, _win(P) if win else None,
+                             addr("out") if out is None else out, *tile, s if s is not None else _sync())
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -73,8 +86,8 @@ def test_gemm_rs_rejects(kw, expect):
 def test_gemm_rs_unfused_rejects(kw, expect):
     a = dict(P=4, M=256, N=256, K=256, tile=(64, 64), A=FAKE, win=True)
     a.update(kw)
-    st = hocf.hocf_gemm_rs_unfused(a["P"], a["M"], a["N"], a["K"], F32, F32, F32, a["A"], FAKE,
-                                   _win(a["P"]) if a["win"] else None, FAKE, *a["tile"], _sync())
+    st = hocf.hocf_gemm_rs_unfused(a["P"], a["M"], a["N"], a["K"], F32, F32, F32, a["A"], addr("W"),
+                                   _win(a["P"]) if a["win"] else None, addr("out"), *a["tile"], _sync())
     assert st == expect
 
 
@@ -98,18 +111,21 @@ def test_workspace_queries():
     assert hocf.hocf_gemm_rs_workspace_bytes(3, 256, 256, 64, 64) == 0   # M % P != 0
 
 
+OUT = addr("out")
+
+
 def gemm_ar(P=4, M=256, N=256, K=256, dts=(F32, F32, F32), tile=(64, 64), outs="ok"):
     if outs == "ok":
-        outs = [FAKE + q * M * N * 4 for q in range(P)]
-    return hocf.hocf_gemm_ar(P, M, N, K, *dts, FAKE, FAKE, _win(P), outs, *tile, _sync())
+        outs = [OUT + q * M * N * 4 for q in range(P)]
+    return hocf.hocf_gemm_ar(P, M, N, K, *dts, FAKE, addr("W"), _win(P), outs, *tile, _sync())
 
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(P=0), INVALID), (dict(M=254), INVALID), (dict(tile=(128, 64)), UNSUPPORTED),
     (dict(outs=None), INVALID),
-    (dict(outs=[FAKE, 0, FAKE + 2 * 262144, FAKE + 3 * 262144]), INVALID),        # NULL output
-    (dict(outs=[FAKE, FAKE + 262144 + 8, FAKE + 2 * 262144 + 16, FAKE + 4 * 262144]), INVALID),  # misaligned
-    (dict(outs=[FAKE, FAKE + 262144 - 16, FAKE + 2 * 262144, FAKE + 3 * 262144]), INVALID),  # overlap
+    (dict(outs=[OUT, 0, OUT + 2 * 262144, OUT + 3 * 262144]), INVALID),        # NULL output
+    (dict(outs=[OUT, OUT + 262144 + 8, OUT + 2 * 262144 + 16, OUT + 4 * 262144]), INVALID),  # misaligned
+    (dict(outs=[OUT, OUT + 262144 - 16, OUT + 2 * 262144, OUT + 3 * 262144]), INVALID),  # overlap
 ])
 def test_gemm_ar_rejects(kw, expect):
     assert gemm_ar(**kw) == expect
@@ -131,10 +147,11 @@ def test_gemm_ar_valid_reaches_device():
     (dict(N=8190), INVALID), (dict(in_dt=F32), UNSUPPORTED), (dict(part=0), INVALID),
 ])
 def test_gemv_ar_rejects(kw, expect):
-    a = dict(P=8, Mb=4, N=8192, K=1024, in_dt=BF16, slot_dt=F32, out_dt=BF16, part=FAKE, tile_n=256)
+    a = dict(P=8, Mb=4, N=8192, K=1024, in_dt=BF16, slot_dt=F32, out_dt=BF16, part=addr("part"), tile_n=256)
     a.update(kw)
     st = hocf.hocf_gemv_ar(a["P"], a["Mb"], a["N"], a["K"], a["in_dt"], a["slot_dt"], a["out_dt"],
-                           FAKE, FAKE, a["part"], FAKE, _win(max(a["P"], 1)), a["tile_n"], _sync())
+                           FAKE, addr("W"), a["part"], addr("part_flags"), _win(max(a["P"], 1)), a["tile_n"],
+                           _sync())
     assert st == expect
 
 
@@ -142,32 +159,50 @@ def test_gemv_ar_rejects(kw, expect):
     (dict(P=0), INVALID), (dict(Mb=9), UNSUPPORTED), (dict(part=0), INVALID), (dict(N=8190), INVALID),
 ])
 def test_gemv_ar_unfused_rejects(kw, expect):
-    a = dict(P=8, Mb=4, N=8192, part=FAKE)
+    a = dict(P=8, Mb=4, N=8192, part=addr("part"))
     a.update(kw)
-    st = hocf.hocf_gemv_ar_unfused(a["P"], a["Mb"], a["N"], 1024, BF16, F32, BF16, FAKE, FAKE, a["part"], FAKE,
-                                   _win(max(a["P"], 1)), 256, _sync())
+    st = hocf.hocf_gemv_ar_unfused(a["P"], a["Mb"], a["N"], 1024, BF16, F32, BF16, FAKE, addr("W"), a["part"],
+                                   addr("part_flags"), _win(max(a["P"], 1)), 256, _sync())
     assert st == expect
 
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(P=0), INVALID), (dict(tile=(256, 128)), UNSUPPORTED), (dict(K=100), INVALID),
-    (dict(flags=FAKE + 2), INVALID), (dict(flags=0), INVALID),
+    (dict(flags=addr("cflags") + 2), INVALID), (dict(flags=0), INVALID),
+    (dict(N=1 << 22, out_dt=F32), UNSUPPORTED),       # a 256-row band of fp32 output rows reaches 2 GiB
+    (dict(out=FAKE + 4096), INVALID),                 # the output overlaps the gathered chunks
+    (dict(out=addr("W")), INVALID),                   # ... or W
+    (dict(flags=addr("out") + 64), INVALID),          # the chunk flags inside the output
+    (dict(s=_sync(ws=addr("out"))), INVALID),         # the workspace inside the output
 ])
 def test_ag_gemm_rejects(kw, expect):
-    a = dict(P=8, Mc=1024, N=1792, K=4096, tile=(256, 256), flags=FAKE)
+    a = dict(P=8, Mc=1024, N=1792, K=4096, tile=(256, 256), flags=addr("cflags"), out=addr("out"), out_dt=BF16,
+             s=None)
     a.update(kw)
-    st = hocf.hocf_ag_gemm(a["P"], a["Mc"], a["N"], a["K"], BF16, BF16, FAKE, a["flags"], FAKE,
-                           FAKE, *a["tile"], _sync())
+    st = hocf.hocf_ag_gemm(a["P"], a["Mc"], a["N"], a["K"], BF16, a["out_dt"], FAKE, a["flags"], addr("W"),
+                           a["out"], *a["tile"], a["s"] if a["s"] is not None else _sync())
     assert st == expect
+    assert hocf.last_error()
+
+
+def test_ag_gemm_valid_reaches_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    st = hocf.hocf_ag_gemm(8, 1024, 1792, 4096, BF16, BF16, FAKE, addr("cflags"), addr("W"), addr("out"),
+                           256, 256, _sync())
+    assert st == HIP
 
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(P=0), INVALID), (dict(B=16383), INVALID), (dict(D=126), INVALID),
     (dict(D=516), UNSUPPORTED), (dict(tile_bags=0), INVALID), (dict(tables=FAKE + 4), INVALID),
-    (dict(offsets=FAKE + 4), INVALID), (dict(indices=0), INVALID),
+    (dict(offsets=addr("offsets") + 4), INVALID), (dict(indices=0), INVALID),
+    (dict(indices=addr("win3") + 4096), INVALID),      # a window overlaps the indices
+    (dict(tables=addr("win0") - 4096), INVALID),       # ... or the tables
 ])
 def test_embbag_rejects(kw, expect):
-    a = dict(T=64, R=1000000, D=128, B=16384, L=20, P=8, tables=FAKE, indices=FAKE, offsets=None,
+    a = dict(T=64, R=1000000, D=128, B=16384, L=20, P=8, tables=FAKE, indices=addr("indices"), offsets=None,
              tile_bags=64)
     a.update(kw)
     st = hocf.hocf_embbag_a2a(a["T"], a["R"], a["D"], a["B"], a["L"], a["P"], a["tables"],
@@ -176,9 +211,10 @@ def test_embbag_rejects(kw, expect):
 
 
 def _a2a(P=2, E=2, T=512, N=256, K=256, off=(0, 256, 512), counts=(3, 4), cap=8, tile=(256, 256),
-         in_dt=BF16, out_dt=BF16, win=True, X=FAKE, dest=FAKE):
-    return hocf.hocf_gemm_a2a(P, E, T, N, K, in_dt, out_dt, X, FAKE, off, dest, FAKE, counts,
-                              _win(P) if win else None, cap, *tile, _sync())
+         in_dt=BF16, out_dt=BF16, win=True, X=FAKE, dest=None, slot=None):
+    return hocf.hocf_gemm_a2a(P, E, T, N, K, in_dt, out_dt, X, addr("W"), off,
+                              addr("dest") if dest is None else dest, addr("slot") if slot is None else slot,
+                              counts, _win(P) if win else None, cap, *tile, _sync())
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -188,7 +224,10 @@ def _a2a(P=2, E=2, T=512, N=256, K=256, off=(0, 256, 512), counts=(3, 4), cap=8,
     (dict(K=100), UNSUPPORTED), (dict(off=(0, 200, 512)), INVALID), (dict(off=(0, 256, 256)), INVALID),
     (dict(off=(0, 512, 256)), INVALID), (dict(counts=(3, 9)), INVALID), (dict(counts=(-1, 4)), INVALID),
     (dict(off=None), INVALID), (dict(counts=None), INVALID), (dict(win=False), INVALID),
-    (dict(X=0), INVALID), (dict(X=FAKE + 8), INVALID), (dict(dest=FAKE + 2), INVALID), (dict(dest=0), INVALID),
+    (dict(X=0), INVALID), (dict(X=FAKE + 8), INVALID), (dict(dest=addr("dest") + 2), INVALID),
+    (dict(dest=0), INVALID),
+    (dict(slot=addr("win1")), INVALID),               # a window overlaps the routing
+    (dict(X=addr("win0") - 256 * 512), INVALID),      # ... or the token rows
 ])
 def test_gemm_a2a_rejects(kw, expect):
     assert _a2a(**kw) == expect
@@ -214,3 +253,93 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(hocf, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         hocf.lib()
+
+
+# ---------------------------------------------------------------- aliasing
+# An output range may overlap nothing else the call touches (inputs, other
+# outputs, windows, flags, workspace, status); such calls are rejected before
+# anything is enqueued.
+
+def _gemm_rs_with_windows(pairs, **kw):
+    return hocf.hocf_gemm_rs(4, 256, 256, 256, F32, F32, F32, kw.get("A", FAKE), kw.get("W", addr("W")),
+                             hocf.windows(pairs), kw.get("out", addr("out")), 64, 64,
+                             kw.get("s", _sync()))
+
+
+def _pairs(P=4):
+    return [(addr(f"win{r}"), addr(f"flags{r}")) for r in range(P)]
+
+
+@pytest.mark.parametrize("case", ["out_is_A", "out_is_W", "out_in_window", "windows_share_data",
+                                  "flags_in_data", "flags_shared", "workspace_in_window",
+                                  "status_in_flags", "A_in_window"])
+def test_gemm_rs_rejects_aliasing(case):
+    pairs = _pairs()
+    kw = {}
+    if case == "out_is_A":
+        kw["out"] = FAKE
+    elif case == "out_is_W":
+        kw["out"] = addr("W") + 1024
+    elif case == "out_in_window":
+        kw["out"] = addr("win2") + 4096
+    elif case == "windows_share_data":
+        pairs[1] = (pairs[0][0] + 256 * 256 * 4 - 16, pairs[1][1])   # overlaps window 0's last bytes
+    elif case == "flags_in_data":
+        pairs[3] = (pairs[3][0], pairs[0][0] + 64)
+    elif case == "flags_shared":
+        pairs[2] = (pairs[2][0], pairs[1][1])
+    elif case == "workspace_in_window":
+        kw["s"] = _sync(ws=addr("win1") + 1024)
+    elif case == "status_in_flags":
+        kw["s"] = _sync(status=addr("flags0"))
+    elif case == "A_in_window":
+        kw["A"] = addr("win3")
+    assert _gemm_rs_with_windows(pairs, **kw) == INVALID
+    assert "overlap" in hocf.last_error()
+
+
+def test_gemm_rs_adjacent_ranges_accepted():
+    """Ranges that touch without overlapping are fine: slots of one allocation."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    base = addr("one_allocation")
+    wb = 256 * 256 * 4                    # one window: [P src][Mc][N] fp32 = M*N*4 bytes
+    pairs = [(base + r * wb, addr(f"flags{r}")) for r in range(4)]
+    assert _gemm_rs_with_windows(pairs, out=base + 4 * wb) == HIP
+
+
+@pytest.mark.parametrize("case", ["part_in_x", "window_is_part", "part_flags_in_window", "windows_share"])
+def test_gemv_ar_rejects_aliasing(case):
+    P, Mb, N, K = 8, 4, 8192, 1024
+    wins = [(addr(f"win{q}"), addr(f"flags{q}")) for q in range(P)]
+    part, pflags, x = addr("part"), addr("part_flags"), FAKE
+    if case == "part_in_x":
+        part = x + 1024
+    elif case == "window_is_part":
+        wins[5] = (part, wins[5][1])
+    elif case == "part_flags_in_window":
+        pflags = addr("win7") + 16
+    elif case == "windows_share":
+        wins[2] = (wins[1][0], wins[2][1])
+    st = hocf.hocf_gemv_ar(P, Mb, N, K, BF16, F32, BF16, x, addr("W"), part, pflags, hocf.windows(wins), 256,
+                           _sync())
+    assert st == INVALID
+    assert "overlap" in hocf.last_error()
+
+
+def test_gemv_ar_valid_reaches_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    st = hocf.hocf_gemv_ar(8, 4, 8192, 1024, BF16, F32, BF16, FAKE, addr("W"), addr("part"), addr("part_flags"),
+                           _win(8), 256, _sync())
+    assert st == HIP
+
+
+def test_embbag_valid_reaches_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    st = hocf.hocf_embbag_a2a(64, 1000000, 128, 16384, 20, 8, FAKE, addr("indices"), None, _win(8), 64, _sync())
+    assert st == HIP

@@ -120,6 +120,52 @@ def test_gemm_rs_full_tiles_integer_bit_exact(tm, sdt, odt):
     np.testing.assert_array_equal(bf.to_host(run.win_data, sdt), slots)
 
 
+@pytest.mark.parametrize("K,tm,sdt", [(192, 256, F32), (320, 256, BF16), (1856, 256, F32), (448, 128, F32)])
+def test_gemm_rs_full_tiles_k_not_whole_rounds_integer_bit_exact(K, tm, sdt):
+    """Full row and column tiles with K = 64 (mod 128): the direct-to-LDS
+    mainloop covers only K in whole rounds of 128, so the launcher must send
+    these to the register-staged mainloop (bit-exact on integer inputs)."""
+    P, Mc, N = 3, 2 * tm, 2 * tm
+    say(f"gemm_rs full tiles, K={K} (not a multiple of 128), integer, tile={tm} slot={sdt}")
+    ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    run, slots, out = _gemm_rs(P, Mc, N, K, BF16, sdt, BF16, tm, tm, seed=K, dist=ints)
+    np.testing.assert_array_equal(bf.to_host(run.out, BF16), out)
+    np.testing.assert_array_equal(bf.to_host(run.win_data, sdt), slots)
+
+
+@pytest.mark.parametrize("op", ["gemm_rs", "gemv_ar"])
+def test_abort_word_set_before_the_call(op):
+    """With the abort word already nonzero, every wait of the call ends at once
+    (HOCF_ERR_ABORTED) and the kernel exits; a call that happened not to wait
+    reports OK, and its result is then right (integer inputs: bit-exact)."""
+    say(f"{op} with the abort word set before the call")
+    addr, _ = hocf.host_coherent(4)
+    np.frombuffer(bf.ctypes_char_array(addr, 4), dtype=np.uint32)[0] = 1
+    ints = dict(dist_a=("int", -2, 2), dist_w=("int", -2, 2))
+    if op == "gemm_rs":
+        P, Mc, N, K = 4, 512, 512, 256
+        A, W = gen.gemm_rs_inputs(P, P * Mc, N, K, BF16, seed=21, **ints)
+        run = bf.GemmRS(P, P * Mc, N, K, BF16, F32, BF16, 256, 256, A, W)
+        _, want = oracle.gemm_rs(P, P * Mc, N, K, BF16, F32, BF16, A, W, want_slots=False)
+        got = lambda: bf.to_host(run.out, BF16)
+    else:
+        P, Mb, N, K = 8, 4, 1024, 512
+        x, W = gen.gemv_ar_inputs(P, Mb, N, K, seed=21, dist_x=("int", -2, 2), dist_w=("int", -2, 2))
+        run = bf.GemvAR(P, Mb, N, K, BF16, F32, BF16, 256, x, W)
+        _, want = oracle.gemv_ar(P, Mb, N, K, BF16, F32, BF16, x, W)
+        got = lambda: bf.to_host(run.win_data, BF16)
+    for _ in range(3):
+        run.status.zero_()
+        run.poison()
+        run.run(abort_flag=addr, spin_timeout_ns=5_000_000_000)
+        sync()
+        st = run.status_value()
+        assert st in (0, hocf.HOCF_ERR_ABORTED)
+        if st == 0:
+            np.testing.assert_array_equal(got(), want)
+        assert torch.all(run.ws == 0), "the call must leave the workspace zeroed"
+
+
 @pytest.mark.parametrize("tm", [256, 128])
 def test_gemm_rs_full_tiles_values(tm):
     P, Mc, N, K = 4, 2 * tm, 3 * tm, 512
@@ -252,6 +298,25 @@ def test_gemm_rs_many_shards_integer_bit_exact(P, tm):
     run, slots, out = _gemm_rs(P, Mc, N, K, BF16, F32, BF16, tm, tm, seed=100 + P, dist=ints)
     np.testing.assert_array_equal(bf.to_host(run.out, BF16), out)
     np.testing.assert_array_equal(bf.to_host(run.win_data, F32), slots)
+
+
+@pytest.mark.parametrize("sdt", [F32, BF16])
+def test_gemm_rs_full_mlpdown_every_element(sdt):
+    """The headline workload in the bench's launch configuration, every output
+    element and every published slot element against the full oracle."""
+    c = cfgs.GEMM_RS_MLP
+    say(f"gemm_rs full {c.name} slot={sdt} (every element)")
+    A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, BF16, seed=0)
+    run = bf.GemmRS(c.P, c.M, c.N, c.K, BF16, sdt, c.out_dt, c.tile_m, c.tile_n, A, W)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    assert torch.all(run.win_flags == run.epoch)
+    slots, out = oracle.gemm_rs(c.P, c.M, c.N, c.K, BF16, sdt, c.out_dt, A, W)
+    assert relerr(val(bf.to_host(run.out, BF16), BF16), val(out, BF16)) <= TOL[BF16]
+    del out
+    assert relerr(val(bf.to_host(run.win_data, sdt), sdt), val(slots, sdt)) <= TOL[BF16]
 
 
 @pytest.mark.parametrize("sdt", [F32, BF16])
@@ -724,6 +789,22 @@ def test_gemm_a2a_bad_slot_reported_and_skipped():
         rows_ok = np.arange(int(counts[d])) if d != d_v else np.nonzero(ok[:counts[d]])[0]
         assert relerr(val(got[d, rows_ok], BF16), val(want[d, rows_ok], BF16)) <= TOL[BF16]
     assert int(run.win_flags[d_v, 0]) != run.epoch                # its destination is incomplete
+    # the call still leaves the workspace zeroed (the incomplete destination's
+    # arrival counter included), so a valid call on it counts from zero
+    assert torch.all(run.ws == 0)
+    good = bf.GemmA2A(P, E, N, K, BF16, run.X, run.W, off, dest, slot, counts, cap)
+    good.ws, good.ws_bytes = run.ws, run.ws_bytes
+    good.win_data, good.win_flags, good.win = run.win_data, run.win_flags, run.win
+    good.epoch = run.epoch
+    run.status.zero_()
+    good.status = run.status
+    good.poison()
+    good.run()
+    sync()
+    assert good.status_value() == 0
+    assert torch.all(good.win_flags[:, 0] == good.epoch)
+    _check_a2a(good, want, counts)
+    assert torch.all(good.ws == 0)
 
 
 def test_gemm_a2a_expert_without_rows_and_no_rows_at_all():
@@ -977,7 +1058,7 @@ def test_ag_gemm_abort():
 
 def test_ag_gemm_full_colpar():
     c = cfgs.AG_GEMM_COL
-    say(f"ag_gemm full {c.name} (sampled; pre-released and host-released orders)")
+    say(f"ag_gemm full {c.name} (every element; pre-released and host-released orders)")
     chunks, W, order = _ag_inputs(c.P, c.Mc, c.N, c.K, seed=0)
     run = bf.AgGemm(c.P, c.Mc, c.N, c.K, BF16, c.tile_m, c.tile_n, chunks, W)
     run.poison()
@@ -990,12 +1071,8 @@ def test_ag_gemm_full_colpar():
     sync()
     assert host.status_value() == 0
     assert torch.equal(run.out, host.out)
-    rng = np.random.default_rng(7)
-    ms = rng.integers(0, c.P * c.Mc, 3000)
-    ns = rng.integers(0, c.N, 3000)
-    want = oracle.ag_gemm_points(c.P, c.Mc, c.N, c.K, BF16, BF16, list(chunks), W, ms, ns)
-    got = bf.to_host(run.out, BF16)[ms, ns]
-    assert relerr(val(got, BF16), val(want, BF16)) <= TOL[BF16]
+    _, want = oracle.ag_gemm(c.P, c.Mc, c.N, c.K, BF16, BF16, list(chunks), W)   # every element
+    assert relerr(val(bf.to_host(run.out, BF16), BF16), val(want, BF16)) <= TOL[BF16]
     assert not torch.isnan(run.out.view(torch.bfloat16)).any()
 
 
