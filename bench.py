@@ -5,6 +5,8 @@ One step = one pass of the whole hot path: one call of each fused operator
 at its workload size, on one HIP stream, inputs already resident in HBM:
 
   gemm_rs     GEMM+ReduceScatter, P=8, A_p 8192x1792, W_p 1792x4096 bf16, tile 256x256
+  gemm_rs_tiny  GEMM+ReduceScatter, P=4, A_p and W_p 256x256 fp32 U[-1,1), tile 64x64 (the fp32
+              matrix-core path; its roofline is the fp32 MFMA peak, its time is launch-bound)
   gemv_ar     GEMV+AllReduce, P=8, x_p 4x1024, W_p 1024x8192 bf16 (4 weight replicas rotate;
               a 1 GiB scratch read before each call, outside the timed events)
   ag_gemm     AllGather+GEMM, 8 chunks 1024x4096, W 4096x1792 bf16, chunk flags written in a
@@ -14,7 +16,10 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
               the flags (host-coherent memory) 55 us apart after the launch (--chunk-gap-us);
               after_last_arrival_us = the kernel's span minus the 385 us arrival span
   embbag_a2a  64 tables 1e6x128 fp32, batch 16384, 20 rows per bag, Zipf(1.05), P=8
-              (a 1 GiB scratch read before each call, outside the timed events)
+              (a 1 GiB scratch read before each call, outside the timed events); its roofline
+              counts the compulsory bytes (every distinct row once, the indices, the pooled
+              rows written), which no gather can go below; `logical_gbps` counts every
+              looked-up row (Zipf repeats included, served mostly by the caches)
   gemm_ar     GEMM+AllReduce, the gemm_rs shapes; the folded chunks land in all 8 windows
   gemm_a2a    GEMM+All-to-All (MoE combine): 8 ranks x 4096 tokens, top-2 of 32 experts, this
               rank's 4 experts 1792 -> 4096 bf16, each result row sent to its token's rank
@@ -46,7 +51,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused GEMM+ReduceScatter TFLOP/s & GEMV/embbag GB/s, % roofline, 1 GPU"
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 flop/clock)
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -60,8 +66,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)  # >= 200 timed calls of each operator
     ap.add_argument("--warmup", type=int, default=10)  # untimed steps first (10 calls of each operator)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
-    ap.add_argument("--ops", default="gemm_rs,gemv_ar,ag_gemm,ag_gemm_paced,embbag_a2a,gemm_ar,gemm_a2a,"
-                                     "gemm_rs_unfused,gemv_ar_unfused,hipblaslt_bmm")
+    ap.add_argument("--ops", default="gemm_rs,gemm_rs_tiny,gemv_ar,ag_gemm,ag_gemm_paced,embbag_a2a,gemm_ar,"
+                                     "gemm_a2a,gemm_rs_unfused,gemv_ar_unfused,hipblaslt_bmm")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
     ap.add_argument("--a2a-tile-m", type=int, default=0, help="GEMM+A2A tile rows (default: the config's)")
     ap.add_argument("--chunk-gap-us", type=float, default=55.0,
@@ -165,6 +171,20 @@ def main():
                                bound="mfma", peak=PEAK_BF16_TFLOPS, bytes=algo_bytes,
                                config=dict(workload=c.name, P=c.P, M=c.M, N=c.N, K=c.K,
                                            tile=[c.tile_m, c.tile_n], slot_dtype=args.slot_dtype))
+    if "gemm_rs_tiny" in ops:
+        c = cfgs.GEMM_RS_TINY
+        log(f"inputs {c.name}")
+        A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, c.in_dt, seed=0, dist_a=c.dist_a, dist_w=c.dist_w)
+        rt = bf.GemmRS(c.P, c.M, c.N, c.K, c.in_dt, c.slot_dt, c.out_dt, c.tile_m, c.tile_n, A, W)
+        algo_bytes = (4 * (c.P * c.M * c.K + c.P * c.K * c.N)      # A, W read
+                      + 2 * 4 * c.P * c.M * c.N                    # slots written + read
+                      + 4 * c.M * c.N)                             # out written
+        runs["gemm_rs_tiny"] = dict(call=lambda r=rt: r.run(stream), obj=rt, work=c.flops, unit="TFLOP/s",
+                                    variant=f"tile={c.tile_m}x{c.tile_n}", bound="mfma", peak=PEAK_F32_TFLOPS,
+                                    bytes=algo_bytes,
+                                    config=dict(workload=c.name, P=c.P, M=c.M, N=c.N, K=c.K,
+                                                tile=[c.tile_m, c.tile_n], dtype="f32",
+                                                peak_note="fp32 MFMA 157.3 TFLOP/s"))
     if "gemv_ar" in ops:
         c = cfgs.GEMV_AR_DECODE
         log(f"inputs {c.name}")
@@ -243,18 +263,24 @@ def main():
         tables = gen.embbag_tables_torch(c.T, c.R, c.D, seed=0, device=dev)
         idx = gen.zipf_indices(c.T, c.B, c.L, c.R, alpha=c.alpha, seed=0)
         e = bf.EmbbagA2A(c.T, c.R, c.D, c.B, c.L, c.P, c.tile_bags, tables, idx)
-        algo_bytes = (4 * c.T * c.B * c.L * c.D      # every looked-up row (logical, no dedup)
-                      + 4 * c.T * c.B * c.L          # indices
-                      + 4 * c.T * c.B * c.D)         # pooled rows written to the buckets
+        logical = (4 * c.T * c.B * c.L * c.D          # every looked-up row (Zipf repeats included)
+                   + 4 * c.T * c.B * c.L              # indices
+                   + 4 * c.T * c.B * c.D)             # pooled rows written to the buckets
+        uniq = sum(int(np.unique(idx[t]).size) for t in range(c.T))
+        compulsory = (4 * uniq * c.D                  # every distinct row once
+                      + 4 * c.T * c.B * c.L           # indices
+                      + 4 * c.T * c.B * c.D)          # pooled rows written to the buckets
+        del idx
         # the 1 GiB scratch read between calls (untimed: each call has its own events) keeps the
         # 256 MB Infinity Cache from carrying rows over from the previous call; reuse inside a
         # call (Zipf) is the workload's own locality
-        runs["embbag_a2a"] = dict(call=lambda e=e: e.run(stream), obj=e, work=algo_bytes, unit="GB/s",
-                                  pre=mall_flush,
+        runs["embbag_a2a"] = dict(call=lambda e=e: e.run(stream), obj=e, work=compulsory, unit="GB/s",
+                                  pre=mall_flush, logical=logical,
                                   variant=f"tile_bags={c.tile_bags}",
-                                  bound="hbm", peak=PEAK_HBM_GBS, bytes=algo_bytes,
+                                  bound="hbm", peak=PEAK_HBM_GBS, bytes=compulsory,
                                   config=dict(workload=c.name, T=c.T, R=c.R, D=c.D, B=c.B, L=c.L, P=c.P,
-                                              tile_bags=c.tile_bags, zipf_alpha=c.alpha))
+                                              tile_bags=c.tile_bags, zipf_alpha=c.alpha, distinct_rows=uniq,
+                                              bytes="compulsory: distinct rows once + indices + pooled rows"))
     if "gemm_ar" in ops:
         c = cfgs.GEMM_AR_MLP
         log(f"inputs {c.name}")
@@ -364,9 +390,11 @@ def main():
             tables = gen.embbag_tables_torch(c.T, c.R, c.D, seed=0, device=dev)
         uidx = gen.uniform_indices(c.T, c.B, c.L, c.R, seed=1)
         eu = bf.EmbbagA2A(c.T, c.R, c.D, c.B, c.L, c.P, c.tile_bags, tables, uidx)
-        algo_bytes = 4 * c.T * c.B * c.L * c.D + 4 * c.T * c.B * c.L + 4 * c.T * c.B * c.D
+        logical_u = 4 * c.T * c.B * c.L * c.D + 4 * c.T * c.B * c.L + 4 * c.T * c.B * c.D
+        uniq_u = sum(int(np.unique(uidx[t]).size) for t in range(c.T))
+        algo_bytes = 4 * uniq_u * c.D + 4 * c.T * c.B * c.L + 4 * c.T * c.B * c.D
         runs["embbag_uniform"] = dict(call=lambda e=eu: e.run(stream), obj=eu, work=algo_bytes, unit="GB/s",
-                                      pre=mall_flush, variant="uniform indices",
+                                      pre=mall_flush, variant="uniform indices", logical=logical_u,
                                       bound="hbm", peak=PEAK_HBM_GBS, bytes=algo_bytes,
                                       config=dict(workload=c.name + "_uniform_indices", T=c.T, R=c.R, D=c.D,
                                                   B=c.B, L=c.L, P=c.P, tile_bags=c.tile_bags))
@@ -436,12 +464,16 @@ def main():
                          "unit": R["unit"] if R["bound"] == "mfma" else "GB/s",
                          "frac": round(v / R["peak"], 4), "traffic": None if tb is None else int(tb)},
             "algo_bytes": R["bytes"],
-            # HBM-side rate from the profiled traffic (null until a current profile exists)
-            "dram": None if tb is None else {
+            # bytes between the L2s and the memory fabric (the FETCH_SIZE and WRITE_SIZE counters,
+            # calibrated on a copy of known size): the fabric side of the L2s, where the 256 MB
+            # Infinity Cache may still serve a part; null until a profile of the current sources exists
+            "l2_fabric": None if tb is None else {
                 "bytes": int(tb), "gbps": round(tb / (avg * 1e-3) / 1e9, 1),
-                "frac": round(tb / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                "frac_of_hbm_peak": round(tb / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
             "config": R["config"],
         }
+        if "logical" in R:
+            out_ops[n]["logical_gbps"] = round(R["logical"] / (avg * 1e-3) / 1e9, 1)
         if n == "ag_gemm_paced":
             # how long the kernel runs on after the last chunk has arrived
             out_ops[n]["after_last_arrival_us"] = round(avg * 1e3 - R["config"]["arrival_span_us"], 1)

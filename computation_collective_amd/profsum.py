@@ -15,14 +15,16 @@ GRBM_GUI_ACTIVE` -- and writes one summary per operator,
   * FETCH_SIZE and WRITE_SIZE in KiB per dispatch (median over dispatches),
     the same counters for the 1 GiB calibration pass (a negating copy that
     reads and writes 1 GiB), the factors known/measured they give, and the
-    scaled HBM bytes per launch;
+    scaled bytes per launch between the L2s and the memory fabric (which the
+    Infinity Cache may partly serve);
   * the hash of the library sources the counters were taken with, and the
     variant (slot dtype, tile) that was profiled;
   * with the MFMA run: matrix-core busy cycles summed over all SIMDs,
     GRBM_GUI_ACTIVE (reported summed over the 8 XCDs, so divided by 8 for
     one XCD's busy cycles), the MFMA utilisation busy / (XCD cycles *
-    SIMDs), the bf16 MFMA flops the kernel issued (MOPS * 512), and the
-    clock it ran at (XCD cycles / the dispatch's counter window).
+    SIMDs), the bf16 MFMA flops the kernel issued (MOPS * 512), and, for
+    dispatches of 100 us or more, the clock it ran at (XCD cycles / the
+    dispatch's counter window).
 
 `traffic(op, variant)` returns the scaled bytes, or None when there is no
 summary, it was taken for another variant, or the sources have changed.
@@ -44,7 +46,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30  # the calibration pass reads and writes 1 GiB
 
 # kernel-name fragment -> operator name used by bench.py
-KERNELS = [("gemm_rs_kernel", "gemm_rs"), ("gemm_ar_kernel", "gemm_ar"), ("gemm_a2a_kernel", "gemm_a2a"),
+KERNELS = [("gemm_rs_kernel<hocf::TileF32", "gemm_rs_tiny"), ("gemm_rs_kernel", "gemm_rs"), ("gemm_ar_kernel", "gemm_ar"), ("gemm_a2a_kernel", "gemm_a2a"),
            ("unfused_gemm_kernel", "gemm_rs_unfused_gemm"), ("unfused_fold_kernel", "gemm_rs_unfused_fold"),
            ("unfused_gemv_kernel", "gemv_ar_unfused_gemv"), ("unfused_gemv_fold_kernel", "gemv_ar_unfused_fold"), ("gemv_ar_kernel", "gemv_ar"),
            ("ag_gemm_kernel", "ag_gemm"), ("embbag_kernel", "embbag_a2a"),
@@ -56,6 +58,7 @@ def workloads():
     from . import configs as c
     return {
         "gemm_rs": (c.GEMM_RS_MLP.name, f"slot_dtype=f32 tile={c.GEMM_RS_MLP.tile_m}x{c.GEMM_RS_MLP.tile_n}"),
+        "gemm_rs_tiny": (c.GEMM_RS_TINY.name, f"tile={c.GEMM_RS_TINY.tile_m}x{c.GEMM_RS_TINY.tile_n}"),
         "gemm_rs_unfused_gemm": (c.GEMM_RS_MLP.name + "_unfused_gemm",
                                  f"slot_dtype=f32 tile={c.GEMM_RS_MLP.tile_m}x{c.GEMM_RS_MLP.tile_n}"),
         "gemm_rs_unfused_fold": (c.GEMM_RS_MLP.name + "_unfused_fold",
@@ -166,15 +169,23 @@ def summarize(stats_dir, fetch_dir, write_dir, out_dir, stats_cmd, counter_cmd, 
                  f"sources {src}",
                  f"stats calls={calls} avg_us={avg:.2f} min_us={mn:.2f} max_us={mx:.2f}"]
         if op in fetch and op in write:
+            # (FETCH_SIZE / WRITE_SIZE count traffic between the L2s and the memory fabric; the
+            # Infinity Cache behind the fabric may serve part of it, so it is an upper bound of
+            # the DRAM traffic, not a DRAM-side count)
             b = fetch[op] * 1024 * ff + write[op] * 1024 * fw
             lines.append(f"counters fetch_kib={fetch[op]:.0f} write_kib={write[op]:.0f} "
-                         f"fetch_factor={ff:.4f} write_factor={fw:.4f} hbm_bytes={b:.0f}")
+                         f"fetch_factor={ff:.4f} write_factor={fw:.4f} l2_fabric_bytes={b:.0f}")
         if op in busy and op in active and active[op] > 0:
             xcd_cycles = active[op] / XCDS
             util = busy[op] / (xcd_cycles * SIMDS)
-            lines.append(f"mfma busy_cycles={busy[op]:.0f} gui_active_cycles={active[op]:.0f} xcds={XCDS} "
-                         f"simds={SIMDS} util={util:.4f} bf16_flops={mops.get(op, 0) * 512:.0f} "
-                         f"window_us={window[op]:.1f} clock_mhz={xcd_cycles / window[op]:.0f}")
+            line = (f"mfma busy_cycles={busy[op]:.0f} gui_active_cycles={active[op]:.0f} xcds={XCDS} "
+                    f"simds={SIMDS} util={util:.4f} bf16_flops={mops.get(op, 0) * 512:.0f} "
+                    f"window_us={window[op]:.1f}")
+            # the clock only for long dispatches: a fixed overhead of some 20 k cycles per dispatch
+            # in the counter window makes it meaningless below ~100 us
+            if avg >= 100.0:
+                line += f" clock_mhz={xcd_cycles / window[op]:.0f}"
+            lines.append(line)
         with open(os.path.join(out_dir, wl + ".txt"), "w") as fh:
             fh.write("\n".join(lines) + "\n")
 
@@ -211,7 +222,7 @@ def traffic(op: str, variant: str | None = None):
     if d.get("sources") != source_hash() or d.get("variant") != (variant or wl[1]) or "counters" not in d:
         return None
     kv = dict(x.split("=") for x in d["counters"].split())
-    return float(kv["hbm_bytes"])
+    return float(kv["l2_fabric_bytes"]) if "l2_fabric_bytes" in kv else None
 
 
 if __name__ == "__main__":
