@@ -2,7 +2,12 @@
 
 Every source is compiled by hipcc into its own object (in parallel), then
 linked into ``computation_collective_amd/libhocf.so``.  The device code is
-built with packed-fp32 instructions disabled (plain fp32 arithmetic only)."""
+built with packed-fp32 instructions disabled (plain fp32 arithmetic only).
+
+The trace build, ``libhocf_trace.so``, is the same library with HOCF_TRACE
+defined in the sources that use it (the GEMM + ReduceScatter / AllReduce
+kernel records per-iteration timestamps into its workspace; see
+csrc/trace.hpp); the other objects are shared."""
 
 from __future__ import annotations
 
@@ -16,7 +21,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhocf.so")
+TRACE_LIB = os.path.join(HERE, "libhocf_trace.so")
 SOURCES = ["abi.cpp", "gemm_rs.hip", "gemv_ar.hip", "ag_gemm.hip", "embbag_a2a.hip", "gemm_a2a.hip"]
+TRACE_SOURCES = ["abi.cpp", "gemm_rs.hip"]   # the sources HOCF_TRACE changes
 ARCH = "gfx950"
 
 
@@ -33,9 +40,10 @@ def flags() -> list[str]:
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, trace: bool = False) -> str:
+    out = os.path.join(BUILD, "trace") if trace else BUILD
+    obj = os.path.join(out, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + flags() + (["-DHOCF_TRACE=1"] if trace else []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,16 +57,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Both libraries; returns the product library's path."""
+    os.makedirs(os.path.join(BUILD, "trace"), exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + [(s, True) for s in TRACE_SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    plain = dict(zip(SOURCES, objs[:len(SOURCES)]))
+    traced = dict(zip(TRACE_SOURCES, objs[len(SOURCES):]))
+    _link([plain[s] for s in SOURCES], LIB, verbose)
+    _link([traced.get(s, plain[s]) for s in SOURCES], TRACE_LIB, verbose)
     return LIB
 
 

@@ -12,6 +12,7 @@
 
 #include "../../include/hocf.h"
 #include "internal.hpp"
+#include "trace.hpp"
 
 namespace {
 
@@ -212,12 +213,22 @@ const char* hocf_last_error(void) { return g_err; }
 
 /* ------------------------------------------------------------ GEMM + RS */
 
-size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n) {
+// The GEMM + ReduceScatter / AllReduce scheduler words, in bytes.
+static size_t gemm_rs_sched_bytes(int P, int M, int N, int tile_m, int tile_n) {
   if (P <= 0 || M < 0 || N < 0 || tile_m <= 0 || tile_n <= 0 || M % P) return 0;
   const int64_t tpc = cdiv(M / P, tile_m) * cdiv(N, tile_n);
   // arrival counters [P][tpc], band queue heads and tails [8 + 8], band queues [8][P * tpc]
   return (size_t)(hocf::kWsBaseWords + (int64_t)P * tpc + 2 * hocf::kNumQueues +
                   (int64_t)hocf::kNumQueues * P * tpc) * 4;
+}
+
+// Where the trace build's per-iteration records start (after the scheduler words).
+static size_t trace_offset(size_t sched) { return (sched + 255) & ~(size_t)255; }
+
+size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n) {
+  const size_t sched = gemm_rs_sched_bytes(P, M, N, tile_m, tile_n);
+  if (!hocf::kTraceBuild || sched == 0) return sched;
+  return trace_offset(sched) + (size_t)hocf::kTraceBytes;
 }
 
 // Checks and launch shared by GEMM + ReduceScatter (one output) and GEMM +
@@ -271,6 +282,7 @@ static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, h
     add_sync(rg, sync, need);
     if ((st = rg.check(op)) != HOCF_OK) return st;
   }
+  void* ws = sync->workspace;
 
   hocf::SyncArgs sa;
   if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
@@ -280,13 +292,17 @@ static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, h
   a.nout = nout;
   a.mode = mode;
   for (int r = 0; r < P; ++r) { a.win_data[r] = win[r].data; a.win_flags[r] = win[r].flags; }
-  a.ws = static_cast<uint32_t*>(sync->workspace);
+  a.ws = static_cast<uint32_t*>(ws);
   a.P = P; a.M = M; a.N = N; a.K = K; a.Mc = M / P;
   a.slot_dt = slot_dt; a.out_dt = out_dt;
   a.mtiles = (int)cdiv(a.Mc, tile_m);
   a.ntiles = (int)cdiv(N, tile_n);
   a.total = (int64_t)P * P * a.mtiles * a.ntiles;
   a.sync = sa;
+  a.trace = nullptr;
+  if (hocf::kTraceBuild)
+    a.trace = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
+                                          trace_offset(gemm_rs_sched_bytes(P, M, N, tile_m, tile_n)));
   return launched(hocf::launch_gemm_rs(a, tile_m, tile_n, in_dt, static_cast<hipStream_t>(stream)), op);
 }
 

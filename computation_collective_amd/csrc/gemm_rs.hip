@@ -48,6 +48,7 @@
 #include "mfma_tile.hpp"
 #include "publish.hpp"
 #include "sync.hpp"
+#include "trace.hpp"
 
 namespace hocf {
 
@@ -178,6 +179,8 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
   // iteration ahead; a claimed band slot (queue, index) waits in pend_* until
   // its band has been handed out
   ClaimAhead tiles;
+  TraceSink trace;
+  trace.init(a.trace);
   int pend_q = -1;
   uint32_t pend_i = 0;
   bool band_ahead = false;
@@ -186,6 +189,7 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
   for (;;) {
     // the next tile, and a band of a completed tile to fold in this
     // iteration if one is ready (one thread-0 region between two barriers)
+    trace.mark(kTrStart);
     __syncthreads();
     if (tid == 0 && !FUSED) {
       // unfused: tiles only; the folds are a separate kernel
@@ -248,6 +252,7 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
     const int64_t item = uniform64(s_item);
     const int state = uniform(s_state);
     const int band = uniform(s_band);
+    trace.mark(kTrClaimed);
     if (item < 0) tiles_left = false;
     if (item < 0 && state != 1) {
       if (state >= 2 || !tiles_left) break;  // all bands taken, or a timeout was reported
@@ -277,6 +282,7 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
       if constexpr (kSplit) Tile::prologue(At, K, Wt, N, K, stages);
     }
     if (state == 1 && !band_in_loop) reduce_band<Tile, RAGGED, SDT, ODT>(a, band / S, band % S, nout);
+    trace.mark(kTrMainStart);
 
     if (item >= 0) {
       const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
@@ -300,6 +306,8 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
         Tile::template run<RAGGED>(At, K, Wt, N, rows_valid, cols_valid, K, stages, acc);
       }
 
+      trace.mark(kTrMainEnd);
+
       // 1. publish the tile into window r, slot p
       char* wdata = reinterpret_cast<char*>(a.win_data[r]);
       const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
@@ -307,9 +315,11 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
                                                           rows_valid, cols_valid, acc, stages);
     }
 
+    uint32_t completed = 0;  // (thread 0, trace build only)
     if (FUSED && item >= 0) {
       wait_memory();  // this thread's stores of the tile have completed
       __syncthreads();
+      trace.mark(kTrStored);
       // 2. ready flag; 3. arrival count -> the last producer hands out the bands
       if (tid == 0) {
         // (the tile's data is complete; readers of the flag re-read it, bounded,
@@ -322,9 +332,15 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
           // the last producer: the tile's bands are ready
           __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(&gready[(int64_t)r * tpc + tflag], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          completed = kTrCompleted;
         }
       }
       // (the barrier at the top of the loop ends this thread-0 region)
+    }
+    if constexpr (kTraceBuild) {
+      trace.mark(kTrDone);
+      trace.commit(item, state == 1 ? band : -1,
+                   completed | (state == 1 ? (band_in_loop ? kTrBandInLoop : kTrBandAlone) : 0u));
     }
   }
 

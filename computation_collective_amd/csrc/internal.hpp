@@ -26,6 +26,7 @@ struct GemmRsArgs {
   int mtiles, ntiles;  // tile grid of one chunk
   int64_t total;       // P (sources) * P (chunks) * mtiles * ntiles
   SyncArgs sync;
+  uint64_t* trace;     // the trace build's per-iteration records (trace.hpp), else NULL
 };
 
 struct GemvArArgs {

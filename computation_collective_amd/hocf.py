@@ -15,6 +15,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhocf.so")
+TRACE_LIB_PATH = os.path.join(HERE, "libhocf_trace.so")
 
 HOCF_OK = 0
 HOCF_ERR_INVALID_ARG = 1
@@ -56,6 +57,17 @@ class HocfError(RuntimeError):
 
 
 _lib = None
+
+
+def use_trace_library() -> None:
+    """Load the trace build (libhocf_trace.so: the GEMM + ReduceScatter /
+    AllReduce kernel records per-iteration timestamps into its workspace, and
+    their workspace queries ask for room for them) instead of the product
+    library.  Must be called before the first call into the library."""
+    global LIB_PATH
+    if _lib is not None and LIB_PATH != TRACE_LIB_PATH:
+        raise RuntimeError("the product library is already loaded")
+    LIB_PATH = TRACE_LIB_PATH
 
 
 def lib():
