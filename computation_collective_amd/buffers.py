@@ -66,8 +66,9 @@ class GemmRS(_Common):
     """hocf_gemm_rs: A [P][M][K], W [P][K][N] -> windows [P dst][P src][Mc][N], out [M][N]."""
 
     def __init__(self, P, M, N, K, in_dt, slot_dt, out_dt, tile_m, tile_n, A, W, device="cuda",
-                 unfused=False):
+                 unfused=False, noalloc=False):
         self.unfused = unfused   # hocf_gemm_rs_unfused: the GEMM kernel, then the fold kernel
+        self.noalloc = noalloc   # hocf_gemm_rs_noalloc: no workspace (the library's scratch)
         self.P, self.M, self.N, self.K = P, M, N, K
         self.in_dt, self.slot_dt, self.out_dt = in_dt, slot_dt, out_dt
         self.tile_m, self.tile_n = tile_m, tile_n
@@ -87,7 +88,11 @@ class GemmRS(_Common):
 
     def call(self, stream=None, **kw) -> int:
         s = self.next_sync(**kw)
-        fn = hocf.hocf_gemm_rs_unfused if self.unfused else hocf.hocf_gemm_rs
+        if getattr(self, "noalloc", False):
+            s.workspace, s.workspace_bytes = None, 0
+            fn = hocf.hocf_gemm_rs_noalloc
+        else:
+            fn = hocf.hocf_gemm_rs_unfused if self.unfused else hocf.hocf_gemm_rs
         return fn(self.P, self.M, self.N, self.K, self.in_dt, self.slot_dt, self.out_dt, self.A, self.W,
                   self.win, self.out, self.tile_m, self.tile_n, s, stream)
 

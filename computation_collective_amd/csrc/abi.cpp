@@ -233,10 +233,14 @@ size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n)
 
 // Checks and launch shared by GEMM + ReduceScatter (one output) and GEMM +
 // AllReduce (nout = P outputs, every one receiving all M rows).
+// With noalloc, the scheduler words live in the library's per-device
+// scratch instead of the caller's workspace (which must then be absent): it
+// is zeroed on the stream before the kernel.
 static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, hocf_dtype in_dt,
                                    hocf_dtype slot_dt, hocf_dtype out_dt, const void* A, const void* W,
                                    const hocf_window* win, void* const* outs, int nout, int mode,
-                                   int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
+                                   int tile_m, int tile_n, const hocf_sync* sync, void* stream,
+                                   bool noalloc = false) {
   if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "%s: P=%d outside [1, %d]", op, P, HOCF_MAX_P);
   if (M < 0 || N < 0 || K < 0) return fail(HOCF_ERR_INVALID_ARG, "%s: negative dimension", op);
   if (M % P) return fail(HOCF_ERR_INVALID_ARG, "%s: M=%d not divisible by P=%d", op, M, P);
@@ -255,8 +259,20 @@ static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, h
   if ((int64_t)tile_m * N * 4 >= ((int64_t)1 << 31))
     return fail(HOCF_ERR_UNSUPPORTED, "%s: tile_m * N = %lld elements per tile row band exceeds 2^29", op,
                 (long long)tile_m * N);
-  const size_t need = hocf_gemm_rs_workspace_bytes(P, M, N, tile_m, tile_n);
-  hocf_status st = check_sync(sync, need);
+  // (the no-allocation entry point holds the scheduler words only, never trace records)
+  const size_t need = noalloc ? gemm_rs_sched_bytes(P, M, N, tile_m, tile_n)
+                              : hocf_gemm_rs_workspace_bytes(P, M, N, tile_m, tile_n);
+  hocf_status st;
+  if (noalloc) {
+    if (sync && (sync->workspace || sync->workspace_bytes))
+      return fail(HOCF_ERR_INVALID_ARG, "%s: the workspace must be NULL (the library's scratch is used)", op);
+    if (need > (size_t)hocf::kNoAllocScratchBytes)
+      return fail(HOCF_ERR_UNSUPPORTED, "%s: %zu bytes of scheduler words exceed the %lld-byte scratch", op, need,
+                  (long long)hocf::kNoAllocScratchBytes);
+    st = check_sync(sync, 0);
+  } else {
+    st = check_sync(sync, need);
+  }
   if (st != HOCF_OK) return st;
   if (M == 0 || N == 0) return ok();
   if (!A || !W || !outs) return fail(HOCF_ERR_INVALID_ARG, "%s: NULL tensor", op);
@@ -279,10 +295,14 @@ static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, h
       rg.out("win.data", r, win[r].data, (int64_t)M * N * ses);  // [P src][Mc][N]
       rg.out("win.flags", r, win[r].flags, (int64_t)P * tpc * 4);
     }
-    add_sync(rg, sync, need);
+    add_sync(rg, sync, noalloc ? 0 : need);
     if ((st = rg.check(op)) != HOCF_OK) return st;
   }
   void* ws = sync->workspace;
+  if (noalloc) {
+    const hipError_t e = hocf::noalloc_scratch(&ws);
+    if (e != hipSuccess) return fail(HOCF_ERR_HIP, "%s: scratch address: %s", op, hipGetErrorString(e));
+  }
 
   hocf::SyncArgs sa;
   if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
@@ -300,9 +320,13 @@ static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, h
   a.total = (int64_t)P * P * a.mtiles * a.ntiles;
   a.sync = sa;
   a.trace = nullptr;
-  if (hocf::kTraceBuild)
+  if (hocf::kTraceBuild && !noalloc)
     a.trace = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
                                           trace_offset(gemm_rs_sched_bytes(P, M, N, tile_m, tile_n)));
+  if (noalloc) {
+    const int e = hocf::launch_zero_words(a.ws, (int64_t)(need / 4), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return launched(e, op);
+  }
   return launched(hocf::launch_gemm_rs(a, tile_m, tile_n, in_dt, static_cast<hipStream_t>(stream)), op);
 }
 
@@ -320,6 +344,14 @@ hocf_status hocf_gemm_rs_unfused(int P, int M, int N, int K, hocf_dtype in_dt, h
   void* const outs[1] = {out};
   return gemm_collective("gemm_rs_unfused", P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, 1, 2, tile_m,
                          tile_n, sync, stream);
+}
+
+hocf_status hocf_gemm_rs_noalloc(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                                 hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
+                                 void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream) {
+  void* const outs[1] = {out};
+  return gemm_collective("gemm_rs_noalloc", P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, 1, 0, tile_m,
+                         tile_n, sync, stream, true);
 }
 
 /* ------------------------------------------------------------ GEMM + AR */

@@ -42,7 +42,9 @@
 // the other queues; tiles are always claimed by running workgroups, so
 // every slot becomes ready and the kernel ends.
 // No step needs an L2-wide write-back or invalidate (publish.hpp).
+#include <mutex>
 #include <type_traits>
+#include <unordered_map>
 
 #include "internal.hpp"
 #include "mfma_tile.hpp"
@@ -432,6 +434,48 @@ int launch_gemm_rs(const GemmRsArgs& a, int tm, int tn, int in_dt, hipStream_t s
     if (tm == 64 && tn == 64) return launch_tile<TileF32<64, 64, 2, 2>, false, kF32, kF32>(a, s);
   }
   return kNoKernel;
+}
+
+// ------------------------------------------------------------------------
+// Scratch of the entry point that allocates nothing (hocf_gemm_rs_noalloc):
+// the scheduler words a caller's workspace holds otherwise, in a file-scope
+// device array.  Each device the library runs on holds its own copy until
+// the process ends; every no-allocation call on a device shares it, so such
+// calls must not overlap on one device.  In host code `scratch` names a
+// host-side stand-in, never the device memory: kernels receive the address
+// noalloc_scratch() obtained from the runtime for the current device.
+static __device__ __align__(256) uint32_t scratch[kNoAllocScratchBytes / 4];
+
+hipError_t noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static std::unordered_map<int, void*> addr;  // device -> its copy of `scratch`
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    // (once per device, with that device current)
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    it = addr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+
+// Zeroes n words at p: a kernel, not a memset, so that a caller may capture
+// the call in a HIP graph.
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+int launch_zero_words(uint32_t* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
 }
 
 }  // namespace hocf

@@ -112,4 +112,11 @@ int launch_gemm_a2a(const GemmA2aArgs& a, int tile_m, hipStream_t s);
 // Workspace words each operator needs.
 constexpr int64_t kWsBaseWords = kNumQueues + 1;
 
+// The entry point that allocates nothing: the size of its per-device
+// scratch (HOCF_NOALLOC_SCRATCH_BYTES), the device address of the current
+// device's copy, and a kernel that zeroes n words of it on a stream.
+constexpr int64_t kNoAllocScratchBytes = int64_t(1) << 20;
+hipError_t noalloc_scratch(void** out);
+int launch_zero_words(uint32_t* p, int64_t n, hipStream_t s);
+
 }  // namespace hocf

@@ -30,7 +30,7 @@ HOCF_BF16 = 1
 HOCF_MAX_P = 16
 
 EXPORTED = [
-    "hocf_gemm_rs", "hocf_gemm_rs_workspace_bytes",
+    "hocf_gemm_rs", "hocf_gemm_rs_workspace_bytes", "hocf_gemm_rs_noalloc",
     "hocf_gemm_ar", "hocf_gemm_ar_workspace_bytes", "hocf_gemm_rs_unfused",
     "hocf_gemv_ar", "hocf_gemv_ar_workspace_bytes", "hocf_gemv_ar_unfused",
     "hocf_ag_gemm", "hocf_ag_gemm_workspace_bytes",
@@ -84,6 +84,7 @@ def lib():
         L.hocf_gemm_rs.argtypes = [i, i, i, i, i, i, i, vp, vp, W, vp, i, i, S, vp]
         L.hocf_gemm_rs_workspace_bytes.argtypes = [i, i, i, i, i]
         L.hocf_gemm_rs_unfused.argtypes = [i, i, i, i, i, i, i, vp, vp, W, vp, i, i, S, vp]
+        L.hocf_gemm_rs_noalloc.argtypes = [i, i, i, i, i, i, i, vp, vp, W, vp, i, i, S, vp]
         L.hocf_gemm_ar.argtypes = [i, i, i, i, i, i, i, vp, vp, W, ctypes.POINTER(vp), i, i, S, vp]
         L.hocf_gemm_ar_workspace_bytes.argtypes = [i, i, i, i, i]
         L.hocf_gemv_ar.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, W, i, S, vp]
@@ -95,7 +96,7 @@ def lib():
         L.hocf_embbag_a2a_workspace_bytes.argtypes = []
         L.hocf_gemm_a2a.argtypes = [i, i, i64, i, i, i, i, vp, vp, vp, vp, vp, vp, W, i64, i, i, S, vp]
         L.hocf_gemm_a2a_workspace_bytes.argtypes = [i]
-        for f in ("hocf_gemm_rs", "hocf_gemm_rs_unfused", "hocf_gemm_ar", "hocf_gemv_ar", "hocf_gemv_ar_unfused", "hocf_ag_gemm",
+        for f in ("hocf_gemm_rs", "hocf_gemm_rs_unfused", "hocf_gemm_rs_noalloc", "hocf_gemm_ar", "hocf_gemv_ar", "hocf_gemv_ar_unfused", "hocf_ag_gemm",
                   "hocf_embbag_a2a", "hocf_gemm_a2a"):
             getattr(L, f).restype = i
         for f in ("hocf_gemm_rs_workspace_bytes", "hocf_gemm_ar_workspace_bytes", "hocf_gemv_ar_workspace_bytes",
@@ -202,6 +203,16 @@ def hocf_gemm_rs_unfused(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, out, til
                          stream=None) -> int:
     return lib().hocf_gemm_rs_unfused(P, M, N, K, in_dt, slot_dt, out_dt, ptr(A), ptr(W), win, ptr(out),
                                       tile_m, tile_n, ctypes.byref(sync_), _stream(stream))
+
+
+def hocf_gemm_rs_noalloc(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, out, tile_m, tile_n, sync_,
+                         stream=None) -> int:
+    """sync_.workspace must be None (the library's own scratch is used)."""
+    return lib().hocf_gemm_rs_noalloc(P, M, N, K, in_dt, slot_dt, out_dt, ptr(A), ptr(W), win, ptr(out),
+                                      tile_m, tile_n, ctypes.byref(sync_), _stream(stream))
+
+
+HOCF_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 
 def hocf_gemm_ar(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, tile_m, tile_n, sync_,

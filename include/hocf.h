@@ -156,6 +156,33 @@ hocf_status hocf_gemm_rs(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtyp
 size_t hocf_gemm_rs_workspace_bytes(int P, int M, int N, int tile_m, int tile_n);
 
 /* ------------------------------------------------------------------------
+ * GEMM + ReduceScatter that allocates nothing.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * operator, arguments, arithmetic and results as hocf_gemm_rs (bit for bit),
+ * except that the scheduler words the workspace holds come from a scratch
+ * array of HOCF_NOALLOC_SCRATCH_BYTES inside the library, one per device,
+ * held until the process ends.  sync->workspace must be NULL and
+ * sync->workspace_bytes 0; the caller still passes every input, output,
+ * window and flag array.  Each call first zeroes the scratch words it uses
+ * (with a kernel on `stream`, no memset), then enqueues the operator's
+ * kernel; neither the call nor the library ever calls hipMalloc or hipFree.
+ *
+ * The scratch is shared by every call on a device: calls that may overlap
+ * on one device (different streams, or graphs replayed concurrently) race
+ * and give unspecified results.  A shape whose scheduler words
+ * (hocf_gemm_rs_workspace_bytes) exceed the scratch returns
+ * HOCF_ERR_UNSUPPORTED before anything is enqueued: the limit is some 29,000
+ * output tiles x shards, e.g. the 8-shard 8192 x 4096 workload with 256 x 256
+ * tiles needs 147 KB.  Other errors as for hocf_gemm_rs.
+ * ---------------------------------------------------------------------- */
+#define HOCF_NOALLOC_SCRATCH_BYTES (1u << 20)
+hocf_status hocf_gemm_rs_noalloc(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                                 hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
+                                 void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream);
+
+/* ------------------------------------------------------------------------
  * GEMM + ReduceScatter, unfused (the baseline the fused operator is
  * measured against).
  *

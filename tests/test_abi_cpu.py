@@ -343,3 +343,30 @@ def test_embbag_valid_reaches_device():
         pytest.skip("GPU present")
     st = hocf.hocf_embbag_a2a(64, 1000000, 128, 16384, 20, 8, FAKE, addr("indices"), None, _win(8), 64, _sync())
     assert st == HIP
+
+
+# ---------------------------------------------------------------- no allocation
+
+def test_gemm_rs_noalloc_rejects_before_touching_the_device():
+    P, M, N, K = 4, 256, 256, 256
+    s = _sync()                                   # a caller workspace: refused
+    st = hocf.hocf_gemm_rs_noalloc(P, M, N, K, F32, F32, F32, FAKE, addr("W"), _win(P), addr("out"), 64, 64, s)
+    assert st == INVALID and "workspace" in hocf.last_error()
+    s = hocf.sync(1, None, 0)
+    # scheduler words beyond the 1 MiB scratch: 16 shards x 8192 output tiles of 128 x 128
+    Pb, Mb, Nb = 16, 16 * 128 * 64, 128 * 128
+    assert hocf.hocf_gemm_rs_workspace_bytes(Pb, Mb, Nb, 128, 128) > hocf.HOCF_NOALLOC_SCRATCH_BYTES
+    st = hocf.hocf_gemm_rs_noalloc(Pb, Mb, Nb, 256, BF16, F32, BF16, FAKE, addr("W"), _win(Pb), addr("out"),
+                                   128, 128, s)
+    assert st == UNSUPPORTED and "scratch" in hocf.last_error()
+    st = hocf.hocf_gemm_rs_noalloc(P, 254, N, K, F32, F32, F32, FAKE, addr("W"), _win(P), addr("out"), 64, 64, s)
+    assert st == INVALID                          # the same shape checks as hocf_gemm_rs
+
+
+def test_gemm_rs_noalloc_valid_reaches_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    st = hocf.hocf_gemm_rs_noalloc(4, 256, 256, 256, F32, F32, F32, FAKE, addr("W"), _win(4), addr("out"), 64, 64,
+                                   hocf.sync(1, None, 0))
+    assert st == HIP
