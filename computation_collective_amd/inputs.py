@@ -173,6 +173,23 @@ def csr_bag_offsets(T, B, max_len, seed=0, empty_frac=0.1) -> np.ndarray:
     return off
 
 
+def moe_choices(P, E, B, topk, seed=0):
+    """Top-k router choices of an expert-parallel MoE layer: int32 [P][B][topk],
+    source rank p's token b picks `topk` distinct global experts out of the
+    P*E, uniformly at random (the first topk of a random permutation)."""
+    rng = np.random.default_rng(seed)
+    return np.argsort(rng.random((P, B, P * E)), axis=2)[:, :, :topk].astype(np.int32)
+
+
+def a2a_gemm_inputs(P, B, K, E, N, dtype=BF16, seed=0, dist_x=("normal", 1.0), dist_w=("normal", 0.02)):
+    """Token rows X [P][B][K] of the P source ranks, then the local experts'
+    weights W [E][K][N]."""
+    rng = np.random.default_rng(seed + 1)
+    X = _draw(rng, (P, B, K), dist_x, dtype)
+    W = _draw(rng, (E, K, N), dist_w, dtype)
+    return X, W
+
+
 def moe_routing(P, E, B, topk, tile_m, seed=0):
     """Top-k routing of an expert-parallel MoE layer, seen from rank 0.
 
@@ -188,8 +205,7 @@ def moe_routing(P, E, B, topk, tile_m, seed=0):
     Returns (offsets int64 [E+1] (row ranges of the expert groups), dest int32
     [T] (-1 for a padding row), slot int32 [T] (-1 for padding), send_counts
     int64 [P]), T = offsets[-1]."""
-    rng = np.random.default_rng(seed)
-    choice = np.argsort(rng.random((P, B, P * E)), axis=2)[:, :, :topk]   # [d][t][k] expert ids
+    choice = moe_choices(P, E, B, topk, seed=seed)     # [d][t][k] expert ids
     local = choice < E
     d_idx, t_idx, k_idx = np.nonzero(local)            # (d, t, k) order
     experts = choice[d_idx, t_idx, k_idx]

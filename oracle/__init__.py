@@ -38,6 +38,8 @@ def _load():
         lib.oracle_gemm_ar.argtypes = [i32] * 7 + [vp] * 4
         lib.oracle_gemm_a2a.argtypes = [i32, i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64, vp]
         lib.oracle_ag_gemm.argtypes = [i32] * 6 + [vp] * 4
+        lib.oracle_a2a_gemm.argtypes = [i32] * 9 + [vp] * 3 + [i32, i64] + [vp] * 6
+        lib.oracle_a2a_gemm.restype = ctypes.c_int
         lib.oracle_ag_gemm_points.argtypes = [i32] * 6 + [vp, vp, i64, vp, vp, vp]
         lib.oracle_embbag_a2a.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp]
         lib.oracle_set_threads.argtypes = [i32]
@@ -136,6 +138,33 @@ def gemm_a2a(P, E, N, K, in_dt, out_dt, X, W, offsets, dest, slot, cap, win=None
     if rc != 0:
         raise ValueError(f"oracle_gemm_a2a rejected its arguments (rc={rc})")
     return win
+
+
+def a2a_gemm(P, E, e0, B, topk, N, K, in_dt, out_dt, X, experts, W, tile_m, cap, recv=None, Y=None,
+             dest=None, slot=None):
+    """All-to-All + GEMM (MoE dispatch + GEMM), this rank owning experts e0 .. e0+E-1.
+    Returns (recv [cap][K], Y [cap][N], offsets [E+1], dest [cap], slot [cap], send_counts [P]);
+    rows from offsets[E] on keep the contents of the arrays passed in (or zeros / -1)."""
+    _check(in_dt, X, W)
+    assert X.shape == (P, B, K) and W.shape == (E, K, N)
+    experts = np.ascontiguousarray(experts, dtype=np.int32)
+    assert experts.shape == (P, B, topk)
+    if recv is None:
+        recv = np.zeros((cap, K), dtype=_np_dt(in_dt))
+    if Y is None:
+        Y = np.zeros((cap, N), dtype=_np_dt(out_dt))
+    if dest is None:
+        dest = np.full(cap, -1, dtype=np.int32)
+    if slot is None:
+        slot = np.full(cap, -1, dtype=np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    send_counts = np.zeros(P, dtype=np.int64)
+    rc = _load().oracle_a2a_gemm(P, E, e0, B, topk, N, K, in_dt, out_dt, _ptr(X), _ptr(experts), _ptr(W),
+                                 tile_m, cap, _ptr(recv), _ptr(Y), _ptr(offsets), _ptr(dest), _ptr(slot),
+                                 _ptr(send_counts))
+    if rc != 0:
+        raise ValueError(f"oracle_a2a_gemm rejected its arguments (rc={rc})")
+    return recv, Y, offsets, dest, slot, send_counts
 
 
 def gemv_ar(P, Mb, N, K, in_dt, slot_dt, out_dt, x, W):

@@ -280,6 +280,97 @@ int oracle_gemm_a2a(int P, int E, int64_t T, int N, int K, int in_dt, int out_dt
     return 0;
 }
 
+/* ---- All-to-All + GEMM (MoE dispatch + GEMM) -------------------------------
+ * The mKernel news item (section on its five fused kernels) lists MoE
+ * Dispatch + GEMM: the All-to-All that delivers each token row to the rank
+ * holding each expert its router picked, followed by the expert GEMM.  One
+ * rank's share: P source ranks each hold B tokens X[p][b] ([K] each) and
+ * their top-k choices experts[p][b][j] (global expert ids); this rank owns
+ * experts e0 .. e0+E-1.
+ * Dispatch (this rank's side of the All-to-All, the standard semantics: what
+ * every source sends here, in source-rank order):
+ *   - the rows of local expert e are the pairs (p, b, j) with
+ *     experts[p][b][j] == e0 + e, in (p, b, j) order;
+ *   - the groups follow one another in expert order, each padded with zero
+ *     rows to a multiple of tile_m (the block-aligned layout of a grouped
+ *     GEMM): offsets[0] = 0, offsets[e+1] = offsets[e] + ceil(n_e / tile_m)
+ *     * tile_m;
+ *   - recv[offsets[e] + i] = X[p][b] for the i-th pair of expert e;
+ *   - dest[row] = p (where the result goes back) and slot[row] = the pair's
+ *     position among source p's pairs that land here, in (b, j) order;
+ *     padding rows have dest = slot = -1; send_counts[p] = source p's pairs
+ *     that land here.
+ * GEMM: Y[row] = recv[row] . W_e (fp64, k ascending, rounded once to out_dt),
+ * padding rows included (they are zero).
+ *   X [P][B][K], W [E][K][N] of in_dt; experts [P][B][topk] int32 (ids outside
+ *   [e0, e0+E) are other ranks' experts); recv [cap][K] of in_dt, Y [cap][N]
+ *   of out_dt, dest and slot [cap] int32, offsets [E+1] and send_counts [P]
+ *   int64.  Rows from offsets[E] to cap are left as they were;
+ *   offsets[E] > cap is an error (-1, nothing written). */
+int oracle_a2a_gemm(int P, int E, int e0, int B, int topk, int N, int K, int in_dt, int out_dt,
+                    const void* X, const int32_t* experts, const void* W, int tile_m, int64_t cap,
+                    void* recv, void* Y, int64_t* offsets, int32_t* dest, int32_t* slot,
+                    int64_t* send_counts) {
+    if (P <= 0 || E <= 0 || B < 0 || topk < 0 || N < 0 || K < 0 || tile_m <= 0 || cap < 0) return -1;
+    if (!dt_ok(in_dt) || !dt_ok(out_dt)) return -1;
+    const int in_es = in_dt == DT_BF16 ? 2 : 4;
+
+    /* pairs per local expert, then the padded group offsets */
+    int64_t* n = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    int64_t* next = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    if (!n || !next) { free(n); free(next); return -1; }
+    for (int64_t i = 0; i < (int64_t)P * B * topk; ++i) {
+        const int64_t e = (int64_t)experts[i] - e0;
+        if (e >= 0 && e < E) n[e] += 1;
+    }
+    int64_t total = 0;
+    for (int e = 0; e < E; ++e) total += (n[e] + tile_m - 1) / tile_m * tile_m;
+    if (total > cap) { free(n); free(next); return -1; }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + (n[e] + tile_m - 1) / tile_m * tile_m;
+
+    /* every pair in (p, b, j) order takes the next row of its expert's group */
+    for (int p = 0; p < P; ++p) {
+        int64_t s = 0;   /* source p's pairs that land here so far */
+        for (int b = 0; b < B; ++b)
+            for (int j = 0; j < topk; ++j) {
+                const int64_t e = (int64_t)experts[((int64_t)p * B + b) * topk + j] - e0;
+                if (e < 0 || e >= E) continue;
+                const int64_t row = offsets[e] + next[e]++;
+                memcpy((char*)recv + row * K * in_es, (const char*)X + ((int64_t)p * B + b) * K * in_es,
+                       (size_t)K * in_es);
+                dest[row] = p;
+                slot[row] = (int32_t)s++;
+            }
+        send_counts[p] = s;
+    }
+    /* the padding rows of every group */
+    for (int e = 0; e < E; ++e)
+        for (int64_t row = offsets[e] + n[e]; row < offsets[e + 1]; ++row) {
+            memset((char*)recv + row * K * in_es, 0, (size_t)K * in_es);
+            dest[row] = -1;
+            slot[row] = -1;
+        }
+    free(n);
+    free(next);
+
+    /* the expert GEMM, row by row */
+    for (int e = 0; e < E; ++e) {
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t row = offsets[e]; row < offsets[e + 1]; ++row) {
+            double* acc = (double*)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+            for (int64_t k = 0; k < K; ++k) {
+                const double a = load_in(recv, in_dt, row * K + k);
+                const int64_t wrow = ((int64_t)e * K + k) * N;
+                for (int64_t c = 0; c < N; ++c) acc[c] += a * load_in(W, in_dt, wrow + c);
+            }
+            for (int64_t c = 0; c < N; ++c) store_f32_as(Y, out_dt, row * N + c, (float)acc[c]);
+            free(acc);
+        }
+    }
+    return 0;
+}
+
 /* ---- GEMV + AllReduce -----------------------------------------------------
  * x [P][Mb][K], W [P][K][N].  Shard p computes y_p = x_p . W_p (Mb x N),
  * carried in slot_dt; the AllReduce folds y_0..y_{P-1} in rank order in fp32,

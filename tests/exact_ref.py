@@ -103,6 +103,31 @@ def gemm_a2a(P, E, N, K, X, W, offsets, dest, slot, cap, out_fmt):
     return win
 
 
+def a2a_gemm(P, E, e0, B, topk, N, K, X, experts, W, tile_m, out_fmt):
+    """MoE dispatch + GEMM by enumeration: for each local expert, the pairs
+    (p, b, j) that chose it, listed in (p, b, j) order; the group padded to a
+    multiple of tile_m; a pair's slot = its index in the list of its source's
+    pairs that choose any local expert.  Returns (rows, offsets, send_counts)
+    with rows[i] = (dest, slot, token row as a list, Y row as Fractions); a
+    padding row is (-1, -1, None, zeros)."""
+    local = lambda v: e0 <= v < e0 + E
+    per_source = [[(b, j) for b in range(B) for j in range(topk) if local(experts[p][b][j])] for p in range(P)]
+    rows, offsets = [], [0]
+    for e in range(E):
+        pairs = [(p, b, j) for p in range(P) for b in range(B) for j in range(topk) if experts[p][b][j] == e0 + e]
+        for (p, b, j) in pairs:
+            y = []
+            for n in range(N):
+                s = sum((fr(X[p][b][k]) * fr(W[e][k][n]) for k in range(K)), Fraction(0))
+                v = round_to(s, FP32)
+                y.append(round_to(v, out_fmt) if out_fmt is BF16 else v)
+            rows.append((p, per_source[p].index((b, j)), list(X[p][b]), y))
+        pad = -len(pairs) % tile_m
+        rows += [(-1, -1, None, [Fraction(0)] * N)] * pad
+        offsets.append(offsets[-1] + len(pairs) + pad)
+    return rows, offsets, [len(per_source[p]) for p in range(P)]
+
+
 def gemv_ar(P, Mb, N, K, x, W, slot_fmt, out_fmt):
     """Returns (part[p][b][n], win[q][b][n])."""
     part = [[[None] * N for _ in range(Mb)] for _ in range(P)]

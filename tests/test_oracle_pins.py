@@ -543,3 +543,118 @@ def test_generator_seeded():
     a2, w2 = gen.gemm_rs_inputs(2, 4, 4, 4, BF16, seed=0)
     np.testing.assert_array_equal(a1, a2)
     np.testing.assert_array_equal(w1, w2)
+
+
+# ------------------------------------------------------------------ All-to-All + GEMM (MoE dispatch + GEMM)
+
+@pytest.mark.parametrize("g", _golden("a2a_gemm"))
+def test_a2a_gemm_golden(g):
+    X, W = _arr(g["X"], g["in_dt"]), _arr(g["W"], g["in_dt"])
+    recv, Y, off, dest, slot, counts = oracle.a2a_gemm(
+        g["P"], g["E"], g["e0"], g["B"], g["topk"], g["N"], g["K"], g["in_dt"], g["out_dt"], X,
+        np.asarray(g["experts"], np.int32), W, g["tile_m"], g["cap"])
+    np.testing.assert_array_equal(off, g["offsets"])
+    np.testing.assert_array_equal(dest, g["dest"])
+    np.testing.assert_array_equal(slot, g["slot"])
+    np.testing.assert_array_equal(counts, g["send_counts"])
+    np.testing.assert_array_equal(_val(recv, g["in_dt"]), np.asarray(g["recv"], np.float64))
+    np.testing.assert_array_equal(_val(Y, g["out_dt"]), np.asarray(g["Y"], np.float64))
+
+
+def _dispatch_case(P, E, B, topk, K, N, in_dt, seed, e0=0, **dist):
+    experts = gen.moe_choices(P, E, B, topk, seed=seed)
+    X, W = gen.a2a_gemm_inputs(P, B, K, E, N, dtype=in_dt, seed=seed, **dist)
+    return experts, X, W
+
+
+@pytest.mark.parametrize("P,E,e0,B,topk,tile_m,N,K", [(1, 1, 0, 3, 1, 2, 2, 3), (2, 2, 2, 4, 2, 3, 3, 2),
+                                                     (3, 2, 0, 5, 2, 4, 2, 3), (2, 3, 3, 6, 3, 1, 1, 4)])
+@pytest.mark.parametrize("in_dt,out_dt", [(F32, F32), (BF16, BF16), (BF16, F32)])
+def test_a2a_gemm_bruteforce(P, E, e0, B, topk, tile_m, N, K, in_dt, out_dt):
+    """The oracle against an enumeration written from the definition (exact
+    rationals, IEEE rounding by hand), layout bit-exact, values bit-exact
+    (<= 1 ulp for fp32 inputs, whose fp64 sum may round)."""
+    experts, X, W = _dispatch_case(P, E, B, topk, K, N, in_dt, seed=P * 7 + E + B, e0=e0)
+    cap = P * B * topk + E * tile_m
+    recv, Y, off, dest, slot, counts = oracle.a2a_gemm(P, E, e0, B, topk, N, K, in_dt, out_dt, X, experts, W,
+                                                       tile_m, cap)
+    rows, eoff, ecounts = ex.a2a_gemm(P, E, e0, B, topk, N, K, _val(X, in_dt).tolist(), experts.tolist(),
+                                      _val(W, in_dt).tolist(), tile_m, ex.BF16 if out_dt == BF16 else ex.FP32)
+    assert off.tolist() == eoff and counts.tolist() == ecounts
+    Xv, Yv = _val(recv, in_dt), _val(Y, out_dt)
+    for i, (d, s_, xrow, y) in enumerate(rows):
+        assert (int(dest[i]), int(slot[i])) == (d, s_)
+        np.testing.assert_array_equal(Xv[i], np.zeros(K) if xrow is None else np.asarray(xrow, np.float64))
+        for n in range(N):
+            want = float(y[n])
+            if in_dt == BF16:
+                assert Yv[i, n] == want
+            else:
+                assert abs(Yv[i, n] - want) <= np.spacing(np.float32(abs(want)))
+    assert len(rows) == off[-1]
+    assert np.all(dest[off[-1]:] == -1) and np.all(Yv[off[-1]:] == 0)   # untouched past the groups
+
+
+def test_a2a_gemm_layout_matches_the_combine_routing():
+    """The dispatch's layout (groups, dest, slot, send counts) equals the
+    routing the GEMM + All-to-All combine receives for the same router
+    choices (inputs.moe_routing, written separately as that operator's input
+    generator): what the dispatch delivers is what the combine sends back."""
+    P, E, B, topk, tile_m = 8, 4, 256, 2, 32
+    experts, X, W = _dispatch_case(P, E, B, topk, 16, 8, BF16, seed=23)
+    off_c, dest_c, slot_c, counts_c = gen.moe_routing(P, E, B, topk, tile_m, seed=23)
+    cap = int(off_c[-1]) + 64
+    recv, Y, off, dest, slot, counts = oracle.a2a_gemm(P, E, 0, B, topk, 8, 16, BF16, BF16, X, experts, W,
+                                                       tile_m, cap)
+    np.testing.assert_array_equal(off, off_c)
+    np.testing.assert_array_equal(counts, counts_c)
+    np.testing.assert_array_equal(dest[:off[-1]], dest_c)
+    np.testing.assert_array_equal(slot[:off[-1]], slot_c)
+
+
+def test_a2a_gemm_buckets_and_closed_form():
+    """Every pair choosing a local expert lands in exactly one row of that
+    expert's group, carrying its token row; groups are whole tiles in (p, b,
+    j) order; each group's Y is its rows times the expert's W (numpy fp64);
+    rows past the groups keep what was there (NaN prefill)."""
+    P, E, e0, B, topk, tile_m, N, K = 4, 3, 3, 64, 3, 16, 24, 40
+    experts, X, W = _dispatch_case(P, E, B, topk, K, N, BF16, seed=31, e0=e0)
+    cap = 600
+    Ypre = np.full((cap, N), np.nan, np.float32)
+    recv, Y, off, dest, slot, counts = oracle.a2a_gemm(P, E, e0, B, topk, N, K, BF16, F32, X, experts, W,
+                                                       tile_m, cap, Y=Ypre)
+    Xv, Wv = _val(X, BF16), _val(W, BF16)
+    seen = np.zeros((P, B, topk), np.int64)
+    for e in range(E):
+        assert (off[e + 1] - off[e]) % tile_m == 0
+        grp = range(off[e], off[e + 1])
+        real = [i for i in grp if dest[i] >= 0]
+        assert real == list(range(off[e], off[e] + len(real)))          # padding only at the end
+        keys = []
+        for i in real:
+            p = int(dest[i])
+            b, j = [(b, j) for b in range(B) for j in range(topk) if experts[p, b, j] >= e0
+                    and experts[p, b, j] < e0 + E][slot[i]]
+            assert experts[p, b, j] == e0 + e
+            seen[p, b, j] += 1
+            keys.append((p, b, j))
+            np.testing.assert_array_equal(_val(recv[i], BF16), Xv[p, b])
+        assert keys == sorted(keys)
+        Ye = _val(recv[off[e]:off[e + 1]], BF16) @ Wv[e]
+        assert _normwise(Y[off[e]:off[e + 1]].astype(np.float64), Ye) <= 1e-6
+    local = (experts >= e0) & (experts < e0 + E)
+    assert np.all(seen[local] == 1) and np.all(seen[~local] == 0)
+    assert counts.tolist() == local.reshape(P, -1).sum(axis=1).tolist()
+    assert np.isnan(Y[off[-1]:]).all()
+
+
+def test_a2a_gemm_capacity_and_no_local_pairs():
+    P, E, B, topk, N, K = 2, 2, 8, 2, 4, 4
+    experts, X, W = _dispatch_case(P, E, B, topk, K, N, F32, seed=2)
+    n_local = int(((experts >= 0) & (experts < E)).sum())
+    with pytest.raises(ValueError):                   # more rows than the receive buffer holds
+        oracle.a2a_gemm(P, E, 0, B, topk, N, K, F32, F32, X, experts, W, 1, n_local - 1)
+    none = np.full_like(experts, 2 * E)               # every pair chose another rank's expert
+    recv, Y, off, dest, slot, counts = oracle.a2a_gemm(P, E, 0, B, topk, N, K, F32, F32, X, none, W, 4, 8)
+    assert off.tolist() == [0] * (E + 1) and counts.tolist() == [0] * P
+    assert np.all(dest == -1) and np.all(Y == 0)
