@@ -23,9 +23,13 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
   gemm_ar     GEMM+AllReduce, the gemm_rs shapes; the folded chunks land in all 8 windows
   gemm_a2a    GEMM+All-to-All (MoE combine): 8 ranks x 4096 tokens, top-2 of 32 experts, this
               rank's 4 experts 1792 -> 4096 bf16, each result row sent to its token's rank
+  a2a_gemm    All-to-All+GEMM (MoE dispatch): the same routing; the rows chosen for this rank's 4
+              experts are counted, placed and delivered on the device, grouped by expert, and
+              projected 4096 -> 1792 bf16 as their row tiles complete
   gemm_rs_unfused, gemv_ar_unfused  the gemm_rs / gemv_ar workloads as two kernels (the
               computation publishing its partials, then the fold): the bulk-synchronous
               baseline; `fusion` reports the time each fused operator saves against it
+  a2a_gemm_unfused  the dispatch delivering every row, then the expert GEMM (two kernels)
 
 hipblaslt_bmm: context, not an operator of this library -- torch.bmm (hipBLASLt) on the same
 eight shard GEMMs as gemm_rs, with no collective.
@@ -67,7 +71,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)  # untimed steps first (10 calls of each operator)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--ops", default="gemm_rs,gemm_rs_tiny,gemv_ar,ag_gemm,ag_gemm_paced,embbag_a2a,gemm_ar,"
-                                     "gemm_a2a,gemm_rs_unfused,gemv_ar_unfused,hipblaslt_bmm")
+                                     "gemm_a2a,a2a_gemm,gemm_rs_unfused,gemv_ar_unfused,a2a_gemm_unfused,"
+                                     "hipblaslt_bmm")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
     ap.add_argument("--a2a-tile-m", type=int, default=0, help="GEMM+A2A tile rows (default: the config's)")
     ap.add_argument("--chunk-gap-us", type=float, default=55.0,
@@ -314,6 +319,32 @@ def main():
                                 config=dict(workload=c.name, P=c.P, E=c.E, B=c.B, topk=c.topk, N=c.N, K=c.K,
                                             cap=c.cap, rows=rows, padded_rows=int(off[-1]),
                                             tile=[atm, c.tile_n]))
+    for a2g_op in ("a2a_gemm", "a2a_gemm_unfused"):
+        if a2g_op not in ops:
+            continue
+        # the MoE dispatch: routing (counts, prefix sums, row placement) and row delivery on the
+        # device, then the expert GEMM; the unfused form delivers every row before any tile starts
+        c = cfgs.A2A_GEMM_MOE
+        log(f"inputs {c.name}" + (" (unfused)" if a2g_op.endswith("unfused") else ""))
+        experts = gen.moe_choices(c.P, c.E, c.B, c.topk, seed=0)
+        X, W = gen.a2a_gemm_inputs(c.P, c.B, c.K, c.E, c.N, seed=0)
+        dg = bf.A2aGemm(c.P, c.E, 0, c.B, c.topk, c.N, c.K, bf.BF16, X, experts, W, c.cap, tile_m=c.tile_m,
+                        unfused=a2g_op.endswith("unfused"))
+        del X, W
+        n_e = np.bincount(experts[experts < c.E].ravel(), minlength=c.E)
+        rows = int(n_e.sum())
+        padded = int(sum(-(-int(n) // c.tile_m) * c.tile_m for n in n_e))
+        flops = 2.0 * rows * c.N * c.K                        # the routed rows (padding rows excluded)
+        algo_bytes = (4 * c.P * c.B * c.topk                  # router choices
+                      + 2 * rows * c.K                        # token rows read
+                      + 2 * 2 * padded * c.K                  # received rows written, then read by the GEMM
+                      + 2 * c.E * c.K * c.N                   # W read
+                      + 2 * padded * c.N)                     # Y written
+        runs[a2g_op] = dict(call=lambda r=dg: r.run(stream), obj=dg, work=flops, unit="TFLOP/s", bound="mfma",
+                            variant=f"tile={c.tile_m}x{c.tile_n}", peak=PEAK_BF16_TFLOPS, bytes=algo_bytes,
+                            config=dict(workload=c.name + ("_unfused" if a2g_op.endswith("unfused") else ""),
+                                        P=c.P, E=c.E, B=c.B, topk=c.topk, N=c.N, K=c.K, cap=c.cap, rows=rows,
+                                        padded_rows=padded, tile=[c.tile_m, c.tile_n]))
     if "gemm_rs_unfused" in ops:
         # the baseline of the fused operator: the same GEMM, then a separate fold kernel
         c = cfgs.GEMM_RS_MLP
@@ -501,7 +532,7 @@ def main():
     }
     # fused against unfused (the computation, then the collective) on the same GPU
     fusion = {}
-    for op in ("gemm_rs", "gemv_ar"):
+    for op in ("gemm_rs", "gemv_ar", "a2a_gemm"):
         if op in out_ops and op + "_unfused" in out_ops:
             f, u = out_ops[op]["ms_avg"], out_ops[op + "_unfused"]["ms_avg"]
             fusion[op] = {"fused_ms": f, "unfused_ms": u, "time_saved": round(1.0 - f / u, 4)}

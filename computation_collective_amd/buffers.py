@@ -297,3 +297,44 @@ class GemmA2A(_Common):
 
     def run(self, stream=None, **kw):
         hocf.check(self.call(stream, **kw))
+
+
+class A2aGemm(_Common):
+    """hocf_a2a_gemm: token rows X [P][B][K] and router choices [P][B][topk] of the
+    P source ranks, this rank's experts W [E][K][N] (global ids e0 ..) -> the
+    received rows recv [cap][K] grouped by expert, Y [cap][N], expert_offsets
+    [E+1], dest / slot [cap], send_counts [P]."""
+
+    def __init__(self, P, E, e0, B, topk, N, K, out_dt, X, experts, W, cap, tile_m=256, device="cuda",
+                 unfused=False):
+        self.P, self.E, self.e0, self.B, self.topk, self.N, self.K = P, E, e0, B, topk, N, K
+        self.out_dt, self.cap, self.tile_m, self.unfused = out_dt, cap, tile_m, unfused
+        self.X = X if isinstance(X, torch.Tensor) else to_device(X, device)
+        self.W = W if isinstance(W, torch.Tensor) else to_device(W, device)
+        self.experts = experts if isinstance(experts, torch.Tensor) else \
+            to_device(np.ascontiguousarray(experts, dtype=np.int32), device)
+        self.recv = torch.empty((cap, K), dtype=torch.int16, device=device)
+        self.Y = torch.empty((cap, N), dtype=tdtype(out_dt), device=device)
+        self.offsets = torch.empty(E + 1, dtype=torch.int64, device=device)
+        self.dest = torch.empty(cap, dtype=torch.int32, device=device)
+        self.slot = torch.empty(cap, dtype=torch.int32, device=device)
+        self.send_counts = torch.empty(P, dtype=torch.int64, device=device)
+        self._alloc_sync(hocf.hocf_a2a_gemm_workspace_bytes(P, E, B, topk, cap, tile_m), device)
+
+    def poison(self):
+        nan_fill(self.recv)
+        nan_fill(self.Y)
+        self.dest.fill_(-77)        # (not -1: that is what padding rows get)
+        self.slot.fill_(-77)
+        self.offsets.fill_(-7)
+        self.send_counts.fill_(-7)
+
+    def call(self, stream=None, **kw) -> int:
+        s = self.next_sync(**kw)
+        return hocf.hocf_a2a_gemm(self.P, self.E, self.e0, self.B, self.topk, self.N, self.K, BF16, self.out_dt,
+                                  self.X, self.experts, self.W, self.cap, self.recv, self.Y, self.offsets,
+                                  self.dest, self.slot, self.send_counts, self.tile_m, 256, s, stream,
+                                  unfused=self.unfused)
+
+    def run(self, stream=None, **kw):
+        hocf.check(self.call(stream, **kw))

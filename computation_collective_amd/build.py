@@ -22,7 +22,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhocf.so")
 TRACE_LIB = os.path.join(HERE, "libhocf_trace.so")
-SOURCES = ["abi.cpp", "gemm_rs.hip", "gemv_ar.hip", "ag_gemm.hip", "embbag_a2a.hip", "gemm_a2a.hip"]
+SOURCES = ["abi.cpp", "gemm_rs.hip", "gemv_ar.hip", "ag_gemm.hip", "embbag_a2a.hip", "gemm_a2a.hip",
+           "a2a_gemm.hip"]
 TRACE_SOURCES = ["abi.cpp", "gemm_rs.hip"]   # the sources HOCF_TRACE changes
 ARCH = "gfx950"
 

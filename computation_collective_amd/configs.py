@@ -126,3 +126,24 @@ GEMM_A2A_MOE = GemmA2A("gemm_a2a_moe_p8_e4_b4096_top2_1792x4096_bf16", P=8, E=4,
                        N=4096, K=1792, cap=2048)
 
 ALL = [GEMM_RS_TINY, GEMV_AR_DECODE, GEMM_RS_MLP, AG_GEMM_COL, EMBBAG_DLRM]
+
+
+@dataclass(frozen=True)
+class A2aGemm:
+    name: str
+    P: int          # source ranks
+    E: int          # experts per rank (P * E in all); this rank owns experts 0 .. E-1
+    B: int          # tokens per source rank
+    topk: int       # experts per token
+    N: int          # expert hidden width (output of the up projection)
+    K: int          # model width
+    cap: int        # rows of the receive buffer
+    tile_m: int = 256
+    tile_n: int = 256
+
+
+# All-to-All + GEMM, the MoE dispatch: 8 ranks x 4096 tokens, top-2 of 32 experts; the rows
+# routed to this rank's 4 experts arrive grouped by expert and are projected 4096 -> 1792
+# (the up projection; the GEMM + All-to-All combine above is the matching down projection).
+A2A_GEMM_MOE = A2aGemm("a2a_gemm_moe_p8_e4_b4096_top2_4096x1792_bf16", P=8, E=4, B=4096, topk=2,
+                       N=1792, K=4096, cap=12288)

@@ -205,6 +205,7 @@ const char* hocf_status_string(hocf_status s) {
     case HOCF_ERR_ABORTED: return "aborted";
     case HOCF_ERR_BAD_INDEX: return "embedding index out of range";
     case HOCF_ERR_PROTOCOL: return "partial consumed before its flag was set";
+    case HOCF_ERR_CAPACITY: return "more rows routed here than the receive buffer holds";
   }
   return "unknown status";
 }
@@ -456,6 +457,130 @@ hocf_status hocf_gemm_a2a(int P, int E, int64_t T, int N, int K, hocf_dtype in_d
   a.total = (int)items;
   a.sync = sa;
   return launched(hocf::launch_gemm_a2a(a, tile_m, static_cast<hipStream_t>(stream)), "gemm_a2a");
+}
+
+/* ------------------------------------------------------------ A2A + GEMM */
+
+// Router-entry chunks: kA2gChunk entries of one source each (at least one per source).
+static int64_t a2g_chunks_per_source(int B, int topk) {
+  const int64_t n = cdiv((int64_t)B * topk, hocf::kA2gChunk);
+  return n > 0 ? n : 1;
+}
+
+size_t hocf_a2a_gemm_workspace_bytes(int P, int E, int B, int topk, int64_t cap, int tile_m) {
+  if (P <= 0 || E <= 0 || B < 0 || topk < 0 || cap < 0 || tile_m <= 0) return 0;
+  const int64_t C = (int64_t)P * a2g_chunks_per_source(B, topk);
+  // misc [4 + 8 tile queues], hist and base [C][E+1] each, group rows [E+1], pairs [E], tiles [E+1],
+  // arrivals [cap / tile_m]
+  return (size_t)(hocf::kWsBaseWords + 4 + hocf::kNumQueues + 2 * C * (E + 1) + 3 * (int64_t)E + 2 +
+                  cap / tile_m) * 4;
+}
+
+static hocf_status a2a_gemm_call(const char* op, bool fused, int P, int E, int e0, int B, int topk, int N, int K,
+                                 hocf_dtype in_dt, hocf_dtype out_dt, const void* X, const int32_t* experts,
+                                 const void* W, int64_t cap, void* recv, void* Y, int64_t* expert_offsets,
+                                 int32_t* dest, int32_t* slot, int64_t* send_counts, int tile_m, int tile_n,
+                                 const hocf_sync* sync, void* stream) {
+  if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "%s: P=%d outside [1, %d]", op, P, HOCF_MAX_P);
+  if (E < 1 || E > hocf::kMaxExperts)
+    return fail(HOCF_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", op, E, hocf::kMaxExperts);
+  if (B < 0 || topk < 0 || N < 0 || K < 0 || cap < 0) return fail(HOCF_ERR_INVALID_ARG, "%s: negative size", op);
+  if (!dt_ok(in_dt) || !dt_ok(out_dt)) return fail(HOCF_ERR_INVALID_ARG, "%s: unknown dtype", op);
+  if (in_dt != HOCF_BF16) return fail(HOCF_ERR_UNSUPPORTED, "%s: inputs must be bf16", op);
+  if ((tile_m != 256 && tile_m != 128) || tile_n != 256)
+    return fail(HOCF_ERR_UNSUPPORTED, "%s: tile %dx%d (256x256 or 128x256 only)", op, tile_m, tile_n);
+  if (tile_m == 128 && out_dt != HOCF_BF16)
+    return fail(HOCF_ERR_UNSUPPORTED, "%s: 128-row tiles take bf16 output only", op);
+  if (N % 256 || K % 128)
+    return fail(HOCF_ERR_UNSUPPORTED, "%s: N=%d must be a multiple of 256 and K=%d of 128", op, N, K);
+  const int oes = out_dt == HOCF_BF16 ? 2 : 4;
+  if ((int64_t)P * B * topk >= ((int64_t)1 << 31) || cap >= ((int64_t)1 << 31))
+    return fail(HOCF_ERR_UNSUPPORTED, "%s: router entries or receive rows reach 2^31", op);
+  if ((int64_t)K * N * 2 >= ((int64_t)1 << 31) || ((int64_t)tile_m * K + K) * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)tile_m * N * oes >= ((int64_t)1 << 31))
+    return fail(HOCF_ERR_UNSUPPORTED, "%s: an expert's W, a row tile or an output tile reaches 2 GiB", op);
+  const size_t need = hocf_a2a_gemm_workspace_bytes(P, E, B, topk, cap, tile_m);
+  hocf_status st = check_sync(sync, need);
+  if (st != HOCF_OK) return st;
+  if (!expert_offsets || !send_counts) return fail(HOCF_ERR_INVALID_ARG, "%s: NULL offsets or send counts", op);
+  if ((reinterpret_cast<uintptr_t>(expert_offsets) | reinterpret_cast<uintptr_t>(send_counts)) & 7u)
+    return fail(HOCF_ERR_INVALID_ARG, "%s: offsets and send counts must be 8-byte aligned", op);
+  if ((int64_t)B * topk > 0) {
+    if (!experts) return fail(HOCF_ERR_INVALID_ARG, "%s: NULL router choices", op);
+    if (reinterpret_cast<uintptr_t>(experts) & 3u)
+      return fail(HOCF_ERR_INVALID_ARG, "%s: router choices must be 4-byte aligned", op);
+    if (K > 0 && (!X || !aligned16(X))) return fail(HOCF_ERR_INVALID_ARG, "%s: X NULL or not 16-byte aligned", op);
+  }
+  if (cap > 0) {
+    if (!dest || !slot || ((reinterpret_cast<uintptr_t>(dest) | reinterpret_cast<uintptr_t>(slot)) & 3u))
+      return fail(HOCF_ERR_INVALID_ARG, "%s: dest and slot must be 4-byte aligned device arrays", op);
+    if (K > 0 && (!recv || !aligned16(recv)))
+      return fail(HOCF_ERR_INVALID_ARG, "%s: recv NULL or not 16-byte aligned", op);
+    if (N > 0 && (!Y || !aligned16(Y))) return fail(HOCF_ERR_INVALID_ARG, "%s: Y NULL or not 16-byte aligned", op);
+    if (N > 0 && K > 0 && (!W || !aligned16(W)))
+      return fail(HOCF_ERR_INVALID_ARG, "%s: W NULL or not 16-byte aligned", op);
+  }
+  {
+    Ranges rg;
+    rg.in("X", 0, X, (int64_t)P * B * K * 2);
+    rg.in("experts", 0, experts, (int64_t)P * B * topk * 4);
+    rg.in("W", 0, W, (int64_t)E * K * N * 2);
+    rg.out("recv", 0, recv, cap * K * 2);
+    rg.out("Y", 0, Y, cap * N * oes);
+    rg.out("expert_offsets", 0, expert_offsets, (int64_t)(E + 1) * 8);
+    rg.out("dest", 0, dest, cap * 4);
+    rg.out("slot", 0, slot, cap * 4);
+    rg.out("send_counts", 0, send_counts, (int64_t)P * 8);
+    add_sync(rg, sync, need);
+    if ((st = rg.check(op)) != HOCF_OK) return st;
+  }
+
+  hocf::SyncArgs sa;
+  if ((st = to_sync_args(sync, &sa)) != HOCF_OK) return st;
+  hocf::A2aGemmArgs a{};
+  a.X = static_cast<const uint16_t*>(X);
+  a.experts = experts;
+  a.W = static_cast<const uint16_t*>(W);
+  a.recv = static_cast<uint16_t*>(recv);
+  a.Y = Y;
+  a.expert_offsets = expert_offsets;
+  a.dest = dest; a.slot = slot;
+  a.send_counts = send_counts;
+  a.cps = (int)a2g_chunks_per_source(B, topk);
+  a.C = P * a.cps;
+  uint32_t* w = static_cast<uint32_t*>(sync->workspace) + hocf::kWsBaseWords;
+  a.misc = w;
+  a.hist = a.misc + 4 + hocf::kNumQueues;
+  a.base = a.hist + (int64_t)a.C * (E + 1);
+  a.grp = a.base + (int64_t)a.C * (E + 1);
+  a.cnt = a.grp + (E + 1);
+  a.toff = a.cnt + E;
+  a.arrivals = a.toff + (E + 1);
+  a.cap = cap;
+  a.P = P; a.E = E; a.e0 = e0; a.B = B; a.topk = topk; a.N = N; a.K = K; a.out_dt = out_dt;
+  a.tile_m = tile_m;
+  a.ntiles = N / tile_n;
+  a.nrt = (int)(cap / tile_m);
+  a.max_tiles = (int64_t)a.nrt * a.ntiles;
+  a.sync = sa;
+  return launched(hocf::launch_a2a_gemm(a, fused, static_cast<hipStream_t>(stream)), op);
+}
+
+hocf_status hocf_a2a_gemm(int P, int E, int e0, int B, int topk, int N, int K, hocf_dtype in_dt, hocf_dtype out_dt,
+                          const void* X, const int32_t* experts, const void* W, int64_t cap, void* recv, void* Y,
+                          int64_t* expert_offsets, int32_t* dest, int32_t* slot, int64_t* send_counts, int tile_m,
+                          int tile_n, const hocf_sync* sync, void* stream) {
+  return a2a_gemm_call("a2a_gemm", true, P, E, e0, B, topk, N, K, in_dt, out_dt, X, experts, W, cap, recv, Y,
+                       expert_offsets, dest, slot, send_counts, tile_m, tile_n, sync, stream);
+}
+
+hocf_status hocf_a2a_gemm_unfused(int P, int E, int e0, int B, int topk, int N, int K, hocf_dtype in_dt,
+                                  hocf_dtype out_dt, const void* X, const int32_t* experts, const void* W,
+                                  int64_t cap, void* recv, void* Y, int64_t* expert_offsets, int32_t* dest,
+                                  int32_t* slot, int64_t* send_counts, int tile_m, int tile_n, const hocf_sync* sync,
+                                  void* stream) {
+  return a2a_gemm_call("a2a_gemm_unfused", false, P, E, e0, B, topk, N, K, in_dt, out_dt, X, experts, W, cap, recv,
+                       Y, expert_offsets, dest, slot, send_counts, tile_m, tile_n, sync, stream);
 }
 
 /* ------------------------------------------------------------ GEMV + AR */

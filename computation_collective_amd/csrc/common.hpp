@@ -101,7 +101,7 @@ __device__ __forceinline__ int opaque_lane() {
 }
 
 // Status codes the kernels record (values of hocf_status).
-constexpr uint32_t kErrTimeout = 4, kErrAborted = 5, kErrBadIndex = 6, kErrProtocol = 7;
+constexpr uint32_t kErrTimeout = 4, kErrAborted = 5, kErrBadIndex = 6, kErrProtocol = 7, kErrCapacity = 8;
 
 // Synchronisation arguments common to every kernel.
 struct SyncArgs {

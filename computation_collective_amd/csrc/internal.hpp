@@ -88,6 +88,33 @@ struct GemmA2aArgs {
   SyncArgs sync;
 };
 
+// All-to-All + GEMM (the MoE dispatch): router entries are taken in chunks
+// of kA2gChunk of one source rank.
+constexpr int kA2gChunk = 256;
+
+struct A2aGemmArgs {
+  const uint16_t* X;        // [P][B][K] token rows of the source ranks
+  const int32_t* experts;   // [P][B][topk] global expert ids
+  const uint16_t* W;        // [E][K][N]
+  uint16_t* recv;           // [cap][K] received rows, grouped by local expert
+  void* Y;                  // [cap][N] out_dt
+  int64_t* expert_offsets;  // [E+1]
+  int32_t* dest;            // [cap]
+  int32_t* slot;            // [cap]
+  int64_t* send_counts;     // [P]
+  // workspace (uint32): misc words [0] scatter claim counter, [1] nonzero
+  // when the rows exceed cap, [2] expert tiles, [3] spare, [4..12) the tile
+  // queues' claim counters (one per XCD); per chunk a histogram and its exclusive scan ([C][E+1]: local
+  // experts, then pairs landing here from the chunk); per expert the group's
+  // first row [E+1], its pairs [E], its first tile [E+1]; per row tile the
+  // rows that have landed [nrt]
+  uint32_t *misc, *hist, *base, *grp, *cnt, *toff, *arrivals;
+  int64_t cap;
+  int P, E, e0, B, topk, N, K, out_dt, tile_m, ntiles, C, cps, nrt;
+  int64_t max_tiles;  // tiles the grid is sized for: (cap / tile_m) * ntiles
+  SyncArgs sync;
+};
+
 // Device properties the launches need, cached per device.
 struct DeviceInfo {
   int cus = 0;
@@ -108,6 +135,7 @@ int launch_gemv_ar(const GemvArArgs& a, hipStream_t s);
 int launch_ag_gemm(const AgGemmArgs& a, int tile_m, int tile_n, hipStream_t s);
 int launch_embbag_a2a(const EmbbagArgs& a, hipStream_t s);
 int launch_gemm_a2a(const GemmA2aArgs& a, int tile_m, hipStream_t s);
+int launch_a2a_gemm(const A2aGemmArgs& a, bool fused, hipStream_t s);
 
 // Workspace words each operator needs.
 constexpr int64_t kWsBaseWords = kNumQueues + 1;

@@ -25,6 +25,7 @@ HOCF_ERR_TIMEOUT = 4
 HOCF_ERR_ABORTED = 5
 HOCF_ERR_BAD_INDEX = 6
 HOCF_ERR_PROTOCOL = 7
+HOCF_ERR_CAPACITY = 8
 HOCF_F32 = 0
 HOCF_BF16 = 1
 HOCF_MAX_P = 16
@@ -36,6 +37,7 @@ EXPORTED = [
     "hocf_ag_gemm", "hocf_ag_gemm_workspace_bytes",
     "hocf_embbag_a2a", "hocf_embbag_a2a_workspace_bytes",
     "hocf_gemm_a2a", "hocf_gemm_a2a_workspace_bytes",
+    "hocf_a2a_gemm", "hocf_a2a_gemm_unfused", "hocf_a2a_gemm_workspace_bytes",
     "hocf_status_string", "hocf_last_error", "hocf_abi_version",
 ]
 
@@ -96,6 +98,11 @@ def lib():
         L.hocf_embbag_a2a_workspace_bytes.argtypes = []
         L.hocf_gemm_a2a.argtypes = [i, i, i64, i, i, i, i, vp, vp, vp, vp, vp, vp, W, i64, i, i, S, vp]
         L.hocf_gemm_a2a_workspace_bytes.argtypes = [i]
+        for f in ("hocf_a2a_gemm", "hocf_a2a_gemm_unfused"):
+            getattr(L, f).argtypes = [i] * 9 + [vp] * 3 + [i64] + [vp] * 6 + [i, i, S, vp]
+            getattr(L, f).restype = i
+        L.hocf_a2a_gemm_workspace_bytes.argtypes = [i, i, i, i, i64, i]
+        L.hocf_a2a_gemm_workspace_bytes.restype = sz
         for f in ("hocf_gemm_rs", "hocf_gemm_rs_unfused", "hocf_gemm_rs_noalloc", "hocf_gemm_ar", "hocf_gemv_ar", "hocf_gemv_ar_unfused", "hocf_ag_gemm",
                   "hocf_embbag_a2a", "hocf_gemm_a2a"):
             getattr(L, f).restype = i
@@ -249,6 +256,19 @@ def hocf_embbag_a2a(T, R, D, B, L, P, tables, indices, offsets, win, tile_bags, 
 
 def hocf_gemm_a2a_workspace_bytes(P) -> int:
     return lib().hocf_gemm_a2a_workspace_bytes(P)
+
+
+def hocf_a2a_gemm_workspace_bytes(P, E, B, topk, cap, tile_m) -> int:
+    return lib().hocf_a2a_gemm_workspace_bytes(P, E, B, topk, cap, tile_m)
+
+
+def hocf_a2a_gemm(P, E, e0, B, topk, N, K, in_dt, out_dt, X, experts, W, cap, recv, Y, expert_offsets, dest,
+                  slot, send_counts, tile_m, tile_n, sync_, stream=None, unfused=False) -> int:
+    """All-to-All + GEMM (MoE dispatch + GEMM); every array a device buffer."""
+    fn = lib().hocf_a2a_gemm_unfused if unfused else lib().hocf_a2a_gemm
+    return fn(P, E, e0, B, topk, N, K, in_dt, out_dt, ptr(X), ptr(experts), ptr(W), cap, ptr(recv), ptr(Y),
+              ptr(expert_offsets), ptr(dest), ptr(slot), ptr(send_counts), tile_m, tile_n, ctypes.byref(sync_),
+              _stream(stream))
 
 
 def _host_i64(a):

@@ -50,6 +50,9 @@ KERNELS = [("gemm_rs_kernel<hocf::TileF32", "gemm_rs_tiny"), ("gemm_rs_kernel", 
            ("unfused_gemm_kernel", "gemm_rs_unfused_gemm"), ("unfused_fold_kernel", "gemm_rs_unfused_fold"),
            ("unfused_gemv_kernel", "gemv_ar_unfused_gemv"), ("unfused_gemv_fold_kernel", "gemv_ar_unfused_fold"), ("gemv_ar_kernel", "gemv_ar"),
            ("ag_gemm_kernel", "ag_gemm"), ("embbag_kernel", "embbag_a2a"),
+           ("a2a_gemm_kernel<hocf::TileBf16Direct<256, 256, 2, 2, 32, 4>, 1, true, true>", "a2a_gemm"),
+           ("a2a_gemm_kernel<hocf::TileBf16Direct<256, 256, 2, 2, 32, 4>, 1, true, false>", "a2a_gemm_unfused_scatter"),
+           ("a2a_gemm_kernel<hocf::TileBf16Direct<256, 256, 2, 2, 32, 4>, 1, false, true>", "a2a_gemm_unfused_gemm"),
            ("neg_kernel", "copy")]
 
 
@@ -72,6 +75,11 @@ def workloads():
         "gemv_ar": (c.GEMV_AR_DECODE.name, f"tile_n={c.GEMV_AR_DECODE.tile_n} weight_replicas=4"),
         "ag_gemm": (c.AG_GEMM_COL.name, f"tile={c.AG_GEMM_COL.tile_m}x{c.AG_GEMM_COL.tile_n} prereleased"),
         "embbag_a2a": (c.EMBBAG_DLRM.name, f"tile_bags={c.EMBBAG_DLRM.tile_bags}"),
+        "a2a_gemm": (c.A2A_GEMM_MOE.name, f"tile={c.A2A_GEMM_MOE.tile_m}x{c.A2A_GEMM_MOE.tile_n}"),
+        "a2a_gemm_unfused_scatter": (c.A2A_GEMM_MOE.name + "_unfused_scatter",
+                                     f"tile={c.A2A_GEMM_MOE.tile_m}x{c.A2A_GEMM_MOE.tile_n}"),
+        "a2a_gemm_unfused_gemm": (c.A2A_GEMM_MOE.name + "_unfused_gemm",
+                                  f"tile={c.A2A_GEMM_MOE.tile_m}x{c.A2A_GEMM_MOE.tile_n}"),
     }
 
 
@@ -202,6 +210,7 @@ def _fields(path):
 
 # bench operators whose timed call launches several kernels
 COMPOSITE = {"gemm_rs_unfused": ("gemm_rs_unfused_gemm", "gemm_rs_unfused_fold"),
+             "a2a_gemm_unfused": ("a2a_gemm_unfused_scatter", "a2a_gemm_unfused_gemm"),
              "gemv_ar_unfused": ("gemv_ar_unfused_gemv", "gemv_ar_unfused_fold")}
 
 

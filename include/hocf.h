@@ -1,7 +1,7 @@
 /*
  * hocf — computations fused with their collective epilogue, on one MI355X.
  *
- * C ABI of libhocf.so.  Six operators, each one GPU's share of a P-way
+ * C ABI of libhocf.so.  Seven operators, each one GPU's share of a P-way
  * tensor-parallel (or model-parallel) step with the P logical shards'
  * receive windows in local HBM:
  *
@@ -19,6 +19,8 @@
  *   hocf_ag_gemm     AllGather + GEMM       (mKernel news item, same section)
  *   hocf_embbag_a2a  embedding bag + All-to-All (SC24 abstract)
  *   hocf_gemm_a2a    GEMM + All-to-All, the MoE combine (SC24 abstract)
+ *   hocf_a2a_gemm    All-to-All + GEMM, the MoE dispatch (mKernel news item,
+ *                    section on its five fused kernels)
  *
  * The method (SC24 abstract; mKernel, section on persistent kernels and
  * tile/chunk overlap): the workgroups of one kernel each finish an output
@@ -103,7 +105,8 @@ typedef enum hocf_status {
     HOCF_ERR_TIMEOUT = 4,     /* (async) a flag wait exceeded sync->spin_timeout_ns */
     HOCF_ERR_ABORTED = 5,     /* (async) *sync->abort_flag became nonzero during a wait */
     HOCF_ERR_BAD_INDEX = 6,   /* (async) an embedding index outside [0, R) was skipped */
-    HOCF_ERR_PROTOCOL = 7     /* (async) a reducer found a partial's flag not set */
+    HOCF_ERR_PROTOCOL = 7,    /* (async) a reducer found a partial's flag not set */
+    HOCF_ERR_CAPACITY = 8     /* (async) more rows routed here than the receive buffer holds */
 } hocf_status;
 
 typedef enum hocf_dtype { HOCF_F32 = 0, HOCF_BF16 = 1 } hocf_dtype;
@@ -336,6 +339,59 @@ hocf_status hocf_gemm_a2a(int P, int E, int64_t T, int N, int K, hocf_dtype in_d
                           const int32_t* slot, const int64_t* send_counts, const hocf_window* win,
                           int64_t cap, int tile_m, int tile_n, const hocf_sync* sync, void* stream);
 size_t hocf_gemm_a2a_workspace_bytes(int P);
+
+/* ------------------------------------------------------------------------
+ * All-to-All + GEMM (the mixture-of-experts dispatch, then the expert GEMM).
+ *
+ * The mKernel news item ("GPU-vezérelt kommunikációval gyorsítják az
+ * AI-betanítást a kutatók", section on its five fused kernels) lists MoE
+ * Dispatch + GEMM.  One rank's share: P source ranks each hold B tokens
+ * X[p][b] ([K] each) and their router's top-k choices experts[p][b][j]
+ * (global expert ids); this rank owns experts e0 .. e0+E-1.  The dispatch
+ * delivers, for each local expert e in turn, the token rows of the pairs
+ * (p, b, j) that chose it, in (p, b, j) order, the group padded with zero
+ * rows to a multiple of tile_m; then each group is multiplied by its
+ * expert's W_e (fp32 accumulation, rounded once to out_dt).  Counting,
+ * prefix sums, row placement and the row copies all run on the device; an
+ * expert tile starts as soon as its tile_m rows have landed, while other
+ * workgroups still deliver rows.
+ *
+ *   X         [P][B][K] in_dt          experts  [P][B][topk] int32 (ids
+ *             outside [e0, e0+E) belong to other ranks and are skipped)
+ *   W         [E][K][N] in_dt
+ *   recv      [cap][K] in_dt: the received rows, grouped by expert
+ *   Y         [cap][N] out_dt: recv . W_e, group by group (padding rows: 0)
+ *   expert_offsets  device int64 [E+1]: group e is rows [o_e, o_{e+1});
+ *             o_E = rows used (a multiple of tile_m per group)
+ *   dest, slot  device int32 [cap]: the source rank of each row and its
+ *             position among that source's pairs landing here, in (b, j)
+ *             order (-1 for padding): the routing GEMM + All-to-All takes to
+ *             send each result row back
+ *   send_counts device int64 [P]: each source's pairs landing here
+ * Rows from o_E to cap are left as they were.  When the rows would exceed
+ * cap, HOCF_ERR_CAPACITY goes to the status word, expert_offsets and
+ * send_counts are written, and nothing else is.
+ *
+ * Supported: in BF16; tile 256x256 with out BF16 or F32, tile 128x256 with
+ * out BF16; N a multiple of 256, K of 128; 1 <= E <= 64.  The workspace
+ * (hocf_a2a_gemm_workspace_bytes) needs no zeroing: each call initialises
+ * what it uses.  Three kernels are enqueued (counts, scans, the fused
+ * dispatch + GEMM).
+ * ---------------------------------------------------------------------- */
+hocf_status hocf_a2a_gemm(int P, int E, int e0, int B, int topk, int N, int K, hocf_dtype in_dt, hocf_dtype out_dt,
+                          const void* X, const int32_t* experts, const void* W, int64_t cap, void* recv, void* Y,
+                          int64_t* expert_offsets, int32_t* dest, int32_t* slot, int64_t* send_counts, int tile_m,
+                          int tile_n, const hocf_sync* sync, void* stream);
+size_t hocf_a2a_gemm_workspace_bytes(int P, int E, int B, int topk, int64_t cap, int tile_m);
+
+/* The same, unfused (the baseline): the dispatch as one kernel, then the
+ * expert GEMM as the next (no tile overlaps the row delivery); the same
+ * arguments and results, bit for bit. */
+hocf_status hocf_a2a_gemm_unfused(int P, int E, int e0, int B, int topk, int N, int K, hocf_dtype in_dt,
+                                  hocf_dtype out_dt, const void* X, const int32_t* experts, const void* W,
+                                  int64_t cap, void* recv, void* Y, int64_t* expert_offsets, int32_t* dest,
+                                  int32_t* slot, int64_t* send_counts, int tile_m, int tile_n,
+                                  const hocf_sync* sync, void* stream);
 
 /* ------------------------------------------------------------------------
  * Embedding bag + All-to-All.

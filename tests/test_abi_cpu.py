@@ -370,3 +370,41 @@ def test_gemm_rs_noalloc_valid_reaches_device():
     st = hocf.hocf_gemm_rs_noalloc(4, 256, 256, 256, F32, F32, F32, FAKE, addr("W"), _win(4), addr("out"), 64, 64,
                                    hocf.sync(1, None, 0))
     assert st == HIP
+
+
+# ---------------------------------------------------------------- All-to-All + GEMM
+
+def _a2g(P=8, E=4, e0=0, B=4096, topk=2, N=1792, K=4096, in_dt=BF16, out_dt=BF16, cap=12288, tile=(256, 256),
+         X=None, experts=None, recv=None, Y=None, offs=None, dest=None, unfused=False, s=None):
+    return hocf.hocf_a2a_gemm(P, E, e0, B, topk, N, K, in_dt, out_dt, X or FAKE, experts or addr("experts"),
+                              addr("W"), cap, recv or addr("recv"), Y or addr("Y"), offs or addr("offsets"),
+                              dest or addr("dest"), addr("slot"), addr("send_counts"), *tile,
+                              s if s is not None else _sync(nbytes=1 << 24), unfused=unfused)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(P=0), INVALID), (dict(P=17), INVALID), (dict(E=0), INVALID), (dict(E=65), INVALID),
+    (dict(B=-1), INVALID), (dict(in_dt=F32), UNSUPPORTED), (dict(tile=(64, 256)), UNSUPPORTED),
+    (dict(tile=(128, 256), out_dt=F32), UNSUPPORTED), (dict(N=1800), UNSUPPORTED), (dict(K=4000), UNSUPPORTED),
+    (dict(s=_sync(nbytes=64)), INVALID),                  # workspace too small
+    (dict(offs=addr("offsets") + 4), INVALID),           # offsets not 8-byte aligned
+    (dict(experts=addr("experts") + 2), INVALID),
+    (dict(X=FAKE + 8), INVALID),
+    (dict(recv=FAKE + 4096), INVALID),                   # the receive buffer overlaps the token rows
+    (dict(Y=addr("recv") + 1024), INVALID),              # Y overlaps the receive buffer
+    (dict(dest=addr("experts")), INVALID),               # dest overlaps the router choices
+    (dict(unfused=True, P=0), INVALID),
+])
+def test_a2a_gemm_rejects(kw, expect):
+    assert _a2g(**kw) == expect
+    assert hocf.last_error()
+
+
+def test_a2a_gemm_valid_reaches_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    assert _a2g() == HIP and _a2g(unfused=True) == HIP
+    C = 8 * 32
+    assert hocf.hocf_a2a_gemm_workspace_bytes(8, 4, 4096, 2, 12288, 256) == \
+        (8 + 1 + 4 + 8 + 2 * C * 5 + 3 * 4 + 2 + 12288 // 256) * 4

@@ -1275,3 +1275,152 @@ def test_thousand_calls_bit_identical(op, monkeypatch):
         call = lambda i: (r.poison(), r.run())
     assert _repeat_identical(call, outs) == 0
     assert r.status_value() == 0
+
+
+# ====================================================================== A2A + GEMM (MoE dispatch)
+
+def _a2g_case(P, E, e0, B, topk, N, K, seed, dist=None):
+    experts = gen.moe_choices(P, E, B, topk, seed=seed)
+    X, W = gen.a2a_gemm_inputs(P, B, K, E, N, seed=seed, **(dist or {}))
+    return experts, X, W
+
+
+def _a2g_check(run, want, integer=False):
+    """Layout, received rows and dest/slot bit-exact; Y within tolerance (bit-exact
+    for integer inputs); rows past the groups untouched (poison)."""
+    recv_o, Y_o, off_o, dest_o, slot_o, cnt_o = want
+    off = run.offsets.cpu().numpy()
+    np.testing.assert_array_equal(off, off_o)
+    np.testing.assert_array_equal(run.send_counts.cpu().numpy(), cnt_o)
+    T = int(off[-1])
+    np.testing.assert_array_equal(run.dest.cpu().numpy()[:T], dest_o[:T])
+    np.testing.assert_array_equal(run.slot.cpu().numpy()[:T], slot_o[:T])
+    np.testing.assert_array_equal(bf.to_host(run.recv, BF16)[:T], recv_o[:T])
+    Y = bf.to_host(run.Y, run.out_dt)
+    if T:
+        if integer:
+            np.testing.assert_array_equal(Y[:T], Y_o[:T])
+        else:
+            assert relerr(val(Y[:T], run.out_dt), val(Y_o[:T], run.out_dt)) <= TOL[BF16]
+    assert np.all(run.dest.cpu().numpy()[T:] == -77), "rows past the groups were written"
+    if T < run.cap:
+        assert np.isnan(val(Y[T:], run.out_dt)).all()
+
+
+@pytest.mark.parametrize("P,E,e0,B,topk,N,K,odt,tm", [
+    (2, 2, 0, 100, 2, 256, 128, BF16, 256),      # one row tile per expert, mostly padding
+    (4, 3, 3, 300, 2, 512, 256, F32, 256),       # this rank owns experts 3..5 of 12
+    (3, 2, 2, 700, 3, 256, 384, BF16, 128),      # 128-row groups; chunks straddle tokens (topk 3)
+    (8, 4, 0, 512, 2, 768, 512, BF16, 256),
+])
+def test_a2a_gemm_values(P, E, e0, B, topk, N, K, odt, tm):
+    say(f"a2a_gemm P={P} E={E} e0={e0} B={B} topk={topk} N={N} K={K} out={odt} tile={tm}")
+    experts, X, W = _a2g_case(P, E, e0, B, topk, N, K, seed=P + E + B)
+    cap = P * B * topk // 2 + E * tm
+    run = bf.A2aGemm(P, E, e0, B, topk, N, K, odt, X, experts, W, cap, tile_m=tm)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    want = oracle.a2a_gemm(P, E, e0, B, topk, N, K, BF16, odt, X, experts, W, tm, cap)
+    _a2g_check(run, want)
+
+
+@pytest.mark.parametrize("grid", [0, 1, 3])
+def test_a2a_gemm_integer_bit_exact_and_unfused_identical(grid, monkeypatch):
+    """Integer inputs: Y bit-exact.  With a grid of one or a few workgroups
+    every tile's rows come from items the same few workgroups claimed
+    earlier (the kernel needs no co-residency).  The unfused pair (scatter
+    kernel, then GEMM kernel) gives the same bits."""
+    if grid:
+        monkeypatch.setenv("HOCF_MAX_WORKGROUPS", str(grid))
+    P, E, e0, B, topk, N, K = 4, 2, 2, 400, 2, 512, 256
+    say(f"a2a_gemm integer, grid cap {grid}")
+    ints = dict(dist_x=("int", -2, 2), dist_w=("int", -2, 2))
+    experts, X, W = _a2g_case(P, E, e0, B, topk, N, K, seed=77, dist=ints)
+    cap = 1024
+    run = bf.A2aGemm(P, E, e0, B, topk, N, K, F32, X, experts, W, cap)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    want = oracle.a2a_gemm(P, E, e0, B, topk, N, K, BF16, F32, X, experts, W, 256, cap)
+    _a2g_check(run, want, integer=True)
+    un = bf.A2aGemm(P, E, e0, B, topk, N, K, F32, run.X, run.experts, run.W, cap, unfused=True)
+    un.poison()
+    un.run()
+    sync()
+    assert un.status_value() == 0
+    T = int(run.offsets[-1])
+    assert torch.equal(un.Y[:T], run.Y[:T]) and torch.equal(un.recv[:T], run.recv[:T])
+    assert torch.equal(un.dest, run.dest) and torch.equal(un.slot, run.slot)
+    assert torch.equal(un.offsets, run.offsets) and torch.equal(un.send_counts, run.send_counts)
+
+
+def test_a2a_gemm_capacity_and_no_local_pairs():
+    """More rows than the receive buffer holds: HOCF_ERR_CAPACITY, no row
+    delivered, no tile computed; then the same object with every choice
+    elsewhere: empty groups, zero send counts, nothing written."""
+    P, E, B, topk, N, K = 4, 2, 256, 2, 256, 128
+    say("a2a_gemm capacity exceeded, then no local pairs")
+    experts, X, W = _a2g_case(P, E, 0, B, topk, N, K, seed=5)
+    run = bf.A2aGemm(P, E, 0, B, topk, N, K, BF16, X, experts, W, cap=256)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == hocf.HOCF_ERR_CAPACITY
+    assert torch.all(run.dest == -77)
+    assert torch.isnan(run.Y.view(torch.bfloat16).float()).all()
+    none = torch.full_like(run.experts, 99)
+    empty = bf.A2aGemm(P, E, 0, B, topk, N, K, BF16, run.X, none, run.W, cap=256)
+    empty.poison()
+    empty.run()
+    sync()
+    assert empty.status_value() == 0
+    assert empty.offsets.cpu().tolist() == [0] * (E + 1)
+    assert empty.send_counts.cpu().tolist() == [0] * P
+    assert torch.all(empty.dest == -77)
+
+
+def test_a2a_gemm_full_moe_dispatch_every_element():
+    """The MoE dispatch workload (8 ranks x 4096 tokens, top-2 of 32 experts,
+    this rank's 4 experts 4096 -> 1792) in the bench's launch configuration:
+    layout and received rows bit-exact, every Y element against the oracle,
+    and 20 repeated calls bit-identical."""
+    c = cfgs.A2A_GEMM_MOE
+    say(f"a2a_gemm full {c.name}")
+    experts, X, W = _a2g_case(c.P, c.E, 0, c.B, c.topk, c.N, c.K, seed=0)
+    run = bf.A2aGemm(c.P, c.E, 0, c.B, c.topk, c.N, c.K, BF16, X, experts, W, c.cap, tile_m=c.tile_m)
+    run.poison()
+    run.run()
+    sync()
+    assert run.status_value() == 0
+    want = oracle.a2a_gemm(c.P, c.E, 0, c.B, c.topk, c.N, c.K, BF16, BF16, X, experts, W, c.tile_m, c.cap)
+    _a2g_check(run, want)
+    first = run.Y.clone()
+    for _ in range(20):
+        run.run()
+    sync()
+    assert run.status_value() == 0
+    assert torch.equal(run.Y, first)
+
+
+def test_a2a_gemm_alternating_inputs_no_stale_reads():
+    """Two different routings and token sets on the same receive and output
+    buffers, one call after the other, three times: every call matches its
+    own oracle (the tiles never read received rows left by the previous
+    call from an XCD's L2)."""
+    P, E, B, topk, N, K = 4, 2, 512, 2, 512, 256
+    say("a2a_gemm alternating inputs on the same buffers")
+    cases = [_a2g_case(P, E, 0, B, topk, N, K, seed=s) for s in (101, 202)]
+    wants = [oracle.a2a_gemm(P, E, 0, B, topk, N, K, BF16, BF16, X, ex_, W, 256, 2048) for ex_, X, W in cases]
+    run = bf.A2aGemm(P, E, 0, B, topk, N, K, BF16, cases[0][1], cases[0][0], cases[0][2], 2048)
+    dev = [(bf.to_device(X), bf.to_device(np.ascontiguousarray(ex_, np.int32)), bf.to_device(W)) for ex_, X, W in cases]
+    for k in range(6):
+        run.X, run.experts, run.W = dev[k % 2]
+        run.dest.fill_(-77)          # (recv is not touched between the calls)
+        bf.nan_fill(run.Y)
+        run.run()
+        sync()
+        assert run.status_value() == 0
+        _a2g_check(run, wants[k % 2])
