@@ -30,6 +30,9 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
               computation publishing its partials, then the fold): the bulk-synchronous
               baseline; `fusion` reports the time each fused operator saves against it
   a2a_gemm_unfused  the dispatch delivering every row, then the expert GEMM (two kernels)
+  gemm_rs_decomp<d>_f<F>  Compass's inter-operator decomposition on one GPU: the gemm_rs workload
+              as d column pieces, each piece's GEMM on the step's stream with F CUs left free, its
+              fold on a second stream overlapping the next piece's GEMM; `fusion.gemm_rs` lists them
 
 hipblaslt_bmm: context, not an operator of this library -- torch.bmm (hipBLASLt) on the same
 eight shard GEMMs as gemm_rs, with no collective.
@@ -72,6 +75,7 @@ def parse():
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--ops", default="gemm_rs,gemm_rs_tiny,gemv_ar,ag_gemm,ag_gemm_paced,embbag_a2a,gemm_ar,"
                                      "gemm_a2a,a2a_gemm,gemm_rs_unfused,gemv_ar_unfused,a2a_gemm_unfused,"
+                                     "gemm_rs_decomp2_f32,gemm_rs_decomp4_f32,gemm_rs_decomp8_f32,"
                                      "hipblaslt_bmm")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
     ap.add_argument("--a2a-tile-m", type=int, default=0, help="GEMM+A2A tile rows (default: the config's)")
@@ -345,6 +349,25 @@ def main():
                             config=dict(workload=c.name + ("_unfused" if a2g_op.endswith("unfused") else ""),
                                         P=c.P, E=c.E, B=c.B, topk=c.topk, N=c.N, K=c.K, cap=c.cap, rows=rows,
                                         padded_rows=padded, tile=[c.tile_m, c.tile_n]))
+    for o in [o for o in ops if o.startswith("gemm_rs_decomp")]:
+        # Compass's InterDecom on one GPU: the gemm_rs workload in d column pieces, each piece's
+        # GEMM on the step's stream (leaving F CUs free), its fold on a second stream:
+        # gemm_rs_decomp<d>_f<F> (e.g. gemm_rs_decomp4_f32)
+        d_, f_ = o[len("gemm_rs_decomp"):].split("_f")
+        c = cfgs.GEMM_RS_MLP
+        log(f"inputs {c.name} (decomposed, {d_} pieces, {f_} CUs for the folds)")
+        A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, c.in_dt, seed=0)
+        dr = bf.GemmRS(c.P, c.M, c.N, c.K, c.in_dt, sdt, c.out_dt, c.tile_m, c.tile_n, A, W, pieces=int(d_),
+                       fold_cus=int(f_))
+        del A, W
+        runs[o] = dict(call=lambda r=dr: r.run(stream), obj=dr, work=c.flops, unit="TFLOP/s", bound="mfma",
+                       variant=f"slot_dtype={args.slot_dtype} tile={c.tile_m}x{c.tile_n} pieces={d_} fold_cus={f_}",
+                       peak=PEAK_BF16_TFLOPS,
+                       bytes=(2 * (c.P * c.M * c.K + c.P * c.K * c.N)
+                              + 2 * (4 if sdt == bf.F32 else 2) * c.P * c.M * c.N + 2 * c.M * c.N),
+                       config=dict(workload=c.name + f"_decomposed_d{d_}_f{f_}", P=c.P, M=c.M, N=c.N, K=c.K,
+                                   tile=[c.tile_m, c.tile_n], pieces=int(d_), fold_cus=int(f_),
+                                   slot_dtype=args.slot_dtype))
     if "gemm_rs_unfused" in ops:
         # the baseline of the fused operator: the same GEMM, then a separate fold kernel
         c = cfgs.GEMM_RS_MLP
@@ -537,6 +560,13 @@ def main():
             f, u = out_ops[op]["ms_avg"], out_ops[op + "_unfused"]["ms_avg"]
             fusion[op] = {"fused_ms": f, "unfused_ms": u, "time_saved": round(1.0 - f / u, 4)}
             log(f"fusion: {op} fused {f:.4f} ms, unfused {u:.4f} ms ({100 * (1 - f / u):.1f}% less time)")
+    # Compass's InterDecom (column pieces pipelined on two streams) against the same two
+    decomp = {o: out_ops[o]["ms_avg"] for o in out_ops if o.startswith("gemm_rs_decomp")}
+    if decomp and "gemm_rs" in fusion:
+        fusion["gemm_rs"]["decomposed_ms"] = decomp
+        for o, v in decomp.items():
+            log(f"interdecom: {o} {v:.4f} ms (fused {fusion['gemm_rs']['fused_ms']:.4f}, "
+                f"unfused {fusion['gemm_rs']['unfused_ms']:.4f})")
     if fusion:
         res["fusion"] = fusion
     if not args.no_cpu_baseline and "gemm_rs" in out_ops:

@@ -66,9 +66,13 @@ class GemmRS(_Common):
     """hocf_gemm_rs: A [P][M][K], W [P][K][N] -> windows [P dst][P src][Mc][N], out [M][N]."""
 
     def __init__(self, P, M, N, K, in_dt, slot_dt, out_dt, tile_m, tile_n, A, W, device="cuda",
-                 unfused=False, noalloc=False):
+                 unfused=False, noalloc=False, pieces=0, fold_cus=0):
         self.unfused = unfused   # hocf_gemm_rs_unfused: the GEMM kernel, then the fold kernel
         self.noalloc = noalloc   # hocf_gemm_rs_noalloc: no workspace (the library's scratch)
+        # hocf_gemm_rs_decomposed: `pieces` column pieces, GEMM on the call's stream (leaving
+        # fold_cus CUs), each fold on a second stream
+        self.pieces, self.fold_cus = pieces, fold_cus
+        self.coll = torch.cuda.Stream(device=device) if pieces else None
         self.P, self.M, self.N, self.K = P, M, N, K
         self.in_dt, self.slot_dt, self.out_dt = in_dt, slot_dt, out_dt
         self.tile_m, self.tile_n = tile_m, tile_n
@@ -88,6 +92,12 @@ class GemmRS(_Common):
 
     def call(self, stream=None, **kw) -> int:
         s = self.next_sync(**kw)
+        if getattr(self, "pieces", 0):
+            return hocf.hocf_gemm_rs_decomposed(self.P, self.M, self.N, self.K, self.in_dt, self.slot_dt,
+                                                self.out_dt, self.A, self.W, self.win, self.out, self.tile_m,
+                                                self.tile_n, self.pieces, self.fold_cus, s,
+                                                stream if stream is not None else torch.cuda.current_stream(),
+                                                self.coll)
         if getattr(self, "noalloc", False):
             s.workspace, s.workspace_bytes = None, 0
             fn = hocf.hocf_gemm_rs_noalloc

@@ -155,7 +155,7 @@ hipError_t device_info(DeviceInfo* out) {
   return hipSuccess;
 }
 
-hipError_t persistent_grid(const void* kernel, int threads, int64_t work, int* grid) {
+hipError_t persistent_grid(const void* kernel, int threads, int64_t work, int* grid, int cap) {
   static std::mutex mu;
   static std::unordered_map<const void*, std::unordered_map<int, int>> occ;
   DeviceInfo di;
@@ -179,6 +179,7 @@ hipError_t persistent_grid(const void* kernel, int threads, int64_t work, int* g
   }
   int64_t g = (int64_t)per_cu * di.cus;
   if (work < g) g = work;
+  if (cap > 0 && cap < g) g = cap;
   // optional cap on the persistent grid (documented with the ABI)
   if (const char* cap = std::getenv("HOCF_MAX_WORKGROUPS")) {
     const long v = std::strtol(cap, nullptr, 10);
@@ -241,7 +242,8 @@ static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, h
                                    hocf_dtype slot_dt, hocf_dtype out_dt, const void* A, const void* W,
                                    const hocf_window* win, void* const* outs, int nout, int mode,
                                    int tile_m, int tile_n, const hocf_sync* sync, void* stream,
-                                   bool noalloc = false) {
+                                   bool noalloc = false, int pieces = 0, int fold_cus = 0,
+                                   void* coll = nullptr) {
   if (P < 1 || P > HOCF_MAX_P) return fail(HOCF_ERR_INVALID_ARG, "%s: P=%d outside [1, %d]", op, P, HOCF_MAX_P);
   if (M < 0 || N < 0 || K < 0) return fail(HOCF_ERR_INVALID_ARG, "%s: negative dimension", op);
   if (M % P) return fail(HOCF_ERR_INVALID_ARG, "%s: M=%d not divisible by P=%d", op, M, P);
@@ -320,6 +322,7 @@ static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, h
   a.ntiles = (int)cdiv(N, tile_n);
   a.total = (int64_t)P * P * a.mtiles * a.ntiles;
   a.sync = sa;
+  a.Nc = N;
   a.trace = nullptr;
   if (hocf::kTraceBuild && !noalloc)
     a.trace = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
@@ -328,6 +331,10 @@ static hocf_status gemm_collective(const char* op, int P, int M, int N, int K, h
     const int e = hocf::launch_zero_words(a.ws, (int64_t)(need / 4), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return launched(e, op);
   }
+  if (pieces > 0)
+    return launched(hocf::launch_gemm_rs_pieces(a, tile_m, tile_n, in_dt, pieces, fold_cus,
+                                                static_cast<hipStream_t>(stream), static_cast<hipStream_t>(coll)),
+                    op);
   return launched(hocf::launch_gemm_rs(a, tile_m, tile_n, in_dt, static_cast<hipStream_t>(stream)), op);
 }
 
@@ -353,6 +360,21 @@ hocf_status hocf_gemm_rs_noalloc(int P, int M, int N, int K, hocf_dtype in_dt, h
   void* const outs[1] = {out};
   return gemm_collective("gemm_rs_noalloc", P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, 1, 0, tile_m,
                          tile_n, sync, stream, true);
+}
+
+hocf_status hocf_gemm_rs_decomposed(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                                    hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
+                                    void* out, int tile_m, int tile_n, int pieces, int fold_cus,
+                                    const hocf_sync* sync, void* stream, void* coll_stream) {
+  if (pieces < 1 || pieces > hocf::kMaxPieces)
+    return fail(HOCF_ERR_INVALID_ARG, "gemm_rs_decomposed: pieces=%d outside [1, %d]", pieces, hocf::kMaxPieces);
+  if (fold_cus < 0) return fail(HOCF_ERR_INVALID_ARG, "gemm_rs_decomposed: fold_cus=%d < 0", fold_cus);
+  if (tile_n <= 0 || N % pieces || (N / pieces) % tile_n)
+    return fail(HOCF_ERR_UNSUPPORTED, "gemm_rs_decomposed: N=%d is not %d pieces of whole %d-column tiles", N,
+                pieces, tile_n);
+  void* const outs[1] = {out};
+  return gemm_collective("gemm_rs_decomposed", P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, 1, 2, tile_m,
+                         tile_n, sync, stream, false, pieces, fold_cus, coll_stream);
 }
 
 /* ------------------------------------------------------------ GEMM + AR */

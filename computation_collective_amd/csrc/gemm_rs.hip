@@ -45,6 +45,7 @@
 #include <mutex>
 #include <type_traits>
 #include <unordered_map>
+#include <vector>
 
 #include "internal.hpp"
 #include "mfma_tile.hpp"
@@ -73,7 +74,7 @@ struct BandRef {
     const int r = (int)(g / tpc), tflag = (int)(g % tpc);
     const int mt = tflag / a.ntiles, nt = tflag % a.ntiles;
     rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
-    cols_valid = min(Tile::TN, N - nt * Tile::TN);
+    cols_valid = min(Tile::TN, a.Nc - nt * Tile::TN);
     row0 = piece * RL::PIECE_ROWS;
     const int64_t tile_off = (int64_t)mt * Tile::TM * N + (int64_t)nt * Tile::TN;
     slot0 = reinterpret_cast<const char*>(a.win_data[r]) + tile_off * SES;
@@ -288,7 +289,7 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
 
     if (item >= 0) {
       const int rows_valid = min(Tile::TM, Mc - mt * Tile::TM);
-      const int cols_valid = min(Tile::TN, N - nt * Tile::TN);
+      const int cols_valid = min(Tile::TN, a.Nc - nt * Tile::TN);
       floatx16 acc[Tile::FM][Tile::FN];
       if constexpr (kBandInLoop) {
         if (band_in_loop) {
@@ -383,23 +384,29 @@ static int launch_one(const GemmRsArgs& a, hipStream_t s) {
   auto kern = a.mode == kFusedAR ? &gemm_ar_kernel<Tile, RAGGED, BF16IN, SDT, ODT>
             : a.mode == kGemmOnly ? &unfused_gemm_kernel<Tile, RAGGED, BF16IN, SDT, ODT>
                                   : &gemm_rs_kernel<Tile, RAGGED, BF16IN, SDT, ODT>;
+  // the fold kernel of the unfused form: P chunks x tiles per chunk x bands per tile workgroups
+  const int64_t folds = (int64_t)a.P * a.mtiles * a.ntiles * ReduceLayout<Tile, SDT>::PIECES;
+  if (a.mode == kGemmOnly && folds > 0x7FFFFFFF) return kNoKernel;
   int grid = 0;
-  hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), Tile::NT, a.total, &grid);
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), Tile::NT, a.total, &grid, a.max_wg);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(Tile::NT), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.mode != kGemmOnly) return e;
-  // the fold kernel: P chunks x tiles per chunk x bands per tile workgroups
-  const int64_t folds = (int64_t)a.P * a.mtiles * a.ntiles * ReduceLayout<Tile, SDT>::PIECES;
-  if (folds > 0x7FFFFFFF) return kNoKernel;
-  hipLaunchKernelGGL((unfused_fold_kernel<Tile, RAGGED, SDT, ODT>), dim3((unsigned)folds), dim3(Tile::NT), 0, s,
+  hipStream_t fs = s;
+  if (a.fold_stream) {
+    fs = static_cast<hipStream_t>(a.fold_stream);
+    if ((e = hipEventRecord(static_cast<hipEvent_t>(a.gemm_done), s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(fs, static_cast<hipEvent_t>(a.gemm_done), 0)) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((unfused_fold_kernel<Tile, RAGGED, SDT, ODT>), dim3((unsigned)folds), dim3(Tile::NT), 0, fs,
                      a);
   return hipGetLastError();
 }
 
 template <class Tile, bool BF16IN, int SDT, int ODT>
 static int launch_tile(const GemmRsArgs& a, hipStream_t s) {
-  const bool ragged = (a.Mc % Tile::TM) || (a.N % Tile::TN) || (a.K % Tile::BK);
+  const bool ragged = (a.Mc % Tile::TM) || (a.Nc % Tile::TN) || (a.K % Tile::BK);
   return ragged ? launch_one<Tile, true, BF16IN, SDT, ODT>(a, s)
                 : launch_one<Tile, false, BF16IN, SDT, ODT>(a, s);
 }
@@ -411,7 +418,7 @@ static int launch_bf16_dt(const GemmRsArgs& a, hipStream_t s) {
   using Staged = TileBf16<TM, TN, 2, 2>;
   using Direct = TileBf16Direct<TM, TN, 2, 2>;
   // the direct tile takes full tiles whose operands it can address with 32-bit offsets
-  const bool ragged = (a.Mc % TM) || (a.N % TN) || !Direct::k_fits(a.K) ||
+  const bool ragged = (a.Mc % TM) || (a.Nc % TN) || !Direct::k_fits(a.K) ||
                       !Direct::operands_fit(a.K, a.N, a.K);
   return ragged ? launch_one<Staged, true, true, SDT, ODT>(a, s)
                 : launch_one<Direct, false, true, SDT, ODT>(a, s);
@@ -434,6 +441,62 @@ int launch_gemm_rs(const GemmRsArgs& a, int tm, int tn, int in_dt, hipStream_t s
     if (tm == 64 && tn == 64) return launch_tile<TileF32<64, 64, 2, 2>, false, kF32, kF32>(a, s);
   }
   return kNoKernel;
+}
+
+// ------------------------------------------------------------------------
+// The decomposed form (Compass, abstract: inter-operator decomposition, a
+// tensor split into parts whose computation and communication are
+// pipelined).  Piece i is columns [i*N/pieces, (i+1)*N/pieces) of every
+// partial and of the output: its shard GEMMs (the unfused GEMM kernel, the
+// grid capped to leave fold_cus CUs free) run on s, an event marks their
+// end, and its fold runs on coll after that event -- while piece i+1's
+// GEMMs run on s.  At the end s waits for coll's last fold.  The events are
+// kept per device (created at first use and reused by every later call).
+static hipError_t piece_events(hipEvent_t** out) {
+  static std::mutex mu;
+  static std::unordered_map<int, std::vector<hipEvent_t>> ev;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  std::vector<hipEvent_t>& v = ev[dev];
+  while (v.size() < (size_t)kMaxPieces + 1) {
+    hipEvent_t x = nullptr;
+    if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
+    v.push_back(x);
+  }
+  *out = v.data();
+  return hipSuccess;
+}
+
+int launch_gemm_rs_pieces(const GemmRsArgs& a0, int tm, int tn, int in_dt, int pieces, int fold_cus,
+                          hipStream_t s, hipStream_t coll) {
+  if (pieces < 1 || pieces > kMaxPieces || a0.N % pieces || (a0.N / pieces) % tn) return kNoKernel;
+  hipEvent_t* ev = nullptr;
+  hipError_t e = piece_events(&ev);
+  if (e != hipSuccess) return e;
+  DeviceInfo di;
+  if ((e = device_info(&di)) != hipSuccess) return e;
+  const int ses = a0.slot_dt == kBF16 ? 2 : 4, oes = a0.out_dt == kBF16 ? 2 : 4, ies = in_dt == kBF16 ? 2 : 4;
+  const int w = a0.N / pieces;
+  for (int i = 0; i < pieces; ++i) {
+    GemmRsArgs a = a0;
+    const int64_t c0 = (int64_t)i * w;
+    a.W = static_cast<const char*>(a0.W) + c0 * ies;
+    for (int r = 0; r < a.P; ++r) a.win_data[r] = static_cast<char*>(a0.win_data[r]) + c0 * ses;
+    a.outs[0] = static_cast<char*>(a0.outs[0]) + c0 * oes;
+    a.Nc = w;
+    a.ntiles = w / tn;
+    a.total = (int64_t)a.P * a.P * a.mtiles * a.ntiles;
+    a.mode = kGemmOnly;
+    a.max_wg = fold_cus > 0 && fold_cus < di.cus ? di.cus - fold_cus : 0;
+    a.fold_stream = coll;
+    a.gemm_done = ev[i];
+    const int r = launch_gemm_rs(a, tm, tn, in_dt, s);
+    if (r != hipSuccess) return r;
+  }
+  if ((e = hipEventRecord(ev[kMaxPieces], coll)) != hipSuccess) return e;
+  return hipStreamWaitEvent(s, ev[kMaxPieces], 0);
 }
 
 // ------------------------------------------------------------------------

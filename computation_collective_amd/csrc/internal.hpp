@@ -27,6 +27,14 @@ struct GemmRsArgs {
   int64_t total;       // P (sources) * P (chunks) * mtiles * ntiles
   SyncArgs sync;
   uint64_t* trace;     // the trace build's per-iteration records (trace.hpp), else NULL
+  int Nc;              // columns computed (N for a whole call; a column piece's width otherwise:
+                       // W, the windows and the outputs then point at the piece's first column,
+                       // N stays their leading dimension)
+  int max_wg;          // cap on the persistent grid (0: none)
+  // the unfused form only: when set, the fold kernel goes to fold_stream,
+  // after a wait on gemm_done (recorded on the call's stream after the GEMM)
+  void* fold_stream;
+  void* gemm_done;
 };
 
 struct GemvArArgs {
@@ -124,12 +132,19 @@ hipError_t device_info(DeviceInfo* out);
 
 // Persistent-grid size for a kernel: resident workgroups the device can hold
 // (occupancy x CUs), capped by the work available.
-hipError_t persistent_grid(const void* kernel, int threads, int64_t work, int* grid);
+hipError_t persistent_grid(const void* kernel, int threads, int64_t work, int* grid, int cap = 0);
+
+// The decomposed GEMM + ReduceScatter: `pieces` (<= kMaxPieces) column pieces, each an
+// unfused GEMM (grid capped to leave `fold_cus` CUs) on s, then its fold on
+// coll after an event; s waits for coll's last fold.
+int launch_gemm_rs_pieces(const GemmRsArgs& a, int tile_m, int tile_n, int in_dt, int pieces, int fold_cus,
+                          hipStream_t s, hipStream_t coll);
 
 // Each returns hipSuccess, the HIP error a runtime call gave (a hipError_t
 // value), or kNoKernel when it has no kernel for the shape (found before
 // anything is enqueued).
 constexpr int kNoKernel = -1;
+constexpr int kMaxPieces = 16;  // column pieces of the decomposed GEMM + ReduceScatter
 int launch_gemm_rs(const GemmRsArgs& a, int tile_m, int tile_n, int in_dt, hipStream_t s);
 int launch_gemv_ar(const GemvArArgs& a, hipStream_t s);
 int launch_ag_gemm(const AgGemmArgs& a, int tile_m, int tile_n, hipStream_t s);

@@ -31,7 +31,7 @@ HOCF_BF16 = 1
 HOCF_MAX_P = 16
 
 EXPORTED = [
-    "hocf_gemm_rs", "hocf_gemm_rs_workspace_bytes", "hocf_gemm_rs_noalloc",
+    "hocf_gemm_rs", "hocf_gemm_rs_workspace_bytes", "hocf_gemm_rs_noalloc", "hocf_gemm_rs_decomposed",
     "hocf_gemm_ar", "hocf_gemm_ar_workspace_bytes", "hocf_gemm_rs_unfused",
     "hocf_gemv_ar", "hocf_gemv_ar_workspace_bytes", "hocf_gemv_ar_unfused",
     "hocf_ag_gemm", "hocf_ag_gemm_workspace_bytes",
@@ -87,6 +87,8 @@ def lib():
         L.hocf_gemm_rs_workspace_bytes.argtypes = [i, i, i, i, i]
         L.hocf_gemm_rs_unfused.argtypes = [i, i, i, i, i, i, i, vp, vp, W, vp, i, i, S, vp]
         L.hocf_gemm_rs_noalloc.argtypes = [i, i, i, i, i, i, i, vp, vp, W, vp, i, i, S, vp]
+        L.hocf_gemm_rs_decomposed.argtypes = [i, i, i, i, i, i, i, vp, vp, W, vp, i, i, i, i, S, vp, vp]
+        L.hocf_gemm_rs_decomposed.restype = i
         L.hocf_gemm_ar.argtypes = [i, i, i, i, i, i, i, vp, vp, W, ctypes.POINTER(vp), i, i, S, vp]
         L.hocf_gemm_ar_workspace_bytes.argtypes = [i, i, i, i, i]
         L.hocf_gemv_ar.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, W, i, S, vp]
@@ -220,6 +222,13 @@ def hocf_gemm_rs_noalloc(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, out, til
 
 
 HOCF_NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def hocf_gemm_rs_decomposed(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, out, tile_m, tile_n, pieces, fold_cus,
+                            sync_, stream=None, coll_stream=None) -> int:
+    return lib().hocf_gemm_rs_decomposed(P, M, N, K, in_dt, slot_dt, out_dt, ptr(A), ptr(W), win, ptr(out),
+                                         tile_m, tile_n, pieces, fold_cus, ctypes.byref(sync_), _stream(stream),
+                                         _stream(coll_stream))
 
 
 def hocf_gemm_ar(P, M, N, K, in_dt, slot_dt, out_dt, A, W, win, outs, tile_m, tile_n, sync_,

@@ -13,6 +13,9 @@
  *                    the same GEMM + ReduceScatter / GEMV + AllReduce as two
  *                    kernels, the computation then the collective (the
  *                    baseline SC24 measures its fused operators against)
+ *   hocf_gemm_rs_decomposed
+ *                    the same GEMM + ReduceScatter in column pieces pipelined
+ *                    on two streams (Compass, abstract: InterDecom)
  *   hocf_gemv_ar     GEMV + AllReduce       ("Optimizing Distributed ML
  *                    Communication with Fused Computation-Collective
  *                    Operations", SC24, abstract)
@@ -205,6 +208,35 @@ hocf_status hocf_gemm_rs_noalloc(int P, int M, int N, int K, hocf_dtype in_dt, h
 hocf_status hocf_gemm_rs_unfused(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
                                  hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
                                  void* out, int tile_m, int tile_n, const hocf_sync* sync, void* stream);
+
+/* ------------------------------------------------------------------------
+ * GEMM + ReduceScatter, decomposed (the inter-operator decomposition of
+ * "Compass: Dissecting Communication and Computation Operators for
+ * Efficient LLM Training", abstract: the tensor split into parts whose
+ * computation and communication are pipelined, the number of parts being
+ * the decomposition degree).
+ *
+ * The same arguments, arithmetic and results as hocf_gemm_rs, bit for bit
+ * (the same tile products and the same rank-order fold), computed as
+ * `pieces` column pieces: piece i is columns [i*N/pieces, (i+1)*N/pieces)
+ * of every partial and of the output.  Its shard GEMMs (the unfused GEMM
+ * kernel, publishing into the piece's columns of the slots) run on `stream`
+ * with the grid capped to leave `fold_cus` compute units free (0: no cap);
+ * its fold runs on `coll_stream` once that GEMM kernel has ended (an event),
+ * while piece i+1's GEMMs run on `stream`.  `stream` then waits for the
+ * last fold, so the results are complete when `stream` reaches the end of
+ * the call.  No tile flag is written.  `coll_stream` may equal `stream`
+ * (then nothing overlaps).  The library keeps 17 HIP events per device,
+ * created at its first call and reused by every later one.
+ *
+ * Requires 1 <= pieces <= 16 and N a multiple of pieces * tile_n
+ * (else HOCF_ERR_UNSUPPORTED); supported combinations, limits, workspace
+ * (hocf_gemm_rs_workspace_bytes) and errors as for hocf_gemm_rs.
+ * ---------------------------------------------------------------------- */
+hocf_status hocf_gemm_rs_decomposed(int P, int M, int N, int K, hocf_dtype in_dt, hocf_dtype slot_dt,
+                                    hocf_dtype out_dt, const void* A, const void* W, const hocf_window* win,
+                                    void* out, int tile_m, int tile_n, int pieces, int fold_cus,
+                                    const hocf_sync* sync, void* stream, void* coll_stream);
 
 /* ------------------------------------------------------------------------
  * GEMM + AllReduce.

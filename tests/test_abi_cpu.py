@@ -408,3 +408,21 @@ def test_a2a_gemm_valid_reaches_device():
     C = 8 * 32
     assert hocf.hocf_a2a_gemm_workspace_bytes(8, 4, 4096, 2, 12288, 256) == \
         (8 + 1 + 4 + 8 + 2 * C * 5 + 3 * 4 + 2 + 12288 // 256) * 4
+
+
+@pytest.mark.parametrize("pieces,fold_cus,N,expect", [(0, 0, 256, INVALID), (17, 0, 256, INVALID),
+                                                      (2, -1, 256, INVALID), (3, 0, 256, UNSUPPORTED),
+                                                      (8, 0, 256, UNSUPPORTED)])
+def test_gemm_rs_decomposed_rejects(pieces, fold_cus, N, expect):
+    st = hocf.hocf_gemm_rs_decomposed(4, 256, N, 256, F32, F32, F32, FAKE, addr("W"), _win(4), addr("out"), 64, 64,
+                                      pieces, fold_cus, _sync())
+    assert st == expect
+
+
+def test_gemm_rs_decomposed_valid_reaches_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    st = hocf.hocf_gemm_rs_decomposed(4, 256, 256, 256, F32, F32, F32, FAKE, addr("W"), _win(4), addr("out"), 64, 64,
+                                      4, 16, _sync())
+    assert st == HIP

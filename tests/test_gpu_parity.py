@@ -1424,3 +1424,51 @@ def test_a2a_gemm_alternating_inputs_no_stale_reads():
         sync()
         assert run.status_value() == 0
         _a2g_check(run, wants[k % 2])
+
+
+# ====================================================================== GEMM + RS, decomposed (InterDecom)
+
+@pytest.mark.parametrize("pieces,fold_cus", [(1, 0), (2, 32), (4, 0), (4, 64), (8, 32)])
+def test_gemm_rs_decomposed_identical_to_fused(pieces, fold_cus):
+    """Column pieces pipelined on two streams give the fused operator's bits
+    (output and every slot): the same tile products, the same fold."""
+    P, Mc, N, K = 4, 512, 2048, 512
+    say(f"gemm_rs decomposed pieces={pieces} fold_cus={fold_cus}")
+    A, W = gen.gemm_rs_inputs(P, P * Mc, N, K, BF16, seed=pieces)
+    fused = bf.GemmRS(P, P * Mc, N, K, BF16, F32, BF16, 256, 256, A, W)
+    fused.poison()
+    fused.run()
+    dec = bf.GemmRS(P, P * Mc, N, K, BF16, F32, BF16, 256, 256, fused.A, fused.W, pieces=pieces, fold_cus=fold_cus)
+    dec.poison()
+    dec.run()
+    sync()
+    assert fused.status_value() == 0 and dec.status_value() == 0
+    assert torch.equal(dec.out, fused.out)
+    assert torch.equal(dec.win_data, fused.win_data)
+    _, out = oracle.gemm_rs(P, P * Mc, N, K, BF16, F32, BF16, A, W, want_slots=False)
+    assert relerr(val(bf.to_host(dec.out, BF16), BF16), val(out, BF16)) <= TOL[BF16]
+
+
+def test_gemm_rs_decomposed_tiny_fp32_and_full_mlpdown():
+    """The tiny fp32 workload in 4 pieces of 64 columns, and the MLP-down
+    workload in 4 pieces with 32 CUs left to the folds: bit-identical to
+    the fused operator."""
+    c = cfgs.GEMM_RS_TINY
+    say(f"gemm_rs decomposed {c.name} pieces=4")
+    A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, F32, seed=0, dist_a=c.dist_a, dist_w=c.dist_w)
+    f = bf.GemmRS(c.P, c.M, c.N, c.K, F32, F32, F32, 64, 64, A, W)
+    d = bf.GemmRS(c.P, c.M, c.N, c.K, F32, F32, F32, 64, 64, f.A, f.W, pieces=4, fold_cus=16)
+    f.poison(); d.poison()
+    f.run(); d.run()
+    sync()
+    assert torch.equal(d.out, f.out)
+    c = cfgs.GEMM_RS_MLP
+    say(f"gemm_rs decomposed {c.name} pieces=4 fold_cus=32")
+    A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, BF16, seed=0)
+    f = bf.GemmRS(c.P, c.M, c.N, c.K, BF16, F32, BF16, 256, 256, A, W)
+    d = bf.GemmRS(c.P, c.M, c.N, c.K, BF16, F32, BF16, 256, 256, f.A, f.W, pieces=4, fold_cus=32)
+    f.poison(); d.poison()
+    f.run(); d.run()
+    sync()
+    assert f.status_value() == 0 and d.status_value() == 0
+    assert torch.equal(d.out, f.out)
