@@ -40,6 +40,10 @@
 
 namespace hocf {
 
+// Each expert group's padding (up to tile_m - 1 rows) is filled in this
+// many pieces, so that no single workgroup writes all of it.
+constexpr int kA2gPadPieces = 8;
+
 // 1. Histogram of one chunk: hist[c][e] for local expert e, hist[c][E] for
 // all of the chunk's pairs that land on this rank.
 __global__ __launch_bounds__(kA2gChunk) void a2g_count_kernel(A2aGemmArgs a) {
@@ -65,6 +69,9 @@ __global__ __launch_bounds__(kA2gChunk) void a2g_count_kernel(A2aGemmArgs a) {
 __global__ __launch_bounds__(256) void a2g_scan_kernel(A2aGemmArgs a) {
   __shared__ uint32_t tot[kMaxExperts + 1];
   __shared__ uint32_t src0[kMaxP + 1];
+  __shared__ uint32_t sb[(kMaxP + 1) * kMaxExperts];  // expert e's rows from sources before p
+  __shared__ uint32_t ssn[kMaxP * kMaxExperts];       // items of stage p for expert e's tiles
+  __shared__ uint32_t sitems[kMaxP];                  // items of stage p
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, C = a.C, W1 = E + 1;
   // every column: base[c][i] = sum over chunks c' < c of hist[c'][i]; one
@@ -94,6 +101,8 @@ __global__ __launch_bounds__(256) void a2g_scan_kernel(A2aGemmArgs a) {
   // send count
   if (tid < a.P) src0[tid] = a.base[(int64_t)tid * a.cps * W1 + E];
   if (tid == 0) src0[a.P] = tot[E];
+  for (int i = tid; i < (a.P + 1) * E; i += 256)
+    sb[i] = i < a.P * E ? a.base[(int64_t)(i / E) * a.cps * W1 + i % E] : tot[i % E];
   __syncthreads();
   for (int c = tid; c < C; c += 256) a.base[(int64_t)c * W1 + E] -= src0[c / a.cps];
   if (tid < a.P) a.send_counts[tid] = (int64_t)(src0[tid + 1] - src0[tid]);
@@ -116,11 +125,42 @@ __global__ __launch_bounds__(256) void a2g_scan_kernel(A2aGemmArgs a) {
     a.misc[0] = 0;
     a.misc[1] = over ? 1u : 0u;
     a.misc[2] = over ? 0u : tile;
-    a.misc[3] = 0;
     for (int q = 0; q < kNumQueues; ++q) a.misc[4 + q] = 0;
     if (over) report_status(a.sync, kErrCapacity);
   }
   for (int i = tid; i < a.nrt; i += 256) a.arrivals[i] = 0;
+  // The fused kernel's schedule: after the padding pieces, stage p = the
+  // chunks of source p, then every tile whose row tile gets its last row from
+  // source p.  Rows of a group are in source order, so a row tile's last row
+  // names the last source it waits for, and the row tiles of expert e whose
+  // last row lies in source p's rows [lo, hi) are the run [F(lo), F(hi)),
+  // F(x) = the row tiles whose last row is below x = (x >= n ? all : x / tile_m).
+  const int P = a.P;
+  for (int i = tid; i < P * E; i += 256) {
+    const int e = i % E;
+    const uint32_t n = tot[e], tm = (uint32_t)a.tile_m, mtiles = (n + tm - 1) / tm;
+    const uint32_t lo = sb[i] >= n ? mtiles : sb[i] / tm;
+    const uint32_t hi = sb[i + E] >= n ? mtiles : sb[i + E] / tm;
+    a.slo[i] = lo;
+    a.sn[i] = hi - lo;
+    ssn[i] = (hi - lo) * (uint32_t)a.ntiles;
+  }
+  __syncthreads();
+  if (tid < P) {
+    uint32_t c = (uint32_t)a.cps;
+    for (int e = 0; e < E; ++e) c += ssn[tid * E + e];
+    sitems[tid] = c;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t at = 0;
+    for (int st = 0; st < P; ++st) {
+      a.stage_item[st] = at;
+      at += sitems[st];
+    }
+    a.stage_item[P] = at;
+    a.misc[3] = (uint32_t)(E * kA2gPadPieces) + at;  // the fused kernel's items
+  }
 }
 
 // Copies (or, with src == nullptr, zeroes) one row of K bf16 elements into
@@ -172,9 +212,7 @@ __device__ __forceinline__ void move_rows(const uint16_t* const (&src)[R], uint1
 
 // Piece `piece` (of kA2gPadPieces) of the padding rows of expert e's group:
 // zero token rows, dest = slot = -1; they all lie in the group's last row
-// tile.  (A group's padding, up to tile_m - 1 rows of K elements, is cut in
-// pieces so that no single workgroup writes all of it.)
-constexpr int kA2gPadPieces = 8;
+// tile.
 template <int NT>
 __device__ __forceinline__ void a2g_pad(const A2aGemmArgs& a, int e, int piece) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -297,14 +335,18 @@ __global__ __launch_bounds__(Tile::NT) void a2a_gemm_kernel(A2aGemmArgs a) {
   const int E = a.E;
   const int64_t npad = (int64_t)E * kA2gPadPieces;
   const int64_t nscatter = SCATTER ? npad + a.C : 0;
-  const uint32_t ntile = GEMM ? a.misc[2] : 0u;
-  // tiles are dealt from eight queues, one per XCD (home queue blockIdx mod
-  // 8, then the others in turn), each a contiguous run of the tile list
-  // (expert, row tile, column tile), so an XCD's tiles share row tiles and W
-  // panels in its L2; scatter items come first, from one counter
+  // Fused: one counter deals the staged schedule (the padding pieces, then
+  // per source its chunks and the tiles that wait only on it and earlier
+  // sources), so tiles start while later sources' rows are still moving;
+  // every tile waits only on items dealt before it.  Unfused: the scatter
+  // kernel deals its items in order; the GEMM kernel deals tiles from eight
+  // queues, one per XCD (home queue blockIdx mod 8, then the others), each a
+  // contiguous run of the tile list (expert, row tile, column tile), so an
+  // XCD's tiles share row tiles and W panels in its L2.
+  const int64_t nsched = FUSED ? (int64_t)a.misc[3] : nscatter;
+  const uint32_t ntile = (GEMM && !FUSED) ? a.misc[2] : 0u;
   uint32_t* tq = &a.misc[4];
   auto qbeg = [&](int q) { return (uint32_t)(((uint64_t)ntile * q) / kNumQueues); };
-  bool scattering = SCATTER;
   int qoff = 0;
   if constexpr (GEMM) {
     // received rows went to memory with device-coherent stores and none is
@@ -317,17 +359,15 @@ __global__ __launch_bounds__(Tile::NT) void a2a_gemm_kernel(A2aGemmArgs a) {
     __syncthreads();  // the previous item's LDS use is over
     if (tid == 0) {
       int64_t it = -1;
-      if (scattering) {
+      if (SCATTER) {
         const uint32_t v = __hip_atomic_fetch_add(&a.misc[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((int64_t)v < nscatter) it = v;
-      }
-      if (it < 0 && GEMM) {
-        // (reached only once every scatter item has been claimed)
+        if ((int64_t)v < nsched) it = v;
+      } else {
         const int home = (int)(blockIdx.x % kNumQueues);
         while (qoff < kNumQueues) {
           const int q = (home + qoff) % kNumQueues;
           const uint32_t v = __hip_atomic_fetch_add(&tq[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (v < qbeg(q + 1) - qbeg(q)) { it = nscatter + qbeg(q) + v; break; }
+          if (v < qbeg(q + 1) - qbeg(q)) { it = qbeg(q) + v; break; }
           ++qoff;
         }
       }
@@ -336,22 +376,39 @@ __global__ __launch_bounds__(Tile::NT) void a2a_gemm_kernel(A2aGemmArgs a) {
     __syncthreads();
     const int64_t item = uniform64(s_item);
     if (item < 0) break;
-    if (item < nscatter) scattering = true;
-    else scattering = false;
     if (SCATTER && item < npad) {
       a2g_pad<Tile::NT>(a, (int)(item / kA2gPadPieces), (int)(item % kA2gPadPieces));
       continue;
     }
-    if (SCATTER && item < nscatter) {
+    int e = 0, mt = 0, nt = 0;
+    if constexpr (FUSED) {
+      // stage st holds schedule positions [stage_item[st], stage_item[st+1]) after the padding
+      const uint32_t o = (uint32_t)(item - npad);
+      int st = 0;
+      while (st + 1 < a.P && o >= a.stage_item[st + 1]) ++st;
+      const uint32_t off = o - a.stage_item[st];
+      if (off < (uint32_t)a.cps) {
+        a2g_chunk<Tile::NT>(a, st * a.cps + (int)off, smem0);
+        continue;
+      }
+      uint32_t t = off - (uint32_t)a.cps;
+      while (e + 1 < E && t >= a.sn[st * E + e] * (uint32_t)a.ntiles) {
+        t -= a.sn[st * E + e] * (uint32_t)a.ntiles;
+        ++e;
+      }
+      mt = (int)(a.slo[st * E + e] + t / (uint32_t)a.ntiles);
+      nt = (int)(t % (uint32_t)a.ntiles);
+    } else if constexpr (SCATTER) {
       a2g_chunk<Tile::NT>(a, (int)(item - npad), smem0);
       continue;
+    } else {
+      // an expert tile of the list: (expert e, row tile mt, column tile nt)
+      const uint32_t t = (uint32_t)item;
+      while (e + 1 < E && t >= a.toff[e + 1]) ++e;
+      const uint32_t local = t - a.toff[e];
+      mt = (int)(local / (uint32_t)a.ntiles);
+      nt = (int)(local % (uint32_t)a.ntiles);
     }
-    // an expert tile: (expert e, row tile mt, column tile nt)
-    const uint32_t t = (uint32_t)(item - nscatter);
-    int e = 0;
-    while (e + 1 < E && t >= a.toff[e + 1]) ++e;
-    const uint32_t local = t - a.toff[e];
-    const int mt = (int)(local / (uint32_t)a.ntiles), nt = (int)(local % (uint32_t)a.ntiles);
     const uint32_t row0 = a.grp[e] + (uint32_t)mt * Tile::TM;
     if constexpr (FUSED) {
       // the row tile's rows (copied or zero-filled by items claimed earlier)
