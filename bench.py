@@ -73,8 +73,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)  # >= 200 timed calls of each operator
     ap.add_argument("--warmup", type=int, default=10)  # untimed steps first (10 calls of each operator)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
-    ap.add_argument("--ops", default="gemm_rs,gemm_rs_tiny,gemv_ar,ag_gemm,ag_gemm_paced,embbag_a2a,gemm_ar,"
-                                     "gemm_a2a,a2a_gemm,gemm_rs_unfused,gemv_ar_unfused,a2a_gemm_unfused,"
+    # (each fused operator and its unfused baseline run back to back within a step)
+    ap.add_argument("--ops", default="gemm_rs,gemm_rs_unfused,gemv_ar,gemv_ar_unfused,a2a_gemm,a2a_gemm_unfused,"
+                                     "gemm_rs_tiny,ag_gemm,ag_gemm_paced,embbag_a2a,gemm_ar,gemm_a2a,"
                                      "gemm_rs_decomp2_f32,gemm_rs_decomp4_f32,gemm_rs_decomp8_f32,"
                                      "hipblaslt_bmm")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")
@@ -463,11 +464,19 @@ def main():
                             config=dict(workload="device copy 1 GiB (counter calibration)"))
     torch.cuda.synchronize()
 
-    names = list(runs)
+    # timed in the order --ops lists them (operators added under another name last)
+    names = [o for o in ops if o in runs] + [n for n in runs if n not in ops]
     ev = {n: [] for n in names}
 
+    # every other step runs the operators in reverse order, so the two members of a
+    # fused / unfused pair each follow the other half of the time (an operator that comes
+    # right after a large GEMM measures slower than in isolation)
+    nstep = {"i": 0}
+
     def step(record):
-        for n in names:
+        order = names if nstep["i"] % 2 == 0 else names[::-1]
+        nstep["i"] += 1
+        for n in order:
             if "pre" in runs[n]:
                 runs[n]["pre"]()
             if record:

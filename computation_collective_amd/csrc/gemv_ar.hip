@@ -100,7 +100,10 @@ __device__ __forceinline__ void gemv_body(const GemvArArgs& a) {
   uint32_t* grp = a.ws + kWsExtra;
 
   for (int64_t item = blockIdx.x; item < a.total; item += gridDim.x) {
-    const int p = (int)(item / a.ntiles), j = (int)(item % a.ntiles);
+    // shard-minor numbering: with P = 8 the workgroups of one XCD (dispatched
+    // round-robin, XCD = index mod 8) all stream the same shard's weights,
+    // which measures about 3 % faster than spreading every shard over all XCDs
+    const int p = (int)(item % P), j = (int)(item / P);
     const int n0 = j * TN;
     const int cols_valid = min(TN, N - n0);
     const bool col_ok = cg * 8 < cols_valid;
@@ -231,11 +234,13 @@ __device__ __forceinline__ void gemv_body(const GemvArArgs& a) {
     }
     __syncthreads();
     if (uniform(s_last)) {
-      if (tid < P) {
-        const uint32_t* f = &a.part_flags[(int64_t)tid * a.ntiles + j];
-        expect_flag(f, load_flag_agent(f), a.sync);
-      }
+      // the count says every partial of tile j has landed (each producer
+      // waited for its stores before counting), so the fold's loads need not
+      // wait for the flags: they are read first and checked after the fold
+      const uint32_t* f = &a.part_flags[(int64_t)min(tid, P - 1) * a.ntiles + j];
+      const uint32_t seen = tid < P ? load_flag_agent(f) : a.sync.epoch;
       fold_column_tile<MB, TN, SDT, ODT>(a, j);
+      if (tid < P) expect_flag(f, seen, a.sync);
       wait_memory();
       __syncthreads();
       if (tid < P)

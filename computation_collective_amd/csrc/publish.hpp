@@ -143,6 +143,9 @@ __device__ __forceinline__ void store_tile(char* dst, int64_t ld, int rows_valid
       }
     // staged rows -> memory, 64 chunks (two to eight rows) per instruction;
     // LDS operations of one wave complete in order, so no barrier is needed
+    // (the clobber: lanes read rows other lanes wrote, so the compiler must
+    // not reuse loads from the previous block)
+    __asm__ volatile("" ::: "memory");
 #pragma unroll
     for (int it0 = 0; it0 < NIT; it0 += BATCH) {
       u32x4 v[BATCH];
