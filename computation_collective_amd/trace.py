@@ -22,6 +22,7 @@ the band it took.  From those:
     between XCDs).
 
   python -m computation_collective_amd.trace [--calls N] [--slot-dtype f32|bf16] [--out FILE]
+                                            [--save-out FILE.npy]
 
 runs the 8-shard 8192 x 4096 x 1792 bf16 workload (tile 256 x 256) N times
 on cuda:0 with the trace library and writes the summary of the last call.
@@ -190,6 +191,7 @@ def main(argv=None):
     ap.add_argument("--calls", type=int, default=3)
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--out", default=None)
+    ap.add_argument("--save-out", default=None, help="also save the last call's output tensor (.npy)")
     args = ap.parse_args(argv)
 
     sys.path.insert(0, ROOT)
@@ -240,6 +242,8 @@ def main(argv=None):
     lines += summarize(d, khz, c.P, mtiles, ntiles, pieces, span_event_us=ev_us)
     text = "\n".join(lines) + "\n"
     print(text, flush=True)
+    if args.save_out:
+        np.save(args.save_out, run.out.cpu().numpy())
     if args.out:
         os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
         with open(args.out, "w") as f:
