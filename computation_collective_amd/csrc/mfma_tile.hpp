@@ -269,22 +269,29 @@ struct NoSide {
   __device__ void fold(int) {}
 };
 
-// bf16 tile, full tiles only (no ragged rows, columns or K): both operand
-// slices go from global memory straight into LDS (gfx950 global_load_lds,
-// 16 bytes per lane, a wave writing 1 KB of LDS per instruction), so no
-// registers hold staged data and nothing is transposed in registers.
+// bf16 tile, full tiles only (no ragged rows, columns or K): both operands
+// go from global memory straight into LDS (gfx950 global_load_lds, 16 bytes
+// per lane, a wave writing 1 KB of LDS per instruction), so no registers hold
+// staged data and nothing is transposed in registers.
 //
-// NST LDS stages of a BK-deep K slice, loads issued NST-1 slices ahead: a
-// slice's loads have NST-1 slices of MFMA work to land, which hides the
-// latency of the L2 misses.  Each stage is its own __shared__ array (declared
-// by the kernel) and the K loop is unrolled by NST, so every LDS access names
-// its array; the compiler then knows that reading one stage does not alias
-// the loads still in flight into the others, and does not wait for them.
+// W: NST = 4 LDS stages of one 32-deep K slice ([BK][TN] rows, the kernel's
+// four stage arrays), loads issued three slices ahead.  A: two double stages
+// of two slices each ([TM][2*BK] rows of 128 bytes, direct_a_stage0/1).  An
+// A row of a single 32-deep slice would be 64 bytes, half a cache line, and
+// the vector L1 would then send two miss requests per line of A; the
+// operand stream of a tile is bound by how many misses the L1 keeps in
+// flight, and whole-line A requests (a third fewer requests in all) made
+// GEMM+ReduceScatter 3.5 % faster.  The price: an A double stage holding
+// slices (2d, 2d+1) is refilled, with slices 2d+4 and 2d+5, only after slice
+// 2d+1's reads, so A's loads get about a slice and a half to land where W's
+// get three.  Every stage is its own __shared__ array and the K loop is
+// unrolled by four slices, so every LDS access names its array; the compiler
+// then knows that reading one stage does not alias the loads still in flight
+// into the others, and does not wait for them.
 //
-// LDS per stage: A as [TM][BK] rows, W as [BK][TN] rows, in 16-byte chunks
-// XOR-swizzled on the global side (a lane may fetch any global address):
-//   A row m, logical chunk c -> physical chunk c ^ ((m / (16/CA)) mod CA),
-//                                CA = BK/8 chunks per A row
+// Layouts, in 16-byte chunks XOR-swizzled on the global side (a lane may
+// fetch any global address):
+//   A row m, logical chunk c (of 8) -> physical chunk c ^ ((m / 2) mod 8)
 //   W row k, logical chunk c -> physical chunk c ^ (4 * (k mod 4))
 // A fragments are 16-byte ds_read_b128 (8 consecutive k of one row of A).
 // W fragments use the gfx950 transposing read ds_read_b64_tr_b16: within a
@@ -292,30 +299,50 @@ struct NoSide {
 // lane i receives W[k0 .. k0+3][n0 + i]; two such reads give the 8
 // consecutive k of one column of W.  Both read patterns touch 16 distinct
 // 16-byte bank groups per 16 lanes (conflict-free).
+//
+// Load order: the prologue issues A(0..1), W(0), W(1), A(2..3), W(2); the
+// body W(3); slice j then issues W(j+4) and, for odd j, A(j+3 .. j+4).  The
+// wait of slice j counts the operations issued after the last one slice
+// j+1 needs: 2 W_LD + A_LD after an even slice, W_LD after an odd one, and
+// 2 W_LD + A_LD, 0, 0 in the last round (the band loads a side pass adds
+// in flight come on top).
+
+// The direct tiles' two A double stages (up to 256 rows x 64 k of bf16
+// each): one __shared__ array each, one definition per kernel, shared by
+// every direct tile the kernel uses.
+constexpr int kDirectAStageBytes = 256 * 64 * 2;
+__device__ __forceinline__ char* direct_a_stage0() {
+  __shared__ __attribute__((aligned(1024))) char a0[kDirectAStageBytes];
+  return a0;
+}
+__device__ __forceinline__ char* direct_a_stage1() {
+  __shared__ __attribute__((aligned(1024))) char a1[kDirectAStageBytes];
+  return a1;
+}
+
 template <int TM_, int TN_, int WM_, int WN_, int BK_ = 32, int NST_ = 4>
 struct TileBf16Direct {
   static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
   static constexpr bool kSplitMainloop = true;
   static constexpr int NW = WM * WN, NT = 64 * NW;
+  static_assert(BK_ == 32 && NST_ == 4, "one 32-deep slice per W stage, four W stages, two A double stages");
   static constexpr int BK = BK_, NST = NST_;
   static constexpr int WTM = TM / WM, WTN = TN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int A_BYTES = TM * BK * 2, W_BYTES = BK * TN * 2;
-  static constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
-  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
-  static constexpr int A_BLOCKS = A_BYTES / 1024, W_BLOCKS = W_BYTES / 1024;
-  static constexpr int A_LD = A_BLOCKS / NW, W_LD = W_BLOCKS / NW;  // per wave per stage
-  static constexpr int LPS = A_LD + W_LD;      // loads per wave per stage
-  static constexpr int CA = BK / 8;            // 16-byte chunks per A row
-  static constexpr int AROWS_PER_BLOCK = 1024 / (BK * 2);
-  static constexpr int CW = TN / 8;            // 16-byte chunks per W row
+  static constexpr int A2_BYTES = TM * 2 * BK * 2;   // two slices of A, 128-byte rows
+  static constexpr int W_BYTES = BK * TN * 2;
+  static constexpr int SMEM_BYTES = W_BYTES;          // each of the kernel's 4 stage arrays holds one W slice
+  static constexpr int LDS_BYTES = NST * W_BYTES + 2 * A2_BYTES;
+  static constexpr int A_LD = A2_BYTES / 1024 / NW;   // loads per wave per A double stage
+  static constexpr int W_LD = W_BYTES / 1024 / NW;    // loads per wave per W slice
+  static constexpr int CA = 2 * BK / 8;               // 16-byte chunks per A row (8)
+  static constexpr int AROWS_PER_BLOCK = 1024 / (2 * BK * 2);
+  static constexpr int CW = TN / 8;
   static constexpr int WROWS_PER_BLOCK = 512 / TN;
-  static constexpr int KSTEP = NST * BK;       // K must be a multiple of this
-  static constexpr int SMEM_BYTES = STAGE_BYTES;  // each of the NST stage arrays
+  static constexpr int KSTEP = NST * BK;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-  static_assert(A_BLOCKS % NW == 0 && W_BLOCKS % NW == 0 && TN >= 128 && TN <= 512, "layout");
-  static_assert((BK == 32 || BK == 64) && NST >= 2 && NST <= 4, "pipeline shape");
-  static_assert(2 * LPS <= 63 && NST <= 4, "vmcnt range");
+  static_assert((A2_BYTES / 1024) % NW == 0 && (W_BYTES / 1024) % NW == 0 && TN >= 128 && TN <= 512, "layout");
+  static_assert(A2_BYTES <= kDirectAStageBytes, "A double stage larger than the shared arrays");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
   __device__ static __forceinline__ void quad(int i, int j, int g, int lane, int wave, int& row,
@@ -332,13 +359,6 @@ struct TileBf16Direct {
         base, ld, rows_valid, cols_valid, acc);
   }
 
-  // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima)
-  template <int N>
-  __device__ static __forceinline__ void wait_vmcnt() {
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-  }
-
-  // The whole tile: prologue (the first NST slices' loads) and body.
   template <bool RAGGED>
   __device__ static __forceinline__ void run(const uint16_t* __restrict__ A, int64_t lda,
                                              const uint16_t* __restrict__ W, int64_t ldw,
@@ -347,12 +367,11 @@ struct TileBf16Direct {
     NoSide none;
     parts<RAGGED, true, true>(A, lda, W, ldw, rows_valid, cols_valid, K, stages, acc, none);
   }
-  // Split use: prologue() issues the loads of the first NST-1 slices into
-  // the stage arrays and returns; body() (same arguments) then issues the
-  // last and runs the K loop.  Between the two the workgroup may do anything
-  // that leaves the stage arrays alone and keeps at most 39 vector-memory
-  // operations of its own in flight at a time, while the prologue's loads
-  // are in flight.
+  // Split use: prologue() issues the loads of the first slices (A(0..3),
+  // W(0..2)) and returns; body() (same arguments) then issues W(3) and runs
+  // the K loop.  Between the two the workgroup may do anything that leaves
+  // the stage arrays alone: vector-memory operations it issues meanwhile only
+  // make body()'s first wait (counted from the end) wait longer.
   __device__ static __forceinline__ void prologue(const uint16_t* __restrict__ A, int64_t lda,
                                                   const uint16_t* __restrict__ W, int64_t ldw, int K,
                                                   char* const (&stages)[4]) {
@@ -368,12 +387,12 @@ struct TileBf16Direct {
     NoSide none;
     parts<RAGGED, false, true>(A, lda, W, ldw, rows_valid, cols_valid, K, stages, acc, none);
   }
-  // body() carrying side work at the ends of its rounds of NST slices:
+  // body() carrying side work at the ends of its rounds of four slices:
   // side.issue(u) after round u's last loads, side.fold(u) after round u+1
   // (u < Side::NPASS).  The caller guarantees K / (NST * BK) >= NPASS + 2,
   // so the side work ends before the last round that loads.
   static constexpr bool side_fits(int K, int npass) { return K / (NST * BK) >= npass + 2; }
-  // K values the slice schedule covers exactly (whole rounds of NST slices)
+  // K values the slice schedule covers exactly (whole rounds of four slices)
   static constexpr bool k_fits(int64_t K) { return K > 0 && K % KSTEP == 0; }
   // the operand loads address A's TM rows and W's K rows through 2 GiB
   // buffer resources (32-bit offsets from the tile's origin)
@@ -396,9 +415,7 @@ struct TileBf16Direct {
                                                char* const (&stages)[4], floatx16 (&acc)[FM][FN],
                                                Side& side) {
     static_assert(!RAGGED, "full tiles only");
-#if defined(__HIP_DEVICE_COMPILE__)  // device-only body (the host pass only needs the declaration)
-    // the wave index is wave-uniform: kept in a scalar register, so every
-    // per-wave LDS address below is scalar too
+#if defined(__HIP_DEVICE_COMPILE__)
     const int tid = threadIdx.x, lane = opaque_lane(), wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     if constexpr (BODY) {
@@ -410,11 +427,8 @@ struct TileBf16Direct {
           for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     }
     const int nk = K / BK;
-    // precondition (every launcher checks k_fits(K) before choosing this
-    // tile): K is a multiple of NST * BK.  Anything else would make the slice
-    // schedule below load past row K; should it ever get here, nothing is
-    // loaded and the accumulators are NaN, so the result cannot pass for a
-    // product (K == 0 is the empty product: zeros).
+    // precondition (every launcher checks k_fits(K)): K is a multiple of
+    // NST * BK; otherwise nothing is loaded and the accumulators are NaN
     if (nk == 0 || nk % NST != 0 || K % BK != 0) {
       if constexpr (BODY) {
         if (K != 0) {
@@ -428,11 +442,8 @@ struct TileBf16Direct {
       }
       return;
     }
+    char* const a_st[2] = {direct_a_stage0(), direct_a_stage1()};
 
-    // operand loads go through buffer resources over the tile's A rows and W
-    // columns: a 32-bit byte offset per lane and load (fixed over K), the
-    // slice's k offset in a scalar register -- no 64-bit pointer per load and
-    // stage in vector registers
     const __amdgpu_buffer_rsrc_t rsa = raw_rsrc(A), rsw = raw_rsrc(W);
     uint32_t aoff[A_LD], woff[W_LD];
 #pragma unroll
@@ -449,44 +460,46 @@ struct TileBf16Direct {
       const int c = (lane % CW) ^ (4 * (k & 3));
       woff[t] = (uint32_t)(((int64_t)k * ldw + c * 8) * 2);
     }
-    auto load_stage = [&](char* sb, int ks) {
-      const uint32_t ak = (uint32_t)ks * (BK * 2);
-      const uint32_t wk = (uint32_t)ks * (uint32_t)(BK * ldw * 2);
+    // A rows [.., k0 .. k0+63] of double stage kd (k0 = 64 kd) into ab
+    auto load_a = [&](char* ab, int kd) {
+      const uint32_t ak = (uint32_t)kd * (2 * BK * 2);
 #pragma unroll
       for (int t = 0; t < A_LD; ++t)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsa, (__attribute__((address_space(3))) void*)(sb + (t * NW + wave) * 1024), 16, aoff[t], ak, 0, 0);
+            rsa, (__attribute__((address_space(3))) void*)(ab + (t * NW + wave) * 1024), 16, aoff[t], ak, 0, 0);
+    };
+    auto load_w = [&](char* wb, int ks) {
+      const uint32_t wk = (uint32_t)ks * (uint32_t)(BK * ldw * 2);
 #pragma unroll
       for (int t = 0; t < W_LD; ++t)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsw, (__attribute__((address_space(3))) void*)(sb + A_BYTES + (t * NW + wave) * 1024), 16, woff[t],
-            wk, 0, 0);
+            rsw, (__attribute__((address_space(3))) void*)(wb + (t * NW + wave) * 1024), 16, woff[t], wk, 0, 0);
     };
 
     typedef short short4v __attribute__((ext_vector_type(4)));
-    auto read_frags = [&](const char* sb, int kk, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+    // fragments of k-substep kk of a slice: its A rows from half h of double
+    // stage ab, its W rows from stage wb
+    auto read_frags = [&](const char* ab, int h, const char* wb, int kk, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int m = wm * WTM + 32 * i + (lane & 31);
-        const int c = (kk * 2 + (lane >> 5)) ^ ((m / (16 / CA)) % CA);
-        a[i] = __builtin_bit_cast(bf16x8,
-                                  *reinterpret_cast<const uint4*>(sb + m * (BK * 2) + c * 16));
+        const int c = (h * 4 + kk * 2 + (lane >> 5)) ^ ((m / (16 / CA)) % CA);
+        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ab + m * (2 * BK * 2) + c * 16));
       }
       const int G = lane >> 4, s = lane & 15;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int n = wn * WTN + 32 * j + (G & 1) * 16 + 4 * (s & 3);
-        short4v h[2];
+        short4v hv[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int k = kk * 16 + (G >> 1) * 8 + 4 * hh + (s >> 2);
           const int c = (n >> 3) ^ (4 * (k & 3));
-          const char* p = sb + A_BYTES + k * (TN * 2) + c * 16 + (n & 7) * 2;
-          h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) short4v*)(p));
+          const char* p = wb + k * (TN * 2) + c * 16 + (n & 7) * 2;
+          hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
         }
-        const short __attribute__((ext_vector_type(8))) v8 = {h[0][0], h[0][1], h[0][2], h[0][3],
-                                                             h[1][0], h[1][1], h[1][2], h[1][3]};
+        const short __attribute__((ext_vector_type(8))) v8 = {hv[0][0], hv[0][1], hv[0][2], hv[0][3],
+                                                             hv[1][0], hv[1][1], hv[1][2], hv[1][3]};
         b[j] = __builtin_bit_cast(bf16x8, v8);
       }
     };
@@ -497,100 +510,77 @@ struct TileBf16Direct {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     };
-    // Schedule of one K slice j (two 16-deep k-substeps), with the
-    // fragments of substep 0 already in registers (set 0):
-    //   first half:  MFMAs of substep 0, interleaved one for one with the
-    //                LDS reads of substep 1's fragments (set 1);
-    //   sync:        this wave's share of slice j+1 has landed and its LDS
-    //                reads of slice j are done; barrier (so slice j+1 is
-    //                complete and stage j is free in every wave);
-    //   second half: loads of slice j+NST into stage j, MFMAs of substep 1,
-    //                and the LDS reads of slice j+1's substep-0 fragments
-    //                (set 0), all interleaved.
-    // Every LDS read thus has 16 MFMAs of work to hide behind, and the
-    // matrix pipe has queued work on both sides of the barrier.
-    constexpr int ND = FM + 2 * FN;  // LDS reads per substep
-    constexpr int NM = FM * FN;      // MFMAs per substep
-    static_assert(BK == 32, "the interleaved schedule covers two k-substeps per slice");
+    constexpr int ND = FM + 2 * FN;
+    constexpr int NM = FM * FN;
     bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
 
-    // waits for this wave's loads up to slice j+1 (LATER slices' loads may stay
-    // in flight) and for its LDS reads, then meets the other waves.  A bare
-    // s_barrier: __syncthreads() would add a release fence that drains every
-    // load in flight.
-    auto sync_slices = [&](auto later_c, auto extra_c) {
-      constexpr int N = decltype(later_c)::value * LPS + decltype(extra_c)::value;
+    auto sync_n = [&](auto n_c) {
+      constexpr int N = decltype(n_c)::value;
       static_assert(N <= 63, "vmcnt range");
       __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);  // vmcnt(N) lgkmcnt(0)
       __asm__ volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
     };
-    // slice j in stage ST; LOAD: issue slice j+NST into stage ST after the
-    // barrier; NEXT: read slice j+1's first fragments from stage (ST+1)%NST;
-    // LATER: slices whose loads were issued after slice j+1's; EXTRA: other
-    // vector-memory operations issued after slice j+1's loads
-    auto slice = [&](auto st_c, auto load_c, auto next_c, auto later_c, auto extra_c, int j) {
-      constexpr int ST = decltype(st_c)::value;
-      char* const sb = stages[ST];
-      read_frags(sb, 1, fa1, fb1);
+    // slice j = j0 + S of a round (W stage S, A double stage S / 2, half S % 2);
+    // LOAD: issue W(j+4) and, for odd S, A(j+3 .. j+4); NEXT: read slice j+1's
+    // first fragments; N: this slice's wait count
+    auto slice = [&](auto s_c, auto load_c, auto next_c, auto n_c, int j) {
+      constexpr int S = decltype(s_c)::value;
+      char* const wb = stages[S];
+      char* const ab = a_st[S / 2];
+      read_frags(ab, S % 2, wb, 1, fa1, fb1);
       mfmas(fa0, fb0);
       interleave<NM, ND, 0>();
-      sync_slices(later_c, extra_c);
-      if constexpr (decltype(load_c)::value) load_stage(sb, j + NST);
-      if constexpr (decltype(next_c)::value) read_frags(stages[(ST + 1) % NST], 0, fa0, fb0);
+      sync_n(n_c);
+      constexpr bool LOADA = decltype(load_c)::value && (S % 2 == 1);
+      if constexpr (decltype(load_c)::value) load_w(wb, j + NST);
+      if constexpr (LOADA) load_a(a_st[((S + 3) / 2) % 2], (j + 3) / 2);
+      if constexpr (decltype(next_c)::value)
+        read_frags(a_st[((S + 1) % NST) / 2], (S + 1) % 2, stages[(S + 1) % NST], 0, fa0, fb0);
       mfmas(fa1, fb1);
-      interleave<NM, decltype(next_c)::value ? ND : 0, decltype(load_c)::value ? LPS : 0>();
+      interleave<NM, decltype(next_c)::value ? ND : 0,
+                 decltype(load_c)::value ? W_LD + (LOADA ? A_LD : 0) : 0>();
     };
     using T_ = std::integral_constant<bool, true>;
     using F_ = std::integral_constant<bool, false>;
 
-    // prologue: every stage loading.  In split use the prologue issues the
-    // first NST-1 stages (NST-1 batches of LPS loads) and the body the last
-    // one, so that whatever runs in between can keep up to 63 - (NST-1)*LPS
-    // (= 39) more vector-memory operations of its own in flight.
     if constexpr (PRO) {
-#pragma unroll
-      for (int s = 0; s < NST - 1; ++s) load_stage(stages[s], s);
+      load_a(a_st[0], 0);
+      load_w(stages[0], 0);
+      load_w(stages[1], 1);
+      load_a(a_st[1], 1);
+      load_w(stages[2], 2);
     }
     if constexpr (!BODY) return;
-    using Z_ = std::integral_constant<int, 0>;
-    load_stage(stages[NST - 1], NST - 1);
-    // slice 0 landed everywhere: the wait leaves only the NST-1 batches issued
-    // last in flight, and slice 0's were issued before them
-    sync_slices(std::integral_constant<int, NST - 1>{}, Z_{});
-    read_frags(stages[0], 0, fa0, fb0);
+    load_w(stages[3], 3);
+    sync_n(std::integral_constant<int, 2 * W_LD + A_LD + W_LD>{});  // slice 0 landed: W(1), A(2..3), W(2), W(3) may not have
+    read_frags(a_st[0], 0, stages[0], 0, fa0, fb0);
 
-    // One round = NST slices starting at slice j0 (stage s holds slice j0+s).
-    // Every slice of a round but the last waits for loads issued in the
-    // previous round; if side work issued PV loads at that round's end, after
-    // those, the waits allow for them (PV more operations in flight).
-    static_assert(NST == 4, "round structure");
     auto round = [&](auto pv_c, auto loads_c, int j0) {
+      constexpr int PV = decltype(pv_c)::value;
       using L_ = decltype(loads_c);
-      using LT_ = std::integral_constant<int, NST - 2>;
       if constexpr (L_::value) {
-        slice(std::integral_constant<int, 0>{}, T_{}, T_{}, LT_{}, pv_c, j0);
-        slice(std::integral_constant<int, 1>{}, T_{}, T_{}, LT_{}, pv_c, j0 + 1);
-        slice(std::integral_constant<int, 2>{}, T_{}, T_{}, LT_{}, pv_c, j0 + 2);
-        slice(std::integral_constant<int, 3>{}, T_{}, T_{}, LT_{}, Z_{}, j0 + 3);
+        slice(std::integral_constant<int, 0>{}, T_{}, T_{}, std::integral_constant<int, 2 * W_LD + A_LD + PV>{}, j0);
+        slice(std::integral_constant<int, 1>{}, T_{}, T_{}, std::integral_constant<int, W_LD + PV>{}, j0 + 1);
+        slice(std::integral_constant<int, 2>{}, T_{}, T_{}, std::integral_constant<int, 2 * W_LD + A_LD + PV>{}, j0 + 2);
+        slice(std::integral_constant<int, 3>{}, T_{}, T_{}, std::integral_constant<int, W_LD>{}, j0 + 3);
       } else {
-        // the last round: no loads
-        slice(std::integral_constant<int, 0>{}, F_{}, T_{}, LT_{}, pv_c, j0);
-        slice(std::integral_constant<int, 1>{}, F_{}, T_{}, std::integral_constant<int, 1>{}, pv_c, j0 + 1);
-        slice(std::integral_constant<int, 2>{}, F_{}, T_{}, Z_{}, pv_c, j0 + 2);
-        slice(std::integral_constant<int, 3>{}, F_{}, F_{}, Z_{}, Z_{}, j0 + 3);
+        slice(std::integral_constant<int, 0>{}, F_{}, T_{}, std::integral_constant<int, 2 * W_LD + A_LD + PV>{}, j0);
+        slice(std::integral_constant<int, 1>{}, F_{}, T_{}, std::integral_constant<int, 0>{}, j0 + 1);
+        slice(std::integral_constant<int, 2>{}, F_{}, T_{}, std::integral_constant<int, 0>{}, j0 + 2);
+        slice(std::integral_constant<int, 3>{}, F_{}, F_{}, std::integral_constant<int, 0>{}, j0 + 3);
       }
     };
-    // side work at a round's end, kept after every load of that round
     auto side_step = [&](auto fold_c, auto issue_c, int u) {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (decltype(fold_c)::value) side.fold(u - 1);
       if constexpr (decltype(issue_c)::value) side.issue(u);
       __builtin_amdgcn_sched_barrier(0);
     };
+    using Z_ = std::integral_constant<int, 0>;
     using PV_ = std::integral_constant<int, Side::V>;
-    const int nr = nk / NST;  // K is a multiple of NST*BK: whole rounds, the last without loads
+    const int nr = nk / NST;
     int r = 0;
     if constexpr (Side::NPASS > 0) {
       round(Z_{}, T_{}, 0);
