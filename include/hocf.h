@@ -9,10 +9,12 @@
  *                    kommunikációval gyorsítják az AI-betanítást a kutatók",
  *                    section on its five fused kernels)
  *   hocf_gemm_ar     GEMM + AllReduce       (mKernel news item, same section)
- *   hocf_gemm_rs_unfused, hocf_gemv_ar_unfused
- *                    the same GEMM + ReduceScatter / GEMV + AllReduce as two
- *                    kernels, the computation then the collective (the
- *                    baseline SC24 measures its fused operators against)
+ *   hocf_gemm_rs_unfused, hocf_gemv_ar_unfused, hocf_a2a_gemm_unfused
+ *                    the same operators as separate kernels, the computation
+ *                    and the collective one after the other (the baseline
+ *                    SC24 measures its fused operators against)
+ *   hocf_gemm_rs_noalloc
+ *                    GEMM + ReduceScatter for callers that cannot allocate
  *   hocf_gemm_rs_decomposed
  *                    the same GEMM + ReduceScatter in column pieces pipelined
  *                    on two streams (Compass, abstract: InterDecom)
