@@ -23,14 +23,16 @@
 //      restarts at every source) -- then the padded group offsets, the
 //      expert tiles, the send counts, and zeroed arrival counters;
 //   3. the fused kernel (persistent): work items in claim order are the
-//      padding fills (each group's padding in a few pieces), the C chunks (each workgroup ranks its chunk's pairs
+//      padding fills (each group's padding in a few pieces), then for each
+//      source its chunks followed by the expert tiles whose row tile gets
+//      its last row from that source.  A chunk item ranks the chunk's pairs
 //      per expert with wave ballots, copies their token rows into the
 //      receive buffer with device-coherent stores, writes dest and slot,
-//      then counts the rows landed per row tile), and the expert tiles;
-//      a tile waits (bounded) until its row tile has all its rows, then runs
-//      the direct-to-LDS MFMA mainloop of the other GEMMs and stores Y.
-//      Every tile waits only on items claimed before it by running
-//      workgroups, so the kernel needs no co-residency to finish.
+//      then counts the rows landed per row tile.  A tile waits (bounded)
+//      until its row tile has all its rows, then runs the direct-to-LDS
+//      MFMA mainloop of the other GEMMs and stores Y.  Every tile waits only
+//      on items claimed before it by running workgroups, so the kernel needs
+//      no co-residency to finish.
 // The unfused baseline runs the scatter items as one kernel and the tiles as
 // the next (bit-identical results).
 #include "internal.hpp"
