@@ -451,14 +451,15 @@ int launch_gemm_rs(const GemmRsArgs& a, int tm, int tn, int in_dt, hipStream_t s
 // grid capped to leave fold_cus CUs free) run on s, an event marks their
 // end, and its fold runs on coll after that event -- while piece i+1's
 // GEMMs run on s.  At the end s waits for coll's last fold.  The events are
-// kept per device (created at first use and reused by every later call).
+// kept per host thread and device (created at first use, reused by every
+// later call of that thread).
 static hipError_t piece_events(hipEvent_t** out) {
-  static std::mutex mu;
-  static std::unordered_map<int, std::vector<hipEvent_t>> ev;
+  // per host thread and device: a call records and waits on its events in
+  // order, so another thread's call cannot record one of them in between
+  thread_local std::unordered_map<int, std::vector<hipEvent_t>> ev;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lk(mu);
   std::vector<hipEvent_t>& v = ev[dev];
   while (v.size() < (size_t)kMaxPieces + 1) {
     hipEvent_t x = nullptr;
