@@ -249,14 +249,20 @@ __device__ __forceinline__ void gemv_body(const GemvArArgs& a) {
   }
 }
 
+// Two workgroups per CU where the registers allow (up to 4 batch rows); with
+// 5 to 8 rows the accumulators and the two load batches need more than the
+// 128 registers two workgroups per CU leave, so those run one per CU rather
+// than spill to scratch.
+constexpr int gemv_wgs_per_cu(int mb) { return mb <= 4 ? 2 : 1; }
+
 template <int MB, int TN, int SDT, int ODT>
-__global__ __launch_bounds__(kGemvThreads, 2) void gemv_ar_kernel(GemvArArgs a) {
+__global__ __launch_bounds__(kGemvThreads, gemv_wgs_per_cu(MB)) void gemv_ar_kernel(GemvArArgs a) {
   gemv_body<MB, TN, SDT, ODT, true>(a);
 }
 
 // The unfused baseline: the GEMV publishing its partials and nothing else ...
 template <int MB, int TN, int SDT, int ODT>
-__global__ __launch_bounds__(kGemvThreads, 2) void unfused_gemv_kernel(GemvArArgs a) {
+__global__ __launch_bounds__(kGemvThreads, gemv_wgs_per_cu(MB)) void unfused_gemv_kernel(GemvArArgs a) {
   gemv_body<MB, TN, SDT, ODT, false>(a);
 }
 

@@ -668,7 +668,9 @@ struct TileF32 {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    float4 ra[A_LD], rb[B_LD];
+    // (vector types, not the float4 struct: an aggregate copy of the struct
+    // into LDS kept these staging registers on the stack)
+    floatx4 ra[A_LD], rb[B_LD];
     const int nk = (K + BK - 1) / BK;
 
     auto load_global = [&](int ks) {
@@ -678,18 +680,18 @@ struct TileF32 {
         const int c = tid + t * NT;
         const int row = c / (BK / 4), k = k0 + (c % (BK / 4)) * 4;
         if (!RAGGED || (row < rows_valid && k < K))
-          ra[t] = *reinterpret_cast<const float4*>(A + (int64_t)row * lda + k);
+          ra[t] = *reinterpret_cast<const floatx4*>(A + (int64_t)row * lda + k);
         else
-          ra[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+          ra[t] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int t = 0; t < B_LD; ++t) {
         const int c = tid + t * NT;
         const int k = k0 + c / (TN / 4), n = (c % (TN / 4)) * 4;
         if (!RAGGED || (k < K && n < cols_valid))
-          rb[t] = *reinterpret_cast<const float4*>(W + (int64_t)k * ldw + n);
+          rb[t] = *reinterpret_cast<const floatx4*>(W + (int64_t)k * ldw + n);
         else
-          rb[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+          rb[t] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
     };
     auto store_lds = [&](int stage) {
@@ -699,16 +701,16 @@ struct TileF32 {
       for (int t = 0; t < A_LD; ++t) {
         const int c = tid + t * NT;
         const int row = c / (BK / 4), kq = (c % (BK / 4)) * 4;
-        As[row * LDA + kq + 0] = ra[t].x;
-        As[row * LDA + kq + 1] = ra[t].y;
-        As[row * LDA + kq + 2] = ra[t].z;
-        As[row * LDA + kq + 3] = ra[t].w;
+        As[row * LDA + kq + 0] = ra[t][0];
+        As[row * LDA + kq + 1] = ra[t][1];
+        As[row * LDA + kq + 2] = ra[t][2];
+        As[row * LDA + kq + 3] = ra[t][3];
       }
 #pragma unroll
       for (int t = 0; t < B_LD; ++t) {
         const int c = tid + t * NT;
         const int k = c / (TN / 4), n = (c % (TN / 4)) * 4;
-        *reinterpret_cast<float4*>(Bs + k * LDB + n) = rb[t];
+        *reinterpret_cast<floatx4*>(Bs + k * LDB + n) = rb[t];
       }
     };
     auto compute = [&](int stage) {
