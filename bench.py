@@ -34,6 +34,16 @@ at its workload size, on one HIP stream, inputs already resident in HBM:
               as d column pieces, each piece's GEMM on the step's stream with F CUs left free, its
               fold on a second stream overlapping the next piece's GEMM; `fusion.gemm_rs` lists them
 
+ag_gemm_dma, ag_gemm_cu_put  the ag_gemm workload with its seven remote chunks delivered during
+              the call by hocf_dma_put on a second stream (HOCCL's copy-engine communication):
+              on the copy (SDMA) engines, no compute unit, or on the runtime's copy kernels
+              (each chunk signalled by its flag)
+dma_put, cu_put  those seven 8 MB puts alone, unsignalled (ordered by the streams alone; GB/s
+              counts each byte read and written)
+gemm_rs_dma_put, gemm_rs_cu_put  the gemm_rs workload with the same unsignalled puts enqueued just
+              before it on a second stream: what communication on the copy engines, or on the
+              compute units, costs a kernel that holds every CU
+
 hipblaslt_bmm: context, not an operator of this library -- torch.bmm (hipBLASLt) on the same
 eight shard GEMMs as gemm_rs, with no collective.
 
@@ -229,7 +239,8 @@ def main():
 
         def ag_pre(a=a, order=order, st=ag_state):
             # the chunk flags, written in the seeded order on the kernel's own stream before the
-            # kernel (the zero-CU releaser); outside the timed events: the kernel's span is timed
+            # kernel (stream write-values: the runtime runs each as a one-workgroup kernel);
+            # outside the timed events: the kernel's span is timed
             st["sync"] = a.prerelease(order, stream=stream)
 
         def ag_call(a=a, st=ag_state):
@@ -267,6 +278,88 @@ def main():
                                                  tile=[c.tile_m, c.tile_n], chunk_gap_us=args.chunk_gap_us,
                                                  arrival_span_us=(c.P - 1) * args.chunk_gap_us,
                                                  release_order=[int(v) for v in order]))
+    # HOCCL's copy-engine communication on one GPU: the AllGather's seven remote 8 MB chunks
+    # moved by hocf_dma_put (each chunk's bytes, then its flag) on a second stream, either on
+    # the copy (SDMA) engines with no compute unit, or on the runtime's copy kernels
+    put_ops = [o for o in ("ag_gemm_dma", "ag_gemm_cu_put", "dma_put", "cu_put", "gemm_rs_dma_put",
+                           "gemm_rs_cu_put") if o in ops]
+    if put_ops:
+        c = cfgs.AG_GEMM_COL
+        log(f"inputs {c.name} (copy-engine puts: {', '.join(put_ops)})")
+        put_stream = torch.cuda.Stream(device=dev)
+        chunks, W, order = gen.ag_gemm_inputs(c.P, c.Mc, c.N, c.K, seed=0)
+        local = int(order[0])          # this rank's own chunk: in place, its put only signals
+        chunk_bytes = 2 * c.Mc * c.K
+        remote = [int(q) for q in order if int(q) != local]
+        put_bytes = chunk_bytes * len(remote)
+        engines = {"dma": hocf.HOCF_ENGINE_DMA, "cu": hocf.HOCF_ENGINE_CU}
+        for name, eng in (("ag_gemm_dma", "dma"), ("ag_gemm_cu_put", "cu")):
+            if name not in ops:
+                continue
+            ad = bf.AgGemm(c.P, c.Mc, c.N, c.K, bf.BF16, c.tile_m, c.tile_n, chunks, W)
+            sends = [None if q == local else ad.A[q].clone() for q in range(c.P)]
+
+            def ag_put_call(a=ad, sends=sends, engine=engines[eng]):
+                a.put_delivered(sends, order, engine, put_stream, stream=stream,
+                                spin_timeout_ns=2_000_000_000)
+
+            runs[name] = dict(call=ag_put_call, obj=ad, work=c.flops, unit="TFLOP/s", bound="mfma",
+                              peak=PEAK_BF16_TFLOPS, variant=f"tile={c.tile_m}x{c.tile_n} {eng} puts",
+                              bytes=2 * (c.P * c.Mc * c.K + c.K * c.N + c.P * c.Mc * c.N) + 2 * put_bytes,
+                              put_bytes=put_bytes,
+                              config=dict(workload=f"{c.name}_{eng}_put", P=c.P, Mc=c.Mc, N=c.N, K=c.K,
+                                          tile=[c.tile_m, c.tile_n], engine=eng, put_bytes=put_bytes,
+                                          release_order=[int(v) for v in order]))
+        # the same seven puts alone, and beside the GEMM+ReduceScatter kernel (which holds every CU)
+        psrc = [torch.from_numpy(chunks[q].view(np.int16)).to(dev) for q in remote]
+        pdst = torch.empty((len(remote), c.Mc * c.K), dtype=torch.int16, device=dev)
+
+        def enqueue_puts(engine):
+            put_stream.wait_stream(stream)
+            # no signals: whatever consumes the bytes is ordered after the puts by the streams
+            hocf.check(hocf.hocf_dma_put(psrc, [pdst[i] for i in range(len(remote))], [chunk_bytes] * len(remote),
+                                         None, None, engine, put_stream))
+
+        for name, eng in (("dma_put", "dma"), ("cu_put", "cu")):
+            if name not in ops:
+                continue
+
+            def put_call(engine=engines[eng]):
+                enqueue_puts(engine)
+                stream.wait_stream(put_stream)
+
+            runs[name] = dict(call=put_call, obj=None, work=2 * put_bytes, unit="GB/s", bound="hbm",
+                              peak=PEAK_HBM_GBS, bytes=2 * put_bytes, put_bytes=put_bytes,
+                              config=dict(workload=f"put_7x8MB_{eng}", engine=eng, puts=len(remote),
+                                          put_bytes=put_bytes))
+        gr = [o for o in ("gemm_rs_dma_put", "gemm_rs_cu_put") if o in ops]
+        if gr:
+            cg = cfgs.GEMM_RS_MLP
+            if "gemm_rs" in runs:
+                rg = runs["gemm_rs"]["obj"]
+            else:
+                A_, W_ = gen.gemm_rs_inputs(cg.P, cg.M, cg.N, cg.K, cg.in_dt, seed=0)
+                rg = bf.GemmRS(cg.P, cg.M, cg.N, cg.K, cg.in_dt, sdt, cg.out_dt, cg.tile_m, cg.tile_n, A_, W_)
+                del A_, W_
+            for name in gr:
+                eng = "dma" if name == "gemm_rs_dma_put" else "cu"
+
+                marks = []
+
+                def gemm_put_call(engine=engines[eng], r=rg, marks=marks):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    enqueue_puts(engine)       # first, so the puts do not wait for the GEMM
+                    r.run(stream)
+                    b.record(stream)           # the GEMM's own end, before the wait for the puts
+                    marks.append((a, b))
+                    stream.wait_stream(put_stream)
+
+                runs[name] = dict(call=gemm_put_call, obj=rg, work=cg.flops, unit="TFLOP/s", bound="mfma",
+                                  peak=PEAK_BF16_TFLOPS, bytes=0, put_bytes=put_bytes, marks=marks,
+                                  variant=f"slot_dtype={args.slot_dtype} tile={cg.tile_m}x{cg.tile_n} {eng} puts",
+                                  config=dict(workload=f"{cg.name}_with_{eng}_puts_7x8MB", engine=eng,
+                                              put_bytes=put_bytes, slot_dtype=args.slot_dtype))
     if "embbag_a2a" in ops:
         c = cfgs.EMBBAG_DLRM
         log(f"inputs {c.name} (tables on the device)")
@@ -537,6 +630,14 @@ def main():
         }
         if "logical" in R:
             out_ops[n]["logical_gbps"] = round(R["logical"] / (avg * 1e-3) / 1e9, 1)
+        if "put_bytes" in R:
+            # the puts' own rate: bytes delivered over the call's span
+            out_ops[n]["put_gbps"] = round(R["put_bytes"] / (avg * 1e-3) / 1e9, 1)
+        if "marks" in R:
+            # the kernel's own span (from before the puts to its end), apart from the wait for the puts
+            km = [a.elapsed_time(b) for a, b in R["marks"][-len(ms):]]
+            out_ops[n]["kernel_ms_avg"] = round(sum(km) / len(km), 4)
+            log(f"{n}: kernel {sum(km) / len(km):.4f} ms of the {avg:.4f} ms span")
         if n == "ag_gemm_paced":
             # how long the kernel runs on after the last chunk has arrived
             out_ops[n]["after_last_arrival_us"] = round(avg * 1e3 - R["config"]["arrival_span_us"], 1)

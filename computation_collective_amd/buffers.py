@@ -240,6 +240,50 @@ class AgGemm(_Common):
         return s.epoch
 
 
+    def put_delivered(self, sources, order, engine, put_stream, stream=None, **kw):
+        """Chunks delivered by hocf_dma_put on `put_stream` while the kernel runs on
+        `stream`: one put per chunk in `order` (chunk c's bytes from sources[c] into
+        its rows of the gathered buffer, then its flag); sources[c] None: the chunk is
+        already in place (the local one) and its put only signals.  The puts are
+        enqueued first and wait for nothing but `stream`'s earlier work, so the
+        kernel starts while they land.  Returns the call's sync."""
+        assert self.flags_mode == "device" and isinstance(self.A, torch.Tensor)
+        stream = stream or torch.cuda.current_stream()
+        s = self.next_sync(**kw)
+        chunk_bytes = self.Mc * self.K * 2
+        base, fbase = self.A.data_ptr(), self.chunk_flags.data_ptr()
+        src, dst, nbytes, sig = [], [], [], []
+        for c in order:
+            c = int(c)
+            here = sources[c] is None
+            src.append(None if here else sources[c])
+            dst.append(None if here else base + c * chunk_bytes)
+            nbytes.append(0 if here else chunk_bytes)
+            sig.append(fbase + 4 * c)
+        put_stream.wait_stream(stream)
+        hocf.check(hocf.hocf_dma_put(src, dst, nbytes, sig, epoch_word(s.epoch, self.A.device), engine,
+                                     put_stream))
+        hocf.check(self.call(s, stream))
+        stream.wait_stream(put_stream)
+        return s
+
+
+_epoch_words = {}
+_EPOCH_WORDS = 1 << 16
+
+
+def epoch_word(epoch: int, device) -> int:
+    """Device address of a word holding `epoch` (1 <= epoch < 65536), from a table
+    written once per device: the source a put copies into a flag, so that the
+    put's signal needs no kernel to prepare it."""
+    assert 1 <= epoch < _EPOCH_WORDS, epoch
+    key = str(device)
+    if key not in _epoch_words:
+        _epoch_words[key] = torch.arange(_EPOCH_WORDS, dtype=torch.int32, device=device)
+        torch.cuda.synchronize(device)
+    return _epoch_words[key].data_ptr() + 4 * epoch
+
+
 def ctypes_char_array(addr, nbytes):
     import ctypes
     return (ctypes.c_char * nbytes).from_address(addr)

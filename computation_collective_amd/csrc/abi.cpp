@@ -799,4 +799,75 @@ hocf_status hocf_embbag_a2a(int T, int64_t R, int D, int B, int L, int P, const 
   return launched(hocf::launch_embbag_a2a(a, static_cast<hipStream_t>(stream)), "embbag_a2a");
 }
 
+/* ------------------------------------------------------------ copy-engine puts */
+
+// One device pointer of the current device, checked with the runtime.
+static hocf_status device_range(const char* what, int idx, const void* p, int dev) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // the query's error is ours to clear
+    return fail(HOCF_ERR_INVALID_ARG, "dma_put: %s[%d] is not memory the HIP runtime knows", what, idx);
+  }
+  if (at.type != hipMemoryTypeDevice || at.device != dev)
+    return fail(HOCF_ERR_INVALID_ARG, "dma_put: %s[%d] is not device memory of device %d", what, idx, dev);
+  return HOCF_OK;
+}
+
+hocf_status hocf_dma_put(int n, const void* const* src, void* const* dst, const int64_t* bytes,
+                         uint32_t* const* signal, const uint32_t* signal_value, hocf_engine engine,
+                         void* stream) {
+  if (n < 0 || n > HOCF_MAX_PUTS) return fail(HOCF_ERR_INVALID_ARG, "dma_put: n=%d outside [0, %d]", n, HOCF_MAX_PUTS);
+  if (engine != HOCF_ENGINE_DMA && engine != HOCF_ENGINE_CU)
+    return fail(HOCF_ERR_INVALID_ARG, "dma_put: unknown engine %d", (int)engine);
+  if (n == 0) return ok();
+  if (!src || !dst || !bytes) return fail(HOCF_ERR_INVALID_ARG, "dma_put: NULL argument array");
+  bool signals = false;
+  for (int i = 0; signal && i < n; ++i) signals = signals || signal[i];
+  if (signals && (!signal_value || (reinterpret_cast<uintptr_t>(signal_value) & 3u)))
+    return fail(HOCF_ERR_INVALID_ARG, "dma_put: signal_value NULL or not 4-byte aligned");
+  hocf_status st;
+  {
+    Ranges rg;
+    if (signals) rg.in("signal_value", 0, signal_value, 4);
+    for (int i = 0; i < n; ++i) {
+      if (bytes[i] < 0) return fail(HOCF_ERR_INVALID_ARG, "dma_put: bytes[%d] < 0", i);
+      if (bytes[i] > 0 && (!src[i] || !dst[i])) return fail(HOCF_ERR_INVALID_ARG, "dma_put: put %d has a NULL buffer", i);
+      if (bytes[i] > 0 && (!aligned16(src[i]) || !aligned16(dst[i])))
+        return fail(HOCF_ERR_INVALID_ARG, "dma_put: put %d misaligned (16 bytes)", i);
+      if (signal && signal[i] && (reinterpret_cast<uintptr_t>(signal[i]) & 3u))
+        return fail(HOCF_ERR_INVALID_ARG, "dma_put: signal[%d] not 4-byte aligned", i);
+      rg.in("src", i, src[i], bytes[i]);
+      rg.out("dst", i, dst[i], bytes[i]);
+      if (signal) rg.out("signal", i, signal[i], 4);
+    }
+    if ((st = rg.check("dma_put")) != HOCF_OK) return st;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(HOCF_ERR_HIP, "dma_put: no current HIP device");
+  if (signals && (st = device_range("signal_value", 0, signal_value, dev)) != HOCF_OK) return st;
+  for (int i = 0; i < n; ++i) {
+    if (bytes[i] > 0 && ((st = device_range("src", i, src[i], dev)) != HOCF_OK ||
+                         (st = device_range("dst", i, dst[i], dev)) != HOCF_OK))
+      return st;
+    if (signal && signal[i] && (st = device_range("signal", i, signal[i], dev)) != HOCF_OK) return st;
+  }
+
+  // Each put is one or two copies on the stream: the bytes, then the signal
+  // word.  The stream orders them (each starts once the one before it has
+  // completed), so a consumer that sees the signal sees the bytes.  Asked for
+  // the DMA engine, the runtime moves a copy of 64 KB or more on a copy
+  // (SDMA) engine; it runs smaller ones, and so every signal, as its own
+  // one-workgroup copy kernel.  Asked for the CU engine, it runs its copy
+  // kernels throughout.
+  const hipMemcpyKind kind = engine == HOCF_ENGINE_DMA ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = hipSuccess;
+    if (bytes[i] > 0) e = hipMemcpyAsync(dst[i], src[i], (size_t)bytes[i], kind, s);
+    if (e == hipSuccess && signal && signal[i]) e = hipMemcpyAsync(signal[i], signal_value, 4, kind, s);
+    if (e != hipSuccess) return fail(HOCF_ERR_HIP, "dma_put: put %d of %d: %s (puts before it stay enqueued)", i, n, hipGetErrorString(e));
+  }
+  return ok();
+}
+
 }  // extern "C"

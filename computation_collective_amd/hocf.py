@@ -38,6 +38,7 @@ EXPORTED = [
     "hocf_embbag_a2a", "hocf_embbag_a2a_workspace_bytes",
     "hocf_gemm_a2a", "hocf_gemm_a2a_workspace_bytes",
     "hocf_a2a_gemm", "hocf_a2a_gemm_unfused", "hocf_a2a_gemm_workspace_bytes",
+    "hocf_dma_put",
     "hocf_status_string", "hocf_last_error", "hocf_abi_version",
 ]
 
@@ -112,6 +113,9 @@ def lib():
                   "hocf_ag_gemm_workspace_bytes", "hocf_embbag_a2a_workspace_bytes",
                   "hocf_gemm_a2a_workspace_bytes"):
             getattr(L, f).restype = sz
+        PV = ctypes.POINTER(vp)
+        L.hocf_dma_put.argtypes = [i, PV, PV, ctypes.POINTER(i64), PV, vp, i, vp]
+        L.hocf_dma_put.restype = i
         L.hocf_status_string.argtypes = [i]
         L.hocf_status_string.restype = ctypes.c_char_p
         L.hocf_last_error.argtypes = []
@@ -255,6 +259,18 @@ def hocf_ag_gemm(P, Mc, N, K, in_dt, out_dt, A_gathered, chunk_flags, W, out, ti
                  sync_, stream=None) -> int:
     return lib().hocf_ag_gemm(P, Mc, N, K, in_dt, out_dt, ptr(A_gathered), ptr(chunk_flags),
                               ptr(W), ptr(out), tile_m, tile_n, ctypes.byref(sync_), _stream(stream))
+
+
+HOCF_ENGINE_DMA, HOCF_ENGINE_CU = 0, 1
+
+
+def hocf_dma_put(src, dst, nbytes, signal, signal_value, engine, stream=None) -> int:
+    """Puts i = 0..n-1 on `stream`: nbytes[i] bytes src[i] -> dst[i], then the word
+    at signal_value -> signal[i] (tensors or device addresses; src/dst may be None
+    where nbytes[i] == 0)."""
+    n = len(nbytes)
+    return lib().hocf_dma_put(n, pointers(src), pointers(dst), (ctypes.c_int64 * n)(*[int(b) for b in nbytes]),
+                              pointers(signal), ptr(signal_value), engine, _stream(stream))
 
 
 def hocf_embbag_a2a(T, R, D, B, L, P, tables, indices, offsets, win, tile_bags, sync_,

@@ -3,7 +3,8 @@
  *
  * C ABI of libhocf.so.  Seven operators, each one GPU's share of a P-way
  * tensor-parallel (or model-parallel) step with the P logical shards'
- * receive windows in local HBM:
+ * receive windows in local HBM, their baselines, and a put that moves such
+ * traffic on the copy engines:
  *
  *   hocf_gemm_rs     GEMM + ReduceScatter   (mKernel news item "GPU-vezérelt
  *                    kommunikációval gyorsítják az AI-betanítást a kutatók",
@@ -26,6 +27,10 @@
  *   hocf_gemm_a2a    GEMM + All-to-All, the MoE combine (SC24 abstract)
  *   hocf_a2a_gemm    All-to-All + GEMM, the MoE dispatch (mKernel news item,
  *                    section on its five fused kernels)
+ *   hocf_dma_put     point-to-point puts (optionally signalled) moved by
+ *                    the copy (SDMA) engines instead of the compute units
+ *                    ("HOCCL: Offloading Collective Communication from GPU
+ *                    Cores to Accelerate Distributed Training", abstract)
  *
  * The method (SC24 abstract; mKernel, section on persistent kernels and
  * tile/chunk overlap): the workgroups of one kernel each finish an output
@@ -452,6 +457,57 @@ hocf_status hocf_embbag_a2a(int T, int64_t R, int D, int B, int L, int P, const 
                             const hocf_window* win, int tile_bags, const hocf_sync* sync,
                             void* stream);
 size_t hocf_embbag_a2a_workspace_bytes(void);
+
+/* ------------------------------------------------------------------------
+ * Point-to-point puts, optionally with a completion signal, on the copy
+ * engines.
+ *
+ * HOCCL (abstract) drives collective communication with the GPU's DMA
+ * engines so that no compute unit takes part in moving the data, and keeps
+ * that traffic in order with the compute kernels through their streams.
+ * hocf_dma_put is that point-to-point step: for i = 0 .. n-1, in order on
+ * `stream`, it copies bytes[i] bytes from src[i] to dst[i] and then, if
+ * signal and signal[i] are non-NULL, copies the 32-bit word at signal_value
+ * to signal[i].  Each copy starts once the one before it has completed.
+ *
+ * Two ways to consume the bytes:
+ *   - in stream order (HOCCL's operator-level ordering): work enqueued after
+ *     an event recorded on `stream` behind the puts sees them;
+ *   - while they land: a kernel running on another stream (e.g. hocf_ag_gemm
+ *     with signal[i] = &chunk_flags[c] and *signal_value = its epoch) that
+ *     sees signal[i] equal to *signal_value after a system-scope acquire
+ *     sees all of dst[i].
+ *
+ *   engine HOCF_ENGINE_DMA   copies on a copy (SDMA) engine, no compute unit;
+ *                            but the HIP runtime runs any copy below 64 KB,
+ *                            so every signal, as a one-workgroup copy kernel
+ *                            of a few microseconds, which waits for a free
+ *                            CU (a kernel holding every CU delays it, and
+ *                            the puts after it, until it ends)
+ *          HOCF_ENGINE_CU    the same copies as the runtime's copy kernels,
+ *                            which occupy compute units (the comparison)
+ *   src, dst, bytes          host arrays of n entries; src[i], dst[i]
+ *                            16-byte aligned device memory of the current
+ *                            device (may be NULL when bytes[i] == 0)
+ *   signal                   NULL (no put signals), or a host array of n
+ *                            pointers, each NULL (no signal for that put) or
+ *                            a 4-byte aligned device word
+ *   signal_value             device word, 4-byte aligned, holding the value
+ *                            to publish when the stream reaches the puts
+ *                            (ignored when no put signals)
+ *
+ * 0 <= n <= HOCF_MAX_PUTS.  Every dst range and signal word is written and
+ * may overlap no other range of the call (HOCF_ERR_INVALID_ARG), as may a
+ * pointer the runtime does not know as device memory of the current device.
+ * A copy the runtime refuses returns HOCF_ERR_HIP; the puts before it stay
+ * enqueued.  Nothing is allocated; the caller owns every buffer and must
+ * keep src and signal_value unchanged until the stream has passed the puts.
+ * ---------------------------------------------------------------------- */
+#define HOCF_MAX_PUTS 16
+typedef enum hocf_engine { HOCF_ENGINE_DMA = 0, HOCF_ENGINE_CU = 1 } hocf_engine;
+hocf_status hocf_dma_put(int n, const void* const* src, void* const* dst, const int64_t* bytes,
+                         uint32_t* const* signal, const uint32_t* signal_value, hocf_engine engine,
+                         void* stream);
 
 /* ---------------------------------------------------------------------- */
 const char* hocf_status_string(hocf_status s); /* static string, never NULL */

@@ -426,3 +426,47 @@ def test_gemm_rs_decomposed_valid_reaches_device():
     st = hocf.hocf_gemm_rs_decomposed(4, 256, 256, 256, F32, F32, F32, FAKE, addr("W"), _win(4), addr("out"), 64, 64,
                                       4, 16, _sync())
     assert st == HIP
+
+
+def _put(n=2, **kw):
+    src = kw.get("src", [addr(f"psrc{i}") for i in range(n)])
+    dst = kw.get("dst", [addr(f"pdst{i}") for i in range(n)])
+    nbytes = kw.get("nbytes", [4096] * n)
+    signal = kw.get("signal", [addr("psig") + 4 * i for i in range(n)])
+    value = kw.get("value", addr("pval"))
+    return hocf.hocf_dma_put(src, dst, nbytes, signal, value, kw.get("engine", hocf.HOCF_ENGINE_DMA))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n=17),                                                   # more than HOCF_MAX_PUTS
+    dict(engine=2),                                               # no such engine
+    dict(value=None), dict(value=addr("pval") + 2),               # signal value NULL / misaligned
+    dict(nbytes=[4096, -1]),                                      # negative size
+    dict(src=[addr("psrc0"), None]),                              # NULL source of a non-empty put
+    dict(dst=[addr("pdst0"), addr("pdst1") + 8]),                 # misaligned destination
+    dict(signal=[addr("psig"), addr("psig") + 2]),                # misaligned signal word
+    dict(dst=[addr("pdst0"), addr("pdst0") + 4080]),              # two destinations overlap
+    dict(dst=[addr("pdst0"), addr("psrc0")]),                     # a destination overlaps a source
+    dict(signal=[addr("pdst0") + 16, addr("psig")]),              # a signal word inside a destination
+    dict(signal=[addr("psig"), addr("psig")]),                    # two puts signal the same word
+    dict(value=addr("pdst1") + 64),                               # the signal value inside a destination
+])
+def test_dma_put_rejects(kw):
+    assert _put(**kw) == INVALID
+    assert hocf.last_error()
+
+
+def test_dma_put_valid_reaches_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    assert _put(n=0) == hocf.HOCF_OK                              # nothing to do
+    assert _put() == HIP
+    assert _put(engine=hocf.HOCF_ENGINE_CU) == HIP
+    # a put of no bytes only signals: its buffers may be NULL
+    assert _put(n=1, src=[None], dst=[None], nbytes=[0]) == HIP
+    # puts without signals (ordered by the stream alone), or with some signalled
+    assert _put(signal=None, value=None) == HIP
+    assert _put(signal=[None, addr("psig")]) == HIP
+    # adjacent destinations and a signal word right after a destination are fine
+    assert _put(dst=[addr("pdst0"), addr("pdst0") + 4096], signal=[addr("pdst0") + 8192, addr("psig")]) == HIP

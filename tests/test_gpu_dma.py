@@ -1,0 +1,148 @@
+"""Copy-engine puts (hocf_dma_put): point-to-point transfers with a completion
+signal, moved by the DMA (SDMA) engines with no compute unit taking part, as
+HOCCL's abstract describes ("HOCCL: Offloading Collective Communication from
+GPU Cores to Accelerate Distributed Training"), or by the runtime's copy
+kernels for comparison.
+
+* A put copies its bytes exactly (odd sizes included), writes nothing outside
+  its destination, and publishes the signal word.
+* AllGather + GEMM with its chunks delivered by puts while the kernel runs
+  (the puts enqueued first on a second stream, the kernel right after):
+  bit-identical to the same kernel on pre-delivered chunks, and within the
+  bf16 tolerance of the oracle.  The gathered buffer is NaN-poisoned before
+  every call and the chunk contents alternate between calls, so a row read
+  before its put landed (or a stale copy of the previous call's rows) cannot
+  pass.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from computation_collective_amd import buffers as bf
+from computation_collective_amd import configs as cfgs
+from computation_collective_amd import hocf
+from computation_collective_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+BF16 = hocf.HOCF_BF16
+ENGINES = [pytest.param(hocf.HOCF_ENGINE_DMA, id="dma"), pytest.param(hocf.HOCF_ENGINE_CU, id="cu")]
+SPIN_NS = 2_000_000_000   # a chunk that never lands ends the call with HOCF_ERR_TIMEOUT, not a hang
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def relerr(g, o):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    assert not np.isnan(g).any(), "unwritten (NaN) elements"
+    return float(np.max(np.abs(g - o)) / max(np.max(np.abs(o)), 1e-30))
+
+
+@pytest.mark.parametrize("signalled", [True, False], ids=["signalled", "unsignalled"])
+@pytest.mark.parametrize("engine", ENGINES)
+def test_put_copies_bytes_and_signals(engine, signalled):
+    sizes = [1, 16, 4097, 65536 + 48, 3 * (1 << 20) + 5, 8 << 20]
+    say(f"dma_put engine={engine} signalled={signalled} sizes={sizes}")
+    g = torch.Generator().manual_seed(7)
+    srcs = [torch.randint(0, 256, (n,), dtype=torch.uint8, generator=g).cuda() for n in sizes]
+    # destinations packed into one buffer, each at a 16-byte-aligned offset with a
+    # 64-byte guard band after it that must keep its sentinel
+    offs, o = [], 0
+    for n in sizes:
+        offs.append(o)
+        o += (n + 64 + 15) // 16 * 16
+    dst = torch.full((o,), 0xA5, dtype=torch.uint8, device="cuda")
+    flags = torch.zeros(len(sizes) + 2, dtype=torch.int32, device="cuda")
+    epoch = 4242
+    put_stream = torch.cuda.Stream()
+    put_stream.wait_stream(torch.cuda.current_stream())
+    sig = [flags.data_ptr() + 4 * (i + 1) for i in range(len(sizes))] if signalled else None
+    st = hocf.hocf_dma_put(srcs, [dst.data_ptr() + off for off in offs], sizes, sig,
+                           bf.epoch_word(epoch, dst.device) if signalled else None, engine, put_stream)
+    assert st == hocf.HOCF_OK, hocf.last_error()
+    # consumed in stream order: a copy enqueued behind the puts on the default stream
+    done = torch.cuda.Event()
+    done.record(put_stream)
+    torch.cuda.current_stream().wait_event(done)
+    got = dst.clone()
+    torch.cuda.synchronize()
+    want = torch.full((o,), 0xA5, dtype=torch.uint8)
+    for s_, off in zip(srcs, offs):
+        want[off:off + s_.numel()] = s_.cpu()
+    assert torch.equal(got.cpu(), want)
+    f = flags.cpu().numpy()
+    assert f[0] == 0 and f[-1] == 0 and np.all(f[1:-1] == (epoch if signalled else 0))
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("P,Mc,N,K,tm", [(4, 300, 520, 200, 256), (8, 128, 256, 64, 128)])
+def test_ag_gemm_put_delivered_chunks(engine, P, Mc, N, K, tm):
+    """Every chunk comes from its own send buffer by a put; two input sets
+    alternate over four calls, in different orders."""
+    say(f"ag_gemm put-delivered engine={engine} P={P} Mc={Mc} N={N} K={K} tile={tm}")
+    sets = [gen.ag_gemm_inputs(P, Mc, N, K, seed=s) for s in (P + N, P + N + 1)]
+    W = sets[0][1]
+    sends = [[bf.to_device(ch[c]) for c in range(P)] for ch, _, _ in sets]
+    run = bf.AgGemm(P, Mc, N, K, BF16, tm, tm, np.zeros_like(sets[0][0]), W)
+    pre = bf.AgGemm(P, Mc, N, K, BF16, tm, tm, np.zeros_like(sets[0][0]), W)
+    put_stream = torch.cuda.Stream()
+    wants = []
+    for k, (chunks, _, order) in enumerate(sets):
+        pre.A.copy_(bf.to_device(chunks))
+        pre.poison()
+        pre.run_prereleased(order)
+        torch.cuda.synchronize()
+        assert pre.status_value() == 0
+        wants.append(pre.out.clone())
+        _, ref = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
+        assert relerr(gen.bf16_decode(bf.to_host(pre.out, BF16)), gen.bf16_decode(ref)) <= 2e-2
+    for call in range(4):
+        k = call % 2
+        order = sets[k][2] if call < 2 else sets[k][2][::-1]
+        bf.nan_fill(run.A)
+        run.poison()
+        run.put_delivered(sends[k], order, engine, put_stream, spin_timeout_ns=SPIN_NS)
+        torch.cuda.synchronize()
+        assert run.status_value() == 0, hocf.status_string(run.status_value())
+        assert torch.equal(run.out, wants[k]), f"call {call}: output differs from the pre-delivered run"
+        assert torch.all(run.ws == 0)
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_ag_gemm_full_put_delivered(engine):
+    """The bench's AllGather + GEMM workload with the seven remote chunks
+    delivered by puts during the call (the local chunk in place, its put only
+    signals): every element bit-identical to the pre-delivered run, and within
+    tolerance of the oracle."""
+    c = cfgs.AG_GEMM_COL
+    say(f"ag_gemm full {c.name} put-delivered engine={engine}")
+    chunks, W, order = gen.ag_gemm_inputs(c.P, c.Mc, c.N, c.K, seed=0)
+    pre = bf.AgGemm(c.P, c.Mc, c.N, c.K, BF16, c.tile_m, c.tile_n, chunks, W)
+    pre.poison()
+    pre.run_prereleased(order)
+    torch.cuda.synchronize()
+    assert pre.status_value() == 0
+    local = int(order[0])
+    sends = [None if q == local else pre.A[q].clone() for q in range(c.P)]
+    run = bf.AgGemm(c.P, c.Mc, c.N, c.K, BF16, c.tile_m, c.tile_n, chunks, pre.W)
+    keep = run.A[local].clone()
+    bf.nan_fill(run.A)
+    run.A[local].copy_(keep)
+    run.poison()
+    run.put_delivered(sends, order, engine, torch.cuda.Stream(), spin_timeout_ns=SPIN_NS)
+    torch.cuda.synchronize()
+    assert run.status_value() == 0, hocf.status_string(run.status_value())
+    assert torch.equal(run.out, pre.out)
+    _, want = oracle.ag_gemm(c.P, c.Mc, c.N, c.K, BF16, BF16, list(chunks), W)
+    assert relerr(gen.bf16_decode(bf.to_host(run.out, BF16)), gen.bf16_decode(want)) <= 2e-2
