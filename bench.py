@@ -85,7 +85,8 @@ def parse():
     ap.add_argument("--slot-dtype", choices=["f32", "bf16"], default="f32")
     # (each fused operator and its unfused baseline run back to back within a step)
     ap.add_argument("--ops", default="gemm_rs,gemm_rs_unfused,gemv_ar,gemv_ar_unfused,a2a_gemm,a2a_gemm_unfused,"
-                                     "gemm_rs_tiny,ag_gemm,ag_gemm_paced,embbag_a2a,gemm_ar,gemm_a2a,"
+                                     "gemm_rs_tiny,ag_gemm,ag_gemm_paced,ag_gemm_dma,ag_gemm_cu_put,dma_put,cu_put,"
+                                     "gemm_rs_dma_put,gemm_rs_cu_put,embbag_a2a,gemm_ar,gemm_a2a,"
                                      "gemm_rs_decomp2_f32,gemm_rs_decomp4_f32,gemm_rs_decomp8_f32,"
                                      "hipblaslt_bmm")
     ap.add_argument("--gemv-tile", type=int, default=0, help="GEMV column tile (default: the config's)")

@@ -26,6 +26,12 @@ GRBM_GUI_ACTIVE` -- and writes one summary per operator,
     dispatches of 100 us or more, the clock it ran at (XCD cycles / the
     dispatch's counter window).
 
+  python -m computation_collective_amd.profsum copies TRACE_DIR OUT_FILE "COMMAND" "TITLE"
+
+summarises a `rocprofv3 --kernel-trace --memory-copy-trace --stats` run of
+bench.py's put operators: the kernels that ran (the runtime's copy kernels
+among them) and the copies the copy engines ran.
+
 `traffic(op, variant)` returns the scaled bytes, or None when there is no
 summary, it was taken for another variant, or the sources have changed.
 """
@@ -234,7 +240,32 @@ def traffic(op: str, variant: str | None = None):
     return float(kv["l2_fabric_bytes"]) if "l2_fabric_bytes" in kv else None
 
 
+def summarize_copies(trace_dir, out_file, command, title) -> None:
+    """Summary of a `rocprofv3 --kernel-trace --memory-copy-trace --stats` run
+    of bench.py's put operators: every kernel with its call count and average
+    duration (the runtime's copy kernels among them), and every kind of memory
+    copy the copy engines ran.  Host-to-device copies are the upload of the
+    inputs before the timed steps."""
+    lines = [f"# rocprofv3 summary: {title}", f"# command: {command}",
+             f"sources {source_hash()}", "kernels (name, calls, avg_us, total_us)"]
+    for r in csv.DictReader(open(_find_csv(trace_dir, "kernel_stats.csv"))):
+        name = r["Name"]
+        short = name if len(name) <= 90 else name[:87] + "..."
+        lines.append(f"  {short} calls={r['Calls']} avg_us={float(r['AverageNs']) / 1e3:.2f} "
+                     f"total_us={float(r['TotalDurationNs']) / 1e3:.1f}")
+    lines.append("copy-engine copies (direction, calls, avg_us, min_us, max_us, total_us)")
+    for r in csv.DictReader(open(_find_csv(trace_dir, "memory_copy_stats.csv"))):
+        lines.append(f"  {r['Name']} calls={r['Calls']} avg_us={float(r['AverageNs']) / 1e3:.2f} "
+                     f"min_us={float(r['MinNs']) / 1e3:.2f} max_us={float(r['MaxNs']) / 1e3:.2f} "
+                     f"total_us={float(r['TotalDurationNs']) / 1e3:.1f}")
+    with open(out_file, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
-    if len(sys.argv) not in (7, 9):
+    if len(sys.argv) == 6 and sys.argv[1] == "copies":
+        summarize_copies(*sys.argv[2:])
+    elif len(sys.argv) in (7, 9):
+        summarize(*sys.argv[1:])
+    else:
         raise SystemExit(__doc__)
-    summarize(*sys.argv[1:])
