@@ -146,3 +146,36 @@ def test_ag_gemm_full_put_delivered(engine):
     assert torch.equal(run.out, pre.out)
     _, want = oracle.ag_gemm(c.P, c.Mc, c.N, c.K, BF16, BF16, list(chunks), W)
     assert relerr(gen.bf16_decode(bf.to_host(run.out, BF16)), gen.bf16_decode(want)) <= 2e-2
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_puts_beside_a_kernel_holding_every_cu(engine):
+    """Unsignalled puts on one stream while the GEMM + ReduceScatter kernel
+    (a persistent grid of every CU) runs on another: the puts land exactly,
+    and the kernel's output is bit-identical to the same call run alone."""
+    c = cfgs.GEMM_RS_MLP
+    say(f"gemm_rs {c.name} with 7 x 8 MB of puts beside it, engine={engine}")
+    A, W = gen.gemm_rs_inputs(c.P, c.M, c.N, c.K, c.in_dt, seed=3)
+    run = bf.GemmRS(c.P, c.M, c.N, c.K, c.in_dt, c.slot_dt, c.out_dt, c.tile_m, c.tile_n, A, W)
+    run.poison()
+    run.run()
+    torch.cuda.synchronize()
+    assert run.status_value() == 0
+    alone = run.out.clone()
+    nb = 8 << 20
+    g = torch.Generator().manual_seed(11)
+    srcs = [torch.randint(-2**31, 2**31 - 1, (nb // 4,), dtype=torch.int32, generator=g).cuda() for _ in range(7)]
+    dsts = [torch.full((nb // 4,), -1, dtype=torch.int32, device="cuda") for _ in range(7)]
+    run.poison()
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    main.wait_stream(torch.cuda.current_stream())
+    side.wait_stream(main)
+    st = hocf.hocf_dma_put(srcs, dsts, [nb] * 7, None, None, engine, side)   # first, so they do not wait
+    assert st == hocf.HOCF_OK, hocf.last_error()
+    run.run(main)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    assert run.status_value() == 0
+    assert torch.equal(run.out, alone)
+    for s_, d_ in zip(srcs, dsts):
+        assert torch.equal(s_, d_)
