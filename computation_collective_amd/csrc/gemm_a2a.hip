@@ -96,9 +96,9 @@ __device__ __forceinline__ void scatter_rows(const GemmA2aArgs& a, int col0,
   }
 }
 
-// One tile (or the half-height tile `half` = 0/1 of it, with the Half
-// tile shape) of the grouped GEMM, scattered; returns after the barrier that
-// follows its stores.
+// One tile of the grouped GEMM (whole, or one of its half- or
+// quarter-height parts, with the tile shape T), scattered; returns after the
+// barrier that follows its stores.
 template <class T, int ODT>
 __device__ __forceinline__ void a2a_tile(const GemmA2aArgs& a, int64_t row0, int e, int nt,
                                          char* const (&stages)[4], int2* s_route, const uint64_t* s_win,
@@ -143,16 +143,21 @@ __global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
   constexpr int kColBlock = 8;
   //
   // Tiles [keep, total) -- the last, partial round of whole tiles -- run as
-  // two half-height tiles each, so that round takes half as long (the same
-  // rows, each computed once; only 256-row tiles with bf16 output split).
-  using Half = TileBf16Direct<Tile::TM / 2, Tile::TN, 2, 2>;
-  constexpr bool kHalves = ODT == kBF16 && Tile::TM == 256;
-  static_assert(!kHalves || (Half::SMEM_BYTES <= Tile::SMEM_BYTES && Half::NT == Tile::NT), "half tile");
-  const int nwork = kHalves ? a.keep + 2 * (a.total - a.keep) : a.total;
+  // `split` (2 or 4) tiles of 256 / split rows each, so that round takes a
+  // half or a quarter as long (the same rows, each computed once; only
+  // 256-row tiles with bf16 output split).
+  constexpr bool kSplits = ODT == kBF16 && Tile::TM == 256;
+  using Half = TileBf16Direct<kSplits ? Tile::TM / 2 : Tile::TM, Tile::TN, 2, 2>;
+  using Quarter = TileBf16Direct<kSplits ? Tile::TM / 4 : Tile::TM, Tile::TN, 2, 2>;
+  static_assert(!kSplits || (Half::SMEM_BYTES <= Tile::SMEM_BYTES && Half::NT == Tile::NT &&
+                             Quarter::SMEM_BYTES <= Tile::SMEM_BYTES && Quarter::NT == Tile::NT),
+                "part tiles");
+  const int split = kSplits ? a.split : 1;
+  const int nwork = a.keep + split * (a.total - a.keep);
   const int first = (int)xcd_contiguous(blockIdx.x, gridDim.x);
   for (int w = first; w < nwork; w += gridDim.x) {
-    const bool split = kHalves && w >= a.keep;
-    const int item = split ? a.keep + (w - a.keep) / 2 : w;
+    const bool part = w >= a.keep;
+    const int item = part ? a.keep + (w - a.keep) / split : w;
     int e = 0;
     while (e + 1 < a.E && item >= a.tile_off[e + 1]) ++e;
     const int local = item - a.tile_off[e];
@@ -162,8 +167,11 @@ __global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
     const int j = local - nb * mtiles * kColBlock;
     const int mt = j / width, nt = nb * kColBlock + j % width;
     const int64_t row0 = a.row_off[e] + (int64_t)mt * Tile::TM;
-    if constexpr (kHalves) {
-      if (split)
+    if constexpr (kSplits) {
+      if (part && split == 4)
+        a2a_tile<Quarter, ODT>(a, row0 + (int64_t)((w - a.keep) % 4) * Quarter::TM, e, nt, stages, s_route, s_win,
+                               s_cnt);
+      else if (part)
         a2a_tile<Half, ODT>(a, row0 + (int64_t)((w - a.keep) % 2) * Half::TM, e, nt, stages, s_route, s_win, s_cnt);
       else
         a2a_tile<Tile, ODT>(a, row0, e, nt, stages, s_route, s_win, s_cnt);
@@ -198,17 +206,18 @@ __global__ __launch_bounds__(Tile::NT) void gemm_a2a_kernel(GemmA2aArgs a) {
 template <class Tile, int ODT>
 static int launch_k(const GemmA2aArgs& a0, hipStream_t s) {
   auto kern = &gemm_a2a_kernel<Tile, ODT>;
-  constexpr bool kHalves = ODT == kBF16 && Tile::TM == 256;  // (as in the kernel)
+  constexpr bool kSplits = ODT == kBF16 && Tile::TM == 256;  // (as in the kernel)
   int grid = 0;
   hipError_t e = persistent_grid(reinterpret_cast<const void*>(kern), Tile::NT,
-                                 kHalves ? 2 * (int64_t)a0.total : a0.total, &grid);
+                                 kSplits ? 4 * (int64_t)a0.total : a0.total, &grid);
   if (e != hipSuccess) return e;
-  // split the last, partial round of whole tiles into half-height tiles when
-  // the halves still fit in one round of the grid (the kernel splits only
-  // 256-row tiles with bf16 output; elsewhere keep is ignored)
+  // split the last, partial round of whole tiles into quarter- or
+  // half-height tiles, the finest whose parts still fit in one round of the
+  // grid (the kernel splits only 256-row tiles with bf16 output)
   GemmA2aArgs a = a0;
   const int rem = a.total % grid;
-  a.keep = (rem != 0 && 2 * rem <= grid) ? a.total - rem : a.total;
+  a.split = !kSplits || rem == 0 ? 1 : 4 * rem <= grid ? 4 : 2 * rem <= grid ? 2 : 1;
+  a.keep = a.split > 1 ? a.total - rem : a.total;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(Tile::NT), 0, s, a);
   return hipGetLastError();
 }

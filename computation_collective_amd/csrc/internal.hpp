@@ -92,7 +92,8 @@ struct GemmA2aArgs {
   int64_t T, cap;
   int P, E, N, K, ntiles, out_dt;
   int total;  // tiles: row tiles x column tiles over all experts
-  int keep;   // tiles [0, keep) run whole; each later tile runs as two half-height tiles
+  int keep;   // tiles [0, keep) run whole; each later tile runs as `split` tiles of
+  int split;  // tile_m / split rows (split = 1, 2 or 4; keep == total when 1)
   SyncArgs sync;
 };
 

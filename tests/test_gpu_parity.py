@@ -870,18 +870,20 @@ def test_gemm_a2a_most_experts_and_destinations():
     assert torch.all(run.win_flags[:, 0] == run.epoch)
 
 
-@pytest.mark.parametrize("grid", [8, 16, 32])
-def test_gemm_a2a_last_round_in_half_tiles_bit_exact(grid, monkeypatch):
-    """A grid that leaves a partial last round: those tiles run as two
-    half-height tiles each (every row still computed once); integer
+@pytest.mark.parametrize("grid,parts", [(8, 2), (16, 4), (32, 2)])
+def test_gemm_a2a_last_round_in_part_tiles_bit_exact(grid, parts, monkeypatch):
+    """A grid that leaves a partial last round: those tiles run as quarter-
+    height tiles when four times their number fits one round of the grid,
+    else as half-height tiles (every row still computed once); integer
     operands, bit-exact, every flag set."""
     monkeypatch.setenv("HOCF_MAX_WORKGROUPS", str(grid))
     P, E, B, topk, N, K = 8, 3, 400, 2, 1024, 256
     off, dest, slot, counts, X, W = _moe_case(P, E, B, topk, N, K, seed=70 + grid, dist_x=("int", -2, 2),
                                               dist_w=("int", -2, 2))
     tiles = int(off[-1]) // 256 * (N // 256)
-    say(f"gemm_a2a half tiles: {tiles} tiles on a grid of {grid} (remainder {tiles % grid})")
-    assert 0 < tiles % grid <= grid // 2          # the case where the last round splits
+    rem = tiles % grid
+    say(f"gemm_a2a part tiles: {tiles} tiles on a grid of {grid} (remainder {rem}, {parts} parts)")
+    assert 0 < rem and (4 * rem <= grid if parts == 4 else grid < 4 * rem <= 2 * grid)
     cap = int(counts.max())
     run = bf.GemmA2A(P, E, N, K, BF16, X, W, off, dest, slot, counts, cap)
     run.poison()
