@@ -22,17 +22,21 @@
 //      its first slot among its source's pairs (the per-source column
 //      restarts at every source) -- then the padded group offsets, the
 //      expert tiles, the send counts, and zeroed arrival counters;
-//   3. the fused kernel (persistent): work items in claim order are the
-//      padding fills (each group's padding in a few pieces), then for each
-//      source its chunks followed by the expert tiles whose row tile gets
-//      its last row from that source.  A chunk item ranks the chunk's pairs
-//      per expert with wave ballots, copies their token rows into the
-//      receive buffer with device-coherent stores, writes dest and slot,
-//      then counts the rows landed per row tile.  A tile waits (bounded)
-//      until its row tile has all its rows, then runs the direct-to-LDS
-//      MFMA mainloop of the other GEMMs and stores Y.  Every tile waits only
-//      on items claimed before it by running workgroups, so the kernel needs
-//      no co-residency to finish.
+//   3. the fused kernel (persistent): a workgroup first claims delivery
+//      items from one counter -- the padding fills (each group's padding in
+//      a few pieces), then the chunks -- and, once that counter is
+//      exhausted, expert tiles from eight queues, one per XCD, each a
+//      contiguous run of the tile list (expert, row tile, column tile), so
+//      an XCD's tiles share row tiles and W panels in its L2.  A chunk item
+//      ranks the chunk's pairs per expert with wave ballots, copies their
+//      token rows into the receive buffer with device-coherent stores,
+//      writes dest and slot, then counts the rows landed per row tile.  A
+//      tile waits (bounded) until its row tile has all its rows, then runs
+//      the direct-to-LDS MFMA mainloop of the other GEMMs and stores Y; so
+//      the tiles whose rows land first start while other workgroups still
+//      deliver.  A tile is claimed only after every delivery item has been
+//      claimed by a running workgroup (which waits on nothing), so the
+//      kernel needs no co-residency to finish.
 // The unfused baseline runs the scatter items as one kernel and the tiles as
 // the next (bit-identical results).
 #include "internal.hpp"
@@ -71,9 +75,6 @@ __global__ __launch_bounds__(kA2gChunk) void a2g_count_kernel(A2aGemmArgs a) {
 __global__ __launch_bounds__(256) void a2g_scan_kernel(A2aGemmArgs a) {
   __shared__ uint32_t tot[kMaxExperts + 1];
   __shared__ uint32_t src0[kMaxP + 1];
-  __shared__ uint32_t sb[(kMaxP + 1) * kMaxExperts];  // expert e's rows from sources before p
-  __shared__ uint32_t ssn[kMaxP * kMaxExperts];       // items of stage p for expert e's tiles
-  __shared__ uint32_t sitems[kMaxP];                  // items of stage p
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, C = a.C, W1 = E + 1;
   // every column: base[c][i] = sum over chunks c' < c of hist[c'][i]; one
@@ -103,8 +104,6 @@ __global__ __launch_bounds__(256) void a2g_scan_kernel(A2aGemmArgs a) {
   // send count
   if (tid < a.P) src0[tid] = a.base[(int64_t)tid * a.cps * W1 + E];
   if (tid == 0) src0[a.P] = tot[E];
-  for (int i = tid; i < (a.P + 1) * E; i += 256)
-    sb[i] = i < a.P * E ? a.base[(int64_t)(i / E) * a.cps * W1 + i % E] : tot[i % E];
   __syncthreads();
   for (int c = tid; c < C; c += 256) a.base[(int64_t)c * W1 + E] -= src0[c / a.cps];
   if (tid < a.P) a.send_counts[tid] = (int64_t)(src0[tid + 1] - src0[tid]);
@@ -131,38 +130,6 @@ __global__ __launch_bounds__(256) void a2g_scan_kernel(A2aGemmArgs a) {
     if (over) report_status(a.sync, kErrCapacity);
   }
   for (int i = tid; i < a.nrt; i += 256) a.arrivals[i] = 0;
-  // The fused kernel's schedule: after the padding pieces, stage p = the
-  // chunks of source p, then every tile whose row tile gets its last row from
-  // source p.  Rows of a group are in source order, so a row tile's last row
-  // names the last source it waits for, and the row tiles of expert e whose
-  // last row lies in source p's rows [lo, hi) are the run [F(lo), F(hi)),
-  // F(x) = the row tiles whose last row is below x = (x >= n ? all : x / tile_m).
-  const int P = a.P;
-  for (int i = tid; i < P * E; i += 256) {
-    const int e = i % E;
-    const uint32_t n = tot[e], tm = (uint32_t)a.tile_m, mtiles = (n + tm - 1) / tm;
-    const uint32_t lo = sb[i] >= n ? mtiles : sb[i] / tm;
-    const uint32_t hi = sb[i + E] >= n ? mtiles : sb[i + E] / tm;
-    a.slo[i] = lo;
-    a.sn[i] = hi - lo;
-    ssn[i] = (hi - lo) * (uint32_t)a.ntiles;
-  }
-  __syncthreads();
-  if (tid < P) {
-    uint32_t c = (uint32_t)a.cps;
-    for (int e = 0; e < E; ++e) c += ssn[tid * E + e];
-    sitems[tid] = c;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t at = 0;
-    for (int st = 0; st < P; ++st) {
-      a.stage_item[st] = at;
-      at += sitems[st];
-    }
-    a.stage_item[P] = at;
-    a.misc[3] = (uint32_t)(E * kA2gPadPieces) + at;  // the fused kernel's items
-  }
 }
 
 // Copies (or, with src == nullptr, zeroes) one row of K bf16 elements into
@@ -337,16 +304,16 @@ __global__ __launch_bounds__(Tile::NT) void a2a_gemm_kernel(A2aGemmArgs a) {
   const int E = a.E;
   const int64_t npad = (int64_t)E * kA2gPadPieces;
   const int64_t nscatter = SCATTER ? npad + a.C : 0;
-  // Fused: one counter deals the staged schedule (the padding pieces, then
-  // per source its chunks and the tiles that wait only on it and earlier
-  // sources), so tiles start while later sources' rows are still moving;
-  // every tile waits only on items dealt before it.  Unfused: the scatter
-  // kernel deals its items in order; the GEMM kernel deals tiles from eight
-  // queues, one per XCD (home queue blockIdx mod 8, then the others), each a
-  // contiguous run of the tile list (expert, row tile, column tile), so an
-  // XCD's tiles share row tiles and W panels in its L2.
-  const int64_t nsched = FUSED ? (int64_t)a.misc[3] : nscatter;
-  const uint32_t ntile = (GEMM && !FUSED) ? a.misc[2] : 0u;
+  // Delivery items (the padding pieces, then the chunks) are dealt in order
+  // by one counter; tiles by eight queues, one per XCD (home queue blockIdx
+  // mod 8, then the others), each a contiguous run of the tile list
+  // (expert, row tile, column tile), so an XCD's tiles share row tiles and
+  // W panels in its L2.  Fused, a workgroup turns to the tile queues once
+  // the delivery counter is exhausted: every tile then waits only on items
+  // already claimed.  Item numbers: delivery items [0, nscatter), tile t is
+  // nscatter + t.
+  const uint32_t ntile = GEMM ? a.misc[2] : 0u;
+  bool delivering = SCATTER;  // (thread 0) the delivery counter may have items left
   uint32_t* tq = &a.misc[4];
   auto qbeg = [&](int q) { return (uint32_t)(((uint64_t)ntile * q) / kNumQueues); };
   int qoff = 0;
@@ -361,15 +328,17 @@ __global__ __launch_bounds__(Tile::NT) void a2a_gemm_kernel(A2aGemmArgs a) {
     __syncthreads();  // the previous item's LDS use is over
     if (tid == 0) {
       int64_t it = -1;
-      if (SCATTER) {
+      if (delivering) {
         const uint32_t v = __hip_atomic_fetch_add(&a.misc[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((int64_t)v < nsched) it = v;
-      } else {
+        if ((int64_t)v < nscatter) it = v;
+        else delivering = false;
+      }
+      if (it < 0 && GEMM) {
         const int home = (int)(blockIdx.x % kNumQueues);
         while (qoff < kNumQueues) {
           const int q = (home + qoff) % kNumQueues;
           const uint32_t v = __hip_atomic_fetch_add(&tq[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (v < qbeg(q + 1) - qbeg(q)) { it = qbeg(q) + v; break; }
+          if (v < qbeg(q + 1) - qbeg(q)) { it = nscatter + qbeg(q) + v; break; }
           ++qoff;
         }
       }
@@ -382,35 +351,16 @@ __global__ __launch_bounds__(Tile::NT) void a2a_gemm_kernel(A2aGemmArgs a) {
       a2g_pad<Tile::NT>(a, (int)(item / kA2gPadPieces), (int)(item % kA2gPadPieces));
       continue;
     }
-    int e = 0, mt = 0, nt = 0;
-    if constexpr (FUSED) {
-      // stage st holds schedule positions [stage_item[st], stage_item[st+1]) after the padding
-      const uint32_t o = (uint32_t)(item - npad);
-      int st = 0;
-      while (st + 1 < a.P && o >= a.stage_item[st + 1]) ++st;
-      const uint32_t off = o - a.stage_item[st];
-      if (off < (uint32_t)a.cps) {
-        a2g_chunk<Tile::NT>(a, st * a.cps + (int)off, smem0);
-        continue;
-      }
-      uint32_t t = off - (uint32_t)a.cps;
-      while (e + 1 < E && t >= a.sn[st * E + e] * (uint32_t)a.ntiles) {
-        t -= a.sn[st * E + e] * (uint32_t)a.ntiles;
-        ++e;
-      }
-      mt = (int)(a.slo[st * E + e] + t / (uint32_t)a.ntiles);
-      nt = (int)(t % (uint32_t)a.ntiles);
-    } else if constexpr (SCATTER) {
+    if (SCATTER && item < nscatter) {
       a2g_chunk<Tile::NT>(a, (int)(item - npad), smem0);
       continue;
-    } else {
-      // an expert tile of the list: (expert e, row tile mt, column tile nt)
-      const uint32_t t = (uint32_t)item;
-      while (e + 1 < E && t >= a.toff[e + 1]) ++e;
-      const uint32_t local = t - a.toff[e];
-      mt = (int)(local / (uint32_t)a.ntiles);
-      nt = (int)(local % (uint32_t)a.ntiles);
     }
+    // an expert tile of the list: (expert e, row tile mt, column tile nt)
+    const uint32_t t = (uint32_t)(item - nscatter);
+    int e = 0;
+    while (e + 1 < E && t >= a.toff[e + 1]) ++e;
+    const uint32_t local = t - a.toff[e];
+    const int mt = (int)(local / (uint32_t)a.ntiles), nt = (int)(local % (uint32_t)a.ntiles);
     const uint32_t row0 = a.grp[e] + (uint32_t)mt * Tile::TM;
     if constexpr (FUSED) {
       // the row tile's rows (copied or zero-filled by items claimed earlier)

@@ -493,9 +493,9 @@ size_t hocf_a2a_gemm_workspace_bytes(int P, int E, int B, int topk, int64_t cap,
   if (P <= 0 || E <= 0 || B < 0 || topk < 0 || cap < 0 || tile_m <= 0) return 0;
   const int64_t C = (int64_t)P * a2g_chunks_per_source(B, topk);
   // misc [4 + 8 tile queues], hist and base [C][E+1] each, group rows [E+1], pairs [E], tiles [E+1],
-  // stages [P+1] and [P][E] twice, arrivals [cap / tile_m]
-  return (size_t)(hocf::kWsBaseWords + 4 + hocf::kNumQueues + 2 * C * (E + 1) + 3 * (int64_t)E + 2 + (P + 1) +
-                  2 * (int64_t)P * E + cap / tile_m) * 4;
+  // arrivals [cap / tile_m]
+  return (size_t)(hocf::kWsBaseWords + 4 + hocf::kNumQueues + 2 * C * (E + 1) + 3 * (int64_t)E + 2 +
+                  cap / tile_m) * 4;
 }
 
 static hocf_status a2a_gemm_call(const char* op, bool fused, int P, int E, int e0, int B, int topk, int N, int K,
@@ -577,10 +577,7 @@ static hocf_status a2a_gemm_call(const char* op, bool fused, int P, int E, int e
   a.grp = a.base + (int64_t)a.C * (E + 1);
   a.cnt = a.grp + (E + 1);
   a.toff = a.cnt + E;
-  a.stage_item = a.toff + (E + 1);
-  a.slo = a.stage_item + (P + 1);
-  a.sn = a.slo + P * E;
-  a.arrivals = a.sn + P * E;
+  a.arrivals = a.toff + (E + 1);
   a.cap = cap;
   a.P = P; a.E = E; a.e0 = e0; a.B = B; a.topk = topk; a.N = N; a.K = K; a.out_dt = out_dt;
   a.tile_m = tile_m;

@@ -111,18 +111,13 @@ struct A2aGemmArgs {
   int32_t* dest;            // [cap]
   int32_t* slot;            // [cap]
   int64_t* send_counts;     // [P]
-  // workspace (uint32): misc words [0] scatter / schedule claim counter, [1]
-  // nonzero when the rows exceed cap, [2] expert tiles, [3] the fused
-  // kernel's schedule length, [4..12) the tile queues' claim counters (one
-  // per XCD); per chunk a histogram and its exclusive scan ([C][E+1]: local
-  // experts, then pairs landing here from the chunk); per expert the group's
-  // first row [E+1], its pairs [E], its first tile [E+1]; per row tile the
-  // rows that have landed [nrt]
+  // workspace (uint32): misc words [0] delivery claim counter, [1] nonzero
+  // when the rows exceed cap, [2] expert tiles, [3] spare, [4..12) the tile
+  // queues' claim counters (one per XCD); per chunk a histogram and its
+  // exclusive scan ([C][E+1]: local experts, then pairs landing here from
+  // the chunk); per expert the group's first row [E+1], its pairs [E], its
+  // first tile [E+1]; per row tile the rows that have landed [nrt]
   uint32_t *misc, *hist, *base, *grp, *cnt, *toff, *arrivals;
-  // the fused kernel's staged schedule: stage s (source s's chunks, then the
-  // tiles whose last row comes from source s) starts at stage_item[s] [P+1];
-  // expert e's row tiles of stage s are [slo[s][e], slo[s][e] + sn[s][e])
-  uint32_t *stage_item, *slo, *sn;
   int64_t cap;
   int P, E, e0, B, topk, N, K, out_dt, tile_m, ntiles, C, cps, nrt;
   int64_t max_tiles;  // tiles the grid is sized for: (cap / tile_m) * ntiles

@@ -407,7 +407,7 @@ def test_a2a_gemm_valid_reaches_device():
     assert _a2g() == HIP and _a2g(unfused=True) == HIP
     C = 8 * 32
     assert hocf.hocf_a2a_gemm_workspace_bytes(8, 4, 4096, 2, 12288, 256) == \
-        (8 + 1 + 4 + 8 + 2 * C * 5 + 3 * 4 + 2 + 9 + 2 * 8 * 4 + 12288 // 256) * 4
+        (8 + 1 + 4 + 8 + 2 * C * 5 + 3 * 4 + 2 + 12288 // 256) * 4
 
 
 @pytest.mark.parametrize("pieces,fold_cus,N,expect", [(0, 0, 256, INVALID), (17, 0, 256, INVALID),
