@@ -197,7 +197,7 @@ extern "C" {
 int hocf_abi_version(void) { return HOCF_ABI_VERSION; }
 
 const char* hocf_status_string(hocf_status s) {
-  switch (s) {
+  switch (s) {  // (any int: e.g. a status word read back from the device)
     case HOCF_OK: return "ok";
     case HOCF_ERR_INVALID_ARG: return "invalid argument";
     case HOCF_ERR_UNSUPPORTED: return "unsupported combination";

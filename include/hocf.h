@@ -107,7 +107,17 @@ extern "C" {
 #define HOCF_ABI_VERSION 1
 #define HOCF_MAX_P 16 /* largest shard count any operator accepts */
 
-typedef enum hocf_status {
+/* In C++ the enums below take int as their fixed underlying type, so that
+ * every int a C caller passes is a value of the type (the library checks
+ * it; an enum without a fixed type would leave out-of-range values
+ * undefined in C++).  The ABI is int either way. */
+#ifdef __cplusplus
+#define HOCF_ENUM_INT : int
+#else
+#define HOCF_ENUM_INT
+#endif
+
+typedef enum hocf_status HOCF_ENUM_INT {
     HOCF_OK = 0,
     HOCF_ERR_INVALID_ARG = 1, /* bad shape, pointer, alignment, epoch or workspace */
     HOCF_ERR_UNSUPPORTED = 2, /* valid, but no kernel for this combination */
@@ -119,7 +129,7 @@ typedef enum hocf_status {
     HOCF_ERR_CAPACITY = 8     /* (async) more rows routed here than the receive buffer holds */
 } hocf_status;
 
-typedef enum hocf_dtype { HOCF_F32 = 0, HOCF_BF16 = 1 } hocf_dtype;
+typedef enum hocf_dtype HOCF_ENUM_INT { HOCF_F32 = 0, HOCF_BF16 = 1 } hocf_dtype;
 
 /* One destination's receive window: its data buffer and its flag words. */
 typedef struct hocf_window {
@@ -504,7 +514,7 @@ size_t hocf_embbag_a2a_workspace_bytes(void);
  * keep src and signal_value unchanged until the stream has passed the puts.
  * ---------------------------------------------------------------------- */
 #define HOCF_MAX_PUTS 16
-typedef enum hocf_engine { HOCF_ENGINE_DMA = 0, HOCF_ENGINE_CU = 1 } hocf_engine;
+typedef enum hocf_engine HOCF_ENUM_INT { HOCF_ENGINE_DMA = 0, HOCF_ENGINE_CU = 1 } hocf_engine;
 hocf_status hocf_dma_put(int n, const void* const* src, void* const* dst, const int64_t* bytes,
                          uint32_t* const* signal, const uint32_t* signal_value, hocf_engine engine,
                          void* stream);
