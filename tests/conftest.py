@@ -29,10 +29,10 @@ _ensure_built()
 
 
 def pytest_runtest_logreport(report):
-    """On a GPU machine, write each failure's details to gpurun_out/ as it happens,
-    so they survive a run that is cut short."""
-    if report.failed and os.environ.get("GRAFT_REPO_ROOT"):
-        out = os.path.join(ROOT, "gpurun_out")
-        os.makedirs(out, exist_ok=True)
-        with open(os.path.join(out, "failures.log"), "a") as f:
+    """If HOCF_FAILURE_LOG names a file, append each failure's details to it as
+    it happens, so they survive a run that is cut short."""
+    path = os.environ.get("HOCF_FAILURE_LOG")
+    if report.failed and path:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "a") as f:
             f.write(f"==== {report.nodeid} ({report.when})\n{report.longreprtext}\n")

@@ -93,7 +93,7 @@ def test_gemm_rs_unfused_rejects(kw, expect):
 
 def test_gemm_rs_valid_reaches_device():
     """A valid call gets past validation; here no GPU is present, so it stops at
-    the device query (HOCF_ERR_HIP) -- on a GPU machine the same call launches."""
+    the device query (HOCF_ERR_HIP) -- on a host with a GPU the same call launches."""
     import torch
     if torch.cuda.is_available():
         pytest.skip("GPU present")
