@@ -285,6 +285,16 @@ def main():
     put_ops = [o for o in ("ag_gemm_dma", "ag_gemm_cu_put", "dma_put", "cu_put", "gemm_rs_dma_put",
                            "gemm_rs_cu_put") if o in ops]
     if put_ops:
+        # one small put on each engine first: a runtime without copy-engine support drops
+        # these operators (logged) rather than the whole bench line
+        probe = torch.zeros(2, 1 << 16, dtype=torch.int32, device=dev)
+        for eng in (hocf.HOCF_ENGINE_DMA, hocf.HOCF_ENGINE_CU):
+            st = hocf.hocf_dma_put([probe[0]], [probe[1]], [1 << 18], None, None, eng, torch.cuda.current_stream())
+            if st != hocf.HOCF_OK:
+                log(f"copy-engine puts skipped: engine {eng}: {hocf.last_error()}")
+                put_ops = []
+        torch.cuda.synchronize()
+    if put_ops:
         c = cfgs.AG_GEMM_COL
         log(f"inputs {c.name} (copy-engine puts: {', '.join(put_ops)})")
         put_stream = torch.cuda.Stream(device=dev)
@@ -295,7 +305,7 @@ def main():
         put_bytes = chunk_bytes * len(remote)
         engines = {"dma": hocf.HOCF_ENGINE_DMA, "cu": hocf.HOCF_ENGINE_CU}
         for name, eng in (("ag_gemm_dma", "dma"), ("ag_gemm_cu_put", "cu")):
-            if name not in ops:
+            if name not in put_ops:
                 continue
             ad = bf.AgGemm(c.P, c.Mc, c.N, c.K, bf.BF16, c.tile_m, c.tile_n, chunks, W)
             sends = [None if q == local else ad.A[q].clone() for q in range(c.P)]
@@ -322,7 +332,7 @@ def main():
                                          None, None, engine, put_stream))
 
         for name, eng in (("dma_put", "dma"), ("cu_put", "cu")):
-            if name not in ops:
+            if name not in put_ops:
                 continue
 
             def put_call(engine=engines[eng]):
@@ -333,7 +343,7 @@ def main():
                               peak=PEAK_HBM_GBS, bytes=2 * put_bytes, put_bytes=put_bytes,
                               config=dict(workload=f"put_7x8MB_{eng}", engine=eng, puts=len(remote),
                                           put_bytes=put_bytes))
-        gr = [o for o in ("gemm_rs_dma_put", "gemm_rs_cu_put") if o in ops]
+        gr = [o for o in ("gemm_rs_dma_put", "gemm_rs_cu_put") if o in put_ops]
         if gr:
             cg = cfgs.GEMM_RS_MLP
             if "gemm_rs" in runs:
