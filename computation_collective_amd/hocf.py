@@ -262,6 +262,7 @@ def hocf_ag_gemm(P, Mc, N, K, in_dt, out_dt, A_gathered, chunk_flags, W, out, ti
 
 
 HOCF_ENGINE_DMA, HOCF_ENGINE_CU = 0, 1
+HOCF_MAX_PUTS = 16
 
 
 def hocf_dma_put(src, dst, nbytes, signal, signal_value, engine, stream=None) -> int:

@@ -179,3 +179,31 @@ def test_puts_beside_a_kernel_holding_every_cu(engine):
     assert torch.equal(run.out, alone)
     for s_, d_ in zip(srcs, dsts):
         assert torch.equal(s_, d_)
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_sixteen_puts_mixed(engine):
+    """HOCF_MAX_PUTS puts in one call on the null stream: empty puts that only
+    signal, puts below and above the runtime's 64 KB copy-engine threshold,
+    and puts without a signal."""
+    n = hocf.HOCF_MAX_PUTS
+    sizes = [0, 4, 4096, 65536, 65552, 1 << 20, 0, 48, 131072 + 16, 16, 3 << 16, 256, 0, 1 << 18, 12, 65536 - 16][:n]
+    say(f"dma_put engine={engine} {n} puts, sizes {sizes}")
+    g = torch.Generator().manual_seed(21)
+    srcs = [torch.randint(0, 256, (max(b, 16),), dtype=torch.uint8, generator=g).cuda() for b in sizes]
+    dsts = [torch.full((max(b, 16) + 64,), 0x5A, dtype=torch.uint8, device="cuda") for b in sizes]
+    flags = torch.zeros(n, dtype=torch.int32, device="cuda")
+    signalled = [i % 5 != 3 for i in range(n)]              # a few puts without a signal
+    sig = [flags.data_ptr() + 4 * i if signalled[i] else None for i in range(n)]
+    torch.cuda.synchronize()
+    st = hocf.hocf_dma_put([s if b else None for s, b in zip(srcs, sizes)],
+                           [d if b else None for d, b in zip(dsts, sizes)], sizes, sig,
+                           bf.epoch_word(99, flags.device), engine, None)
+    assert st == hocf.HOCF_OK, hocf.last_error()
+    torch.cuda.synchronize()
+    f = flags.cpu().numpy()
+    for i, b in enumerate(sizes):
+        d = dsts[i].cpu()
+        assert torch.equal(d[:b], srcs[i].cpu()[:b]), f"put {i}"
+        assert torch.all(d[b:] == 0x5A), f"put {i} wrote past its end"
+        assert f[i] == (99 if signalled[i] else 0), f"signal {i}"
