@@ -19,7 +19,10 @@ the band it took.  From those:
     least one, and at least half of them, were;
   * phases per tile iteration, the drain (from the last mainloop's end to
     the kernel's last record), and each XCD's last mainloop end (the skew
-    between XCDs).
+    between XCDs);
+  * store contention: during each tile's slot stores, how many other
+    workgroups of the same XCD are storing, and the store time by that
+    count.
 
   python -m computation_collective_amd.trace [--calls N] [--slot-dtype f32|bf16] [--out FILE]
                                             [--save-out FILE.npy]
@@ -178,8 +181,34 @@ def summarize(d, khz: int, P: int, mtiles: int, ntiles: int, pieces: int,
         lines.append(f"ready_to_folded_us median={np.median(lat):.1f} p90={np.percentile(lat, 90):.1f} "
                      f"max={lat.max():.1f} output_tiles_completed={len(ready)}")
 
-    # skew between XCDs (workgroups are dispatched round-robin: XCD = index mod 8)
+    # slot-store contention: while a workgroup stores its tile, how many other
+    # workgroups of its XCD store theirs (all of an XCD's stores leave through
+    # that XCD's L2), and the store time against that count
     xcd = d["wg"][has_tile] % XCDS
+    s0, s1 = tl[:, T_MAIN1], tl[:, T_STORED]
+    same = np.zeros(len(tl))
+    for x in range(XCDS):
+        m = np.nonzero(xcd == x)[0]
+        if len(m) == 0:
+            continue
+        c = np.zeros(nb + 1)
+        np.add.at(c, np.floor(s0[m] / step).astype(np.int64), 1)
+        np.add.at(c, np.floor(s1[m] / step).astype(np.int64), -1)
+        storing = np.cumsum(c)[:nb]
+        for k in m:
+            i0 = int(s0[k] / step)
+            i1 = max(int(s1[k] / step), i0 + 1)
+            same[k] = storing[i0:i1].mean() - 1
+    dur = s1 - s0
+    buckets = []
+    for lo, hi in ((0, 8), (8, 16), (16, 24), (24, 10 ** 9)):
+        m = (same >= lo) & (same < hi)
+        if m.any():
+            buckets.append(f"{lo}-{hi - 1 if hi < 10 ** 9 else 'up'}:{dur[m].mean():.2f},{int(m.sum())}")
+    lines.append(f"store_contention same_xcd_others_storing_mean={same.mean():.1f} "
+                 f"store_us_by_others_storing(mean,count)=" + " ".join(buckets))
+
+    # skew between XCDs (workgroups are dispatched round-robin: XCD = index mod 8)
     lastx = np.array([tl[xcd == x, T_MAIN1].max() for x in range(XCDS) if np.any(xcd == x)])
     lines.append("xcd_last_mainloop_end_us " + " ".join(f"{v:.1f}" for v in lastx) +
                  f" spread={lastx.max() - lastx.min():.1f}")

@@ -65,3 +65,23 @@ def test_output_tile_matches_the_kernels_item_order():
                 for mt in range(mtiles):
                     item = p * tpc * P + r * tpc + nt * mtiles + mt
                     assert tr.output_tile(item, P, mtiles, ntiles) == r * tpc + mt * ntiles + nt
+
+
+def test_store_contention_counts_the_same_xcds_storers():
+    # workgroups are dispatched round-robin over 8 XCDs: 0, 8 and 16 share XCD 0, 1 is on XCD 1.
+    # wg 0 and wg 8 store 10..14 us together; wg 16 stores 30..32 us alone on its XCD;
+    # wg 1 stores 10..12 us on another XCD (not counted against XCD 0)
+    T = lambda *us: [int(1000 + 100 * u) for u in us]
+    rows = [
+        _rec(0, 0, T(0, 1, 2, 10, 14, 15), 0, 0, tr.BIT_IN_LOOP),
+        _rec(8, 0, T(0, 1, 2, 10, 14, 15), 1, -1, 0),
+        _rec(16, 0, T(20, 21, 22, 30, 32, 33), 2, -1, 0),
+        _rec(1, 0, T(0, 1, 2, 10, 12, 13), 3, -1, 0),
+    ]
+    d = tr.parse(_records(rows), tr.TRACE_WGS)
+    lines = tr.summarize(d, 100_000, P=2, mtiles=1, ntiles=2, pieces=2)
+    line = next(l for l in lines if l.startswith("store_contention"))
+    f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
+    assert abs(float(f["same_xcd_others_storing_mean"]) - 0.5) < 1e-9    # (1 + 1 + 0 + 0) / 4
+    # all four below 8 others: store times 4, 4, 2, 2 us
+    assert line.endswith("0-7:3.00,4")
