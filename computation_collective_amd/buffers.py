@@ -250,6 +250,11 @@ class AgGemm(_Common):
         assert self.flags_mode == "device" and isinstance(self.A, torch.Tensor)
         stream = stream or torch.cuda.current_stream()
         s = self.next_sync(**kw)
+        if s.epoch >= _EPOCH_WORDS:
+            # the signal table holds epochs below 2^16: start over at 1 (it still
+            # differs from the previous call's epoch, the flags' only requirement)
+            self.epoch = 0
+            s = self.next_sync(**kw)
         chunk_bytes = self.Mc * self.K * 2
         base, fbase = self.A.data_ptr(), self.chunk_flags.data_ptr()
         src, dst, nbytes, sig = [], [], [], []

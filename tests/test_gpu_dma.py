@@ -89,7 +89,8 @@ def test_put_copies_bytes_and_signals(engine, signalled):
 @pytest.mark.parametrize("P,Mc,N,K,tm", [(4, 300, 520, 200, 256), (8, 128, 256, 64, 128)])
 def test_ag_gemm_put_delivered_chunks(engine, P, Mc, N, K, tm):
     """Every chunk comes from its own send buffer by a put; two input sets
-    alternate over four calls, in different orders."""
+    alternate over six calls, in different orders, the last two across the
+    wrap of the epochs the put signals can carry."""
     say(f"ag_gemm put-delivered engine={engine} P={P} Mc={Mc} N={N} K={K} tile={tm}")
     sets = [gen.ag_gemm_inputs(P, Mc, N, K, seed=s) for s in (P + N, P + N + 1)]
     W = sets[0][1]
@@ -107,16 +108,20 @@ def test_ag_gemm_put_delivered_chunks(engine, P, Mc, N, K, tm):
         wants.append(pre.out.clone())
         _, ref = oracle.ag_gemm(P, Mc, N, K, BF16, BF16, list(chunks), W)
         assert relerr(gen.bf16_decode(bf.to_host(pre.out, BF16)), gen.bf16_decode(ref)) <= 2e-2
-    for call in range(4):
+    for call in range(6):
         k = call % 2
         order = sets[k][2] if call < 2 else sets[k][2][::-1]
+        if call == 4:
+            run.epoch = (1 << 16) - 2   # the next two calls: the last epoch the signal table holds, then 1
         bf.nan_fill(run.A)
         run.poison()
-        run.put_delivered(sends[k], order, engine, put_stream, spin_timeout_ns=SPIN_NS)
+        s = run.put_delivered(sends[k], order, engine, put_stream, spin_timeout_ns=SPIN_NS)
         torch.cuda.synchronize()
         assert run.status_value() == 0, hocf.status_string(run.status_value())
         assert torch.equal(run.out, wants[k]), f"call {call}: output differs from the pre-delivered run"
         assert torch.all(run.ws == 0)
+        if call == 5:
+            assert s.epoch == 1
 
 
 @pytest.mark.parametrize("engine", ENGINES)
