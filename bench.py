@@ -572,13 +572,17 @@ def main():
     names = [o for o in ops if o in runs] + [n for n in runs if n not in ops]
     ev = {n: [] for n in names}
 
-    # every other step runs the operators in reverse order, so the two members of a
-    # fused / unfused pair each follow the other half of the time (an operator that comes
-    # right after a large GEMM measures slower than in isolation)
+    # every other step swaps the two members of each fused / unfused pair, so each follows
+    # the other half of the time and the operator before the pair the other half (an
+    # operator that comes right after a large GEMM measures slower than in isolation)
     nstep = {"i": 0}
+    swapped = list(names)
+    for i in range(len(swapped) - 1):
+        if swapped[i + 1] == swapped[i] + "_unfused":
+            swapped[i], swapped[i + 1] = swapped[i + 1], swapped[i]
 
     def step(record):
-        order = names if nstep["i"] % 2 == 0 else names[::-1]
+        order = names if nstep["i"] % 2 == 0 else swapped
         nstep["i"] += 1
         for n in order:
             if "pre" in runs[n]:
