@@ -18,9 +18,9 @@
 //   1. stores it into destination r's window, slot p (publish), with
 //      device-coherent full-row stores, and waits for their completion,
 //   2. stores the epoch into the tile's ready flag in window r,
-//   3. counts itself in the output tile's arrival counter; the workgroup
-//      that completes the count (the last of the P producers) marks the
-//      tile ready: its reduction is PIECES bands of rows, band q of every
+//   3. counts itself in the output tile's arrival counter (an atomic add
+//      whose result it does not wait for); the tile is ready once the count
+//      reaches P: its reduction is PIECES bands of rows, band q of every
 //      output tile sitting in band queue q (one queue per XCD),
 //   4. folds one band of a completed tile, if its band queue has one for it:
 //      checks the P flags and folds the P slots of the band's rows in rank
@@ -36,8 +36,8 @@
 // queue follow the order in which output tiles complete (every shard's
 // items run in the same chunk and tile order), so a workgroup claims the
 // next slot of its home queue with one atomic add, holds it, and checks its
-// tile's ready word after each of its own tiles, never waiting while tiles
-// remain; completing an output tile costs its last producer one store.
+// tile's arrival count after each of its own tiles, never waiting while
+// tiles remain.  The last workgroup out zeroes the counts for the next call.
 // Without tiles a workgroup waits (bounded) for its slot, then helps drain
 // the other queues; tiles are always claimed by running workgroups, so
 // every slot becomes ready and the kernel ends.
@@ -156,17 +156,16 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
   const int nout = AR ? a.nout : 1;
   const int tpc = a.mtiles * a.ntiles;
   const int64_t ngroups = (int64_t)P * tpc;
-  // workspace after the queue block: arrival counters [P][tpc], band queue
-  // heads [8] (and 8 spare words), then one ready word per output tile
-  // (the rest of that area is spare)
+  // workspace after the queue block: arrival counters [P][tpc] (an output
+  // tile is ready when its count reaches P), band queue heads [8] (and 8
+  // spare words), then one spare word per output tile
   uint32_t* grp = a.ws + kWsExtra;
   uint32_t* bq_head = grp + ngroups;
-  uint32_t* gready = bq_head + 2 * kNumQueues;
   // Band queue q (q < S) holds band q of every output tile, in the order in
   // which the tiles' last contributions are computed (chunk-major, then the
   // item order within a chunk): slot t -> output tile band_tile(t).  A slot
   // is claimed with one atomic add on the queue's head and is ready once
-  // its tile's ready word is set; producers never touch the queues.
+  // its tile's arrival count is P; producers never touch the queues.
   auto bq_total = [&](int q) { return q < S ? (uint32_t)ngroups : 0u; };
   auto band_tile = [&](uint32_t t) {
     const int r = (int)(t / tpc), tq = (int)(t % tpc);
@@ -221,7 +220,7 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
       }
       if (pend_q >= 0) {
         const int64_t g = band_tile(pend_i);
-        uint32_t e = __hip_atomic_load(&gready[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t e = __hip_atomic_load(&grp[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)P;
         if (e == 0 && !tl) {
           // nothing else to do: wait (bounded; an abort request ends it) for
           // the slot's tile to complete
@@ -229,7 +228,7 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
           int w = kWaitOk;
           while (e == 0) {
             __builtin_amdgcn_s_sleep(4);
-            e = __hip_atomic_load(&gready[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            e = __hip_atomic_load(&grp[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)P;
             if (e != 0) break;
             if (abort_requested(a.sync)) { w = kWaitAborted; break; }
             if (wl.expired()) { w = kWaitTimeout; break; }
@@ -323,19 +322,18 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
       wait_memory();  // this thread's stores of the tile have completed
       __syncthreads();
       trace.mark(kTrStored);
-      // 2. ready flag; 3. arrival count -> the last producer hands out the bands
+      // 2. ready flag; 3. arrival count (P: the tile's bands are ready)
       if (tid == 0) {
         // (the tile's data is complete; readers of the flag re-read it, bounded,
         // if they get there before the flag store has)
         __hip_atomic_store(&a.win_flags[r][(int64_t)p * tpc + tflag], a.sync.epoch, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t* cnt = &grp[(int64_t)r * tpc + tflag];
-        const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == (uint32_t)(P - 1)) {
-          // the last producer: the tile's bands are ready
-          __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(&gready[(int64_t)r * tpc + tflag], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          completed = kTrCompleted;
+        // (no wait for the result: a band's claimer reads the count itself;
+        // only the trace build looks at it, to mark the tile's completion)
+        const uint32_t prev =
+            __hip_atomic_fetch_add(&grp[(int64_t)r * tpc + tflag], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (kTraceBuild) {
+          if (prev == (uint32_t)(P - 1)) completed = kTrCompleted;
         }
       }
       // (the barrier at the top of the loop ends this thread-0 region)
@@ -347,10 +345,11 @@ __device__ __forceinline__ void gemm_collective(const GemmRsArgs& a) {
     }
   }
 
-  // the last workgroup out leaves the workspace zeroed
+  // the last workgroup out leaves the workspace zeroed (arrival counts, queue
+  // heads and the spare words after them)
   if (finish_workgroup_last(a.ws, &s_last)) {
-    for (int64_t i = tid; i < 2 * kNumQueues + ngroups; i += Tile::NT)
-      __hip_atomic_store(&bq_head[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int64_t i = tid; i < ngroups + 2 * kNumQueues + ngroups; i += Tile::NT)
+      __hip_atomic_store(&grp[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
