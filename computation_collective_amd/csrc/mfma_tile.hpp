@@ -670,47 +670,51 @@ struct TileF32 {
 
     // (vector types, not the float4 struct: an aggregate copy of the struct
     // into LDS kept these staging registers on the stack)
-    floatx4 ra[A_LD], rb[B_LD];
+    // A ring of D slices in registers: slice ks + D is requested while slice
+    // ks is computed, so D slices' load latencies overlap (the small-K calls
+    // this tile serves are bound by that latency, not by the matrix cores).
+    constexpr int D = 8;
+    floatx4 ra[D][A_LD], rb[D][B_LD];
     const int nk = (K + BK - 1) / BK;
 
-    auto load_global = [&](int ks) {
+    auto load_global = [&](int ks, floatx4 (&pa)[A_LD], floatx4 (&pb)[B_LD]) {
       const int k0 = ks * BK;
 #pragma unroll
       for (int t = 0; t < A_LD; ++t) {
         const int c = tid + t * NT;
         const int row = c / (BK / 4), k = k0 + (c % (BK / 4)) * 4;
         if (!RAGGED || (row < rows_valid && k < K))
-          ra[t] = *reinterpret_cast<const floatx4*>(A + (int64_t)row * lda + k);
+          pa[t] = *reinterpret_cast<const floatx4*>(A + (int64_t)row * lda + k);
         else
-          ra[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+          pa[t] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int t = 0; t < B_LD; ++t) {
         const int c = tid + t * NT;
         const int k = k0 + c / (TN / 4), n = (c % (TN / 4)) * 4;
         if (!RAGGED || (k < K && n < cols_valid))
-          rb[t] = *reinterpret_cast<const floatx4*>(W + (int64_t)k * ldw + n);
+          pb[t] = *reinterpret_cast<const floatx4*>(W + (int64_t)k * ldw + n);
         else
-          rb[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+          pb[t] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
     };
-    auto store_lds = [&](int stage) {
+    auto store_lds = [&](int stage, const floatx4 (&pa)[A_LD], const floatx4 (&pb)[B_LD]) {
       float* As = lds + stage * STAGE;
       float* Bs = As + A_ELEMS;
 #pragma unroll
       for (int t = 0; t < A_LD; ++t) {
         const int c = tid + t * NT;
         const int row = c / (BK / 4), kq = (c % (BK / 4)) * 4;
-        As[row * LDA + kq + 0] = ra[t][0];
-        As[row * LDA + kq + 1] = ra[t][1];
-        As[row * LDA + kq + 2] = ra[t][2];
-        As[row * LDA + kq + 3] = ra[t][3];
+        As[row * LDA + kq + 0] = pa[t][0];
+        As[row * LDA + kq + 1] = pa[t][1];
+        As[row * LDA + kq + 2] = pa[t][2];
+        As[row * LDA + kq + 3] = pa[t][3];
       }
 #pragma unroll
       for (int t = 0; t < B_LD; ++t) {
         const int c = tid + t * NT;
         const int k = c / (TN / 4), n = (c % (TN / 4)) * 4;
-        *reinterpret_cast<floatx4*>(Bs + k * LDB + n) = rb[t];
+        *reinterpret_cast<floatx4*>(Bs + k * LDB + n) = pb[t];
       }
     };
     auto compute = [&](int stage) {
@@ -733,14 +737,23 @@ struct TileF32 {
     };
 
     if (nk == 0) return;
-    load_global(0);
-    store_lds(0);
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < nk) load_global(d, ra[d], rb[d]);
+    store_lds(0, ra[0], rb[0]);
     __syncthreads();
-    for (int ks = 0; ks < nk; ++ks) {
-      if (ks + 1 < nk) load_global(ks + 1);
-      compute(ks & 1);
-      if (ks + 1 < nk) store_lds((ks + 1) & 1);
-      __syncthreads();
+    for (int ks0 = 0; ks0 < nk; ks0 += D) {
+      // ring slot u holds slice ks0 + u until it is in LDS, then slice ks0 + u + D
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const int ks = ks0 + u;
+        if (ks < nk) {
+          if (ks + D < nk) load_global(ks + D, ra[u], rb[u]);
+          compute(ks & 1);
+          if (ks + 1 < nk) store_lds((ks + 1) & 1, ra[(u + 1) % D], rb[(u + 1) % D]);
+          __syncthreads();
+        }
+      }
     }
   }
 };
